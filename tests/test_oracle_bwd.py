@@ -1,0 +1,72 @@
+"""Pins of the fp64 oracle's BPTT (M²RNN notes §2.7) against central finite differences of the
+oracle's own forward (an independent code path), and against the closed form at f = 1."""
+import numpy as np
+import pytest
+
+import oracle
+from matrix_state_nonlinear_m2rnn_amd import inputs
+
+
+def loss(d, dy, dHT):
+    y, H_T = oracle.ref_fwd(d["q"], d["k"], d["v"], d["f"], d["W"], d["w_r"], d["H0"])
+    return float(np.sum(y * dy) + np.sum(H_T * dHT))
+
+
+@pytest.mark.parametrize("B,T,N,K,V", [(1, 5, 2, 3, 2), (2, 4, 1, 2, 3)])
+def test_gradients_match_central_differences(B, T, N, K, V):
+    d = inputs.make_inputs(B, T, N, K, V, qkv_dtype="f32", seed=31 + K, with_H0=True, with_dy=True,
+                           with_dHT=True)
+    d = {x: (a.astype(np.float64) if a is not None else None) for x, a in d.items()}
+    d["W"] *= 1.5  # leave the near-linear regime
+    d["k"] *= 3.0
+    dy, dHT = d.pop("dy"), d.pop("dH_T")
+    g = oracle.ref_bwd(d["q"], d["k"], d["v"], d["f"], d["W"], d["w_r"], d["H0"], dy, dHT)
+    names = {"q": "dq", "k": "dk", "v": "dv", "f": "df", "W": "dW", "w_r": "dw_r", "H0": "dH0"}
+    h = 1e-6
+    for x, gx in names.items():
+        a = d[x]
+        num = np.empty_like(a)
+        flat = a.reshape(-1)
+        for i in range(flat.size):
+            keep = flat[i]
+            flat[i] = keep + h
+            lp = loss(d, dy, dHT)
+            flat[i] = keep - h
+            lm = loss(d, dy, dHT)
+            flat[i] = keep
+            num.reshape(-1)[i] = (lp - lm) / (2 * h)
+        err = np.max(np.abs(num - g[gx])) / max(1e-3, np.max(np.abs(num)))
+        assert err < 1e-6, (x, err)
+
+
+def test_closed_form_when_f_is_one():
+    # f = 1 freezes the state at H_0 and blocks the tanh branch (1 - f = 0), so D = 0:
+    # dk = 0, dW = 0, dv_t = w_r (.) u_t, dq_t = H_0 u_t, dw_r = sum_t u_t (.) v_t,
+    # dH_0 = dH_T + sum_t q_t u_t^T, and df_t = <R_t, H_0 - Z_t> with R_t = dH_T + sum_{s>=t} q_s u_s^T.
+    B, T, N, K, V = 2, 6, 2, 3, 4
+    d = inputs.make_inputs(B, T, N, K, V, qkv_dtype="f32", seed=77, with_H0=True, with_dy=True, with_dHT=True)
+    d = {x: (a.astype(np.float64) if a is not None else None) for x, a in d.items()}
+    d["f"][:] = 1.0
+    g = oracle.ref_bwd(d["q"], d["k"], d["v"], d["f"], d["W"], d["w_r"], d["H0"], d["dy"], d["dH_T"])
+    u, q, v, k = d["dy"], d["q"], d["v"], d["k"]
+    assert np.all(g["dk"] == 0.0) and np.all(g["dW"] == 0.0)
+    np.testing.assert_allclose(g["dv"], d["w_r"][None, None] * u, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(g["dq"], np.einsum("bnkv,btnv->btnk", d["H0"], u), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(g["dw_r"], np.einsum("btnv,btnv->nv", u, v), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["dH0"], d["dH_T"] + np.einsum("btnk,btnv->bnkv", q, u), rtol=0, atol=1e-12)
+    for b in range(B):
+        for n in range(N):
+            R = d["dH_T"][b, n].copy()
+            for t in range(T - 1, -1, -1):
+                R = R + np.outer(q[b, t, n], u[b, t, n])
+                Z = np.tanh(d["H0"][b, n] @ d["W"][n] + np.outer(k[b, t, n], v[b, t, n]))
+                np.testing.assert_allclose(g["df"][b, t, n], np.sum(R * (d["H0"][b, n] - Z)), rtol=1e-12,
+                                           atol=1e-12)
+
+
+def test_zero_upstream_gives_zero_gradients():
+    d = inputs.make_inputs(2, 5, 2, 4, 4, qkv_dtype="f32", seed=3, with_dy=True)
+    dy = np.zeros_like(d["dy"])
+    g = oracle.ref_bwd(d["q"], d["k"], d["v"], d["f"], d["W"], d["w_r"], None, dy, None)
+    for x in g.values():
+        assert np.all(x == 0.0)
