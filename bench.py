@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of the M²RNN forward recurrence on one MI355X (gfx950).
+
+One step = one full forward pass (all T steps of the recurrence for every (batch, head)) of the
+16K-token workload B=2, N=32 heads, T=16384, K=V=64 with bf16 q/k/v and fp32 state, on synthetic
+seeded inputs already resident in HBM.  The step runs the library's two launches (the scan and the
+readout finish) exactly as ``m2rnn_fwd`` does; HIP events on the launch stream bracket the scan
+kernel of every timed step, which gives the dominant kernel's average duration for the roofline.
+
+Prints ONE JSON line.  ``--gpus`` above 1 is refused: the recurrence of one (batch, head) pair is
+a serial chain that this build runs on a single GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "M²RNN fwd head-steps/sec + % MFMA peak at K=V=64, T=16384 (1 GPU)"
+# MI355X published dense peaks (TFLOP/s).
+PEAK_TFLOPS = {"f32": 157.3, "f16x3": 2500.0, "bf16x3": 2500.0, "bf16": 2500.0}
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["m2rnn_device.h", "m2rnn_fwd_kernel.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "matrix_state_nonlinear_m2rnn_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, math_mode: str):
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary, or None when the
+    summary is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"m2rnn_scan_fwd_{workload}_{math_mode}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_sources_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(d, w, seconds: float):
+    """Times the fp64 oracle (as it stands) on a bounded sample of the same workload: the first
+    `threads` (batch, head) units, each over the first T_s steps, one unit per thread.  T_s is
+    sized from a one-thread probe so that the sample takes about `seconds` of wall time."""
+    import numpy as np
+    import oracle
+
+    nthreads = oracle.default_threads()
+    units = min(w.B * w.N, nthreads)
+    pairs = [(u // w.N, u % w.N) for u in range(units)]
+
+    def run(T, nunits, threads):
+        # Units become the heads of one batch entry: q [1, T, units, K], W [units, V, V], ...
+        sel = pairs[:nunits]
+        g = lambda a: np.stack([a[b, :T, n] for b, n in sel], axis=1)[None]  # noqa: E731
+        W = np.stack([d["W"][n] for _, n in sel])
+        w_r = np.stack([d["w_r"][n] for _, n in sel])
+        t0 = time.perf_counter()
+        oracle.ref_fwd(g(d["q"]), g(d["k"]), g(d["v"]), g(d["f"]), W, w_r, None, nthreads=threads)
+        return time.perf_counter() - t0
+
+    probe_T = min(w.T, 128)
+    per_step = run(probe_T, 1, 1) / probe_T
+    T_s = int(max(64, min(w.T, seconds / max(per_step, 1e-9))))
+    wall = run(T_s, units, nthreads)
+    return {"value": units * T_s / wall, "unit": "head-steps/s", "cores": min(nthreads, units), "kind": "oracle",
+            "sample": f"{units} (batch, head) units x {T_s} steps of {w.name} (fp64, one unit per thread)",
+            "wall_s": round(wall, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_b2_h32_t16384_kv64")
+    ap.add_argument("--math", default="auto", choices=["auto", "f32", "f16x3", "bf16x3", "bf16"])
+    ap.add_argument("--row-blocks", type=int, default=0)
+    ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of known size (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): the recurrence of a "
+              "(batch, head) pair is a serial chain and this build has no multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    from matrix_state_nonlinear_m2rnn_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    w = inputs.WORKLOADS[args.workload]
+    math_mode = "f16x3" if args.math == "auto" else args.math
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    d = inputs.workload_inputs(w.name)
+    dev = torch.device("cuda:0")
+    qkv_t = torch.bfloat16 if w.qkv_dtype == "bf16" else torch.float32
+    t = {n: torch.from_numpy(np.ascontiguousarray(a)).to(dev) for n, a in d.items() if a is not None}
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(qkv_t).contiguous()
+    B, T, N, K, V = w.B, w.T, w.N, w.K, w.V
+    y = torch.empty((B, T, N, V), dtype=torch.float32, device=dev)
+    H_T = torch.empty((B, N, K, V), dtype=torch.float32, device=dev)
+    dims = m2.Dims(B, T, N, K, V)
+    dt = m2.DTYPE_BF16 if w.qkv_dtype == "bf16" else m2.DTYPE_F32
+    nbytes = m2.m2rnn_fwd_workspace_size(dims, dt, math_mode, args.row_blocks)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    common = dict(math=math_mode, row_blocks=args.row_blocks, y=y, H_T=H_T, workspace=ws)
+
+    def step(ev0=None, ev1=None):
+        if ev0 is not None:
+            ev0.record()
+        m2.m2rnn_scan_fwd(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], None, **common)
+        if ev1 is not None:
+            ev1.record()
+        m2.m2rnn_scan_fwd_finish(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], None, **common)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e_start.record()
+    for i in range(args.steps):
+        step(*evs[i])
+    e_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = e_start.elapsed_time(e_end)
+    scan_ms = [a.elapsed_time(b) for a, b in evs]
+    scan_avg = sum(scan_ms) / len(scan_ms)
+    head_steps = B * N * T
+    value = head_steps * args.steps / (total_ms * 1e-3)
+    flops = 2.0 * K * V * V * head_steps
+    achieved = flops / (scan_avg * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[math_mode]
+    traffic = measured_traffic(w.name, math_mode)
+
+    if args.copy_calibration:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings scale the scan's.
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "head-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "N": N, "K": K, "V": V, "qkv_dtype": w.qkv_dtype,
+                   "math": math_mode, "row_blocks": args.row_blocks or "auto"},
+        "tokens_per_s": B * T * args.steps / (total_ms * 1e-3),
+        "ns_per_recurrence_step": scan_avg * 1e6 / T,
+        "scan_ms": scan_avg,
+        "wall_s": wall,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "algorithmic_flops_per_launch": flops,
+                     "frac_of_fp32_mfma_peak": achieved / PEAK_TFLOPS["f32"]},
+    }
+    if args.cpu_baseline == "on":
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(d, w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,149 @@
+/*
+ * m2rnn.h — C ABI of the MI355X (gfx950) M²RNN recurrence library (libm2rnn.so).
+ *
+ * The operation is the M²RNN matrix-state nonlinear recurrence of the reading notes
+ * "M²RNN：矩阵状态非线性 RNN 的容量、表达力与系统代价" on arXiv:2603.14360v2 ("M²RNN notes"):
+ * for every batch entry b and head n, independently, starting from H_0 (zeros, or a given state),
+ *
+ *     Z_t = tanh(H_{t-1} W_n + k_t v_t^T)          (§2.1, Eq. 10)
+ *     H_t = f_t H_{t-1} + (1 - f_t) Z_t             (§2.1, Eq. 11)
+ *     y_t = H_t^T q_t + w_r,n (.) v_t               (§2.1, Eq. 12)
+ *
+ * with H_t a K x V state, W_n a V x V matrix per head (right-multiplied, so it mixes the value
+ * dimension only: (H W)[i][j] = sum_l H[i][l] W[l][j]), f_t a scalar per (batch, step, head),
+ * and w_r,n a V-vector per head.  The backward is the chain-rule BPTT of §2.7.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensor layouts are contiguous row-major:
+ *        q, k      [B, T, N, K]     (dtype given by qkv_dtype)
+ *        v         [B, T, N, V]     (dtype given by qkv_dtype)
+ *        f         [B, T, N]        fp32, expected in [0, 1] (not checked, computed as given)
+ *        W         [N, V, V]        fp32
+ *        w_r       [N, V]           fp32
+ *        H0, H_T   [B, N, K, V]     fp32
+ *        y, dy     [B, T, N, V]     fp32
+ *    Gradients have the shape of their input and are fp32.
+ *  - Every array pointer is a DEVICE pointer on the current HIP device, 16-byte aligned.  The
+ *    caller owns all memory, including the workspace; the library allocates no device memory
+ *    and keeps no mutable global state, so calls on different streams may run concurrently.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call returns
+ *    without synchronising.  Outputs are valid once the stream reaches that point.
+ *  - Outputs are overwritten, never accumulated.  Outputs must not alias inputs or each other.
+ *  - Arguments are validated on the host before anything is enqueued; an invalid call returns
+ *    an error status and touches no memory.  M2RNN_EHIP reports a launch failure
+ *    (m2rnn_last_hip_error() gives the hipError_t of the most recent one on this thread).
+ *  - Supported sizes: V in {16, 32, 64, 128}; K a positive multiple of 16; B, T, N >= 0.
+ *    T = 0 is legal: y is empty and H_T = H0 (or zeros).
+ */
+#ifndef M2RNN_H_
+#define M2RNN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct m2rnn_dims {
+  int64_t B; /* batch */
+  int64_t T; /* steps */
+  int64_t N; /* heads */
+  int64_t K; /* key size: rows of the state */
+  int64_t V; /* value size: columns of the state, side of W */
+} m2rnn_dims;
+
+/* dtype of q, k, v. */
+enum { M2RNN_DTYPE_F32 = 0, M2RNN_DTYPE_BF16 = 1 };
+
+/* How the per-step contraction H_{t-1} W runs on the matrix cores.  The state, the
+ * accumulation and everything outside the contraction are fp32 in every mode.
+ *   F32     fp32 MFMA (v_mfma_f32_16x16x4_f32).
+ *   F16X3   split precision: H = H_hi (fp16) + H_lo (bf16), W = W_hi (fp16) + W_lo (fp16);
+ *           H W ~ W_hi H_hi + W_lo H_hi + W_bf16 H_lo on fp16/bf16 MFMA, fp32 accumulate.
+ *   BF16X3  split precision with bf16 halves: W_hi H_hi + W_lo H_hi + W_hi H_lo.
+ *   BF16    one bf16 pass: bf16(W) bf16(H) (coarse; meant for a 2e-2 error budget).
+ *   AUTO    the library's default (F16X3). */
+enum { M2RNN_MATH_AUTO = -1, M2RNN_MATH_F32 = 0, M2RNN_MATH_F16X3 = 1, M2RNN_MATH_BF16X3 = 2, M2RNN_MATH_BF16 = 3 };
+
+/* Status codes. */
+enum {
+  M2RNN_OK = 0,
+  M2RNN_EINVAL = -1,      /* null required pointer, negative size, misaligned pointer, bad enum */
+  M2RNN_EUNSUPPORTED = -2, /* K or V outside the supported set, or a mode not built */
+  M2RNN_EWORKSPACE = -3,   /* workspace missing or smaller than the *_workspace_size answer */
+  M2RNN_EHIP = -4          /* a HIP launch or runtime call failed */
+};
+
+/* Library version, as MAJOR*10000 + MINOR*100 + PATCH. */
+int m2rnn_version(void);
+
+/* Human-readable text for a status code (static storage). */
+const char* m2rnn_status_string(int status);
+
+/* hipError_t of the last HIP failure seen by this thread (0 if none). */
+int m2rnn_last_hip_error(void);
+
+/*
+ * Forward pass, Eq. (10)-(12).  One pass over all T steps for every (b, n).
+ *
+ *   row_blocks   0 = automatic; otherwise the number of 16-row blocks of the state that one
+ *                workgroup carries (must divide K/16).  The K rows of a state evolve
+ *                independently (W mixes only the value dimension, §1.2), so a (b, n) pair may be
+ *                split over S = K/(16*row_blocks) workgroups; when S > 1 their partial readouts are
+ *                summed by a second, deterministic pass.
+ *   H0           initial state, or NULL for zeros.
+ *   y            output [B,T,N,V] (may be NULL only when T == 0 or B*N == 0).
+ *   H_T          final state [B,N,K,V], or NULL to skip it.
+ *   workspace    device scratch of at least m2rnn_fwd_workspace_size() bytes (NULL if that is 0).
+ */
+int m2rnn_fwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks,
+                             size_t* bytes);
+int m2rnn_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q,
+              const void* k, const void* v, const float* f, const float* W, const float* w_r,
+              const float* H0, float* y, float* H_T, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+/*
+ * The two launches m2rnn_fwd makes, exposed so that a caller can time them apart.  Same
+ * arguments as m2rnn_fwd.  m2rnn_scan_fwd runs the recurrence (it writes y directly when one
+ * workgroup carries all K rows, else per-workgroup partial readouts into the workspace);
+ * m2rnn_scan_fwd_finish then forms y = sum of partials + w_r (.) v, and is a no-op when the scan
+ * already wrote y.  Calling both, in order, on one stream is exactly m2rnn_fwd.
+ */
+int m2rnn_scan_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q,
+                   const void* k, const void* v, const float* f, const float* W, const float* w_r,
+                   const float* H0, float* y, float* H_T, void* workspace, size_t workspace_bytes,
+                   void* stream);
+int m2rnn_scan_fwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks,
+                          const void* q, const void* k, const void* v, const float* f,
+                          const float* W, const float* w_r, const float* H0, float* y, float* H_T,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass (BPTT of §2.7) for the loss L = sum_t <dy_t, y_t> + <dH_T, H_T>.
+ *
+ * The forward states are not taken from the caller: the library re-runs the recurrence and keeps
+ * the state every `M2RNN_BWD_CHECKPOINT` steps, then walks the segments from last to first,
+ * recomputing each segment's states from its checkpoint (the notes' §2.6 re-runs the recurrence
+ * at the start of the backward; here only checkpoints are stored, not every state).
+ *
+ *   dH_T   upstream gradient of the final state, or NULL for zeros.
+ *   dq, dk [B,T,N,K]; dv [B,T,N,V]; df [B,T,N]; dW [N,V,V] and dw_r [N,V] summed over batch and
+ *   time; dH0 [B,N,K,V] or NULL to skip it.  All fp32.
+ *   math   M2RNN_MATH_F32 or M2RNN_MATH_F16X3 (AUTO = F16X3).
+ */
+#define M2RNN_BWD_CHECKPOINT 64
+int m2rnn_bwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes);
+int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k,
+              const void* v, const float* f, const float* W, const float* w_r, const float* H0,
+              const float* dy, const float* dH_T, float* dq, float* dk, float* dv, float* df,
+              float* dW, float* dw_r, float* dH0, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M2RNN_H_ */

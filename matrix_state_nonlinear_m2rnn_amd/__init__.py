@@ -1,0 +1,240 @@
+"""MI355X (gfx950) M²RNN recurrence: thin Python binding of libm2rnn.so.
+
+The functions here carry the names of the C entry points in ``include/m2rnn.h`` and only marshal
+arguments: they check devices, dtypes and shapes of torch tensors, allocate outputs and the
+workspace with torch (device memory and streams are all torch is used for), and pass raw device
+pointers plus the current HIP stream to the library.  Every step of the recurrence runs in the
+library's HIP kernels.  There is no fallback: if ``libm2rnn.so`` is missing or fails to load, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libm2rnn.so")
+
+M2RNN_OK = 0
+M2RNN_EINVAL = -1
+M2RNN_EUNSUPPORTED = -2
+M2RNN_EWORKSPACE = -3
+M2RNN_EHIP = -4
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+MATH = {"auto": -1, "f32": 0, "f16x3": 1, "bf16x3": 2, "bf16": 3}
+BWD_CHECKPOINT = 64
+
+EXPORTED = (
+    "m2rnn_version", "m2rnn_status_string", "m2rnn_last_hip_error", "m2rnn_fwd_workspace_size", "m2rnn_fwd",
+    "m2rnn_scan_fwd", "m2rnn_scan_fwd_finish", "m2rnn_bwd_workspace_size", "m2rnn_bwd",
+)
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("V", ctypes.c_int64)]
+
+
+class M2RNNError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str, hip_error: int = 0):
+        extra = f" (hipError {hip_error})" if status == M2RNN_EHIP else ""
+        super().__init__(f"{fn} failed: {msg} [status {status}]{extra}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libm2rnn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                               "g.build()'` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, ci = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        dp = ctypes.POINTER(Dims)
+        L.m2rnn_version.restype = ci
+        L.m2rnn_version.argtypes = []
+        L.m2rnn_status_string.restype = ctypes.c_char_p
+        L.m2rnn_status_string.argtypes = [ci]
+        L.m2rnn_last_hip_error.restype = ci
+        L.m2rnn_last_hip_error.argtypes = []
+        L.m2rnn_fwd_workspace_size.restype = ci
+        L.m2rnn_fwd_workspace_size.argtypes = [dp, ci, ci, ci, ctypes.POINTER(sz)]
+        fwd_args = [dp, ci, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp] + [vp, sz, vp]
+        for name in ("m2rnn_fwd", "m2rnn_scan_fwd", "m2rnn_scan_fwd_finish"):
+            fn = getattr(L, name)
+            fn.restype = ci
+            fn.argtypes = fwd_args
+        if hasattr(L, "m2rnn_bwd"):
+            L.m2rnn_bwd_workspace_size.restype = ci
+            L.m2rnn_bwd_workspace_size.argtypes = [dp, ci, ci, ctypes.POINTER(sz)]
+            L.m2rnn_bwd.restype = ci
+            L.m2rnn_bwd.argtypes = [dp, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp] + [vp] * 7 + [vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().m2rnn_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != M2RNN_OK:
+        raise M2RNNError(fn, status, status_string(status), lib().m2rnn_last_hip_error())
+
+
+def _math(math) -> int:
+    if isinstance(math, int):
+        return math
+    if math not in MATH:
+        raise ValueError(f"math must be one of {sorted(MATH)}, got {math!r}")
+    return MATH[math]
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _require(t, name, dtype, shape, device):
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _fwd_prepare(q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, return_state):
+    import torch
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [B,T,N,K] and v [B,T,N,V]")
+    B, T, N, K = q.shape
+    V = v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU (HIP) device")
+    qkv_dtype = q.dtype
+    if qkv_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    _require(q, "q", qkv_dtype, (B, T, N, K), dev)
+    _require(k, "k", qkv_dtype, (B, T, N, K), dev)
+    _require(v, "v", qkv_dtype, (B, T, N, V), dev)
+    _require(f, "f", torch.float32, (B, T, N), dev)
+    _require(W, "W", torch.float32, (N, V, V), dev)
+    _require(w_r, "w_r", torch.float32, (N, V), dev)
+    if H0 is not None:
+        _require(H0, "H0", torch.float32, (B, N, K, V), dev)
+    if y is None:
+        y = torch.empty((B, T, N, V), dtype=torch.float32, device=dev)
+    _require(y, "y", torch.float32, (B, T, N, V), dev)
+    if H_T is None and return_state:
+        H_T = torch.empty((B, N, K, V), dtype=torch.float32, device=dev)
+    if H_T is not None:
+        _require(H_T, "H_T", torch.float32, (B, N, K, V), dev)
+    dims = Dims(B, T, N, K, V)
+    dt = DTYPE_BF16 if qkv_dtype == torch.bfloat16 else DTYPE_F32
+    return dims, dt, _math(math), int(row_blocks), y, H_T
+
+
+def m2rnn_fwd_workspace_size(dims: Dims, qkv_dtype: int, math="auto", row_blocks: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check("m2rnn_fwd_workspace_size",
+           lib().m2rnn_fwd_workspace_size(ctypes.byref(dims), qkv_dtype, _math(math), int(row_blocks), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _workspace(nbytes: int, device, workspace):
+    import torch
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _call_fwd(name, q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, workspace, stream, return_state):
+    dims, dt, m, rb, y, H_T = _fwd_prepare(q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, return_state)
+    nbytes = m2rnn_fwd_workspace_size(dims, dt, m, rb)
+    ws = _workspace(nbytes, q.device, workspace)
+    fn = getattr(lib(), name)
+    _check(name, fn(ctypes.byref(dims), dt, m, rb, _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0),
+                    _ptr(y), _ptr(H_T), _ptr(ws), nbytes, _stream(stream)))
+    return y, H_T, ws
+
+
+def m2rnn_fwd(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int = 0, y=None, H_T=None, workspace=None,
+              stream=None, return_state: bool = True) -> Tuple[object, Optional[object]]:
+    """Forward recurrence (M²RNN notes §2.1, Eq. 10-12) on the current HIP stream.
+
+    q, k: [B,T,N,K]; v: [B,T,N,V] (all float32 or all bfloat16); f: [B,T,N] fp32; W: [N,V,V] fp32;
+    w_r: [N,V] fp32; H0: [B,N,K,V] fp32 or None.  Returns (y [B,T,N,V] fp32, H_T [B,N,K,V] fp32).
+    """
+    y, H_T, _ = _call_fwd("m2rnn_fwd", q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, workspace, stream,
+                          return_state)
+    return y, H_T
+
+
+def m2rnn_scan_fwd(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int = 0, y=None, H_T=None,
+                   workspace=None, stream=None, return_state: bool = True):
+    """The scan launch of m2rnn_fwd alone; returns (y, H_T, workspace) for m2rnn_scan_fwd_finish."""
+    return _call_fwd("m2rnn_scan_fwd", q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, workspace, stream,
+                     return_state)
+
+
+def m2rnn_scan_fwd_finish(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int = 0, y=None, H_T=None,
+                          workspace=None, stream=None):
+    """The second launch of m2rnn_fwd (sums partial readouts when the rows were split)."""
+    y, H_T, _ = _call_fwd("m2rnn_scan_fwd_finish", q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, workspace,
+                          stream, False)
+    return y
+
+
+def m2rnn_bwd_workspace_size(dims: Dims, qkv_dtype: int, math="auto") -> int:
+    n = ctypes.c_size_t(0)
+    _check("m2rnn_bwd_workspace_size",
+           lib().m2rnn_bwd_workspace_size(ctypes.byref(dims), qkv_dtype, _math(math), ctypes.byref(n)))
+    return int(n.value)
+
+
+def m2rnn_bwd(q, k, v, f, W, w_r, H0, dy, dH_T=None, *, math="auto", want_dH0: bool = True, workspace=None,
+              stream=None) -> Dict[str, object]:
+    """BPTT (M²RNN notes §2.7) for L = sum <dy, y> + <dH_T, H_T>; returns dq, dk, dv, df, dW, dw_r, dH0."""
+    import torch
+    dims, dt, m, _, _, _ = _fwd_prepare(q, k, v, f, W, w_r, H0, None, None, math, 0, False)
+    B, T, N, K, V = dims.B, dims.T, dims.N, dims.K, dims.V
+    dev = q.device
+    _require(dy, "dy", torch.float32, (B, T, N, V), dev)
+    if dH_T is not None:
+        _require(dH_T, "dH_T", torch.float32, (B, N, K, V), dev)
+    e = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
+    out = {"dq": e(B, T, N, K), "dk": e(B, T, N, K), "dv": e(B, T, N, V), "df": e(B, T, N), "dW": e(N, V, V),
+           "dw_r": e(N, V), "dH0": e(B, N, K, V) if want_dH0 else None}
+    nbytes = m2rnn_bwd_workspace_size(dims, dt, m)
+    ws = _workspace(nbytes, dev, workspace)
+    _check("m2rnn_bwd", lib().m2rnn_bwd(
+        ctypes.byref(dims), dt, m, _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(dy),
+        _ptr(dH_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dW"]),
+        _ptr(out["dw_r"]), _ptr(out["dH0"]), _ptr(ws), nbytes, _stream(stream)))
+    return out

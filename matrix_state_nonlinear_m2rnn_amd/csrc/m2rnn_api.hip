@@ -1,0 +1,262 @@
+// Host side of libm2rnn.so: argument validation, launch planning and the C entry points
+// declared in include/m2rnn.h.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <unordered_map>
+
+#include "../../include/m2rnn.h"
+#include "m2rnn_select.h"
+
+using namespace m2rnn;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return M2RNN_OK;
+  g_last_hip_error = (int)e;
+  return M2RNN_EHIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_dims(const m2rnn_dims* d, int qkv_dtype) {
+  if (!d) return M2RNN_EINVAL;
+  if (d->B < 0 || d->T < 0 || d->N < 0 || d->K < 0 || d->V < 0) return M2RNN_EINVAL;
+  if (qkv_dtype != M2RNN_DTYPE_F32 && qkv_dtype != M2RNN_DTYPE_BF16) return M2RNN_EINVAL;
+  if (d->V != 16 && d->V != 32 && d->V != 64 && d->V != 128) return M2RNN_EUNSUPPORTED;
+  if (d->K <= 0 || d->K % 16 != 0) return M2RNN_EUNSUPPORTED;
+  // 32-bit indices inside the kernels: every (b, t, n) index and plane must fit.
+  const double plane = (double)d->B * d->T * d->N * (d->K > d->V ? d->K : d->V);
+  if (plane * 4.0 > 2147483647.0 || (double)d->B * d->N * d->K / 16 > 2147483647.0) return M2RNN_EUNSUPPORTED;
+  return M2RNN_OK;
+}
+
+int resolve_math(int math) {
+  if (math == M2RNN_MATH_AUTO) return M2RNN_MATH_F16X3;
+  if (math < M2RNN_MATH_F32 || math > M2RNN_MATH_BF16) return -1;
+  return math;
+}
+
+const void* fwd_kernel(int math, int V, int rb, bool bf16, int mode) {
+  switch (math) {
+    case M2RNN_MATH_F32: return fwd_kernel_f32(V, rb, bf16, mode);
+    case M2RNN_MATH_F16X3: return fwd_kernel_f16x3(V, rb, bf16, mode);
+    case M2RNN_MATH_BF16X3: return fwd_kernel_bf16x3(V, rb, bf16, mode);
+    case M2RNN_MATH_BF16: return fwd_kernel_bf16(V, rb, bf16, mode);
+    default: return nullptr;
+  }
+}
+
+struct DeviceInfo {
+  int cus = 0;
+};
+
+DeviceInfo device_info() {
+  static std::mutex mu;
+  static std::unordered_map<int, DeviceInfo> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DeviceInfo{};
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  DeviceInfo info;
+  if (hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) info.cus = 0;
+  cache[dev] = info;
+  return info;
+}
+
+int occupancy(const void* kernel, int threads) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, int> cache;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(kernel);
+    if (it != cache.end()) return it->second;
+  }
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, threads, 0) != hipSuccess) blocks = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  cache[kernel] = blocks;
+  return blocks;
+}
+
+// Row blocks per workgroup: the smallest that lets every workgroup be resident at once (one
+// wave of workgroups), else the one with the fewest waves of workgroups.
+int plan_row_blocks(const m2rnn_dims* d, int math, bool bf16, int mode, int requested) {
+  const int kb = (int)(d->K / 16);
+  if (requested > 0) return (kb % requested == 0 && fwd_kernel(math, (int)d->V, requested, bf16, mode)) ? requested : -1;
+  const DeviceInfo info = device_info();
+  const long units = d->B * d->N;
+  int best = -1;
+  double best_rounds = 1e30;
+  for (int rb : {1, 2, 4}) {
+    if (kb % rb != 0) continue;
+    const void* kern = fwd_kernel(math, (int)d->V, rb, bf16, mode);
+    if (!kern) continue;
+    const long blocks = units * (kb / rb);
+    const int occ = info.cus > 0 ? occupancy(kern, (int)(4 * d->V)) : 0;
+    const double cap = (double)occ * info.cus;
+    const double rounds = cap > 0 ? (double)((blocks + (long)cap - 1) / (long)cap) : 1.0;
+    if (rounds < best_rounds) {
+      best_rounds = rounds;
+      best = rb;
+    }
+    if (rounds <= 1.0) break;
+  }
+  return best;
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t fwd_partial_bytes(const m2rnn_dims* d, int rb) {
+  const long S = d->K / (16 * rb);
+  if (S <= 1) return 0;
+  return round_up((size_t)S * d->B * d->T * d->N * d->V * sizeof(float));
+}
+
+struct FwdCall {
+  const m2rnn_dims* d;
+  int qkv_dtype, math, row_blocks;
+  const void *q, *k, *v;
+  const float *f, *W, *w_r, *H0;
+  float *y, *H_T;
+  void* ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+
+// Validates a forward call; on success fills the resolved math mode and row blocks.
+int check_fwd(const FwdCall& c, int* math_out, int* rb_out) {
+  int st = check_dims(c.d, c.qkv_dtype);
+  if (st) return st;
+  const int math = resolve_math(c.math);
+  if (math < 0 || c.row_blocks < 0) return M2RNN_EINVAL;
+  const m2rnn_dims* d = c.d;
+  const bool empty = d->B == 0 || d->N == 0;
+  const bool bf16 = c.qkv_dtype == M2RNN_DTYPE_BF16;
+  if (!empty) {
+    if (!c.W || !c.w_r) return M2RNN_EINVAL;
+    if (d->T > 0 && (!c.q || !c.k || !c.v || !c.f || !c.y)) return M2RNN_EINVAL;
+    const void* ptrs[] = {c.q, c.k, c.v, c.W, c.w_r, c.H0, c.y, c.H_T};
+    for (const void* p : ptrs)
+      if (p && !aligned16(p)) return M2RNN_EINVAL;
+    if (c.f && ((uintptr_t)c.f & 3u)) return M2RNN_EINVAL;
+  }
+  const int rb = plan_row_blocks(d, math, bf16, MODE_FWD, c.row_blocks);
+  if (rb < 0) return c.row_blocks > 0 && (d->K / 16) % c.row_blocks != 0 ? M2RNN_EINVAL : M2RNN_EUNSUPPORTED;
+  const size_t need = empty ? 0 : fwd_partial_bytes(d, rb);
+  if (need > 0 && (!c.ws || c.ws_bytes < need || !aligned16(c.ws))) return M2RNN_EWORKSPACE;
+  *math_out = math;
+  *rb_out = rb;
+  return M2RNN_OK;
+}
+
+int launch_scan(const FwdCall& c, int math, int rb) {
+  const m2rnn_dims* d = c.d;
+  if (d->B == 0 || d->N == 0) return M2RNN_OK;
+  const bool bf16 = c.qkv_dtype == M2RNN_DTYPE_BF16;
+  const int S = (int)(d->K / (16 * rb));
+  if (d->T == 0) {
+    // Nothing to scan: H_T = H0 (or zeros).
+    if (!c.H_T) return M2RNN_OK;
+    const size_t bytes = (size_t)d->B * d->N * d->K * d->V * sizeof(float);
+    if (c.H0) return hip_status(hipMemcpyAsync(c.H_T, c.H0, bytes, hipMemcpyDeviceToDevice, c.stream));
+    return hip_status(hipMemsetAsync(c.H_T, 0, bytes, c.stream));
+  }
+  FwdArgs a{};
+  a.q = c.q; a.k = c.k; a.v = c.v; a.f = c.f; a.W = c.W; a.w_r = c.w_r; a.H0 = c.H0;
+  a.y = S > 1 ? (float*)c.ws : c.y;
+  a.H_T = c.H_T;
+  a.ckpt = nullptr;
+  a.B = (int)d->B; a.T = (int)d->T; a.N = (int)d->N; a.K = (int)d->K;
+  a.S = S;
+  a.seg = 0;
+  const void* kern = fwd_kernel(math, (int)d->V, rb, bf16, MODE_FWD);
+  if (!kern) return M2RNN_EUNSUPPORTED;
+  void* args[] = {&a};
+  const dim3 grid((unsigned)(d->B * d->N * S)), block((unsigned)(4 * d->V));
+  return hip_status(hipLaunchKernel(kern, grid, block, args, 0, c.stream));
+}
+
+int launch_finish(const FwdCall& c, int rb) {
+  const m2rnn_dims* d = c.d;
+  if (d->B == 0 || d->N == 0 || d->T == 0) return M2RNN_OK;
+  const int S = (int)(d->K / (16 * rb));
+  if (S <= 1) return M2RNN_OK;
+  const long plane = d->B * d->T * d->N * d->V;
+  const unsigned blocks = (unsigned)((plane / 4 + 255) / 256);
+  if (c.qkv_dtype == M2RNN_DTYPE_BF16)
+    hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<true>, dim3(blocks), dim3(256), 0, c.stream, (const float*)c.ws, S,
+                       plane, c.v, c.w_r, (int)d->N, (int)d->V, c.y);
+  else
+    hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<false>, dim3(blocks), dim3(256), 0, c.stream, (const float*)c.ws, S,
+                       plane, c.v, c.w_r, (int)d->N, (int)d->V, c.y);
+  return hip_status(hipGetLastError());
+}
+
+}  // namespace
+
+extern "C" {
+
+int m2rnn_version(void) { return 100; }
+
+const char* m2rnn_status_string(int status) {
+  switch (status) {
+    case M2RNN_OK: return "ok";
+    case M2RNN_EINVAL: return "invalid argument";
+    case M2RNN_EUNSUPPORTED: return "unsupported size or mode";
+    case M2RNN_EWORKSPACE: return "workspace missing or too small";
+    case M2RNN_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int m2rnn_last_hip_error(void) { return g_last_hip_error; }
+
+int m2rnn_fwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, size_t* bytes) {
+  if (!bytes) return M2RNN_EINVAL;
+  int st = check_dims(dims, qkv_dtype);
+  if (st) return st;
+  const int m = resolve_math(math);
+  if (m < 0 || row_blocks < 0) return M2RNN_EINVAL;
+  const int rb = plan_row_blocks(dims, m, qkv_dtype == M2RNN_DTYPE_BF16, MODE_FWD, row_blocks);
+  if (rb < 0) return row_blocks > 0 && (dims->K / 16) % row_blocks != 0 ? M2RNN_EINVAL : M2RNN_EUNSUPPORTED;
+  *bytes = (dims->B == 0 || dims->N == 0) ? 0 : fwd_partial_bytes(dims, rb);
+  return M2RNN_OK;
+}
+
+#define FWD_CALL                                                                                          \
+  FwdCall c{dims, qkv_dtype, math, row_blocks, q, k, v, f, W, w_r, H0, y, H_T, workspace, workspace_bytes, \
+            (hipStream_t)stream};                                                                         \
+  int m = 0, rb = 0;                                                                                      \
+  int st = check_fwd(c, &m, &rb);                                                                         \
+  if (st) return st;
+
+int m2rnn_scan_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q, const void* k,
+                   const void* v, const float* f, const float* W, const float* w_r, const float* H0, float* y,
+                   float* H_T, void* workspace, size_t workspace_bytes, void* stream) {
+  FWD_CALL
+  return launch_scan(c, m, rb);
+}
+
+int m2rnn_scan_fwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q,
+                          const void* k, const void* v, const float* f, const float* W, const float* w_r,
+                          const float* H0, float* y, float* H_T, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  FWD_CALL
+  return launch_finish(c, rb);
+}
+
+int m2rnn_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q, const void* k,
+              const void* v, const float* f, const float* W, const float* w_r, const float* H0, float* y, float* H_T,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  FWD_CALL
+  st = launch_scan(c, m, rb);
+  if (st) return st;
+  return launch_finish(c, rb);
+}
+
+}  // extern "C"

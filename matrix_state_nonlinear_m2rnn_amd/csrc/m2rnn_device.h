@@ -1,0 +1,116 @@
+// Device-side building blocks for the gfx950 M²RNN kernels: MFMA operand types, the
+// split-precision conversions, wave-level DPP reductions and an LDS-only workgroup barrier.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m2rnn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Contraction modes (values match the public M2RNN_MATH_* enum).
+enum { MATH_F32 = 0, MATH_F16X3 = 1, MATH_BF16X3 = 2, MATH_BF16 = 3 };
+
+// 2*log2(e): the kernels keep c*P instead of P so that exp(2P) is a single v_exp_f32 (2^x).
+constexpr float kTwoLog2e = 2.88539008177792681472f;
+
+// Workgroup barrier whose fences cover LDS only: it waits for this wave's LDS traffic
+// (lgkmcnt(0)) but not for its outstanding global loads/stores, so input prefetches and output
+// stores stay in flight across the per-step barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_amdgcn_update_dpp(0.0f, x, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15-i within each row of 16
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7-i within each half-row of 8
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+
+// Sums four per-lane values over the 16 lanes of each DPP row at once: on return, lane n of a
+// row holds sum_{lanes m of the row} x_{(n >> 2) & 3}(m).  Lanes xor 15 and xor 7 exchange the
+// halves that each keeps, then two quad swaps finish the sum (11 VALU ops for 4 row sums).
+__device__ __forceinline__ float row16_sum4(float x0, float x1, float x2, float x3, int lane) {
+  const bool b3 = (lane & 8) != 0;
+  const bool b2 = (lane & 4) != 0;
+  const float s0 = b3 ? x0 : x2, s1 = b3 ? x1 : x3;
+  const float k0 = b3 ? x2 : x0, k1 = b3 ? x3 : x1;
+  const float a0 = k0 + dpp<kDppRowMirror>(s0);
+  const float a1 = k1 + dpp<kDppRowMirror>(s1);
+  const float s = b2 ? a0 : a1, k = b2 ? a1 : a0;
+  float c = k + dpp<kDppRowHalfMirror>(s);
+  c += dpp<kDppQuadXor1>(c);
+  c += dpp<kDppQuadXor2>(c);
+  return c;
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 p;
+  p[0] = (__bf16)a;  // round to nearest even (v_cvt_pk_bf16_f32)
+  p[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, p);
+}
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  fp16x2 p;
+  p[0] = (__fp16)a;  // round to nearest even (v_cvt_pk_f16_f32)
+  p[1] = (__fp16)b;
+  return __builtin_bit_cast(uint32_t, p);
+}
+__device__ __forceinline__ float f16_lo_to_f32(uint32_t w) {
+  return (float)__builtin_bit_cast(fp16x2, w)[0];
+}
+__device__ __forceinline__ float f16_hi_to_f32(uint32_t w) {
+  return (float)__builtin_bit_cast(fp16x2, w)[1];
+}
+
+// Splits two fp32 values into (hi, lo) 16-bit pairs for the split-precision contraction.
+//   F16X3:  hi = fp16(x), lo = bf16(x - hi)  (x - hi is exact in fp32)
+//   BF16X3: hi = bf16(x), lo = bf16(x - hi)
+//   BF16:   hi = bf16(x), lo unused
+template <int MATH>
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  if constexpr (MATH == MATH_F16X3) {
+    hi = pack_f16(a, b);
+    lo = pack_bf16(a - f16_lo_to_f32(hi), b - f16_hi_to_f32(hi));
+  } else if constexpr (MATH == MATH_BF16X3) {
+    hi = pack_bf16(a, b);
+    lo = pack_bf16(a - bf16_lo_to_f32(hi), b - bf16_hi_to_f32(hi));
+  } else {
+    hi = pack_bf16(a, b);
+    lo = 0;
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+// tanh(x/c) from x = c*P, c = 2 log2 e:  tanh(P) = 1 - 2 / (1 + 2^x).  Returns r = 1/(1 + 2^x)
+// so that callers fold "1 - 2r" into the gate blend.  2^x overflowing to +inf gives r = 0
+// (tanh = 1); underflowing to 0 gives r = 1 (tanh = -1).
+__device__ __forceinline__ float tanh_recip(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
+}
+
+}  // namespace m2rnn

@@ -1,0 +1,6 @@
+// Forward scan kernels with the BF16 contraction.
+#include "m2rnn_select.h"
+
+namespace m2rnn {
+const void* fwd_kernel_bf16(int V, int rb, bool bf16, int mode) { return pick_fwd<MATH_BF16>(V, rb, bf16, mode); }
+}  // namespace m2rnn

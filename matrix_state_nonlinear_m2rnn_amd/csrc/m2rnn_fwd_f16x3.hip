@@ -1,0 +1,6 @@
+// Forward scan kernels with the F16X3 contraction.
+#include "m2rnn_select.h"
+
+namespace m2rnn {
+const void* fwd_kernel_f16x3(int V, int rb, bool bf16, int mode) { return pick_fwd<MATH_F16X3>(V, rb, bf16, mode); }
+}  // namespace m2rnn

@@ -1,0 +1,436 @@
+// Forward scan of the M²RNN recurrence (M²RNN notes §2.1, Eq. 10-12) for gfx950.
+//
+// Work decomposition
+//   One workgroup carries ROWS = 16*RB consecutive rows of the K x V state of one (b, n) pair;
+//   the rows of a state never mix (W acts on the value side only, §1.2), so a pair's K rows may
+//   be spread over S = K/ROWS workgroups.  Inside a workgroup, wave w (of V/16) owns the 16
+//   value columns [16w, 16w+16) of every row block: it computes those columns of
+//   P = H_{t-1} W + k v^T, applies tanh and the gate, and keeps the result in registers.
+//
+// Register layout (16x16 MFMA tiles, transposed)
+//   The kernel computes P^T = W^T H^T so that the accumulator of lane (g = lane/16, n = lane%16),
+//   register r holds P[row n][col 16w + 4g + r].  That is exactly the B-operand layout of the
+//   next step's MFMA (B[k][n] at lane (k-group, n)) once the contraction index k is permuted to
+//   v = 16*tile + 4g + r; the A operand W^T uses the same permutation.  So the state never needs
+//   a transpose: each step every wave publishes its 16-column tile to LDS (16 B per lane), one
+//   barrier, and every wave reads all V/16 tiles back as B operands.
+//
+// Per step, per wave: acc = (c k) v^T (VALU) ; acc += W'^T H^T (MFMA, c = 2 log2 e folded into W')
+//   ; r = 1/(1 + 2^acc) ; H = fma(-2(1-f), r, fma(f, H, 1-f))      [= f H + (1-f) tanh(P)]
+//   ; y partial = sum over the block's rows of H[row][col] q[row] (DPP row reduction).
+// q, k, v, f are staged through LDS in chunks of TC steps, double-buffered: chunk c+1 is read
+// from HBM into registers while chunk c is consumed.
+#pragma once
+
+#include "m2rnn_device.h"
+
+namespace m2rnn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* f;
+  const float* W;
+  const float* w_r;
+  const float* H0;
+  float* y;       // final readout (S == 1) or partial readouts [S][B*T*N*V] (S > 1)
+  float* H_T;     // may be null
+  float* ckpt;    // checkpoint mode: states entering each segment [B][N][nseg][K][V]
+  int B, T, N, K;
+  int S;          // workgroups per (b, n)
+  int seg;        // checkpoint interval (checkpoint mode)
+};
+
+template <int V>
+struct FwdShape {
+  static constexpr int NT = V / 16;          // value tiles = waves per workgroup
+  static constexpr int NTH = 64 * NT;        // threads per workgroup
+  static constexpr int TC = V >= 128 ? 16 : 32;  // steps per staged chunk
+};
+
+// Per-step stage record (fp32): [f, 1-f, -2(1-f), 0 | q rows | c*k rows | v (V)].
+template <int V, int RB>
+struct Stage {
+  static constexpr int ROWS = 16 * RB;
+  static constexpr int OQ = 4;
+  static constexpr int OK = 4 + ROWS;
+  static constexpr int OV = 4 + 2 * ROWS;
+  static constexpr int STEP = 4 + 2 * ROWS + V;  // floats, multiple of 4
+};
+
+// Copies of a TC x COLS tile of a [.., T, N, COLS_total] tensor into registers, 16 B at a time.
+template <int TC, int COLS, int NTH, bool BF16>
+struct TileLoader {
+  static constexpr int VEC = BF16 ? 8 : 4;  // elements per 16-byte load
+  static constexpr int PER_ROW = COLS / VEC;
+  static constexpr int NVEC = TC * PER_ROW;
+  static constexpr int PER = (NVEC + NTH - 1) / NTH;
+  uint4 r[PER];
+
+  __device__ __forceinline__ void load(const void* base, long row_stride_elems, int valid_rows, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NTH;
+      const int row = idx / PER_ROW, cv = idx % PER_ROW;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (idx < NVEC && row < valid_rows) {
+        const char* p = (const char*)base + ((long)row * row_stride_elems + cv * VEC) * (BF16 ? 2 : 4);
+        val = *(const uint4*)p;
+      }
+      r[i] = val;
+    }
+  }
+  // Writes the tile as fp32 into LDS rows of `row_pitch` floats starting at column `col0`,
+  // multiplied by `scale`.
+  __device__ __forceinline__ void store(float* lds, int row_pitch, int col0, float scale, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NTH;
+      if (idx < NVEC) {
+        const int row = idx / PER_ROW, cv = idx % PER_ROW;
+        float* d = lds + row * row_pitch + col0 + cv * VEC;
+        if constexpr (BF16) {
+          const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+          float4 a = make_float4(bf16_lo_to_f32(w[0]) * scale, bf16_hi_to_f32(w[0]) * scale,
+                                 bf16_lo_to_f32(w[1]) * scale, bf16_hi_to_f32(w[1]) * scale);
+          float4 b = make_float4(bf16_lo_to_f32(w[2]) * scale, bf16_hi_to_f32(w[2]) * scale,
+                                 bf16_lo_to_f32(w[3]) * scale, bf16_hi_to_f32(w[3]) * scale);
+          *(float4*)d = a;
+          *(float4*)(d + 4) = b;
+        } else {
+          *(float4*)d = make_float4(__uint_as_float(r[i].x) * scale, __uint_as_float(r[i].y) * scale,
+                                    __uint_as_float(r[i].z) * scale, __uint_as_float(r[i].w) * scale);
+        }
+      }
+    }
+  }
+};
+
+// Prefetch registers for one chunk of q, k, v, f.
+template <int V, int RB, bool BF16>
+struct ChunkRegs {
+  using S = FwdShape<V>;
+  static constexpr int ROWS = 16 * RB;
+  TileLoader<S::TC, ROWS, S::NTH, BF16> q, k;
+  TileLoader<S::TC, V, S::NTH, BF16> v;
+  float f;
+
+  __device__ __forceinline__ void load(const FwdArgs& a, int b, int nh, int row0, int t0, int tid) {
+    const int valid = min(S::TC, a.T - t0);
+    const long qk_off = (((long)b * a.T + t0) * a.N + nh) * a.K + row0;
+    const long v_off = (((long)b * a.T + t0) * a.N + nh) * V;
+    const int esz = BF16 ? 2 : 4;
+    q.load((const char*)a.q + qk_off * esz, (long)a.N * a.K, valid, tid);
+    k.load((const char*)a.k + qk_off * esz, (long)a.N * a.K, valid, tid);
+    v.load((const char*)a.v + v_off * esz, (long)a.N * V, valid, tid);
+    f = 1.0f;
+    if (tid < valid) f = a.f[((long)b * a.T + t0 + tid) * a.N + nh];
+  }
+  __device__ __forceinline__ void store(float* stage, int tid) const {
+    using St = Stage<V, RB>;
+    q.store(stage, St::STEP, St::OQ, 1.0f, tid);
+    k.store(stage, St::STEP, St::OK, kTwoLog2e, tid);
+    v.store(stage, St::STEP, St::OV, 1.0f, tid);
+    if (tid < S::TC) {
+      const float g = 1.0f - f;
+      *(float4*)(stage + tid * St::STEP) = make_float4(f, g, -2.0f * g, 0.0f);
+    }
+  }
+};
+
+// MODE_FWD: full forward with readout.  MODE_CKPT: state only, storing the state that enters
+// every `seg`-step segment (used by the backward pass).
+enum { MODE_FWD = 0, MODE_CKPT = 1 };
+
+template <int V, int RB, int MATH, bool BF16IN, int MODE>
+__global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const FwdArgs a) {
+  using Sh = FwdShape<V>;
+  using St = Stage<V, RB>;
+  constexpr int NT = Sh::NT;
+  constexpr int TC = Sh::TC;
+  constexpr int ROWS = 16 * RB;
+  constexpr bool SPLIT = MATH != MATH_F32;
+  constexpr int NCH = (NT + 1) / 2;  // 32-wide contraction chunks of the split modes
+
+  __shared__ __attribute__((aligned(16))) float stage[2][TC * St::STEP];
+  // Exchange buffer of the state tiles, double-buffered by step parity.
+  //   F32:   [2][RB][NT][64 lanes][4 floats]
+  //   split: [2][RB][NCH][hi|lo][64 lanes][4 dwords]; wave w fills dwords 2(w&1), 2(w&1)+1
+  //          of chunk w/2, so one 16-byte read yields the 8 contraction values of a chunk.
+  constexpr int XWORDS = SPLIT ? (RB * NCH * 2 * 64 * 4) : (RB * NT * 64 * 4);
+  __shared__ __attribute__((aligned(16))) uint32_t xbuf[2][XWORDS];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+
+  // Block -> (pair u, row group s).  When the pair count is a multiple of 8, the S workgroups
+  // of one pair get block ids congruent mod 8, which the dispatcher places on the same XCD, so
+  // they share that XCD's L2 for q, k, v, f.
+  const int U = a.B * a.N;
+  int u, s;
+  if ((U & 7) == 0 && a.S > 1) {
+    const int slot = blockIdx.x >> 3;
+    s = slot % a.S;
+    u = (slot / a.S) * 8 + (blockIdx.x & 7);
+  } else {
+    u = blockIdx.x / a.S;
+    s = blockIdx.x % a.S;
+  }
+  const int b = u / a.N;
+  const int nh = u % a.N;
+  const int row0 = s * ROWS;
+  const long KV = (long)a.K * V;
+
+  // ---- W operands (A = W'^T with the permuted contraction index), W' = c W ----
+  const float* Wn = a.W + (long)nh * V * V;
+  const int col = 16 * w + n;  // output column of A-operand row m = n
+  float wA[SPLIT ? 1 : NT * 4];
+  uint4 wHi[SPLIT ? NCH : 1], wLo[SPLIT ? NCH : 1], wBf[SPLIT ? NCH : 1];
+  if constexpr (!SPLIT) {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wA[tt * 4 + r] = kTwoLog2e * Wn[(16 * tt + 4 * g + r) * V + col];
+  } else {
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+      float wv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int tile = 2 * cc + (i >> 2);
+        const int vin = 16 * tile + 4 * g + (i & 3);
+        wv[i] = tile < NT ? kTwoLog2e * Wn[vin * V + col] : 0.0f;
+      }
+      uint32_t h[4], l[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = wv[2 * i], x1 = wv[2 * i + 1];
+        if constexpr (MATH == MATH_F16X3) {
+          h[i] = pack_f16(x0, x1);
+          l[i] = pack_f16(x0 - f16_lo_to_f32(h[i]), x1 - f16_hi_to_f32(h[i]));
+          bf[i] = pack_bf16(x0, x1);
+        } else {
+          h[i] = pack_bf16(x0, x1);
+          l[i] = pack_bf16(x0 - bf16_lo_to_f32(h[i]), x1 - bf16_hi_to_f32(h[i]));
+          bf[i] = h[i];
+        }
+      }
+      wHi[cc] = make_uint4(h[0], h[1], h[2], h[3]);
+      wLo[cc] = make_uint4(l[0], l[1], l[2], l[3]);
+      wBf[cc] = make_uint4(bf[0], bf[1], bf[2], bf[3]);
+    }
+  }
+
+  // ---- initial state ----
+  float H[RB][4];
+  const long state_base = ((long)b * a.N + nh) * KV;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const long off = state_base + (long)(row0 + 16 * rb + n) * V + 16 * w + 4 * g;
+    if (a.H0) {
+      const float4 h = *(const float4*)(a.H0 + off);
+      H[rb][0] = h.x; H[rb][1] = h.y; H[rb][2] = h.z; H[rb][3] = h.w;
+    } else {
+      H[rb][0] = H[rb][1] = H[rb][2] = H[rb][3] = 0.0f;
+    }
+  }
+
+  // Publishes this wave's tile of H into exchange buffer `buf`.
+  auto publish = [&](int buf) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if constexpr (!SPLIT) {
+        *(float4*)&xbuf[buf][((rb * NT + w) * 64 + lane) * 4] = make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
+      } else {
+        uint32_t h01, h23, l01, l23;
+        split2<MATH>(H[rb][0], H[rb][1], h01, l01);
+        split2<MATH>(H[rb][2], H[rb][3], h23, l23);
+        const int base = ((rb * NCH + (w >> 1)) * 2) * 64 * 4 + lane * 4 + 2 * (w & 1);
+        *(uint2*)&xbuf[buf][base] = make_uint2(h01, h23);
+        if constexpr (MATH != MATH_BF16) *(uint2*)&xbuf[buf][base + 64 * 4] = make_uint2(l01, l23);
+      }
+    }
+  };
+
+  // Odd tile counts leave half of the last chunk unwritten: zero both buffers once.
+  if constexpr (SPLIT && (NT & 1)) {
+    for (int i = tid; i < 2 * XWORDS; i += Sh::NTH) (&xbuf[0][0])[i] = 0u;
+    lds_barrier();
+  }
+
+  // Readout bookkeeping: after the row reduction, lane (g, n) holds column 16w + 4g + (n >> 2);
+  // lanes with n % 4 == 0 store it.  (w_r is read before chunk 0 so that the wait for chunk 0
+  // covers it and no wait is left inside the step loop.)
+  const int ycol = 16 * w + 4 * g + (n >> 2);
+  const bool ystore = (n & 3) == 0;
+  const float wr = (MODE == MODE_FWD && a.S == 1) ? a.w_r[(long)nh * V + ycol] : 0.0f;
+
+  // ---- stage chunk 0, prefetch chunk 1 ----
+  ChunkRegs<V, RB, BF16IN> pre;
+  pre.load(a, b, nh, row0, 0, tid);
+  pre.store(stage[0], tid);
+  if (a.T > TC) pre.load(a, b, nh, row0, TC, tid);
+  publish(0);
+
+  float* ydst = nullptr;
+  if constexpr (MODE == MODE_FWD) {
+    const long plane = (long)a.B * a.T * a.N * V;
+    ydst = a.y + (a.S > 1 ? (long)s * plane : 0) + ((long)b * a.T * a.N + nh) * V + ycol;
+  }
+  const long ystep = (long)a.N * V;
+  const int nseg = MODE == MODE_CKPT ? (a.T + a.seg - 1) / a.seg : 0;
+
+  lds_barrier();
+
+  int j = 0, cb = 0;
+  for (int t = 0; t < a.T; ++t) {
+    if constexpr (MODE == MODE_CKPT) {
+      if (t % a.seg == 0) {
+        float* dst = a.ckpt + ((long)(b * a.N + nh) * nseg + t / a.seg) * KV;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          *(float4*)(dst + (long)(row0 + 16 * rb + n) * V + 16 * w + 4 * g) =
+              make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
+      }
+    }
+    const float* st = stage[cb] + j * St::STEP;
+    const float4 fg = *(const float4*)st;  // f, 1-f, -2(1-f)
+    const float4 vv = *(const float4*)(st + St::OV + 16 * w + 4 * g);
+    float qn[RB], kn[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      qn[rb] = st[St::OQ + 16 * rb + n];
+      kn[rb] = st[St::OK + 16 * rb + n];
+    }
+    const uint32_t* xr = xbuf[t & 1];
+
+    f32x4 acc[RB];
+    f32x4 acc2[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      acc[rb][0] = kn[rb] * vv.x;
+      acc[rb][1] = kn[rb] * vv.y;
+      acc[rb][2] = kn[rb] * vv.z;
+      acc[rb][3] = kn[rb] * vv.w;
+      acc2[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    if constexpr (!SPLIT) {
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const float4 hb = *(const float4*)&xr[((rb * NT + tt) * 64 + lane) * 4];
+          acc[rb] = mfma_f32(wA[tt * 4 + 0], hb.x, acc[rb]);
+          acc[rb] = mfma_f32(wA[tt * 4 + 1], hb.y, acc[rb]);
+          acc[rb] = mfma_f32(wA[tt * 4 + 2], hb.z, acc[rb]);
+          acc[rb] = mfma_f32(wA[tt * 4 + 3], hb.w, acc[rb]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int base = ((rb * NCH + cc) * 2) * 64 * 4 + lane * 4;
+          const uint4 bh = *(const uint4*)&xr[base];
+          if constexpr (MATH == MATH_F16X3) {
+            const uint4 bl = *(const uint4*)&xr[base + 64 * 4];
+            acc[rb] = mfma_f16(wHi[cc], bh, acc[rb]);
+            acc2[rb] = mfma_f16(wLo[cc], bh, acc2[rb]);
+            acc2[rb] = mfma_bf16(wBf[cc], bl, acc2[rb]);
+          } else if constexpr (MATH == MATH_BF16X3) {
+            const uint4 bl = *(const uint4*)&xr[base + 64 * 4];
+            acc[rb] = mfma_bf16(wHi[cc], bh, acc[rb]);
+            acc2[rb] = mfma_bf16(wLo[cc], bh, acc2[rb]);
+            acc2[rb] = mfma_bf16(wHi[cc], bl, acc2[rb]);
+          } else {
+            acc[rb] = mfma_bf16(wHi[cc], bh, acc[rb]);
+          }
+        }
+      }
+    }
+
+    // tanh + gate blend: H = f H + (1-f)(1 - 2r) = fma(-2(1-f), r, fma(f, H, 1-f)).
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = acc[rb][r];
+        if constexpr (SPLIT && MATH != MATH_BF16) x += acc2[rb][r];
+        const float rr = tanh_recip(x);
+        H[rb][r] = __builtin_fmaf(fg.z, rr, __builtin_fmaf(fg.x, H[rb][r], fg.y));
+      }
+    }
+    publish((t + 1) & 1);
+
+    if constexpr (MODE == MODE_FWD) {
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float sacc = H[0][r] * qn[0];
+#pragma unroll
+        for (int rb = 1; rb < RB; ++rb) sacc = __builtin_fmaf(H[rb][r], qn[rb], sacc);
+        x[r] = sacc;
+      }
+      // w_r (.) v is added here when this workgroup holds all K rows (wr = 0 otherwise).
+      const float yv = __builtin_fmaf(wr, st[St::OV + ycol], row16_sum4(x[0], x[1], x[2], x[3], lane));
+      if (ystore) ydst[(long)t * ystep] = yv;
+    }
+
+    const bool last_in_chunk = (j == TC - 1);
+    if (last_in_chunk) pre.store(stage[cb ^ 1], tid);
+    lds_barrier();
+    if (last_in_chunk) {
+      const int t_next = t + 1 + TC;  // first step of the chunk after the one just staged
+      if (t_next < a.T) pre.load(a, b, nh, row0, t_next, tid);
+      j = 0;
+      cb ^= 1;
+    } else {
+      ++j;
+    }
+  }
+
+  if (a.H_T) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      *(float4*)(a.H_T + state_base + (long)(row0 + 16 * rb + n) * V + 16 * w + 4 * g) =
+          make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
+  }
+}
+
+// y = sum_s partial_s + w_r (.) v, elementwise over [B,T,N,V] (4 elements per thread).
+template <bool BF16IN>
+__global__ void __launch_bounds__(256) m2rnn_fwd_finish_kernel(const float* __restrict__ part, int S,
+                                                                long plane, const void* __restrict__ v,
+                                                                const float* __restrict__ w_r, int N, int V,
+                                                                float* __restrict__ y) {
+  const long i4 = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long i = i4 * 4;
+  if (i >= plane) return;
+  float4 acc = *(const float4*)(part + i);
+  for (int s = 1; s < S; ++s) {
+    const float4 p = *(const float4*)(part + (long)s * plane + i);
+    acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+  }
+  const int colv = (int)(i % V);
+  const int nh = (int)((i / V) % N);
+  const float4 wr = *(const float4*)(w_r + (long)nh * V + colv);
+  float4 vv;
+  if constexpr (BF16IN) {
+    const uint2 raw = *(const uint2*)((const char*)v + i * 2);
+    vv = make_float4(bf16_lo_to_f32(raw.x), bf16_hi_to_f32(raw.x), bf16_lo_to_f32(raw.y), bf16_hi_to_f32(raw.y));
+  } else {
+    vv = *(const float4*)((const float*)v + i);
+  }
+  acc.x = __builtin_fmaf(wr.x, vv.x, acc.x);
+  acc.y = __builtin_fmaf(wr.y, vv.y, acc.y);
+  acc.z = __builtin_fmaf(wr.z, vv.z, acc.z);
+  acc.w = __builtin_fmaf(wr.w, vv.w, acc.w);
+  *(float4*)(y + i) = acc;
+}
+
+}  // namespace m2rnn

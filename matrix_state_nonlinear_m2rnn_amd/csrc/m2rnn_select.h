@@ -1,0 +1,49 @@
+// Kernel selection: each contraction mode is compiled in its own translation unit, which
+// exports one function mapping (V, RB, input dtype, mode) to the kernel's host stub.
+#pragma once
+
+#include "m2rnn_fwd_kernel.h"
+
+namespace m2rnn {
+
+template <int MATH, int V, int RB>
+const void* pick_fwd_vrb(bool bf16, int mode) {
+  if (mode == MODE_FWD)
+    return bf16 ? (const void*)&m2rnn_scan_fwd_kernel<V, RB, MATH, true, MODE_FWD>
+                : (const void*)&m2rnn_scan_fwd_kernel<V, RB, MATH, false, MODE_FWD>;
+  if constexpr (MATH == MATH_F32 || MATH == MATH_F16X3) {
+    if (mode == MODE_CKPT)
+      return bf16 ? (const void*)&m2rnn_scan_fwd_kernel<V, RB, MATH, true, MODE_CKPT>
+                  : (const void*)&m2rnn_scan_fwd_kernel<V, RB, MATH, false, MODE_CKPT>;
+  }
+  return nullptr;
+}
+
+template <int MATH, int V>
+const void* pick_fwd_v(int rb, bool bf16, int mode) {
+  switch (rb) {
+    case 1: return pick_fwd_vrb<MATH, V, 1>(bf16, mode);
+    case 2: return pick_fwd_vrb<MATH, V, 2>(bf16, mode);
+    case 4: return pick_fwd_vrb<MATH, V, 4>(bf16, mode);
+    default: return nullptr;
+  }
+}
+
+template <int MATH>
+const void* pick_fwd(int V, int rb, bool bf16, int mode) {
+  switch (V) {
+    case 16: return pick_fwd_v<MATH, 16>(rb, bf16, mode);
+    case 32: return pick_fwd_v<MATH, 32>(rb, bf16, mode);
+    case 64: return pick_fwd_v<MATH, 64>(rb, bf16, mode);
+    case 128: return pick_fwd_v<MATH, 128>(rb, bf16, mode);
+    default: return nullptr;
+  }
+}
+
+// One per contraction mode (defined in m2rnn_fwd_<mode>.hip).
+const void* fwd_kernel_f32(int V, int rb, bool bf16, int mode);
+const void* fwd_kernel_f16x3(int V, int rb, bool bf16, int mode);
+const void* fwd_kernel_bf16x3(int V, int rb, bool bf16, int mode);
+const void* fwd_kernel_bf16(int V, int rb, bool bf16, int mode);
+
+}  // namespace m2rnn

@@ -27,7 +27,9 @@ Value distributions (``N(mu, s2)`` names the *variance* s2)
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import Dict, Optional
 
 import numpy as np
@@ -36,7 +38,7 @@ _GAMMA = 0x9E3779B97F4A7C15
 _M1 = 0xBF58476D1CE4E5B9
 _M2 = 0x94D049BB133111EB
 _MASK64 = (1 << 64) - 1
-_BLOCK = 1 << 22  # draws per vectorised block (bounds the temporaries to ~100 MB)
+_BLOCK = 1 << 21  # draws per vectorised block (bounds each thread's temporaries to ~50 MB)
 
 TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "f": 4, "W": 5, "w_r": 6, "H0": 7, "dy": 8, "dH_T": 9}
 BASE_SEED = 0x4D32524E
@@ -74,12 +76,23 @@ def uniform01(key: int, start: int, count: int) -> np.ndarray:
     return ((x >> np.uint64(11)).astype(np.float64) + 0.5) * (2.0 ** -53)
 
 
+def _threads() -> int:
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:  # pragma: no cover
+        return max(1, min(16, os.cpu_count() or 1))
+
+
 def normal(key: int, count: int, mean: float = 0.0, var: float = 1.0) -> np.ndarray:
-    """``count`` fp64 normals N(mean, var) from stream ``key`` (Box–Muller on uniform pairs)."""
+    """``count`` fp64 normals N(mean, var) from stream ``key`` (Box–Muller on uniform pairs).
+
+    The stream is counter-based, so blocks are drawn in parallel threads; the result does not
+    depend on the thread count."""
     out = np.empty(count, dtype=np.float64)
     npairs = (count + 1) // 2
     sd = float(np.sqrt(var))
-    for p0 in range(0, npairs, _BLOCK // 2):
+
+    def block(p0: int) -> None:
         p = min(_BLOCK // 2, npairs - p0)
         u = uniform01(key, 2 * p0, 2 * p)
         u1, u2 = u[0::2], u[1::2]
@@ -91,15 +104,27 @@ def normal(key: int, count: int, mean: float = 0.0, var: float = 1.0) -> np.ndar
         lo = 2 * p0
         hi = min(count, lo + 2 * p)
         out[lo:hi] = z[: hi - lo] * sd + mean
+
+    starts = list(range(0, npairs, _BLOCK // 2))
+    if len(starts) <= 1:
+        for p0 in starts:
+            block(p0)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=_threads()) as ex:
+            list(ex.map(block, starts))
     return out
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """fp32 -> nearest bf16 (ties to even), returned as fp32 holding the bf16 value."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    bits = (bits + np.uint64(0x7FFF) + ((bits >> np.uint64(16)) & np.uint64(1))) & np.uint64(0xFFFF0000)
-    return bits.astype(np.uint32).view(np.float32)
+    bits = x.view(np.uint32)
+    # No carry leaves 32 bits for finite inputs (largest: 0xFF7FFFFF + 0x8000).
+    out = (bits >> np.uint32(16)) & np.uint32(1)
+    out += np.uint32(0x7FFF)
+    out += bits
+    out &= np.uint32(0xFFFF0000)
+    return out.view(np.float32)
 
 
 def haar_orthogonal(g: np.ndarray) -> np.ndarray:

@@ -1,0 +1,65 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that include/m2rnn.h
+declares, and rejects invalid calls with the documented status before enqueuing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import matrix_state_nonlinear_m2rnn_amd as m2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "m2rnn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(m2rnn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    L = m2.lib()
+    names = declared_functions()
+    assert "m2rnn_fwd" in names and "m2rnn_bwd" in names
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(m2.EXPORTED)
+
+
+def test_version_and_status_strings():
+    assert m2.lib().m2rnn_version() >= 100
+    assert m2.status_string(0) == "ok"
+    assert "workspace" in m2.status_string(m2.M2RNN_EWORKSPACE)
+
+
+def fwd(dims, dtype=0, math=-1, rb=0, ptr=16, ws=None, nbytes=0, y=True, q=True, f=True):
+    L = m2.lib()
+    p = ctypes.c_void_p(ptr)
+    return L.m2rnn_fwd(ctypes.byref(dims) if dims is not None else None, dtype, math, rb, p if q else None, p, p,
+                       p if f else None, p, p, None, p if y else None, None, ws, nbytes, None)
+
+
+def test_invalid_arguments_are_rejected_on_the_host():
+    D = m2.Dims
+    assert fwd(None) == m2.M2RNN_EINVAL
+    assert fwd(D(-1, 4, 2, 16, 16)) == m2.M2RNN_EINVAL
+    assert fwd(D(1, 4, 2, 16, 16), dtype=7) == m2.M2RNN_EINVAL
+    assert fwd(D(1, 4, 2, 16, 16), math=9) == m2.M2RNN_EINVAL
+    assert fwd(D(1, 4, 2, 16, 48)) == m2.M2RNN_EUNSUPPORTED      # V not in {16,32,64,128}
+    assert fwd(D(1, 4, 2, 24, 16)) == m2.M2RNN_EUNSUPPORTED      # K not a multiple of 16
+    assert fwd(D(1, 4, 2, 16, 16), y=False) == m2.M2RNN_EINVAL    # missing output
+    assert fwd(D(1, 4, 2, 16, 16), q=False) == m2.M2RNN_EINVAL
+    assert fwd(D(1, 4, 2, 16, 16), f=False) == m2.M2RNN_EINVAL
+    assert fwd(D(1, 4, 2, 16, 16), ptr=18) == m2.M2RNN_EINVAL     # misaligned
+    assert fwd(D(1, 4, 2, 48, 16), rb=2) == m2.M2RNN_EINVAL       # rb must divide K/16
+    # K = 64 with one 16-row block per workgroup splits each state over 4 workgroups: the partial
+    # readouts need a workspace.
+    assert fwd(D(1, 4, 2, 64, 16), rb=1) == m2.M2RNN_EWORKSPACE
+
+
+def test_workspace_size_query():
+    n = m2.m2rnn_fwd_workspace_size(m2.Dims(2, 10, 3, 64, 32), 1, "f16x3", 1)
+    assert n >= 4 * 2 * 10 * 3 * 32 * 4
+    assert m2.m2rnn_fwd_workspace_size(m2.Dims(2, 10, 3, 64, 32), 1, "f16x3", 4) == 0
+    with pytest.raises(m2.M2RNNError):
+        m2.m2rnn_fwd_workspace_size(m2.Dims(2, 10, 3, 64, 40), 1, "f16x3", 0)

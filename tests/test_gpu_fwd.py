@@ -1,0 +1,138 @@
+"""GPU parity of the forward scan (HIP path through the C ABI) against the fp64 oracle.
+
+Tolerances are the stated budgets: max-abs <= 5e-4 on y and H_T when the state is fp32 (f32,
+f16x3 and bf16x3 contractions) and <= 2e-2 for the single-pass bf16 contraction.
+"""
+import numpy as np
+import pytest
+
+from matrix_state_nonlinear_m2rnn_amd import inputs
+
+from _gpu import TOL, gpu_fwd, max_abs, oracle_fwd, oracle_units, say, to_device, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+MATHS = ["f32", "f16x3", "bf16x3", "bf16"]
+
+
+@pytest.mark.parametrize("math", MATHS)
+def test_tiny_f32_workload(math):
+    torch_cuda()
+    d = inputs.workload_inputs("tiny_f32")
+    say("tiny_f32", math)
+    y, H = gpu_fwd(to_device(d, "f32"), math)
+    yr, Hr = oracle_fwd(d)
+    assert max_abs(y, yr) <= TOL[math] and max_abs(H, Hr) <= TOL[math], (max_abs(y, yr), max_abs(H, Hr))
+    assert np.all(np.abs(H) <= 1.0 + 1e-6)
+
+
+@pytest.mark.parametrize("math", MATHS)
+def test_b4_h16_t2048_kv64_full(math):
+    torch_cuda()
+    d = inputs.workload_inputs("b4_h16_t2048_kv64")
+    say("b4_h16_t2048_kv64", math)
+    y, H = gpu_fwd(to_device(d, "bf16"), math)
+    yr, Hr = oracle_fwd(d)
+    ey, eh = max_abs(y, yr), max_abs(H, Hr)
+    say("errors", ey, eh)
+    assert ey <= TOL[math] and eh <= TOL[math], (ey, eh)
+
+
+@pytest.mark.parametrize("name,units,math", [
+    ("long_b2_h32_t16384_kv64", [(0, 0), (1, 31), (0, 17), (1, 5)], "f16x3"),
+    ("long_b2_h32_t16384_kv64", [(0, 3), (1, 20)], "f32"),
+    ("b8_h16_t4096_kv128", [(0, 0), (7, 15)], "f16x3"),
+    ("b1_h16_t4096_kv128", [(0, 0), (0, 9)], "f16x3"),
+])
+def test_full_size_sampled_units(name, units, math):
+    # Full-size launch exactly as the benchmark runs it; the oracle re-computes sampled units.
+    torch_cuda()
+    w = inputs.WORKLOADS[name]
+    d = inputs.workload_inputs(name)
+    say(name, math, "units", units)
+    y, H = gpu_fwd(to_device(d, w.qkv_dtype), math)
+    assert np.all(np.abs(H) <= 1.0 + 1e-6)
+    assert np.isfinite(y).all()
+    ref = oracle_units(d, units)
+    for (b, n), (yr, Hr) in ref.items():
+        ey, eh = max_abs(y[b, :, n], yr), max_abs(H[b, n], Hr)
+        say((b, n), ey, eh)
+        assert ey <= TOL[math] and eh <= TOL[math], ((b, n), ey, eh)
+
+
+@pytest.mark.parametrize("K,V", [(16, 16), (32, 32), (48, 64), (64, 32), (16, 128), (128, 64)])
+@pytest.mark.parametrize("T", [1, 31, 33, 70])
+def test_shapes_and_ragged_steps(K, V, T):
+    torch_cuda()
+    d = inputs.make_inputs(2, T, 3, K, V, qkv_dtype="bf16", seed=1000 + K + V + T, with_H0=True)
+    dd = to_device(d, "bf16")
+    yr, Hr = oracle_fwd(d)
+    for math in ("f32", "f16x3"):
+        say("shape", K, V, T, math)
+        y, H = gpu_fwd(dd, math)
+        assert max_abs(y, yr) <= TOL[math] and max_abs(H, Hr) <= TOL[math], (math, max_abs(y, yr), max_abs(H, Hr))
+
+
+@pytest.mark.parametrize("rb", [1, 2, 4])
+def test_row_split_matches(rb):
+    # The rows of one state may be spread over K/(16*rb) workgroups; all splits agree.
+    torch_cuda()
+    d = inputs.make_inputs(2, 100, 2, 64, 64, qkv_dtype="bf16", seed=77)
+    dd = to_device(d, "bf16")
+    say("row_blocks", rb)
+    y, H = gpu_fwd(dd, "f16x3", row_blocks=rb)
+    y1, H1 = gpu_fwd(dd, "f16x3", row_blocks=4)
+    assert np.array_equal(H, H1)  # rows evolve identically whatever the split
+    assert max_abs(y, y1) <= 1e-5
+    yr, Hr = oracle_fwd(d)
+    assert max_abs(y, yr) <= 5e-4 and max_abs(H, Hr) <= 5e-4
+
+
+def test_hold_when_f_is_one_is_bit_exact():
+    torch_cuda()
+    d = inputs.make_inputs(2, 40, 2, 32, 64, qkv_dtype="f32", seed=5, with_H0=True)
+    d["f"][:] = 1.0
+    dd = to_device(d, "f32")
+    for math in ("f32", "f16x3"):
+        say("hold", math)
+        y, H = gpu_fwd(dd, math)
+        assert np.array_equal(H, d["H0"].astype(np.float64))
+        yr, _ = oracle_fwd(d)
+        assert max_abs(y, yr) <= 1e-5
+
+
+def test_zero_steps_and_empty_batch():
+    torch = torch_cuda()
+    d = inputs.make_inputs(2, 0, 2, 16, 16, qkv_dtype="f32", seed=6, with_H0=True)
+    dd = to_device(d, "f32")
+    y, H = gpu_fwd(dd, "f16x3")
+    assert y.shape == (2, 0, 2, 16) and np.array_equal(H, d["H0"].astype(np.float64))
+    d = inputs.make_inputs(2, 0, 2, 16, 16, qkv_dtype="f32", seed=6)
+    y, H = gpu_fwd(to_device(d, "f32"), "f16x3")
+    assert np.all(H == 0.0)
+    d = inputs.make_inputs(0, 5, 2, 16, 16, qkv_dtype="f32", seed=6)
+    y, H = gpu_fwd(to_device(d, "f32"), "f16x3")
+    assert y.shape == (0, 5, 2, 16)
+    torch.cuda.synchronize()
+
+
+def test_deterministic_across_runs():
+    torch_cuda()
+    d = inputs.make_inputs(2, 300, 4, 64, 64, qkv_dtype="bf16", seed=8)
+    dd = to_device(d, "bf16")
+    for math in ("f32", "f16x3"):
+        y1, H1 = gpu_fwd(dd, math)
+        y2, H2 = gpu_fwd(dd, math)
+        assert np.array_equal(y1, y2) and np.array_equal(H1, H2)
+
+
+def test_state_bound_under_saturation():
+    torch_cuda()
+    d = inputs.make_inputs(1, 200, 2, 64, 64, qkv_dtype="f32", seed=9)
+    d["k"] *= 20.0
+    d["v"] *= 20.0
+    d["f"][:, ::4] = 0.0
+    y, H = gpu_fwd(to_device(d, "f32"), "f16x3")
+    assert np.all(np.abs(H) <= 1.0 + 1e-6)
+    yr, Hr = oracle_fwd(d)
+    assert max_abs(H, Hr) <= 5e-4
