@@ -26,8 +26,9 @@ SOURCES = [
 ]
 
 # Packed fp32 VALU ops stay off: hipcc -O3 would otherwise form v_pk_{add,mul,fma}_f32.
+# MFMA results stay in ordinary VGPRs (no accumulation-register copies in the step loop).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-         "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+         "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-unused-command-line-argument"]
 
 
 def hipcc() -> str:

@@ -46,7 +46,7 @@ template <int V>
 struct FwdShape {
   static constexpr int NT = V / 16;          // value tiles = waves per workgroup
   static constexpr int NTH = 64 * NT;        // threads per workgroup
-  static constexpr int TC = V >= 128 ? 16 : 32;  // steps per staged chunk
+  static constexpr int TC = 16;              // steps per staged chunk (the step loop is unrolled per chunk)
 };
 
 // Per-step stage record (fp32): [f, 1-f, -2(1-f), 0 | q rows | c*k rows | v (V)].
@@ -139,6 +139,78 @@ struct ChunkRegs {
   }
 };
 
+// Per-step inputs a lane needs, read from the stage ring one step ahead.
+template <int RB, bool SPLIT>
+struct StepIn {
+  float f, g, m2g;             // f, 1-f, -2(1-f)
+  float av;                    // A operand of the rank-1 MFMA: v[16w + n] on lanes with g == 0, else 0
+  float bk[RB];                // B operand of the rank-1 MFMA: c*k[row] on lanes with g == 0, else 0
+  float4 q4[SPLIT ? RB : 1];   // split modes: q of rows 16rb + 4g .. 16rb + 4g + 3
+  float qn[SPLIT ? 1 : RB];    // f32 mode:    q of row 16rb + n
+  float vcol;                  // v[ycol] for the w_r (.) v readout term
+};
+
+// Lane-constant offsets (in floats) into one stage record.
+template <int RB>
+struct StepOffsets {
+  int av;
+  int bk[RB];
+  int q;
+  int vcol;
+};
+
+template <int V, int RB, bool SPLIT>
+__device__ __forceinline__ StepIn<RB, SPLIT> read_step(const float* st, const StepOffsets<RB>& o) {
+  using Sg = Stage<V, RB>;
+  StepIn<RB, SPLIT> s;
+  const float4 fg = *(const float4*)st;
+  s.f = fg.x;
+  s.g = fg.y;
+  s.m2g = fg.z;
+  s.av = st[o.av];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) s.bk[rb] = st[o.bk[rb]];
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s.q4[rb] = *(const float4*)(st + o.q + 16 * rb);
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s.qn[rb] = st[o.q + 16 * rb];
+  }
+  s.vcol = st[o.vcol];
+  return s;
+}
+
+// Splits (a, b) into packed 16-bit high parts and the packed 16-bit rounding remainders.
+//   F16X3:  hi = fp16(x) (RNE), lo = fp16(x - hi) computed by v_fma_mix in fp32 (x - hi is exact).
+//   BF16X3: hi = bf16(x), lo = bf16(x - hi).
+//   BF16:   hi = bf16(x), lo = 0.
+template <int MATH>
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  if constexpr (MATH == MATH_F16X3) {
+    hi = pack_f16(a, b);
+    uint32_t l;
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l) : "v"(hi), "v"(a));
+    asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(l) : "v"(hi), "v"(b));
+    lo = l;
+  } else if constexpr (MATH == MATH_BF16X3) {
+    hi = pack_bf16(a, b);
+    lo = pack_bf16(a - bf16_lo_to_f32(hi), b - bf16_hi_to_f32(hi));
+  } else {
+    hi = pack_bf16(a, b);
+    lo = 0;
+  }
+}
+
+// Sum over the four 16-lane rows of the wave (lanes j, j+16, j+32, j+48) with the gfx950
+// row-swap permutes; every lane ends with the total of its column j.
+__device__ __forceinline__ float sum_rows4(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto p2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(p2[0]) + __uint_as_float(p2[1]);
+}
+
 // MODE_FWD: full forward with readout.  MODE_CKPT: state only, storing the state that enters
 // every `seg`-step segment (used by the backward pass).
 enum { MODE_FWD = 0, MODE_CKPT = 1 };
@@ -152,6 +224,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   constexpr int ROWS = 16 * RB;
   constexpr bool SPLIT = MATH != MATH_F32;
   constexpr int NCH = (NT + 1) / 2;  // 32-wide contraction chunks of the split modes
+  static_assert(TC % 2 == 0, "the exchange-buffer parity is derived from the step index within a chunk");
 
   __shared__ __attribute__((aligned(16))) float stage[2][TC * St::STEP];
   // Exchange buffer of the state tiles, double-buffered by step parity.
@@ -189,7 +262,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   const float* Wn = a.W + (long)nh * V * V;
   const int col = 16 * w + n;  // output column of A-operand row m = n
   float wA[SPLIT ? 1 : NT * 4];
-  uint4 wHi[SPLIT ? NCH : 1], wLo[SPLIT ? NCH : 1], wBf[SPLIT ? NCH : 1];
+  uint4 wHi[SPLIT ? NCH : 1], wLo[SPLIT ? NCH : 1];
   if constexpr (!SPLIT) {
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
@@ -205,24 +278,32 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
         const int vin = 16 * tile + 4 * g + (i & 3);
         wv[i] = tile < NT ? kTwoLog2e * Wn[vin * V + col] : 0.0f;
       }
-      uint32_t h[4], l[4], bf[4];
+      uint32_t h[4], l[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float x0 = wv[2 * i], x1 = wv[2 * i + 1];
         if constexpr (MATH == MATH_F16X3) {
           h[i] = pack_f16(x0, x1);
           l[i] = pack_f16(x0 - f16_lo_to_f32(h[i]), x1 - f16_hi_to_f32(h[i]));
-          bf[i] = pack_bf16(x0, x1);
         } else {
           h[i] = pack_bf16(x0, x1);
           l[i] = pack_bf16(x0 - bf16_lo_to_f32(h[i]), x1 - bf16_hi_to_f32(h[i]));
-          bf[i] = h[i];
         }
       }
       wHi[cc] = make_uint4(h[0], h[1], h[2], h[3]);
       wLo[cc] = make_uint4(l[0], l[1], l[2], l[3]);
-      wBf[cc] = make_uint4(bf[0], bf[1], bf[2], bf[3]);
     }
+  }
+  // B operand of the readout's transposing MFMA: selects k-slot (g, e) for output column
+  // j = 4g + (e & 3), adding the hi (e < 4) and lo (e >= 4) parts.
+  uint4 bsel = make_uint4(0, 0, 0, 0);
+  if constexpr (SPLIT) {
+    const uint32_t one = MATH == MATH_F16X3 ? 0x3C00u : 0x3F80u;
+    uint32_t e16[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) e16[e] = (n == 4 * g + (e & 3)) ? one : 0u;
+    bsel = make_uint4(e16[0] | (e16[1] << 16), e16[2] | (e16[3] << 16), e16[4] | (e16[5] << 16),
+                      e16[6] | (e16[7] << 16));
   }
 
   // ---- initial state ----
@@ -239,6 +320,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
     }
   }
 
+  // Split halves of this wave's tile (kept for the readout's transposing MFMA).
+  uint32_t hs[RB][4];
   // Publishes this wave's tile of H into exchange buffer `buf`.
   auto publish = [&](int buf) {
 #pragma unroll
@@ -246,12 +329,11 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
       if constexpr (!SPLIT) {
         *(float4*)&xbuf[buf][((rb * NT + w) * 64 + lane) * 4] = make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
       } else {
-        uint32_t h01, h23, l01, l23;
-        split2<MATH>(H[rb][0], H[rb][1], h01, l01);
-        split2<MATH>(H[rb][2], H[rb][3], h23, l23);
+        split_pair<MATH>(H[rb][0], H[rb][1], hs[rb][0], hs[rb][2]);
+        split_pair<MATH>(H[rb][2], H[rb][3], hs[rb][1], hs[rb][3]);
         const int base = ((rb * NCH + (w >> 1)) * 2) * 64 * 4 + lane * 4 + 2 * (w & 1);
-        *(uint2*)&xbuf[buf][base] = make_uint2(h01, h23);
-        if constexpr (MATH != MATH_BF16) *(uint2*)&xbuf[buf][base + 64 * 4] = make_uint2(l01, l23);
+        *(uint2*)&xbuf[buf][base] = make_uint2(hs[rb][0], hs[rb][1]);
+        if constexpr (MATH != MATH_BF16) *(uint2*)&xbuf[buf][base + 64 * 4] = make_uint2(hs[rb][2], hs[rb][3]);
       }
     }
   };
@@ -262,12 +344,22 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
     lds_barrier();
   }
 
-  // Readout bookkeeping: after the row reduction, lane (g, n) holds column 16w + 4g + (n >> 2);
-  // lanes with n % 4 == 0 store it.  (w_r is read before chunk 0 so that the wait for chunk 0
-  // covers it and no wait is left inside the step loop.)
-  const int ycol = 16 * w + 4 * g + (n >> 2);
-  const bool ystore = (n & 3) == 0;
+  // Readout bookkeeping.
+  //   split modes: after the transposing MFMA lane (g, j) holds column 16w + j; lanes g == 0 store.
+  //   f32 mode:    after the DPP row reduction lane (g, n) holds column 16w + 4g + n/4; lanes with
+  //                n % 4 == 0 store.
+  // (w_r is read before chunk 0 so that the wait for chunk 0 covers it and no wait is left inside
+  // the step loop.)
+  const int ycol = SPLIT ? 16 * w + n : 16 * w + 4 * g + (n >> 2);
+  const bool ystore = SPLIT ? (g == 0) : ((n & 3) == 0);
   const float wr = (MODE == MODE_FWD && a.S == 1) ? a.w_r[(long)nh * V + ycol] : 0.0f;
+
+  StepOffsets<RB> so;
+  so.av = g == 0 ? St::OV + 16 * w + n : 3;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) so.bk[rb] = g == 0 ? St::OK + 16 * rb + n : 3;
+  so.q = SPLIT ? St::OQ + 4 * g : St::OQ + n;
+  so.vcol = St::OV + ycol;
 
   // ---- stage chunk 0, prefetch chunk 1 ----
   ChunkRegs<V, RB, BF16IN> pre;
@@ -286,111 +378,185 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
 
   lds_barrier();
 
-  int j = 0, cb = 0;
-  for (int t = 0; t < a.T; ++t) {
-    if constexpr (MODE == MODE_CKPT) {
-      if (t % a.seg == 0) {
-        float* dst = a.ckpt + ((long)(b * a.N + nh) * nseg + t / a.seg) * KV;
+  // Software pipeline of the step loop.  Step t:
+  //   1. rank-1 term acc = (c k_t) v_t^T as an fp32 MFMA, and the LDS reads of the B operands
+  //      (the state tiles published at step t-1);
+  //   2. finish the readout of step t-1 while those reads are in flight;
+  //   3. the MFMA contraction acc += W'^T H_{t-1}^T;
+  //   4. read step t+1's staged inputs while the MFMAs run;
+  //   5. tanh + gate blend -> H_t, publish H_t's tile (and, in the split modes, start the readout of
+  //      step t with a transposing MFMA), one barrier.
+  // Chunk c+1 is written to the stage ring at step TC-2 of chunk c, so every step's inputs are in
+  // LDS one barrier before step 4 of the previous step reads them.  Inside a chunk the loop is
+  // unrolled, which makes the stage offsets and the exchange-buffer parity compile-time.
+  StepIn<RB, SPLIT> cur = read_step<V, RB, SPLIT>(stage[0], so);
+  StepIn<RB, SPLIT> prev = cur;
+  f32x4 yT[RB];  // transposed tile of H_{t-1} (split modes) for the pending readout
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          *(float4*)(dst + (long)(row0 + 16 * rb + n) * V + 16 * w + 4 * g) =
-              make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
-      }
-    }
-    const float* st = stage[cb] + j * St::STEP;
-    const float4 fg = *(const float4*)st;  // f, 1-f, -2(1-f)
-    const float4 vv = *(const float4*)(st + St::OV + 16 * w + 4 * g);
-    float qn[RB], kn[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      qn[rb] = st[St::OQ + 16 * rb + n];
-      kn[rb] = st[St::OK + 16 * rb + n];
-    }
-    const uint32_t* xr = xbuf[t & 1];
+  for (int rb = 0; rb < RB; ++rb) yT[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
-    f32x4 acc[RB];
-    f32x4 acc2[RB];
+  for (int c0 = 0; c0 < a.T; c0 += TC) {
+    const int cb = (c0 / TC) & 1;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      acc[rb][0] = kn[rb] * vv.x;
-      acc[rb][1] = kn[rb] * vv.y;
-      acc[rb][2] = kn[rb] * vv.z;
-      acc[rb][3] = kn[rb] * vv.w;
-      acc2[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    if constexpr (!SPLIT) {
+    for (int j = 0; j < TC; ++j) {
+      const int t = c0 + j;
+      if (t >= a.T) break;
+      if constexpr (MODE == MODE_CKPT) {
+        if (t % a.seg == 0) {
+          float* dst = a.ckpt + ((long)(b * a.N + nh) * nseg + t / a.seg) * KV;
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const float4 hb = *(const float4*)&xr[((rb * NT + tt) * 64 + lane) * 4];
-          acc[rb] = mfma_f32(wA[tt * 4 + 0], hb.x, acc[rb]);
-          acc[rb] = mfma_f32(wA[tt * 4 + 1], hb.y, acc[rb]);
-          acc[rb] = mfma_f32(wA[tt * 4 + 2], hb.z, acc[rb]);
-          acc[rb] = mfma_f32(wA[tt * 4 + 3], hb.w, acc[rb]);
+          for (int rb = 0; rb < RB; ++rb)
+            *(float4*)(dst + (long)(row0 + 16 * rb + n) * V + 16 * w + 4 * g) =
+                make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
         }
       }
-    } else {
+      const uint32_t* xr = xbuf[j & 1];
+
+      // (1) rank-1 term and B operands of this step.
+      f32x4 acc[RB];
 #pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
+      for (int rb = 0; rb < RB; ++rb) acc[rb] = mfma_f32(cur.av, cur.bk[rb], zero4);
+      float4 hb[SPLIT ? 1 : RB * NT];
+      uint4 bh[SPLIT ? RB * NCH : 1], bl[SPLIT ? RB * NCH : 1];
+      if constexpr (!SPLIT) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int base = ((rb * NCH + cc) * 2) * 64 * 4 + lane * 4;
-          const uint4 bh = *(const uint4*)&xr[base];
-          if constexpr (MATH == MATH_F16X3) {
-            const uint4 bl = *(const uint4*)&xr[base + 64 * 4];
-            acc[rb] = mfma_f16(wHi[cc], bh, acc[rb]);
-            acc2[rb] = mfma_f16(wLo[cc], bh, acc2[rb]);
-            acc2[rb] = mfma_bf16(wBf[cc], bl, acc2[rb]);
-          } else if constexpr (MATH == MATH_BF16X3) {
-            const uint4 bl = *(const uint4*)&xr[base + 64 * 4];
-            acc[rb] = mfma_bf16(wHi[cc], bh, acc[rb]);
-            acc2[rb] = mfma_bf16(wLo[cc], bh, acc2[rb]);
-            acc2[rb] = mfma_bf16(wHi[cc], bl, acc2[rb]);
+        for (int i = 0; i < RB * NT; ++i) hb[i] = *(const float4*)&xr[(i * 64 + lane) * 4];
+      } else {
+#pragma unroll
+        for (int i = 0; i < RB * NCH; ++i) {
+          bh[i] = *(const uint4*)&xr[(i * 2) * 64 * 4 + lane * 4];
+          if constexpr (MATH != MATH_BF16) bl[i] = *(const uint4*)&xr[(i * 2 + 1) * 64 * 4 + lane * 4];
+        }
+      }
+
+      // (2) Readout of step t-1.
+      if constexpr (MODE == MODE_FWD) {
+        if (t > 0) {
+          float yv;
+          if constexpr (SPLIT) {
+            float x = 0.0f;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+              x = __builtin_fmaf(prev.q4[rb].x, yT[rb][0], x);
+              x = __builtin_fmaf(prev.q4[rb].y, yT[rb][1], x);
+              x = __builtin_fmaf(prev.q4[rb].z, yT[rb][2], x);
+              x = __builtin_fmaf(prev.q4[rb].w, yT[rb][3], x);
+            }
+            yv = sum_rows4(x);
           } else {
-            acc[rb] = mfma_bf16(wHi[cc], bh, acc[rb]);
+            float x[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float sacc = H[0][r] * prev.qn[0];
+#pragma unroll
+              for (int rb = 1; rb < RB; ++rb) sacc = __builtin_fmaf(H[rb][r], prev.qn[rb], sacc);
+              x[r] = sacc;
+            }
+            yv = row16_sum4(x[0], x[1], x[2], x[3], lane);
+          }
+          yv = __builtin_fmaf(wr, prev.vcol, yv);
+          if (ystore) ydst[(long)(t - 1) * ystep] = yv;
+        }
+      }
+
+      // (3) Contraction acc += W'^T H^T.
+      if constexpr (!SPLIT) {
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const float4 h4 = hb[rb * NT + tt];
+            acc[rb] = mfma_f32(wA[tt * 4 + 0], h4.x, acc[rb]);
+            acc[rb] = mfma_f32(wA[tt * 4 + 1], h4.y, acc[rb]);
+            acc[rb] = mfma_f32(wA[tt * 4 + 2], h4.z, acc[rb]);
+            acc[rb] = mfma_f32(wA[tt * 4 + 3], h4.w, acc[rb]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < NCH; ++cc) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const uint4 h = bh[rb * NCH + cc];
+            if constexpr (MATH == MATH_F16X3) {
+              acc[rb] = mfma_f16(wHi[cc], h, acc[rb]);
+              acc[rb] = mfma_f16(wLo[cc], h, acc[rb]);
+              acc[rb] = mfma_f16(wHi[cc], bl[rb * NCH + cc], acc[rb]);
+            } else if constexpr (MATH == MATH_BF16X3) {
+              acc[rb] = mfma_bf16(wHi[cc], h, acc[rb]);
+              acc[rb] = mfma_bf16(wLo[cc], h, acc[rb]);
+              acc[rb] = mfma_bf16(wHi[cc], bl[rb * NCH + cc], acc[rb]);
+            } else {
+              acc[rb] = mfma_bf16(wHi[cc], h, acc[rb]);
+            }
           }
         }
       }
-    }
 
-    // tanh + gate blend: H = f H + (1-f)(1 - 2r) = fma(-2(1-f), r, fma(f, H, 1-f)).
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = acc[rb][r];
-        if constexpr (SPLIT && MATH != MATH_BF16) x += acc2[rb][r];
-        const float rr = tanh_recip(x);
-        H[rb][r] = __builtin_fmaf(fg.z, rr, __builtin_fmaf(fg.x, H[rb][r], fg.y));
+      // (4) Next step's inputs (the stage record of step t+1 is complete, see above).
+      StepIn<RB, SPLIT> nxt = cur;
+      if (t + 1 < a.T) {
+        const int jn = (j + 1) % TC;
+        const int cbn = j + 1 == TC ? cb ^ 1 : cb;
+        nxt = read_step<V, RB, SPLIT>(stage[cbn] + jn * St::STEP, so);
       }
-    }
-    publish((t + 1) & 1);
 
-    if constexpr (MODE == MODE_FWD) {
-      float x[4];
+      // (5) tanh + gate blend: H = f H + (1-f)(1 - 2r) = fma(-2(1-f), r, fma(f, H, 1-f)).
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float sacc = H[0][r] * qn[0];
+      for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int rb = 1; rb < RB; ++rb) sacc = __builtin_fmaf(H[rb][r], qn[rb], sacc);
-        x[r] = sacc;
+        for (int r = 0; r < 4; ++r) {
+          const float keep = __builtin_fmaf(cur.f, H[rb][r], cur.g);
+          H[rb][r] = __builtin_fmaf(cur.m2g, tanh_recip(acc[rb][r]), keep);
+        }
       }
-      // w_r (.) v is added here when this workgroup holds all K rows (wr = 0 otherwise).
-      const float yv = __builtin_fmaf(wr, st[St::OV + ycol], row16_sum4(x[0], x[1], x[2], x[3], lane));
-      if (ystore) ydst[(long)t * ystep] = yv;
-    }
+      publish((j + 1) & 1);
+      if constexpr (SPLIT && MODE == MODE_FWD) {
+        // Transposing MFMA: yT[rb] at lane (g, j) = H_t[row 16rb + 4g + r][col 16w + j].
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const uint4 av = make_uint4(hs[rb][0], hs[rb][1], hs[rb][2], hs[rb][3]);
+          yT[rb] = MATH == MATH_F16X3 ? mfma_f16(av, bsel, zero4) : mfma_bf16(av, bsel, zero4);
+        }
+      }
 
-    const bool last_in_chunk = (j == TC - 1);
-    if (last_in_chunk) pre.store(stage[cb ^ 1], tid);
-    lds_barrier();
-    if (last_in_chunk) {
-      const int t_next = t + 1 + TC;  // first step of the chunk after the one just staged
-      if (t_next < a.T) pre.load(a, b, nh, row0, t_next, tid);
-      j = 0;
-      cb ^= 1;
-    } else {
-      ++j;
+      if (j == TC - 2) pre.store(stage[cb ^ 1], tid);
+      lds_barrier();
+      if (j == TC - 2) {
+        const int t_next = c0 + 2 * TC;  // first step of the chunk after the one just staged
+        if (t_next < a.T) pre.load(a, b, nh, row0, t_next, tid);
+      }
+      prev = cur;
+      cur = nxt;
+    }
+  }
+  if constexpr (MODE == MODE_FWD) {
+    if (a.T > 0) {
+      float yv;
+      if constexpr (SPLIT) {
+        float x = 0.0f;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          x = __builtin_fmaf(prev.q4[rb].x, yT[rb][0], x);
+          x = __builtin_fmaf(prev.q4[rb].y, yT[rb][1], x);
+          x = __builtin_fmaf(prev.q4[rb].z, yT[rb][2], x);
+          x = __builtin_fmaf(prev.q4[rb].w, yT[rb][3], x);
+        }
+        yv = sum_rows4(x);
+      } else {
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float sacc = H[0][r] * prev.qn[0];
+#pragma unroll
+          for (int rb = 1; rb < RB; ++rb) sacc = __builtin_fmaf(H[rb][r], prev.qn[rb], sacc);
+          x[r] = sacc;
+        }
+        yv = row16_sum4(x[0], x[1], x[2], x[3], lane);
+      }
+      yv = __builtin_fmaf(wr, prev.vcol, yv);
+      if (ystore) ydst[(long)(a.T - 1) * ystep] = yv;
     }
   }
 
