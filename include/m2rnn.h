@@ -60,8 +60,9 @@ enum { M2RNN_DTYPE_F32 = 0, M2RNN_DTYPE_BF16 = 1 };
 /* How the per-step contraction H_{t-1} W runs on the matrix cores.  The state, the
  * accumulation and everything outside the contraction are fp32 in every mode.
  *   F32     fp32 MFMA (v_mfma_f32_16x16x4_f32).
- *   F16X3   split precision: H = H_hi (fp16) + H_lo (bf16), W = W_hi (fp16) + W_lo (fp16);
- *           H W ~ W_hi H_hi + W_lo H_hi + W_bf16 H_lo on fp16/bf16 MFMA, fp32 accumulate.
+ *   F16X3   split precision: H = H_hi + H_lo and W = W_hi + W_lo, all four fp16 (H_lo, W_lo the
+ *           fp16 rounding remainders); H W ~ W_hi H_hi + W_lo H_hi + W_hi H_lo on fp16 MFMA with
+ *           fp32 accumulation (about 22 significant bits per product).
  *   BF16X3  split precision with bf16 halves: W_hi H_hi + W_lo H_hi + W_hi H_lo.
  *   BF16    one bf16 pass: bf16(W) bf16(H) (coarse; meant for a 2e-2 error budget).
  *   AUTO    the library's default (F16X3). */
@@ -132,7 +133,7 @@ int m2rnn_scan_fwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, int r
  *   dH_T   upstream gradient of the final state, or NULL for zeros.
  *   dq, dk [B,T,N,K]; dv [B,T,N,V]; df [B,T,N]; dW [N,V,V] and dw_r [N,V] summed over batch and
  *   time; dH0 [B,N,K,V] or NULL to skip it.  All fp32.
- *   math   M2RNN_MATH_F32 or M2RNN_MATH_F16X3 (AUTO = F16X3).
+ *   math   M2RNN_MATH_F16X3 or M2RNN_MATH_AUTO (the other modes return M2RNN_EUNSUPPORTED).
  */
 #define M2RNN_BWD_CHECKPOINT 64
 int m2rnn_bwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes);

@@ -6,6 +6,7 @@
 #include <unordered_map>
 
 #include "../../include/m2rnn.h"
+#include "m2rnn_bwd_kernel.h"
 #include "m2rnn_select.h"
 
 using namespace m2rnn;
@@ -197,6 +198,58 @@ int launch_finish(const FwdCall& c, int rb) {
   return hip_status(hipGetLastError());
 }
 
+// ---------------------------------------------------------------- backward
+
+__global__ void m2rnn_fill_kernel(float* __restrict__ dst, const float* __restrict__ src, long count) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) dst[i] = src ? src[i] : 0.0f;
+}
+
+int fill(float* dst, const float* src, long count, hipStream_t stream) {
+  if (!dst || count <= 0) return M2RNN_OK;
+  hipLaunchKernelGGL(m2rnn_fill_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream, dst, src, count);
+  return hip_status(hipGetLastError());
+}
+
+struct BwdLayout {
+  size_t ckpt = 0, seg = 0, dv = 0, df = 0, dW = 0, total = 0;
+};
+
+BwdLayout bwd_layout(const m2rnn_dims* d) {
+  BwdLayout L;
+  const long S = d->K / 16;
+  const long nseg = (d->T + kBwdSeg - 1) / kBwdSeg;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += round_up(bytes);
+    return at;
+  };
+  L.ckpt = take((size_t)d->B * d->N * nseg * d->K * d->V * sizeof(float));
+  L.seg = take((size_t)d->B * d->N * S * kBwdSeg * (d->V / 16) * 64 * 8 * sizeof(float));
+  L.dv = take(S > 1 ? (size_t)S * d->B * d->T * d->N * d->V * sizeof(float) : 0);
+  L.df = take(S > 1 ? (size_t)S * d->B * d->T * d->N * sizeof(float) : 0);
+  L.dW = take((size_t)d->B * S * d->N * d->V * d->V * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+const void* bwd_kernel(int V, bool bf16) {
+  switch (V) {
+    case 16: return bf16 ? (const void*)&m2rnn_scan_bwd_kernel<16, true> : (const void*)&m2rnn_scan_bwd_kernel<16, false>;
+    case 32: return bf16 ? (const void*)&m2rnn_scan_bwd_kernel<32, true> : (const void*)&m2rnn_scan_bwd_kernel<32, false>;
+    case 64: return bf16 ? (const void*)&m2rnn_scan_bwd_kernel<64, true> : (const void*)&m2rnn_scan_bwd_kernel<64, false>;
+    case 128: return bf16 ? (const void*)&m2rnn_scan_bwd_kernel<128, true> : (const void*)&m2rnn_scan_bwd_kernel<128, false>;
+    default: return nullptr;
+  }
+}
+
+int resolve_bwd_math(int math) {
+  if (math == M2RNN_MATH_AUTO || math == M2RNN_MATH_F16X3) return M2RNN_MATH_F16X3;
+  if (math >= M2RNN_MATH_F32 && math <= M2RNN_MATH_BF16) return -2;  // valid enum, not built
+  return -1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +310,100 @@ int m2rnn_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, c
   st = launch_scan(c, m, rb);
   if (st) return st;
   return launch_finish(c, rb);
+}
+
+int m2rnn_bwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes) {
+  if (!bytes) return M2RNN_EINVAL;
+  int st = check_dims(dims, qkv_dtype);
+  if (st) return st;
+  const int m = resolve_bwd_math(math);
+  if (m == -1) return M2RNN_EINVAL;
+  if (m == -2) return M2RNN_EUNSUPPORTED;
+  *bytes = (dims->B == 0 || dims->N == 0 || dims->T == 0) ? 0 : bwd_layout(dims).total;
+  return M2RNN_OK;
+}
+
+int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k, const void* v,
+              const float* f, const float* W, const float* w_r, const float* H0, const float* dy,
+              const float* dH_T, float* dq, float* dk, float* dv, float* df, float* dW, float* dw_r, float* dH0,
+              void* workspace, size_t workspace_bytes, void* stream_) {
+  int st = check_dims(dims, qkv_dtype);
+  if (st) return st;
+  const int m = resolve_bwd_math(math);
+  if (m == -1) return M2RNN_EINVAL;
+  if (m == -2) return M2RNN_EUNSUPPORTED;
+  const m2rnn_dims* d = dims;
+  hipStream_t stream = (hipStream_t)stream_;
+  const bool bf16 = qkv_dtype == M2RNN_DTYPE_BF16;
+  if (d->B == 0 || d->N == 0) return M2RNN_OK;
+  if (!W || !w_r || !dW || !dw_r) return M2RNN_EINVAL;
+  if (d->T > 0 && (!q || !k || !v || !f || !dy || !dq || !dk || !dv || !df)) return M2RNN_EINVAL;
+  {
+    const void* ptrs[] = {q, k, v, W, w_r, H0, dy, dH_T, dq, dk, dv, dW, dw_r, dH0};
+    for (const void* p : ptrs)
+      if (p && !aligned16(p)) return M2RNN_EINVAL;
+    if ((f && ((uintptr_t)f & 3u)) || (df && ((uintptr_t)df & 3u))) return M2RNN_EINVAL;
+  }
+  const long N = d->N, V = d->V, K = d->K, B = d->B, T = d->T;
+  if (T == 0) {
+    // No steps: every gradient is zero except dH0 = dH_T.
+    if ((st = fill(dW, nullptr, N * V * V, stream))) return st;
+    if ((st = fill(dw_r, nullptr, N * V, stream))) return st;
+    return fill(dH0, dH_T, B * N * K * V, stream);
+  }
+  const BwdLayout L = bwd_layout(d);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return M2RNN_EWORKSPACE;
+  char* ws = (char*)workspace;
+  const int S = (int)(K / 16);
+
+  // 1. Checkpoints: the state entering every kBwdSeg-step segment.
+  {
+    FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.H0 = H0;
+    a.y = nullptr; a.H_T = nullptr; a.ckpt = (float*)(ws + L.ckpt);
+    a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S; a.seg = kBwdSeg;
+    const void* kern = fwd_kernel(M2RNN_MATH_F16X3, (int)V, 1, bf16, MODE_CKPT);
+    if (!kern) return M2RNN_EUNSUPPORTED;
+    void* args[] = {&a};
+    st = hip_status(hipLaunchKernel(kern, dim3((unsigned)(B * N * S)), dim3((unsigned)(4 * V)), args, 0, stream));
+    if (st) return st;
+  }
+  // 2. Reverse scan.
+  {
+    BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.dy = dy; a.dH_T = dH_T;
+    a.ckpt = (const float*)(ws + L.ckpt);
+    a.seg_ws = (float*)(ws + L.seg);
+    a.dq = dq; a.dk = dk;
+    a.dv = S > 1 ? (float*)(ws + L.dv) : dv;
+    a.df = S > 1 ? (float*)(ws + L.df) : df;
+    a.dW_part = (float*)(ws + L.dW);
+    a.dH0 = dH0;
+    a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S;
+    const void* kern = bwd_kernel((int)V, bf16);
+    if (!kern) return M2RNN_EUNSUPPORTED;
+    void* args[] = {&a};
+    st = hip_status(hipLaunchKernel(kern, dim3((unsigned)(B * N * S)), dim3((unsigned)(4 * V)), args, 0, stream));
+    if (st) return st;
+  }
+  // 3. Deterministic sums of the per-workgroup partials, and dw_r.
+  if (S > 1) {
+    const long plane = B * T * N * V;
+    hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<false>, dim3((unsigned)((plane / 4 + 255) / 256)), dim3(256), 0, stream,
+                       (const float*)(ws + L.dv), S, plane, (const void*)dy, w_r, (int)N, (int)V, dv);
+    const long cnt = B * T * N;
+    hipLaunchKernelGGL(m2rnn_bwd_sum_df_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream,
+                       (const float*)(ws + L.df), S, cnt, df);
+  }
+  hipLaunchKernelGGL(m2rnn_bwd_sum_dW_kernel, dim3((unsigned)((N * V * V + 255) / 256)), dim3(256), 0, stream,
+                     (const float*)(ws + L.dW), (int)(B * S), (int)N, (int)(V * V), dW);
+  if (bf16)
+    hipLaunchKernelGGL(m2rnn_bwd_dwr_kernel<true>, dim3((unsigned)N), dim3(256), 0, stream, dy, v, (int)B, (int)T,
+                       (int)N, (int)V, dw_r);
+  else
+    hipLaunchKernelGGL(m2rnn_bwd_dwr_kernel<false>, dim3((unsigned)N), dim3(256), 0, stream, dy, v, (int)B, (int)T,
+                       (int)N, (int)V, dw_r);
+  return hip_status(hipGetLastError());
 }
 
 }  // extern "C"

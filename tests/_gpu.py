@@ -64,3 +64,25 @@ def oracle_units(d, units):
 
 def max_abs(a, b):
     return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64)))) if np.size(a) else 0.0
+
+
+def gpu_bwd(dd, math="auto", dH_T=None, want_dH0=True):
+    torch = torch_cuda()
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    g = m2.m2rnn_bwd(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], dd.get("H0"), dd["dy"],
+                     dH_T if dH_T is not None else dd.get("dH_T"), math=math, want_dH0=want_dH0)
+    torch.cuda.synchronize()
+    return {name: (t.cpu().numpy().astype(np.float64) if t is not None else None) for name, t in g.items()}
+
+
+def oracle_bwd(d):
+    return oracle.ref_bwd(d["q"], d["k"], d["v"], d["f"], d["W"], d["w_r"], d.get("H0"), d["dy"], d.get("dH_T"))
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.linalg.norm(b)
+    if den == 0.0:
+        return float(np.linalg.norm(a))
+    return float(np.linalg.norm(a - b) / den)
