@@ -67,7 +67,7 @@ def cpu_baseline(d, w, seconds: float):
 
     nthreads = oracle.default_threads()
     units = min(w.B * w.N, nthreads)
-    pairs = [(u // w.N, u % w.N) for u in range(units)]
+    pairs = [(u // w.N, u % w.N) for u in range(w.B * w.N)]
 
     def run(T, nunits, threads):
         # Units become the heads of one batch entry: q [1, T, units, K], W [units, V, V], ...
@@ -82,10 +82,60 @@ def cpu_baseline(d, w, seconds: float):
     probe_T = min(w.T, 128)
     per_step = run(probe_T, 1, 1) / probe_T
     T_s = int(max(64, min(w.T, seconds / max(per_step, 1e-9))))
+    if T_s == w.T:
+        # A full-length unit per thread is shorter than the target: give each thread more units.
+        reps = max(1, int(seconds / max(per_step * w.T, 1e-9)))
+        units = min(w.B * w.N, nthreads * reps)
     wall = run(T_s, units, nthreads)
     return {"value": units * T_s / wall, "unit": "head-steps/s", "cores": min(nthreads, units), "kind": "oracle",
-            "sample": f"{units} (batch, head) units x {T_s} steps of {w.name} (fp64, one unit per thread)",
+            "sample": f"{units} (batch, head) units x {T_s} steps of {w.name} (fp64, units spread over threads)",
             "wall_s": round(wall, 3)}
+
+
+def bench_backward(args) -> int:
+    """Times m2rnn_bwd (checkpoint forward + reverse scan + sums) on the BPTT workload."""
+    import numpy as np
+    import torch
+
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    from matrix_state_nonlinear_m2rnn_amd import inputs
+
+    name = args.workload if args.workload != "long_b2_h32_t16384_kv64" else "bwd_b4_h16_t4096_kv64"
+    w = inputs.WORKLOADS[name]
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    d = inputs.workload_inputs(w.name, with_dy=True)
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(np.ascontiguousarray(a)).to(dev) for n, a in d.items() if a is not None}
+    if w.qkv_dtype == "bf16":
+        for n in ("q", "k", "v"):
+            t[n] = t[n].to(torch.bfloat16).contiguous()
+    B, T, N, K, V = w.B, w.T, w.N, w.K, w.V
+    dims = m2.Dims(B, T, N, K, V)
+    dt = m2.DTYPE_BF16 if w.qkv_dtype == "bf16" else m2.DTYPE_F32
+    ws = torch.empty(max(m2.m2rnn_bwd_workspace_size(dims, dt, "auto"), 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        return m2.m2rnn_bwd(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], None, t["dy"], None, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    hs = B * N * T
+    out = {"metric": "M²RNN bwd (BPTT) head-steps/sec", "value": hs / (ms * 1e-3), "unit": "head-steps/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": w.name, "B": B, "T": T, "N": N, "K": K, "V": V, "qkv_dtype": w.qkv_dtype,
+                      "math": "f16x3", "checkpoint": m2.BWD_CHECKPOINT},
+           "tokens_per_s": B * T / (ms * 1e-3)}
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -98,6 +148,8 @@ def main() -> int:
     ap.add_argument("--row-blocks", type=int, default=0)
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--backward", action="store_true",
+                    help="time m2rnn_bwd on the BPTT workload instead of the forward (its own JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -117,6 +169,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.backward:
+        return bench_backward(args)
     w = inputs.WORKLOADS[args.workload]
     math_mode = "f16x3" if args.math == "auto" else args.math
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
