@@ -212,7 +212,7 @@ int fill(float* dst, const float* src, long count, hipStream_t stream) {
 }
 
 struct BwdLayout {
-  size_t ckpt = 0, seg = 0, dv = 0, df = 0, dW = 0, total = 0;
+  size_t ckpt = 0, seg = 0, dv = 0, df = 0, dW = 0, dwr = 0, total = 0;
 };
 
 BwdLayout bwd_layout(const m2rnn_dims* d) {
@@ -230,6 +230,7 @@ BwdLayout bwd_layout(const m2rnn_dims* d) {
   L.dv = take(S > 1 ? (size_t)S * d->B * d->T * d->N * d->V * sizeof(float) : 0);
   L.df = take(S > 1 ? (size_t)S * d->B * d->T * d->N * sizeof(float) : 0);
   L.dW = take((size_t)d->B * S * d->N * d->V * d->V * sizeof(float));
+  L.dwr = take((size_t)d->B * d->N * d->V * sizeof(float));
   L.total = off;
   return L;
 }
@@ -378,6 +379,7 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
     a.dv = S > 1 ? (float*)(ws + L.dv) : dv;
     a.df = S > 1 ? (float*)(ws + L.df) : df;
     a.dW_part = (float*)(ws + L.dW);
+    a.dwr_part = (float*)(ws + L.dwr);
     a.dH0 = dH0;
     a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S;
     const void* kern = bwd_kernel((int)V, bf16);
@@ -397,12 +399,8 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
   }
   hipLaunchKernelGGL(m2rnn_bwd_sum_dW_kernel, dim3((unsigned)((N * V * V + 255) / 256)), dim3(256), 0, stream,
                      (const float*)(ws + L.dW), (int)(B * S), (int)N, (int)(V * V), dW);
-  if (bf16)
-    hipLaunchKernelGGL(m2rnn_bwd_dwr_kernel<true>, dim3((unsigned)N), dim3(256), 0, stream, dy, v, (int)B, (int)T,
-                       (int)N, (int)V, dw_r);
-  else
-    hipLaunchKernelGGL(m2rnn_bwd_dwr_kernel<false>, dim3((unsigned)N), dim3(256), 0, stream, dy, v, (int)B, (int)T,
-                       (int)N, (int)V, dw_r);
+  hipLaunchKernelGGL(m2rnn_bwd_sum_dwr_kernel, dim3((unsigned)((N * V + 255) / 256)), dim3(256), 0, stream,
+                     (const float*)(ws + L.dwr), (int)B, (int)(N * V), dw_r);
   return hip_status(hipGetLastError());
 }
 

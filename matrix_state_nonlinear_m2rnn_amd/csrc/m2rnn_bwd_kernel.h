@@ -16,7 +16,7 @@
 //     3. walk the segment backwards: R, D and the row/column reductions in registers; D is
 //        published through LDS exactly like H in the forward, and the chain's D W^T runs on the
 //        split-precision MFMA; every wave transposes the D tiles it has just read (one MFMA per
-//        tile) and accumulates dW[own columns of H_{t-1}][all columns of D] with fp32 MFMAs.
+//        tile) and accumulates dW[own columns of H_{t-1}][all columns of D] with split-fp16 MFMAs.
 //   Per-workgroup partials of dv, df and dW are summed by separate, deterministic passes.
 #pragma once
 
@@ -42,6 +42,7 @@ struct BwdArgs {
   float* dv;           // final dv (S == 1) or partials [S][B*T*N*V]
   float* df;           // final df (S == 1) or partials [S][B*T*N]
   float* dW_part;      // [B*S][N][V][V]
+  float* dwr_part;     // [B][N][V] (written by the workgroups with s == 0)
   float* dH0;          // may be null
   int B, T, N, K;
   int S;
@@ -246,6 +247,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   float* dv_dst = a.dv + (a.S > 1 ? (long)s * plane : 0);
   float* df_dst = a.df + (a.S > 1 ? (long)s * a.B * a.T * a.N : 0);
   const float wr_col = a.S == 1 ? a.w_r[(long)nh * V + 16 * w + n] : 0.0f;  // for dv's w_r (.) u term
+  float dwr = 0.0f;  // dw_r[16w + n] partial over this batch entry (workgroups with s == 0, lanes g == 0)
 
   for (int seg = nseg - 1; seg >= 0; --seg) {
     const int t0 = seg * kBwdSeg;
@@ -299,6 +301,15 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     __threadfence_block();  // the segment store is read back by the same lanes below
 
     // ---------------- 2. walk the segment backwards ----------------
+    // The segment store is read two steps ahead of use (its latency is that of L2 / HBM).
+    uint4 nh0 = *(const uint4*)(segs + (nst - 1) * SEG_STEP);
+    float4 nz0 = *(const float4*)(segs + (nst - 1) * SEG_STEP + 4);
+    uint4 nh1 = make_uint4(0, 0, 0, 0);
+    float4 nz1 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (nst >= 2) {
+      nh1 = *(const uint4*)(segs + (nst - 2) * SEG_STEP);
+      nz1 = *(const float4*)(segs + (nst - 2) * SEG_STEP + 4);
+    }
     for (int j = nst - 1; j >= 0; --j) {
       const int t = t0 + j;
       const float* st = stage + j * St::STEP;
@@ -306,8 +317,15 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       const float qn = st[St::OQ + n];
       const float4 u4 = *(const float4*)(st + St::OU + 16 * w + 4 * g);
       const float4 v4 = *(const float4*)(st + St::OV + 16 * w + 4 * g);
-      const uint4 hsp = *(const uint4*)(segs + j * SEG_STEP);  // H_{t-1} split
-      const float4 z4 = *(const float4*)(segs + j * SEG_STEP + 4);
+      const uint4 hsp = nh0;  // H_{t-1} split
+      const float4 z4 = nz0;
+      nh0 = nh1;
+      nz0 = nz1;
+      if (j >= 2) {
+        nh1 = *(const uint4*)(segs + (j - 2) * SEG_STEP);
+        nz1 = *(const float4*)(segs + (j - 2) * SEG_STEP + 4);
+      }
+      if (s == 0 && g == 0) dwr = __builtin_fmaf(st[St::OU + 16 * w + n], st[St::OV + 16 * w + n], dwr);
       const float Z[4] = {z4.x, z4.y, z4.z, z4.w};
       const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
       const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
@@ -384,11 +402,21 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       }
       // Transposed own H_{t-1} tile: hT at lane (g, m) reg r = H_{t-1}[row 4g + r][col 16w + m].
       const f32x4 hT = mfma_f16(hsp, bsel, zero4);
-      // dW[16w + m][16tt + j] += sum_rows H_{t-1}[row][16w + m] D[row][16tt + j].
+      // dW[16w + m][16tt + j] += sum_rows H_{t-1}[row][16w + m] D[row][16tt + j]: one 16x16x16
+      // MFMA per split term, A = hT (k = row), B = dT[tt] (k = row), both re-split to fp16 hi/lo.
+      uint32_t th[4];
+      split_pair<MATH_F16X3>(hT[0], hT[1], th[0], th[2]);
+      split_pair<MATH_F16X3>(hT[2], hT[3], th[1], th[3]);
+      const uint2 hThi = make_uint2(th[0], th[1]), hTlo = make_uint2(th[2], th[3]);
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) dWacc[tt] = mfma_f32(hT[c], dT[tt][c], dWacc[tt]);
+        uint32_t dd[4];
+        split_pair<MATH_F16X3>(dT[tt][0], dT[tt][1], dd[0], dd[2]);
+        split_pair<MATH_F16X3>(dT[tt][2], dT[tt][3], dd[1], dd[3]);
+        const uint2 dhi = make_uint2(dd[0], dd[1]), dlo = make_uint2(dd[2], dd[3]);
+        dWacc[tt] = mfma16_f16(hThi, dhi, dWacc[tt]);
+        dWacc[tt] = mfma16_f16(hTlo, dhi, dWacc[tt]);
+        dWacc[tt] = mfma16_f16(hThi, dlo, dWacc[tt]);
       }
       // dv[col 16w + j] = sum_rows D[row][col] k[row] (+ w_r u when this workgroup holds all rows).
       {
@@ -413,6 +441,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   }
 
   if (a.dH0) *(float4*)(a.dH0 + own_off) = make_float4(C[0], C[1], C[2], C[3]);
+  if (s == 0 && g == 0) a.dwr_part[((long)b * a.N + nh) * V + 16 * w + n] = dwr;
   // dW partial of this workgroup: dWacc[tt] at lane (g, j) reg r = dW[16w + 4g + r][16tt + j].
   float* dWp = a.dW_part + ((long)(b * a.S + s) * a.N + nh) * V * V;
 #pragma unroll
@@ -441,33 +470,14 @@ __global__ void __launch_bounds__(256) m2rnn_bwd_sum_dW_kernel(const float* __re
   dW[i] = acc;
 }
 
-// dw_r[n][j] = sum_{b,t} dy[b,t,n,j] v[b,t,n,j]; one block per head, a fixed-order tree per column.
-template <bool BF16IN>
-__global__ void __launch_bounds__(256) m2rnn_bwd_dwr_kernel(const float* __restrict__ dy, const void* __restrict__ v,
-                                                             int B, int T, int N, int V, float* __restrict__ dw_r) {
-  __shared__ float red[256];
-  const int nh = blockIdx.x;
-  const int lanes_per_col = 256 / V;  // V divides 256
-  const int j = threadIdx.x % V;
-  const int part = threadIdx.x / V;
+// dw_r[n][j] = sum over b of the per-batch-entry partials (each already summed over t).
+__global__ void __launch_bounds__(256) m2rnn_bwd_sum_dwr_kernel(const float* __restrict__ part, int B, int NV,
+                                                                 float* __restrict__ dw_r) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= NV) return;
   float acc = 0.0f;
-  for (long bt = part; bt < (long)B * T; bt += lanes_per_col) {
-    const long idx = (bt * N + nh) * V + j;
-    float vv;
-    if constexpr (BF16IN) {
-      vv = __uint_as_float(((uint32_t)((const uint16_t*)v)[idx]) << 16);
-    } else {
-      vv = ((const float*)v)[idx];
-    }
-    acc = __builtin_fmaf(dy[idx], vv, acc);
-  }
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  if (part == 0) {
-    float sum = 0.0f;
-    for (int p = 0; p < lanes_per_col; ++p) sum += red[p * V + j];
-    dw_r[(long)nh * V + j] = sum;
-  }
+  for (int b = 0; b < B; ++b) acc += part[(long)b * NV + i];
+  dw_r[i] = acc;
 }
 
 }  // namespace m2rnn

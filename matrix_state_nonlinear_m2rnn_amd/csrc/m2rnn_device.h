@@ -101,6 +101,16 @@ __device__ __forceinline__ f32x4 mfma_f16(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
                                                 0, 0, 0);
 }
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short bf16x4_bits __attribute__((ext_vector_type(4)));
+// 16x16x16 variants: K = 16, four 16-bit values per lane (2 dwords).
+__device__ __forceinline__ f32x4 mfma16_f16(uint2 a, uint2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_bf16(uint2 a, uint2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_bits, a), __builtin_bit_cast(bf16x4_bits, b),
+                                                   c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                  c, 0, 0, 0);

@@ -190,8 +190,12 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
   if constexpr (MATH == MATH_F16X3) {
     hi = pack_f16(a, b);
     uint32_t l;
-    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l) : "v"(hi), "v"(a));
-    asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(l) : "v"(hi), "v"(b));
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\ts_nop 1" : "=v"(l) : "v"(hi), "v"(a));
+    // The trailing s_nop gives the two wait states that a VALU write needs before an MFMA may read
+    // the register; the compiler inserts them for its own instructions but not after inline asm.
+    asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\ts_nop 1"
+        : "+v"(l)
+        : "v"(hi), "v"(b));
     lo = l;
   } else if constexpr (MATH == MATH_BF16X3) {
     hi = pack_bf16(a, b);
@@ -262,36 +266,46 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   const float* Wn = a.W + (long)nh * V * V;
   const int col = 16 * w + n;  // output column of A-operand row m = n
   float wA[SPLIT ? 1 : NT * 4];
-  uint4 wHi[SPLIT ? NCH : 1], wLo[SPLIT ? NCH : 1];
+  // Split modes: the 32-wide chunk holding this wave's own tile is contracted with the own tile's
+  // values taken from registers (k-slots 0..3 of each lane group) and only the partner tile's read
+  // from LDS (k-slots 4..7); the other chunks are read whole.  The A operands follow that order.
+  constexpr int NOTH = NCH > 1 ? NCH - 1 : 1;
+  const int co = w >> 1;  // own chunk
+  uint4 wOwnHi, wOwnLo, wOthHi[NOTH], wOthLo[NOTH];
+  auto wchunk = [&](int t_lo, int t_hi, uint4& hi, uint4& lo) {
+    float wv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tile = (i >> 2) ? t_hi : t_lo;
+      const int vin = 16 * tile + 4 * g + (i & 3);
+      wv[i] = tile < NT ? kTwoLog2e * Wn[vin * V + col] : 0.0f;
+    }
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x0 = wv[2 * i], x1 = wv[2 * i + 1];
+      if constexpr (MATH == MATH_F16X3) {
+        h[i] = pack_f16(x0, x1);
+        l[i] = pack_f16(x0 - f16_lo_to_f32(h[i]), x1 - f16_hi_to_f32(h[i]));
+      } else {
+        h[i] = pack_bf16(x0, x1);
+        l[i] = pack_bf16(x0 - bf16_lo_to_f32(h[i]), x1 - bf16_hi_to_f32(h[i]));
+      }
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+  };
   if constexpr (!SPLIT) {
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) wA[tt * 4 + r] = kTwoLog2e * Wn[(16 * tt + 4 * g + r) * V + col];
   } else {
+    wchunk(w, w ^ 1, wOwnHi, wOwnLo);
 #pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-      float wv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tile = 2 * cc + (i >> 2);
-        const int vin = 16 * tile + 4 * g + (i & 3);
-        wv[i] = tile < NT ? kTwoLog2e * Wn[vin * V + col] : 0.0f;
-      }
-      uint32_t h[4], l[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x0 = wv[2 * i], x1 = wv[2 * i + 1];
-        if constexpr (MATH == MATH_F16X3) {
-          h[i] = pack_f16(x0, x1);
-          l[i] = pack_f16(x0 - f16_lo_to_f32(h[i]), x1 - f16_hi_to_f32(h[i]));
-        } else {
-          h[i] = pack_bf16(x0, x1);
-          l[i] = pack_bf16(x0 - bf16_lo_to_f32(h[i]), x1 - bf16_hi_to_f32(h[i]));
-        }
-      }
-      wHi[cc] = make_uint4(h[0], h[1], h[2], h[3]);
-      wLo[cc] = make_uint4(l[0], l[1], l[2], l[3]);
+    for (int i = 0; i < NCH - 1; ++i) {
+      const int cc = i < co ? i : i + 1;
+      wchunk(2 * cc, 2 * cc + 1, wOthHi[i], wOthLo[i]);
     }
   }
   // B operand of the readout's transposing MFMA: selects k-slot (g, e) for output column
@@ -418,15 +432,25 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) acc[rb] = mfma_f32(cur.av, cur.bk[rb], zero4);
       float4 hb[SPLIT ? 1 : RB * NT];
-      uint4 bh[SPLIT ? RB * NCH : 1], bl[SPLIT ? RB * NCH : 1];
+      uint4 bh[SPLIT ? RB * NOTH : 1], bl[SPLIT ? RB * NOTH : 1];
+      uint2 ph[SPLIT ? RB : 1], pl[SPLIT ? RB : 1];
       if constexpr (!SPLIT) {
 #pragma unroll
         for (int i = 0; i < RB * NT; ++i) hb[i] = *(const float4*)&xr[(i * 64 + lane) * 4];
       } else {
 #pragma unroll
-        for (int i = 0; i < RB * NCH; ++i) {
-          bh[i] = *(const uint4*)&xr[(i * 2) * 64 * 4 + lane * 4];
-          if constexpr (MATH != MATH_BF16) bl[i] = *(const uint4*)&xr[(i * 2 + 1) * 64 * 4 + lane * 4];
+        for (int rb = 0; rb < RB; ++rb) {
+          // partner half of the own chunk
+          const int pbase = ((rb * NCH + co) * 2) * 64 * 4 + lane * 4 + 2 * ((w & 1) ^ 1);
+          ph[rb] = *(const uint2*)&xr[pbase];
+          if constexpr (MATH != MATH_BF16) pl[rb] = *(const uint2*)&xr[pbase + 64 * 4];
+#pragma unroll
+          for (int i = 0; i < NCH - 1; ++i) {
+            const int cc = i < co ? i : i + 1;
+            const int base = ((rb * NCH + cc) * 2) * 64 * 4 + lane * 4;
+            bh[rb * NOTH + i] = *(const uint4*)&xr[base];
+            if constexpr (MATH != MATH_BF16) bl[rb * NOTH + i] = *(const uint4*)&xr[base + 64 * 4];
+          }
         }
       }
 
@@ -474,24 +498,30 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
           }
         }
       } else {
-#pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) {
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const uint4 h = bh[rb * NCH + cc];
-            if constexpr (MATH == MATH_F16X3) {
-              acc[rb] = mfma_f16(wHi[cc], h, acc[rb]);
-              acc[rb] = mfma_f16(wLo[cc], h, acc[rb]);
-              acc[rb] = mfma_f16(wHi[cc], bl[rb * NCH + cc], acc[rb]);
-            } else if constexpr (MATH == MATH_BF16X3) {
-              acc[rb] = mfma_bf16(wHi[cc], h, acc[rb]);
-              acc[rb] = mfma_bf16(wLo[cc], h, acc[rb]);
-              acc[rb] = mfma_bf16(wHi[cc], bl[rb * NCH + cc], acc[rb]);
-            } else {
-              acc[rb] = mfma_bf16(wHi[cc], h, acc[rb]);
-            }
+        auto contract = [&](int rb, const uint4& Ahi, const uint4& Alo, const uint4& h, const uint4& l) {
+          if constexpr (MATH == MATH_F16X3) {
+            acc[rb] = mfma_f16(Ahi, h, acc[rb]);
+            acc[rb] = mfma_f16(Alo, h, acc[rb]);
+            acc[rb] = mfma_f16(Ahi, l, acc[rb]);
+          } else if constexpr (MATH == MATH_BF16X3) {
+            acc[rb] = mfma_bf16(Ahi, h, acc[rb]);
+            acc[rb] = mfma_bf16(Alo, h, acc[rb]);
+            acc[rb] = mfma_bf16(Ahi, l, acc[rb]);
+          } else {
+            acc[rb] = mfma_bf16(Ahi, h, acc[rb]);
           }
+        };
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          // own chunk: own tile (registers, H_{t-1} split at the last publish) + partner half
+          const uint4 h = make_uint4(hs[rb][0], hs[rb][1], ph[rb].x, ph[rb].y);
+          const uint4 l = MATH != MATH_BF16 ? make_uint4(hs[rb][2], hs[rb][3], pl[rb].x, pl[rb].y) : h;
+          contract(rb, wOwnHi, wOwnLo, h, l);
         }
+#pragma unroll
+        for (int i = 0; i < NCH - 1; ++i)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) contract(rb, wOthHi[i], wOthLo[i], bh[rb * NOTH + i], bl[rb * NOTH + i]);
       }
 
       // (4) Next step's inputs (the stage record of step t+1 is complete, see above).
