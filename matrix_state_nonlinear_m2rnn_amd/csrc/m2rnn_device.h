@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace m2rnn {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -18,6 +20,13 @@ enum { MATH_F32 = 0, MATH_F16X3 = 1, MATH_BF16X3 = 2, MATH_BF16 = 3 };
 
 // 2*log2(e): the kernels keep c*P instead of P so that exp(2P) is a single v_exp_f32 (2^x).
 constexpr float kTwoLog2e = 2.88539008177792681472f;
+
+// Word 3 of a gfx9 buffer resource for raw (unformatted, stride 0) dword access: 32-bit data
+// format, no swizzle.  With stride 0 the buffer unit checks each access's byte offset against the
+// resource's size and drops out-of-range stores (and returns 0 for out-of-range loads).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+// A byte offset past the end of every buffer resource built here (sizes stay below 2^31 bytes).
+constexpr uint32_t kBufferDrop = 0x80000000u;
 
 // Workgroup barrier whose fences cover LDS only: it waits for this wave's LDS traffic
 // (lgkmcnt(0)) but not for its outstanding global loads/stores, so input prefetches and output

@@ -215,6 +215,19 @@ __device__ __forceinline__ float sum_rows4(float x) {
   return __uint_as_float(p2[0]) + __uint_as_float(p2[1]);
 }
 
+// Sums of four values over the four 16-lane rows at once: lane (g, j) returns
+// x_g(j) + x_g(16 + j) + x_g(32 + j) + x_g(48 + j).  The 32-lane swap pairs x0 with x2 and x1
+// with x3 (each half of the wave keeps the value it will return), the 16-lane swap then pairs the
+// two partial sums: three swaps and three adds for four reductions.
+__device__ __forceinline__ float reduce_rows4(float x0, float x1, float x2, float x3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x2), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x1), __float_as_uint(x3), false, false);
+  const float s02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float s13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // MODE_FWD: full forward with readout.  MODE_CKPT: state only, storing the state that enters
 // every `seg`-step segment (used by the backward pass).
 enum { MODE_FWD = 0, MODE_CKPT = 1 };
@@ -308,16 +321,15 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
       wchunk(2 * cc, 2 * cc + 1, wOthHi[i], wOthLo[i]);
     }
   }
-  // B operand of the readout's transposing MFMA: selects k-slot (g, e) for output column
-  // j = 4g + (e & 3), adding the hi (e < 4) and lo (e >= 4) parts.
-  uint4 bsel = make_uint4(0, 0, 0, 0);
+  // B operand of the readout's transposing MFMAs (16x16x16, contraction over the tile's 16
+  // columns): the identity, k-slot (g, e) = column 4g + e selected for output column j = 4g + e.
+  uint2 bsel = make_uint2(0, 0);
   if constexpr (SPLIT) {
     const uint32_t one = MATH == MATH_F16X3 ? 0x3C00u : 0x3F80u;
-    uint32_t e16[8];
+    uint32_t e16[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) e16[e] = (n == 4 * g + (e & 3)) ? one : 0u;
-    bsel = make_uint4(e16[0] | (e16[1] << 16), e16[2] | (e16[3] << 16), e16[4] | (e16[5] << 16),
-                      e16[6] | (e16[7] << 16));
+    for (int e = 0; e < 4; ++e) e16[e] = (n == 4 * g + e) ? one : 0u;
+    bsel = make_uint2(e16[0] | (e16[1] << 16), e16[2] | (e16[3] << 16));
   }
 
   // ---- initial state ----
@@ -334,8 +346,13 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
     }
   }
 
-  // Split halves of this wave's tile (kept for the readout's transposing MFMA).
-  uint32_t hs[RB][4];
+  // This wave's tile of H_{t-1} as B operands of its own 32-wide chunk (split modes): hq holds the
+  // high halves [own tile, k-slots 0..3 | partner tile, k-slots 4..7], lq the low halves.  The own
+  // halves are written when the tile is published (and are also the A operands of the readout's
+  // transposing MFMAs); the partner halves are read from LDS straight into the upper two dwords.
+  uint4 hq[RB], lq[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) hq[rb] = lq[rb] = make_uint4(0, 0, 0, 0);
   // Publishes this wave's tile of H into exchange buffer `buf`.
   auto publish = [&](int buf) {
 #pragma unroll
@@ -343,11 +360,16 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
       if constexpr (!SPLIT) {
         *(float4*)&xbuf[buf][((rb * NT + w) * 64 + lane) * 4] = make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
       } else {
-        split_pair<MATH>(H[rb][0], H[rb][1], hs[rb][0], hs[rb][2]);
-        split_pair<MATH>(H[rb][2], H[rb][3], hs[rb][1], hs[rb][3]);
+        uint32_t h0, h1, l0, l1;
+        split_pair<MATH>(H[rb][0], H[rb][1], h0, l0);
+        split_pair<MATH>(H[rb][2], H[rb][3], h1, l1);
+        hq[rb].x = h0;
+        hq[rb].y = h1;
+        lq[rb].x = l0;
+        lq[rb].y = l1;
         const int base = ((rb * NCH + (w >> 1)) * 2) * 64 * 4 + lane * 4 + 2 * (w & 1);
-        *(uint2*)&xbuf[buf][base] = make_uint2(hs[rb][0], hs[rb][1]);
-        if constexpr (MATH != MATH_BF16) *(uint2*)&xbuf[buf][base + 64 * 4] = make_uint2(hs[rb][2], hs[rb][3]);
+        *(uint2*)&xbuf[buf][base] = make_uint2(h0, h1);
+        if constexpr (MATH != MATH_BF16) *(uint2*)&xbuf[buf][base + 64 * 4] = make_uint2(l0, l1);
       }
     }
   };
@@ -358,15 +380,35 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
     lds_barrier();
   }
 
-  // Readout bookkeeping.
-  //   split modes: after the transposing MFMA lane (g, j) holds column 16w + j; lanes g == 0 store.
+  // Readout.
+  //   split modes: the transposing MFMA leaves lane (g, j) with rows 4g..4g+3 of column 16w + j;
+  //                the lane's q-weighted sum over them is kept for four consecutive steps, and one
+  //                cross-row reduction of the four leaves lane (g, j) with y[t0 + g][16w + j], so
+  //                every lane stores, once per four steps.
   //   f32 mode:    after the DPP row reduction lane (g, n) holds column 16w + 4g + n/4; lanes with
-  //                n % 4 == 0 store.
+  //                n % 4 == 0 store, every step.
+  // Stores go through a buffer resource whose size ends at the last valid step of this (b, n):
+  // the (padded) steps past T and the lanes that do not store get offsets past that end, which
+  // the buffer unit drops, so the step loop carries no branches for them.
   // (w_r is read before chunk 0 so that the wait for chunk 0 covers it and no wait is left inside
   // the step loop.)
   const int ycol = SPLIT ? 16 * w + n : 16 * w + 4 * g + (n >> 2);
-  const bool ystore = SPLIT ? (g == 0) : ((n & 3) == 0);
+  const bool ystore = SPLIT || ((n & 3) == 0);
   const float wr = (MODE == MODE_FWD && a.S == 1) ? a.w_r[(long)nh * V + ycol] : 0.0f;
+  const int ystep = a.N * V;  // floats between consecutive steps of y
+  float* ybase = nullptr;  // y (S == 1) or this row group's partial plane, at [b, 0, nh, 0]
+  int ybytes = 0;
+  if constexpr (MODE == MODE_FWD) {
+    const long plane = (long)a.B * a.T * a.N * V;
+    ybase = a.y + (a.S > 1 ? (long)s * plane : 0) + ((long)b * a.T * a.N + nh) * V;
+    // Element (t, nh, c) is valid iff t < T, i.e. iff it lies below (T N V - nh V) floats from ybase.
+    ybytes = (a.T * a.N - nh) * V * 4;
+  }
+  const __amdgpu_buffer_rsrc_t yres = __builtin_amdgcn_make_buffer_rsrc(ybase, (short)0, ybytes, kBufferRsrcWord3);
+  // Byte offset of this lane's element at step 0 (split: step g), or kBufferDrop.
+  const uint32_t ylane = ystore ? (uint32_t)(((SPLIT ? g * ystep : 0) + ycol) * 4) : kBufferDrop;
+  // Stage-record offset of v[ycol] for the readout of step t0 + g (split modes).
+  const int vlane = (SPLIT ? g * St::STEP : 0) + St::OV + ycol;
 
   StepOffsets<RB> so;
   so.av = g == 0 ? St::OV + 16 * w + n : 3;
@@ -382,42 +424,51 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   if (a.T > TC) pre.load(a, b, nh, row0, TC, tid);
   publish(0);
 
-  float* ydst = nullptr;
-  if constexpr (MODE == MODE_FWD) {
-    const long plane = (long)a.B * a.T * a.N * V;
-    ydst = a.y + (a.S > 1 ? (long)s * plane : 0) + ((long)b * a.T * a.N + nh) * V + ycol;
-  }
-  const long ystep = (long)a.N * V;
   const int nseg = MODE == MODE_CKPT ? (a.T + a.seg - 1) / a.seg : 0;
 
   lds_barrier();
 
   // Software pipeline of the step loop.  Step t:
-  //   1. rank-1 term acc = (c k_t) v_t^T as an fp32 MFMA, and the LDS reads of the B operands
-  //      (the state tiles published at step t-1);
-  //   2. finish the readout of step t-1 while those reads are in flight;
+  //   1. the LDS reads of the B operands (the state tiles published at step t-1), and the rank-1
+  //      term acc = (c k_t) v_t^T as an fp32 MFMA;
+  //   2. the readout of step t-1 while those reads are in flight;
   //   3. the MFMA contraction acc += W'^T H_{t-1}^T;
   //   4. read step t+1's staged inputs while the MFMAs run;
   //   5. tanh + gate blend -> H_t, publish H_t's tile (and, in the split modes, start the readout of
   //      step t with a transposing MFMA), one barrier.
   // Chunk c+1 is written to the stage ring at step TC-2 of chunk c, so every step's inputs are in
-  // LDS one barrier before step 4 of the previous step reads them.  Inside a chunk the loop is
-  // unrolled, which makes the stage offsets and the exchange-buffer parity compile-time.
+  // LDS one barrier before step 4 of the previous step reads them.  Two chunks are unrolled per
+  // loop trip, which makes the stage offsets and the exchange-buffer parity compile-time.  The
+  // last chunk runs whole: its steps past T are staged with f = 1 and k = v = q = 0, which leaves
+  // H bit-for-bit unchanged (H = fma(-0, r, fma(1, H, 0)) = H), and their y stores are dropped.
   StepIn<RB, SPLIT> cur = read_step<V, RB, SPLIT>(stage[0], so);
   StepIn<RB, SPLIT> prev = cur;
   f32x4 yT[RB];  // transposed tile of H_{t-1} (split modes) for the pending readout
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) yT[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  float xq[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // split readout: partial sums of the last four steps
+  f32x4 kv[RB];                            // rank-1 term (c k_t) v_t^T of the coming step
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) kv[rb] = mfma_f32(cur.av, cur.bk[rb], zero4);
+  // Offsets (in dwords) of the partner half of the own chunk, high and low parts.  The low
+  // offset goes through an empty asm so that the compiler keeps the two 8-byte reads apart
+  // (fused into one 16-byte read, the halves would need copies into their operand registers).
+  int phi_off[RB], plo_off[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    phi_off[rb] = ((rb * NCH + co) * 2) * 64 * 4 + lane * 4 + 2 * ((w & 1) ^ 1);
+    plo_off[rb] = phi_off[rb] + 64 * 4;
+    asm volatile("" : "+v"(plo_off[rb]));
+  }
 
-  for (int c0 = 0; c0 < a.T; c0 += TC) {
-    const int cb = (c0 / TC) & 1;
+  auto run_chunk = [&](auto CB, int c0) __attribute__((always_inline)) {
+    constexpr int cb = decltype(CB)::value;
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
       const int t = c0 + j;
-      if (t >= a.T) break;
       if constexpr (MODE == MODE_CKPT) {
-        if (t % a.seg == 0) {
+        if (t % a.seg == 0 && t < a.T) {
           float* dst = a.ckpt + ((long)(b * a.N + nh) * nseg + t / a.seg) * KV;
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
@@ -427,13 +478,9 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
       }
       const uint32_t* xr = xbuf[j & 1];
 
-      // (1) rank-1 term and B operands of this step.
-      f32x4 acc[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) acc[rb] = mfma_f32(cur.av, cur.bk[rb], zero4);
+      // (1) B operands of this step and the rank-1 term.
       float4 hb[SPLIT ? 1 : RB * NT];
       uint4 bh[SPLIT ? RB * NOTH : 1], bl[SPLIT ? RB * NOTH : 1];
-      uint2 ph[SPLIT ? RB : 1], pl[SPLIT ? RB : 1];
       if constexpr (!SPLIT) {
 #pragma unroll
         for (int i = 0; i < RB * NT; ++i) hb[i] = *(const float4*)&xr[(i * 64 + lane) * 4];
@@ -441,9 +488,14 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           // partner half of the own chunk
-          const int pbase = ((rb * NCH + co) * 2) * 64 * 4 + lane * 4 + 2 * ((w & 1) ^ 1);
-          ph[rb] = *(const uint2*)&xr[pbase];
-          if constexpr (MATH != MATH_BF16) pl[rb] = *(const uint2*)&xr[pbase + 64 * 4];
+          const uint2 ph = *(const uint2*)(xr + phi_off[rb]);
+          hq[rb].z = ph.x;
+          hq[rb].w = ph.y;
+          if constexpr (MATH != MATH_BF16) {
+            const uint2 pl = *(const uint2*)(xbuf[j & 1] + plo_off[rb]);
+            lq[rb].z = pl.x;
+            lq[rb].w = pl.y;
+          }
 #pragma unroll
           for (int i = 0; i < NCH - 1; ++i) {
             const int cc = i < co ? i : i + 1;
@@ -453,34 +505,52 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
           }
         }
       }
+      float vterm = 0.0f;
+      if constexpr (MODE == MODE_FWD && SPLIT) {
+        // v of steps t-4 .. t-3 for the readout finished at this step (j % 4 == 0); at j == 0 they
+        // are the last four of the previous chunk.
+        if (j % 4 == 0)
+          vterm = (j == 0 ? stage[cb ^ 1] + (TC - 4) * St::STEP : stage[cb] + (j - 4) * St::STEP)[vlane];
+      }
+      // Keep every LDS read above issued before the work below, so that their latencies overlap.
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 acc[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[rb] = kv[rb];
 
-      // (2) Readout of step t-1.
+      // (2) Readout of step t-1 (nothing is stored for t = 0: its offsets are moved past the end).
       if constexpr (MODE == MODE_FWD) {
-        if (t > 0) {
-          float yv;
-          if constexpr (SPLIT) {
-            float x = 0.0f;
+        const bool live = j > 0 || c0 > 0;
+        if constexpr (SPLIT) {
+          float x = 0.0f;
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-              x = __builtin_fmaf(prev.q4[rb].x, yT[rb][0], x);
-              x = __builtin_fmaf(prev.q4[rb].y, yT[rb][1], x);
-              x = __builtin_fmaf(prev.q4[rb].z, yT[rb][2], x);
-              x = __builtin_fmaf(prev.q4[rb].w, yT[rb][3], x);
-            }
-            yv = sum_rows4(x);
-          } else {
-            float x[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              float sacc = H[0][r] * prev.qn[0];
-#pragma unroll
-              for (int rb = 1; rb < RB; ++rb) sacc = __builtin_fmaf(H[rb][r], prev.qn[rb], sacc);
-              x[r] = sacc;
-            }
-            yv = row16_sum4(x[0], x[1], x[2], x[3], lane);
+          for (int rb = 0; rb < RB; ++rb) {
+            x = __builtin_fmaf(prev.q4[rb].x, yT[rb][0], x);
+            x = __builtin_fmaf(prev.q4[rb].y, yT[rb][1], x);
+            x = __builtin_fmaf(prev.q4[rb].z, yT[rb][2], x);
+            x = __builtin_fmaf(prev.q4[rb].w, yT[rb][3], x);
           }
+          xq[(j + 3) & 3] = x;
+          if (j % 4 == 0) {
+            // Steps t-4 .. t-1 are complete.
+            float yv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
+            yv = __builtin_fmaf(wr, vterm, yv);
+            const uint32_t off = live ? ylane + (uint32_t)((t - 4) * ystep * 4) : kBufferDrop;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, off, 0, 0);
+          }
+        } else {
+          float x[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float sacc = H[0][r] * prev.qn[0];
+#pragma unroll
+            for (int rb = 1; rb < RB; ++rb) sacc = __builtin_fmaf(H[rb][r], prev.qn[rb], sacc);
+            x[r] = sacc;
+          }
+          float yv = row16_sum4(x[0], x[1], x[2], x[3], lane);
           yv = __builtin_fmaf(wr, prev.vcol, yv);
-          if (ystore) ydst[(long)(t - 1) * ystep] = yv;
+          const uint32_t off = live ? ylane + (uint32_t)((t - 1) * ystep * 4) : kBufferDrop;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, off, 0, 0);
         }
       }
 
@@ -512,25 +582,17 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
           }
         };
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          // own chunk: own tile (registers, H_{t-1} split at the last publish) + partner half
-          const uint4 h = make_uint4(hs[rb][0], hs[rb][1], ph[rb].x, ph[rb].y);
-          const uint4 l = MATH != MATH_BF16 ? make_uint4(hs[rb][2], hs[rb][3], pl[rb].x, pl[rb].y) : h;
-          contract(rb, wOwnHi, wOwnLo, h, l);
-        }
+        for (int rb = 0; rb < RB; ++rb) contract(rb, wOwnHi, wOwnLo, hq[rb], lq[rb]);
 #pragma unroll
         for (int i = 0; i < NCH - 1; ++i)
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) contract(rb, wOthHi[i], wOthLo[i], bh[rb * NOTH + i], bl[rb * NOTH + i]);
       }
 
-      // (4) Next step's inputs (the stage record of step t+1 is complete, see above).
-      StepIn<RB, SPLIT> nxt = cur;
-      if (t + 1 < a.T) {
-        const int jn = (j + 1) % TC;
-        const int cbn = j + 1 == TC ? cb ^ 1 : cb;
-        nxt = read_step<V, RB, SPLIT>(stage[cbn] + jn * St::STEP, so);
-      }
+      // (4) Next step's inputs (the stage record of step t+1 is complete, see above; past the
+      // last step this reads a stale record that is never used).
+      const StepIn<RB, SPLIT> nxt =
+          read_step<V, RB, SPLIT>(j + 1 == TC ? stage[cb ^ 1] : stage[cb] + (j + 1) * St::STEP, so);
 
       // (5) tanh + gate blend: H = f H + (1-f)(1 - 2r) = fma(-2(1-f), r, fma(f, H, 1-f)).
 #pragma unroll
@@ -543,13 +605,22 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
       }
       publish((j + 1) & 1);
       if constexpr (SPLIT && MODE == MODE_FWD) {
-        // Transposing MFMA: yT[rb] at lane (g, j) = H_t[row 16rb + 4g + r][col 16w + j].
+        // Transposing MFMAs: yT[rb] at lane (g, j) = H_t[row 16rb + 4g + r][col 16w + j] (hi + lo).
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          const uint4 av = make_uint4(hs[rb][0], hs[rb][1], hs[rb][2], hs[rb][3]);
-          yT[rb] = MATH == MATH_F16X3 ? mfma_f16(av, bsel, zero4) : mfma_bf16(av, bsel, zero4);
+          const uint2 oh = make_uint2(hq[rb].x, hq[rb].y), ol = make_uint2(lq[rb].x, lq[rb].y);
+          if constexpr (MATH == MATH_F16X3) {
+            yT[rb] = mfma16_f16(ol, bsel, mfma16_f16(oh, bsel, zero4));
+          } else if constexpr (MATH == MATH_BF16X3) {
+            yT[rb] = mfma16_bf16(ol, bsel, mfma16_bf16(oh, bsel, zero4));
+          } else {
+            yT[rb] = mfma16_bf16(oh, bsel, zero4);
+          }
         }
       }
+      // Rank-1 term of step t+1.
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) kv[rb] = mfma_f32(nxt.av, nxt.bk[rb], zero4);
 
       if (j == TC - 2) pre.store(stage[cb ^ 1], tid);
       lds_barrier();
@@ -560,10 +631,18 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
       prev = cur;
       cur = nxt;
     }
+  };
+
+  for (int c0 = 0; c0 < a.T; c0 += 2 * TC) {
+    run_chunk(std::integral_constant<int, 0>{}, c0);
+    if (c0 + TC < a.T) run_chunk(std::integral_constant<int, 1>{}, c0 + TC);
   }
+
+  // Readout of the last step (and, in the split modes, of the last group of four).
   if constexpr (MODE == MODE_FWD) {
-    if (a.T > 0) {
-      float yv;
+    const int tp = (a.T + TC - 1) / TC * TC;  // steps run, a multiple of TC
+    if (tp > 0) {
+      const int cbl = (tp / TC - 1) & 1;      // stage buffer of the last chunk
       if constexpr (SPLIT) {
         float x = 0.0f;
 #pragma unroll
@@ -573,7 +652,10 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
           x = __builtin_fmaf(prev.q4[rb].z, yT[rb][2], x);
           x = __builtin_fmaf(prev.q4[rb].w, yT[rb][3], x);
         }
-        yv = sum_rows4(x);
+        xq[3] = x;
+        float yv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
+        yv = __builtin_fmaf(wr, stage[cbl][(TC - 4) * St::STEP + vlane], yv);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, ylane + (uint32_t)((tp - 4) * ystep * 4), 0, 0);
       } else {
         float x[4];
 #pragma unroll
@@ -583,10 +665,10 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
           for (int rb = 1; rb < RB; ++rb) sacc = __builtin_fmaf(H[rb][r], prev.qn[rb], sacc);
           x[r] = sacc;
         }
-        yv = row16_sum4(x[0], x[1], x[2], x[3], lane);
+        float yv = row16_sum4(x[0], x[1], x[2], x[3], lane);
+        yv = __builtin_fmaf(wr, prev.vcol, yv);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, ylane + (uint32_t)((tp - 1) * ystep * 4), 0, 0);
       }
-      yv = __builtin_fmaf(wr, prev.vcol, yv);
-      if (ystore) ydst[(long)(a.T - 1) * ystep] = yv;
     }
   }
 
