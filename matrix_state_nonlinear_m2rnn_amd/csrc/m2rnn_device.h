@@ -41,10 +41,21 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_amdgcn_update_dpp(0.0f, x, CTRL, 0xF, 0xF, false);
 }
+
+// DPP lane permutation with all lanes written (no `old` value), so that the compiler can fold
+// the permutation into the consuming VALU instruction's first operand.
+template <int CTRL>
+__device__ __forceinline__ float dpp_all(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
 constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15-i within each row of 16
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7-i within each half-row of 8
 constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppQuadBcast0 = 0x00;      // quad_perm [0,0,0,0]
+constexpr int kDppQuadBcast1 = 0x55;      // quad_perm [1,1,1,1]
+constexpr int kDppQuadBcast2 = 0xAA;      // quad_perm [2,2,2,2]
+constexpr int kDppQuadBcast3 = 0xFF;      // quad_perm [3,3,3,3]
 
 // Sums four per-lane values over the 16 lanes of each DPP row at once: on return, lane n of a
 // row holds sum_{lanes m of the row} x_{(n >> 2) & 3}(m).  Lanes xor 15 and xor 7 exchange the

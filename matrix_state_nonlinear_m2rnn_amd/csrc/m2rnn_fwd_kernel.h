@@ -49,7 +49,8 @@ struct FwdShape {
   static constexpr int TC = 16;              // steps per staged chunk (the step loop is unrolled per chunk)
 };
 
-// Per-step stage record (fp32): [f, 1-f, -2(1-f), 0 | q rows | c*k rows | v (V)].
+// Per-step stage record (fp32): [f, 0, 0, 0 | q rows | c*k rows | v (V)] (slot 3 is the zero that
+// the lanes without a rank-1 operand read).
 template <int V, int RB>
 struct Stage {
   static constexpr int ROWS = 16 * RB;
@@ -132,22 +133,19 @@ struct ChunkRegs {
     q.store(stage, St::STEP, St::OQ, 1.0f, tid);
     k.store(stage, St::STEP, St::OK, kTwoLog2e, tid);
     v.store(stage, St::STEP, St::OV, 1.0f, tid);
-    if (tid < S::TC) {
-      const float g = 1.0f - f;
-      *(float4*)(stage + tid * St::STEP) = make_float4(f, g, -2.0f * g, 0.0f);
-    }
+    if (tid < S::TC) *(float4*)(stage + tid * St::STEP) = make_float4(f, 0.0f, 0.0f, 0.0f);
   }
 };
 
 // Per-step inputs a lane needs, read from the stage ring one step ahead.
 template <int RB, bool SPLIT>
 struct StepIn {
-  float f, g, m2g;             // f, 1-f, -2(1-f)
+  float f;                     // the gate (1-f and -2(1-f) are formed in registers)
   float av;                    // A operand of the rank-1 MFMA: v[16w + n] on lanes with g == 0, else 0
   float bk[RB];                // B operand of the rank-1 MFMA: c*k[row] on lanes with g == 0, else 0
-  float4 q4[SPLIT ? RB : 1];   // split modes: q of rows 16rb + 4g .. 16rb + 4g + 3
-  float qn[SPLIT ? 1 : RB];    // f32 mode:    q of row 16rb + n
-  float vcol;                  // v[ycol] for the w_r (.) v readout term
+  float qn[RB];                // split modes: q of row 16rb + 4g + (n & 3) (a quad holds rows 4g..4g+3)
+                               // f32 mode:    q of row 16rb + n
+  float vcol;                  // f32 mode: v[ycol] for the w_r (.) v readout term
 };
 
 // Lane-constant offsets (in floats) into one stage record.
@@ -163,21 +161,13 @@ template <int V, int RB, bool SPLIT>
 __device__ __forceinline__ StepIn<RB, SPLIT> read_step(const float* st, const StepOffsets<RB>& o) {
   using Sg = Stage<V, RB>;
   StepIn<RB, SPLIT> s;
-  const float4 fg = *(const float4*)st;
-  s.f = fg.x;
-  s.g = fg.y;
-  s.m2g = fg.z;
+  s.f = st[0];
   s.av = st[o.av];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) s.bk[rb] = st[o.bk[rb]];
-  if constexpr (SPLIT) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) s.q4[rb] = *(const float4*)(st + o.q + 16 * rb);
-  } else {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) s.qn[rb] = st[o.q + 16 * rb];
-  }
-  s.vcol = st[o.vcol];
+  for (int rb = 0; rb < RB; ++rb) s.qn[rb] = st[o.q + 16 * rb];
+  s.vcol = SPLIT ? 0.0f : st[o.vcol];
   return s;
 }
 
@@ -380,8 +370,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
     lds_barrier();
   }
 
-  // Readout.
-  //   split modes: the transposing MFMA leaves lane (g, j) with rows 4g..4g+3 of column 16w + j;
+  // Readout, done right after H_t is published, while this wave waits for that LDS write.
+  //   split modes: the transposing MFMAs leave lane (g, j) with rows 4g..4g+3 of column 16w + j;
   //                the lane's q-weighted sum over them is kept for four consecutive steps, and one
   //                cross-row reduction of the four leaves lane (g, j) with y[t0 + g][16w + j], so
   //                every lane stores, once per four steps.
@@ -414,7 +404,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   so.av = g == 0 ? St::OV + 16 * w + n : 3;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) so.bk[rb] = g == 0 ? St::OK + 16 * rb + n : 3;
-  so.q = SPLIT ? St::OQ + 4 * g : St::OQ + n;
+  so.q = SPLIT ? St::OQ + 4 * g + (n & 3) : St::OQ + n;
   so.vcol = St::OV + ycol;
 
   // ---- stage chunk 0, prefetch chunk 1 ----
@@ -429,25 +419,27 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   lds_barrier();
 
   // Software pipeline of the step loop.  Step t:
-  //   1. the LDS reads of the B operands (the state tiles published at step t-1), and the rank-1
-  //      term acc = (c k_t) v_t^T as an fp32 MFMA;
-  //   2. the readout of step t-1 while those reads are in flight;
-  //   3. the MFMA contraction acc += W'^T H_{t-1}^T;
-  //   4. read step t+1's staged inputs while the MFMAs run;
-  //   5. tanh + gate blend -> H_t, publish H_t's tile (and, in the split modes, start the readout of
-  //      step t with a transposing MFMA), one barrier.
+  //   1. the LDS reads of the B operands (the state tiles published at step t-1);
+  //   2. the MFMA contraction acc = (c k_t) v_t^T + W'^T H_{t-1}^T (the rank-1 term was issued at
+  //      the end of step t-1), and step t+1's staged inputs read while the MFMAs run;
+  //   3. tanh + gate blend -> H_t, publish H_t's tile;
+  //   4. while that write completes: the readout of step t, and the rank-1 MFMA of step t+1;
+  //      one barrier.
   // Chunk c+1 is written to the stage ring at step TC-2 of chunk c, so every step's inputs are in
-  // LDS one barrier before step 4 of the previous step reads them.  Two chunks are unrolled per
+  // LDS one barrier before step 2 of the previous step reads them.  Two chunks are unrolled per
   // loop trip, which makes the stage offsets and the exchange-buffer parity compile-time.  The
   // last chunk runs whole: its steps past T are staged with f = 1 and k = v = q = 0, which leaves
   // H bit-for-bit unchanged (H = fma(-0, r, fma(1, H, 0)) = H), and their y stores are dropped.
   StepIn<RB, SPLIT> cur = read_step<V, RB, SPLIT>(stage[0], so);
-  StepIn<RB, SPLIT> prev = cur;
-  f32x4 yT[RB];  // transposed tile of H_{t-1} (split modes) for the pending readout
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) yT[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
   float xq[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // split readout: partial sums of the last four steps
+  f32x4 yT[RB];                            // split readout: transposed tile of H_{t-1}
+  float qprev[RB];                         // and q_{t-1} (quad layout)
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    yT[rb] = zero4;
+    qprev[rb] = 0.0f;
+  }
   f32x4 kv[RB];                            // rank-1 term (c k_t) v_t^T of the coming step
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) kv[rb] = mfma_f32(cur.av, cur.bk[rb], zero4);
@@ -478,7 +470,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
       }
       const uint32_t* xr = xbuf[j & 1];
 
-      // (1) B operands of this step and the rank-1 term.
+      // (1) B operands of this step.
       float4 hb[SPLIT ? 1 : RB * NT];
       uint4 bh[SPLIT ? RB * NOTH : 1], bl[SPLIT ? RB * NOTH : 1];
       if constexpr (!SPLIT) {
@@ -505,56 +497,39 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
           }
         }
       }
-      float vterm = 0.0f;
+      float vterm = 0.0f, ygrp = 0.0f;
       if constexpr (MODE == MODE_FWD && SPLIT) {
-        // v of steps t-4 .. t-3 for the readout finished at this step (j % 4 == 0); at j == 0 they
+        // v of steps t-4 .. t-1 for the readout finished at this step (j % 4 == 0); at j == 0 they
         // are the last four of the previous chunk.
         if (j % 4 == 0)
           vterm = (j == 0 ? stage[cb ^ 1] + (TC - 4) * St::STEP : stage[cb] + (j - 4) * St::STEP)[vlane];
       }
       // Keep every LDS read above issued before the work below, so that their latencies overlap.
       __builtin_amdgcn_sched_barrier(0);
+
+      // Readout of step t-1 (split modes) while those reads are in flight: the q-weighted sum of the
+      // transposed tile (broadcast of q within each quad of lanes), and every fourth step the
+      // cross-row reduction and store of four steps.  Nothing is stored for t = 0: its offsets are
+      // moved past the end.
+      if constexpr (MODE == MODE_FWD && SPLIT) {
+        float x = 0.0f;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          x = rb == 0 ? dpp_all<kDppQuadBcast0>(qprev[rb]) * yT[rb][0]
+                      : __builtin_fmaf(dpp_all<kDppQuadBcast0>(qprev[rb]), yT[rb][0], x);
+          x = __builtin_fmaf(dpp_all<kDppQuadBcast1>(qprev[rb]), yT[rb][1], x);
+          x = __builtin_fmaf(dpp_all<kDppQuadBcast2>(qprev[rb]), yT[rb][2], x);
+          x = __builtin_fmaf(dpp_all<kDppQuadBcast3>(qprev[rb]), yT[rb][3], x);
+        }
+        xq[(j + 3) & 3] = x;
+        if (j % 4 == 0) ygrp = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);  // finished after the publish
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // (2) Contraction acc = (c k_t) v_t^T + W'^T H^T.
       f32x4 acc[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) acc[rb] = kv[rb];
-
-      // (2) Readout of step t-1 (nothing is stored for t = 0: its offsets are moved past the end).
-      if constexpr (MODE == MODE_FWD) {
-        const bool live = j > 0 || c0 > 0;
-        if constexpr (SPLIT) {
-          float x = 0.0f;
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            x = __builtin_fmaf(prev.q4[rb].x, yT[rb][0], x);
-            x = __builtin_fmaf(prev.q4[rb].y, yT[rb][1], x);
-            x = __builtin_fmaf(prev.q4[rb].z, yT[rb][2], x);
-            x = __builtin_fmaf(prev.q4[rb].w, yT[rb][3], x);
-          }
-          xq[(j + 3) & 3] = x;
-          if (j % 4 == 0) {
-            // Steps t-4 .. t-1 are complete.
-            float yv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
-            yv = __builtin_fmaf(wr, vterm, yv);
-            const uint32_t off = live ? ylane + (uint32_t)((t - 4) * ystep * 4) : kBufferDrop;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, off, 0, 0);
-          }
-        } else {
-          float x[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float sacc = H[0][r] * prev.qn[0];
-#pragma unroll
-            for (int rb = 1; rb < RB; ++rb) sacc = __builtin_fmaf(H[rb][r], prev.qn[rb], sacc);
-            x[r] = sacc;
-          }
-          float yv = row16_sum4(x[0], x[1], x[2], x[3], lane);
-          yv = __builtin_fmaf(wr, prev.vcol, yv);
-          const uint32_t off = live ? ylane + (uint32_t)((t - 1) * ystep * 4) : kBufferDrop;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, off, 0, 0);
-        }
-      }
-
-      // (3) Contraction acc += W'^T H^T.
       if constexpr (!SPLIT) {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
@@ -589,38 +564,64 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
           for (int rb = 0; rb < RB; ++rb) contract(rb, wOthHi[i], wOthLo[i], bh[rb * NOTH + i], bl[rb * NOTH + i]);
       }
 
-      // (4) Next step's inputs (the stage record of step t+1 is complete, see above; past the
-      // last step this reads a stale record that is never used).
+      // Next step's inputs (the stage record of step t+1 is complete, see above; past the last
+      // step this reads a stale record that is never used).
       const StepIn<RB, SPLIT> nxt =
           read_step<V, RB, SPLIT>(j + 1 == TC ? stage[cb ^ 1] : stage[cb] + (j + 1) * St::STEP, so);
 
-      // (5) tanh + gate blend: H = f H + (1-f)(1 - 2r) = fma(-2(1-f), r, fma(f, H, 1-f)).
+      // (3) tanh + gate blend: H = f H + (1-f)(1 - 2r) = fma(-2(1-f), r, fma(f, H, 1-f)).
+      const float gf = 1.0f - cur.f, m2g = -2.0f * gf;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float keep = __builtin_fmaf(cur.f, H[rb][r], cur.g);
-          H[rb][r] = __builtin_fmaf(cur.m2g, tanh_recip(acc[rb][r]), keep);
+          const float keep = __builtin_fmaf(cur.f, H[rb][r], gf);
+          H[rb][r] = __builtin_fmaf(m2g, tanh_recip(acc[rb][r]), keep);
         }
       }
       publish((j + 1) & 1);
-      if constexpr (SPLIT && MODE == MODE_FWD) {
-        // Transposing MFMAs: yT[rb] at lane (g, j) = H_t[row 16rb + 4g + r][col 16w + j] (hi + lo).
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const uint2 oh = make_uint2(hq[rb].x, hq[rb].y), ol = make_uint2(lq[rb].x, lq[rb].y);
-          if constexpr (MATH == MATH_F16X3) {
-            yT[rb] = mfma16_f16(ol, bsel, mfma16_f16(oh, bsel, zero4));
-          } else if constexpr (MATH == MATH_BF16X3) {
-            yT[rb] = mfma16_bf16(ol, bsel, mfma16_bf16(oh, bsel, zero4));
-          } else {
-            yT[rb] = mfma16_bf16(oh, bsel, zero4);
+      // The work below fills the wait for that write; keep it after the write and before the barrier.
+      __builtin_amdgcn_sched_barrier(0);
+
+      // (4) Readout of step t and the rank-1 term of step t+1, in the shadow of the write.
+      if constexpr (MODE == MODE_FWD) {
+        if constexpr (SPLIT) {
+          if (j % 4 == 0) {
+            const float yv = __builtin_fmaf(wr, vterm, ygrp);
+            const uint32_t off = (j > 0 || c0 > 0) ? ylane + (uint32_t)((t - 4) * ystep * 4) : kBufferDrop;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, off, 0, 0);
           }
+          // Transposing MFMAs: yT at lane (g, j) = H_t[row 16rb + 4g + r][col 16w + j] (hi + lo),
+          // used by the next step.
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const uint2 oh = make_uint2(hq[rb].x, hq[rb].y), ol = make_uint2(lq[rb].x, lq[rb].y);
+            if constexpr (MATH == MATH_F16X3) {
+              yT[rb] = mfma16_f16(ol, bsel, mfma16_f16(oh, bsel, zero4));
+            } else if constexpr (MATH == MATH_BF16X3) {
+              yT[rb] = mfma16_bf16(ol, bsel, mfma16_bf16(oh, bsel, zero4));
+            } else {
+              yT[rb] = mfma16_bf16(oh, bsel, zero4);
+            }
+            qprev[rb] = cur.qn[rb];
+          }
+        } else {
+          float x[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float sacc = H[0][r] * cur.qn[0];
+#pragma unroll
+            for (int rb = 1; rb < RB; ++rb) sacc = __builtin_fmaf(H[rb][r], cur.qn[rb], sacc);
+            x[r] = sacc;
+          }
+          float yv = row16_sum4(x[0], x[1], x[2], x[3], lane);
+          yv = __builtin_fmaf(wr, cur.vcol, yv);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, ylane + (uint32_t)(t * ystep * 4), 0, 0);
         }
       }
-      // Rank-1 term of step t+1.
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) kv[rb] = mfma_f32(nxt.av, nxt.bk[rb], zero4);
+      __builtin_amdgcn_sched_barrier(0);
 
       if (j == TC - 2) pre.store(stage[cb ^ 1], tid);
       lds_barrier();
@@ -628,7 +629,6 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
         const int t_next = c0 + 2 * TC;  // first step of the chunk after the one just staged
         if (t_next < a.T) pre.load(a, b, nh, row0, t_next, tid);
       }
-      prev = cur;
       cur = nxt;
     }
   };
@@ -638,37 +638,23 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
     if (c0 + TC < a.T) run_chunk(std::integral_constant<int, 1>{}, c0 + TC);
   }
 
-  // Readout of the last step (and, in the split modes, of the last group of four).
-  if constexpr (MODE == MODE_FWD) {
+  // Readout of the last group of four steps (split modes).
+  if constexpr (MODE == MODE_FWD && SPLIT) {
     const int tp = (a.T + TC - 1) / TC * TC;  // steps run, a multiple of TC
     if (tp > 0) {
       const int cbl = (tp / TC - 1) & 1;      // stage buffer of the last chunk
-      if constexpr (SPLIT) {
-        float x = 0.0f;
+      float x = 0.0f;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          x = __builtin_fmaf(prev.q4[rb].x, yT[rb][0], x);
-          x = __builtin_fmaf(prev.q4[rb].y, yT[rb][1], x);
-          x = __builtin_fmaf(prev.q4[rb].z, yT[rb][2], x);
-          x = __builtin_fmaf(prev.q4[rb].w, yT[rb][3], x);
-        }
-        xq[3] = x;
-        float yv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
-        yv = __builtin_fmaf(wr, stage[cbl][(TC - 4) * St::STEP + vlane], yv);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, ylane + (uint32_t)((tp - 4) * ystep * 4), 0, 0);
-      } else {
-        float x[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float sacc = H[0][r] * prev.qn[0];
-#pragma unroll
-          for (int rb = 1; rb < RB; ++rb) sacc = __builtin_fmaf(H[rb][r], prev.qn[rb], sacc);
-          x[r] = sacc;
-        }
-        float yv = row16_sum4(x[0], x[1], x[2], x[3], lane);
-        yv = __builtin_fmaf(wr, prev.vcol, yv);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, ylane + (uint32_t)((tp - 1) * ystep * 4), 0, 0);
+      for (int rb = 0; rb < RB; ++rb) {
+        x = __builtin_fmaf(dpp_all<kDppQuadBcast0>(qprev[rb]), yT[rb][0], x);
+        x = __builtin_fmaf(dpp_all<kDppQuadBcast1>(qprev[rb]), yT[rb][1], x);
+        x = __builtin_fmaf(dpp_all<kDppQuadBcast2>(qprev[rb]), yT[rb][2], x);
+        x = __builtin_fmaf(dpp_all<kDppQuadBcast3>(qprev[rb]), yT[rb][3], x);
       }
+      xq[3] = x;
+      float yv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
+      yv = __builtin_fmaf(wr, stage[cbl][(TC - 4) * St::STEP + vlane], yv);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, ylane + (uint32_t)((tp - 4) * ystep * 4), 0, 0);
     }
   }
 
