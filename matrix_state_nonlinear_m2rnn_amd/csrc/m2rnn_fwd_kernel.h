@@ -236,8 +236,9 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   __shared__ __attribute__((aligned(16))) float stage[2][TC * St::STEP];
   // Exchange buffer of the state tiles, double-buffered by step parity.
   //   F32:   [2][RB][NT][64 lanes][4 floats]
-  //   split: [2][RB][NCH][hi|lo][64 lanes][4 dwords]; wave w fills dwords 2(w&1), 2(w&1)+1
-  //          of chunk w/2, so one 16-byte read yields the 8 contraction values of a chunk.
+  //   split: [2][RB][NCH][hi|lo][half][64 lanes][2 dwords]; wave w fills half w&1 of chunk w/2.
+  //          Every access is 8 contiguous bytes per lane (no LDS bank conflicts); the two halves
+  //          of a chunk, 512 bytes apart, are read by one 2 x 8-byte instruction.
   constexpr int XWORDS = SPLIT ? (RB * NCH * 2 * 64 * 4) : (RB * NT * 64 * 4);
   __shared__ __attribute__((aligned(16))) uint32_t xbuf[2][XWORDS];
 
@@ -357,9 +358,9 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
         hq[rb].y = h1;
         lq[rb].x = l0;
         lq[rb].y = l1;
-        const int base = ((rb * NCH + (w >> 1)) * 2) * 64 * 4 + lane * 4 + 2 * (w & 1);
+        const int base = ((rb * NCH + (w >> 1)) * 4 + (w & 1)) * 128 + lane * 2;
         *(uint2*)&xbuf[buf][base] = make_uint2(h0, h1);
-        if constexpr (MATH != MATH_BF16) *(uint2*)&xbuf[buf][base + 64 * 4] = make_uint2(l0, l1);
+        if constexpr (MATH != MATH_BF16) *(uint2*)&xbuf[buf][base + 256] = make_uint2(l0, l1);
       }
     }
   };
@@ -443,14 +444,14 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   f32x4 kv[RB];                            // rank-1 term (c k_t) v_t^T of the coming step
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) kv[rb] = mfma_f32(cur.av, cur.bk[rb], zero4);
-  // Offsets (in dwords) of the partner half of the own chunk, high and low parts.  The low
+  // Offsets (in 8-byte units) of the partner half of the own chunk, high and low parts.  The low
   // offset goes through an empty asm so that the compiler keeps the two 8-byte reads apart
   // (fused into one 16-byte read, the halves would need copies into their operand registers).
   int phi_off[RB], plo_off[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    phi_off[rb] = ((rb * NCH + co) * 2) * 64 * 4 + lane * 4 + 2 * ((w & 1) ^ 1);
-    plo_off[rb] = phi_off[rb] + 64 * 4;
+    phi_off[rb] = ((rb * NCH + co) * 4 + ((w & 1) ^ 1)) * 64 + lane;
+    plo_off[rb] = phi_off[rb] + 128;
     asm volatile("" : "+v"(plo_off[rb]));
   }
 
@@ -480,20 +481,24 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           // partner half of the own chunk
-          const uint2 ph = *(const uint2*)(xr + phi_off[rb]);
+          const uint2 ph = ((const uint2*)xr)[phi_off[rb]];
           hq[rb].z = ph.x;
           hq[rb].w = ph.y;
           if constexpr (MATH != MATH_BF16) {
-            const uint2 pl = *(const uint2*)(xbuf[j & 1] + plo_off[rb]);
+            const uint2 pl = ((const uint2*)xbuf[j & 1])[plo_off[rb]];
             lq[rb].z = pl.x;
             lq[rb].w = pl.y;
           }
 #pragma unroll
           for (int i = 0; i < NCH - 1; ++i) {
             const int cc = i < co ? i : i + 1;
-            const int base = ((rb * NCH + cc) * 2) * 64 * 4 + lane * 4;
-            bh[rb * NOTH + i] = *(const uint4*)&xr[base];
-            if constexpr (MATH != MATH_BF16) bl[rb * NOTH + i] = *(const uint4*)&xr[base + 64 * 4];
+            const int base = (rb * NCH + cc) * 4 * 128 + lane * 2;
+            const uint2 h0 = *(const uint2*)&xr[base], h1 = *(const uint2*)&xr[base + 128];
+            bh[rb * NOTH + i] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+            if constexpr (MATH != MATH_BF16) {
+              const uint2 l0 = *(const uint2*)&xr[base + 256], l1 = *(const uint2*)&xr[base + 384];
+              bl[rb * NOTH + i] = make_uint4(l0.x, l0.y, l1.x, l1.y);
+            }
           }
         }
       }
