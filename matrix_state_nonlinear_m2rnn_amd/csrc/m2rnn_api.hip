@@ -226,7 +226,8 @@ BwdLayout bwd_layout(const m2rnn_dims* d) {
     return at;
   };
   L.ckpt = take((size_t)d->B * d->N * nseg * d->K * d->V * sizeof(float));
-  L.seg = take((size_t)d->B * d->N * S * kBwdSeg * (d->V / 16) * 64 * 8 * sizeof(float));
+  const long nsub = kBwdSeg / (d->V <= 32 ? BwdSub<32>::value : d->V == 64 ? BwdSub<64>::value : BwdSub<128>::value);
+  L.seg = take((size_t)d->B * d->N * S * nsub * 16 * d->V * sizeof(float));
   L.dv = take(S > 1 ? (size_t)S * d->B * d->T * d->N * d->V * sizeof(float) : 0);
   L.df = take(S > 1 ? (size_t)S * d->B * d->T * d->N * sizeof(float) : 0);
   L.dW = take((size_t)d->B * S * d->N * d->V * d->V * sizeof(float));
@@ -374,7 +375,7 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
     BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.dy = dy; a.dH_T = dH_T;
     a.ckpt = (const float*)(ws + L.ckpt);
-    a.seg_ws = (float*)(ws + L.seg);
+    a.subck = (float*)(ws + L.seg);
     a.dq = dq; a.dk = dk;
     a.dv = S > 1 ? (float*)(ws + L.dv) : dv;
     a.df = S > 1 ? (float*)(ws + L.df) : df;

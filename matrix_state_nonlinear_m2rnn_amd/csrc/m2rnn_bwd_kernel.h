@@ -7,17 +7,18 @@
 //     dW = sum_t H_{t-1}^T D_t,  dw_r = sum_t u_t (.) v_t,  dH_0 = C_0.
 //
 // Work decomposition (one 16-row block of one (b, n) pair per workgroup, wave w owns value
-// columns [16w, 16w+16), same register layout as the forward scan):
-//   for every 64-step segment, last to first:
-//     1. stage the segment's q, k, v, f, dy in LDS;
-//     2. recompute the segment forward from its checkpoint, writing each step's H_{t-1} (split
-//        fp16 hi/lo, the form that is exchanged anyway) and Z_t (fp32) to a per-workgroup
-//        workspace slice;
-//     3. walk the segment backwards: R, D and the row/column reductions in registers; D is
-//        published through LDS exactly like H in the forward, and the chain's D W^T runs on the
-//        split-precision MFMA; every wave transposes the D tiles it has just read (one MFMA per
-//        tile) and accumulates dW[own columns of H_{t-1}][all columns of D] with split-fp16 MFMAs.
-//   Per-workgroup partials of dv, df and dW are summed by separate, deterministic passes.
+// columns [16w, 16w+16), same register layout as the forward scan).  For every 64-step segment,
+// last to first:
+//   1. stage the segment's q, k, v, f, dy in LDS (a ragged last segment is padded with f = 1 and
+//      zero inputs, steps that leave the state and the chain exactly unchanged);
+//   2. pass A: run the forward from the segment's checkpoint, keeping the state that enters every
+//      SUB-step sub-segment;
+//   3. for every sub-segment, last to first: recompute it from its entry state, keeping each
+//      step's H_{t-1} (split fp16 hi/lo) and Z_t in LDS, then walk it backwards: R, D and the
+//      row/column partial sums in registers; D is published through LDS like H in the forward and
+//      the chain's D W^T runs on the split-precision MFMA; dW and dv read the H_{t-1} and D tiles
+//      transposed straight from LDS (ds_read_b64_tr_b16).
+// Per-workgroup partials of dv, df and dW are summed by separate, deterministic passes.
 #pragma once
 
 #include "m2rnn_fwd_kernel.h"
@@ -36,7 +37,7 @@ struct BwdArgs {
   const float* dy;
   const float* dH_T;
   const float* ckpt;   // [B][N][nseg][K][V] states entering each segment
-  float* seg_ws;       // per-workgroup segment store
+  float* subck;        // per-workgroup states entering each sub-segment
   float* dq;
   float* dk;
   float* dv;           // final dv (S == 1) or partials [S][B*T*N*V]
@@ -49,7 +50,7 @@ struct BwdArgs {
 };
 
 // Per-step stage record of the backward (fp32):
-//   [f, 1-f, -2(1-f), 0 | q (16) | c*k (16) | k (16) | v (V) | u (V)]
+//   [f, 0, 0, 0 | q (16) | c*k (16) | k (16) | v (V) | u (V)]   (slot 3 is a zero)
 template <int V>
 struct BwdStage {
   static constexpr int OQ = 4;
@@ -60,34 +61,44 @@ struct BwdStage {
   static constexpr int STEP = 52 + 2 * V;
 };
 
-// Loads the (up to) kBwdSeg steps [t0, t0 + n_steps) of one 16-row block into the stage.
+// Steps of a segment whose H_{t-1} and Z_t are held in LDS at once.
+template <int V>
+struct BwdSub {
+  static constexpr int value = V <= 32 ? 16 : (V == 64 ? 8 : 2);
+};
+
+// Loads steps [t0, t0 + n_steps) of one 16-row block into the stage; the records from n_steps up
+// to `n_pad` get f = 1 and zero q, k, v, u.
 template <int V, bool BF16IN>
 __device__ __forceinline__ void bwd_stage_segment(const BwdArgs& a, int b, int nh, int row0, int t0, int n_steps,
-                                                  float* stage, int tid, int nth) {
+                                                  int n_pad, float* stage, int tid, int nth) {
   using St = BwdStage<V>;
   const int esz = BF16IN ? 2 : 4;
   constexpr int VEC = BF16IN ? 8 : 4;
   // q, k: 16 values per step, VEC per load.
   constexpr int QV = 16 / VEC;
-  for (int i = tid; i < kBwdSeg * QV * 2; i += nth) {
-    const int which = i / (kBwdSeg * QV);  // 0 = q, 1 = k
-    const int r = i % (kBwdSeg * QV);
+  for (int i = tid; i < n_pad * QV * 2; i += nth) {
+    const int which = i / (n_pad * QV);  // 0 = q, 1 = k
+    const int r = i % (n_pad * QV);
     const int step = r / QV, cv = r % QV;
-    if (step >= n_steps) continue;
-    const long off = ((((long)b * a.T + t0 + step) * a.N + nh) * a.K + row0 + cv * VEC);
-    const void* src = which == 0 ? a.q : a.k;
-    const uint4 raw = *(const uint4*)((const char*)src + off * esz);
     float vals[VEC];
-    if constexpr (BF16IN) {
-      const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vals[2 * e] = bf16_lo_to_f32(wds[e]);
-        vals[2 * e + 1] = bf16_hi_to_f32(wds[e]);
+    for (int e = 0; e < VEC; ++e) vals[e] = 0.0f;
+    if (step < n_steps) {
+      const long off = ((((long)b * a.T + t0 + step) * a.N + nh) * a.K + row0 + cv * VEC);
+      const void* src = which == 0 ? a.q : a.k;
+      const uint4 raw = *(const uint4*)((const char*)src + off * esz);
+      if constexpr (BF16IN) {
+        const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vals[2 * e] = bf16_lo_to_f32(wds[e]);
+          vals[2 * e + 1] = bf16_hi_to_f32(wds[e]);
+        }
+      } else {
+        vals[0] = __uint_as_float(raw.x); vals[1] = __uint_as_float(raw.y);
+        vals[2] = __uint_as_float(raw.z); vals[3] = __uint_as_float(raw.w);
       }
-    } else {
-      vals[0] = __uint_as_float(raw.x); vals[1] = __uint_as_float(raw.y);
-      vals[2] = __uint_as_float(raw.z); vals[3] = __uint_as_float(raw.w);
     }
     float* d = stage + step * St::STEP;
 #pragma unroll
@@ -102,12 +113,16 @@ __device__ __forceinline__ void bwd_stage_segment(const BwdArgs& a, int b, int n
   }
   // v (dtype of the inputs) and u = dy (fp32): V values per step.
   constexpr int VV = V / VEC;
-  for (int i = tid; i < kBwdSeg * VV; i += nth) {
+  for (int i = tid; i < n_pad * VV; i += nth) {
     const int step = i / VV, cv = i % VV;
-    if (step >= n_steps) continue;
+    float* d = stage + step * St::STEP + St::OV + cv * VEC;
+    if (step >= n_steps) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) d[e] = 0.0f;
+      continue;
+    }
     const long off = (((long)b * a.T + t0 + step) * a.N + nh) * V + cv * VEC;
     const uint4 raw = *(const uint4*)((const char*)a.v + off * esz);
-    float* d = stage + step * St::STEP + St::OV + cv * VEC;
     if constexpr (BF16IN) {
       const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -120,18 +135,33 @@ __device__ __forceinline__ void bwd_stage_segment(const BwdArgs& a, int b, int n
     }
   }
   constexpr int UV = V / 4;
-  for (int i = tid; i < kBwdSeg * UV; i += nth) {
+  for (int i = tid; i < n_pad * UV; i += nth) {
     const int step = i / UV, cv = i % UV;
-    if (step >= n_steps) continue;
-    const long off = (((long)b * a.T + t0 + step) * a.N + nh) * V + cv * 4;
-    *(float4*)(stage + step * St::STEP + St::OU + cv * 4) = *(const float4*)(a.dy + off);
+    float4 u4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (step < n_steps) u4 = *(const float4*)(a.dy + (((long)b * a.T + t0 + step) * a.N + nh) * V + cv * 4);
+    *(float4*)(stage + step * St::STEP + St::OU + cv * 4) = u4;
   }
-  for (int i = tid; i < kBwdSeg; i += nth) {
-    if (i >= n_steps) continue;
-    const float fv = a.f[((long)b * a.T + t0 + i) * a.N + nh];
-    const float g = 1.0f - fv;
-    *(float4*)(stage + i * St::STEP) = make_float4(fv, g, -2.0f * g, 0.0f);
+  for (int i = tid; i < n_pad; i += nth) {
+    const float fv = i < n_steps ? a.f[((long)b * a.T + t0 + i) * a.N + nh] : 1.0f;
+    *(float4*)(stage + i * St::STEP) = make_float4(fv, 0.0f, 0.0f, 0.0f);
   }
+}
+
+// Slot (8-byte unit) of columns [4gam, 4gam + 4) of row rho in a 16x16 fp16 tile stored as 64 slots
+// (512 bytes).  The xor keeps three access patterns free of LDS bank conflicts: a lane (g, n)
+// writing or reading its own record (row n, group g), and the transposing read in which the 16
+// lanes of group g fetch rows 4g .. 4g+3 of all four column groups.
+__device__ __forceinline__ int tile_slot(int rho, int gam) { return 16 * gam + (rho ^ (4 * gam)); }
+
+// Transposing LDS read of a 16x16 fp16 tile stored with tile_slot: lane (g, i) supplies the slot of
+// row 4g + (i >> 2), columns 4(i & 3) ..; the 16 lanes of a group then receive column i of rows
+// 4g .. 4g+3, i.e. the 16x16x16 MFMA operand layout with the contraction index running over rows.
+__device__ __forceinline__ uint2 lds_read_tr(const uint32_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+  uint2 o;
+  __builtin_memcpy(&o, &r, sizeof(o));
+  return o;
 }
 
 template <int V, bool BF16IN>
@@ -139,13 +169,24 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   constexpr int NT = V / 16;
   constexpr int NTH = 64 * NT;
   constexpr int NCH = (NT + 1) / 2;
+  constexpr int NOTH = NCH > 1 ? NCH - 1 : 1;
+  constexpr int SUB = BwdSub<V>::value;
+  constexpr int NSUB = kBwdSeg / SUB;
+  constexpr bool GROUP4 = SUB % 4 == 0;  // dv reduced four steps at a time
+  constexpr int ENTRY = NT * 256;        // dwords of one step's split tiles (all waves)
   using St = BwdStage<V>;
-  constexpr int XWORDS = NCH * 2 * 64 * 4;
+  static_assert(kBwdSeg % SUB == 0 && SUB % 2 == 0, "sub-segments tile a segment");
 
   __shared__ __attribute__((aligned(16))) float stage[kBwdSeg * St::STEP];
-  __shared__ __attribute__((aligned(16))) uint32_t xbuf[2][XWORDS];
-  // Cross-wave partial sums of dq, dk (per row) and df, by step parity.
-  __shared__ float red_q[2][NT][16], red_k[2][NT][16], red_f[2][NT];
+  // H_{t-1} of the sub-segment's steps, split fp16: [SUB][NT tiles][hi|lo][64 slots][2 dwords].
+  // Pass A uses entries 0 and 1 as its exchange buffer.
+  __shared__ __attribute__((aligned(16))) uint32_t hst[SUB * ENTRY];
+  // Z_t of the sub-segment's steps: [SUB][NT][64 lanes][4 floats].
+  __shared__ __attribute__((aligned(16))) float zst[SUB * NT * 64 * 4];
+  // D_t exchange, by step parity: [2][NT tiles][hi|lo][64 slots][2 dwords].
+  __shared__ __attribute__((aligned(16))) uint32_t dx[2 * ENTRY];
+  // Per-wave partial sums of dq, dk (per row) and df over the sub-segment's steps.
+  __shared__ float red_q[SUB][NT][16], red_k[SUB][NT][16], red_f[SUB][NT];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -173,60 +214,127 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   // ---- operands of W ----
   // forward contraction: A = (c W)^T, A[m][k] = c W[k][16w + m]   (as in the forward scan)
   // backward chain:      A = W,       A[m][k] = W[16w + m][k]
+  // The chunk holding this wave's own tile takes that tile in k-slots 0..3 (from registers) and
+  // its partner tile w^1 in k-slots 4..7; the other chunks hold tiles 2cc, 2cc+1.
   const float* Wn = a.W + (long)nh * V * V;
   const int col = 16 * w + n;
-  uint4 fHi[NCH], fLo[NCH], bHi[NCH], bLo[NCH];
-#pragma unroll
-  for (int cc = 0; cc < NCH; ++cc) {
-    float fv[8], bv[8];
+  const int co = w >> 1;
+  auto wchunk = [&](int t_lo, int t_hi, bool fwd, uint4& hi, uint4& lo) {
+    float wv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int tile = 2 * cc + (i >> 2);
+      const int tile = (i >> 2) ? t_hi : t_lo;
       const int vin = 16 * tile + 4 * g + (i & 3);
-      fv[i] = tile < NT ? kTwoLog2e * Wn[vin * V + col] : 0.0f;
-      bv[i] = tile < NT ? Wn[col * V + vin] : 0.0f;
+      wv[i] = tile < NT ? (fwd ? kTwoLog2e * Wn[vin * V + col] : Wn[col * V + vin]) : 0.0f;
     }
-    uint32_t fh[4], fl[4], bh[4], bl[4];
+    uint32_t h[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      fh[i] = pack_f16(fv[2 * i], fv[2 * i + 1]);
-      fl[i] = pack_f16(fv[2 * i] - f16_lo_to_f32(fh[i]), fv[2 * i + 1] - f16_hi_to_f32(fh[i]));
-      bh[i] = pack_f16(bv[2 * i], bv[2 * i + 1]);
-      bl[i] = pack_f16(bv[2 * i] - f16_lo_to_f32(bh[i]), bv[2 * i + 1] - f16_hi_to_f32(bh[i]));
+      h[i] = pack_f16(wv[2 * i], wv[2 * i + 1]);
+      l[i] = pack_f16(wv[2 * i] - f16_lo_to_f32(h[i]), wv[2 * i + 1] - f16_hi_to_f32(h[i]));
     }
-    fHi[cc] = make_uint4(fh[0], fh[1], fh[2], fh[3]);
-    fLo[cc] = make_uint4(fl[0], fl[1], fl[2], fl[3]);
-    bHi[cc] = make_uint4(bh[0], bh[1], bh[2], bh[3]);
-    bLo[cc] = make_uint4(bl[0], bl[1], bl[2], bl[3]);
-  }
-  // Transposing-MFMA selector (see the forward readout).
-  uint4 bsel;
-  {
-    uint32_t e16[8];
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+  };
+  uint4 fOwnHi, fOwnLo, bOwnHi, bOwnLo, fOthHi[NOTH], fOthLo[NOTH], bOthHi[NOTH], bOthLo[NOTH];
+  wchunk(w, w ^ 1, true, fOwnHi, fOwnLo);
+  wchunk(w, w ^ 1, false, bOwnHi, bOwnLo);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) e16[e] = (n == 4 * g + (e & 3)) ? 0x3C00u : 0u;
-    bsel = make_uint4(e16[0] | (e16[1] << 16), e16[2] | (e16[3] << 16), e16[4] | (e16[5] << 16),
-                      e16[6] | (e16[7] << 16));
+  for (int i = 0; i < NCH - 1; ++i) {
+    const int cc = i < co ? i : i + 1;
+    wchunk(2 * cc, 2 * cc + 1, true, fOthHi[i], fOthLo[i]);
+    wchunk(2 * cc, 2 * cc + 1, false, bOthHi[i], bOthLo[i]);
   }
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  if constexpr (NT & 1) {
-    for (int i = tid; i < 2 * XWORDS; i += NTH) (&xbuf[0][0])[i] = 0u;
-  }
+  // Lane-constant slots: own record (row n, group g) and the transposing-read slot.
+  const int own_slot = tile_slot(n, g);
+  const int tr_slot = tile_slot(4 * g + (n >> 2), n & 3);
+  // Dword offset of (tile, hi|lo) within one entry of hst or dx.
+  auto tile_off = [](int tile, int hl) { return (tile * 2 + hl) * 128; };
+  constexpr bool has_partner = NT > 1;  // (with an even tile count every wave has one)
 
-  // Publishes a split tile (hi01, hi23, lo01, lo23) into exchange buffer `buf`.
-  auto publish = [&](int buf, const uint32_t (&hs)[4]) {
-    const int base = ((w >> 1) * 2) * 64 * 4 + lane * 4 + 2 * (w & 1);
-    *(uint2*)&xbuf[buf][base] = make_uint2(hs[0], hs[1]);
-    *(uint2*)&xbuf[buf][base + 64 * 4] = make_uint2(hs[2], hs[3]);
+  // Writes this wave's tile (split fp16) into `entry`; returns the split (own B-operand halves).
+  auto put_tile = [&](uint32_t* entry, const float (&x)[4], uint2& hi, uint2& lo) {
+    uint32_t h01, h23, l01, l23;
+    split_pair<MATH_F16X3>(x[0], x[1], h01, l01);
+    split_pair<MATH_F16X3>(x[2], x[3], h23, l23);
+    hi = make_uint2(h01, h23);
+    lo = make_uint2(l01, l23);
+    *(uint2*)(entry + tile_off(w, 0) + 2 * own_slot) = hi;
+    *(uint2*)(entry + tile_off(w, 1) + 2 * own_slot) = lo;
   };
-  auto split4 = [&](const float (&x)[4], uint32_t (&hs)[4]) {
-    split_pair<MATH_F16X3>(x[0], x[1], hs[0], hs[2]);
-    split_pair<MATH_F16X3>(x[2], x[3], hs[1], hs[3]);
+  // B operands of one contraction from a step's entry: the partner halves of the own chunk and the
+  // other chunks (the own halves come from registers).
+  struct Ops {
+    uint2 ph, pl;
+    uint4 oh[NOTH], ol[NOTH];
+  };
+  auto read_ops = [&](const uint32_t* entry) {
+    Ops o;
+    o.ph = o.pl = make_uint2(0, 0);
+    if constexpr (has_partner) {
+      o.ph = *(const uint2*)(entry + tile_off(w ^ 1, 0) + 2 * own_slot);
+      o.pl = *(const uint2*)(entry + tile_off(w ^ 1, 1) + 2 * own_slot);
+    }
+#pragma unroll
+    for (int i = 0; i < NCH - 1; ++i) {
+      const int cc = i < co ? i : i + 1;
+      const uint2 h0 = *(const uint2*)(entry + tile_off(2 * cc, 0) + 2 * own_slot);
+      const uint2 h1 = *(const uint2*)(entry + tile_off(2 * cc + 1, 0) + 2 * own_slot);
+      const uint2 l0 = *(const uint2*)(entry + tile_off(2 * cc, 1) + 2 * own_slot);
+      const uint2 l1 = *(const uint2*)(entry + tile_off(2 * cc + 1, 1) + 2 * own_slot);
+      o.oh[i] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+      o.ol[i] = make_uint4(l0.x, l0.y, l1.x, l1.y);
+    }
+    return o;
+  };
+  // acc += A B over all chunks (three split passes per chunk).
+  auto contract = [&](f32x4 acc, const uint4& AownHi, const uint4& AownLo, const uint4 (&AothHi)[NOTH],
+                      const uint4 (&AothLo)[NOTH], const uint2& own_hi, const uint2& own_lo, const Ops& o) {
+    const uint4 bh = make_uint4(own_hi.x, own_hi.y, o.ph.x, o.ph.y);
+    const uint4 bl = make_uint4(own_lo.x, own_lo.y, o.pl.x, o.pl.y);
+    acc = mfma_f16(AownHi, bh, acc);
+    acc = mfma_f16(AownLo, bh, acc);
+    acc = mfma_f16(AownHi, bl, acc);
+#pragma unroll
+    for (int i = 0; i < NCH - 1; ++i) {
+      acc = mfma_f16(AothHi[i], o.oh[i], acc);
+      acc = mfma_f16(AothLo[i], o.oh[i], acc);
+      acc = mfma_f16(AothHi[i], o.ol[i], acc);
+    }
+    return acc;
   };
 
-  // State of the chain, and H_t for dq (the state after the step being processed).
-  float C[4], Hc[4];
+  // One recompute step: reads H_{t-1} from `src` (own halves in hh, hl), advances H, returns Z_t,
+  // and publishes H_t's split into `dst` (if non-null), leaving its halves in hh, hl.
+  auto fwd_step = [&](const float* st, const uint32_t* src, uint32_t* dst, float (&H)[4], float (&Z)[4],
+                      uint2& hh, uint2& hl) {
+    const Ops o = read_ops(src);
+    const float av = st[g == 0 ? St::OV + 16 * w + n : 3];
+    const float bk = st[g == 0 ? St::OCK + n : 3];
+    __builtin_amdgcn_sched_barrier(0);
+    const float f = st[0], g1 = 1.0f - f, m2g = -2.0f * g1;
+    f32x4 acc = contract(mfma_f32(av, bk, zero4), fOwnHi, fOwnLo, fOthHi, fOthLo, hh, hl, o);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float rr = tanh_recip(acc[r]);
+      Z[r] = __builtin_fmaf(-2.0f, rr, 1.0f);
+      H[r] = __builtin_fmaf(m2g, rr, __builtin_fmaf(f, H[r], g1));
+    }
+    if (dst) {
+      put_tile(dst, H, hh, hl);
+    } else {
+      uint32_t h01, h23, l01, l23;
+      split_pair<MATH_F16X3>(H[0], H[1], h01, l01);
+      split_pair<MATH_F16X3>(H[2], H[3], h23, l23);
+      hh = make_uint2(h01, h23);
+      hl = make_uint2(l01, l23);
+    }
+  };
+
+  // State of the chain.
+  float C[4];
   const long own_off = ((long)b * a.N + nh) * KV + (long)(row0 + n) * V + 16 * w + 4 * g;
   if (a.dH_T) {
     const float4 c4 = *(const float4*)(a.dH_T + own_off);
@@ -234,214 +342,264 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   } else {
     C[0] = C[1] = C[2] = C[3] = 0.0f;
   }
-  Hc[0] = Hc[1] = Hc[2] = Hc[3] = 0.0f;
   f32x4 dWacc[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) dWacc[tt] = zero4;
 
-  // Per-workgroup segment store: [kBwdSeg][NT waves][64 lanes][8 words] = (H_{t-1} split, Z).
-  float* segs = a.seg_ws + (long)wg * kBwdSeg * NT * 64 * 8 + ((long)w * 64 + lane) * 8;
-  constexpr long SEG_STEP = (long)NT * 64 * 8;
+  // Per-workgroup scratch of the states entering sub-segments 1 .. NSUB-1: [NSUB][16 rows][V].
+  float* subck = a.subck + (long)wg * NSUB * 16 * V + (long)n * V + 16 * w + 4 * g;
 
+  // dv goes through a buffer resource that ends at the last valid step of this (b, n), so the
+  // stores of padded steps are dropped (see the forward's y stores).
   const long plane = (long)a.B * a.T * a.N * V;
-  float* dv_dst = a.dv + (a.S > 1 ? (long)s * plane : 0);
-  float* df_dst = a.df + (a.S > 1 ? (long)s * a.B * a.T * a.N : 0);
+  float* dv_base = a.dv + (a.S > 1 ? (long)s * plane : 0) + ((long)b * a.T * a.N + nh) * V;  // [b, 0, nh, 0]
+  const __amdgpu_buffer_rsrc_t dvres =
+      __builtin_amdgcn_make_buffer_rsrc(dv_base, (short)0, (a.T * a.N - nh) * V * 4, kBufferRsrcWord3);
+  const int ystep = a.N * V;
+  // Byte offset of this lane's dv element at step 0 (grouped: step g), column 16w + n.
+  const uint32_t dv_lane = (uint32_t)(((GROUP4 ? g * ystep : 0) + 16 * w + n) * 4);
   const float wr_col = a.S == 1 ? a.w_r[(long)nh * V + 16 * w + n] : 0.0f;  // for dv's w_r (.) u term
-  float dwr = 0.0f;  // dw_r[16w + n] partial over this batch entry (workgroups with s == 0, lanes g == 0)
+  float* df_dst = a.df + (a.S > 1 ? (long)s * a.B * a.T * a.N : 0);
+  // dw_r[16w + 4g + r] partial over this batch entry (every lane of a row group holds the same sums;
+  // the workgroups with s == 0 write them).
+  float dwr4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  // dq, dk, df of the sub-segment's steps [tb, tb + SUB) from the per-wave partials.
+  auto finalize = [&](int tb) {
+    for (int i = tid; i < SUB * 16 * 2 + SUB; i += NTH) {
+      if (i < SUB * 32) {
+        const int which = i / (SUB * 16), j = (i / 16) % SUB, row = i % 16;
+        const int t = tb + j;
+        float acc = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NT; ++ww) acc += which == 0 ? red_q[j][ww][row] : red_k[j][ww][row];
+        if (t < a.T) (which == 0 ? a.dq : a.dk)[(((long)b * a.T + t) * a.N + nh) * a.K + row0 + row] = acc;
+      } else {
+        const int j = i - SUB * 32;
+        const int t = tb + j;
+        float acc = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NT; ++ww) acc += red_f[j][ww];
+        if (t < a.T) df_dst[((long)b * a.T + t) * a.N + nh] = acc;
+      }
+    }
+  };
+
+  float xq[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // dv partials of the current group of four steps
+  int pending_tb = -1;                     // sub-segment whose dq, dk, df await finalize
 
   for (int seg = nseg - 1; seg >= 0; --seg) {
     const int t0 = seg * kBwdSeg;
     const int nst = min(kBwdSeg, a.T - t0);
+    const int nsub = (nst + SUB - 1) / SUB;
     lds_barrier();  // the previous segment's readers are done with the stage
-    bwd_stage_segment<V, BF16IN>(a, b, nh, row0, t0, nst, stage, tid, NTH);
+    if (pending_tb >= 0) finalize(pending_tb);
+    pending_tb = -1;
+    bwd_stage_segment<V, BF16IN>(a, b, nh, row0, t0, nst, nsub * SUB, stage, tid, NTH);
 
-    // ---------------- 1. recompute the segment forward ----------------
+    const float* ck = a.ckpt + ((long)u * nseg + seg) * KV + (long)(row0 + n) * V + 16 * w + 4 * g;
     float H[4];
     {
-      const float4 h4 = *(const float4*)(a.ckpt + ((long)u * nseg + seg) * KV + (long)(row0 + n) * V + 16 * w + 4 * g);
+      const float4 h4 = *(const float4*)ck;
       H[0] = h4.x; H[1] = h4.y; H[2] = h4.z; H[3] = h4.w;
     }
-    uint32_t hs[4];
-    split4(H, hs);
-    publish(0, hs);
-    lds_barrier();
-    for (int j = 0; j < nst; ++j) {
-      const float* st = stage + j * St::STEP;
-      const float4 fg = *(const float4*)st;
-      const float av = g == 0 ? st[St::OV + 16 * w + n] : 0.0f;
-      const float bk = g == 0 ? st[St::OCK + n] : 0.0f;
-      f32x4 acc = mfma_f32(av, bk, zero4);
-      const uint32_t* xr = xbuf[j & 1];
-#pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
-        const uint4 bh = *(const uint4*)&xr[(cc * 2) * 64 * 4 + lane * 4];
-        const uint4 bl = *(const uint4*)&xr[(cc * 2 + 1) * 64 * 4 + lane * 4];
-        acc = mfma_f16(fHi[cc], bh, acc);
-        acc = mfma_f16(fLo[cc], bh, acc);
-        acc = mfma_f16(fHi[cc], bl, acc);
-      }
-      float Z[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float rr = tanh_recip(acc[r]);
-        Z[r] = __builtin_fmaf(-2.0f, rr, 1.0f);
-        H[r] = __builtin_fmaf(fg.z, rr, __builtin_fmaf(fg.x, H[r], fg.y));
-      }
-      // Store H_{t-1} (split) and Z_t for the reverse walk.
-      *(uint4*)(segs + j * SEG_STEP) = make_uint4(hs[0], hs[1], hs[2], hs[3]);
-      *(float4*)(segs + j * SEG_STEP + 4) = make_float4(Z[0], Z[1], Z[2], Z[3]);
-      split4(H, hs);
-      publish((j + 1) & 1, hs);
+
+    // ---------------- pass A: forward up to the last sub-segment ----------------
+    if (nsub > 1) {
+      uint2 hh, hl;
+      put_tile(hst, H, hh, hl);
       lds_barrier();
-    }
-    if (seg == nseg - 1) {
-      // H_T: the state after the last step, for dq_{T-1}.
-      Hc[0] = H[0]; Hc[1] = H[1]; Hc[2] = H[2]; Hc[3] = H[3];
-    }
-    __threadfence_block();  // the segment store is read back by the same lanes below
-
-    // ---------------- 2. walk the segment backwards ----------------
-    // The segment store is read two steps ahead of use (its latency is that of L2 / HBM).
-    uint4 nh0 = *(const uint4*)(segs + (nst - 1) * SEG_STEP);
-    float4 nz0 = *(const float4*)(segs + (nst - 1) * SEG_STEP + 4);
-    uint4 nh1 = make_uint4(0, 0, 0, 0);
-    float4 nz1 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (nst >= 2) {
-      nh1 = *(const uint4*)(segs + (nst - 2) * SEG_STEP);
-      nz1 = *(const float4*)(segs + (nst - 2) * SEG_STEP + 4);
-    }
-    for (int j = nst - 1; j >= 0; --j) {
-      const int t = t0 + j;
-      const float* st = stage + j * St::STEP;
-      const float4 fg = *(const float4*)st;
-      const float qn = st[St::OQ + n];
-      const float4 u4 = *(const float4*)(st + St::OU + 16 * w + 4 * g);
-      const float4 v4 = *(const float4*)(st + St::OV + 16 * w + 4 * g);
-      const uint4 hsp = nh0;  // H_{t-1} split
-      const float4 z4 = nz0;
-      nh0 = nh1;
-      nz0 = nz1;
-      if (j >= 2) {
-        nh1 = *(const uint4*)(segs + (j - 2) * SEG_STEP);
-        nz1 = *(const float4*)(segs + (j - 2) * SEG_STEP + 4);
-      }
-      if (s == 0 && g == 0) dwr = __builtin_fmaf(st[St::OU + 16 * w + n], st[St::OV + 16 * w + n], dwr);
-      const float Z[4] = {z4.x, z4.y, z4.z, z4.w};
-      const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
-      const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-      float Hp[4];
-      Hp[0] = f16_lo_to_f32(hsp.x) + f16_lo_to_f32(hsp.z);
-      Hp[1] = f16_hi_to_f32(hsp.x) + f16_hi_to_f32(hsp.z);
-      Hp[2] = f16_lo_to_f32(hsp.y) + f16_lo_to_f32(hsp.w);
-      Hp[3] = f16_hi_to_f32(hsp.y) + f16_hi_to_f32(hsp.w);
-
-      float R[4], D[4], cinit[4];
-      float dq_l = 0.0f, dk_l = 0.0f, df_l = 0.0f;
+      for (int m = 0; m < nsub - 1; ++m) {
+        if (m > 0) *(float4*)(subck + (long)m * 16 * V) = make_float4(H[0], H[1], H[2], H[3]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        R[r] = __builtin_fmaf(qn, uu[r], C[r]);
-        D[r] = (fg.y * R[r]) * __builtin_fmaf(-Z[r], Z[r], 1.0f);
-        df_l = __builtin_fmaf(R[r], Hp[r] - Z[r], df_l);
-        dq_l = __builtin_fmaf(Hc[r], uu[r], dq_l);
-        dk_l = __builtin_fmaf(D[r], vv[r], dk_l);
-        cinit[r] = fg.x * R[r];
-      }
-      // Row sums over this wave's 16 columns (the four lane rows), then one slot per wave.
-      dq_l = sum_rows4(dq_l);
-      dk_l = sum_rows4(dk_l);
-      df_l = sum_rows4(df_l);
-      // df also sums over the 16 rows (lanes of a row).
-      df_l += dpp<kDppRowMirror>(df_l);
-      df_l += dpp<kDppRowHalfMirror>(df_l);
-      df_l += dpp<kDppQuadXor1>(df_l);
-      df_l += dpp<kDppQuadXor2>(df_l);
-      const int par = j & 1;
-      if (g == 0) {
-        red_q[par][w][n] = dq_l;
-        red_k[par][w][n] = dk_l;
-        if (n == 0) red_f[par][w] = df_l;
-      }
-      uint32_t ds[4];
-      split4(D, ds);
-      publish(par, ds);
-      lds_barrier();
-
-      // Completed row sums of dq, dk and the step's df.
-      if (w == 0 && g == 0) {
-        float sq = 0.0f, sk = 0.0f;
-#pragma unroll
-        for (int ww = 0; ww < NT; ++ww) {
-          sq += red_q[par][ww][n];
-          sk += red_k[par][ww][n];
-        }
-        const long qk = (((long)b * a.T + t) * a.N + nh) * a.K + row0 + n;
-        a.dq[qk] = sq;
-        a.dk[qk] = sk;
-        if (n == 0) {
-          float sf = 0.0f;
-#pragma unroll
-          for (int ww = 0; ww < NT; ++ww) sf += red_f[par][ww];
-          df_dst[((long)b * a.T + t) * a.N + nh] = sf;
+        for (int j = 0; j < SUB; ++j) {
+          float Z[4];
+          fwd_step(stage + (m * SUB + j) * St::STEP, hst + (j & 1) * ENTRY, hst + ((j + 1) & 1) * ENTRY, H, Z, hh,
+                   hl);
+          lds_barrier();
         }
       }
+      __threadfence_block();  // the scratch states are read back by the same lanes below
+    }
 
-      // Chain: C_{t-1} = f R + D W^T, on the split-precision MFMA; and the transposes of the
-      // D tiles for dW and dv.
-      const uint32_t* xr = xbuf[par];
-      f32x4 acc = {cinit[0], cinit[1], cinit[2], cinit[3]};
-      f32x4 dT[NT];
-#pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
-        const uint4 bh = *(const uint4*)&xr[(cc * 2) * 64 * 4 + lane * 4];
-        const uint4 bl = *(const uint4*)&xr[(cc * 2 + 1) * 64 * 4 + lane * 4];
-        acc = mfma_f16(bHi[cc], bh, acc);
-        acc = mfma_f16(bLo[cc], bh, acc);
-        acc = mfma_f16(bHi[cc], bl, acc);
-        dT[2 * cc] = mfma_f16(make_uint4(bh.x, bh.y, bl.x, bl.y), bsel, zero4);
-        if (2 * cc + 1 < NT) dT[2 * cc + 1] = mfma_f16(make_uint4(bh.z, bh.w, bl.z, bl.w), bsel, zero4);
+    // ---------------- sub-segments, last to first ----------------
+    float4 nextH = make_float4(0.0f, 0.0f, 0.0f, 0.0f);  // prefetched state entering sub-segment m - 1
+    for (int m = nsub - 1; m >= 0; --m) {
+      const int jb = m * SUB;
+      if (m < nsub - 1) {
+        H[0] = nextH.x; H[1] = nextH.y; H[2] = nextH.z; H[3] = nextH.w;
       }
-      // Transposed own H_{t-1} tile: hT at lane (g, m) reg r = H_{t-1}[row 4g + r][col 16w + m].
-      const f32x4 hT = mfma_f16(hsp, bsel, zero4);
-      // dW[16w + m][16tt + j] += sum_rows H_{t-1}[row][16w + m] D[row][16tt + j]: one 16x16x16
-      // MFMA per split term, A = hT (k = row), B = dT[tt] (k = row), both re-split to fp16 hi/lo.
-      uint32_t th[4];
-      split_pair<MATH_F16X3>(hT[0], hT[1], th[0], th[2]);
-      split_pair<MATH_F16X3>(hT[2], hT[3], th[1], th[3]);
-      const uint2 hThi = make_uint2(th[0], th[1]), hTlo = make_uint2(th[2], th[3]);
+      if (m > 0) nextH = *(const float4*)(m - 1 > 0 ? subck + (long)(m - 1) * 16 * V : ck);
+
+      // 1. Recompute the sub-segment: hst[j] = H_{t-1} (split), zst[j] = Z_t.
+      lds_barrier();  // the previous walk is done with hst, zst and the partial sums
+      if (pending_tb >= 0) finalize(pending_tb);
+      pending_tb = t0 + jb;
+      uint2 hh, hl;
+      put_tile(hst, H, hh, hl);
+      lds_barrier();
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        uint32_t dd[4];
-        split_pair<MATH_F16X3>(dT[tt][0], dT[tt][1], dd[0], dd[2]);
-        split_pair<MATH_F16X3>(dT[tt][2], dT[tt][3], dd[1], dd[3]);
-        const uint2 dhi = make_uint2(dd[0], dd[1]), dlo = make_uint2(dd[2], dd[3]);
-        dWacc[tt] = mfma16_f16(hThi, dhi, dWacc[tt]);
-        dWacc[tt] = mfma16_f16(hTlo, dhi, dWacc[tt]);
-        dWacc[tt] = mfma16_f16(hThi, dlo, dWacc[tt]);
+      for (int j = 0; j < SUB; ++j) {
+        float Z[4];
+        const float* st = stage + (jb + j) * St::STEP;
+        fwd_step(st, hst + j * ENTRY, j + 1 < SUB ? hst + (j + 1) * ENTRY : nullptr, H, Z, hh, hl);
+        *(float4*)(zst + ((j * NT + w) * 64 + lane) * 4) = make_float4(Z[0], Z[1], Z[2], Z[3]);
+        __builtin_amdgcn_sched_barrier(0);
+        // dq_t = H_t u_t (row sums over this wave's 16 columns) needs no backward quantity: it is
+        // formed here, in the shadow of the writes above.
+        const float4 u4 = *(const float4*)(st + St::OU + 16 * w + 4 * g);
+        float dq_l = H[0] * u4.x;
+        dq_l = __builtin_fmaf(H[1], u4.y, dq_l);
+        dq_l = __builtin_fmaf(H[2], u4.z, dq_l);
+        dq_l = __builtin_fmaf(H[3], u4.w, dq_l);
+        dq_l = sum_rows4(dq_l);
+        if (g == 0) red_q[j][w][n] = dq_l;
+        lds_barrier();
       }
-      // dv[col 16w + j] = sum_rows D[row][col] k[row] (+ w_r u when this workgroup holds all rows).
-      {
+
+      // 2. Walk the sub-segment backwards, software-pipelined: the inputs of step j-1 are read right
+      //    after step j's barrier together with step j's exchange reads, and iteration j ends with
+      //    step j-1's R, D and publish (which wait for step j's chain MFMAs).
+      struct RevIn {
+        float f, qn;
+        float4 u4, v4, z4;
+        uint2 h_hi, h_lo;
+      };
+      auto load_rev = [&](int j) {
+        RevIn in;
+        const float* st = stage + (jb + j) * St::STEP;
+        const uint32_t* hj = hst + j * ENTRY;
+        in.f = st[0];
+        in.qn = st[St::OQ + n];
+        in.u4 = *(const float4*)(st + St::OU + 16 * w + 4 * g);
+        in.v4 = *(const float4*)(st + St::OV + 16 * w + 4 * g);
+        in.h_hi = *(const uint2*)(hj + tile_off(w, 0) + 2 * own_slot);
+        in.h_lo = *(const uint2*)(hj + tile_off(w, 1) + 2 * own_slot);
+        in.z4 = *(const float4*)(zst + ((j * NT + w) * 64 + lane) * 4);
+        return in;
+      };
+      struct RevFront {
+        uint2 dh, dl;   // own split D tile (own halves of the chain's B operand)
+        float cinit[4]; // f R
+        float dk_l, df_l;
+      };
+      // R, D of step j (the chain's critical path), published at once; then f R and the per-lane
+      // partial sums of dk, df and dw_r in the shadow of that write.
+      auto front = [&](int j, const RevIn& in) {
+        RevFront fr;
+        const float Z[4] = {in.z4.x, in.z4.y, in.z4.z, in.z4.w};
+        const float uu[4] = {in.u4.x, in.u4.y, in.u4.z, in.u4.w};
+        const float vv[4] = {in.v4.x, in.v4.y, in.v4.z, in.v4.w};
+        const float g1 = 1.0f - in.f;
+        float R[4], D[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          R[r] = __builtin_fmaf(in.qn, uu[r], C[r]);
+          D[r] = (g1 * R[r]) * __builtin_fmaf(-Z[r], Z[r], 1.0f);
+        }
+        put_tile(dx + (j & 1) * ENTRY, D, fr.dh, fr.dl);
+        __builtin_amdgcn_sched_barrier(0);
+        float Hp[4];  // H_{t-1}
+        Hp[0] = f16_lo_to_f32(in.h_hi.x) + f16_lo_to_f32(in.h_lo.x);
+        Hp[1] = f16_hi_to_f32(in.h_hi.x) + f16_hi_to_f32(in.h_lo.x);
+        Hp[2] = f16_lo_to_f32(in.h_hi.y) + f16_lo_to_f32(in.h_lo.y);
+        Hp[3] = f16_hi_to_f32(in.h_hi.y) + f16_hi_to_f32(in.h_lo.y);
+        fr.dk_l = fr.df_l = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          fr.cinit[r] = in.f * R[r];
+          fr.df_l = __builtin_fmaf(R[r], Hp[r] - Z[r], fr.df_l);
+          fr.dk_l = __builtin_fmaf(D[r], vv[r], fr.dk_l);
+          dwr4[r] = __builtin_fmaf(uu[r], vv[r], dwr4[r]);
+        }
+        return fr;
+      };
+
+      RevIn nxt = load_rev(SUB - 1);
+      RevFront fr = front(SUB - 1, nxt);
+#pragma unroll
+      for (int j = SUB - 1; j >= 0; --j) {
+        const int js = jb + j;
+        const float* st = stage + js * St::STEP;
+        const uint32_t* hj = hst + j * ENTRY;
+        const uint32_t* dxp = dx + (j & 1) * ENTRY;
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+
+        // Step j's exchange reads (chain operands, transposed tiles for dW and dv), and step j-1's
+        // inputs.
+        const Ops o = read_ops(dxp);
+        const uint2 hT = lds_read_tr(hj + tile_off(w, 0) + 2 * tr_slot);
+        uint2 dT[NT], dThi = make_uint2(0, 0);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          dT[tt] = lds_read_tr(dxp + tile_off(tt, 0) + 2 * tr_slot);
+          if (tt == w) dThi = dT[tt];  // (a select: indexing dT by w would put dT in memory)
+        }
+        const uint2 dTlo = lds_read_tr(dxp + tile_off(w, 1) + 2 * tr_slot);
         const float4 k4 = *(const float4*)(st + St::OK + 4 * g);
-        const f32x4 dTo = dT[w];
-        float x = k4.x * dTo[0];
-        x = __builtin_fmaf(k4.y, dTo[1], x);
-        x = __builtin_fmaf(k4.z, dTo[2], x);
-        x = __builtin_fmaf(k4.w, dTo[3], x);
-        x = sum_rows4(x);
+        if (j > 0) nxt = load_rev(j - 1);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Chain: C_{t-1} = f R + D W^T on the split-precision MFMA.
+        const f32x4 acc =
+            contract(f32x4{fr.cinit[0], fr.cinit[1], fr.cinit[2], fr.cinit[3]}, bOwnHi, bOwnLo, bOthHi, bOthLo,
+                     fr.dh, fr.dl, o);
+
+        // Off the chain, while the MFMAs run.  dk, df: sums over this wave's 16 columns (the four
+        // lane rows); df also over the 16 rows.
+        float dk_l = sum_rows4(fr.dk_l);
+        float df_l = sum_rows4(fr.df_l);
+        df_l += dpp<kDppRowMirror>(df_l);
+        df_l += dpp<kDppRowHalfMirror>(df_l);
+        df_l += dpp<kDppQuadXor1>(df_l);
+        df_l += dpp<kDppQuadXor2>(df_l);
         if (g == 0) {
-          const float ucol = st[St::OU + 16 * w + n];
-          dv_dst[(((long)b * a.T + t) * a.N + nh) * V + 16 * w + n] = __builtin_fmaf(wr_col, ucol, x);
+          red_k[j][w][n] = dk_l;
+          if (n == 0) red_f[j][w] = df_l;
         }
-      }
+
+        // dW[16w + m][16tt + j] += sum_rows H_{t-1}[row][16w + m] D[row][16tt + j]: one fp16 16x16x16
+        // MFMA per D tile, both operands read transposed from LDS (rows on the contraction index).
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        C[r] = acc[r];
-        Hc[r] = Hp[r];
+        for (int tt = 0; tt < NT; ++tt) dWacc[tt] = mfma16_f16(hT, dT[tt], dWacc[tt]);
+
+        // dv[col 16w + i] = sum_rows D[row][col] k[row] (+ w_r u when this workgroup holds all rows).
+        float x = k4.x * (f16_lo_to_f32(dThi.x) + f16_lo_to_f32(dTlo.x));
+        x = __builtin_fmaf(k4.y, f16_hi_to_f32(dThi.x) + f16_hi_to_f32(dTlo.x), x);
+        x = __builtin_fmaf(k4.z, f16_lo_to_f32(dThi.y) + f16_lo_to_f32(dTlo.y), x);
+        x = __builtin_fmaf(k4.w, f16_hi_to_f32(dThi.y) + f16_hi_to_f32(dTlo.y), x);
+        if constexpr (GROUP4) {
+          // Steps jb + (j & ~3) + q are collected in xq[q]; one cross-row reduction of the four
+          // leaves lane (g, i) with dv[step jb + (j & ~3) + g][16w + i].
+          xq[j & 3] = x;
+          if ((j & 3) == 0) {
+            float dvv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
+            const float ucol = stage[(jb + j + g) * St::STEP + St::OU + 16 * w + n];
+            dvv = __builtin_fmaf(wr_col, ucol, dvv);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv), dvres,
+                                                  dv_lane + (uint32_t)((t0 + js) * ystep * 4), 0, 0);
+          }
+        } else {
+          x = sum_rows4(x);
+          const float ucol = st[St::OU + 16 * w + n];
+          const float dvv = __builtin_fmaf(wr_col, ucol, x);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv), dvres,
+                                                g == 0 ? dv_lane + (uint32_t)((t0 + js) * ystep * 4) : kBufferDrop, 0,
+                                                0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) C[r] = acc[r];
+        if (j > 0) fr = front(j - 1, nxt);
       }
     }
   }
+  lds_barrier();
+  if (pending_tb >= 0) finalize(pending_tb);
 
   if (a.dH0) *(float4*)(a.dH0 + own_off) = make_float4(C[0], C[1], C[2], C[3]);
-  if (s == 0 && g == 0) a.dwr_part[((long)b * a.N + nh) * V + 16 * w + n] = dwr;
+  if (s == 0 && n == 0)
+    *(float4*)(a.dwr_part + ((long)b * a.N + nh) * V + 16 * w + 4 * g) = make_float4(dwr4[0], dwr4[1], dwr4[2], dwr4[3]);
   // dW partial of this workgroup: dWacc[tt] at lane (g, j) reg r = dW[16w + 4g + r][16tt + j].
   float* dWp = a.dW_part + ((long)(b * a.S + s) * a.N + nh) * V * V;
 #pragma unroll
