@@ -306,16 +306,25 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     return acc;
   };
 
-  // One recompute step: reads H_{t-1} from `src` (own halves in hh, hl), advances H, returns Z_t,
-  // and publishes H_t's split into `dst` (if non-null), leaving its halves in hh, hl.
-  auto fwd_step = [&](const float* st, const uint32_t* src, uint32_t* dst, float (&H)[4], float (&Z)[4],
-                      uint2& hh, uint2& hl) {
+  // Rank-1 term (c k_t) v_t^T of the step whose stage record is `st`.
+  auto rank1 = [&](const float* st) {
+    return mfma_f32(st[g == 0 ? St::OV + 16 * w + n : 3], st[g == 0 ? St::OCK + n : 3], zero4);
+  };
+  // One recompute step: reads H_{t-1} from `src` (own halves in hh, hl), adds the contraction to
+  // the rank-1 term kv, advances H, returns Z_t, and publishes H_t's split into `dst` (if
+  // non-null), leaving its halves in hh, hl.  Ends with the next step's rank-1 MFMA (record
+  // `st_next`, if non-null), issued before the caller's barrier.
+  auto fwd_step = [&](const float* st, const float* st_next, const uint32_t* src, uint32_t* dst, f32x4& kv,
+                      float (&H)[4], float (&Z)[4], uint2& hh, uint2& hl) {
     const Ops o = read_ops(src);
-    const float av = st[g == 0 ? St::OV + 16 * w + n : 3];
-    const float bk = st[g == 0 ? St::OCK + n : 3];
+    float avn = 0.0f, bkn = 0.0f;
+    if (st_next) {
+      avn = st_next[g == 0 ? St::OV + 16 * w + n : 3];
+      bkn = st_next[g == 0 ? St::OCK + n : 3];
+    }
     __builtin_amdgcn_sched_barrier(0);
     const float f = st[0], g1 = 1.0f - f, m2g = -2.0f * g1;
-    f32x4 acc = contract(mfma_f32(av, bk, zero4), fOwnHi, fOwnLo, fOthHi, fOthLo, hh, hl, o);
+    f32x4 acc = contract(kv, fOwnHi, fOwnLo, fOthHi, fOthLo, hh, hl, o);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float rr = tanh_recip(acc[r]);
@@ -331,6 +340,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       hh = make_uint2(h01, h23);
       hl = make_uint2(l01, l23);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (st_next) kv = mfma_f32(avn, bkn, zero4);
   };
 
   // State of the chain.
@@ -408,14 +419,15 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     if (nsub > 1) {
       uint2 hh, hl;
       put_tile(hst, H, hh, hl);
-      lds_barrier();
+      lds_barrier();  // (also makes the stage written above visible)
+      f32x4 kv = rank1(stage);
       for (int m = 0; m < nsub - 1; ++m) {
         if (m > 0) *(float4*)(subck + (long)m * 16 * V) = make_float4(H[0], H[1], H[2], H[3]);
 #pragma unroll
         for (int j = 0; j < SUB; ++j) {
           float Z[4];
-          fwd_step(stage + (m * SUB + j) * St::STEP, hst + (j & 1) * ENTRY, hst + ((j + 1) & 1) * ENTRY, H, Z, hh,
-                   hl);
+          const float* st = stage + (m * SUB + j) * St::STEP;
+          fwd_step(st, st + St::STEP, hst + (j & 1) * ENTRY, hst + ((j + 1) & 1) * ENTRY, kv, H, Z, hh, hl);
           lds_barrier();
         }
       }
@@ -437,12 +449,14 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       pending_tb = t0 + jb;
       uint2 hh, hl;
       put_tile(hst, H, hh, hl);
+      f32x4 kv = rank1(stage + jb * St::STEP);  // (the stage is complete: barriers since it was written)
       lds_barrier();
 #pragma unroll
       for (int j = 0; j < SUB; ++j) {
         float Z[4];
         const float* st = stage + (jb + j) * St::STEP;
-        fwd_step(st, hst + j * ENTRY, j + 1 < SUB ? hst + (j + 1) * ENTRY : nullptr, H, Z, hh, hl);
+        fwd_step(st, j + 1 < SUB ? st + St::STEP : nullptr, hst + j * ENTRY,
+                 j + 1 < SUB ? hst + (j + 1) * ENTRY : nullptr, kv, H, Z, hh, hl);
         *(float4*)(zst + ((j * NT + w) * 64 + lane) * 4) = make_float4(Z[0], Z[1], Z[2], Z[3]);
         __builtin_amdgcn_sched_barrier(0);
         // dq_t = H_t u_t (row sums over this wave's 16 columns) needs no backward quantity: it is
@@ -546,6 +560,11 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
             contract(f32x4{fr.cinit[0], fr.cinit[1], fr.cinit[2], fr.cinit[3]}, bOwnHi, bOwnLo, bOthHi, bOthLo,
                      fr.dh, fr.dl, o);
 
+        // dW[16w + m][16tt + j] += sum_rows H_{t-1}[row][16w + m] D[row][16tt + j]: one fp16 16x16x16
+        // MFMA per D tile, both operands read transposed from LDS (rows on the contraction index).
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) dWacc[tt] = mfma16_f16(hT, dT[tt], dWacc[tt]);
+
         // Off the chain, while the MFMAs run.  dk, df: sums over this wave's 16 columns (the four
         // lane rows); df also over the 16 rows.
         float dk_l = sum_rows4(fr.dk_l);
@@ -559,10 +578,10 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
           if (n == 0) red_f[j][w] = df_l;
         }
 
-        // dW[16w + m][16tt + j] += sum_rows H_{t-1}[row][16w + m] D[row][16tt + j]: one fp16 16x16x16
-        // MFMA per D tile, both operands read transposed from LDS (rows on the contraction index).
+        // Step j-1's R, D and publish as soon as the chain has produced C.
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) dWacc[tt] = mfma16_f16(hT, dT[tt], dWacc[tt]);
+        for (int r = 0; r < 4; ++r) C[r] = acc[r];
+        if (j > 0) fr = front(j - 1, nxt);
 
         // dv[col 16w + i] = sum_rows D[row][col] k[row] (+ w_r u when this workgroup holds all rows).
         float x = k4.x * (f16_lo_to_f32(dThi.x) + f16_lo_to_f32(dTlo.x));
@@ -588,9 +607,6 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
                                                 g == 0 ? dv_lane + (uint32_t)((t0 + js) * ystep * 4) : kBufferDrop, 0,
                                                 0);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) C[r] = acc[r];
-        if (j > 0) fr = front(j - 1, nxt);
       }
     }
   }
