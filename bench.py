@@ -31,10 +31,17 @@ KERNEL_SOURCES = ["m2rnn_device.h", "m2rnn_fwd_kernel.h"]
 
 
 def kernel_hash() -> str:
+    """Hash of the forward kernel's sources with comments and blank lines removed: a counter
+    summary stays valid across edits of comments, and goes stale with any change of code."""
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "matrix_state_nonlinear_m2rnn_amd", "csrc", name), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "matrix_state_nonlinear_m2rnn_amd", "csrc", name)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].strip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

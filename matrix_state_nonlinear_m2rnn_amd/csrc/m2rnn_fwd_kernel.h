@@ -13,11 +13,12 @@
 //   next step's MFMA (B[k][n] at lane (k-group, n)) once the contraction index k is permuted to
 //   v = 16*tile + 4g + r; the A operand W^T uses the same permutation.  So the state never needs
 //   a transpose: each step every wave publishes its 16-column tile to LDS (16 B per lane), one
-//   barrier, and every wave reads all V/16 tiles back as B operands.
+//   barrier, and every wave reads the other tiles back as B operands (its own stays in registers).
 //
-// Per step, per wave: acc = (c k) v^T (VALU) ; acc += W'^T H^T (MFMA, c = 2 log2 e folded into W')
+// Per step, per wave: acc = (c k) v^T (MFMA) ; acc += W'^T H^T (MFMA, c = 2 log2 e folded into W')
 //   ; r = 1/(1 + 2^acc) ; H = fma(-2(1-f), r, fma(f, H, 1-f))      [= f H + (1-f) tanh(P)]
-//   ; y partial = sum over the block's rows of H[row][col] q[row] (DPP row reduction).
+//   ; y partial = sum over the block's rows of H[row][col] q[row] (transposing MFMA + cross-lane
+//   reduction; DPP row reduction in the fp32 mode).
 // q, k, v, f are staged through LDS in chunks of TC steps, double-buffered: chunk c+1 is read
 // from HBM into registers while chunk c is consumed.
 #pragma once
@@ -371,8 +372,10 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
     lds_barrier();
   }
 
-  // Readout, done right after H_t is published, while this wave waits for that LDS write.
-  //   split modes: the transposing MFMAs leave lane (g, j) with rows 4g..4g+3 of column 16w + j;
+  // Readout.
+  //   split modes: the transposing MFMAs (issued after H_t is published, before the barrier) leave
+  //                lane (g, j) with rows 4g..4g+3 of column 16w + j; after the barrier, while the
+  //                exchange reads are in flight, each lane forms its q-weighted sum of those rows;
   //                the lane's q-weighted sum over them is kept for four consecutive steps, and one
   //                cross-row reduction of the four leaves lane (g, j) with y[t0 + g][16w + j], so
   //                every lane stores, once per four steps.
@@ -420,12 +423,13 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   lds_barrier();
 
   // Software pipeline of the step loop.  Step t:
-  //   1. the LDS reads of the B operands (the state tiles published at step t-1);
+  //   1. the LDS reads of the B operands (the state tiles published at step t-1), and, while they
+  //      are in flight, the readout sums of step t-1;
   //   2. the MFMA contraction acc = (c k_t) v_t^T + W'^T H_{t-1}^T (the rank-1 term was issued at
   //      the end of step t-1), and step t+1's staged inputs read while the MFMAs run;
   //   3. tanh + gate blend -> H_t, publish H_t's tile;
-  //   4. while that write completes: the readout of step t, and the rank-1 MFMA of step t+1;
-  //      one barrier.
+  //   4. while that write completes: the readout store of a finished group of four steps, the
+  //      transposing MFMAs of H_t's tile and the rank-1 MFMA of step t+1; one barrier.
   // Chunk c+1 is written to the stage ring at step TC-2 of chunk c, so every step's inputs are in
   // LDS one barrier before step 2 of the previous step reads them.  Two chunks are unrolled per
   // loop trip, which makes the stage offsets and the exchange-buffer parity compile-time.  The
