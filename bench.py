@@ -145,6 +145,92 @@ def bench_backward(args) -> int:
     return 0
 
 
+def bench_decode(args) -> int:
+    """Times m2rnn_decode_step (one token for every (batch, head), state in HBM) on the batch-128
+    decode workload.  The state is updated in place, as a serving loop would."""
+    import numpy as np
+    import torch
+
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    from matrix_state_nonlinear_m2rnn_amd import inputs
+
+    name = args.workload if args.workload != "long_b2_h32_t16384_kv64" else "decode_b128_h32_kv64"
+    w = inputs.WORKLOADS[name]
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    d = inputs.workload_inputs(w.name)
+    dev = torch.device("cuda:0")
+    qkv_t = torch.bfloat16 if w.qkv_dtype == "bf16" else torch.float32
+    B, N, K, V = w.B, w.N, w.K, w.V
+    t = {n: torch.from_numpy(np.ascontiguousarray(a)).to(dev) for n, a in d.items() if a is not None}
+    q, k, v = (t[n][:, 0].to(qkv_t).contiguous() for n in ("q", "k", "v"))
+    f = t["f"][:, 0].contiguous()
+    H = t["H0"].clone()
+    y = torch.empty((B, N, V), dtype=torch.float32, device=dev)
+
+    def step():
+        m2.m2rnn_decode_step(q, k, v, f, t["W"], t["w_r"], H, H_out=H, y=y)
+
+    # A serving loop issues decode steps from a HIP graph.  The K timed steps are captured into one
+    # graph (K launches of the kernel, each updating the state in place) so that the GPU runs them
+    # back to back without host launch overhead between tokens; one replay is the timed region.
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(max(args.warmup, 1)):
+            step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    graph.replay()  # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e_start.record(cur)
+    graph.replay()
+    e_end.record(cur)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = e_start.elapsed_time(e_end)
+    # Average kernel duration: the launches run back to back inside the replay, so the per-step
+    # time is the kernel duration plus the (small) gap between consecutive kernels.
+    kern_ms = total_ms / args.steps
+    esz = 2 if w.qkv_dtype == "bf16" else 4
+    # Algorithmic HBM bytes per launch: the state read and written once, q, k, v, f read, y
+    # written, and W, w_r read once per head.
+    per_unit = 2 * K * V * 4 + (2 * K + V) * esz + 4 + 4 * V
+    nbytes = B * N * per_unit + N * (V * V + V) * 4
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    head_steps = B * N
+    out = {"metric": f"M²RNN decode step head-steps/sec (B={B}, N={N}, K={K}, V={V}, state in HBM)",
+           "value": head_steps * args.steps / (total_ms * 1e-3), "unit": "head-steps/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": total_ms / args.steps,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": w.name, "B": B, "T": 1, "N": N, "K": K, "V": V, "qkv_dtype": w.qkv_dtype,
+                      "math": "f16x3", "in_place": True, "launch": "K steps captured in one hip graph"},
+           "kernel_us": kern_ms * 1e3, "wall_s": wall,
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": achieved / PEAK_HBM_GBS, "traffic": None, "algorithmic_bytes_per_launch": nbytes}}
+    if args.cpu_baseline == "on":
+        import oracle
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        nthreads = oracle.default_threads()
+        reps, t_total = 0, 0.0
+        while t_total < min(args.cpu_seconds, 10.0) or reps == 0:
+            t0 = time.perf_counter()
+            oracle.ref_fwd(d["q"], d["k"], d["v"], d["f"], d["W"], d["w_r"], d["H0"], nthreads=nthreads)
+            t_total += time.perf_counter() - t0
+            reps += 1
+        out["cpu_baseline"] = {"value": head_steps * reps / t_total, "unit": "head-steps/s",
+                               "cores": min(nthreads, head_steps), "kind": "oracle",
+                               "sample": f"{reps} whole decode steps of {w.name} (fp64, units spread over threads)",
+                               "wall_s": round(t_total, 3)}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +243,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--backward", action="store_true",
                     help="time m2rnn_bwd on the BPTT workload instead of the forward (its own JSON line)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time m2rnn_decode_step on the batch-128 decode workload (its own JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -178,6 +266,8 @@ def main() -> int:
         return 2
     if args.backward:
         return bench_backward(args)
+    if args.decode:
+        return bench_decode(args)
     w = inputs.WORKLOADS[args.workload]
     math_mode = "f16x3" if args.math == "auto" else args.math
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)

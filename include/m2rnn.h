@@ -143,6 +143,25 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
               float* dW, float* dw_r, float* dH0, void* workspace, size_t workspace_bytes,
               void* stream);
 
+/*
+ * One step of Eq. (10)-(12) for every (b, n), with the state kept in device memory: the decode
+ * (token-by-token inference) form of the layer.  The notes point out that inference carries a
+ * fixed-size recurrent state (§2.6); this call reads it, advances it by one token and writes it
+ * back, so its cost is the state traffic (about 8 K V bytes per (b, n)), not the contraction.
+ *
+ *   dims         T must be 1.  Layouts are those of m2rnn_fwd with T = 1:
+ *                q, k [B,1,N,K]; v [B,1,N,V] (dtype qkv_dtype); f [B,1,N]; W [N,V,V]; w_r [N,V].
+ *   H_in         the state before the step [B,N,K,V], or NULL for zeros.
+ *   H_out        the state after the step [B,N,K,V].  H_out == H_in updates the state in place;
+ *                any other overlap of the two is rejected (M2RNN_EINVAL).
+ *   y            the readout of the step [B,1,N,V].
+ *   math         M2RNN_MATH_F16X3 or M2RNN_MATH_AUTO (the other modes return M2RNN_EUNSUPPORTED).
+ * No workspace.  Results equal m2rnn_fwd over one step with H0 = H_in, up to rounding order.
+ */
+int m2rnn_decode_step(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k,
+                      const void* v, const float* f, const float* W, const float* w_r,
+                      const float* H_in, float* H_out, float* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

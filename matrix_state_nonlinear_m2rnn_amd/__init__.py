@@ -29,7 +29,7 @@ BWD_CHECKPOINT = 64
 
 EXPORTED = (
     "m2rnn_version", "m2rnn_status_string", "m2rnn_last_hip_error", "m2rnn_fwd_workspace_size", "m2rnn_fwd",
-    "m2rnn_scan_fwd", "m2rnn_scan_fwd_finish", "m2rnn_bwd_workspace_size", "m2rnn_bwd",
+    "m2rnn_scan_fwd", "m2rnn_scan_fwd_finish", "m2rnn_bwd_workspace_size", "m2rnn_bwd", "m2rnn_decode_step",
 )
 
 
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
             L.m2rnn_bwd_workspace_size.argtypes = [dp, ci, ci, ctypes.POINTER(sz)]
             L.m2rnn_bwd.restype = ci
             L.m2rnn_bwd.argtypes = [dp, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp] + [vp] * 7 + [vp, sz, vp]
+        L.m2rnn_decode_step.restype = ci
+        L.m2rnn_decode_step.argtypes = [dp, ci, ci] + [vp] * 3 + [vp] * 3 + [vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -238,3 +240,44 @@ def m2rnn_bwd(q, k, v, f, W, w_r, H0, dy, dH_T=None, *, math="auto", want_dH0: b
         _ptr(dH_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dW"]),
         _ptr(out["dw_r"]), _ptr(out["dH0"]), _ptr(ws), nbytes, _stream(stream)))
     return out
+
+
+def m2rnn_decode_step(q, k, v, f, W, w_r, H=None, *, H_out=None, y=None, math="auto",
+                      stream=None) -> Tuple[object, object]:
+    """One recurrence step (M²RNN notes §2.1, Eq. 10-12) with the state in device memory (decode).
+
+    q, k: [B,N,K]; v: [B,N,V] (float32 or bfloat16, all alike); f: [B,N] fp32; W: [N,V,V];
+    w_r: [N,V]; H: the state [B,N,K,V] fp32 or None (zeros).  Returns (y [B,N,V], H_out
+    [B,N,K,V]).  Pass ``H_out=H`` to update the state in place.
+    """
+    import torch
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [B,N,K] and v [B,N,V]")
+    B, N, K = q.shape
+    V = v.shape[2]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU (HIP) device")
+    qkv_dtype = q.dtype
+    if qkv_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    _require(q, "q", qkv_dtype, (B, N, K), dev)
+    _require(k, "k", qkv_dtype, (B, N, K), dev)
+    _require(v, "v", qkv_dtype, (B, N, V), dev)
+    _require(f, "f", torch.float32, (B, N), dev)
+    _require(W, "W", torch.float32, (N, V, V), dev)
+    _require(w_r, "w_r", torch.float32, (N, V), dev)
+    if H is not None:
+        _require(H, "H", torch.float32, (B, N, K, V), dev)
+    if H_out is None:
+        H_out = torch.empty((B, N, K, V), dtype=torch.float32, device=dev)
+    _require(H_out, "H_out", torch.float32, (B, N, K, V), dev)
+    if y is None:
+        y = torch.empty((B, N, V), dtype=torch.float32, device=dev)
+    _require(y, "y", torch.float32, (B, N, V), dev)
+    dims = Dims(B, 1, N, K, V)
+    dt = DTYPE_BF16 if qkv_dtype == torch.bfloat16 else DTYPE_F32
+    _check("m2rnn_decode_step", lib().m2rnn_decode_step(
+        ctypes.byref(dims), dt, _math(math), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H),
+        _ptr(H_out), _ptr(y), _stream(stream)))
+    return y, H_out

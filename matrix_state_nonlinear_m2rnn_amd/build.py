@@ -23,6 +23,7 @@ SOURCES = [
     "m2rnn_fwd_f16x3.hip",
     "m2rnn_fwd_bf16x3.hip",
     "m2rnn_fwd_bf16.hip",
+    "m2rnn_decode.hip",
 ]
 
 # Packed fp32 VALU ops stay off: hipcc -O3 would otherwise form v_pk_{add,mul,fma}_f32.

@@ -7,6 +7,7 @@
 
 #include "../../include/m2rnn.h"
 #include "m2rnn_bwd_kernel.h"
+#include "m2rnn_decode_kernel.h"
 #include "m2rnn_select.h"
 
 using namespace m2rnn;
@@ -112,6 +113,19 @@ int plan_row_blocks(const m2rnn_dims* d, int math, bool bf16, int mode, int requ
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// dst = src (or zeros when src is null), as a kernel: no memset or copy nodes, so the calls stay
+// capturable in a HIP graph.
+__global__ void m2rnn_fill_kernel(float* __restrict__ dst, const float* __restrict__ src, long count) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) dst[i] = src ? src[i] : 0.0f;
+}
+
+int fill(float* dst, const float* src, long count, hipStream_t stream) {
+  if (!dst || count <= 0) return M2RNN_OK;
+  hipLaunchKernelGGL(m2rnn_fill_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream, dst, src, count);
+  return hip_status(hipGetLastError());
+}
+
 size_t fwd_partial_bytes(const m2rnn_dims* d, int rb) {
   const long S = d->K / (16 * rb);
   if (S <= 1) return 0;
@@ -162,10 +176,7 @@ int launch_scan(const FwdCall& c, int math, int rb) {
   const int S = (int)(d->K / (16 * rb));
   if (d->T == 0) {
     // Nothing to scan: H_T = H0 (or zeros).
-    if (!c.H_T) return M2RNN_OK;
-    const size_t bytes = (size_t)d->B * d->N * d->K * d->V * sizeof(float);
-    if (c.H0) return hip_status(hipMemcpyAsync(c.H_T, c.H0, bytes, hipMemcpyDeviceToDevice, c.stream));
-    return hip_status(hipMemsetAsync(c.H_T, 0, bytes, c.stream));
+    return fill(c.H_T, c.H0, d->B * d->N * d->K * d->V, c.stream);
   }
   FwdArgs a{};
   a.q = c.q; a.k = c.k; a.v = c.v; a.f = c.f; a.W = c.W; a.w_r = c.w_r; a.H0 = c.H0;
@@ -199,17 +210,6 @@ int launch_finish(const FwdCall& c, int rb) {
 }
 
 // ---------------------------------------------------------------- backward
-
-__global__ void m2rnn_fill_kernel(float* __restrict__ dst, const float* __restrict__ src, long count) {
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) dst[i] = src ? src[i] : 0.0f;
-}
-
-int fill(float* dst, const float* src, long count, hipStream_t stream) {
-  if (!dst || count <= 0) return M2RNN_OK;
-  hipLaunchKernelGGL(m2rnn_fill_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream, dst, src, count);
-  return hip_status(hipGetLastError());
-}
 
 struct BwdLayout {
   size_t ckpt = 0, seg = 0, dv = 0, df = 0, dW = 0, dwr = 0, total = 0;
@@ -403,6 +403,42 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
   hipLaunchKernelGGL(m2rnn_bwd_sum_dwr_kernel, dim3((unsigned)((N * V + 255) / 256)), dim3(256), 0, stream,
                      (const float*)(ws + L.dwr), (int)B, (int)(N * V), dw_r);
   return hip_status(hipGetLastError());
+}
+
+int m2rnn_decode_step(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k,
+                      const void* v, const float* f, const float* W, const float* w_r, const float* H_in,
+                      float* H_out, float* y, void* stream) {
+  int st = check_dims(dims, qkv_dtype);
+  if (st) return st;
+  if (dims->T != 1) return M2RNN_EINVAL;
+  const int m = resolve_bwd_math(math);  // the decode kernel is built for F16X3 (= AUTO) only
+  if (m == -1) return M2RNN_EINVAL;
+  if (m == -2) return M2RNN_EUNSUPPORTED;
+  const m2rnn_dims* d = dims;
+  if (d->B == 0 || d->N == 0) return M2RNN_OK;
+  if (!q || !k || !v || !f || !W || !w_r || !H_out || !y) return M2RNN_EINVAL;
+  {
+    const void* ptrs[] = {q, k, v, W, w_r, H_in, H_out, y};
+    for (const void* p : ptrs)
+      if (p && !aligned16(p)) return M2RNN_EINVAL;
+    if ((uintptr_t)f & 3u) return M2RNN_EINVAL;
+  }
+  // H_out may be H_in itself (in-place update), but must not overlap it partially.
+  const size_t sbytes = (size_t)d->B * d->N * d->K * d->V * sizeof(float);
+  if (H_in && H_in != H_out) {
+    const char *a0 = (const char*)H_in, *b0 = (const char*)H_out;
+    if (a0 < b0 + sbytes && b0 < a0 + sbytes) return M2RNN_EINVAL;
+  }
+  const void* kern = decode_kernel((int)d->V, qkv_dtype == M2RNN_DTYPE_BF16);
+  if (!kern) return M2RNN_EUNSUPPORTED;
+  const long groups = (d->B + kDecWaves - 1) / kDecWaves;
+  if ((double)groups * d->N > 2147483647.0) return M2RNN_EUNSUPPORTED;
+  DecArgs a{};
+  a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.H_in = H_in; a.H_out = H_out; a.y = y;
+  a.B = (int)d->B; a.N = (int)d->N; a.K = (int)d->K;
+  void* args[] = {&a};
+  return hip_status(hipLaunchKernel(kern, dim3((unsigned)(groups * d->N)), dim3(64 * kDecWaves), args, 0,
+                                    (hipStream_t)stream));
 }
 
 }  // extern "C"

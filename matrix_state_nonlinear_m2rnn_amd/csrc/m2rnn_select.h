@@ -46,4 +46,7 @@ const void* fwd_kernel_f16x3(int V, int rb, bool bf16, int mode);
 const void* fwd_kernel_bf16x3(int V, int rb, bool bf16, int mode);
 const void* fwd_kernel_bf16(int V, int rb, bool bf16, int mode);
 
+// Single-step (decode) kernel for value size V (defined in m2rnn_decode.hip).
+const void* decode_kernel(int V, bool bf16);
+
 }  // namespace m2rnn

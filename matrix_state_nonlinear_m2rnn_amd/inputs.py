@@ -147,6 +147,7 @@ class Workload:
     f_mean: float
     seed: int
     backward: bool = False
+    decode: bool = False  # one step with a given state (H0 drawn), the token-by-token form
     note: str = ""
 
     @property
@@ -169,6 +170,9 @@ WORKLOADS: Dict[str, Workload] = {
     "bwd_b4_h16_t4096_kv64": Workload("bwd_b4_h16_t4096_kv64", 4, 4096, 16, 64, 64, "f32", 1.5, BASE_SEED + 4,
                                       backward=True,
                                       note="forward + BPTT, B4 N16 T4096 K=V=64, fp32 q/k/v"),
+    "decode_b128_h32_kv64": Workload("decode_b128_h32_kv64", 128, 1, 32, 64, 64, "bf16", 1.5, BASE_SEED + 5,
+                                     decode=True,
+                                     note="one decode step at batch 128, N32 K=V=64, bf16 q/k/v, state in HBM"),
 }
 
 
@@ -212,5 +216,6 @@ def workload_inputs(name: str, **overrides) -> Dict[str, Optional[np.ndarray]]:
     dims.update({k: v for k, v in overrides.items() if k in dims})
     extra = {k: v for k, v in overrides.items() if k not in dims}
     extra.setdefault("with_dy", w.backward)
+    extra.setdefault("with_H0", w.decode)
     return make_inputs(dims["B"], dims["T"], dims["N"], dims["K"], dims["V"], qkv_dtype=w.qkv_dtype,
                        f_mean=w.f_mean, seed=w.seed, **extra)

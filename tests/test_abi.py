@@ -63,3 +63,27 @@ def test_workspace_size_query():
     assert m2.m2rnn_fwd_workspace_size(m2.Dims(2, 10, 3, 64, 32), 1, "f16x3", 4) == 0
     with pytest.raises(m2.M2RNNError):
         m2.m2rnn_fwd_workspace_size(m2.Dims(2, 10, 3, 64, 40), 1, "f16x3", 0)
+
+
+def decode(dims, dtype=0, math=-1, ptr=16, H_in=16, H_out=16, y=True, f=True):
+    L = m2.lib()
+    p = ctypes.c_void_p(ptr)
+    return L.m2rnn_decode_step(ctypes.byref(dims), dtype, math, p, p, p, p if f else None, p, p,
+                               ctypes.c_void_p(H_in) if H_in else None, ctypes.c_void_p(H_out) if H_out else None,
+                               p if y else None, None)
+
+
+def test_decode_step_invalid_arguments_are_rejected_on_the_host():
+    D = m2.Dims
+    assert decode(D(2, 2, 3, 16, 16)) == m2.M2RNN_EINVAL              # T must be 1
+    assert decode(D(2, 0, 3, 16, 16)) == m2.M2RNN_EINVAL
+    assert decode(D(2, 1, 3, 16, 48)) == m2.M2RNN_EUNSUPPORTED         # V not in {16,32,64,128}
+    assert decode(D(2, 1, 3, 16, 16), math=0) == m2.M2RNN_EUNSUPPORTED  # only the split-fp16 contraction
+    assert decode(D(2, 1, 3, 16, 16), math=9) == m2.M2RNN_EINVAL
+    assert decode(D(2, 1, 3, 16, 16), y=False) == m2.M2RNN_EINVAL
+    assert decode(D(2, 1, 3, 16, 16), f=False) == m2.M2RNN_EINVAL
+    assert decode(D(2, 1, 3, 16, 16), H_out=0) == m2.M2RNN_EINVAL
+    assert decode(D(2, 1, 3, 16, 16), ptr=24) == m2.M2RNN_EINVAL       # misaligned
+    # H_out may be H_in (in place) but must not overlap it otherwise.
+    assert decode(D(2, 1, 3, 16, 16), H_in=1 << 20, H_out=(1 << 20) + 256) == m2.M2RNN_EINVAL
+    assert decode(D(0, 1, 3, 16, 16)) == m2.M2RNN_OK                   # nothing to do
