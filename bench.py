@@ -79,7 +79,8 @@ def cpu_baseline(d, w, seconds: float):
     def run(T, nunits, threads):
         # Units become the heads of one batch entry: q [1, T, units, K], W [units, V, V], ...
         sel = pairs[:nunits]
-        g = lambda a: np.stack([a[b, :T, n] for b, n in sel], axis=1)[None]  # noqa: E731
+        # q, k shared by all heads ([B,T,1,K]) are taken per unit like the per-head ones.
+        g = lambda a: np.stack([a[b, :T, n if a.shape[2] > 1 else 0] for b, n in sel], axis=1)[None]  # noqa: E731
         W = np.stack([d["W"][n] for _, n in sel])
         w_r = np.stack([d["w_r"][n] for _, n in sel])
         t0 = time.perf_counter()

@@ -16,7 +16,8 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Tensor layouts are contiguous row-major:
- *        q, k      [B, T, N, K]     (dtype given by qkv_dtype)
+ *        q, k      [B, T, Nqk, K]   (dtype given by qkv_dtype; Nqk = N, or 1 when all value heads
+ *                                    share one query/key, the notes' multi-value layout §2.4)
  *        v         [B, T, N, V]     (dtype given by qkv_dtype)
  *        f         [B, T, N]        fp32, expected in [0, 1] (not checked, computed as given)
  *        W         [N, V, V]        fp32
@@ -33,7 +34,8 @@
  *  - Arguments are validated on the host before anything is enqueued; an invalid call returns
  *    an error status and touches no memory.  M2RNN_EHIP reports a launch failure
  *    (m2rnn_last_hip_error() gives the hipError_t of the most recent one on this thread).
- *  - Supported sizes: V in {16, 32, 64, 128}; K a positive multiple of 16; B, T, N >= 0.
+ *  - Supported sizes: V in {16, 32, 64, 128}; K a positive multiple of 16; B, T, N >= 0;
+ *    Nqk in {0, 1, N}.
  *    T = 0 is legal: y is empty and H_T = H0 (or zeros).
  */
 #ifndef M2RNN_H_
@@ -52,6 +54,9 @@ typedef struct m2rnn_dims {
   int64_t N; /* heads */
   int64_t K; /* key size: rows of the state */
   int64_t V; /* value size: columns of the state, side of W */
+  int64_t Nqk; /* heads of q and k: N (one query/key per head) or 1 (one query/key shared by all
+                  N value heads, §2.4: N_q = N_k = 1); 0 means N.  With Nqk = 1, dq and dk are
+                  the gradients of the shared q and k, summed over the heads (§2.7). */
 } m2rnn_dims;
 
 /* dtype of q, k, v. */
@@ -131,7 +136,7 @@ int m2rnn_scan_fwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, int r
  * at the start of the backward; here only checkpoints are stored, not every state).
  *
  *   dH_T   upstream gradient of the final state, or NULL for zeros.
- *   dq, dk [B,T,N,K]; dv [B,T,N,V]; df [B,T,N]; dW [N,V,V] and dw_r [N,V] summed over batch and
+ *   dq, dk [B,T,Nqk,K]; dv [B,T,N,V]; df [B,T,N]; dW [N,V,V] and dw_r [N,V] summed over batch and
  *   time; dH0 [B,N,K,V] or NULL to skip it.  All fp32.
  *   math   M2RNN_MATH_F16X3 or M2RNN_MATH_AUTO (the other modes return M2RNN_EUNSUPPORTED).
  */

@@ -35,7 +35,7 @@ EXPORTED = (
 
 class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
-                ("V", ctypes.c_int64)]
+                ("V", ctypes.c_int64), ("Nqk", ctypes.c_int64)]
 
 
 class M2RNNError(RuntimeError):
@@ -129,17 +129,19 @@ def _require(t, name, dtype, shape, device):
 def _fwd_prepare(q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, return_state):
     import torch
     if q.dim() != 4 or v.dim() != 4:
-        raise ValueError("q must be [B,T,N,K] and v [B,T,N,V]")
-    B, T, N, K = q.shape
-    V = v.shape[3]
+        raise ValueError("q must be [B,T,Nqk,K] and v [B,T,N,V]")
+    B, T, Nqk, K = q.shape
+    N, V = v.shape[2], v.shape[3]
+    if Nqk not in (1, N):
+        raise ValueError(f"q and k carry {Nqk} heads: expected {N} (one per head) or 1 (shared by all heads)")
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU (HIP) device")
     qkv_dtype = q.dtype
     if qkv_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("q, k, v must be float32 or bfloat16")
-    _require(q, "q", qkv_dtype, (B, T, N, K), dev)
-    _require(k, "k", qkv_dtype, (B, T, N, K), dev)
+    _require(q, "q", qkv_dtype, (B, T, Nqk, K), dev)
+    _require(k, "k", qkv_dtype, (B, T, Nqk, K), dev)
     _require(v, "v", qkv_dtype, (B, T, N, V), dev)
     _require(f, "f", torch.float32, (B, T, N), dev)
     _require(W, "W", torch.float32, (N, V, V), dev)
@@ -153,7 +155,7 @@ def _fwd_prepare(q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, return_state)
         H_T = torch.empty((B, N, K, V), dtype=torch.float32, device=dev)
     if H_T is not None:
         _require(H_T, "H_T", torch.float32, (B, N, K, V), dev)
-    dims = Dims(B, T, N, K, V)
+    dims = Dims(B, T, N, K, V, Nqk)
     dt = DTYPE_BF16 if qkv_dtype == torch.bfloat16 else DTYPE_F32
     return dims, dt, _math(math), int(row_blocks), y, H_T
 
@@ -190,8 +192,9 @@ def m2rnn_fwd(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int = 0, 
               stream=None, return_state: bool = True) -> Tuple[object, Optional[object]]:
     """Forward recurrence (M²RNN notes §2.1, Eq. 10-12) on the current HIP stream.
 
-    q, k: [B,T,N,K]; v: [B,T,N,V] (all float32 or all bfloat16); f: [B,T,N] fp32; W: [N,V,V] fp32;
-    w_r: [N,V] fp32; H0: [B,N,K,V] fp32 or None.  Returns (y [B,T,N,V] fp32, H_T [B,N,K,V] fp32).
+    q, k: [B,T,Nqk,K] with Nqk = N, or 1 for one query/key shared by all heads (§2.4); v: [B,T,N,V]
+    (all float32 or all bfloat16); f: [B,T,N] fp32; W: [N,V,V] fp32; w_r: [N,V] fp32; H0: [B,N,K,V]
+    fp32 or None.  Returns (y [B,T,N,V] fp32, H_T [B,N,K,V] fp32).
     """
     y, H_T, _ = _call_fwd("m2rnn_fwd", q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, workspace, stream,
                           return_state)
@@ -222,16 +225,18 @@ def m2rnn_bwd_workspace_size(dims: Dims, qkv_dtype: int, math="auto") -> int:
 
 def m2rnn_bwd(q, k, v, f, W, w_r, H0, dy, dH_T=None, *, math="auto", want_dH0: bool = True, workspace=None,
               stream=None) -> Dict[str, object]:
-    """BPTT (M²RNN notes §2.7) for L = sum <dy, y> + <dH_T, H_T>; returns dq, dk, dv, df, dW, dw_r, dH0."""
+    """BPTT (M²RNN notes §2.7) for L = sum <dy, y> + <dH_T, H_T>; returns dq, dk, dv, df, dW, dw_r, dH0.
+
+    dq, dk have q's shape [B,T,Nqk,K]: with a shared query/key (Nqk = 1) they are summed over heads."""
     import torch
     dims, dt, m, _, _, _ = _fwd_prepare(q, k, v, f, W, w_r, H0, None, None, math, 0, False)
-    B, T, N, K, V = dims.B, dims.T, dims.N, dims.K, dims.V
+    B, T, N, K, V, Nqk = dims.B, dims.T, dims.N, dims.K, dims.V, dims.Nqk
     dev = q.device
     _require(dy, "dy", torch.float32, (B, T, N, V), dev)
     if dH_T is not None:
         _require(dH_T, "dH_T", torch.float32, (B, N, K, V), dev)
     e = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
-    out = {"dq": e(B, T, N, K), "dk": e(B, T, N, K), "dv": e(B, T, N, V), "df": e(B, T, N), "dW": e(N, V, V),
+    out = {"dq": e(B, T, Nqk, K), "dk": e(B, T, Nqk, K), "dv": e(B, T, N, V), "df": e(B, T, N), "dW": e(N, V, V),
            "dw_r": e(N, V), "dH0": e(B, N, K, V) if want_dH0 else None}
     nbytes = m2rnn_bwd_workspace_size(dims, dt, m)
     ws = _workspace(nbytes, dev, workspace)
@@ -246,23 +251,26 @@ def m2rnn_decode_step(q, k, v, f, W, w_r, H=None, *, H_out=None, y=None, math="a
                       stream=None) -> Tuple[object, object]:
     """One recurrence step (M²RNN notes §2.1, Eq. 10-12) with the state in device memory (decode).
 
-    q, k: [B,N,K]; v: [B,N,V] (float32 or bfloat16, all alike); f: [B,N] fp32; W: [N,V,V];
+    q, k: [B,Nqk,K] (Nqk = N, or 1 when shared by all heads); v: [B,N,V] (float32 or bfloat16,
+    all alike); f: [B,N] fp32; W: [N,V,V];
     w_r: [N,V]; H: the state [B,N,K,V] fp32 or None (zeros).  Returns (y [B,N,V], H_out
     [B,N,K,V]).  Pass ``H_out=H`` to update the state in place.
     """
     import torch
     if q.dim() != 3 or v.dim() != 3:
-        raise ValueError("q must be [B,N,K] and v [B,N,V]")
-    B, N, K = q.shape
-    V = v.shape[2]
+        raise ValueError("q must be [B,Nqk,K] and v [B,N,V]")
+    B, Nqk, K = q.shape
+    N, V = v.shape[1], v.shape[2]
+    if Nqk not in (1, N):
+        raise ValueError(f"q and k carry {Nqk} heads: expected {N} (one per head) or 1 (shared by all heads)")
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU (HIP) device")
     qkv_dtype = q.dtype
     if qkv_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("q, k, v must be float32 or bfloat16")
-    _require(q, "q", qkv_dtype, (B, N, K), dev)
-    _require(k, "k", qkv_dtype, (B, N, K), dev)
+    _require(q, "q", qkv_dtype, (B, Nqk, K), dev)
+    _require(k, "k", qkv_dtype, (B, Nqk, K), dev)
     _require(v, "v", qkv_dtype, (B, N, V), dev)
     _require(f, "f", torch.float32, (B, N), dev)
     _require(W, "W", torch.float32, (N, V, V), dev)
@@ -275,7 +283,7 @@ def m2rnn_decode_step(q, k, v, f, W, w_r, H=None, *, H_out=None, y=None, math="a
     if y is None:
         y = torch.empty((B, N, V), dtype=torch.float32, device=dev)
     _require(y, "y", torch.float32, (B, N, V), dev)
-    dims = Dims(B, 1, N, K, V)
+    dims = Dims(B, 1, N, K, V, Nqk)
     dt = DTYPE_BF16 if qkv_dtype == torch.bfloat16 else DTYPE_F32
     _check("m2rnn_decode_step", lib().m2rnn_decode_step(
         ctypes.byref(dims), dt, _math(math), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H),

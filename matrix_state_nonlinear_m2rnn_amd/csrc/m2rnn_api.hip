@@ -28,6 +28,7 @@ int check_dims(const m2rnn_dims* d, int qkv_dtype) {
   if (!d) return M2RNN_EINVAL;
   if (d->B < 0 || d->T < 0 || d->N < 0 || d->K < 0 || d->V < 0) return M2RNN_EINVAL;
   if (qkv_dtype != M2RNN_DTYPE_F32 && qkv_dtype != M2RNN_DTYPE_BF16) return M2RNN_EINVAL;
+  if (d->Nqk != 0 && d->Nqk != 1 && d->Nqk != d->N) return M2RNN_EINVAL;
   if (d->V != 16 && d->V != 32 && d->V != 64 && d->V != 128) return M2RNN_EUNSUPPORTED;
   if (d->K <= 0 || d->K % 16 != 0) return M2RNN_EUNSUPPORTED;
   // 32-bit indices inside the kernels: every (b, t, n) index and plane must fit.
@@ -35,6 +36,9 @@ int check_dims(const m2rnn_dims* d, int qkv_dtype) {
   if (plane * 4.0 > 2147483647.0 || (double)d->B * d->N * d->K / 16 > 2147483647.0) return M2RNN_EUNSUPPORTED;
   return M2RNN_OK;
 }
+
+// Heads of q and k: N (one query/key per head) or 1 (shared by all heads).
+int qk_heads(const m2rnn_dims* d) { return d->Nqk == 1 ? 1 : (int)d->N; }
 
 int resolve_math(int math) {
   if (math == M2RNN_MATH_AUTO) return M2RNN_MATH_F16X3;
@@ -184,6 +188,7 @@ int launch_scan(const FwdCall& c, int math, int rb) {
   a.H_T = c.H_T;
   a.ckpt = nullptr;
   a.B = (int)d->B; a.T = (int)d->T; a.N = (int)d->N; a.K = (int)d->K;
+  a.Nqk = qk_heads(d);
   a.S = S;
   a.seg = 0;
   const void* kern = fwd_kernel(math, (int)d->V, rb, bf16, MODE_FWD);
@@ -212,8 +217,12 @@ int launch_finish(const FwdCall& c, int rb) {
 // ---------------------------------------------------------------- backward
 
 struct BwdLayout {
-  size_t ckpt = 0, seg = 0, dv = 0, df = 0, dW = 0, dwr = 0, total = 0;
+  size_t ckpt = 0, seg = 0, dv = 0, df = 0, dW = 0, dwr = 0, dq = 0, dk = 0, total = 0;
 };
+
+// A shared query/key (Nqk = 1) with several heads: per-head dq, dk go to the workspace and are
+// summed over the heads afterwards.
+bool shared_qk_sum(const m2rnn_dims* d) { return qk_heads(d) == 1 && d->N > 1; }
 
 BwdLayout bwd_layout(const m2rnn_dims* d) {
   BwdLayout L;
@@ -232,6 +241,9 @@ BwdLayout bwd_layout(const m2rnn_dims* d) {
   L.df = take(S > 1 ? (size_t)S * d->B * d->T * d->N * sizeof(float) : 0);
   L.dW = take((size_t)d->B * S * d->N * d->V * d->V * sizeof(float));
   L.dwr = take((size_t)d->B * d->N * d->V * sizeof(float));
+  const size_t qk_part = shared_qk_sum(d) ? (size_t)d->B * d->T * d->N * d->K * sizeof(float) : 0;
+  L.dq = take(qk_part);
+  L.dk = take(qk_part);
   L.total = off;
   return L;
 }
@@ -364,6 +376,7 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
     a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.H0 = H0;
     a.y = nullptr; a.H_T = nullptr; a.ckpt = (float*)(ws + L.ckpt);
     a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S; a.seg = kBwdSeg;
+    a.Nqk = qk_heads(d);
     const void* kern = fwd_kernel(M2RNN_MATH_F16X3, (int)V, 1, bf16, MODE_CKPT);
     if (!kern) return M2RNN_EUNSUPPORTED;
     void* args[] = {&a};
@@ -376,13 +389,16 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
     a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.dy = dy; a.dH_T = dH_T;
     a.ckpt = (const float*)(ws + L.ckpt);
     a.subck = (float*)(ws + L.seg);
-    a.dq = dq; a.dk = dk;
+    const bool sum_qk = shared_qk_sum(d);
+    a.dq = sum_qk ? (float*)(ws + L.dq) : dq;
+    a.dk = sum_qk ? (float*)(ws + L.dk) : dk;
     a.dv = S > 1 ? (float*)(ws + L.dv) : dv;
     a.df = S > 1 ? (float*)(ws + L.df) : df;
     a.dW_part = (float*)(ws + L.dW);
     a.dwr_part = (float*)(ws + L.dwr);
     a.dH0 = dH0;
     a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S;
+    a.Nqk = qk_heads(d);
     const void* kern = bwd_kernel((int)V, bf16);
     if (!kern) return M2RNN_EUNSUPPORTED;
     void* args[] = {&a};
@@ -397,6 +413,13 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
     const long cnt = B * T * N;
     hipLaunchKernelGGL(m2rnn_bwd_sum_df_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream,
                        (const float*)(ws + L.df), S, cnt, df);
+  }
+  if (shared_qk_sum(d)) {
+    const long cnt = B * T * K;
+    hipLaunchKernelGGL(m2rnn_bwd_sum_heads_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream,
+                       (const float*)(ws + L.dq), (int)N, B * T, (int)K, dq);
+    hipLaunchKernelGGL(m2rnn_bwd_sum_heads_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream,
+                       (const float*)(ws + L.dk), (int)N, B * T, (int)K, dk);
   }
   hipLaunchKernelGGL(m2rnn_bwd_sum_dW_kernel, dim3((unsigned)((N * V * V + 255) / 256)), dim3(256), 0, stream,
                      (const float*)(ws + L.dW), (int)(B * S), (int)N, (int)(V * V), dW);
@@ -436,6 +459,7 @@ int m2rnn_decode_step(const m2rnn_dims* dims, int qkv_dtype, int math, const voi
   DecArgs a{};
   a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.H_in = H_in; a.H_out = H_out; a.y = y;
   a.B = (int)d->B; a.N = (int)d->N; a.K = (int)d->K;
+  a.Nqk = qk_heads(d);
   void* args[] = {&a};
   return hip_status(hipLaunchKernel(kern, dim3((unsigned)(groups * d->N)), dim3(64 * kDecWaves), args, 0,
                                     (hipStream_t)stream));

@@ -38,14 +38,15 @@ struct BwdArgs {
   const float* dH_T;
   const float* ckpt;   // [B][N][nseg][K][V] states entering each segment
   float* subck;        // per-workgroup states entering each sub-segment
-  float* dq;
-  float* dk;
+  float* dq;           // per head [B][T][N][K] (summed over heads afterwards when q is shared)
+  float* dk;           // per head [B][T][N][K]
   float* dv;           // final dv (S == 1) or partials [S][B*T*N*V]
   float* df;           // final df (S == 1) or partials [S][B*T*N]
   float* dW_part;      // [B*S][N][V][V]
   float* dwr_part;     // [B][N][V] (written by the workgroups with s == 0)
   float* dH0;          // may be null
   int B, T, N, K;
+  int Nqk;             // heads of q and k: N, or 1 when one query/key is shared by all heads
   int S;
 };
 
@@ -85,7 +86,7 @@ __device__ __forceinline__ void bwd_stage_segment(const BwdArgs& a, int b, int n
 #pragma unroll
     for (int e = 0; e < VEC; ++e) vals[e] = 0.0f;
     if (step < n_steps) {
-      const long off = ((((long)b * a.T + t0 + step) * a.N + nh) * a.K + row0 + cv * VEC);
+      const long off = ((((long)b * a.T + t0 + step) * a.Nqk + (a.Nqk == 1 ? 0 : nh)) * a.K + row0 + cv * VEC);
       const void* src = which == 0 ? a.q : a.k;
       const uint4 raw = *(const uint4*)((const char*)src + off * esz);
       if constexpr (BF16IN) {
@@ -632,6 +633,20 @@ __global__ void __launch_bounds__(256) m2rnn_bwd_sum_df_kernel(const float* __re
   float acc = part[i];
   for (int s = 1; s < S; ++s) acc += part[(long)s * count + i];
   df[i] = acc;
+}
+
+// Gradient of a query/key shared by all heads (§2.7: summed over the heads): out[bt][k] =
+// sum over n (in order) of the per-head gradients part[bt][n][k].
+__global__ void __launch_bounds__(256) m2rnn_bwd_sum_heads_kernel(const float* __restrict__ part, int N, long rows,
+                                                                   int K, float* __restrict__ out) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;  // index into [rows][K]
+  if (i >= rows * K) return;
+  const long bt = i / K;
+  const int kk = (int)(i % K);
+  const float* p = part + bt * N * K + kk;
+  float acc = p[0];
+  for (int n = 1; n < N; ++n) acc += p[(long)n * K];
+  out[i] = acc;
 }
 
 // dW[n] = sum over (b, s) of the workgroup partials, in a fixed order.

@@ -24,8 +24,8 @@
 namespace m2rnn {
 
 struct DecArgs {
-  const void* q;      // [B, N, K]
-  const void* k;      // [B, N, K]
+  const void* q;      // [B, Nqk, K]
+  const void* k;      // [B, Nqk, K]
   const void* v;      // [B, N, V]
   const float* f;     // [B, N]
   const float* W;     // [N, V, V]
@@ -34,6 +34,7 @@ struct DecArgs {
   float* H_out;       // [B, N, K, V] (may equal H_in)
   float* y;           // [B, N, V]
   int B, N, K;
+  int Nqk;            // heads of q and k: N, or 1 when one query/key is shared by all heads
 };
 
 constexpr int kDecWaves = 4;  // batch entries (one wave each) per workgroup
@@ -140,7 +141,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) m2rnn_decode_kernel(const DecA
     // Next block in flight while this one is computed.
     float Hn[NT][4];
     if (rb + 1 < KB) load_block(rb + 1, Hn);
-    const long row = unit * a.K + 16 * rb + n;
+    const long row = ((long)b * a.Nqk + (a.Nqk == 1 ? 0 : nh)) * a.K + 16 * rb + n;
     const float qv = load_scalar<BF16IN>(a.q, row);
     const float ck = kTwoLog2e * load_scalar<BF16IN>(a.k, row);
 

@@ -39,6 +39,7 @@ struct FwdArgs {
   float* H_T;     // may be null
   float* ckpt;    // checkpoint mode: states entering each segment [B][N][nseg][K][V]
   int B, T, N, K;
+  int Nqk;        // heads of q and k: N, or 1 when one query/key is shared by all heads
   int S;          // workgroups per (b, n)
   int seg;        // checkpoint interval (checkpoint mode)
 };
@@ -120,11 +121,11 @@ struct ChunkRegs {
 
   __device__ __forceinline__ void load(const FwdArgs& a, int b, int nh, int row0, int t0, int tid) {
     const int valid = min(S::TC, a.T - t0);
-    const long qk_off = (((long)b * a.T + t0) * a.N + nh) * a.K + row0;
+    const long qk_off = (((long)b * a.T + t0) * a.Nqk + (a.Nqk == 1 ? 0 : nh)) * a.K + row0;
     const long v_off = (((long)b * a.T + t0) * a.N + nh) * V;
     const int esz = BF16 ? 2 : 4;
-    q.load((const char*)a.q + qk_off * esz, (long)a.N * a.K, valid, tid);
-    k.load((const char*)a.k + qk_off * esz, (long)a.N * a.K, valid, tid);
+    q.load((const char*)a.q + qk_off * esz, (long)a.Nqk * a.K, valid, tid);
+    k.load((const char*)a.k + qk_off * esz, (long)a.Nqk * a.K, valid, tid);
     v.load((const char*)a.v + v_off * esz, (long)a.N * V, valid, tid);
     f = 1.0f;
     if (tid < valid) f = a.f[((long)b * a.T + t0 + tid) * a.N + nh];
@@ -350,7 +351,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if constexpr (!SPLIT) {
-        *(float4*)&xbuf[buf][((rb * NT + w) * 64 + lane) * 4] = make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
+        if constexpr (NT > 1)
+          *(float4*)&xbuf[buf][((rb * NT + w) * 64 + lane) * 4] = make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
       } else {
         uint32_t h0, h1, l0, l1;
         split_pair<MATH>(H[rb][0], H[rb][1], h0, l0);
@@ -359,15 +361,17 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
         hq[rb].y = h1;
         lq[rb].x = l0;
         lq[rb].y = l1;
-        const int base = ((rb * NCH + (w >> 1)) * 4 + (w & 1)) * 128 + lane * 2;
-        *(uint2*)&xbuf[buf][base] = make_uint2(h0, h1);
-        if constexpr (MATH != MATH_BF16) *(uint2*)&xbuf[buf][base + 256] = make_uint2(l0, l1);
+        if constexpr (NT > 1) {
+          const int base = ((rb * NCH + (w >> 1)) * 4 + (w & 1)) * 128 + lane * 2;
+          *(uint2*)&xbuf[buf][base] = make_uint2(h0, h1);
+          if constexpr (MATH != MATH_BF16) *(uint2*)&xbuf[buf][base + 256] = make_uint2(l0, l1);
+        }
       }
     }
   };
 
   // Odd tile counts leave half of the last chunk unwritten: zero both buffers once.
-  if constexpr (SPLIT && (NT & 1)) {
+  if constexpr (SPLIT && (NT & 1) && NT > 1) {
     for (int i = tid; i < 2 * XWORDS; i += Sh::NTH) (&xbuf[0][0])[i] = 0u;
     lds_barrier();
   }
@@ -479,19 +483,26 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
       float4 hb[SPLIT ? 1 : RB * NT];
       uint4 bh[SPLIT ? RB * NOTH : 1], bl[SPLIT ? RB * NOTH : 1];
       if constexpr (!SPLIT) {
+        if constexpr (NT == 1) {
 #pragma unroll
-        for (int i = 0; i < RB * NT; ++i) hb[i] = *(const float4*)&xr[(i * 64 + lane) * 4];
+          for (int rb = 0; rb < RB; ++rb) hb[rb] = make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < RB * NT; ++i) hb[i] = *(const float4*)&xr[(i * 64 + lane) * 4];
+        }
       } else {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          // partner half of the own chunk
-          const uint2 ph = ((const uint2*)xr)[phi_off[rb]];
-          hq[rb].z = ph.x;
-          hq[rb].w = ph.y;
-          if constexpr (MATH != MATH_BF16) {
-            const uint2 pl = ((const uint2*)xbuf[j & 1])[plo_off[rb]];
-            lq[rb].z = pl.x;
-            lq[rb].w = pl.y;
+          // partner half of the own chunk (a single tile has none: those k-slots stay zero)
+          if constexpr (NT > 1) {
+            const uint2 ph = ((const uint2*)xr)[phi_off[rb]];
+            hq[rb].z = ph.x;
+            hq[rb].w = ph.y;
+            if constexpr (MATH != MATH_BF16) {
+              const uint2 pl = ((const uint2*)xbuf[j & 1])[plo_off[rb]];
+              lq[rb].z = pl.x;
+              lq[rb].w = pl.y;
+            }
           }
 #pragma unroll
           for (int i = 0; i < NCH - 1; ++i) {
@@ -633,7 +644,9 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
       __builtin_amdgcn_sched_barrier(0);
 
       if (j == TC - 2) pre.store(stage[cb ^ 1], tid);
-      lds_barrier();
+      // A single-wave workgroup (one 16-column tile) exchanges nothing, and its own LDS writes and
+      // reads of the stage ring are ordered, so it needs no barrier.
+      if constexpr (NT > 1) lds_barrier();
       if (j == TC - 2) {
         const int t_next = c0 + 2 * TC;  // first step of the chunk after the one just staged
         if (t_next < a.T) pre.load(a, b, nh, row0, t_next, tid);

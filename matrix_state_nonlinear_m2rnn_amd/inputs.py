@@ -148,6 +148,7 @@ class Workload:
     seed: int
     backward: bool = False
     decode: bool = False  # one step with a given state (H0 drawn), the token-by-token form
+    shared_qk: bool = False  # one query/key shared by all heads (q, k drawn as [B, T, 1, K])
     note: str = ""
 
     @property
@@ -170,6 +171,10 @@ WORKLOADS: Dict[str, Workload] = {
     "bwd_b4_h16_t4096_kv64": Workload("bwd_b4_h16_t4096_kv64", 4, 4096, 16, 64, 64, "f32", 1.5, BASE_SEED + 4,
                                       backward=True,
                                       note="forward + BPTT, B4 N16 T4096 K=V=64, fp32 q/k/v"),
+    "paper_b4_h128_t4096_k64_v16": Workload("paper_b4_h128_t4096_k64_v16", 4, 4096, 128, 64, 16, "bf16", 1.5,
+                                            BASE_SEED + 6, shared_qk=True,
+                                            note="the pages' head shape K=64, V=16 with one query/key shared "
+                                                 "by all 128 value heads, 4K context, bf16 q/k/v"),
     "decode_b128_h32_kv64": Workload("decode_b128_h32_kv64", 128, 1, 32, 64, 64, "bf16", 1.5, BASE_SEED + 5,
                                      decode=True,
                                      note="one decode step at batch 128, N32 K=V=64, bf16 q/k/v, state in HBM"),
@@ -178,8 +183,11 @@ WORKLOADS: Dict[str, Workload] = {
 
 def make_inputs(B: int, T: int, N: int, K: int, V: int, *, qkv_dtype: str = "f32", f_mean: float = 1.5,
                 seed: int = BASE_SEED, with_H0: bool = False, with_dy: bool = False,
-                with_dHT: bool = False, w_scale: float = 0.9) -> Dict[str, Optional[np.ndarray]]:
-    """All inputs of one workload as fp32 numpy arrays (bf16-exact where q/k/v are bf16)."""
+                with_dHT: bool = False, w_scale: float = 0.9,
+                shared_qk: bool = False) -> Dict[str, Optional[np.ndarray]]:
+    """All inputs of one workload as fp32 numpy arrays (bf16-exact where q/k/v are bf16).
+
+    With ``shared_qk`` q and k are [B, T, 1, K]: one query/key for all N heads."""
     if qkv_dtype not in ("f32", "bf16"):
         raise ValueError(f"qkv_dtype must be 'f32' or 'bf16', got {qkv_dtype!r}")
     key = lambda name: stream_key(seed, TENSOR_IDS[name])  # noqa: E731
@@ -191,8 +199,9 @@ def make_inputs(B: int, T: int, N: int, K: int, V: int, *, qkv_dtype: str = "f32
         return a.reshape(shape)
 
     out: Dict[str, Optional[np.ndarray]] = {}
-    out["q"] = qkv("q", B * T * N * K, 1.0 / K, (B, T, N, K))
-    out["k"] = qkv("k", B * T * N * K, 1.0 / K, (B, T, N, K))
+    Nqk = 1 if shared_qk else N
+    out["q"] = qkv("q", B * T * Nqk * K, 1.0 / K, (B, T, Nqk, K))
+    out["k"] = qkv("k", B * T * Nqk * K, 1.0 / K, (B, T, Nqk, K))
     out["v"] = qkv("v", B * T * N * V, 1.0, (B, T, N, V))
     z = normal(key("f"), B * T * N, f_mean, 1.0)
     out["f"] = (1.0 / (1.0 + np.exp(-z))).astype(np.float32).reshape(B, T, N)
@@ -217,5 +226,6 @@ def workload_inputs(name: str, **overrides) -> Dict[str, Optional[np.ndarray]]:
     extra = {k: v for k, v in overrides.items() if k not in dims}
     extra.setdefault("with_dy", w.backward)
     extra.setdefault("with_H0", w.decode)
+    extra.setdefault("shared_qk", w.shared_qk)
     return make_inputs(dims["B"], dims["T"], dims["N"], dims["K"], dims["V"], qkv_dtype=w.qkv_dtype,
                        f_mean=w.f_mean, seed=w.seed, **extra)

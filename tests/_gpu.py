@@ -46,15 +46,29 @@ def gpu_fwd(dd, math, row_blocks=0, H0=None):
     return y.cpu().numpy().astype(np.float64), H_T.cpu().numpy().astype(np.float64)
 
 
+def per_head_qk(d):
+    """q, k broadcast to every head when one query/key is shared ([B,T,1,K] -> [B,T,N,K]): the
+    oracle takes per-head q and k."""
+    N = d["v"].shape[2]
+    if d["q"].shape[2] == N:
+        return d
+    e = dict(d)
+    for x in ("q", "k"):
+        e[x] = np.ascontiguousarray(np.broadcast_to(d[x], d[x].shape[:2] + (N, d[x].shape[3])))
+    return e
+
+
 def oracle_fwd(d, H0=None):
+    d = per_head_qk(d)
     return oracle.ref_fwd(d["q"], d["k"], d["v"], d["f"], d["W"], d["w_r"], H0 if H0 is not None else d.get("H0"))
 
 
 def oracle_units(d, units):
     """Oracle outputs for a list of (b, n) units: dict (b, n) -> (y [T,V], H_T [K,V])."""
     out = {}
+    nq = lambda n: 0 if d["q"].shape[2] == 1 else n  # noqa: E731
     for b, n in units:
-        sub = dict(q=d["q"][b:b + 1, :, n:n + 1], k=d["k"][b:b + 1, :, n:n + 1], v=d["v"][b:b + 1, :, n:n + 1],
+        sub = dict(q=d["q"][b:b + 1, :, nq(n):nq(n) + 1], k=d["k"][b:b + 1, :, nq(n):nq(n) + 1], v=d["v"][b:b + 1, :, n:n + 1],
                    f=d["f"][b:b + 1, :, n:n + 1], W=d["W"][n:n + 1], w_r=d["w_r"][n:n + 1],
                    H0=None if d.get("H0") is None else d["H0"][b:b + 1, n:n + 1])
         y, H = oracle_fwd(sub)
@@ -76,7 +90,14 @@ def gpu_bwd(dd, math="auto", dH_T=None, want_dH0=True):
 
 
 def oracle_bwd(d):
-    return oracle.ref_bwd(d["q"], d["k"], d["v"], d["f"], d["W"], d["w_r"], d.get("H0"), d["dy"], d.get("dH_T"))
+    """Oracle gradients; with a shared query/key, dq and dk are summed over the heads (§2.7)."""
+    shared = d["q"].shape[2] != d["v"].shape[2]
+    e = per_head_qk(d)
+    g = oracle.ref_bwd(e["q"], e["k"], e["v"], e["f"], e["W"], e["w_r"], e.get("H0"), e["dy"], e.get("dH_T"))
+    if shared:
+        g["dq"] = g["dq"].sum(axis=2, keepdims=True)
+        g["dk"] = g["dk"].sum(axis=2, keepdims=True)
+    return g
 
 
 def rel_l2(a, b):

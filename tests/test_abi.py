@@ -87,3 +87,10 @@ def test_decode_step_invalid_arguments_are_rejected_on_the_host():
     # H_out may be H_in (in place) but must not overlap it otherwise.
     assert decode(D(2, 1, 3, 16, 16), H_in=1 << 20, H_out=(1 << 20) + 256) == m2.M2RNN_EINVAL
     assert decode(D(0, 1, 3, 16, 16)) == m2.M2RNN_OK                   # nothing to do
+
+
+def test_shared_query_key_head_count_is_checked():
+    D = m2.Dims
+    assert fwd(D(1, 4, 3, 16, 16, 2)) == m2.M2RNN_EINVAL      # Nqk must be 0, 1 or N
+    assert fwd(D(1, 4, 3, 16, 16, -1)) == m2.M2RNN_EINVAL
+    assert decode(D(2, 1, 3, 16, 16, 2)) == m2.M2RNN_EINVAL

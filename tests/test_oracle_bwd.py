@@ -70,3 +70,40 @@ def test_zero_upstream_gives_zero_gradients():
     g = oracle.ref_bwd(d["q"], d["k"], d["v"], d["f"], d["W"], d["w_r"], None, dy, None)
     for x in g.values():
         assert np.all(x == 0.0)
+
+
+def test_shared_query_key_gradient_is_the_sum_over_heads():
+    # One query/key shared by all heads (the notes' multi-value layout, N_q = N_k = 1): the
+    # gradient of the shared q (k) is the sum over heads of the per-head gradients (§2.7).  Pinned
+    # by central differences of the loss with the shared q (k) broadcast to every head.
+    B, T, N, K, V = 1, 4, 3, 3, 2
+    d = inputs.make_inputs(B, T, N, K, V, qkv_dtype="f32", seed=123, with_H0=True, with_dy=True,
+                           with_dHT=True, shared_qk=True)
+    d = {x: (a.astype(np.float64) if a is not None else None) for x, a in d.items()}
+    d["k"] *= 3.0
+    dy, dHT = d.pop("dy"), d.pop("dH_T")
+    assert d["q"].shape == (B, T, 1, K)
+
+    def per_head(dd):
+        e = dict(dd)
+        e["q"] = np.ascontiguousarray(np.broadcast_to(dd["q"], (B, T, N, K)))
+        e["k"] = np.ascontiguousarray(np.broadcast_to(dd["k"], (B, T, N, K)))
+        return e
+
+    e = per_head(d)
+    g = oracle.ref_bwd(e["q"], e["k"], e["v"], e["f"], e["W"], e["w_r"], e["H0"], dy, dHT)
+    h = 1e-6
+    for x, gx in (("q", "dq"), ("k", "dk")):
+        flat = d[x].reshape(-1)
+        num = np.empty(flat.size)
+        for i in range(flat.size):
+            keep = flat[i]
+            flat[i] = keep + h
+            lp = loss(per_head(d), dy, dHT)
+            flat[i] = keep - h
+            lm = loss(per_head(d), dy, dHT)
+            flat[i] = keep
+            num[i] = (lp - lm) / (2 * h)
+        summed = g[gx].sum(axis=2, keepdims=True)
+        err = np.max(np.abs(num.reshape(summed.shape) - summed)) / max(1e-3, np.max(np.abs(num)))
+        assert err < 1e-6, (x, err)
