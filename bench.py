@@ -120,10 +120,26 @@ def bench_backward(args) -> int:
     B, T, N, K, V = w.B, w.T, w.N, w.K, w.V
     dims = m2.Dims(B, T, N, K, V)
     dt = m2.DTYPE_BF16 if w.qkv_dtype == "bf16" else m2.DTYPE_F32
-    ws = torch.empty(max(m2.m2rnn_bwd_workspace_size(dims, dt, "auto"), 1), dtype=torch.uint8, device=dev)
+    train = getattr(args, "train", False)
+    if train:
+        # One training step of the layer: the forward keeping checkpoints, then the backward from them.
+        ws = torch.empty(max(m2.m2rnn_bwd_ckpt_workspace_size(dims, dt, "auto"), 1), dtype=torch.uint8, device=dev)
+        fws = torch.empty(max(m2.m2rnn_fwd_workspace_size(dims, dt, "auto"), 1), dtype=torch.uint8, device=dev)
+        y = torch.empty((B, T, N, V), dtype=torch.float32, device=dev)
+        H_T = torch.empty((B, N, K, V), dtype=torch.float32, device=dev)
+        ck = torch.empty((B, N, m2.checkpoint_count(T), K, V), dtype=torch.float32, device=dev)
 
-    def step():
-        return m2.m2rnn_bwd(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], None, t["dy"], None, workspace=ws)
+        def step():
+            m2.m2rnn_fwd_ckpt(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], None, y=y, H_T=H_T, ckpt=ck,
+                              workspace=fws)
+            return m2.m2rnn_bwd_ckpt(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], ck, t["dy"], None,
+                                     workspace=ws)
+    else:
+        ws = torch.empty(max(m2.m2rnn_bwd_workspace_size(dims, dt, "auto"), 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            return m2.m2rnn_bwd(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], None, t["dy"], None,
+                                workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -136,7 +152,9 @@ def bench_backward(args) -> int:
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     hs = B * N * T
-    out = {"metric": "M²RNN bwd (BPTT) head-steps/sec", "value": hs / (ms * 1e-3), "unit": "head-steps/s",
+    metric = ("M²RNN training step (fwd keeping checkpoints + BPTT) head-steps/sec" if train
+              else "M²RNN bwd (BPTT) head-steps/sec")
+    out = {"metric": metric, "value": hs / (ms * 1e-3), "unit": "head-steps/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "config": {"workload": w.name, "B": B, "T": T, "N": N, "K": K, "V": V, "qkv_dtype": w.qkv_dtype,
@@ -244,6 +262,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--backward", action="store_true",
                     help="time m2rnn_bwd on the BPTT workload instead of the forward (its own JSON line)")
+    ap.add_argument("--train", action="store_true",
+                    help="time one training step of the layer (m2rnn_fwd_ckpt + m2rnn_bwd_ckpt) on the BPTT workload")
     ap.add_argument("--decode", action="store_true",
                     help="time m2rnn_decode_step on the batch-128 decode workload (its own JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -265,7 +285,7 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    if args.backward:
+    if args.backward or args.train:
         return bench_backward(args)
     if args.decode:
         return bench_decode(args)

@@ -149,6 +149,32 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
               void* stream);
 
 /*
+ * Training pair: a forward that keeps the backward's checkpoints, and a backward that takes them
+ * instead of re-running the recurrence.  The notes' §2.6 re-runs the recurrence at the start of the
+ * backward so that the forward keeps no history; when a training step runs the forward anyway,
+ * keeping only the states that enter every M2RNN_BWD_CHECKPOINT-step segment (1/64 of the states)
+ * lets the backward skip that re-run.
+ *
+ * m2rnn_fwd_ckpt     m2rnn_fwd plus `ckpt` [B,N,ceil(T/64),K,V] fp32: ckpt[b][n][s] is the state
+ *                    entering step 64 s (ckpt[b][n][0] = H0, or zeros).  Required when T > 0.
+ * m2rnn_bwd_ckpt     m2rnn_bwd with `ckpt` from m2rnn_fwd_ckpt on the same inputs in place of H0
+ *                    (H0 is ckpt[., ., 0]); its workspace (m2rnn_bwd_ckpt_workspace_size) excludes
+ *                    the checkpoints.  Gradients equal m2rnn_bwd's when the forward used the
+ *                    F16X3 contraction (the backward's own); another contraction mode gives
+ *                    checkpoints, and so gradients, that differ within that mode's error.
+ */
+int m2rnn_fwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q,
+                   const void* k, const void* v, const float* f, const float* W, const float* w_r,
+                   const float* H0, float* y, float* H_T, float* ckpt, void* workspace,
+                   size_t workspace_bytes, void* stream);
+int m2rnn_bwd_ckpt_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes);
+int m2rnn_bwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k,
+                   const void* v, const float* f, const float* W, const float* w_r, const float* ckpt,
+                   const float* dy, const float* dH_T, float* dq, float* dk, float* dv, float* df,
+                   float* dW, float* dw_r, float* dH0, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
  * One step of Eq. (10)-(12) for every (b, n), with the state kept in device memory: the decode
  * (token-by-token inference) form of the layer.  The notes point out that inference carries a
  * fixed-size recurrent state (§2.6); this call reads it, advances it by one token and writes it

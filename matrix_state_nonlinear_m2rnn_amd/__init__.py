@@ -30,6 +30,7 @@ BWD_CHECKPOINT = 64
 EXPORTED = (
     "m2rnn_version", "m2rnn_status_string", "m2rnn_last_hip_error", "m2rnn_fwd_workspace_size", "m2rnn_fwd",
     "m2rnn_scan_fwd", "m2rnn_scan_fwd_finish", "m2rnn_bwd_workspace_size", "m2rnn_bwd", "m2rnn_decode_step",
+    "m2rnn_fwd_ckpt", "m2rnn_bwd_ckpt_workspace_size", "m2rnn_bwd_ckpt",
 )
 
 
@@ -76,6 +77,12 @@ def lib() -> ctypes.CDLL:
             L.m2rnn_bwd_workspace_size.argtypes = [dp, ci, ci, ctypes.POINTER(sz)]
             L.m2rnn_bwd.restype = ci
             L.m2rnn_bwd.argtypes = [dp, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp] + [vp] * 7 + [vp, sz, vp]
+        L.m2rnn_fwd_ckpt.restype = ci
+        L.m2rnn_fwd_ckpt.argtypes = [dp, ci, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp, vp] + [vp, sz, vp]
+        L.m2rnn_bwd_ckpt_workspace_size.restype = ci
+        L.m2rnn_bwd_ckpt_workspace_size.argtypes = [dp, ci, ci, ctypes.POINTER(sz)]
+        L.m2rnn_bwd_ckpt.restype = ci
+        L.m2rnn_bwd_ckpt.argtypes = [dp, ci, ci] + [vp] * 3 + [vp] * 3 + [vp] + [vp, vp] + [vp] * 7 + [vp, sz, vp]
         L.m2rnn_decode_step.restype = ci
         L.m2rnn_decode_step.argtypes = [dp, ci, ci] + [vp] * 3 + [vp] * 3 + [vp, vp, vp, vp]
         _lib = L
@@ -188,6 +195,29 @@ def _call_fwd(name, q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, workspace,
     return y, H_T, ws
 
 
+def checkpoint_count(T: int) -> int:
+    """Segments of BWD_CHECKPOINT steps: the checkpoints a forward keeps for the backward."""
+    return (T + BWD_CHECKPOINT - 1) // BWD_CHECKPOINT
+
+
+def m2rnn_fwd_ckpt(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int = 0, y=None, H_T=None, ckpt=None,
+                   workspace=None, stream=None):
+    """m2rnn_fwd that also keeps the backward's checkpoints: returns (y, H_T, ckpt) with ckpt
+    [B,N,ceil(T/64),K,V] fp32, the state entering every 64-step segment (for m2rnn_bwd_ckpt)."""
+    import torch
+    dims, dt, m, rb, y, H_T = _fwd_prepare(q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, True)
+    shape = (dims.B, dims.N, checkpoint_count(dims.T), dims.K, dims.V)
+    if ckpt is None:
+        ckpt = torch.empty(shape, dtype=torch.float32, device=q.device)
+    _require(ckpt, "ckpt", torch.float32, shape, q.device)
+    nbytes = m2rnn_fwd_workspace_size(dims, dt, m, rb)
+    ws = _workspace(nbytes, q.device, workspace)
+    _check("m2rnn_fwd_ckpt", lib().m2rnn_fwd_ckpt(
+        ctypes.byref(dims), dt, m, rb, _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(y),
+        _ptr(H_T), _ptr(ckpt), _ptr(ws), nbytes, _stream(stream)))
+    return y, H_T, ckpt
+
+
 def m2rnn_fwd(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int = 0, y=None, H_T=None, workspace=None,
               stream=None, return_state: bool = True) -> Tuple[object, Optional[object]]:
     """Forward recurrence (M²RNN notes §2.1, Eq. 10-12) on the current HIP stream.
@@ -221,6 +251,36 @@ def m2rnn_bwd_workspace_size(dims: Dims, qkv_dtype: int, math="auto") -> int:
     _check("m2rnn_bwd_workspace_size",
            lib().m2rnn_bwd_workspace_size(ctypes.byref(dims), qkv_dtype, _math(math), ctypes.byref(n)))
     return int(n.value)
+
+
+def m2rnn_bwd_ckpt_workspace_size(dims: Dims, qkv_dtype: int, math="auto") -> int:
+    n = ctypes.c_size_t(0)
+    _check("m2rnn_bwd_ckpt_workspace_size",
+           lib().m2rnn_bwd_ckpt_workspace_size(ctypes.byref(dims), qkv_dtype, _math(math), ctypes.byref(n)))
+    return int(n.value)
+
+
+def m2rnn_bwd_ckpt(q, k, v, f, W, w_r, ckpt, dy, dH_T=None, *, math="auto", want_dH0: bool = True, workspace=None,
+                   stream=None) -> Dict[str, object]:
+    """m2rnn_bwd from the checkpoints that m2rnn_fwd_ckpt kept (no forward re-run)."""
+    import torch
+    dims, dt, m, _, _, _ = _fwd_prepare(q, k, v, f, W, w_r, None, None, None, math, 0, False)
+    B, T, N, K, V, Nqk = dims.B, dims.T, dims.N, dims.K, dims.V, dims.Nqk
+    dev = q.device
+    _require(ckpt, "ckpt", torch.float32, (B, N, checkpoint_count(T), K, V), dev)
+    _require(dy, "dy", torch.float32, (B, T, N, V), dev)
+    if dH_T is not None:
+        _require(dH_T, "dH_T", torch.float32, (B, N, K, V), dev)
+    e = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
+    out = {"dq": e(B, T, Nqk, K), "dk": e(B, T, Nqk, K), "dv": e(B, T, N, V), "df": e(B, T, N), "dW": e(N, V, V),
+           "dw_r": e(N, V), "dH0": e(B, N, K, V) if want_dH0 else None}
+    nbytes = m2rnn_bwd_ckpt_workspace_size(dims, dt, m)
+    ws = _workspace(nbytes, dev, workspace)
+    _check("m2rnn_bwd_ckpt", lib().m2rnn_bwd_ckpt(
+        ctypes.byref(dims), dt, m, _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(ckpt), _ptr(dy),
+        _ptr(dH_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dW"]),
+        _ptr(out["dw_r"]), _ptr(out["dH0"]), _ptr(ws), nbytes, _stream(stream)))
+    return out
 
 
 def m2rnn_bwd(q, k, v, f, W, w_r, H0, dy, dH_T=None, *, math="auto", want_dH0: bool = True, workspace=None,

@@ -145,6 +145,7 @@ struct FwdCall {
   void* ws;
   size_t ws_bytes;
   hipStream_t stream;
+  float* ckpt = nullptr;  // optional: states entering every kBwdSeg-step segment
 };
 
 // Validates a forward call; on success fills the resolved math mode and row blocks.
@@ -159,7 +160,7 @@ int check_fwd(const FwdCall& c, int* math_out, int* rb_out) {
   if (!empty) {
     if (!c.W || !c.w_r) return M2RNN_EINVAL;
     if (d->T > 0 && (!c.q || !c.k || !c.v || !c.f || !c.y)) return M2RNN_EINVAL;
-    const void* ptrs[] = {c.q, c.k, c.v, c.W, c.w_r, c.H0, c.y, c.H_T};
+    const void* ptrs[] = {c.q, c.k, c.v, c.W, c.w_r, c.H0, c.y, c.H_T, c.ckpt};
     for (const void* p : ptrs)
       if (p && !aligned16(p)) return M2RNN_EINVAL;
     if (c.f && ((uintptr_t)c.f & 3u)) return M2RNN_EINVAL;
@@ -179,18 +180,18 @@ int launch_scan(const FwdCall& c, int math, int rb) {
   const bool bf16 = c.qkv_dtype == M2RNN_DTYPE_BF16;
   const int S = (int)(d->K / (16 * rb));
   if (d->T == 0) {
-    // Nothing to scan: H_T = H0 (or zeros).
+    // Nothing to scan: H_T = H0 (or zeros); there are no segments to checkpoint.
     return fill(c.H_T, c.H0, d->B * d->N * d->K * d->V, c.stream);
   }
   FwdArgs a{};
   a.q = c.q; a.k = c.k; a.v = c.v; a.f = c.f; a.W = c.W; a.w_r = c.w_r; a.H0 = c.H0;
   a.y = S > 1 ? (float*)c.ws : c.y;
   a.H_T = c.H_T;
-  a.ckpt = nullptr;
+  a.ckpt = c.ckpt;
   a.B = (int)d->B; a.T = (int)d->T; a.N = (int)d->N; a.K = (int)d->K;
   a.Nqk = qk_heads(d);
   a.S = S;
-  a.seg = 0;
+  a.seg = c.ckpt ? kBwdSeg : 0;
   const void* kern = fwd_kernel(math, (int)d->V, rb, bf16, MODE_FWD);
   if (!kern) return M2RNN_EUNSUPPORTED;
   void* args[] = {&a};
@@ -218,7 +219,16 @@ int launch_finish(const FwdCall& c, int rb) {
 
 struct BwdLayout {
   size_t ckpt = 0, seg = 0, dv = 0, df = 0, dW = 0, dwr = 0, dq = 0, dk = 0, total = 0;
+  size_t total_no_ckpt = 0;  // the workspace when the caller supplies the checkpoints
 };
+
+static_assert(kBwdSeg % FwdShape<64>::TC == 0, "forward checkpoints are taken at the first step of a chunk");
+
+// Checkpoints: [B][N][ceil(T / kBwdSeg)][K][V] fp32.
+size_t ckpt_bytes(const m2rnn_dims* d) {
+  const long nseg = (d->T + kBwdSeg - 1) / kBwdSeg;
+  return (size_t)d->B * d->N * nseg * d->K * d->V * sizeof(float);
+}
 
 // A shared query/key (Nqk = 1) with several heads: per-head dq, dk go to the workspace and are
 // summed over the heads afterwards.
@@ -234,7 +244,6 @@ BwdLayout bwd_layout(const m2rnn_dims* d) {
     off += round_up(bytes);
     return at;
   };
-  L.ckpt = take((size_t)d->B * d->N * nseg * d->K * d->V * sizeof(float));
   const long nsub = kBwdSeg / (d->V <= 32 ? BwdSub<32>::value : d->V == 64 ? BwdSub<64>::value : BwdSub<128>::value);
   L.seg = take((size_t)d->B * d->N * S * nsub * 16 * d->V * sizeof(float));
   L.dv = take(S > 1 ? (size_t)S * d->B * d->T * d->N * d->V * sizeof(float) : 0);
@@ -244,6 +253,8 @@ BwdLayout bwd_layout(const m2rnn_dims* d) {
   const size_t qk_part = shared_qk_sum(d) ? (size_t)d->B * d->T * d->N * d->K * sizeof(float) : 0;
   L.dq = take(qk_part);
   L.dk = take(qk_part);
+  L.total_no_ckpt = off;
+  L.ckpt = take(ckpt_bytes(d));
   L.total = off;
   return L;
 }
@@ -337,10 +348,16 @@ int m2rnn_bwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, si
   return M2RNN_OK;
 }
 
-int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k, const void* v,
-              const float* f, const float* W, const float* w_r, const float* H0, const float* dy,
-              const float* dH_T, float* dq, float* dk, float* dv, float* df, float* dW, float* dw_r, float* dH0,
-              void* workspace, size_t workspace_bytes, void* stream_) {
+}  // extern "C"
+
+namespace {
+
+// The backward; ckpt_in = the checkpoints of a forward that kept them (then no forward re-run), or
+// null (then the checkpoints are computed here, into the workspace).
+int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k, const void* v,
+             const float* f, const float* W, const float* w_r, const float* H0, const float* ckpt_in,
+             const float* dy, const float* dH_T, float* dq, float* dk, float* dv, float* df, float* dW, float* dw_r,
+             float* dH0, void* workspace, size_t workspace_bytes, void* stream_) {
   int st = check_dims(dims, qkv_dtype);
   if (st) return st;
   const int m = resolve_bwd_math(math);
@@ -353,7 +370,7 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
   if (!W || !w_r || !dW || !dw_r) return M2RNN_EINVAL;
   if (d->T > 0 && (!q || !k || !v || !f || !dy || !dq || !dk || !dv || !df)) return M2RNN_EINVAL;
   {
-    const void* ptrs[] = {q, k, v, W, w_r, H0, dy, dH_T, dq, dk, dv, dW, dw_r, dH0};
+    const void* ptrs[] = {q, k, v, W, w_r, H0, ckpt_in, dy, dH_T, dq, dk, dv, dW, dw_r, dH0};
     for (const void* p : ptrs)
       if (p && !aligned16(p)) return M2RNN_EINVAL;
     if ((f && ((uintptr_t)f & 3u)) || (df && ((uintptr_t)df & 3u))) return M2RNN_EINVAL;
@@ -366,12 +383,14 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
     return fill(dH0, dH_T, B * N * K * V, stream);
   }
   const BwdLayout L = bwd_layout(d);
-  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return M2RNN_EWORKSPACE;
+  const size_t need = ckpt_in ? L.total_no_ckpt : L.total;
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return M2RNN_EWORKSPACE;
   char* ws = (char*)workspace;
   const int S = (int)(K / 16);
 
-  // 1. Checkpoints: the state entering every kBwdSeg-step segment.
-  {
+  // 1. Checkpoints: the state entering every kBwdSeg-step segment (unless the forward kept them).
+  const float* ckpt = ckpt_in ? ckpt_in : (const float*)(ws + L.ckpt);
+  if (!ckpt_in) {
     FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.H0 = H0;
     a.y = nullptr; a.H_T = nullptr; a.ckpt = (float*)(ws + L.ckpt);
@@ -387,7 +406,7 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
   {
     BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.dy = dy; a.dH_T = dH_T;
-    a.ckpt = (const float*)(ws + L.ckpt);
+    a.ckpt = ckpt;
     a.subck = (float*)(ws + L.seg);
     const bool sum_qk = shared_qk_sum(d);
     a.dq = sum_qk ? (float*)(ws + L.dq) : dq;
@@ -426,6 +445,52 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
   hipLaunchKernelGGL(m2rnn_bwd_sum_dwr_kernel, dim3((unsigned)((N * V + 255) / 256)), dim3(256), 0, stream,
                      (const float*)(ws + L.dwr), (int)B, (int)(N * V), dw_r);
   return hip_status(hipGetLastError());
+}
+
+}  // namespace
+
+extern "C" {
+
+int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k, const void* v,
+              const float* f, const float* W, const float* w_r, const float* H0, const float* dy,
+              const float* dH_T, float* dq, float* dk, float* dv, float* df, float* dW, float* dw_r, float* dH0,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(dims, qkv_dtype, math, q, k, v, f, W, w_r, H0, nullptr, dy, dH_T, dq, dk, dv, df, dW, dw_r, dH0,
+                  workspace, workspace_bytes, stream);
+}
+
+int m2rnn_bwd_ckpt_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes) {
+  if (!bytes) return M2RNN_EINVAL;
+  int st = check_dims(dims, qkv_dtype);
+  if (st) return st;
+  const int m = resolve_bwd_math(math);
+  if (m == -1) return M2RNN_EINVAL;
+  if (m == -2) return M2RNN_EUNSUPPORTED;
+  *bytes = (dims->B == 0 || dims->N == 0 || dims->T == 0) ? 0 : bwd_layout(dims).total_no_ckpt;
+  return M2RNN_OK;
+}
+
+int m2rnn_bwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k, const void* v,
+                   const float* f, const float* W, const float* w_r, const float* ckpt, const float* dy,
+                   const float* dH_T, float* dq, float* dk, float* dv, float* df, float* dW, float* dw_r, float* dH0,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (dims && dims->T > 0 && dims->B > 0 && dims->N > 0 && !ckpt) return M2RNN_EINVAL;
+  return bwd_impl(dims, qkv_dtype, math, q, k, v, f, W, w_r, nullptr, ckpt, dy, dH_T, dq, dk, dv, df, dW, dw_r,
+                  dH0, workspace, workspace_bytes, stream);
+}
+
+int m2rnn_fwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q, const void* k,
+                   const void* v, const float* f, const float* W, const float* w_r, const float* H0, float* y,
+                   float* H_T, float* ckpt, void* workspace, size_t workspace_bytes, void* stream) {
+  FwdCall c{dims, qkv_dtype, math, row_blocks, q, k, v, f, W, w_r, H0, y, H_T, workspace, workspace_bytes,
+            (hipStream_t)stream, ckpt};
+  int m = 0, rb = 0;
+  int st = check_fwd(c, &m, &rb);
+  if (st) return st;
+  if (dims->T > 0 && dims->B > 0 && dims->N > 0 && !ckpt) return M2RNN_EINVAL;
+  st = launch_scan(c, m, rb);
+  if (st) return st;
+  return launch_finish(c, rb);
 }
 
 int m2rnn_decode_step(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k,

@@ -37,11 +37,12 @@ struct FwdArgs {
   const float* H0;
   float* y;       // final readout (S == 1) or partial readouts [S][B*T*N*V] (S > 1)
   float* H_T;     // may be null
-  float* ckpt;    // checkpoint mode: states entering each segment [B][N][nseg][K][V]
+  float* ckpt;    // states entering each seg-step segment [B][N][nseg][K][V] (checkpoint mode;
+                  // optional in the forward mode, null = none)
   int B, T, N, K;
   int Nqk;        // heads of q and k: N, or 1 when one query/key is shared by all heads
   int S;          // workgroups per (b, n)
-  int seg;        // checkpoint interval (checkpoint mode)
+  int seg;        // checkpoint interval, a multiple of TC (when ckpt is set)
 };
 
 template <int V>
@@ -422,7 +423,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   if (a.T > TC) pre.load(a, b, nh, row0, TC, tid);
   publish(0);
 
-  const int nseg = MODE == MODE_CKPT ? (a.T + a.seg - 1) / a.seg : 0;
+  const int nseg = a.seg > 0 ? (a.T + a.seg - 1) / a.seg : 0;
 
   lds_barrier();
 
@@ -468,7 +469,10 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
       const int t = c0 + j;
-      if constexpr (MODE == MODE_CKPT) {
+      // The state entering every seg-step segment (checkpoint mode, or a forward asked to keep
+      // checkpoints for the backward).  seg is a multiple of TC, so only a chunk's first step can
+      // start a segment.
+      if (j == 0 && (MODE == MODE_CKPT || a.ckpt != nullptr)) {
         if (t % a.seg == 0 && t < a.T) {
           float* dst = a.ckpt + ((long)(b * a.N + nh) * nseg + t / a.seg) * KV;
 #pragma unroll

@@ -94,3 +94,19 @@ def test_shared_query_key_head_count_is_checked():
     assert fwd(D(1, 4, 3, 16, 16, 2)) == m2.M2RNN_EINVAL      # Nqk must be 0, 1 or N
     assert fwd(D(1, 4, 3, 16, 16, -1)) == m2.M2RNN_EINVAL
     assert decode(D(2, 1, 3, 16, 16, 2)) == m2.M2RNN_EINVAL
+
+
+def test_checkpoint_entry_points_check_their_arguments():
+    L = m2.lib()
+    D = m2.Dims
+    p = ctypes.c_void_p(16)
+    dims = D(1, 4, 2, 16, 16)
+    # forward that keeps checkpoints: the checkpoint buffer is required when there are steps
+    assert L.m2rnn_fwd_ckpt(ctypes.byref(dims), 0, -1, 0, p, p, p, p, p, p, None, p, None, None, None, 0,
+                            None) == m2.M2RNN_EINVAL
+    # backward from checkpoints: likewise
+    assert L.m2rnn_bwd_ckpt(ctypes.byref(dims), 0, -1, p, p, p, p, p, p, None, p, None, p, p, p, p, p, p, None,
+                            p, 1 << 30, None) == m2.M2RNN_EINVAL
+    # its workspace excludes the checkpoints
+    big = m2.Dims(4, 4096, 16, 64, 64)
+    assert m2.m2rnn_bwd_ckpt_workspace_size(big, 0) + 4 * 16 * 64 * 64 * 64 * 4 <= m2.m2rnn_bwd_workspace_size(big, 0)

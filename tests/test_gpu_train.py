@@ -1,0 +1,100 @@
+"""GPU parity of the training pair: m2rnn_fwd_ckpt (the forward keeping the state that enters every
+64-step segment) and m2rnn_bwd_ckpt (the backward from those checkpoints, without re-running the
+recurrence), against the fp64 oracle and against m2rnn_fwd / m2rnn_bwd."""
+import numpy as np
+import pytest
+
+from matrix_state_nonlinear_m2rnn_amd import inputs
+
+from _gpu import TOL, max_abs, oracle_bwd, oracle_fwd, rel_l2, say, to_device, torch_cuda
+
+pytestmark = pytest.mark.gpu
+GRADS = ("dq", "dk", "dv", "df", "dW", "dw_r", "dH0")
+
+
+def fwd_ckpt(dd, math="auto"):
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    return m2.m2rnn_fwd_ckpt(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], dd.get("H0"), math=math)
+
+
+@pytest.mark.parametrize("B,T,N,K,V,dtype,shared", [
+    (2, 200, 3, 32, 64, "bf16", False),   # four segments, the last one ragged
+    (1, 64, 2, 64, 16, "f32", True),      # exactly one segment, shared q/k
+    (2, 129, 2, 16, 128, "bf16", False),
+])
+def test_forward_checkpoints(B, T, N, K, V, dtype, shared):
+    torch = torch_cuda()
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    d = inputs.make_inputs(B, T, N, K, V, qkv_dtype=dtype, seed=700 + T, with_H0=True, shared_qk=shared)
+    say("fwd ckpt", B, T, N, K, V, dtype, shared)
+    dd = to_device(d, dtype)
+    y, H_T, ck = fwd_ckpt(dd)
+    y0, H0T = m2.m2rnn_fwd(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], dd["H0"])
+    torch.cuda.synchronize()
+    # Keeping checkpoints changes nothing else.
+    assert torch.equal(y, y0) and torch.equal(H_T, H0T)
+    ck = ck.cpu().numpy()
+    assert ck.shape == (B, N, (T + 63) // 64, K, V)
+    assert np.array_equal(ck[:, :, 0], d["H0"])
+    for s in range(1, ck.shape[2]):
+        sub = {x: (a[:, :64 * s] if x in ("q", "k", "v", "f") else a) for x, a in d.items() if a is not None}
+        _, Hs = oracle_fwd(sub)
+        e = max_abs(ck[:, :, s], Hs)
+        say("segment", s, e)
+        assert e <= TOL["f16x3"], (s, e)
+
+
+@pytest.mark.parametrize("B,T,N,K,V,dtype,shared", [
+    (2, 130, 3, 32, 64, "bf16", False),
+    (1, 70, 4, 64, 16, "bf16", True),
+    (1, 65, 1, 16, 128, "f32", False),
+])
+def test_backward_from_checkpoints(B, T, N, K, V, dtype, shared):
+    torch = torch_cuda()
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    d = inputs.make_inputs(B, T, N, K, V, qkv_dtype=dtype, seed=800 + T, with_H0=True, with_dy=True, with_dHT=True,
+                           shared_qk=shared)
+    say("bwd ckpt", B, T, N, K, V, dtype, shared)
+    dd = to_device(d, dtype)
+    _, _, ck = fwd_ckpt(dd, "f16x3")
+    g = m2.m2rnn_bwd_ckpt(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], ck, dd["dy"], dd["dH_T"])
+    g0 = m2.m2rnn_bwd(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], dd["H0"], dd["dy"], dd["dH_T"])
+    torch.cuda.synchronize()
+    # The same checkpoints as the backward's own re-run: the same gradients, bit for bit.
+    for n in GRADS:
+        assert torch.equal(g[n], g0[n]), n
+    ref = oracle_bwd(d)
+    errs = {n: rel_l2(g[n].cpu().numpy(), ref[n]) for n in GRADS}
+    say("rel-L2", errs)
+    for n, e in errs.items():
+        assert e <= 1e-3, (n, e)
+
+
+def test_backward_from_fp32_contraction_checkpoints():
+    # Checkpoints from another contraction mode differ within that mode's error; the gradients
+    # still meet the budget.
+    torch_cuda()
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    d = inputs.make_inputs(2, 150, 2, 64, 64, qkv_dtype="bf16", seed=99, with_dy=True)
+    dd = to_device(d, "bf16")
+    _, _, ck = fwd_ckpt(dd, "f32")
+    g = m2.m2rnn_bwd_ckpt(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], ck, dd["dy"])
+    ref = oracle_bwd(d)
+    for n in GRADS:
+        e = rel_l2(g[n].cpu().numpy(), ref[n])
+        assert e <= 1e-3, (n, e)
+
+
+def test_training_pair_on_the_bwd_workload():
+    # B4 N16 T4096 K=V=64 fp32: the pair gives exactly m2rnn_bwd's gradients.
+    torch = torch_cuda()
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    d = inputs.workload_inputs("bwd_b4_h16_t4096_kv64")
+    say("bwd_b4_h16_t4096_kv64 training pair")
+    dd = to_device(d, "f32")
+    _, _, ck = fwd_ckpt(dd)
+    g = m2.m2rnn_bwd_ckpt(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], ck, dd["dy"])
+    g0 = m2.m2rnn_bwd(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], None, dd["dy"])
+    torch.cuda.synchronize()
+    for n in GRADS:
+        assert torch.equal(g[n], g0[n]), n
