@@ -8,6 +8,9 @@ The arithmetic lives in ``m2rnn_ref.c`` (plain fp64 loops in the order of the Mย
 ยง2.1 Eq. (10)-(12) for the forward and ยง2.7's corrected BPTT for the backward); this file only
 builds that library with gcc and marshals numpy arrays into it.
 
+The steps on either side of the recurrence (the gate of ยง2.2, the output gate + RMSNorm and the
+causal conv4 + SiLU of ยง2.3) are plain numpy fp64 in ``oracle/block.py``.
+
 Pins: every function here is pinned by ``tests/test_oracle_*.py`` against facts that do not come
 from the oracle itself (closed forms, invariants, a library tanh-RNN, finite differences).
 """
