@@ -193,6 +193,57 @@ int m2rnn_decode_step(const m2rnn_dims* dims, int qkv_dtype, int math, const voi
                       const void* v, const float* f, const float* W, const float* w_r,
                       const float* H_in, float* H_out, float* y, void* stream);
 
+/*
+ * The steps on either side of the recurrence in the M²RNN block (§2.2, §2.3).  Each is an
+ * HBM-bound stream with its backward; reductions over batch and time run in a fixed order.
+ * Sizes are passed directly; every call enqueues on `stream` and validates arguments on the host
+ * like the calls above.
+ *
+ * Gate (§2.2, Eq. 13/17): f = (1 + e^{a + beta})^{-alpha} = exp(-alpha softplus(a + beta)), with
+ * a the gate pre-activation [B,T,N] (fp32) and alpha, beta [N] per head (alpha >= 0 keeps f in
+ * [0, 1]; not checked).  f [B,T,N] fp32 is the recurrence's f.  The backward takes df (the
+ * recurrence backward's gradient of f) and gives da [B,T,N] and dalpha, dbeta [N] (summed over
+ * batch and time); its workspace holds B T N floats.  Pointers 4-byte aligned.
+ */
+int m2rnn_gate_fwd(int64_t B, int64_t T, int64_t N, const float* a, const float* alpha,
+                   const float* beta, float* f, void* stream);
+int m2rnn_gate_bwd_workspace_size(int64_t B, int64_t T, int64_t N, size_t* bytes);
+int m2rnn_gate_bwd(int64_t B, int64_t T, int64_t N, const float* a, const float* alpha,
+                   const float* beta, const float* df, float* da, float* dalpha, float* dbeta,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Output gate + RMSNorm (§2.3, step 4; the norm's statistic and gradient as in Appendix C):
+ *     x = y (.) SiLU(gz),   out = gamma (.) x / sqrt(mean_j x_j^2 + eps)
+ * normalised over the D features of each of `rows` rows: y, out [rows, D] fp32 (for the layer's
+ * y [B,T,N,V], rows = B T and D = N V, so the statistic spans all heads), gz the output gate's
+ * pre-activation [rows, D] (gz_dtype fp32 or bf16), gamma [D] fp32.  The gate multiplies before
+ * the norm.  eps >= 0 is the caller's (the notes leave it out).  D a multiple of 4, at most 8192.
+ * The backward gives dy, dgz [rows, D] fp32 and dgamma [D] (summed over rows).  Pointers 16-byte
+ * aligned.
+ */
+int m2rnn_out_norm_fwd(int64_t rows, int64_t D, const float* y, const void* gz, int gz_dtype,
+                       const float* gamma, float eps, float* out, void* stream);
+int m2rnn_out_norm_bwd_workspace_size(int64_t rows, int64_t D, size_t* bytes);
+int m2rnn_out_norm_bwd(int64_t rows, int64_t D, const float* y, const void* gz, int gz_dtype,
+                       const float* gamma, float eps, const float* dout, float* dy, float* dgz,
+                       float* dgamma, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Causal depthwise Conv1D of kernel size 4 + SiLU (§2.3, step 1), applied to each of q, k, v:
+ *     u_t[c] = SiLU(sum_{i<4} w[c][i] x_{t-3+i}[c] + bias[c]),   x_t = 0 for t < 0
+ * x, u [B,T,C] in `dtype` (fp32 or bf16; u is rounded to nearest even for bf16), w [C,4] fp32,
+ * bias [C] fp32 or NULL (none).  C a multiple of 4.  The backward takes du [B,T,C] fp32 and gives
+ * dx [B,T,C], dw [C,4] and dbias [C] (NULL to skip) fp32, summed over batch and time.  Pointers
+ * 16-byte aligned.
+ */
+int m2rnn_conv4_silu_fwd(int64_t B, int64_t T, int64_t C, int dtype, const void* x, const float* w,
+                         const float* bias, void* u, void* stream);
+int m2rnn_conv4_silu_bwd_workspace_size(int64_t B, int64_t T, int64_t C, size_t* bytes);
+int m2rnn_conv4_silu_bwd(int64_t B, int64_t T, int64_t C, int dtype, const void* x, const float* w,
+                         const float* bias, const float* du, float* dx, float* dw, float* dbias,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,6 +31,9 @@ EXPORTED = (
     "m2rnn_version", "m2rnn_status_string", "m2rnn_last_hip_error", "m2rnn_fwd_workspace_size", "m2rnn_fwd",
     "m2rnn_scan_fwd", "m2rnn_scan_fwd_finish", "m2rnn_bwd_workspace_size", "m2rnn_bwd", "m2rnn_decode_step",
     "m2rnn_fwd_ckpt", "m2rnn_bwd_ckpt_workspace_size", "m2rnn_bwd_ckpt",
+    "m2rnn_gate_fwd", "m2rnn_gate_bwd_workspace_size", "m2rnn_gate_bwd",
+    "m2rnn_out_norm_fwd", "m2rnn_out_norm_bwd_workspace_size", "m2rnn_out_norm_bwd",
+    "m2rnn_conv4_silu_fwd", "m2rnn_conv4_silu_bwd_workspace_size", "m2rnn_conv4_silu_bwd",
 )
 
 
@@ -83,6 +86,21 @@ def lib() -> ctypes.CDLL:
         L.m2rnn_bwd_ckpt_workspace_size.argtypes = [dp, ci, ci, ctypes.POINTER(sz)]
         L.m2rnn_bwd_ckpt.restype = ci
         L.m2rnn_bwd_ckpt.argtypes = [dp, ci, ci] + [vp] * 3 + [vp] * 3 + [vp] + [vp, vp] + [vp] * 7 + [vp, sz, vp]
+        i64, cf = ctypes.c_int64, ctypes.c_float
+        for name, args in (
+            ("m2rnn_gate_fwd", [i64] * 3 + [vp] * 4 + [vp]),
+            ("m2rnn_gate_bwd_workspace_size", [i64] * 3 + [ctypes.POINTER(sz)]),
+            ("m2rnn_gate_bwd", [i64] * 3 + [vp] * 7 + [vp, sz, vp]),
+            ("m2rnn_out_norm_fwd", [i64, i64, vp, vp, ci, vp, cf, vp, vp]),
+            ("m2rnn_out_norm_bwd_workspace_size", [i64, i64, ctypes.POINTER(sz)]),
+            ("m2rnn_out_norm_bwd", [i64, i64, vp, vp, ci, vp, cf, vp, vp, vp, vp, vp, sz, vp]),
+            ("m2rnn_conv4_silu_fwd", [i64] * 3 + [ci] + [vp] * 4 + [vp]),
+            ("m2rnn_conv4_silu_bwd_workspace_size", [i64] * 3 + [ctypes.POINTER(sz)]),
+            ("m2rnn_conv4_silu_bwd", [i64] * 3 + [ci] + [vp] * 7 + [vp, sz, vp]),
+        ):
+            fn = getattr(L, name)
+            fn.restype = ci
+            fn.argtypes = args
         L.m2rnn_decode_step.restype = ci
         L.m2rnn_decode_step.argtypes = [dp, ci, ci] + [vp] * 3 + [vp] * 3 + [vp, vp, vp, vp]
         _lib = L
@@ -349,3 +367,123 @@ def m2rnn_decode_step(q, k, v, f, W, w_r, H=None, *, H_out=None, y=None, math="a
         ctypes.byref(dims), dt, _math(math), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H),
         _ptr(H_out), _ptr(y), _stream(stream)))
     return y, H_out
+
+
+# ---------------------------------------------------------------- the steps around the recurrence
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"expected float32 or bfloat16, got {t.dtype}")
+
+
+def _size_query(name, *args) -> int:
+    n = ctypes.c_size_t(0)
+    _check(name, getattr(lib(), name)(*args, ctypes.byref(n)))
+    return int(n.value)
+
+
+def m2rnn_gate_fwd(a, alpha, beta, *, f=None, stream=None):
+    """Gate of the notes' §2.2 (Eq. 13/17): f = exp(-alpha softplus(a + beta)); a [B,T,N], alpha, beta [N]."""
+    import torch
+    B, T, N = a.shape
+    for name, t, shape in (("a", a, (B, T, N)), ("alpha", alpha, (N,)), ("beta", beta, (N,))):
+        _require(t, name, torch.float32, shape, a.device)
+    if f is None:
+        f = torch.empty_like(a)
+    _require(f, "f", torch.float32, (B, T, N), a.device)
+    _check("m2rnn_gate_fwd", lib().m2rnn_gate_fwd(B, T, N, _ptr(a), _ptr(alpha), _ptr(beta), _ptr(f), _stream(stream)))
+    return f
+
+
+def m2rnn_gate_bwd(a, alpha, beta, df, *, workspace=None, stream=None) -> Dict[str, object]:
+    """da [B,T,N], dalpha, dbeta [N] of the gate for the upstream df."""
+    import torch
+    B, T, N = a.shape
+    for name, t, shape in (("a", a, (B, T, N)), ("alpha", alpha, (N,)), ("beta", beta, (N,)), ("df", df, (B, T, N))):
+        _require(t, name, torch.float32, shape, a.device)
+    out = {"da": torch.empty_like(a), "dalpha": torch.empty_like(alpha), "dbeta": torch.empty_like(beta)}
+    nbytes = _size_query("m2rnn_gate_bwd_workspace_size", B, T, N)
+    ws = _workspace(nbytes, a.device, workspace)
+    _check("m2rnn_gate_bwd", lib().m2rnn_gate_bwd(B, T, N, _ptr(a), _ptr(alpha), _ptr(beta), _ptr(df), _ptr(out["da"]),
+                                                  _ptr(out["dalpha"]), _ptr(out["dbeta"]), _ptr(ws), nbytes,
+                                                  _stream(stream)))
+    return out
+
+
+def _norm_dims(y, gamma):
+    D = gamma.numel()
+    if tuple(y.shape[y.dim() - gamma.dim():]) != tuple(gamma.shape):
+        raise ValueError(f"y {tuple(y.shape)} must end with gamma's shape {tuple(gamma.shape)}")
+    return y.numel() // max(D, 1), D
+
+
+def m2rnn_out_norm_fwd(y, gz, gamma, eps: float = 1e-6, *, out=None, stream=None):
+    """Output gate + RMSNorm (§2.3, step 4): gamma (.) x / sqrt(mean x^2 + eps), x = y (.) SiLU(gz),
+    normalised over gamma's features (for y [B,T,N,V] and gamma [N,V]: all heads of a token)."""
+    import torch
+    rows, D = _norm_dims(y, gamma)
+    _require(y, "y", torch.float32, tuple(y.shape), y.device)
+    _require(gz, "gz", (torch.float32, torch.bfloat16), tuple(y.shape), y.device)
+    _require(gamma, "gamma", torch.float32, tuple(gamma.shape), y.device)
+    if out is None:
+        out = torch.empty_like(y)
+    _require(out, "out", torch.float32, tuple(y.shape), y.device)
+    _check("m2rnn_out_norm_fwd", lib().m2rnn_out_norm_fwd(rows, D, _ptr(y), _ptr(gz), _dtype_code(gz), _ptr(gamma),
+                                                          float(eps), _ptr(out), _stream(stream)))
+    return out
+
+
+def m2rnn_out_norm_bwd(y, gz, gamma, dout, eps: float = 1e-6, *, workspace=None, stream=None) -> Dict[str, object]:
+    """dy, dgz (fp32, shaped like y) and dgamma of the output gate + RMSNorm (Appendix C)."""
+    import torch
+    rows, D = _norm_dims(y, gamma)
+    _require(y, "y", torch.float32, tuple(y.shape), y.device)
+    _require(gz, "gz", (torch.float32, torch.bfloat16), tuple(y.shape), y.device)
+    _require(gamma, "gamma", torch.float32, tuple(gamma.shape), y.device)
+    _require(dout, "dout", torch.float32, tuple(y.shape), y.device)
+    out = {"dy": torch.empty_like(y), "dgz": torch.empty_like(y), "dgamma": torch.empty_like(gamma)}
+    nbytes = _size_query("m2rnn_out_norm_bwd_workspace_size", rows, D)
+    ws = _workspace(nbytes, y.device, workspace)
+    _check("m2rnn_out_norm_bwd", lib().m2rnn_out_norm_bwd(
+        rows, D, _ptr(y), _ptr(gz), _dtype_code(gz), _ptr(gamma), float(eps), _ptr(dout), _ptr(out["dy"]),
+        _ptr(out["dgz"]), _ptr(out["dgamma"]), _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def m2rnn_conv4_silu_fwd(x, w, bias=None, *, u=None, stream=None):
+    """Causal depthwise conv (kernel 4) + SiLU (§2.3, step 1): x [B,T,C] fp32/bf16, w [C,4], bias [C] or None."""
+    import torch
+    B, T, C = x.shape
+    _require(x, "x", (torch.float32, torch.bfloat16), (B, T, C), x.device)
+    _require(w, "w", torch.float32, (C, 4), x.device)
+    if bias is not None:
+        _require(bias, "bias", torch.float32, (C,), x.device)
+    if u is None:
+        u = torch.empty_like(x)
+    _require(u, "u", x.dtype, (B, T, C), x.device)
+    _check("m2rnn_conv4_silu_fwd", lib().m2rnn_conv4_silu_fwd(B, T, C, _dtype_code(x), _ptr(x), _ptr(w), _ptr(bias),
+                                                              _ptr(u), _stream(stream)))
+    return u
+
+
+def m2rnn_conv4_silu_bwd(x, w, bias, du, *, workspace=None, stream=None) -> Dict[str, object]:
+    """dx [B,T,C] fp32, dw [C,4] and dbias [C] (None without a bias) of the causal conv4 + SiLU."""
+    import torch
+    B, T, C = x.shape
+    _require(x, "x", (torch.float32, torch.bfloat16), (B, T, C), x.device)
+    _require(w, "w", torch.float32, (C, 4), x.device)
+    if bias is not None:
+        _require(bias, "bias", torch.float32, (C,), x.device)
+    _require(du, "du", torch.float32, (B, T, C), x.device)
+    out = {"dx": torch.empty((B, T, C), dtype=torch.float32, device=x.device), "dw": torch.empty_like(w),
+           "dbias": torch.empty_like(bias) if bias is not None else None}
+    nbytes = _size_query("m2rnn_conv4_silu_bwd_workspace_size", B, T, C)
+    ws = _workspace(nbytes, x.device, workspace)
+    _check("m2rnn_conv4_silu_bwd", lib().m2rnn_conv4_silu_bwd(
+        B, T, C, _dtype_code(x), _ptr(x), _ptr(w), _ptr(bias), _ptr(du), _ptr(out["dx"]), _ptr(out["dw"]),
+        _ptr(out["dbias"]), _ptr(ws), nbytes, _stream(stream)))
+    return out

@@ -24,6 +24,7 @@ SOURCES = [
     "m2rnn_fwd_bf16x3.hip",
     "m2rnn_fwd_bf16.hip",
     "m2rnn_decode.hip",
+    "m2rnn_block.hip",
 ]
 
 # Packed fp32 VALU ops stay off: hipcc -O3 would otherwise form v_pk_{add,mul,fma}_f32.

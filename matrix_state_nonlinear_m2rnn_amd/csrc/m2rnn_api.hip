@@ -22,6 +22,14 @@ int hip_status(hipError_t e) {
   return M2RNN_EHIP;
 }
 
+}  // namespace
+
+namespace m2rnn {
+int record_hip_status(hipError_t e) { return hip_status(e); }
+}  // namespace m2rnn
+
+namespace {
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_dims(const m2rnn_dims* d, int qkv_dtype) {

@@ -1,0 +1,390 @@
+// Kernels for the steps on either side of the recurrence in the M²RNN block (M²RNN notes §2.2,
+// §2.3, Appendix C): the gate f = exp(-alpha softplus(a + beta)), the output gate + RMSNorm over
+// the N V features of a token, and the causal depthwise conv of kernel size 4 + SiLU on q, k, v.
+// All of them are HBM-bound streams; every reduction runs in a fixed order, so results are
+// bit-reproducible.
+#pragma once
+
+#include "m2rnn_device.h"
+
+namespace m2rnn {
+
+constexpr int kBlkThreads = 256;
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+// log(1 + e^x) without overflow.
+__device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
+__device__ __forceinline__ float silu_gradf_(float x) {
+  const float s = sigmoidf_(x);
+  return s * (1.0f + x * (1.0f - s));
+}
+
+template <bool BF16>
+__device__ __forceinline__ float4 load4(const void* base, long i) {
+  if constexpr (BF16) {
+    const uint2 r = *(const uint2*)((const uint16_t*)base + i);
+    return make_float4(bf16_lo_to_f32(r.x), bf16_hi_to_f32(r.x), bf16_lo_to_f32(r.y), bf16_hi_to_f32(r.y));
+  }
+  return *(const float4*)((const float*)base + i);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store4(void* base, long i, float4 v) {
+  if constexpr (BF16) {
+    *(uint2*)((uint16_t*)base + i) = make_uint2(pack_bf16(v.x, v.y), pack_bf16(v.z, v.w));
+  } else {
+    *(float4*)((float*)base + i) = v;
+  }
+}
+
+// Sum over the workgroup (kBlkThreads threads) of a pair of values, in a fixed order; every
+// thread receives the totals.  `red` holds 2 * (kBlkThreads / 64) floats.
+__device__ __forceinline__ float2 block_sum2(float a, float b, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    a += __shfl_xor(a, o);
+    b += __shfl_xor(b, o);
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();  // `red` may still be read by the previous call
+  if ((threadIdx.x & 63) == 0) {
+    red[2 * w] = a;
+    red[2 * w + 1] = b;
+  }
+  __syncthreads();
+  float2 s = make_float2(0.0f, 0.0f);
+#pragma unroll
+  for (int i = 0; i < kBlkThreads / 64; ++i) {
+    s.x += red[2 * i];
+    s.y += red[2 * i + 1];
+  }
+  return s;
+}
+
+// ------------------------------------------------------------------ gate (§2.2, Eq. 13/17)
+
+// f[i] = exp(-alpha[n] softplus(a[i] + beta[n])), i over [B*T, N] (n = i % N).
+__global__ void __launch_bounds__(kBlkThreads) m2rnn_gate_fwd_kernel(const float* __restrict__ a,
+                                                                      const float* __restrict__ alpha,
+                                                                      const float* __restrict__ beta, long count, int N,
+                                                                      float* __restrict__ f) {
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (long)gridDim.x * blockDim.x) {
+    const int n = (int)(i % N);
+    f[i] = expf(-alpha[n] * softplusf_(a[i] + beta[n]));
+  }
+}
+
+// da[i] = df f (-alpha sigmoid(z)), z = a + beta; ga[i] = df f (-softplus(z)) (dalpha's terms).
+__global__ void __launch_bounds__(kBlkThreads) m2rnn_gate_bwd_kernel(const float* __restrict__ a,
+                                                                      const float* __restrict__ alpha,
+                                                                      const float* __restrict__ beta,
+                                                                      const float* __restrict__ df, long count, int N,
+                                                                      float* __restrict__ da, float* __restrict__ ga) {
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (long)gridDim.x * blockDim.x) {
+    const int n = (int)(i % N);
+    const float z = a[i] + beta[n];
+    const float sp = softplusf_(z);
+    const float g = df[i] * expf(-alpha[n] * sp);
+    da[i] = -alpha[n] * sigmoidf_(z) * g;
+    ga[i] = -sp * g;
+  }
+}
+
+// out0[n] = sum over r of in0[r * N + n], out1 likewise (one workgroup per n, fixed order).
+__global__ void __launch_bounds__(kBlkThreads) m2rnn_col_sum2_kernel(const float* __restrict__ in0,
+                                                                      const float* __restrict__ in1, long rows, int N,
+                                                                      float* __restrict__ out0,
+                                                                      float* __restrict__ out1) {
+  __shared__ float red[2 * kBlkThreads / 64];
+  const int n = blockIdx.x;
+  float s0 = 0.0f, s1 = 0.0f;
+  for (long r = threadIdx.x; r < rows; r += kBlkThreads) {
+    s0 += in0[r * N + n];
+    s1 += in1[r * N + n];
+  }
+  const float2 s = block_sum2(s0, s1, red);
+  if (threadIdx.x == 0) {
+    out0[n] = s.x;
+    out1[n] = s.y;
+  }
+}
+
+// ------------------------------------------------------------------ output gate + RMSNorm (§2.3, App. C)
+
+// One workgroup per row (token) of D features: x = y (.) SiLU(gz), out = gamma (.) x / sqrt(mean x^2 + eps).
+// Thread t owns the 4-feature groups t, t + 256, ...; D is a multiple of 4.
+template <bool BF16>
+__global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_fwd_kernel(const float* __restrict__ y,
+                                                                          const void* __restrict__ gz,
+                                                                          const float* __restrict__ gamma, int D,
+                                                                          float eps, float* __restrict__ out) {
+  __shared__ float red[2 * kBlkThreads / 64];
+  const long row = blockIdx.x;
+  const long base = row * D;
+  float ss = 0.0f;
+  for (int j = 4 * threadIdx.x; j < D; j += 4 * kBlkThreads) {
+    const float4 yv = *(const float4*)(y + base + j);
+    const float4 g = load4<BF16>(gz, base + j);
+    const float x0 = yv.x * siluf_(g.x), x1 = yv.y * siluf_(g.y), x2 = yv.z * siluf_(g.z), x3 = yv.w * siluf_(g.w);
+    ss += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+  }
+  const float s = 1.0f / sqrtf(block_sum2(ss, 0.0f, red).x / (float)D + eps);
+  for (int j = 4 * threadIdx.x; j < D; j += 4 * kBlkThreads) {
+    const float4 yv = *(const float4*)(y + base + j);
+    const float4 g = load4<BF16>(gz, base + j);
+    const float4 gm = *(const float4*)(gamma + j);
+    *(float4*)(out + base + j) = make_float4(gm.x * yv.x * siluf_(g.x) * s, gm.y * yv.y * siluf_(g.y) * s,
+                                             gm.z * yv.z * siluf_(g.z) * s, gm.w * yv.w * siluf_(g.w) * s);
+  }
+}
+
+// Backward over `rows_per` rows per workgroup (Appendix C): p = gamma (.) dout, r = sum p x,
+// dx = s p - r s^3 x / D; dy = dx (.) SiLU(gz); dgz = dx (.) y (.) SiLU'(gz); the workgroup's partial
+// of dgamma = sum over its rows of dout (.) x s goes to dgamma_part[blockIdx.x][D].  Thread t owns
+// the 4-feature groups t, t + 256, ... (at most kNormMaxGroups of them).
+constexpr int kNormMaxGroups = 8;  // D <= 4 * 256 * 8 = 8192 features
+
+template <bool BF16>
+__global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_bwd_kernel(
+    const float* __restrict__ y, const void* __restrict__ gz, const float* __restrict__ gamma, int D, float eps,
+    const float* __restrict__ dout, long rows, int rows_per, float* __restrict__ dy, float* __restrict__ dgz,
+    float* __restrict__ dgamma_part) {
+  __shared__ float red[2 * kBlkThreads / 64];
+  const long r0 = (long)blockIdx.x * rows_per;
+  const long r1 = r0 + rows_per < rows ? r0 + rows_per : rows;
+  float4 acc[kNormMaxGroups];
+#pragma unroll
+  for (int q = 0; q < kNormMaxGroups; ++q) acc[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (long r = r0; r < r1; ++r) {
+    const long base = r * D;
+    float ss = 0.0f, rp = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kNormMaxGroups; ++q) {
+      const int j = 4 * (threadIdx.x + q * kBlkThreads);
+      if (j < D) {
+        const float4 yv = *(const float4*)(y + base + j);
+        const float4 g = load4<BF16>(gz, base + j);
+        const float4 gm = *(const float4*)(gamma + j);
+        const float4 d = *(const float4*)(dout + base + j);
+        const float x0 = yv.x * siluf_(g.x), x1 = yv.y * siluf_(g.y), x2 = yv.z * siluf_(g.z),
+                    x3 = yv.w * siluf_(g.w);
+        ss += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+        rp += gm.x * d.x * x0 + gm.y * d.y * x1 + gm.z * d.z * x2 + gm.w * d.w * x3;
+      }
+    }
+    const float2 tot = block_sum2(ss, rp, red);
+    const float s = 1.0f / sqrtf(tot.x / (float)D + eps);
+    const float c = tot.y * s * s * s / (float)D;
+#pragma unroll
+    for (int q = 0; q < kNormMaxGroups; ++q) {
+      const int j = 4 * (threadIdx.x + q * kBlkThreads);
+      if (j < D) {
+        const float4 yv = *(const float4*)(y + base + j);
+        const float4 g = load4<BF16>(gz, base + j);
+        const float4 gm = *(const float4*)(gamma + j);
+        const float4 d = *(const float4*)(dout + base + j);
+        const float gs[4] = {g.x, g.y, g.z, g.w}, ys[4] = {yv.x, yv.y, yv.z, yv.w};
+        const float gms[4] = {gm.x, gm.y, gm.z, gm.w}, ds[4] = {d.x, d.y, d.z, d.w};
+        float oy[4], og[4], ag[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sg = siluf_(gs[e]);
+          const float x = ys[e] * sg;
+          const float dx = s * gms[e] * ds[e] - c * x;
+          oy[e] = dx * sg;
+          og[e] = dx * ys[e] * silu_gradf_(gs[e]);
+          ag[e] = ds[e] * x * s;
+        }
+        *(float4*)(dy + base + j) = make_float4(oy[0], oy[1], oy[2], oy[3]);
+        *(float4*)(dgz + base + j) = make_float4(og[0], og[1], og[2], og[3]);
+        acc[q].x += ag[0];
+        acc[q].y += ag[1];
+        acc[q].z += ag[2];
+        acc[q].w += ag[3];
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kNormMaxGroups; ++q) {
+    const int j = 4 * (threadIdx.x + q * kBlkThreads);
+    if (j < D) *(float4*)(dgamma_part + (long)blockIdx.x * D + j) = acc[q];
+  }
+}
+
+// out[j] = sum over p < parts of part[p * count + j] (fixed order).
+__global__ void __launch_bounds__(kBlkThreads) m2rnn_sum_parts_kernel(const float* __restrict__ part, int parts,
+                                                                       long count, float* __restrict__ out) {
+  const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= count) return;
+  float s = 0.0f;
+  for (int p = 0; p < parts; ++p) s += part[(long)p * count + j];
+  out[j] = s;
+}
+
+// ------------------------------------------------------------------ causal conv4 + SiLU (§2.3)
+
+constexpr int kConvChunk = 64;  // steps per thread (a sliding window over time)
+
+// Thread (b, chunk of kConvChunk steps, 4 channels c4): pre_t = sum_i w[c][i] x_{t-3+i} + bias[c],
+// u_t = SiLU(pre_t), with x_t = 0 for t < 0.  Layout [B, T, C]; C is a multiple of 4.
+template <bool BF16>
+__global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_fwd_kernel(const void* __restrict__ x,
+                                                                            const float* __restrict__ w,
+                                                                            const float* __restrict__ bias, int B,
+                                                                            int T, int C, void* __restrict__ u) {
+  const int C4 = C / 4;
+  const int nchunk = (T + kConvChunk - 1) / kConvChunk;
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long)B * nchunk * C4) return;
+  const int c4 = (int)(gid % C4);
+  const int chunk = (int)((gid / C4) % nchunk);
+  const int b = (int)(gid / ((long)C4 * nchunk));
+  const int c = 4 * c4;
+  float wk[4][4];  // [channel][tap]
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float4 t4 = *(const float4*)(w + (long)(c + e) * 4);
+    wk[e][0] = t4.x; wk[e][1] = t4.y; wk[e][2] = t4.z; wk[e][3] = t4.w;
+  }
+  const float4 bv = bias ? *(const float4*)(bias + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const float bs[4] = {bv.x, bv.y, bv.z, bv.w};
+  const int t0 = chunk * kConvChunk;
+  const int t1 = min(T, t0 + kConvChunk);
+  const long row = (long)b * T;
+  // window: xs[0..2] = x_{t-3..t-1}
+  float xs[3][4];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int src = t0 - 3 + i;
+    const float4 v = src >= 0 ? load4<BF16>(x, (row + src) * C + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    xs[i][0] = v.x; xs[i][1] = v.y; xs[i][2] = v.z; xs[i][3] = v.w;
+  }
+  for (int t = t0; t < t1; ++t) {
+    const float4 v = load4<BF16>(x, (row + t) * C + c);
+    const float xc[4] = {v.x, v.y, v.z, v.w};
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pre = wk[e][0] * xs[0][e] + wk[e][1] * xs[1][e] + wk[e][2] * xs[2][e] + wk[e][3] * xc[e] + bs[e];
+      o[e] = siluf_(pre);
+      xs[0][e] = xs[1][e];
+      xs[1][e] = xs[2][e];
+      xs[2][e] = xc[e];
+    }
+    store4<BF16>(u, (row + t) * C + c, make_float4(o[0], o[1], o[2], o[3]));
+  }
+}
+
+// Backward, same thread layout.  dpre_t = du_t SiLU'(pre_t); dx_s = sum_i w[c][i] dpre_{s+3-i};
+// the thread's partials of dw[c][i] = sum dpre_t x_{t-3+i} and dbias[c] = sum dpre_t go to
+// part[(b * nchunk + chunk)][C][5] (4 taps + bias).
+template <bool BF16>
+__global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_bwd_kernel(const void* __restrict__ x,
+                                                                            const float* __restrict__ w,
+                                                                            const float* __restrict__ bias,
+                                                                            const float* __restrict__ du, int B, int T,
+                                                                            int C, float* __restrict__ dx,
+                                                                            float* __restrict__ part) {
+  const int C4 = C / 4;
+  const int nchunk = (T + kConvChunk - 1) / kConvChunk;
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long)B * nchunk * C4) return;
+  const int c4 = (int)(gid % C4);
+  const int chunk = (int)((gid / C4) % nchunk);
+  const int b = (int)(gid / ((long)C4 * nchunk));
+  const int c = 4 * c4;
+  float wk[4][4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float4 t4 = *(const float4*)(w + (long)(c + e) * 4);
+    wk[e][0] = t4.x; wk[e][1] = t4.y; wk[e][2] = t4.z; wk[e][3] = t4.w;
+  }
+  const float4 bv = bias ? *(const float4*)(bias + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const float bs[4] = {bv.x, bv.y, bv.z, bv.w};
+  const int t0 = chunk * kConvChunk;
+  const int t1 = min(T, t0 + kConvChunk);
+  const long row = (long)b * T;
+  auto xat = [&](int t, float (&o)[4]) {
+    const float4 v = (t >= 0 && t < T) ? load4<BF16>(x, (row + t) * C + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  };
+  // dpre at step t (0 outside [0, T)).
+  auto dpre_at = [&](int t, const float (&xw)[4][4], float (&o)[4]) {
+    // xw[i] = x_{t-3+i}
+    if (t < 0 || t >= T) {
+      o[0] = o[1] = o[2] = o[3] = 0.0f;
+      return;
+    }
+    const float4 d = *(const float4*)(du + (row + t) * C + c);
+    const float ds[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pre = wk[e][0] * xw[0][e] + wk[e][1] * xw[1][e] + wk[e][2] * xw[2][e] + wk[e][3] * xw[3][e] + bs[e];
+      o[e] = ds[e] * silu_gradf_(pre);
+    }
+  };
+  // Sliding window over t = t0 .. t1 + 2 of x_{t-3 .. t} and of dpre_{t-3 .. t}: dx_s for s = t - 3
+  // needs dpre_{s .. s+3} = dpre_{t-3 .. t}.
+  float xw[4][4];
+  for (int i = 0; i < 3; ++i) xat(t0 - 3 + i, xw[i]);
+  float dp[4][4];  // dp[i] = dpre_{t-3+i}
+  {
+    float xx[4][4];
+    for (int i = 0; i < 3; ++i) {
+      // dpre_{t0-3+i}: its window is x_{t0-6+i .. t0-3+i}
+      for (int k = 0; k < 4; ++k) xat(t0 - 6 + i + k, xx[k]);
+      dpre_at(t0 - 3 + i, xx, dp[i]);
+    }
+  }
+  float aw[4][4] = {}, ab[4] = {};
+  for (int t = t0; t < t1 + 3; ++t) {
+    xat(t, xw[3]);
+    dpre_at(t, xw, dp[3]);
+    if (t < t1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) aw[e][i] += dp[3][e] * xw[i][e];
+        ab[e] += dp[3][e];
+      }
+    }
+    const int s = t - 3;
+    if (s >= t0) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = wk[e][3] * dp[0][e] + wk[e][2] * dp[1][e] + wk[e][1] * dp[2][e] + wk[e][0] * dp[3][e];
+      *(float4*)(dx + (row + s) * C + c) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xw[i][e] = xw[i + 1][e];
+        dp[i][e] = dp[i + 1][e];
+      }
+  }
+  float* pp = part + (long)(b * nchunk + chunk) * C * 5;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pp[(c + e) * 5 + i] = aw[e][i];
+    pp[(c + e) * 5 + 4] = ab[e];
+  }
+}
+
+// dw[c][i] and dbias[c] from the per-(batch, chunk) partials, summed in order.
+__global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_sum_kernel(const float* __restrict__ part, int parts, int C,
+                                                                       float* __restrict__ dw,
+                                                                       float* __restrict__ dbias) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;  // over [C][5]
+  if (j >= C * 5) return;
+  float s = 0.0f;
+  for (int p = 0; p < parts; ++p) s += part[(long)p * C * 5 + j];
+  const int cc = j / 5, i = j % 5;
+  if (i < 4) dw[cc * 4 + i] = s;
+  else if (dbias) dbias[cc] = s;
+}
+
+}  // namespace m2rnn

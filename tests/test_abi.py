@@ -110,3 +110,23 @@ def test_checkpoint_entry_points_check_their_arguments():
     # its workspace excludes the checkpoints
     big = m2.Dims(4, 4096, 16, 64, 64)
     assert m2.m2rnn_bwd_ckpt_workspace_size(big, 0) + 4 * 16 * 64 * 64 * 64 * 4 <= m2.m2rnn_bwd_workspace_size(big, 0)
+
+
+def test_block_entry_points_check_their_arguments():
+    L = m2.lib()
+    p = ctypes.c_void_p(16)
+    n = ctypes.c_size_t(0)
+    assert L.m2rnn_gate_fwd(-1, 2, 3, p, p, p, p, None) == m2.M2RNN_EINVAL
+    assert L.m2rnn_gate_fwd(1, 2, 3, None, p, p, p, None) == m2.M2RNN_EINVAL
+    assert L.m2rnn_gate_fwd(0, 2, 3, None, None, None, None, None) == m2.M2RNN_OK
+    assert L.m2rnn_gate_bwd(1, 2, 3, p, p, p, p, p, p, p, None, 0, None) == m2.M2RNN_EWORKSPACE
+    assert L.m2rnn_out_norm_fwd(4, 6, p, p, 0, p, ctypes.c_float(1e-6), p, None) == m2.M2RNN_EUNSUPPORTED  # D % 4
+    assert L.m2rnn_out_norm_fwd(4, 16, p, p, 5, p, ctypes.c_float(1e-6), p, None) == m2.M2RNN_EINVAL     # dtype
+    assert L.m2rnn_out_norm_fwd(4, 16, p, p, 0, p, ctypes.c_float(-1.0), p, None) == m2.M2RNN_EINVAL     # eps
+    assert L.m2rnn_out_norm_fwd(4, 16, ctypes.c_void_p(20), p, 0, p, ctypes.c_float(0), p, None) == m2.M2RNN_EINVAL
+    assert L.m2rnn_out_norm_fwd(4, 8196, p, p, 0, p, ctypes.c_float(0), p, None) == m2.M2RNN_EUNSUPPORTED
+    assert L.m2rnn_out_norm_bwd_workspace_size(130, 64, ctypes.byref(n)) == m2.M2RNN_OK and n.value >= 3 * 64 * 4
+    assert L.m2rnn_conv4_silu_fwd(1, 8, 6, 0, p, p, None, p, None) == m2.M2RNN_EUNSUPPORTED             # C % 4
+    assert L.m2rnn_conv4_silu_fwd(1, 8, 8, 3, p, p, None, p, None) == m2.M2RNN_EINVAL
+    assert L.m2rnn_conv4_silu_fwd(1, 8, 8, 0, p, None, None, p, None) == m2.M2RNN_EINVAL                # no weights
+    assert L.m2rnn_conv4_silu_bwd(1, 8, 8, 0, p, p, None, p, p, p, None, None, 0, None) == m2.M2RNN_EWORKSPACE
