@@ -250,6 +250,71 @@ def bench_decode(args) -> int:
     return 0
 
 
+def bench_block(args) -> int:
+    """Times the steps around the recurrence (gate, causal conv4 + SiLU on q, k, v, output gate +
+    RMSNorm), forward and backward, at the shapes of the 16K-token workload; each is an HBM stream,
+    reported against the HBM peak with its algorithmic bytes."""
+    import numpy as np
+    import torch
+
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    from matrix_state_nonlinear_m2rnn_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    B, T, N, K, V = w.B, w.T, w.N, w.K, w.V
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    rn = lambda *s, sd=1.0: (torch.randn(*s, generator=g) * sd).to(dev)  # noqa: E731
+    bf = torch.bfloat16
+    a = rn(B, T, N, sd=2.0)
+    alpha, beta = rn(N).abs() + 0.5, rn(N)
+    dfv = rn(B, T, N)
+    C = N * K
+    x = rn(B, T, C).to(bf)
+    cw, cb = rn(C, 4, sd=0.5), rn(C, sd=0.2)
+    du = rn(B, T, C)
+    y = rn(B, T, N, V)
+    gz = rn(B, T, N, V, sd=2.0).to(bf)
+    gamma = rn(N, V, sd=0.1) + 1.0
+    dout = rn(B, T, N, V)
+    f32, b16 = 4, 2
+    ops = {
+        "gate_fwd": (lambda: m2.m2rnn_gate_fwd(a, alpha, beta), B * T * N * (f32 + f32)),
+        "gate_bwd": (lambda: m2.m2rnn_gate_bwd(a, alpha, beta, dfv), B * T * N * (3 * f32 + 2 * f32 + 2 * f32)),
+        "conv4_silu_fwd": (lambda: m2.m2rnn_conv4_silu_fwd(x, cw, cb), B * T * C * (b16 + b16)),
+        "conv4_silu_bwd": (lambda: m2.m2rnn_conv4_silu_bwd(x, cw, cb, du), B * T * C * (b16 + f32 + f32)),
+        "out_norm_fwd": (lambda: m2.m2rnn_out_norm_fwd(y, gz, gamma), B * T * N * V * (f32 + b16 + f32)),
+        "out_norm_bwd": (lambda: m2.m2rnn_out_norm_bwd(y, gz, gamma, dout),
+                         B * T * N * V * (f32 + b16 + f32 + 2 * f32)),
+    }
+    res = {}
+    for name, (fn, nbytes) in ops.items():
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        res[name] = {"us": ms * 1e3, "GB_s": nbytes / (ms * 1e-3) / 1e9, "algorithmic_bytes": nbytes}
+    dom = max(res, key=lambda k: res[k]["us"])
+    total_ms = sum(r["us"] for r in res.values()) * 1e-3
+    out = {"metric": "M²RNN block ops (gate, conv4+SiLU, output gate+RMSNorm; fwd+bwd) token-steps/sec",
+           "value": B * T / (total_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": total_ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": w.name, "B": B, "T": T, "N": N, "K": K, "V": V, "conv_channels": C,
+                      "activations": "bf16 in, fp32 gradients"},
+           "ops": res,
+           "roofline": {"bound": "hbm", "kernel": dom, "achieved": res[dom]["GB_s"], "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": res[dom]["GB_s"] / PEAK_HBM_GBS, "traffic": None}}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +329,8 @@ def main() -> int:
                     help="time m2rnn_bwd on the BPTT workload instead of the forward (its own JSON line)")
     ap.add_argument("--train", action="store_true",
                     help="time one training step of the layer (m2rnn_fwd_ckpt + m2rnn_bwd_ckpt) on the BPTT workload")
+    ap.add_argument("--block", action="store_true",
+                    help="time the gate, conv4 + SiLU and output gate + RMSNorm (fwd and bwd) at the workload's shapes")
     ap.add_argument("--decode", action="store_true",
                     help="time m2rnn_decode_step on the batch-128 decode workload (its own JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -289,6 +356,8 @@ def main() -> int:
         return bench_backward(args)
     if args.decode:
         return bench_decode(args)
+    if args.block:
+        return bench_block(args)
     w = inputs.WORKLOADS[args.workload]
     math_mode = "f16x3" if args.math == "auto" else args.math
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)

@@ -27,7 +27,38 @@ unsigned grid_for(long count) {
   return (unsigned)(blocks > 0 ? blocks : 1);
 }
 
-constexpr int kNormRowsPer = 64;  // rows per workgroup of the RMSNorm backward
+constexpr int kNormRowsPer = 16;      // rows per wave of the RMSNorm backward
+constexpr long kGateMaxParts = 1024;  // workgroups (partial sums) of the gate backward
+constexpr int kSlice = 64;             // rows per slice of the partial-sum reduction tree
+constexpr int kNormMaxD = 4 * 64 * 32;  // features per row of the RMSNorm (32 groups of 4 per lane)
+
+long ceil_div(long a, long b) { return (a + b - 1) / b; }
+
+// Floats of scratch that reduce_rows needs for `parts` rows of M columns.
+size_t reduce_scratch(long parts, long M) { return (size_t)2 * ceil_div(parts, kSlice) * M; }
+
+// Sums `parts` rows of M floats (row p at part + p * stride) into one row by a fixed tree of
+// kSlice-row slices; the last level writes columns j < M0 to out0[j] and the others to
+// out1[j - M0] (dropped when out1 is null).  `scratch` holds reduce_scratch(parts, M) floats.
+void reduce_rows(const float* part, long parts, long M, long stride, float* out0, long M0, float* out1, float* scratch,
+                 hipStream_t s) {
+  float* bufs[2] = {scratch, scratch + ceil_div(parts, kSlice) * M};
+  const float* src = part;
+  long n = parts, src_stride = stride;
+  int which = 0;
+  const unsigned gx = (unsigned)ceil_div(M, kBlkThreads);
+  while (n > kSlice) {
+    const long m = ceil_div(n, kSlice);
+    hipLaunchKernelGGL(m2rnn_sum_slices_kernel, dim3(gx, (unsigned)m), dim3(kBlkThreads), 0, s, src, (int)n, M,
+                       src_stride, kSlice, bufs[which], M, (float*)nullptr);
+    src = bufs[which];
+    src_stride = M;
+    n = m;
+    which ^= 1;
+  }
+  hipLaunchKernelGGL(m2rnn_sum_slices_kernel, dim3(gx, 1), dim3(kBlkThreads), 0, s, src, (int)n, M, src_stride,
+                     (int)(n > 0 ? n : 1), out0, M0, out1);
+}
 
 int check_gate(int64_t B, int64_t T, int64_t N) {
   if (B < 0 || T < 0 || N < 0) return M2RNN_EINVAL;
@@ -39,7 +70,7 @@ int check_norm(int64_t rows, int64_t D, int gz_dtype, float eps) {
   if (rows < 0 || D <= 0) return M2RNN_EINVAL;
   if (gz_dtype != M2RNN_DTYPE_F32 && gz_dtype != M2RNN_DTYPE_BF16) return M2RNN_EINVAL;
   if (!(eps >= 0.0f) || eps > 1e30f) return M2RNN_EINVAL;
-  if (D % 4 != 0 || D > 4 * kBlkThreads * kNormMaxGroups) return M2RNN_EUNSUPPORTED;
+  if (D % 4 != 0 || D > kNormMaxD) return M2RNN_EUNSUPPORTED;
   if (rows > 2147483647) return M2RNN_EUNSUPPORTED;
   return M2RNN_OK;
 }
@@ -50,6 +81,25 @@ int check_conv(int64_t B, int64_t T, int64_t C, int dtype) {
   if (C % 4 != 0) return M2RNN_EUNSUPPORTED;
   if (B > 2147483647 || T > 2147483647 || C > 2147483647) return M2RNN_EUNSUPPORTED;
   return M2RNN_OK;
+}
+
+// Gate backward workspace: the partials [parts][2N] and their reduction scratch, or (more than
+// kBlkThreads heads) the per-element dalpha terms.
+size_t gate_ws_bytes(int64_t B, int64_t T, int64_t N) {
+  if (N <= kBlkThreads)
+    return round_up256((size_t)2 * N * kGateMaxParts * sizeof(float)) +
+           round_up256(reduce_scratch(kGateMaxParts, 2 * N) * sizeof(float));
+  return round_up256((size_t)B * T * N * sizeof(float));
+}
+
+size_t norm_ws_bytes(int64_t rows, int64_t D) {
+  const long parts = ceil_div(rows, kNormRowsPer);
+  return round_up256((size_t)parts * D * sizeof(float)) + round_up256(reduce_scratch(parts, D) * sizeof(float));
+}
+
+size_t conv_ws_bytes(int64_t B, int64_t T, int64_t C) {
+  const long parts = (long)B * ceil_div(T, kConvChunk);
+  return round_up256((size_t)parts * 5 * C * sizeof(float)) + round_up256(reduce_scratch(parts, 5 * C) * sizeof(float));
 }
 
 long conv_threads(int64_t B, int64_t T, int64_t C) {
@@ -76,7 +126,7 @@ int m2rnn_gate_bwd_workspace_size(int64_t B, int64_t T, int64_t N, size_t* bytes
   if (!bytes) return M2RNN_EINVAL;
   int st = check_gate(B, T, N);
   if (st) return st;
-  *bytes = round_up256((size_t)B * T * N * sizeof(float));
+  *bytes = gate_ws_bytes(B, T, N);
   return M2RNN_OK;
 }
 
@@ -92,9 +142,21 @@ int m2rnn_gate_bwd(int64_t B, int64_t T, int64_t N, const float* a, const float*
   const void* ps[] = {a, alpha, beta, df, da, dalpha, dbeta};
   for (const void* p : ps)
     if (p && !al4(p)) return M2RNN_EINVAL;
-  const size_t need = round_up256((size_t)count * sizeof(float));
-  if (count > 0 && (!workspace || workspace_bytes < need || !al4(workspace))) return M2RNN_EWORKSPACE;
+  const size_t need = gate_ws_bytes(B, T, N);
+  if (count > 0 && (!workspace || workspace_bytes < need || !al16(workspace))) return M2RNN_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
+  if (N <= kBlkThreads && count > 0) {
+    // Workgroups of a multiple of N threads, each summing a contiguous range of (b, t) rows.
+    const int tb = (int)(kBlkThreads / N * N);
+    const long per_block = ceil_div(ceil_div(count, kGateMaxParts), tb) * tb;
+    const long parts = ceil_div(count, per_block);
+    float* part = (float*)workspace;
+    float* scratch = (float*)((char*)workspace + round_up256((size_t)2 * N * kGateMaxParts * sizeof(float)));
+    hipLaunchKernelGGL(m2rnn_gate_bwd_part_kernel, dim3((unsigned)parts), dim3(tb), 0, s, a, alpha, beta, df, count,
+                       (int)N, per_block, da, part);
+    reduce_rows(part, parts, 2 * N, 2 * N, dbeta, N, dalpha, scratch, s);
+    return status(hipGetLastError());
+  }
   float* ga = (float*)workspace;
   if (count > 0)
     hipLaunchKernelGGL(m2rnn_gate_bwd_kernel, dim3(grid_for(count)), dim3(kBlkThreads), 0, s, a, alpha, beta, df,
@@ -127,8 +189,7 @@ int m2rnn_out_norm_bwd_workspace_size(int64_t rows, int64_t D, size_t* bytes) {
   if (!bytes) return M2RNN_EINVAL;
   int st = check_norm(rows, D, M2RNN_DTYPE_F32, 0.0f);
   if (st) return st;
-  const long parts = (rows + kNormRowsPer - 1) / kNormRowsPer;
-  *bytes = round_up256((size_t)parts * D * sizeof(float));
+  *bytes = norm_ws_bytes(rows, D);
   return M2RNN_OK;
 }
 
@@ -143,23 +204,21 @@ int m2rnn_out_norm_bwd(int64_t rows, int64_t D, const float* y, const void* gz, 
   for (const void* p : ps)
     if (p && !al16(p)) return M2RNN_EINVAL;
   hipStream_t s = (hipStream_t)stream;
-  const long parts = (rows + kNormRowsPer - 1) / kNormRowsPer;
+  const long parts = ceil_div(rows, kNormRowsPer);  // one wave per kNormRowsPer rows
   if (parts == 0) {
-    hipLaunchKernelGGL(m2rnn_sum_parts_kernel, dim3((unsigned)((D + kBlkThreads - 1) / kBlkThreads)),
-                       dim3(kBlkThreads), 0, s, (const float*)nullptr, 0, (long)D, dgamma);
+    reduce_rows(nullptr, 0, D, D, dgamma, D, nullptr, nullptr, s);
     return status(hipGetLastError());
   }
-  const size_t need = round_up256((size_t)parts * D * sizeof(float));
-  if (!workspace || workspace_bytes < need || !al16(workspace)) return M2RNN_EWORKSPACE;
+  if (!workspace || workspace_bytes < norm_ws_bytes(rows, D) || !al16(workspace)) return M2RNN_EWORKSPACE;
   float* part = (float*)workspace;
-  if (gz_dtype == M2RNN_DTYPE_BF16)
-    hipLaunchKernelGGL(m2rnn_out_norm_bwd_kernel<true>, dim3((unsigned)parts), dim3(kBlkThreads), 0, s, y, gz, gamma,
-                       (int)D, eps, dout, (long)rows, kNormRowsPer, dy, dgz, part);
-  else
-    hipLaunchKernelGGL(m2rnn_out_norm_bwd_kernel<false>, dim3((unsigned)parts), dim3(kBlkThreads), 0, s, y, gz, gamma,
-                       (int)D, eps, dout, (long)rows, kNormRowsPer, dy, dgz, part);
-  hipLaunchKernelGGL(m2rnn_sum_parts_kernel, dim3((unsigned)((D + kBlkThreads - 1) / kBlkThreads)), dim3(kBlkThreads),
-                     0, s, (const float*)part, (int)parts, (long)D, dgamma);
+  float* scratch = (float*)((char*)workspace + round_up256((size_t)parts * D * sizeof(float)));
+  const dim3 grid((unsigned)ceil_div(parts, kBlkThreads / 64));
+  const bool bf = gz_dtype == M2RNN_DTYPE_BF16;
+  const auto kern = D <= 4 * 64 * 8 ? (bf ? &m2rnn_out_norm_bwd_kernel<true, 8> : &m2rnn_out_norm_bwd_kernel<false, 8>)
+                                    : (bf ? &m2rnn_out_norm_bwd_kernel<true, 32> : &m2rnn_out_norm_bwd_kernel<false, 32>);
+  hipLaunchKernelGGL(kern, grid, dim3(kBlkThreads), 0, s, y, gz, gamma, (int)D, eps, dout, (long)rows, kNormRowsPer,
+                     dy, dgz, part);
+  reduce_rows(part, parts, D, D, dgamma, D, nullptr, scratch, s);
   return status(hipGetLastError());
 }
 
@@ -188,8 +247,7 @@ int m2rnn_conv4_silu_bwd_workspace_size(int64_t B, int64_t T, int64_t C, size_t*
   if (!bytes) return M2RNN_EINVAL;
   int st = check_conv(B, T, C, M2RNN_DTYPE_F32);
   if (st) return st;
-  const long parts = (long)B * ((T + kConvChunk - 1) / kConvChunk);
-  *bytes = round_up256((size_t)parts * C * 5 * sizeof(float));
+  *bytes = conv_ws_bytes(B, T, C);
   return M2RNN_OK;
 }
 
@@ -205,10 +263,11 @@ int m2rnn_conv4_silu_bwd(int64_t B, int64_t T, int64_t C, int dtype, const void*
   for (const void* p : ps)
     if (p && !al16(p)) return M2RNN_EINVAL;
   hipStream_t s = (hipStream_t)stream;
-  const long parts = (long)B * ((T + kConvChunk - 1) / kConvChunk);
-  const size_t need = round_up256((size_t)parts * C * 5 * sizeof(float));
-  if (parts > 0 && (!workspace || workspace_bytes < need || !al16(workspace))) return M2RNN_EWORKSPACE;
+  const long parts = (long)B * ceil_div(T, kConvChunk);
+  if (parts > 0 && (!workspace || workspace_bytes < conv_ws_bytes(B, T, C) || !al16(workspace)))
+    return M2RNN_EWORKSPACE;
   float* part = (float*)workspace;
+  float* scratch = parts > 0 ? (float*)((char*)workspace + round_up256((size_t)parts * 5 * C * sizeof(float))) : nullptr;
   if (nth > 0) {
     const unsigned blocks = (unsigned)((nth + kBlkThreads - 1) / kBlkThreads);
     if (dtype == M2RNN_DTYPE_BF16)
@@ -218,8 +277,7 @@ int m2rnn_conv4_silu_bwd(int64_t B, int64_t T, int64_t C, int dtype, const void*
       hipLaunchKernelGGL(m2rnn_conv4_silu_bwd_kernel<false>, dim3(blocks), dim3(kBlkThreads), 0, s, x, w, bias, du,
                          (int)B, (int)T, (int)C, dx, part);
   }
-  hipLaunchKernelGGL(m2rnn_conv4_sum_kernel, dim3((unsigned)((C * 5 + kBlkThreads - 1) / kBlkThreads)),
-                     dim3(kBlkThreads), 0, s, (const float*)part, (int)parts, (int)C, dw, dbias);
+  reduce_rows(part, parts, 5 * C, 5 * C, dw, 4 * C, dbias, scratch, s);
   return status(hipGetLastError());
 }
 

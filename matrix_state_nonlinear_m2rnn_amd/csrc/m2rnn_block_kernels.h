@@ -11,9 +11,15 @@ namespace m2rnn {
 
 constexpr int kBlkThreads = 256;
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+// e^x and ln x from the hardware's 2^x and log2 x (v_exp_f32, v_log_f32), about 1 ulp each plus the
+// rounding of the base change; 1/x from v_rcp_f32.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ float exp_(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float log_(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + exp_(-x)); }
 // log(1 + e^x) without overflow.
-__device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.0f) + log_(1.0f + exp_(-fabsf(x))); }
 __device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
 __device__ __forceinline__ float silu_gradf_(float x) {
   const float s = sigmoidf_(x);
@@ -71,7 +77,7 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_gate_fwd_kernel(const float
                                                                       float* __restrict__ f) {
   for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (long)gridDim.x * blockDim.x) {
     const int n = (int)(i % N);
-    f[i] = expf(-alpha[n] * softplusf_(a[i] + beta[n]));
+    f[i] = exp_(-alpha[n] * softplusf_(a[i] + beta[n]));
   }
 }
 
@@ -85,9 +91,50 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_gate_bwd_kernel(const float
     const int n = (int)(i % N);
     const float z = a[i] + beta[n];
     const float sp = softplusf_(z);
-    const float g = df[i] * expf(-alpha[n] * sp);
+    const float g = df[i] * exp_(-alpha[n] * sp);
     da[i] = -alpha[n] * sigmoidf_(z) * g;
     ga[i] = -sp * g;
+  }
+}
+
+// The same with the sums over (b, t) taken per workgroup: the workgroup has a multiple of N
+// threads, so thread t meets only column n = t % N of the [B*T, N] elements i0 + t + m * blockDim
+// it handles; its partials are then added in the order of t into part[blockIdx][2][N]
+// (0: dbeta, 1: dalpha).
+__global__ void __launch_bounds__(kBlkThreads) m2rnn_gate_bwd_part_kernel(const float* __restrict__ a,
+                                                                           const float* __restrict__ alpha,
+                                                                           const float* __restrict__ beta,
+                                                                           const float* __restrict__ df, long count,
+                                                                           int N, long per_block, float* __restrict__ da,
+                                                                           float* __restrict__ part) {
+  __shared__ float red[2][kBlkThreads];
+  const int tb = blockDim.x;
+  const int t = threadIdx.x;
+  const int n = t % N;
+  const float al = alpha[n], be = beta[n];
+  const long i0 = (long)blockIdx.x * per_block;
+  const long i1 = i0 + per_block < count ? i0 + per_block : count;
+  float s0 = 0.0f, s1 = 0.0f;
+  for (long i = i0 + t; i < i1; i += tb) {
+    const float z = a[i] + be;
+    const float sp = softplusf_(z);
+    const float g = df[i] * exp_(-al * sp);
+    const float d = -al * sigmoidf_(z) * g;
+    da[i] = d;
+    s0 += d;
+    s1 += -sp * g;
+  }
+  red[0][t] = s0;
+  red[1][t] = s1;
+  __syncthreads();
+  if (t < N) {
+    float r0 = 0.0f, r1 = 0.0f;
+    for (int k = t; k < tb; k += N) {
+      r0 += red[0][k];
+      r1 += red[1][k];
+    }
+    part[((long)blockIdx.x * 2 + 0) * N + t] = r0;
+    part[((long)blockIdx.x * 2 + 1) * N + t] = r1;
   }
 }
 
@@ -139,29 +186,29 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_fwd_kernel(const f
   }
 }
 
-// Backward over `rows_per` rows per workgroup (Appendix C): p = gamma (.) dout, r = sum p x,
-// dx = s p - r s^3 x / D; dy = dx (.) SiLU(gz); dgz = dx (.) y (.) SiLU'(gz); the workgroup's partial
-// of dgamma = sum over its rows of dout (.) x s goes to dgamma_part[blockIdx.x][D].  Thread t owns
-// the 4-feature groups t, t + 256, ... (at most kNormMaxGroups of them).
-constexpr int kNormMaxGroups = 8;  // D <= 4 * 256 * 8 = 8192 features
-
-template <bool BF16>
+// Backward (Appendix C), one wave per `rows_per` consecutive rows, reductions within the wave:
+// p = gamma (.) dout, r = sum p x, dx = s p - r s^3 x / D; dy = dx (.) SiLU(gz);
+// dgz = dx (.) y (.) SiLU'(gz).  The wave's partial of dgamma = sum over its rows of dout (.) x s goes
+// to dgamma_part[wave][D].  Lane l owns the 4-feature groups l, l + 64, ... (QMAX of them at most).
+template <bool BF16, int QMAX>
 __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_bwd_kernel(
     const float* __restrict__ y, const void* __restrict__ gz, const float* __restrict__ gamma, int D, float eps,
     const float* __restrict__ dout, long rows, int rows_per, float* __restrict__ dy, float* __restrict__ dgz,
     float* __restrict__ dgamma_part) {
-  __shared__ float red[2 * kBlkThreads / 64];
-  const long r0 = (long)blockIdx.x * rows_per;
+  const int lane = threadIdx.x & 63;
+  const long wave = (long)blockIdx.x * (kBlkThreads / 64) + (threadIdx.x >> 6);
+  const long r0 = wave * rows_per;
+  if (r0 >= rows) return;  // no barrier in this kernel
   const long r1 = r0 + rows_per < rows ? r0 + rows_per : rows;
-  float4 acc[kNormMaxGroups];
+  float4 acc[QMAX];
 #pragma unroll
-  for (int q = 0; q < kNormMaxGroups; ++q) acc[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int q = 0; q < QMAX; ++q) acc[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (long r = r0; r < r1; ++r) {
     const long base = r * D;
     float ss = 0.0f, rp = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kNormMaxGroups; ++q) {
-      const int j = 4 * (threadIdx.x + q * kBlkThreads);
+    for (int q = 0; q < QMAX; ++q) {
+      const int j = 4 * (lane + 64 * q);
       if (j < D) {
         const float4 yv = *(const float4*)(y + base + j);
         const float4 g = load4<BF16>(gz, base + j);
@@ -173,12 +220,16 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_bwd_kernel(
         rp += gm.x * d.x * x0 + gm.y * d.y * x1 + gm.z * d.z * x2 + gm.w * d.w * x3;
       }
     }
-    const float2 tot = block_sum2(ss, rp, red);
-    const float s = 1.0f / sqrtf(tot.x / (float)D + eps);
-    const float c = tot.y * s * s * s / (float)D;
 #pragma unroll
-    for (int q = 0; q < kNormMaxGroups; ++q) {
-      const int j = 4 * (threadIdx.x + q * kBlkThreads);
+    for (int o = 32; o >= 1; o >>= 1) {
+      ss += __shfl_xor(ss, o);
+      rp += __shfl_xor(rp, o);
+    }
+    const float s = 1.0f / sqrtf(ss / (float)D + eps);
+    const float c = rp * s * s * s / (float)D;
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
+      const int j = 4 * (lane + 64 * q);
       if (j < D) {
         const float4 yv = *(const float4*)(y + base + j);
         const float4 g = load4<BF16>(gz, base + j);
@@ -206,25 +257,34 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_bwd_kernel(
     }
   }
 #pragma unroll
-  for (int q = 0; q < kNormMaxGroups; ++q) {
-    const int j = 4 * (threadIdx.x + q * kBlkThreads);
-    if (j < D) *(float4*)(dgamma_part + (long)blockIdx.x * D + j) = acc[q];
+  for (int q = 0; q < QMAX; ++q) {
+    const int j = 4 * (lane + 64 * q);
+    if (j < D) *(float4*)(dgamma_part + wave * D + j) = acc[q];
   }
 }
 
-// out[j] = sum over p < parts of part[p * count + j] (fixed order).
-__global__ void __launch_bounds__(kBlkThreads) m2rnn_sum_parts_kernel(const float* __restrict__ part, int parts,
-                                                                       long count, float* __restrict__ out) {
+// One level of a fixed-order reduction of `parts` rows of M columns (row p at part + p * stride):
+// slice y of `per` consecutive rows is summed into output row y; output row y, column j goes to
+// out0[y * M + j] when j < M0, else to out1[y * M + j - M0] (out1 may be null: those are dropped).
+__global__ void __launch_bounds__(kBlkThreads) m2rnn_sum_slices_kernel(const float* __restrict__ part, int parts,
+                                                                        long M, long stride, int per,
+                                                                        float* __restrict__ out0, long M0,
+                                                                        float* __restrict__ out1) {
   const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= count) return;
-  float s = 0.0f;
-  for (int p = 0; p < parts; ++p) s += part[(long)p * count + j];
-  out[j] = s;
+  if (j >= M) return;
+  const int p0 = blockIdx.y * per;
+  const int p1 = p0 + per < parts ? p0 + per : parts;
+  float acc = 0.0f;
+#pragma unroll 8
+  for (int p = p0; p < p1; ++p) acc += part[(long)p * stride + j];
+  if (j < M0) out0[(long)blockIdx.y * M + j] = acc;
+  else if (out1) out1[(long)blockIdx.y * M + j - M0] = acc;
 }
 
 // ------------------------------------------------------------------ causal conv4 + SiLU (§2.3)
 
 constexpr int kConvChunk = 64;  // steps per thread (a sliding window over time)
+constexpr int kConvBatch = 4;   // steps whose loads are issued together
 
 // Thread (b, chunk of kConvChunk steps, 4 channels c4): pre_t = sum_i w[c][i] x_{t-3+i} + bias[c],
 // u_t = SiLU(pre_t), with x_t = 0 for t < 0.  Layout [B, T, C]; C is a multiple of 4.
@@ -260,25 +320,35 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_fwd_kernel(const
     const float4 v = src >= 0 ? load4<BF16>(x, (row + src) * C + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     xs[i][0] = v.x; xs[i][1] = v.y; xs[i][2] = v.z; xs[i][3] = v.w;
   }
-  for (int t = t0; t < t1; ++t) {
-    const float4 v = load4<BF16>(x, (row + t) * C + c);
-    const float xc[4] = {v.x, v.y, v.z, v.w};
-    float o[4];
+  // Eight steps' loads are issued together, then consumed in order.
+  for (int tb = t0; tb < t1; tb += kConvBatch) {
+    float4 xv[kConvBatch];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float pre = wk[e][0] * xs[0][e] + wk[e][1] * xs[1][e] + wk[e][2] * xs[2][e] + wk[e][3] * xc[e] + bs[e];
-      o[e] = siluf_(pre);
-      xs[0][e] = xs[1][e];
-      xs[1][e] = xs[2][e];
-      xs[2][e] = xc[e];
+    for (int k = 0; k < kConvBatch; ++k)
+      xv[k] = tb + k < t1 ? load4<BF16>(x, (row + tb + k) * C + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int k = 0; k < kConvBatch; ++k) {
+      if (tb + k < t1) {
+        const float xc[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pre =
+              wk[e][0] * xs[0][e] + wk[e][1] * xs[1][e] + wk[e][2] * xs[2][e] + wk[e][3] * xc[e] + bs[e];
+          o[e] = siluf_(pre);
+          xs[0][e] = xs[1][e];
+          xs[1][e] = xs[2][e];
+          xs[2][e] = xc[e];
+        }
+        store4<BF16>(u, (row + tb + k) * C + c, make_float4(o[0], o[1], o[2], o[3]));
+      }
     }
-    store4<BF16>(u, (row + t) * C + c, make_float4(o[0], o[1], o[2], o[3]));
   }
 }
 
 // Backward, same thread layout.  dpre_t = du_t SiLU'(pre_t); dx_s = sum_i w[c][i] dpre_{s+3-i};
 // the thread's partials of dw[c][i] = sum dpre_t x_{t-3+i} and dbias[c] = sum dpre_t go to
-// part[(b * nchunk + chunk)][C][5] (4 taps + bias).
+// part[(b * nchunk + chunk)] as [C][4] taps followed by C biases.
 template <bool BF16>
 __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_bwd_kernel(const void* __restrict__ x,
                                                                             const float* __restrict__ w,
@@ -338,53 +408,61 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_bwd_kernel(const
     }
   }
   float aw[4][4] = {}, ab[4] = {};
-  for (int t = t0; t < t1 + 3; ++t) {
-    xat(t, xw[3]);
-    dpre_at(t, xw, dp[3]);
-    if (t < t1) {
+  const int tend = t1 + 3;
+  for (int tb = t0; tb < tend; tb += kConvBatch) {
+    // Eight steps' x and du loads in flight together.
+    float4 xv[kConvBatch], dv[kConvBatch];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) aw[e][i] += dp[3][e] * xw[i][e];
-        ab[e] += dp[3][e];
-      }
-    }
-    const int s = t - 3;
-    if (s >= t0) {
-      float o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        o[e] = wk[e][3] * dp[0][e] + wk[e][2] * dp[1][e] + wk[e][1] * dp[2][e] + wk[e][0] * dp[3][e];
-      *(float4*)(dx + (row + s) * C + c) = make_float4(o[0], o[1], o[2], o[3]);
+    for (int k = 0; k < kConvBatch; ++k) {
+      const int t = tb + k;
+      const bool in = t < tend && t < T;
+      xv[k] = in ? load4<BF16>(x, (row + t) * C + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      dv[k] = in ? *(const float4*)(du + (row + t) * C + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
+    for (int k = 0; k < kConvBatch; ++k) {
+      const int t = tb + k;
+      if (t < tend) {
+        xw[3][0] = xv[k].x; xw[3][1] = xv[k].y; xw[3][2] = xv[k].z; xw[3][3] = xv[k].w;
+        const float ds[4] = {dv[k].x, dv[k].y, dv[k].z, dv[k].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xw[i][e] = xw[i + 1][e];
-        dp[i][e] = dp[i + 1][e];
+        for (int e = 0; e < 4; ++e) {
+          const float pre =
+              wk[e][0] * xw[0][e] + wk[e][1] * xw[1][e] + wk[e][2] * xw[2][e] + wk[e][3] * xw[3][e] + bs[e];
+          dp[3][e] = t < T ? ds[e] * silu_gradf_(pre) : 0.0f;
+        }
+        if (t < t1) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) aw[e][i] += dp[3][e] * xw[i][e];
+            ab[e] += dp[3][e];
+          }
+        }
+        const int sidx = t - 3;
+        if (sidx >= t0) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = wk[e][3] * dp[0][e] + wk[e][2] * dp[1][e] + wk[e][1] * dp[2][e] + wk[e][0] * dp[3][e];
+          *(float4*)(dx + (row + sidx) * C + c) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xw[i][e] = xw[i + 1][e];
+            dp[i][e] = dp[i + 1][e];
+          }
       }
+    }
   }
-  float* pp = part + (long)(b * nchunk + chunk) * C * 5;
+  float* pp = part + (long)(b * nchunk + chunk) * C * 5;  // [4C: dw as [C][4] | C: dbias]
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pp[(c + e) * 5 + i] = aw[e][i];
-    pp[(c + e) * 5 + 4] = ab[e];
+    *(float4*)(pp + (c + e) * 4) = make_float4(aw[e][0], aw[e][1], aw[e][2], aw[e][3]);
+    pp[4 * C + c + e] = ab[e];
   }
-}
-
-// dw[c][i] and dbias[c] from the per-(batch, chunk) partials, summed in order.
-__global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_sum_kernel(const float* __restrict__ part, int parts, int C,
-                                                                       float* __restrict__ dw,
-                                                                       float* __restrict__ dbias) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;  // over [C][5]
-  if (j >= C * 5) return;
-  float s = 0.0f;
-  for (int p = 0; p < parts; ++p) s += part[(long)p * C * 5 + j];
-  const int cc = j / 5, i = j % 5;
-  if (i < 4) dw[cc * 4 + i] = s;
-  else if (dbias) dbias[cc] = s;
 }
 
 }  // namespace m2rnn
