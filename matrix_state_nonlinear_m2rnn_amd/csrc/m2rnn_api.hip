@@ -97,19 +97,38 @@ int occupancy(const void* kernel, int threads) {
   return blocks;
 }
 
-// Row blocks per workgroup: the smallest that lets every workgroup be resident at once (one
-// wave of workgroups), else the one with the fewest waves of workgroups.
+// Whether a kernel spills registers to scratch memory (its per-lane private segment is not empty).
+bool spills(const void* kernel) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, bool> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(kernel);
+  if (it != cache.end()) return it->second;
+  hipFuncAttributes attr{};
+  const bool s = hipFuncGetAttributes(&attr, kernel) == hipSuccess && attr.localSizeBytes > 0;
+  cache[kernel] = s;
+  return s;
+}
+
+// Row blocks per workgroup: among the kernels that keep everything in registers, the smallest
+// that lets every workgroup be resident at once (one wave of workgroups), else the one with the
+// fewest waves of workgroups.  A kernel that spills (several row blocks of a wide state) runs
+// far slower than more waves of workgroups, so it is taken only when nothing else is built.
 int plan_row_blocks(const m2rnn_dims* d, int math, bool bf16, int mode, int requested) {
   const int kb = (int)(d->K / 16);
   if (requested > 0) return (kb % requested == 0 && fwd_kernel(math, (int)d->V, requested, bf16, mode)) ? requested : -1;
   const DeviceInfo info = device_info();
   const long units = d->B * d->N;
-  int best = -1;
+  int best = -1, spilling = -1;
   double best_rounds = 1e30;
   for (int rb : {1, 2, 4}) {
     if (kb % rb != 0) continue;
     const void* kern = fwd_kernel(math, (int)d->V, rb, bf16, mode);
     if (!kern) continue;
+    if (info.cus > 0 && spills(kern)) {
+      if (spilling < 0) spilling = rb;
+      continue;
+    }
     const long blocks = units * (kb / rb);
     const int occ = info.cus > 0 ? occupancy(kern, (int)(4 * d->V)) : 0;
     const double cap = (double)occ * info.cus;
@@ -120,7 +139,7 @@ int plan_row_blocks(const m2rnn_dims* d, int math, bool bf16, int mode, int requ
     }
     if (rounds <= 1.0) break;
   }
-  return best;
+  return best > 0 ? best : spilling;
 }
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }

@@ -52,8 +52,8 @@ struct FwdShape {
   static constexpr int TC = 16;              // steps per staged chunk (the step loop is unrolled per chunk)
 };
 
-// Per-step stage record (fp32): [f, 0, 0, 0 | q rows | c*k rows | v (V)] (slot 3 is the zero that
-// the lanes without a rank-1 operand read).
+// Per-step stage record (fp32): [f, 1-f, -2(1-f), 0 | q rows | c*k rows | v (V)] (slot 3 is the
+// zero that the lanes without a rank-1 operand read).
 template <int V, int RB>
 struct Stage {
   static constexpr int ROWS = 16 * RB;
@@ -136,18 +136,25 @@ struct ChunkRegs {
     q.store(stage, St::STEP, St::OQ, 1.0f, tid);
     k.store(stage, St::STEP, St::OK, kTwoLog2e, tid);
     v.store(stage, St::STEP, St::OV, 1.0f, tid);
-    if (tid < S::TC) *(float4*)(stage + tid * St::STEP) = make_float4(f, 0.0f, 0.0f, 0.0f);
+    if (tid < S::TC) {
+      const float gf = 1.0f - f;
+      *(float4*)(stage + tid * St::STEP) = make_float4(f, gf, -2.0f * gf, 0.0f);
+    }
   }
 };
 
 // Per-step inputs a lane needs, read from the stage ring one step ahead.
 template <int RB, bool SPLIT>
 struct StepIn {
-  float f;                     // the gate (1-f and -2(1-f) are formed in registers)
+  float f, gf, m2g;            // the gate f, 1 - f and -2(1 - f)
   float av;                    // A operand of the rank-1 MFMA: v[16w + n] on lanes with g == 0, else 0
   float bk[RB];                // B operand of the rank-1 MFMA: c*k[row] on lanes with g == 0, else 0
-  float qn[RB];                // split modes: q of row 16rb + 4g + (n & 3) (a quad holds rows 4g..4g+3)
-                               // f32 mode:    q of row 16rb + n
+  // q for the readout.  Split modes with one row block: q of rows 4g .. 4g+3 (q4).  Split modes
+  // with several row blocks, where registers are scarce: q of row 16rb + 4g + (n & 3) (qn; a quad of
+  // lanes holds rows 4g .. 4g+3, broadcast by DPP).  f32 mode: q of row 16rb + n (qn).
+  static constexpr bool Q4 = SPLIT && RB == 1;
+  float4 q4[Q4 ? RB : 1];
+  float qn[Q4 ? 1 : RB];
   float vcol;                  // f32 mode: v[ycol] for the w_r (.) v readout term
 };
 
@@ -164,12 +171,20 @@ template <int V, int RB, bool SPLIT>
 __device__ __forceinline__ StepIn<RB, SPLIT> read_step(const float* st, const StepOffsets<RB>& o) {
   using Sg = Stage<V, RB>;
   StepIn<RB, SPLIT> s;
-  s.f = st[0];
+  const float4 gate = *(const float4*)st;
+  s.f = gate.x;
+  s.gf = gate.y;
+  s.m2g = gate.z;
   s.av = st[o.av];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) s.bk[rb] = st[o.bk[rb]];
+  if constexpr (StepIn<RB, SPLIT>::Q4) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) s.qn[rb] = st[o.q + 16 * rb];
+    for (int rb = 0; rb < RB; ++rb) s.q4[rb] = *(const float4*)(st + o.q + 16 * rb);
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s.qn[rb] = st[o.q + 16 * rb];
+  }
   s.vcol = SPLIT ? 0.0f : st[o.vcol];
   return s;
 }
@@ -413,7 +428,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   so.av = g == 0 ? St::OV + 16 * w + n : 3;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) so.bk[rb] = g == 0 ? St::OK + 16 * rb + n : 3;
-  so.q = SPLIT ? St::OQ + 4 * g + (n & 3) : St::OQ + n;
+  so.q = !SPLIT ? St::OQ + n : (StepIn<RB, SPLIT>::Q4 ? St::OQ + 4 * g : St::OQ + 4 * g + (n & 3));
   so.vcol = St::OV + ycol;
 
   // ---- stage chunk 0, prefetch chunk 1 ----
@@ -444,12 +459,18 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
   float xq[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // split readout: partial sums of the last four steps
   f32x4 yT[RB];                            // split readout: transposed tile of H_{t-1}
-  float qprev[RB];                         // and q_{t-1} (quad layout)
+  float4 qprev[RB];                        // and q_{t-1} of rows 4g .. 4g+3 (x only: see StepIn::qn)
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     yT[rb] = zero4;
-    qprev[rb] = 0.0f;
+    qprev[rb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   }
+  // q of rows 4g .. 4g+3 for the readout: read whole (one row block) or quad-broadcast by DPP.
+  auto q_rows = [](const float4& qp) -> float4 {
+    if constexpr (StepIn<RB, SPLIT>::Q4) return qp;
+    return make_float4(dpp_all<kDppQuadBcast0>(qp.x), dpp_all<kDppQuadBcast1>(qp.x), dpp_all<kDppQuadBcast2>(qp.x),
+                       dpp_all<kDppQuadBcast3>(qp.x));
+  };
   f32x4 kv[RB];                            // rank-1 term (c k_t) v_t^T of the coming step
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) kv[rb] = mfma_f32(cur.av, cur.bk[rb], zero4);
@@ -539,11 +560,11 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
         float x = 0.0f;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          x = rb == 0 ? dpp_all<kDppQuadBcast0>(qprev[rb]) * yT[rb][0]
-                      : __builtin_fmaf(dpp_all<kDppQuadBcast0>(qprev[rb]), yT[rb][0], x);
-          x = __builtin_fmaf(dpp_all<kDppQuadBcast1>(qprev[rb]), yT[rb][1], x);
-          x = __builtin_fmaf(dpp_all<kDppQuadBcast2>(qprev[rb]), yT[rb][2], x);
-          x = __builtin_fmaf(dpp_all<kDppQuadBcast3>(qprev[rb]), yT[rb][3], x);
+          const float4 qq = q_rows(qprev[rb]);
+          x = rb == 0 ? qq.x * yT[rb][0] : __builtin_fmaf(qq.x, yT[rb][0], x);
+          x = __builtin_fmaf(qq.y, yT[rb][1], x);
+          x = __builtin_fmaf(qq.z, yT[rb][2], x);
+          x = __builtin_fmaf(qq.w, yT[rb][3], x);
         }
         xq[(j + 3) & 3] = x;
         if (j % 4 == 0) ygrp = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);  // finished after the publish
@@ -594,7 +615,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
           read_step<V, RB, SPLIT>(j + 1 == TC ? stage[cb ^ 1] : stage[cb] + (j + 1) * St::STEP, so);
 
       // (3) tanh + gate blend: H = f H + (1-f)(1 - 2r) = fma(-2(1-f), r, fma(f, H, 1-f)).
-      const float gf = 1.0f - cur.f, m2g = -2.0f * gf;
+      const float gf = cur.gf, m2g = cur.m2g;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
@@ -627,7 +648,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
             } else {
               yT[rb] = mfma16_bf16(oh, bsel, zero4);
             }
-            qprev[rb] = cur.qn[rb];
+            if constexpr (StepIn<RB, SPLIT>::Q4) qprev[rb] = cur.q4[rb];
+            else qprev[rb].x = cur.qn[rb];
           }
         } else {
           float x[4];
@@ -672,10 +694,11 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
       float x = 0.0f;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        x = __builtin_fmaf(dpp_all<kDppQuadBcast0>(qprev[rb]), yT[rb][0], x);
-        x = __builtin_fmaf(dpp_all<kDppQuadBcast1>(qprev[rb]), yT[rb][1], x);
-        x = __builtin_fmaf(dpp_all<kDppQuadBcast2>(qprev[rb]), yT[rb][2], x);
-        x = __builtin_fmaf(dpp_all<kDppQuadBcast3>(qprev[rb]), yT[rb][3], x);
+        const float4 qq = q_rows(qprev[rb]);
+        x = __builtin_fmaf(qq.x, yT[rb][0], x);
+        x = __builtin_fmaf(qq.y, yT[rb][1], x);
+        x = __builtin_fmaf(qq.z, yT[rb][2], x);
+        x = __builtin_fmaf(qq.w, yT[rb][3], x);
       }
       xq[3] = x;
       float yv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
