@@ -54,14 +54,27 @@ int resolve_math(int math) {
   return math;
 }
 
-const void* fwd_kernel(int math, int V, int rb, bool bf16, int mode) {
+const void* fwd_kernel(int math, int V, int rb, int rw, bool bf16, int mode) {
   switch (math) {
-    case M2RNN_MATH_F32: return fwd_kernel_f32(V, rb, bf16, mode);
-    case M2RNN_MATH_F16X3: return fwd_kernel_f16x3(V, rb, bf16, mode);
-    case M2RNN_MATH_BF16X3: return fwd_kernel_bf16x3(V, rb, bf16, mode);
-    case M2RNN_MATH_BF16: return fwd_kernel_bf16(V, rb, bf16, mode);
+    case M2RNN_MATH_F32: return fwd_kernel_f32(V, rb, rw, bf16, mode);
+    case M2RNN_MATH_F16X3: return fwd_kernel_f16x3(V, rb, rw, bf16, mode);
+    case M2RNN_MATH_BF16X3: return fwd_kernel_bf16x3(V, rb, rw, bf16, mode);
+    case M2RNN_MATH_BF16: return fwd_kernel_bf16(V, rb, rw, bf16, mode);
     default: return nullptr;
   }
+}
+
+// Row groups per workgroup of the forward scan: with fewer than four 16-column tiles (V < 64) and
+// one row block per wave, a workgroup carries 4 / (V/16) row blocks side by side, one group of
+// V/16 waves each, so that it has one wave on every SIMD of its CU (single-wave workgroups were
+// spread unevenly over the SIMDs), and sums their readouts itself.  The row blocks of a state must
+// divide evenly; built for the split-precision contractions.
+int row_groups(const m2rnn_dims* d, int rb, int math) {
+  if (rb != 1 || d->V >= 64 || math == M2RNN_MATH_F32) return 1;
+  const long kb = d->K / 16;
+  for (int rw = (int)(64 / d->V); rw > 1; rw /= 2)
+    if (kb % rw == 0) return rw;
+  return 1;
 }
 
 struct DeviceInfo {
@@ -116,21 +129,25 @@ bool spills(const void* kernel) {
 // far slower than more waves of workgroups, so it is taken only when nothing else is built.
 int plan_row_blocks(const m2rnn_dims* d, int math, bool bf16, int mode, int requested) {
   const int kb = (int)(d->K / 16);
-  if (requested > 0) return (kb % requested == 0 && fwd_kernel(math, (int)d->V, requested, bf16, mode)) ? requested : -1;
+  if (requested > 0)
+    return (kb % requested == 0 && fwd_kernel(math, (int)d->V, requested, row_groups(d, requested, math), bf16, mode))
+               ? requested
+               : -1;
   const DeviceInfo info = device_info();
   const long units = d->B * d->N;
   int best = -1, spilling = -1;
   double best_rounds = 1e30;
   for (int rb : {1, 2, 4}) {
     if (kb % rb != 0) continue;
-    const void* kern = fwd_kernel(math, (int)d->V, rb, bf16, mode);
+    const int rw = row_groups(d, rb, math);
+    const void* kern = fwd_kernel(math, (int)d->V, rb, rw, bf16, mode);
     if (!kern) continue;
     if (info.cus > 0 && spills(kern)) {
       if (spilling < 0) spilling = rb;
       continue;
     }
-    const long blocks = units * (kb / rb);
-    const int occ = info.cus > 0 ? occupancy(kern, (int)(4 * d->V)) : 0;
+    const long blocks = units * (kb / (rb * rw));
+    const int occ = info.cus > 0 ? occupancy(kern, (int)(4 * d->V * rw)) : 0;
     const double cap = (double)occ * info.cus;
     const double rounds = cap > 0 ? (double)((blocks + (long)cap - 1) / (long)cap) : 1.0;
     if (rounds < best_rounds) {
@@ -157,8 +174,12 @@ int fill(float* dst, const float* src, long count, hipStream_t stream) {
   return hip_status(hipGetLastError());
 }
 
-size_t fwd_partial_bytes(const m2rnn_dims* d, int rb) {
-  const long S = d->K / (16 * rb);
+// Readout planes of the scan: one per workgroup of a (b, n) pair; more than one go to the workspace
+// and are summed by the finish pass.
+long readout_planes(const m2rnn_dims* d, int rb, int math) { return d->K / (16 * rb * row_groups(d, rb, math)); }
+
+size_t fwd_partial_bytes(const m2rnn_dims* d, int rb, int math) {
+  const long S = readout_planes(d, rb, math);
   if (S <= 1) return 0;
   return round_up((size_t)S * d->B * d->T * d->N * d->V * sizeof(float));
 }
@@ -194,7 +215,7 @@ int check_fwd(const FwdCall& c, int* math_out, int* rb_out) {
   }
   const int rb = plan_row_blocks(d, math, bf16, MODE_FWD, c.row_blocks);
   if (rb < 0) return c.row_blocks > 0 && (d->K / 16) % c.row_blocks != 0 ? M2RNN_EINVAL : M2RNN_EUNSUPPORTED;
-  const size_t need = empty ? 0 : fwd_partial_bytes(d, rb);
+  const size_t need = empty ? 0 : fwd_partial_bytes(d, rb, math);
   if (need > 0 && (!c.ws || c.ws_bytes < need || !aligned16(c.ws))) return M2RNN_EWORKSPACE;
   *math_out = math;
   *rb_out = rb;
@@ -205,31 +226,33 @@ int launch_scan(const FwdCall& c, int math, int rb) {
   const m2rnn_dims* d = c.d;
   if (d->B == 0 || d->N == 0) return M2RNN_OK;
   const bool bf16 = c.qkv_dtype == M2RNN_DTYPE_BF16;
-  const int S = (int)(d->K / (16 * rb));
+  const int rw = row_groups(d, rb, math);
+  const int S = (int)readout_planes(d, rb, math);  // workgroups per (b, n), one readout plane each
+  const int planes = S;
   if (d->T == 0) {
     // Nothing to scan: H_T = H0 (or zeros); there are no segments to checkpoint.
     return fill(c.H_T, c.H0, d->B * d->N * d->K * d->V, c.stream);
   }
   FwdArgs a{};
   a.q = c.q; a.k = c.k; a.v = c.v; a.f = c.f; a.W = c.W; a.w_r = c.w_r; a.H0 = c.H0;
-  a.y = S > 1 ? (float*)c.ws : c.y;
+  a.y = planes > 1 ? (float*)c.ws : c.y;
   a.H_T = c.H_T;
   a.ckpt = c.ckpt;
   a.B = (int)d->B; a.T = (int)d->T; a.N = (int)d->N; a.K = (int)d->K;
   a.Nqk = qk_heads(d);
   a.S = S;
   a.seg = c.ckpt ? kBwdSeg : 0;
-  const void* kern = fwd_kernel(math, (int)d->V, rb, bf16, MODE_FWD);
+  const void* kern = fwd_kernel(math, (int)d->V, rb, rw, bf16, MODE_FWD);
   if (!kern) return M2RNN_EUNSUPPORTED;
   void* args[] = {&a};
-  const dim3 grid((unsigned)(d->B * d->N * S)), block((unsigned)(4 * d->V));
+  const dim3 grid((unsigned)(d->B * d->N * S)), block((unsigned)(4 * d->V * rw));
   return hip_status(hipLaunchKernel(kern, grid, block, args, 0, c.stream));
 }
 
-int launch_finish(const FwdCall& c, int rb) {
+int launch_finish(const FwdCall& c, int math, int rb) {
   const m2rnn_dims* d = c.d;
   if (d->B == 0 || d->N == 0 || d->T == 0) return M2RNN_OK;
-  const int S = (int)(d->K / (16 * rb));
+  const int S = (int)readout_planes(d, rb, math);
   if (S <= 1) return M2RNN_OK;
   const long plane = d->B * d->T * d->N * d->V;
   const unsigned blocks = (unsigned)((plane / 4 + 255) / 256);
@@ -329,7 +352,7 @@ int m2rnn_fwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, in
   if (m < 0 || row_blocks < 0) return M2RNN_EINVAL;
   const int rb = plan_row_blocks(dims, m, qkv_dtype == M2RNN_DTYPE_BF16, MODE_FWD, row_blocks);
   if (rb < 0) return row_blocks > 0 && (dims->K / 16) % row_blocks != 0 ? M2RNN_EINVAL : M2RNN_EUNSUPPORTED;
-  *bytes = (dims->B == 0 || dims->N == 0) ? 0 : fwd_partial_bytes(dims, rb);
+  *bytes = (dims->B == 0 || dims->N == 0) ? 0 : fwd_partial_bytes(dims, rb, m);
   return M2RNN_OK;
 }
 
@@ -352,7 +375,7 @@ int m2rnn_scan_fwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, int r
                           const float* H0, float* y, float* H_T, void* workspace, size_t workspace_bytes,
                           void* stream) {
   FWD_CALL
-  return launch_finish(c, rb);
+  return launch_finish(c, m, rb);
 }
 
 int m2rnn_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q, const void* k,
@@ -361,7 +384,7 @@ int m2rnn_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, c
   FWD_CALL
   st = launch_scan(c, m, rb);
   if (st) return st;
-  return launch_finish(c, rb);
+  return launch_finish(c, m, rb);
 }
 
 int m2rnn_bwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes) {
@@ -423,7 +446,7 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
     a.y = nullptr; a.H_T = nullptr; a.ckpt = (float*)(ws + L.ckpt);
     a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S; a.seg = kBwdSeg;
     a.Nqk = qk_heads(d);
-    const void* kern = fwd_kernel(M2RNN_MATH_F16X3, (int)V, 1, bf16, MODE_CKPT);
+    const void* kern = fwd_kernel(M2RNN_MATH_F16X3, (int)V, 1, 1, bf16, MODE_CKPT);
     if (!kern) return M2RNN_EUNSUPPORTED;
     void* args[] = {&a};
     st = hip_status(hipLaunchKernel(kern, dim3((unsigned)(B * N * S)), dim3((unsigned)(4 * V)), args, 0, stream));
@@ -517,7 +540,7 @@ int m2rnn_fwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, int row_bloc
   if (dims->T > 0 && dims->B > 0 && dims->N > 0 && !ckpt) return M2RNN_EINVAL;
   st = launch_scan(c, m, rb);
   if (st) return st;
-  return launch_finish(c, rb);
+  return launch_finish(c, m, rb);
 }
 
 int m2rnn_decode_step(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k,

@@ -2,5 +2,5 @@
 #include "m2rnn_select.h"
 
 namespace m2rnn {
-const void* fwd_kernel_f16x3(int V, int rb, bool bf16, int mode) { return pick_fwd<MATH_F16X3>(V, rb, bf16, mode); }
+const void* fwd_kernel_f16x3(int V, int rb, int rw, bool bf16, int mode) { return pick_fwd<MATH_F16X3>(V, rb, rw, bf16, mode); }
 }  // namespace m2rnn

@@ -45,10 +45,12 @@ struct FwdArgs {
   int seg;        // checkpoint interval, a multiple of TC (when ckpt is set)
 };
 
-template <int V>
+// RW: row waves, independent groups of NT waves in one workgroup, each carrying its own row
+// blocks (used when V/16 < 4, so that a workgroup still has a wave on each SIMD of its CU).
+template <int V, int RW = 1>
 struct FwdShape {
-  static constexpr int NT = V / 16;          // value tiles = waves per workgroup
-  static constexpr int NTH = 64 * NT;        // threads per workgroup
+  static constexpr int NT = V / 16;          // value tiles = waves per row group
+  static constexpr int NTH = 64 * NT * RW;   // threads per workgroup
   static constexpr int TC = 16;              // steps per staged chunk (the step loop is unrolled per chunk)
 };
 
@@ -112,10 +114,10 @@ struct TileLoader {
 };
 
 // Prefetch registers for one chunk of q, k, v, f.
-template <int V, int RB, bool BF16>
+template <int V, int RB, bool BF16, int RW = 1>
 struct ChunkRegs {
-  using S = FwdShape<V>;
-  static constexpr int ROWS = 16 * RB;
+  using S = FwdShape<V, RW>;
+  static constexpr int ROWS = 16 * RB * RW;  // rows staged for the whole workgroup
   TileLoader<S::TC, ROWS, S::NTH, BF16> q, k;
   TileLoader<S::TC, V, S::NTH, BF16> v;
   float f;
@@ -132,7 +134,7 @@ struct ChunkRegs {
     if (tid < valid) f = a.f[((long)b * a.T + t0 + tid) * a.N + nh];
   }
   __device__ __forceinline__ void store(float* stage, int tid) const {
-    using St = Stage<V, RB>;
+    using St = Stage<V, RB * RW>;
     q.store(stage, St::STEP, St::OQ, 1.0f, tid);
     k.store(stage, St::STEP, St::OK, kTwoLog2e, tid);
     v.store(stage, St::STEP, St::OV, 1.0f, tid);
@@ -240,13 +242,13 @@ __device__ __forceinline__ float reduce_rows4(float x0, float x1, float x2, floa
 // every `seg`-step segment (used by the backward pass).
 enum { MODE_FWD = 0, MODE_CKPT = 1 };
 
-template <int V, int RB, int MATH, bool BF16IN, int MODE>
-__global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const FwdArgs a) {
-  using Sh = FwdShape<V>;
-  using St = Stage<V, RB>;
+template <int V, int RB, int MATH, bool BF16IN, int MODE, int RW = 1>
+__global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(const FwdArgs a) {
+  using Sh = FwdShape<V, RW>;
+  using St = Stage<V, RB * RW>;
   constexpr int NT = Sh::NT;
   constexpr int TC = Sh::TC;
-  constexpr int ROWS = 16 * RB;
+  constexpr int ROWS = 16 * RB;  // rows of one wave (of one row group)
   constexpr bool SPLIT = MATH != MATH_F32;
   constexpr int NCH = (NT + 1) / 2;  // 32-wide contraction chunks of the split modes
   static_assert(TC % 2 == 0, "the exchange-buffer parity is derived from the step index within a chunk");
@@ -258,10 +260,17 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   //          Every access is 8 contiguous bytes per lane (no LDS bank conflicts); the two halves
   //          of a chunk, 512 bytes apart, are read by one 2 x 8-byte instruction.
   constexpr int XWORDS = SPLIT ? (RB * NCH * 2 * 64 * 4) : (RB * NT * 64 * 4);
-  __shared__ __attribute__((aligned(16))) uint32_t xbuf[2][XWORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t xbuf[2][RW][XWORDS];
+  // Several row groups (split modes): their readout partials meet here, [3 chunks][4 groups of four
+  // steps][RW][NT][64 lanes], and are summed in the workgroup (a ring of three chunks: a chunk's
+  // groups are summed one chunk later, and its slot is reused two chunks after that, so barriers
+  // at every chunk keep writers and readers apart).
+  constexpr bool YRED = MODE == MODE_FWD && SPLIT && RW > 1;
+  __shared__ float ybuf[YRED ? 3 * 4 * RW * NT * 64 : 1];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = (tid >> 6) % NT;   // value tile of this wave
+  const int wr = (tid >> 6) / NT;  // row group of this wave
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int n = lane & 15;
@@ -281,7 +290,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   }
   const int b = u / a.N;
   const int nh = u % a.N;
-  const int row0 = s * ROWS;
+  const int row0_wg = s * ROWS * RW;       // first row of the workgroup
+  const int row0 = row0_wg + wr * ROWS;    // first row of this wave
   const long KV = (long)a.K * V;
 
   // ---- W operands (A = W'^T with the permuted contraction index), W' = c W ----
@@ -368,7 +378,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
     for (int rb = 0; rb < RB; ++rb) {
       if constexpr (!SPLIT) {
         if constexpr (NT > 1)
-          *(float4*)&xbuf[buf][((rb * NT + w) * 64 + lane) * 4] = make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
+          *(float4*)&xbuf[buf][wr][((rb * NT + w) * 64 + lane) * 4] = make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
       } else {
         uint32_t h0, h1, l0, l1;
         split_pair<MATH>(H[rb][0], H[rb][1], h0, l0);
@@ -379,8 +389,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
         lq[rb].y = l1;
         if constexpr (NT > 1) {
           const int base = ((rb * NCH + (w >> 1)) * 4 + (w & 1)) * 128 + lane * 2;
-          *(uint2*)&xbuf[buf][base] = make_uint2(h0, h1);
-          if constexpr (MATH != MATH_BF16) *(uint2*)&xbuf[buf][base + 256] = make_uint2(l0, l1);
+          *(uint2*)&xbuf[buf][wr][base] = make_uint2(h0, h1);
+          if constexpr (MATH != MATH_BF16) *(uint2*)&xbuf[buf][wr][base + 256] = make_uint2(l0, l1);
         }
       }
     }
@@ -388,7 +398,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
 
   // Odd tile counts leave half of the last chunk unwritten: zero both buffers once.
   if constexpr (SPLIT && (NT & 1) && NT > 1) {
-    for (int i = tid; i < 2 * XWORDS; i += Sh::NTH) (&xbuf[0][0])[i] = 0u;
+    for (int i = tid; i < 2 * RW * XWORDS; i += Sh::NTH) (&xbuf[0][0][0])[i] = 0u;
     lds_barrier();
   }
 
@@ -408,13 +418,16 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   // the step loop.)
   const int ycol = SPLIT ? 16 * w + n : 16 * w + 4 * g + (n >> 2);
   const bool ystore = SPLIT || ((n & 3) == 0);
-  const float wr = (MODE == MODE_FWD && a.S == 1) ? a.w_r[(long)nh * V + ycol] : 0.0f;
+  // Readout planes: one per workgroup (the row groups' partials are summed in the workgroup);
+  // with one plane y is final here, and row group 0 adds the w_r (.) v term.
+  const int planes = a.S;
+  const float wrv = (MODE == MODE_FWD && planes == 1 && wr == 0) ? a.w_r[(long)nh * V + ycol] : 0.0f;
   const int ystep = a.N * V;  // floats between consecutive steps of y
   float* ybase = nullptr;  // y (S == 1) or this row group's partial plane, at [b, 0, nh, 0]
   int ybytes = 0;
   if constexpr (MODE == MODE_FWD) {
     const long plane = (long)a.B * a.T * a.N * V;
-    ybase = a.y + (a.S > 1 ? (long)s * plane : 0) + ((long)b * a.T * a.N + nh) * V;
+    ybase = a.y + (planes > 1 ? (long)s * plane : 0) + ((long)b * a.T * a.N + nh) * V;
     // Element (t, nh, c) is valid iff t < T, i.e. iff it lies below (T N V - nh V) floats from ybase.
     ybytes = (a.T * a.N - nh) * V * 4;
   }
@@ -427,15 +440,38 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
   StepOffsets<RB> so;
   so.av = g == 0 ? St::OV + 16 * w + n : 3;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) so.bk[rb] = g == 0 ? St::OK + 16 * rb + n : 3;
-  so.q = !SPLIT ? St::OQ + n : (StepIn<RB, SPLIT>::Q4 ? St::OQ + 4 * g : St::OQ + 4 * g + (n & 3));
+  for (int rb = 0; rb < RB; ++rb) so.bk[rb] = g == 0 ? St::OK + wr * ROWS + 16 * rb + n : 3;
+  so.q = wr * ROWS + (!SPLIT ? St::OQ + n : (StepIn<RB, SPLIT>::Q4 ? St::OQ + 4 * g : St::OQ + 4 * g + (n & 3)));
   so.vcol = St::OV + ycol;
 
+  // Row groups' readouts of the group of four steps starting at tg: kept in ybuf ...
+  auto ykeep = [&](int tg, float yv) {
+    if constexpr (YRED) {
+      const int slot = (tg / TC) % 3, k = (tg % TC) / 4;
+      ybuf[(((slot * 4 + k) * RW + wr) * NT + w) * 64 + lane] = yv;
+    }
+  };
+  // ... and summed, for the chunk starting at tc: wave (w, wr) stores the groups k = wr, wr + RW, ...
+  // of its value tile.
+  auto ysum = [&](int tc) {
+    if constexpr (YRED) {
+      const int slot = (tc / TC) % 3;
+#pragma unroll
+      for (int k = wr; k < 4; k += RW) {
+        float yv = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RW; ++r) yv += ybuf[(((slot * 4 + k) * RW + r) * NT + w) * 64 + lane];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, ylane + (uint32_t)((tc + 4 * k) * ystep * 4), 0,
+                                              0);
+      }
+    }
+  };
+
   // ---- stage chunk 0, prefetch chunk 1 ----
-  ChunkRegs<V, RB, BF16IN> pre;
-  pre.load(a, b, nh, row0, 0, tid);
+  ChunkRegs<V, RB, BF16IN, RW> pre;
+  pre.load(a, b, nh, row0_wg, 0, tid);
   pre.store(stage[0], tid);
-  if (a.T > TC) pre.load(a, b, nh, row0, TC, tid);
+  if (a.T > TC) pre.load(a, b, nh, row0_wg, TC, tid);
   publish(0);
 
   const int nseg = a.seg > 0 ? (a.T + a.seg - 1) / a.seg : 0;
@@ -502,7 +538,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
                 make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
         }
       }
-      const uint32_t* xr = xbuf[j & 1];
+      const uint32_t* xr = xbuf[j & 1][wr];
 
       // (1) B operands of this step.
       float4 hb[SPLIT ? 1 : RB * NT];
@@ -524,7 +560,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
             hq[rb].z = ph.x;
             hq[rb].w = ph.y;
             if constexpr (MATH != MATH_BF16) {
-              const uint2 pl = ((const uint2*)xbuf[j & 1])[plo_off[rb]];
+              const uint2 pl = ((const uint2*)xbuf[j & 1][wr])[plo_off[rb]];
               lq[rb].z = pl.x;
               lq[rb].w = pl.y;
             }
@@ -632,9 +668,13 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
       if constexpr (MODE == MODE_FWD) {
         if constexpr (SPLIT) {
           if (j % 4 == 0) {
-            const float yv = __builtin_fmaf(wr, vterm, ygrp);
-            const uint32_t off = (j > 0 || c0 > 0) ? ylane + (uint32_t)((t - 4) * ystep * 4) : kBufferDrop;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, off, 0, 0);
+            const float yv = __builtin_fmaf(wrv, vterm, ygrp);
+            if constexpr (YRED) {
+              if (j > 0 || c0 > 0) ykeep(t - 4, yv);
+            } else {
+              const uint32_t off = (j > 0 || c0 > 0) ? ylane + (uint32_t)((t - 4) * ystep * 4) : kBufferDrop;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, off, 0, 0);
+            }
           }
           // Transposing MFMAs: yT at lane (g, j) = H_t[row 16rb + 4g + r][col 16w + j] (hi + lo),
           // used by the next step.
@@ -661,7 +701,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
             x[r] = sacc;
           }
           float yv = row16_sum4(x[0], x[1], x[2], x[3], lane);
-          yv = __builtin_fmaf(wr, cur.vcol, yv);
+          yv = __builtin_fmaf(wrv, cur.vcol, yv);
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, ylane + (uint32_t)(t * ystep * 4), 0, 0);
         }
       }
@@ -669,13 +709,24 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
       for (int rb = 0; rb < RB; ++rb) kv[rb] = mfma_f32(nxt.av, nxt.bk[rb], zero4);
       __builtin_amdgcn_sched_barrier(0);
 
-      if (j == TC - 2) pre.store(stage[cb ^ 1], tid);
-      // A single-wave workgroup (one 16-column tile) exchanges nothing, and its own LDS writes and
-      // reads of the stage ring are ordered, so it needs no barrier.
-      if constexpr (NT > 1) lds_barrier();
+      // With one 16-column tile per row group nothing is exchanged, so the only barriers are the
+      // two around the stage-ring write (every wave has finished the previous chunk's reads of that
+      // buffer before it is overwritten, and sees the new records after); a single-wave workgroup's
+      // own LDS writes and reads are ordered and need none.
+      if (j == TC - 2) {
+        if constexpr (NT == 1 && RW > 1) lds_barrier();
+        pre.store(stage[cb ^ 1], tid);
+      }
+      if constexpr (NT > 1) {
+        lds_barrier();
+      } else if constexpr (RW > 1) {
+        if (j == TC - 2) lds_barrier();
+      }
       if (j == TC - 2) {
         const int t_next = c0 + 2 * TC;  // first step of the chunk after the one just staged
-        if (t_next < a.T) pre.load(a, b, nh, row0, t_next, tid);
+        if (t_next < a.T) pre.load(a, b, nh, row0_wg, t_next, tid);
+        // The previous chunk's readout groups are all kept (its last one at this chunk's step 0).
+        if (c0 > 0) ysum(c0 - TC);
       }
       cur = nxt;
     }
@@ -702,8 +753,15 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_fwd_kernel(const Fwd
       }
       xq[3] = x;
       float yv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
-      yv = __builtin_fmaf(wr, stage[cbl][(TC - 4) * St::STEP + vlane], yv);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, ylane + (uint32_t)((tp - 4) * ystep * 4), 0, 0);
+      yv = __builtin_fmaf(wrv, stage[cbl][(TC - 4) * St::STEP + vlane], yv);
+      if constexpr (YRED) {
+        ykeep(tp - 4, yv);
+        lds_barrier();
+        ysum(tp - TC);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, ylane + (uint32_t)((tp - 4) * ystep * 4), 0,
+                                              0);
+      }
     }
   }
 

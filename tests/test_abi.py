@@ -52,14 +52,21 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert fwd(D(1, 4, 2, 16, 16), f=False) == m2.M2RNN_EINVAL
     assert fwd(D(1, 4, 2, 16, 16), ptr=18) == m2.M2RNN_EINVAL     # misaligned
     assert fwd(D(1, 4, 2, 48, 16), rb=2) == m2.M2RNN_EINVAL       # rb must divide K/16
-    # K = 64 with one 16-row block per workgroup splits each state over 4 workgroups: the partial
-    # readouts need a workspace.
-    assert fwd(D(1, 4, 2, 64, 16), rb=1) == m2.M2RNN_EWORKSPACE
+    # K = 128, V = 16 with one 16-row block per wave: a workgroup carries four row blocks (one per
+    # SIMD), so each state spans two workgroups whose partial readouts need a workspace.
+    assert fwd(D(1, 4, 2, 128, 16), rb=1) == m2.M2RNN_EWORKSPACE
+    # The fp32 contraction keeps one row block per workgroup: four partial planes at K = 64.
+    assert fwd(D(1, 4, 2, 64, 16), rb=1, math=0) == m2.M2RNN_EWORKSPACE
 
 
 def test_workspace_size_query():
+    # V = 32: two row groups of two waves per workgroup, so K = 64 spans two workgroups (two planes)
     n = m2.m2rnn_fwd_workspace_size(m2.Dims(2, 10, 3, 64, 32), 1, "f16x3", 1)
-    assert n >= 4 * 2 * 10 * 3 * 32 * 4
+    assert n >= 2 * 2 * 10 * 3 * 32 * 4
+    # the fp32 contraction: one row block per workgroup, four planes
+    assert m2.m2rnn_fwd_workspace_size(m2.Dims(2, 10, 3, 64, 32), 1, "f32", 1) >= 4 * 2 * 10 * 3 * 32 * 4
+    # V = 16, K = 64: the four row blocks share one workgroup, so no partial planes at all
+    assert m2.m2rnn_fwd_workspace_size(m2.Dims(2, 10, 3, 64, 16), 1, "f16x3", 1) == 0
     assert m2.m2rnn_fwd_workspace_size(m2.Dims(2, 10, 3, 64, 32), 1, "f16x3", 4) == 0
     with pytest.raises(m2.M2RNNError):
         m2.m2rnn_fwd_workspace_size(m2.Dims(2, 10, 3, 64, 40), 1, "f16x3", 0)

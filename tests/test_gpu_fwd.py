@@ -136,3 +136,25 @@ def test_state_bound_under_saturation():
     assert np.all(np.abs(H) <= 1.0 + 1e-6)
     yr, Hr = oracle_fwd(d)
     assert max_abs(H, Hr) <= 5e-4
+
+
+@pytest.mark.parametrize("K,V,T,math", [
+    (64, 16, 37, "f16x3"),    # four row groups in a workgroup, one readout plane
+    (128, 16, 70, "f16x3"),   # four row groups, two workgroups per state
+    (32, 16, 5, "bf16x3"),    # two row groups, a single partial chunk
+    (64, 32, 16, "f16x3"),    # two row groups of two waves each, exactly one chunk
+    (32, 32, 33, "bf16"),     # two row groups, one plane
+    (48, 16, 1, "f16x3"),     # three row blocks: one group per workgroup
+    (16, 16, 50, "f32"),      # the fp32 contraction keeps one group
+])
+def test_row_groups_in_a_workgroup(K, V, T, math):
+    # Narrow states (V < 64) put several 16-row blocks side by side in one workgroup and sum their
+    # readouts there.
+    torch_cuda()
+    d = inputs.make_inputs(2, T, 3, K, V, qkv_dtype="bf16", seed=6000 + K + V + T, with_H0=True)
+    say("row groups", K, V, T, math)
+    y, H = gpu_fwd(to_device(d, "bf16"), math)
+    yr, Hr = oracle_fwd(d)
+    ey, eh = max_abs(y, yr), max_abs(H, Hr)
+    say("errors", ey, eh)
+    assert ey <= TOL[math] and eh <= TOL[math], (ey, eh)
