@@ -127,7 +127,7 @@ def bench_backward(args) -> int:
         fws = torch.empty(max(m2.m2rnn_fwd_workspace_size(dims, dt, "auto"), 1), dtype=torch.uint8, device=dev)
         y = torch.empty((B, T, N, V), dtype=torch.float32, device=dev)
         H_T = torch.empty((B, N, K, V), dtype=torch.float32, device=dev)
-        ck = torch.empty((B, N, m2.checkpoint_count(T), K, V), dtype=torch.float32, device=dev)
+        ck = torch.empty((B, N, m2.checkpoint_count(T, V), K, V), dtype=torch.float32, device=dev)
 
         def step():
             m2.m2rnn_fwd_ckpt(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], None, y=y, H_T=H_T, ckpt=ck,
@@ -158,7 +158,8 @@ def bench_backward(args) -> int:
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "config": {"workload": w.name, "B": B, "T": T, "N": N, "K": K, "V": V, "qkv_dtype": w.qkv_dtype,
-                      "math": "f16x3", "checkpoint": m2.BWD_CHECKPOINT},
+                      "math": "f16x3", "segment": m2.BWD_CHECKPOINT,
+                      "checkpoint_interval": m2.m2rnn_checkpoint_interval(dims)},
            "tokens_per_s": B * T / (ms * 1e-3)}
     print(json.dumps(out), flush=True)
     return 0

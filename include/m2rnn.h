@@ -131,9 +131,10 @@ int m2rnn_scan_fwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, int r
  * Backward pass (BPTT of §2.7) for the loss L = sum_t <dy_t, y_t> + <dH_T, H_T>.
  *
  * The forward states are not taken from the caller: the library re-runs the recurrence and keeps
- * the state every `M2RNN_BWD_CHECKPOINT` steps, then walks the segments from last to first,
- * recomputing each segment's states from its checkpoint (the notes' §2.6 re-runs the recurrence
- * at the start of the backward; here only checkpoints are stored, not every state).
+ * the state every I = m2rnn_checkpoint_interval() steps, then walks the `M2RNN_BWD_CHECKPOINT`-step
+ * segments from last to first, recomputing each sub-segment's states from its checkpoint in
+ * on-chip memory (the notes' §2.6 re-runs the recurrence at the start of the backward; here only
+ * checkpoints are stored, not every state).
  *
  *   dH_T   upstream gradient of the final state, or NULL for zeros.
  *   dq, dk [B,T,Nqk,K]; dv [B,T,N,V]; df [B,T,N]; dW [N,V,V] and dw_r [N,V] summed over batch and
@@ -152,17 +153,22 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
  * Training pair: a forward that keeps the backward's checkpoints, and a backward that takes them
  * instead of re-running the recurrence.  The notes' §2.6 re-runs the recurrence at the start of the
  * backward so that the forward keeps no history; when a training step runs the forward anyway,
- * keeping only the states that enter every M2RNN_BWD_CHECKPOINT-step segment (1/64 of the states)
+ * keeping only the states that enter every I-th step (an eighth to a sixty-fourth of the states)
  * lets the backward skip that re-run.
  *
- * m2rnn_fwd_ckpt     m2rnn_fwd plus `ckpt` [B,N,ceil(T/64),K,V] fp32: ckpt[b][n][s] is the state
- *                    entering step 64 s (ckpt[b][n][0] = H0, or zeros).  Required when T > 0.
+ * m2rnn_fwd_ckpt     m2rnn_fwd plus `ckpt` [B,N,ceil(T/I),K,V] fp32 with I = m2rnn_checkpoint_interval():
+ *                    ckpt[b][n][s] is the state entering step I s (ckpt[b][n][0] = H0, or zeros).
+ *                    Required when T > 0.
  * m2rnn_bwd_ckpt     m2rnn_bwd with `ckpt` from m2rnn_fwd_ckpt on the same inputs in place of H0
  *                    (H0 is ckpt[., ., 0]); its workspace (m2rnn_bwd_ckpt_workspace_size) excludes
  *                    the checkpoints.  Gradients equal m2rnn_bwd's when the forward used the
  *                    F16X3 contraction (the backward's own); another contraction mode gives
  *                    checkpoints, and so gradients, that differ within that mode's error.
  */
+/* Steps between checkpoints (I above): 16 for V <= 32, 8 for V = 64, 64 for V = 128.  Smaller
+ * intervals let the backward skip a forward pass over every segment; at V = 128 the state is large
+ * and the backward runs that pass itself. */
+int m2rnn_checkpoint_interval(const m2rnn_dims* dims, int64_t* steps);
 int m2rnn_fwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q,
                    const void* k, const void* v, const float* f, const float* W, const float* w_r,
                    const float* H0, float* y, float* H_T, float* ckpt, void* workspace,

@@ -30,7 +30,7 @@ BWD_CHECKPOINT = 64
 EXPORTED = (
     "m2rnn_version", "m2rnn_status_string", "m2rnn_last_hip_error", "m2rnn_fwd_workspace_size", "m2rnn_fwd",
     "m2rnn_scan_fwd", "m2rnn_scan_fwd_finish", "m2rnn_bwd_workspace_size", "m2rnn_bwd", "m2rnn_decode_step",
-    "m2rnn_fwd_ckpt", "m2rnn_bwd_ckpt_workspace_size", "m2rnn_bwd_ckpt",
+    "m2rnn_fwd_ckpt", "m2rnn_bwd_ckpt_workspace_size", "m2rnn_bwd_ckpt", "m2rnn_checkpoint_interval",
     "m2rnn_gate_fwd", "m2rnn_gate_bwd_workspace_size", "m2rnn_gate_bwd",
     "m2rnn_out_norm_fwd", "m2rnn_out_norm_bwd_workspace_size", "m2rnn_out_norm_bwd",
     "m2rnn_conv4_silu_fwd", "m2rnn_conv4_silu_bwd_workspace_size", "m2rnn_conv4_silu_bwd",
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
             L.m2rnn_bwd_workspace_size.argtypes = [dp, ci, ci, ctypes.POINTER(sz)]
             L.m2rnn_bwd.restype = ci
             L.m2rnn_bwd.argtypes = [dp, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp] + [vp] * 7 + [vp, sz, vp]
+        L.m2rnn_checkpoint_interval.restype = ci
+        L.m2rnn_checkpoint_interval.argtypes = [dp, ctypes.POINTER(ctypes.c_int64)]
         L.m2rnn_fwd_ckpt.restype = ci
         L.m2rnn_fwd_ckpt.argtypes = [dp, ci, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp, vp] + [vp, sz, vp]
         L.m2rnn_bwd_ckpt_workspace_size.restype = ci
@@ -213,18 +215,27 @@ def _call_fwd(name, q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, workspace,
     return y, H_T, ws
 
 
-def checkpoint_count(T: int) -> int:
-    """Segments of BWD_CHECKPOINT steps: the checkpoints a forward keeps for the backward."""
-    return (T + BWD_CHECKPOINT - 1) // BWD_CHECKPOINT
+def m2rnn_checkpoint_interval(dims: Dims) -> int:
+    """Steps between the checkpoints that m2rnn_fwd_ckpt keeps for the backward."""
+    n = ctypes.c_int64(0)
+    _check("m2rnn_checkpoint_interval", lib().m2rnn_checkpoint_interval(ctypes.byref(dims), ctypes.byref(n)))
+    return int(n.value)
+
+
+def checkpoint_count(T: int, V: int) -> int:
+    """Checkpoints per (batch, head) that a forward keeps for the backward."""
+    I = m2rnn_checkpoint_interval(Dims(1, T, 1, 16, V))
+    return (T + I - 1) // I
 
 
 def m2rnn_fwd_ckpt(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int = 0, y=None, H_T=None, ckpt=None,
                    workspace=None, stream=None):
     """m2rnn_fwd that also keeps the backward's checkpoints: returns (y, H_T, ckpt) with ckpt
-    [B,N,ceil(T/64),K,V] fp32, the state entering every 64-step segment (for m2rnn_bwd_ckpt)."""
+    [B,N,ceil(T/I),K,V] fp32, the state entering every I-th step, I = m2rnn_checkpoint_interval
+    (for m2rnn_bwd_ckpt)."""
     import torch
     dims, dt, m, rb, y, H_T = _fwd_prepare(q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, True)
-    shape = (dims.B, dims.N, checkpoint_count(dims.T), dims.K, dims.V)
+    shape = (dims.B, dims.N, checkpoint_count(dims.T, dims.V), dims.K, dims.V)
     if ckpt is None:
         ckpt = torch.empty(shape, dtype=torch.float32, device=q.device)
     _require(ckpt, "ckpt", torch.float32, shape, q.device)
@@ -285,7 +296,7 @@ def m2rnn_bwd_ckpt(q, k, v, f, W, w_r, ckpt, dy, dH_T=None, *, math="auto", want
     dims, dt, m, _, _, _ = _fwd_prepare(q, k, v, f, W, w_r, None, None, None, math, 0, False)
     B, T, N, K, V, Nqk = dims.B, dims.T, dims.N, dims.K, dims.V, dims.Nqk
     dev = q.device
-    _require(ckpt, "ckpt", torch.float32, (B, N, checkpoint_count(T), K, V), dev)
+    _require(ckpt, "ckpt", torch.float32, (B, N, checkpoint_count(T, V), K, V), dev)
     _require(dy, "dy", torch.float32, (B, T, N, V), dev)
     if dH_T is not None:
         _require(dH_T, "dH_T", torch.float32, (B, N, K, V), dev)

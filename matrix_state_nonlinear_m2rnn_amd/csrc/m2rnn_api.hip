@@ -184,6 +184,16 @@ size_t fwd_partial_bytes(const m2rnn_dims* d, int rb, int math) {
   return round_up((size_t)S * d->B * d->T * d->N * d->V * sizeof(float));
 }
 
+// Steps between the backward's checkpoints for value size V (see BwdCkpt).
+int ckpt_interval(int V) {
+  switch (V) {
+    case 16: return BwdCkpt<16>::interval;
+    case 32: return BwdCkpt<32>::interval;
+    case 64: return BwdCkpt<64>::interval;
+    default: return BwdCkpt<128>::interval;
+  }
+}
+
 struct FwdCall {
   const m2rnn_dims* d;
   int qkv_dtype, math, row_blocks;
@@ -193,7 +203,7 @@ struct FwdCall {
   void* ws;
   size_t ws_bytes;
   hipStream_t stream;
-  float* ckpt = nullptr;  // optional: states entering every kBwdSeg-step segment
+  float* ckpt = nullptr;  // optional: the backward's checkpoints (every ckpt_interval(V) steps)
 };
 
 // Validates a forward call; on success fills the resolved math mode and row blocks.
@@ -241,7 +251,7 @@ int launch_scan(const FwdCall& c, int math, int rb) {
   a.B = (int)d->B; a.T = (int)d->T; a.N = (int)d->N; a.K = (int)d->K;
   a.Nqk = qk_heads(d);
   a.S = S;
-  a.seg = c.ckpt ? kBwdSeg : 0;
+  a.seg = c.ckpt ? ckpt_interval((int)d->V) : 0;
   const void* kern = fwd_kernel(math, (int)d->V, rb, rw, bf16, MODE_FWD);
   if (!kern) return M2RNN_EUNSUPPORTED;
   void* args[] = {&a};
@@ -272,12 +282,14 @@ struct BwdLayout {
   size_t total_no_ckpt = 0;  // the workspace when the caller supplies the checkpoints
 };
 
-static_assert(kBwdSeg % FwdShape<64>::TC == 0, "forward checkpoints are taken at the first step of a chunk");
+static_assert(BwdCkpt<16>::interval % 8 == 0 && BwdCkpt<64>::interval % 8 == 0 && BwdCkpt<128>::interval % 8 == 0,
+              "the forward takes checkpoints at steps 0 and 8 of a chunk");
 
-// Checkpoints: [B][N][ceil(T / kBwdSeg)][K][V] fp32.
+// Checkpoints: [B][N][ceil(T / ckpt_interval(V))][K][V] fp32.
 size_t ckpt_bytes(const m2rnn_dims* d) {
-  const long nseg = (d->T + kBwdSeg - 1) / kBwdSeg;
-  return (size_t)d->B * d->N * nseg * d->K * d->V * sizeof(float);
+  const long I = ckpt_interval((int)d->V);
+  const long nck = (d->T + I - 1) / I;
+  return (size_t)d->B * d->N * nck * d->K * d->V * sizeof(float);
 }
 
 // A shared query/key (Nqk = 1) with several heads: per-head dq, dk go to the workspace and are
@@ -294,8 +306,10 @@ BwdLayout bwd_layout(const m2rnn_dims* d) {
     off += round_up(bytes);
     return at;
   };
+  // Per-workgroup states entering the sub-segments, when the checkpoints are per segment only.
   const long nsub = kBwdSeg / (d->V <= 32 ? BwdSub<32>::value : d->V == 64 ? BwdSub<64>::value : BwdSub<128>::value);
-  L.seg = take((size_t)d->B * d->N * S * nsub * 16 * d->V * sizeof(float));
+  const bool sub_ckpt = ckpt_interval((int)d->V) < kBwdSeg;
+  L.seg = take(sub_ckpt ? 0 : (size_t)d->B * d->N * S * nsub * 16 * d->V * sizeof(float));
   L.dv = take(S > 1 ? (size_t)S * d->B * d->T * d->N * d->V * sizeof(float) : 0);
   L.df = take(S > 1 ? (size_t)S * d->B * d->T * d->N * sizeof(float) : 0);
   L.dW = take((size_t)d->B * S * d->N * d->V * d->V * sizeof(float));
@@ -444,7 +458,7 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
     FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.H0 = H0;
     a.y = nullptr; a.H_T = nullptr; a.ckpt = (float*)(ws + L.ckpt);
-    a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S; a.seg = kBwdSeg;
+    a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S; a.seg = ckpt_interval((int)V);
     a.Nqk = qk_heads(d);
     const void* kern = fwd_kernel(M2RNN_MATH_F16X3, (int)V, 1, 1, bf16, MODE_CKPT);
     if (!kern) return M2RNN_EUNSUPPORTED;
@@ -507,6 +521,14 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
               void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(dims, qkv_dtype, math, q, k, v, f, W, w_r, H0, nullptr, dy, dH_T, dq, dk, dv, df, dW, dw_r, dH0,
                   workspace, workspace_bytes, stream);
+}
+
+int m2rnn_checkpoint_interval(const m2rnn_dims* dims, int64_t* steps) {
+  if (!steps) return M2RNN_EINVAL;
+  int st = check_dims(dims, M2RNN_DTYPE_F32);
+  if (st) return st;
+  *steps = ckpt_interval((int)dims->V);
+  return M2RNN_OK;
 }
 
 int m2rnn_bwd_ckpt_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes) {

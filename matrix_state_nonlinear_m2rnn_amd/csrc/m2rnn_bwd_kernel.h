@@ -36,8 +36,8 @@ struct BwdArgs {
   const float* w_r;
   const float* dy;
   const float* dH_T;
-  const float* ckpt;   // [B][N][nseg][K][V] states entering each segment
-  float* subck;        // per-workgroup states entering each sub-segment
+  const float* ckpt;   // [B][N][ncheck][K][V]: states entering each segment, or (SUBCK) each sub-segment
+  float* subck;        // per-workgroup states entering each sub-segment (without SUBCK)
   float* dq;           // per head [B][T][N][K] (summed over heads afterwards when q is shared)
   float* dk;           // per head [B][T][N][K]
   float* dv;           // final dv (S == 1) or partials [S][B*T*N*V]
@@ -66,6 +66,16 @@ struct BwdStage {
 template <int V>
 struct BwdSub {
   static constexpr int value = V <= 32 ? 16 : (V == 64 ? 8 : 2);
+};
+
+// Checkpoint interval of the backward: every sub-segment where that stays a modest multiple of
+// the state (V <= 64: every 16 or 8 steps), so the backward needs no forward pass to find the
+// sub-segments' entry states; every segment at V = 128 (sub-segments of 2 steps), where the
+// backward runs that pass itself.
+template <int V>
+struct BwdCkpt {
+  static constexpr bool sub = V <= 64;
+  static constexpr int interval = sub ? BwdSub<V>::value : kBwdSeg;
 };
 
 // Loads steps [t0, t0 + n_steps) of one 16-row block into the stage; the records from n_steps up
@@ -167,6 +177,7 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint32_t* p) {
 
 template <int V, bool BF16IN>
 __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const BwdArgs a) {
+  constexpr bool SUBCK = BwdCkpt<V>::sub;  // checkpoints at every sub-segment
   constexpr int NT = V / 16;
   constexpr int NTH = 64 * NT;
   constexpr int NCH = (NT + 1) / 2;
@@ -210,6 +221,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   const int row0 = s * 16;
   const long KV = (long)a.K * V;
   const int nseg = (a.T + kBwdSeg - 1) / kBwdSeg;
+  const int nck = (a.T + BwdCkpt<V>::interval - 1) / BwdCkpt<V>::interval;  // checkpoints per (b, n)
   const int wg = blockIdx.x;
 
   // ---- operands of W ----
@@ -409,15 +421,18 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     pending_tb = -1;
     bwd_stage_segment<V, BF16IN>(a, b, nh, row0, t0, nst, nsub * SUB, stage, tid, NTH);
 
-    const float* ck = a.ckpt + ((long)u * nseg + seg) * KV + (long)(row0 + n) * V + 16 * w + 4 * g;
+    // The checkpoint entering sub-segment m of this segment (SUBCK), or the segment's own.
+    const long lane_off = (long)(row0 + n) * V + 16 * w + 4 * g;
+    auto ck_at = [&](int m) { return a.ckpt + ((long)u * nck + (SUBCK ? seg * NSUB + m : seg)) * KV + lane_off; };
+    const float* ck = ck_at(0);
     float H[4];
     {
-      const float4 h4 = *(const float4*)ck;
+      const float4 h4 = *(const float4*)(SUBCK ? ck_at(nsub - 1) : ck);
       H[0] = h4.x; H[1] = h4.y; H[2] = h4.z; H[3] = h4.w;
     }
 
-    // ---------------- pass A: forward up to the last sub-segment ----------------
-    if (nsub > 1) {
+    // ---------------- pass A: forward up to the last sub-segment (segment checkpoints only) ----------------
+    if (!SUBCK && nsub > 1) {
       uint2 hh, hl;
       put_tile(hst, H, hh, hl);
       lds_barrier();  // (also makes the stage written above visible)
@@ -442,7 +457,10 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       if (m < nsub - 1) {
         H[0] = nextH.x; H[1] = nextH.y; H[2] = nextH.z; H[3] = nextH.w;
       }
-      if (m > 0) nextH = *(const float4*)(m - 1 > 0 ? subck + (long)(m - 1) * 16 * V : ck);
+      if (m > 0) {
+        if constexpr (SUBCK) nextH = *(const float4*)ck_at(m - 1);
+        else nextH = *(const float4*)(m - 1 > 0 ? subck + (long)(m - 1) * 16 * V : ck);
+      }
 
       // 1. Recompute the sub-segment: hst[j] = H_{t-1} (split), zst[j] = Z_t.
       lds_barrier();  // the previous walk is done with hst, zst and the partial sums

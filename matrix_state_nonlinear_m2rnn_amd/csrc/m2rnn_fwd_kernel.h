@@ -42,7 +42,7 @@ struct FwdArgs {
   int B, T, N, K;
   int Nqk;        // heads of q and k: N, or 1 when one query/key is shared by all heads
   int S;          // workgroups per (b, n)
-  int seg;        // checkpoint interval, a multiple of TC (when ckpt is set)
+  int seg;        // checkpoint interval, a multiple of 8 (when ckpt is set)
 };
 
 // RW: row waves, independent groups of NT waves in one workgroup, each carrying its own row
@@ -527,9 +527,9 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
     for (int j = 0; j < TC; ++j) {
       const int t = c0 + j;
       // The state entering every seg-step segment (checkpoint mode, or a forward asked to keep
-      // checkpoints for the backward).  seg is a multiple of TC, so only a chunk's first step can
-      // start a segment.
-      if (j == 0 && (MODE == MODE_CKPT || a.ckpt != nullptr)) {
+      // checkpoints for the backward).  seg is a multiple of 8, so only steps 0 and 8 of a chunk
+      // can start a segment.
+      if ((j % 8) == 0 && (MODE == MODE_CKPT || a.ckpt != nullptr)) {
         if (t % a.seg == 0 && t < a.T) {
           float* dst = a.ckpt + ((long)(b * a.N + nh) * nseg + t / a.seg) * KV;
 #pragma unroll

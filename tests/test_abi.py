@@ -137,3 +137,9 @@ def test_block_entry_points_check_their_arguments():
     assert L.m2rnn_conv4_silu_fwd(1, 8, 8, 3, p, p, None, p, None) == m2.M2RNN_EINVAL
     assert L.m2rnn_conv4_silu_fwd(1, 8, 8, 0, p, None, None, p, None) == m2.M2RNN_EINVAL                # no weights
     assert L.m2rnn_conv4_silu_bwd(1, 8, 8, 0, p, p, None, p, p, p, None, None, 0, None) == m2.M2RNN_EWORKSPACE
+
+
+def test_checkpoint_interval():
+    # every sub-segment of the backward for V <= 64, every 64-step segment at V = 128
+    assert [m2.m2rnn_checkpoint_interval(m2.Dims(1, 100, 1, 16, V)) for V in (16, 32, 64, 128)] == [16, 16, 8, 64]
+    assert m2.checkpoint_count(4096, 64) == 512 and m2.checkpoint_count(70, 16) == 5

@@ -34,10 +34,11 @@ def test_forward_checkpoints(B, T, N, K, V, dtype, shared):
     # Keeping checkpoints changes nothing else.
     assert torch.equal(y, y0) and torch.equal(H_T, H0T)
     ck = ck.cpu().numpy()
-    assert ck.shape == (B, N, (T + 63) // 64, K, V)
+    I = m2.m2rnn_checkpoint_interval(m2.Dims(B, T, N, K, V))
+    assert ck.shape == (B, N, (T + I - 1) // I, K, V)
     assert np.array_equal(ck[:, :, 0], d["H0"])
     for s in range(1, ck.shape[2]):
-        sub = {x: (a[:, :64 * s] if x in ("q", "k", "v", "f") else a) for x, a in d.items() if a is not None}
+        sub = {x: (a[:, :I * s] if x in ("q", "k", "v", "f") else a) for x, a in d.items() if a is not None}
         _, Hs = oracle_fwd(sub)
         e = max_abs(ck[:, :, s], Hs)
         say("segment", s, e)
