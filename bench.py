@@ -118,7 +118,7 @@ def bench_backward(args) -> int:
         for n in ("q", "k", "v"):
             t[n] = t[n].to(torch.bfloat16).contiguous()
     B, T, N, K, V = w.B, w.T, w.N, w.K, w.V
-    dims = m2.Dims(B, T, N, K, V)
+    dims = m2.Dims(B, T, N, K, V, 1 if w.shared_qk else N)
     dt = m2.DTYPE_BF16 if w.qkv_dtype == "bf16" else m2.DTYPE_F32
     train = getattr(args, "train", False)
     if train:
@@ -371,7 +371,7 @@ def main() -> int:
     B, T, N, K, V = w.B, w.T, w.N, w.K, w.V
     y = torch.empty((B, T, N, V), dtype=torch.float32, device=dev)
     H_T = torch.empty((B, N, K, V), dtype=torch.float32, device=dev)
-    dims = m2.Dims(B, T, N, K, V)
+    dims = m2.Dims(B, T, N, K, V, 1 if w.shared_qk else N)
     dt = m2.DTYPE_BF16 if w.qkv_dtype == "bf16" else m2.DTYPE_F32
     nbytes = m2.m2rnn_fwd_workspace_size(dims, dt, math_mode, args.row_blocks)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)

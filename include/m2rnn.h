@@ -165,7 +165,7 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
  *                    F16X3 contraction (the backward's own); another contraction mode gives
  *                    checkpoints, and so gradients, that differ within that mode's error.
  */
-/* Steps between checkpoints (I above): 16 for V <= 32, 8 for V = 64, 64 for V = 128.  Smaller
+/* Steps between checkpoints (I above): 8 for V <= 64, 64 for V = 128.  Smaller
  * intervals let the backward skip a forward pass over every segment; at V = 128 the state is large
  * and the backward runs that pass itself. */
 int m2rnn_checkpoint_interval(const m2rnn_dims* dims, int64_t* steps);

@@ -65,7 +65,7 @@ struct BwdStage {
 // Steps of a segment whose H_{t-1} and Z_t are held in LDS at once.
 template <int V>
 struct BwdSub {
-  static constexpr int value = V <= 32 ? 16 : (V == 64 ? 8 : 2);
+  static constexpr int value = V <= 64 ? 8 : 2;
 };
 
 // Checkpoint interval of the backward: every sub-segment where that stays a modest multiple of
@@ -158,6 +158,110 @@ __device__ __forceinline__ void bwd_stage_segment(const BwdArgs& a, int b, int n
   }
 }
 
+// One sub-segment's stage records (SUB steps of one 16-row block), loaded into registers ahead of
+// use and written to LDS later, so that their HBM latency overlaps the walk of the sub-segment
+// after them in time.  Steps past T get f = 1 and zero q, k, v, u.
+template <int V, bool BF16IN, int SUB, int NTH>
+struct BwdSubRegs {
+  static constexpr int VEC = BF16IN ? 8 : 4;
+  static constexpr int QV = 16 / VEC;          // loads per step of q (and of k)
+  static constexpr int NQK = 2 * SUB * QV;
+  static constexpr int NVV = SUB * (V / VEC);
+  static constexpr int NU = SUB * (V / 4);
+  static constexpr int PQK = (NQK + NTH - 1) / NTH, PVV = (NVV + NTH - 1) / NTH, PU = (NU + NTH - 1) / NTH;
+  uint4 qk[PQK], vv[PVV];
+  float4 uu[PU];
+  float f;
+
+  __device__ __forceinline__ void load(const BwdArgs& a, int b, int nh, int row0, int t0, int n_steps, int tid) {
+    const int esz = BF16IN ? 2 : 4;
+#pragma unroll
+    for (int p = 0; p < PQK; ++p) {
+      const int i = tid + p * NTH;
+      const int which = i / (SUB * QV), r = i % (SUB * QV), step = r / QV, cv = r % QV;
+      qk[p] = make_uint4(0, 0, 0, 0);
+      if (i < NQK && step < n_steps) {
+        const long off = (((long)b * a.T + t0 + step) * a.Nqk + (a.Nqk == 1 ? 0 : nh)) * a.K + row0 + cv * VEC;
+        qk[p] = *(const uint4*)((const char*)(which == 0 ? a.q : a.k) + off * esz);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PVV; ++p) {
+      const int i = tid + p * NTH;
+      const int step = i / (V / VEC), cv = i % (V / VEC);
+      vv[p] = make_uint4(0, 0, 0, 0);
+      if (i < NVV && step < n_steps)
+        vv[p] = *(const uint4*)((const char*)a.v + ((((long)b * a.T + t0 + step) * a.N + nh) * V + cv * VEC) * esz);
+    }
+#pragma unroll
+    for (int p = 0; p < PU; ++p) {
+      const int i = tid + p * NTH;
+      const int step = i / (V / 4), cv = i % (V / 4);
+      uu[p] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (i < NU && step < n_steps) uu[p] = *(const float4*)(a.dy + (((long)b * a.T + t0 + step) * a.N + nh) * V + cv * 4);
+    }
+    f = 1.0f;
+    if (tid < n_steps && tid < SUB) f = a.f[((long)b * a.T + t0 + tid) * a.N + nh];
+  }
+
+  __device__ __forceinline__ void store(float* stage, int tid) const {
+    using St = BwdStage<V>;
+    auto widen = [](const uint4& raw, float (&x)[VEC]) {
+      if constexpr (BF16IN) {
+        const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = bf16_lo_to_f32(wds[e]);
+          x[2 * e + 1] = bf16_hi_to_f32(wds[e]);
+        }
+      } else {
+        x[0] = __uint_as_float(raw.x); x[1] = __uint_as_float(raw.y);
+        x[2] = __uint_as_float(raw.z); x[3] = __uint_as_float(raw.w);
+      }
+    };
+#pragma unroll
+    for (int p = 0; p < PQK; ++p) {
+      const int i = tid + p * NTH;
+      if (i < NQK) {
+        const int which = i / (SUB * QV), r = i % (SUB * QV), step = r / QV, cv = r % QV;
+        float x[VEC];
+        widen(qk[p], x);
+        float* d = stage + step * St::STEP;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          if (which == 0) {
+            d[St::OQ + cv * VEC + e] = x[e];
+          } else {
+            d[St::OCK + cv * VEC + e] = kTwoLog2e * x[e];
+            d[St::OK + cv * VEC + e] = x[e];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PVV; ++p) {
+      const int i = tid + p * NTH;
+      if (i < NVV) {
+        const int step = i / (V / VEC), cv = i % (V / VEC);
+        float x[VEC];
+        widen(vv[p], x);
+        float* d = stage + step * St::STEP + St::OV + cv * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d[e] = x[e];
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PU; ++p) {
+      const int i = tid + p * NTH;
+      if (i < NU) {
+        const int step = i / (V / 4), cv = i % (V / 4);
+        *(float4*)(stage + step * St::STEP + St::OU + cv * 4) = uu[p];
+      }
+    }
+    if (tid < SUB) *(float4*)(stage + tid * St::STEP) = make_float4(f, 0.0f, 0.0f, 0.0f);
+  }
+};
+
 // Slot (8-byte unit) of columns [4gam, 4gam + 4) of row rho in a 16x16 fp16 tile stored as 64 slots
 // (512 bytes).  The xor keeps three access patterns free of LDS bank conflicts: a lane (g, n)
 // writing or reading its own record (row n, group g), and the transposing read in which the 16
@@ -189,7 +293,9 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   using St = BwdStage<V>;
   static_assert(kBwdSeg % SUB == 0 && SUB % 2 == 0, "sub-segments tile a segment");
 
-  __shared__ __attribute__((aligned(16))) float stage[kBwdSeg * St::STEP];
+  // Stage records: the whole segment (segment checkpoints: pass A runs over it), or only the
+  // sub-segment being recomputed and walked (sub-segment checkpoints).
+  __shared__ __attribute__((aligned(16))) float stage[(SUBCK ? SUB : kBwdSeg) * St::STEP];
   // H_{t-1} of the sub-segment's steps, split fp16: [SUB][NT tiles][hi|lo][64 slots][2 dwords].
   // Pass A uses entries 0 and 1 as its exchange buffer.
   __shared__ __attribute__((aligned(16))) uint32_t hst[SUB * ENTRY];
@@ -412,14 +518,23 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   float xq[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // dv partials of the current group of four steps
   int pending_tb = -1;                     // sub-segment whose dq, dk, df await finalize
 
+  // Sub-segment checkpoints: the stage records of the next sub-segment to walk, in registers.
+  BwdSubRegs<V, BF16IN, SUB, NTH> sub_regs;
+  if constexpr (SUBCK) {
+    const int tl = ((a.T - 1) / SUB) * SUB;  // the last sub-segment
+    sub_regs.load(a, b, nh, row0, tl, min(SUB, a.T - tl), tid);
+  }
+
   for (int seg = nseg - 1; seg >= 0; --seg) {
     const int t0 = seg * kBwdSeg;
     const int nst = min(kBwdSeg, a.T - t0);
     const int nsub = (nst + SUB - 1) / SUB;
-    lds_barrier();  // the previous segment's readers are done with the stage
-    if (pending_tb >= 0) finalize(pending_tb);
-    pending_tb = -1;
-    bwd_stage_segment<V, BF16IN>(a, b, nh, row0, t0, nst, nsub * SUB, stage, tid, NTH);
+    if constexpr (!SUBCK) {
+      lds_barrier();  // the previous segment's readers are done with the stage
+      if (pending_tb >= 0) finalize(pending_tb);
+      pending_tb = -1;
+      bwd_stage_segment<V, BF16IN>(a, b, nh, row0, t0, nst, nsub * SUB, stage, tid, NTH);
+    }
 
     // The checkpoint entering sub-segment m of this segment (SUBCK), or the segment's own.
     const long lane_off = (long)(row0 + n) * V + 16 * w + 4 * g;
@@ -463,17 +578,27 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       }
 
       // 1. Recompute the sub-segment: hst[j] = H_{t-1} (split), zst[j] = Z_t.
-      lds_barrier();  // the previous walk is done with hst, zst and the partial sums
+      lds_barrier();  // the previous walk is done with hst, zst, the partial sums (and the stage)
       if (pending_tb >= 0) finalize(pending_tb);
       pending_tb = t0 + jb;
+      // Records of this sub-segment: in the segment's stage, or (sub-segment checkpoints) written
+      // now from the registers prefetched during the previous walk, which then take the records
+      // of the sub-segment before this one in time.
+      const float* sstage = SUBCK ? stage : stage + jb * St::STEP;
+      if constexpr (SUBCK) {
+        sub_regs.store(stage, tid);
+        const int pm = m > 0 ? m : NSUB;                 // previous sub-segment: (seg, m-1) or (seg-1, last)
+        const int pt0 = (m > 0 ? t0 : t0 - kBwdSeg) + (pm - 1) * SUB;
+        if (pt0 >= 0) sub_regs.load(a, b, nh, row0, pt0, min(SUB, a.T - pt0), tid);
+      }
       uint2 hh, hl;
       put_tile(hst, H, hh, hl);
-      f32x4 kv = rank1(stage + jb * St::STEP);  // (the stage is complete: barriers since it was written)
-      lds_barrier();
+      lds_barrier();  // hst, and the stage records written above by every wave, are complete
+      f32x4 kv = rank1(sstage);
 #pragma unroll
       for (int j = 0; j < SUB; ++j) {
         float Z[4];
-        const float* st = stage + (jb + j) * St::STEP;
+        const float* st = sstage + j * St::STEP;
         fwd_step(st, j + 1 < SUB ? st + St::STEP : nullptr, hst + j * ENTRY,
                  j + 1 < SUB ? hst + (j + 1) * ENTRY : nullptr, kv, H, Z, hh, hl);
         *(float4*)(zst + ((j * NT + w) * 64 + lane) * 4) = make_float4(Z[0], Z[1], Z[2], Z[3]);
@@ -500,7 +625,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       };
       auto load_rev = [&](int j) {
         RevIn in;
-        const float* st = stage + (jb + j) * St::STEP;
+        const float* st = sstage + j * St::STEP;
         const uint32_t* hj = hst + j * ENTRY;
         in.f = st[0];
         in.qn = st[St::OQ + n];
@@ -553,7 +678,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
 #pragma unroll
       for (int j = SUB - 1; j >= 0; --j) {
         const int js = jb + j;
-        const float* st = stage + js * St::STEP;
+        const float* st = sstage + j * St::STEP;
         const uint32_t* hj = hst + j * ENTRY;
         const uint32_t* dxp = dx + (j & 1) * ENTRY;
         __builtin_amdgcn_sched_barrier(0);
@@ -613,7 +738,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
           xq[j & 3] = x;
           if ((j & 3) == 0) {
             float dvv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
-            const float ucol = stage[(jb + j + g) * St::STEP + St::OU + 16 * w + n];
+            const float ucol = sstage[(j + g) * St::STEP + St::OU + 16 * w + n];
             dvv = __builtin_fmaf(wr_col, ucol, dvv);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv), dvres,
                                                   dv_lane + (uint32_t)((t0 + js) * ystep * 4), 0, 0);

@@ -141,5 +141,5 @@ def test_block_entry_points_check_their_arguments():
 
 def test_checkpoint_interval():
     # every sub-segment of the backward for V <= 64, every 64-step segment at V = 128
-    assert [m2.m2rnn_checkpoint_interval(m2.Dims(1, 100, 1, 16, V)) for V in (16, 32, 64, 128)] == [16, 16, 8, 64]
-    assert m2.checkpoint_count(4096, 64) == 512 and m2.checkpoint_count(70, 16) == 5
+    assert [m2.m2rnn_checkpoint_interval(m2.Dims(1, 100, 1, 16, V)) for V in (16, 32, 64, 128)] == [8, 8, 8, 64]
+    assert m2.checkpoint_count(4096, 64) == 512 and m2.checkpoint_count(70, 16) == 9
