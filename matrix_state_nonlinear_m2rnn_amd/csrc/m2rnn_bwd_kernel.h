@@ -290,6 +290,9 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   constexpr int NSUB = kBwdSeg / SUB;
   constexpr bool GROUP4 = SUB % 4 == 0;  // dv reduced four steps at a time
   constexpr int ENTRY = NT * 256;        // dwords of one step's split tiles (all waves)
+  // A single wave needs no parity buffers for D (its own LDS accesses complete in order) and
+  // writes dq, dk, df straight from its lanes.
+  constexpr bool ONE = NT == 1;
   using St = BwdStage<V>;
   static_assert(kBwdSeg % SUB == 0 && SUB % 2 == 0, "sub-segments tile a segment");
 
@@ -301,10 +304,11 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   __shared__ __attribute__((aligned(16))) uint32_t hst[SUB * ENTRY];
   // Z_t of the sub-segment's steps: [SUB][NT][64 lanes][4 floats].
   __shared__ __attribute__((aligned(16))) float zst[SUB * NT * 64 * 4];
-  // D_t exchange, by step parity: [2][NT tiles][hi|lo][64 slots][2 dwords].
-  __shared__ __attribute__((aligned(16))) uint32_t dx[2 * ENTRY];
-  // Per-wave partial sums of dq, dk (per row) and df over the sub-segment's steps.
-  __shared__ float red_q[SUB][NT][16], red_k[SUB][NT][16], red_f[SUB][NT];
+  // D_t exchange, by step parity (one buffer for a single wave): [2][NT tiles][hi|lo][64 slots][2 dwords].
+  __shared__ __attribute__((aligned(16))) uint32_t dx[(ONE ? 1 : 2) * ENTRY];
+  // Per-wave partial sums of dq, dk (per row) and df over the sub-segment's steps (several waves).
+  constexpr int RED = ONE ? 1 : SUB;
+  __shared__ float red_q[RED][NT][16], red_k[RED][NT][16], red_f[RED][NT];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -496,6 +500,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
 
   // dq, dk, df of the sub-segment's steps [tb, tb + SUB) from the per-wave partials.
   auto finalize = [&](int tb) {
+    if constexpr (ONE) return;
     for (int i = tid; i < SUB * 16 * 2 + SUB; i += NTH) {
       if (i < SUB * 32) {
         const int which = i / (SUB * 16), j = (i / 16) % SUB, row = i % 16;
@@ -611,7 +616,12 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
         dq_l = __builtin_fmaf(H[2], u4.z, dq_l);
         dq_l = __builtin_fmaf(H[3], u4.w, dq_l);
         dq_l = sum_rows4(dq_l);
-        if (g == 0) red_q[j][w][n] = dq_l;
+        if constexpr (ONE) {
+          const int t = t0 + jb + j;
+          if (g == 0 && t < a.T) a.dq[(((long)b * a.T + t) * a.N + nh) * a.K + row0 + n] = dq_l;
+        } else {
+          if (g == 0) red_q[j][w][n] = dq_l;
+        }
         lds_barrier();
       }
 
@@ -655,7 +665,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
           R[r] = __builtin_fmaf(in.qn, uu[r], C[r]);
           D[r] = (g1 * R[r]) * __builtin_fmaf(-Z[r], Z[r], 1.0f);
         }
-        put_tile(dx + (j & 1) * ENTRY, D, fr.dh, fr.dl);
+        put_tile(dx + (ONE ? 0 : (j & 1) * ENTRY), D, fr.dh, fr.dl);
         __builtin_amdgcn_sched_barrier(0);
         float Hp[4];  // H_{t-1}
         Hp[0] = f16_lo_to_f32(in.h_hi.x) + f16_lo_to_f32(in.h_lo.x);
@@ -680,7 +690,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
         const int js = jb + j;
         const float* st = sstage + j * St::STEP;
         const uint32_t* hj = hst + j * ENTRY;
-        const uint32_t* dxp = dx + (j & 1) * ENTRY;
+        const uint32_t* dxp = dx + (ONE ? 0 : (j & 1) * ENTRY);
         __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
 
@@ -717,7 +727,12 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
         df_l += dpp<kDppRowHalfMirror>(df_l);
         df_l += dpp<kDppQuadXor1>(df_l);
         df_l += dpp<kDppQuadXor2>(df_l);
-        if (g == 0) {
+        if constexpr (ONE) {
+          if (g == 0 && t0 + js < a.T) {
+            a.dk[(((long)b * a.T + t0 + js) * a.N + nh) * a.K + row0 + n] = dk_l;
+            if (n == 0) df_dst[((long)b * a.T + t0 + js) * a.N + nh] = df_l;
+          }
+        } else if (g == 0) {
           red_k[j][w][n] = dk_l;
           if (n == 0) red_f[j][w] = df_l;
         }
