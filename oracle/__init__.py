@@ -49,7 +49,7 @@ def _load():
         i64, dp, ci = ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.c_int
         lib.m2rnn_ref_fwd.argtypes = [i64] * 5 + [dp] * 9 + [ci]
         lib.m2rnn_ref_fwd.restype = ci
-        lib.m2rnn_ref_bwd.argtypes = [i64] * 5 + [dp] * 16 + [ci]
+        lib.m2rnn_ref_bwd.argtypes = [i64] * 5 + [dp] * 9 + [ctypes.c_double] + [dp] * 7 + [ci]
         lib.m2rnn_ref_bwd.restype = ci
         _lib = lib
     return _lib
@@ -94,8 +94,14 @@ def ref_fwd(q, k, v, f, W, w_r, H0=None, nthreads: int = 0) -> Tuple[np.ndarray,
     return y, H_T
 
 
-def ref_bwd(q, k, v, f, W, w_r, H0, dy, dH_T=None, nthreads: int = 0) -> Dict[str, np.ndarray]:
-    """BPTT in fp64 for L = sum <dy, y> + <dH_T, H_T>: returns dq, dk, dv, df, dW, dw_r, dH0."""
+def ref_bwd(q, k, v, f, W, w_r, H0, dy, dH_T=None, nthreads: int = 0, clip: float = 0.0) -> Dict[str, np.ndarray]:
+    """BPTT in fp64 for L = sum <dy, y> + <dH_T, H_T>: returns dq, dk, dv, df, dW, dw_r, dH0.
+
+    clip > 0 clamps every element of the gradient each step sends back to its input state,
+    C_{t-1} = f_t R_t + D_t W^T, to [-clip, clip] (the per-step recurrent-gradient clipping of the
+    M²RNN notes §2.3, read as an elementwise bound); clip = 0 gives the exact gradient."""
+    if not clip >= 0.0:
+        raise ValueError("clip must be >= 0")
     q, k, v, f, W, w_r, H0, dy, dH_T = map(_d, (q, k, v, f, W, w_r, H0, dy, dH_T))
     B, T, N, K, V = _dims(q, v)
     _check(q, k, v, f, W, w_r, H0, B, T, N, K, V)
@@ -109,7 +115,7 @@ def ref_bwd(q, k, v, f, W, w_r, H0, dy, dH_T=None, nthreads: int = 0) -> Dict[st
         "dH0": np.empty((B, N, K, V)),
     }
     rc = _load().m2rnn_ref_bwd(B, T, N, K, V, _p(q), _p(k), _p(v), _p(f), _p(W), _p(w_r), _p(H0), _p(dy),
-                               _p(dH_T), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["df"]),
+                               _p(dH_T), float(clip), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["df"]),
                                _p(out["dW"]), _p(out["dw_r"]), _p(out["dH0"]), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"m2rnn_ref_bwd failed with status {rc}")

@@ -34,6 +34,7 @@ typedef struct {
   const double *q, *k, *v, *f, *W, *w_r, *H0, *dy, *dH_T;
   double *y, *H_T;
   double *dq, *dk, *dv, *df, *dW_unit, *dw_r_unit, *dH0;
+  double clip; /* > 0: bound on every element of the gradient a step sends back to its input state */
   int64_t unit0, ustride;
   int status;
 } job_t;
@@ -154,12 +155,16 @@ static void* bwd_worker(void* arg) {
           for (int64_t i = 0; i < K; ++i) s += Hprev[i * V + l] * D[i * V + j];
           dWu[l * V + j] += s;
         }
-      /* C_{t-1} = f_t R_t + D_t W^T. */
+      /* C_{t-1} = f_t R_t + D_t W^T, the gradient step t sends back to H_{t-1}; with clipping
+         (the notes' §2.3: the recurrent-state gradient is clipped at every BPTT step), each element
+         is clamped to [-clip, clip] before it is used. */
       for (int64_t i = 0; i < K; ++i)
         for (int64_t l = 0; l < V; ++l) {
           double s = 0.0;
           for (int64_t j = 0; j < V; ++j) s += D[i * V + j] * W[l * V + j];
-          C[i * V + l] = ft * R[i * V + l] + s;
+          double c = ft * R[i * V + l] + s;
+          if (J->clip > 0.0) c = c > J->clip ? J->clip : (c < -J->clip ? -J->clip : c);
+          C[i * V + l] = c;
         }
     }
     if (J->dH0)
@@ -214,8 +219,8 @@ int m2rnn_ref_fwd(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V, const d
  * (zeros); dH0 may be NULL.  dW [N,V,V] and dw_r [N,V] are summed over batch (b ascending). */
 int m2rnn_ref_bwd(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V, const double* q, const double* k,
                   const double* v, const double* f, const double* W, const double* w_r, const double* H0,
-                  const double* dy, const double* dH_T, double* dq, double* dk, double* dv, double* df,
-                  double* dW, double* dw_r, double* dH0, int nthreads) {
+                  const double* dy, const double* dH_T, double clip, double* dq, double* dk, double* dv,
+                  double* df, double* dW, double* dw_r, double* dH0, int nthreads) {
   if (B < 0 || T < 0 || N < 0 || K <= 0 || V <= 0) return -2;
   double* dWu = (double*)calloc((size_t)(B * N * V * V) + 1, sizeof(double));
   double* dwru = (double*)calloc((size_t)(B * N * V) + 1, sizeof(double));
@@ -224,6 +229,7 @@ int m2rnn_ref_bwd(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V, const d
   memset(&J, 0, sizeof(J));
   J.B = B; J.T = T; J.N = N; J.K = K; J.V = V;
   J.q = q; J.k = k; J.v = v; J.f = f; J.W = W; J.w_r = w_r; J.H0 = H0; J.dy = dy; J.dH_T = dH_T;
+  J.clip = clip;
   J.dq = dq; J.dk = dk; J.dv = dv; J.df = df; J.dW_unit = dWu; J.dw_r_unit = dwru; J.dH0 = dH0;
   int rc = run_jobs(&J, nthreads, bwd_worker);
   for (int64_t n = 0; n < N; ++n) {

@@ -107,3 +107,69 @@ def test_shared_query_key_gradient_is_the_sum_over_heads():
         summed = g[gx].sum(axis=2, keepdims=True)
         err = np.max(np.abs(num.reshape(summed.shape) - summed)) / max(1e-3, np.max(np.abs(num)))
         assert err < 1e-6, (x, err)
+
+
+def _autograd_clipped(d, dy, dHT, clip):
+    """The same loss through torch autograd (fp64, CPU): the state entering each step passes an
+    identity whose backward clamps its gradient elementwise to [-clip, clip], so what a step sends
+    back to H_{t-1} is clamped while the readout of H_{t-1} and dH_T reach it unclamped.  Returns
+    the gradients and the fraction of clamped elements."""
+    import torch
+    seen = {"n": 0, "clamped": 0}
+
+    class ClampGrad(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x):
+            return x.view_as(x)
+
+        @staticmethod
+        def backward(ctx, g):
+            seen["n"] += g.numel()
+            seen["clamped"] += int((g.abs() > clip).sum())
+            return g.clamp(-clip, clip)
+
+    t = {x: torch.tensor(a, dtype=torch.float64, requires_grad=True) for x, a in d.items()}
+    q, k, v, f, W, w_r, H = t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], t["H0"]
+    T = q.shape[1]
+    L = torch.zeros((), dtype=torch.float64)
+    for s in range(T):
+        Hin = ClampGrad.apply(H)
+        P = torch.matmul(Hin, W) + k[:, s, :, :, None] * v[:, s, :, None, :]
+        fs = f[:, s, :, None, None]
+        H = fs * Hin + (1 - fs) * torch.tanh(P)
+        y = (H * q[:, s, :, :, None]).sum(dim=2) + w_r * v[:, s]
+        L = L + (y * torch.from_numpy(dy[:, s])).sum()
+    L = L + (H * torch.from_numpy(dHT)).sum()
+    grads = torch.autograd.grad(L, [t[x] for x in ("q", "k", "v", "f", "W", "w_r", "H0")])
+    names = ("dq", "dk", "dv", "df", "dW", "dw_r", "dH0")
+    return {n: g.numpy() for n, g in zip(names, grads)}, seen["clamped"] / max(1, seen["n"])
+
+
+@pytest.mark.parametrize("B,T,N,K,V,clip", [(2, 7, 2, 3, 4, 0.6), (1, 9, 3, 4, 2, 1.5)])
+def test_clipped_gradients_match_autograd_with_a_clamping_identity(B, T, N, K, V, clip):
+    d = inputs.make_inputs(B, T, N, K, V, qkv_dtype="f32", seed=91 + T, with_H0=True, with_dy=True, with_dHT=True)
+    d = {x: (a.astype(np.float64) if a is not None else None) for x, a in d.items()}
+    d["W"] *= 1.5
+    d["k"] *= 3.0
+    dy, dHT = 4.0 * d.pop("dy"), d.pop("dH_T")
+    g = oracle.ref_bwd(d["q"], d["k"], d["v"], d["f"], d["W"], d["w_r"], d["H0"], dy, dHT, clip=clip)
+    ref, frac = _autograd_clipped(d, dy, dHT, clip)
+    assert 0.05 < frac < 0.95, frac  # the bound binds on some elements, not all
+    for n in ref:
+        scale = max(1e-3, float(np.max(np.abs(ref[n]))))
+        assert np.max(np.abs(g[n] - ref[n])) <= 1e-12 * scale, n
+    assert np.max(np.abs(g["dH0"])) <= clip
+    exact = oracle.ref_bwd(d["q"], d["k"], d["v"], d["f"], d["W"], d["w_r"], d["H0"], dy, dHT)
+    assert not np.allclose(exact["dW"], g["dW"])
+
+
+def test_clip_above_every_gradient_is_exact():
+    d = inputs.make_inputs(2, 6, 2, 3, 4, qkv_dtype="f32", seed=5, with_H0=True, with_dy=True, with_dHT=True)
+    d = {x: (a.astype(np.float64) if a is not None else None) for x, a in d.items()}
+    args = (d["q"], d["k"], d["v"], d["f"], d["W"], d["w_r"], d["H0"], d["dy"], d["dH_T"])
+    exact = oracle.ref_bwd(*args)
+    loose = oracle.ref_bwd(*args, clip=1e30)
+    for n in exact:
+        assert np.array_equal(exact[n], loose[n]), n
+    with pytest.raises(ValueError):
+        oracle.ref_bwd(*args, clip=-1.0)
