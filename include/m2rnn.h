@@ -137,6 +137,11 @@ int m2rnn_scan_fwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, int r
  * checkpoints are stored, not every state).
  *
  *   dH_T   upstream gradient of the final state, or NULL for zeros.
+ *   grad_clip  0 for the exact gradient; > 0 clamps every element of the gradient that each step
+ *          sends back to its input state, C_{t-1} = f_t R_t + D_t W^T, to [-grad_clip, grad_clip]
+ *          before it is used (the per-step recurrent-gradient clipping of the notes' §2.3, read as
+ *          an elementwise bound; dH0 is then the clamped C_0).  The readout gradient q_t u_t^T and
+ *          dH_T enter unclamped.  Negative or NaN: M2RNN_EINVAL.
  *   dq, dk [B,T,Nqk,K]; dv [B,T,N,V]; df [B,T,N]; dW [N,V,V] and dw_r [N,V] summed over batch and
  *   time; dH0 [B,N,K,V] or NULL to skip it.  All fp32.
  *   math   M2RNN_MATH_F16X3 or M2RNN_MATH_AUTO (the other modes return M2RNN_EUNSUPPORTED).
@@ -145,8 +150,8 @@ int m2rnn_scan_fwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, int r
 int m2rnn_bwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes);
 int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k,
               const void* v, const float* f, const float* W, const float* w_r, const float* H0,
-              const float* dy, const float* dH_T, float* dq, float* dk, float* dv, float* df,
-              float* dW, float* dw_r, float* dH0, void* workspace, size_t workspace_bytes,
+              const float* dy, const float* dH_T, float grad_clip, float* dq, float* dk, float* dv,
+              float* df, float* dW, float* dw_r, float* dH0, void* workspace, size_t workspace_bytes,
               void* stream);
 
 /*
@@ -176,8 +181,8 @@ int m2rnn_fwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, int row_bloc
 int m2rnn_bwd_ckpt_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes);
 int m2rnn_bwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k,
                    const void* v, const float* f, const float* W, const float* w_r, const float* ckpt,
-                   const float* dy, const float* dH_T, float* dq, float* dk, float* dv, float* df,
-                   float* dW, float* dw_r, float* dH0, void* workspace, size_t workspace_bytes,
+                   const float* dy, const float* dH_T, float grad_clip, float* dq, float* dk, float* dv,
+                   float* df, float* dW, float* dw_r, float* dH0, void* workspace, size_t workspace_bytes,
                    void* stream);
 
 /*

@@ -79,7 +79,8 @@ def lib() -> ctypes.CDLL:
             L.m2rnn_bwd_workspace_size.restype = ci
             L.m2rnn_bwd_workspace_size.argtypes = [dp, ci, ci, ctypes.POINTER(sz)]
             L.m2rnn_bwd.restype = ci
-            L.m2rnn_bwd.argtypes = [dp, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp] + [vp] * 7 + [vp, sz, vp]
+            L.m2rnn_bwd.argtypes = ([dp, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp] + [ctypes.c_float] + [vp] * 7
+                                    + [vp, sz, vp])
         L.m2rnn_checkpoint_interval.restype = ci
         L.m2rnn_checkpoint_interval.argtypes = [dp, ctypes.POINTER(ctypes.c_int64)]
         L.m2rnn_fwd_ckpt.restype = ci
@@ -87,7 +88,8 @@ def lib() -> ctypes.CDLL:
         L.m2rnn_bwd_ckpt_workspace_size.restype = ci
         L.m2rnn_bwd_ckpt_workspace_size.argtypes = [dp, ci, ci, ctypes.POINTER(sz)]
         L.m2rnn_bwd_ckpt.restype = ci
-        L.m2rnn_bwd_ckpt.argtypes = [dp, ci, ci] + [vp] * 3 + [vp] * 3 + [vp] + [vp, vp] + [vp] * 7 + [vp, sz, vp]
+        L.m2rnn_bwd_ckpt.argtypes = ([dp, ci, ci] + [vp] * 3 + [vp] * 3 + [vp] + [vp, vp] + [ctypes.c_float]
+                                     + [vp] * 7 + [vp, sz, vp])
         i64, cf = ctypes.c_int64, ctypes.c_float
         for name, args in (
             ("m2rnn_gate_fwd", [i64] * 3 + [vp] * 4 + [vp]),
@@ -289,8 +291,8 @@ def m2rnn_bwd_ckpt_workspace_size(dims: Dims, qkv_dtype: int, math="auto") -> in
     return int(n.value)
 
 
-def m2rnn_bwd_ckpt(q, k, v, f, W, w_r, ckpt, dy, dH_T=None, *, math="auto", want_dH0: bool = True, workspace=None,
-                   stream=None) -> Dict[str, object]:
+def m2rnn_bwd_ckpt(q, k, v, f, W, w_r, ckpt, dy, dH_T=None, *, math="auto", grad_clip: float = 0.0,
+                   want_dH0: bool = True, workspace=None, stream=None) -> Dict[str, object]:
     """m2rnn_bwd from the checkpoints that m2rnn_fwd_ckpt kept (no forward re-run)."""
     import torch
     dims, dt, m, _, _, _ = _fwd_prepare(q, k, v, f, W, w_r, None, None, None, math, 0, False)
@@ -307,16 +309,18 @@ def m2rnn_bwd_ckpt(q, k, v, f, W, w_r, ckpt, dy, dH_T=None, *, math="auto", want
     ws = _workspace(nbytes, dev, workspace)
     _check("m2rnn_bwd_ckpt", lib().m2rnn_bwd_ckpt(
         ctypes.byref(dims), dt, m, _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(ckpt), _ptr(dy),
-        _ptr(dH_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dW"]),
+        _ptr(dH_T), float(grad_clip), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dW"]),
         _ptr(out["dw_r"]), _ptr(out["dH0"]), _ptr(ws), nbytes, _stream(stream)))
     return out
 
 
-def m2rnn_bwd(q, k, v, f, W, w_r, H0, dy, dH_T=None, *, math="auto", want_dH0: bool = True, workspace=None,
-              stream=None) -> Dict[str, object]:
+def m2rnn_bwd(q, k, v, f, W, w_r, H0, dy, dH_T=None, *, math="auto", grad_clip: float = 0.0, want_dH0: bool = True,
+              workspace=None, stream=None) -> Dict[str, object]:
     """BPTT (M²RNN notes §2.7) for L = sum <dy, y> + <dH_T, H_T>; returns dq, dk, dv, df, dW, dw_r, dH0.
 
-    dq, dk have q's shape [B,T,Nqk,K]: with a shared query/key (Nqk = 1) they are summed over heads."""
+    dq, dk have q's shape [B,T,Nqk,K]: with a shared query/key (Nqk = 1) they are summed over heads.
+    grad_clip > 0 clamps, at every step, each element of the gradient sent back to the step's input
+    state to [-grad_clip, grad_clip] (§2.3's per-step clipping); 0 gives the exact gradient."""
     import torch
     dims, dt, m, _, _, _ = _fwd_prepare(q, k, v, f, W, w_r, H0, None, None, math, 0, False)
     B, T, N, K, V, Nqk = dims.B, dims.T, dims.N, dims.K, dims.V, dims.Nqk
@@ -331,7 +335,7 @@ def m2rnn_bwd(q, k, v, f, W, w_r, H0, dy, dH_T=None, *, math="auto", want_dH0: b
     ws = _workspace(nbytes, dev, workspace)
     _check("m2rnn_bwd", lib().m2rnn_bwd(
         ctypes.byref(dims), dt, m, _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(dy),
-        _ptr(dH_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dW"]),
+        _ptr(dH_T), float(grad_clip), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dW"]),
         _ptr(out["dw_r"]), _ptr(out["dH0"]), _ptr(ws), nbytes, _stream(stream)))
     return out
 

@@ -420,10 +420,11 @@ namespace {
 // null (then the checkpoints are computed here, into the workspace).
 int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k, const void* v,
              const float* f, const float* W, const float* w_r, const float* H0, const float* ckpt_in,
-             const float* dy, const float* dH_T, float* dq, float* dk, float* dv, float* df, float* dW, float* dw_r,
-             float* dH0, void* workspace, size_t workspace_bytes, void* stream_) {
+             const float* dy, const float* dH_T, float grad_clip, float* dq, float* dk, float* dv, float* df,
+             float* dW, float* dw_r, float* dH0, void* workspace, size_t workspace_bytes, void* stream_) {
   int st = check_dims(dims, qkv_dtype);
   if (st) return st;
+  if (!(grad_clip >= 0.0f)) return M2RNN_EINVAL;  // negative or NaN
   const int m = resolve_bwd_math(math);
   if (m == -1) return M2RNN_EINVAL;
   if (m == -2) return M2RNN_EUNSUPPORTED;
@@ -482,6 +483,7 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
     a.dH0 = dH0;
     a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S;
     a.Nqk = qk_heads(d);
+    a.clip = grad_clip;
     const void* kern = bwd_kernel((int)V, bf16);
     if (!kern) return M2RNN_EUNSUPPORTED;
     void* args[] = {&a};
@@ -517,10 +519,10 @@ extern "C" {
 
 int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k, const void* v,
               const float* f, const float* W, const float* w_r, const float* H0, const float* dy,
-              const float* dH_T, float* dq, float* dk, float* dv, float* df, float* dW, float* dw_r, float* dH0,
-              void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(dims, qkv_dtype, math, q, k, v, f, W, w_r, H0, nullptr, dy, dH_T, dq, dk, dv, df, dW, dw_r, dH0,
-                  workspace, workspace_bytes, stream);
+              const float* dH_T, float grad_clip, float* dq, float* dk, float* dv, float* df, float* dW,
+              float* dw_r, float* dH0, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(dims, qkv_dtype, math, q, k, v, f, W, w_r, H0, nullptr, dy, dH_T, grad_clip, dq, dk, dv, df, dW,
+                  dw_r, dH0, workspace, workspace_bytes, stream);
 }
 
 int m2rnn_checkpoint_interval(const m2rnn_dims* dims, int64_t* steps) {
@@ -544,11 +546,11 @@ int m2rnn_bwd_ckpt_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int mat
 
 int m2rnn_bwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k, const void* v,
                    const float* f, const float* W, const float* w_r, const float* ckpt, const float* dy,
-                   const float* dH_T, float* dq, float* dk, float* dv, float* df, float* dW, float* dw_r, float* dH0,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+                   const float* dH_T, float grad_clip, float* dq, float* dk, float* dv, float* df, float* dW,
+                   float* dw_r, float* dH0, void* workspace, size_t workspace_bytes, void* stream) {
   if (dims && dims->T > 0 && dims->B > 0 && dims->N > 0 && !ckpt) return M2RNN_EINVAL;
-  return bwd_impl(dims, qkv_dtype, math, q, k, v, f, W, w_r, nullptr, ckpt, dy, dH_T, dq, dk, dv, df, dW, dw_r,
-                  dH0, workspace, workspace_bytes, stream);
+  return bwd_impl(dims, qkv_dtype, math, q, k, v, f, W, w_r, nullptr, ckpt, dy, dH_T, grad_clip, dq, dk, dv, df, dW,
+                  dw_r, dH0, workspace, workspace_bytes, stream);
 }
 
 int m2rnn_fwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q, const void* k,

@@ -48,6 +48,7 @@ struct BwdArgs {
   int B, T, N, K;
   int Nqk;             // heads of q and k: N, or 1 when one query/key is shared by all heads
   int S;
+  float clip;          // > 0: the gradient each step sends back to its input state is clamped to [-clip, clip]
 };
 
 // Per-step stage record of the backward (fp32):
@@ -469,6 +470,9 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
 
   // State of the chain.
   float C[4];
+  // Bounds of the chain state (infinite without clipping: the clamp is then the identity).
+  const float clip_hi = a.clip > 0.0f ? a.clip : __builtin_inff();
+  const float clip_lo = -clip_hi;
   const long own_off = ((long)b * a.N + nh) * KV + (long)(row0 + n) * V + 16 * w + 4 * g;
   if (a.dH_T) {
     const float4 c4 = *(const float4*)(a.dH_T + own_off);
@@ -738,8 +742,11 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
         }
 
         // Step j-1's R, D and publish as soon as the chain has produced C.
+        // (the padding steps of a ragged tail must leave the chain unchanged: no clamp there)
+        const bool real = t0 + js < a.T;
+        const float lo = real ? clip_lo : -__builtin_inff(), hi = real ? clip_hi : __builtin_inff();
 #pragma unroll
-        for (int r = 0; r < 4; ++r) C[r] = acc[r];
+        for (int r = 0; r < 4; ++r) C[r] = __builtin_amdgcn_fmed3f(acc[r], lo, hi);
         if (j > 0) fr = front(j - 1, nxt);
 
         // dv[col 16w + i] = sum_rows D[row][col] k[row] (+ w_r u when this workgroup holds all rows).

@@ -80,20 +80,21 @@ def max_abs(a, b):
     return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64)))) if np.size(a) else 0.0
 
 
-def gpu_bwd(dd, math="auto", dH_T=None, want_dH0=True):
+def gpu_bwd(dd, math="auto", dH_T=None, want_dH0=True, grad_clip=0.0):
     torch = torch_cuda()
     import matrix_state_nonlinear_m2rnn_amd as m2
     g = m2.m2rnn_bwd(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], dd.get("H0"), dd["dy"],
-                     dH_T if dH_T is not None else dd.get("dH_T"), math=math, want_dH0=want_dH0)
+                     dH_T if dH_T is not None else dd.get("dH_T"), math=math, want_dH0=want_dH0, grad_clip=grad_clip)
     torch.cuda.synchronize()
     return {name: (t.cpu().numpy().astype(np.float64) if t is not None else None) for name, t in g.items()}
 
 
-def oracle_bwd(d):
+def oracle_bwd(d, clip=0.0):
     """Oracle gradients; with a shared query/key, dq and dk are summed over the heads (§2.7)."""
     shared = d["q"].shape[2] != d["v"].shape[2]
     e = per_head_qk(d)
-    g = oracle.ref_bwd(e["q"], e["k"], e["v"], e["f"], e["W"], e["w_r"], e.get("H0"), e["dy"], e.get("dH_T"))
+    g = oracle.ref_bwd(e["q"], e["k"], e["v"], e["f"], e["W"], e["w_r"], e.get("H0"), e["dy"], e.get("dH_T"),
+                       clip=clip)
     if shared:
         g["dq"] = g["dq"].sum(axis=2, keepdims=True)
         g["dk"] = g["dk"].sum(axis=2, keepdims=True)

@@ -112,8 +112,14 @@ def test_checkpoint_entry_points_check_their_arguments():
     assert L.m2rnn_fwd_ckpt(ctypes.byref(dims), 0, -1, 0, p, p, p, p, p, p, None, p, None, None, None, 0,
                             None) == m2.M2RNN_EINVAL
     # backward from checkpoints: likewise
-    assert L.m2rnn_bwd_ckpt(ctypes.byref(dims), 0, -1, p, p, p, p, p, p, None, p, None, p, p, p, p, p, p, None,
+    assert L.m2rnn_bwd_ckpt(ctypes.byref(dims), 0, -1, p, p, p, p, p, p, None, p, None, 0.0, p, p, p, p, p, p, None,
                             p, 1 << 30, None) == m2.M2RNN_EINVAL
+    # the gradient clip must be >= 0 (0 = exact gradient); NaN is rejected too
+    for bad in (-1.0, float("nan")):
+        assert L.m2rnn_bwd(ctypes.byref(dims), 0, -1, p, p, p, p, p, p, None, p, None, bad, p, p, p, p, p, p, None,
+                           p, 1 << 30, None) == m2.M2RNN_EINVAL
+        assert L.m2rnn_bwd_ckpt(ctypes.byref(dims), 0, -1, p, p, p, p, p, p, p, p, None, bad, p, p, p, p, p, p,
+                                None, p, 1 << 30, None) == m2.M2RNN_EINVAL
     # its workspace excludes the checkpoints
     big = m2.Dims(4, 4096, 16, 64, 64)
     assert m2.m2rnn_bwd_ckpt_workspace_size(big, 0) + 4 * 16 * 64 * 64 * 64 * 4 <= m2.m2rnn_bwd_workspace_size(big, 0)

@@ -79,3 +79,23 @@ def test_deterministic():
     b = gpu_bwd(dd)
     for n in GRADS:
         assert np.array_equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("B,T,N,K,V,dtype,clip", [
+    (1, 70, 2, 16, 16, "f32", 0.3),
+    (2, 130, 2, 32, 64, "bf16", 0.6),
+    (1, 65, 1, 16, 128, "bf16", 0.3),
+])
+def test_clipped_recurrent_gradient(B, T, N, K, V, dtype, clip):
+    # Per-step clipping of the gradient sent back to each step's input state (elementwise bound);
+    # the clamp is 1-Lipschitz, so the kernel's rounding cannot grow through it.
+    torch_cuda()
+    d = inputs.make_inputs(B, T, N, K, V, qkv_dtype=dtype, seed=700 + T + V, with_H0=True, with_dy=True,
+                           with_dHT=True)
+    say("bwd clip", B, T, N, K, V, dtype, clip)
+    ref = oracle_bwd(d, clip=clip)
+    exact = oracle_bwd(d)
+    assert rel_l2(ref["dW"], exact["dW"]) > 10 * TOL  # the bound changes the result
+    got = gpu_bwd(to_device(d, dtype), grad_clip=clip)
+    check(got, ref)
+    assert np.max(np.abs(got["dH0"])) <= np.float32(clip)  # the bound as the kernel holds it

@@ -71,6 +71,28 @@ def test_backward_from_checkpoints(B, T, N, K, V, dtype, shared):
         assert e <= 1e-3, (n, e)
 
 
+def test_clipped_backward_from_checkpoints():
+    # The clipping option reaches the checkpoint form of the backward too.
+    torch = torch_cuda()
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    d = inputs.make_inputs(1, 70, 4, 64, 16, qkv_dtype="bf16", seed=870, with_H0=True, with_dy=True, with_dHT=True,
+                           shared_qk=True)
+    dd = to_device(d, "bf16")
+    _, _, ck = fwd_ckpt(dd, "f16x3")
+    g = m2.m2rnn_bwd_ckpt(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], ck, dd["dy"], dd["dH_T"],
+                          grad_clip=0.4)
+    g0 = m2.m2rnn_bwd(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], dd["H0"], dd["dy"], dd["dH_T"],
+                      grad_clip=0.4)
+    torch.cuda.synchronize()
+    for n in GRADS:
+        assert torch.equal(g[n], g0[n]), n
+    ref = oracle_bwd(d, clip=0.4)
+    errs = {n: rel_l2(g[n].cpu().numpy(), ref[n]) for n in GRADS}
+    say("rel-L2", errs)
+    for n, e in errs.items():
+        assert e <= 1e-3, (n, e)
+
+
 def test_backward_from_fp32_contraction_checkpoints():
     # Checkpoints from another contraction mode differ within that mode's error; the gradients
     # still meet the budget.
