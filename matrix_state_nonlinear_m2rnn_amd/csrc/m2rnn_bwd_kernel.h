@@ -289,7 +289,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   constexpr int NOTH = NCH > 1 ? NCH - 1 : 1;
   constexpr int SUB = BwdSub<V>::value;
   constexpr int NSUB = kBwdSeg / SUB;
-  constexpr bool GROUP4 = SUB % 4 == 0;  // dv reduced four steps at a time
+  constexpr bool GROUP4 = SUB % 4 == 0;  // dq, dk, df, dv reduced four steps at a time
   constexpr int ENTRY = NT * 256;        // dwords of one step's split tiles (all waves)
   // A single wave needs no parity buffers for D (its own LDS accesses complete in order) and
   // writes dq, dk, df straight from its lanes.
@@ -307,9 +307,10 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   __shared__ __attribute__((aligned(16))) float zst[SUB * NT * 64 * 4];
   // D_t exchange, by step parity (one buffer for a single wave): [2][NT tiles][hi|lo][64 slots][2 dwords].
   __shared__ __attribute__((aligned(16))) uint32_t dx[(ONE ? 1 : 2) * ENTRY];
-  // Per-wave partial sums of dq, dk (per row) and df over the sub-segment's steps (several waves).
+  // Per-wave partial sums of dq, dk (per row) and df over the sub-segment's steps (several waves;
+  // red_f holds 16 equal copies, one per lane of a row, so that every lane stores).
   constexpr int RED = ONE ? 1 : SUB;
-  __shared__ float red_q[RED][NT][16], red_k[RED][NT][16], red_f[RED][NT];
+  __shared__ float red_q[RED][NT][16], red_k[RED][NT][16], red_f[RED][NT][16];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -498,6 +499,17 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   const uint32_t dv_lane = (uint32_t)(((GROUP4 ? g * ystep : 0) + 16 * w + n) * 4);
   const float wr_col = a.S == 1 ? a.w_r[(long)nh * V + 16 * w + n] : 0.0f;  // for dv's w_r (.) u term
   float* df_dst = a.df + (a.S > 1 ? (long)s * a.B * a.T * a.N : 0);
+  // A one-wave workgroup stores dq, dk and df from its lanes, likewise through resources that end
+  // at the last valid step of this (b, n).  Byte offsets of step 0 (grouped: step g), row row0 + n.
+  const __amdgpu_buffer_rsrc_t dqres = __builtin_amdgcn_make_buffer_rsrc(
+      a.dq + ((long)b * a.T * a.N + nh) * a.K, (short)0, (a.T * a.N - nh) * a.K * 4, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t dkres = __builtin_amdgcn_make_buffer_rsrc(
+      a.dk + ((long)b * a.T * a.N + nh) * a.K, (short)0, (a.T * a.N - nh) * a.K * 4, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t dfres = __builtin_amdgcn_make_buffer_rsrc(
+      df_dst + (long)b * a.T * a.N + nh, (short)0, (a.T * a.N - nh) * 4, kBufferRsrcWord3);
+  const int qkstep = a.N * a.K;
+  const uint32_t qk_lane = (uint32_t)(((GROUP4 ? g * qkstep : 0) + row0 + n) * 4);
+  const uint32_t df_lane = (GROUP4 ? n == 0 : g == 0 && n == 0) ? (uint32_t)((GROUP4 ? g * a.N : 0) * 4) : kBufferDrop;
   // dw_r[16w + 4g + r] partial over this batch entry (every lane of a row group holds the same sums;
   // the workgroups with s == 0 write them).
   float dwr4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -518,13 +530,15 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
         const int t = tb + j;
         float acc = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < NT; ++ww) acc += red_f[j][ww];
+        for (int ww = 0; ww < NT; ++ww) acc += red_f[j][ww][0];
         if (t < a.T) df_dst[((long)b * a.T + t) * a.N + nh] = acc;
       }
     }
   };
 
-  float xq[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // dv partials of the current group of four steps
+  // Lane partials of the current group of four steps: dv, dk, df (walk) and dq (recompute).
+  float xq[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xk[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float xh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   int pending_tb = -1;                     // sub-segment whose dq, dk, df await finalize
 
   // Sub-segment checkpoints: the stage records of the next sub-segment to walk, in registers.
@@ -619,12 +633,27 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
         dq_l = __builtin_fmaf(H[1], u4.y, dq_l);
         dq_l = __builtin_fmaf(H[2], u4.z, dq_l);
         dq_l = __builtin_fmaf(H[3], u4.w, dq_l);
-        dq_l = sum_rows4(dq_l);
-        if constexpr (ONE) {
-          const int t = t0 + jb + j;
-          if (g == 0 && t < a.T) a.dq[(((long)b * a.T + t) * a.N + nh) * a.K + row0 + n] = dq_l;
+        if constexpr (GROUP4) {
+          // Steps j0 .. j0+3 (j0 = j & ~3) are reduced together: lane (g, n) ends with step j0 + g.
+          xh[j & 3] = dq_l;
+          if ((j & 3) == 3) {
+            const float dq4 = reduce_rows4(xh[0], xh[1], xh[2], xh[3]);
+            if constexpr (ONE) {
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq4), dqres,
+                                                    qk_lane + (uint32_t)((t0 + jb + j - 3) * qkstep * 4), 0, 0);
+            } else {
+              red_q[j - 3 + g][w][n] = dq4;
+            }
+          }
         } else {
-          if (g == 0) red_q[j][w][n] = dq_l;
+          dq_l = sum_rows4(dq_l);
+          if constexpr (ONE) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq_l), dqres,
+                                                  g == 0 ? qk_lane + (uint32_t)((t0 + jb + j) * qkstep * 4) : kBufferDrop,
+                                                  0, 0);
+          } else if (g == 0) {
+            red_q[j][w][n] = dq_l;
+          }
         }
         lds_barrier();
       }
@@ -725,20 +754,38 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
 
         // Off the chain, while the MFMAs run.  dk, df: sums over this wave's 16 columns (the four
         // lane rows); df also over the 16 rows.
-        float dk_l = sum_rows4(fr.dk_l);
-        float df_l = sum_rows4(fr.df_l);
-        df_l += dpp<kDppRowMirror>(df_l);
-        df_l += dpp<kDppRowHalfMirror>(df_l);
-        df_l += dpp<kDppQuadXor1>(df_l);
-        df_l += dpp<kDppQuadXor2>(df_l);
-        if constexpr (ONE) {
-          if (g == 0 && t0 + js < a.T) {
-            a.dk[(((long)b * a.T + t0 + js) * a.N + nh) * a.K + row0 + n] = dk_l;
-            if (n == 0) df_dst[((long)b * a.T + t0 + js) * a.N + nh] = df_l;
+        // Grouped: steps j .. j+3 (j % 4 == 0) reduced together, lane (g, n) ending with step j + g.
+        if (!GROUP4 || (j & 3) == 0) {
+          float dk_l, df_l;
+          if constexpr (GROUP4) {
+            xk[j & 3] = fr.dk_l;
+            xf[j & 3] = fr.df_l;
+            dk_l = reduce_rows4(xk[0], xk[1], xk[2], xk[3]);
+            df_l = reduce_rows4(xf[0], xf[1], xf[2], xf[3]);
+          } else {
+            dk_l = sum_rows4(fr.dk_l);
+            df_l = sum_rows4(fr.df_l);
           }
-        } else if (g == 0) {
-          red_k[j][w][n] = dk_l;
-          if (n == 0) red_f[j][w] = df_l;
+          df_l += dpp<kDppRowMirror>(df_l);
+          df_l += dpp<kDppRowHalfMirror>(df_l);
+          df_l += dpp<kDppQuadXor1>(df_l);
+          df_l += dpp<kDppQuadXor2>(df_l);
+          if constexpr (ONE) {
+            const uint32_t tstep = (uint32_t)(t0 + js);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dk_l), dkres,
+                                                  GROUP4 || g == 0 ? qk_lane + tstep * qkstep * 4 : kBufferDrop, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(df_l), dfres,
+                                                  df_lane == kBufferDrop ? kBufferDrop : df_lane + tstep * a.N * 4, 0, 0);
+          } else if constexpr (GROUP4) {
+            red_k[j + g][w][n] = dk_l;
+            red_f[j + g][w][n] = df_l;
+          } else if (g == 0) {
+            red_k[j][w][n] = dk_l;
+            red_f[j][w][n] = df_l;
+          }
+        } else {
+          xk[j & 3] = fr.dk_l;
+          xf[j & 3] = fr.df_l;
         }
 
         // Step j-1's R, D and publish as soon as the chain has produced C.
