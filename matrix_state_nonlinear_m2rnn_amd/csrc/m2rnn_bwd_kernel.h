@@ -161,48 +161,63 @@ __device__ __forceinline__ void bwd_stage_segment(const BwdArgs& a, int b, int n
 
 // One sub-segment's stage records (SUB steps of one 16-row block), loaded into registers ahead of
 // use and written to LDS later, so that their HBM latency overlaps the walk of the sub-segment
-// after them in time.  Steps past T get f = 1 and zero q, k, v, u.
+// after them in time.  The loads go through buffer resources that end at the last step of the
+// (b, n) pair: steps past T read zeros (and get f = 1), with no branch around any load.
 template <int V, bool BF16IN, int SUB, int NTH>
 struct BwdSubRegs {
   static constexpr int VEC = BF16IN ? 8 : 4;
   static constexpr int QV = 16 / VEC;          // loads per step of q (and of k)
-  static constexpr int NQK = 2 * SUB * QV;
+  static constexpr int NQ = SUB * QV;
   static constexpr int NVV = SUB * (V / VEC);
   static constexpr int NU = SUB * (V / 4);
-  static constexpr int PQK = (NQK + NTH - 1) / NTH, PVV = (NVV + NTH - 1) / NTH, PU = (NU + NTH - 1) / NTH;
-  uint4 qk[PQK], vv[PVV];
+  static constexpr int PQ = (NQ + NTH - 1) / NTH, PVV = (NVV + NTH - 1) / NTH, PU = (NU + NTH - 1) / NTH;
+  uint4 q[PQ], k[PQ], vv[PVV];
   float4 uu[PU];
   float f;
 
+  static __device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(x[0], x[1], x[2], x[3]);
+  }
+
   __device__ __forceinline__ void load(const BwdArgs& a, int b, int nh, int row0, int t0, int n_steps, int tid) {
     const int esz = BF16IN ? 2 : 4;
+    const int nq = a.Nqk == 1 ? 0 : nh;
+    const long bt = (long)b * a.T;
+    const __amdgpu_buffer_rsrc_t qres = __builtin_amdgcn_make_buffer_rsrc(
+        (char*)a.q + (bt * a.Nqk + nq) * a.K * esz, (short)0, (a.T * a.Nqk - nq) * a.K * esz, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+        (char*)a.k + (bt * a.Nqk + nq) * a.K * esz, (short)0, (a.T * a.Nqk - nq) * a.K * esz, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
+        (char*)a.v + (bt * a.N + nh) * V * esz, (short)0, (a.T * a.N - nh) * V * esz, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ures = __builtin_amdgcn_make_buffer_rsrc(
+        (float*)a.dy + (bt * a.N + nh) * V, (short)0, (a.T * a.N - nh) * V * 4, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t fres = __builtin_amdgcn_make_buffer_rsrc(
+        (float*)a.f + bt * a.N + nh, (short)0, (a.T * a.N - nh) * 4, kBufferRsrcWord3);
 #pragma unroll
-    for (int p = 0; p < PQK; ++p) {
+    for (int p = 0; p < PQ; ++p) {
       const int i = tid + p * NTH;
-      const int which = i / (SUB * QV), r = i % (SUB * QV), step = r / QV, cv = r % QV;
-      qk[p] = make_uint4(0, 0, 0, 0);
-      if (i < NQK && step < n_steps) {
-        const long off = (((long)b * a.T + t0 + step) * a.Nqk + (a.Nqk == 1 ? 0 : nh)) * a.K + row0 + cv * VEC;
-        qk[p] = *(const uint4*)((const char*)(which == 0 ? a.q : a.k) + off * esz);
-      }
+      const int step = i / QV, cv = i % QV;
+      const uint32_t off = i < NQ ? (uint32_t)(((t0 + step) * a.Nqk * a.K + row0 + cv * VEC) * esz) : kBufferDrop;
+      q[p] = ld128(qres, off);
+      k[p] = ld128(kres, off);
     }
 #pragma unroll
     for (int p = 0; p < PVV; ++p) {
       const int i = tid + p * NTH;
       const int step = i / (V / VEC), cv = i % (V / VEC);
-      vv[p] = make_uint4(0, 0, 0, 0);
-      if (i < NVV && step < n_steps)
-        vv[p] = *(const uint4*)((const char*)a.v + ((((long)b * a.T + t0 + step) * a.N + nh) * V + cv * VEC) * esz);
+      vv[p] = ld128(vres, i < NVV ? (uint32_t)(((t0 + step) * a.N * V + cv * VEC) * esz) : kBufferDrop);
     }
 #pragma unroll
     for (int p = 0; p < PU; ++p) {
       const int i = tid + p * NTH;
       const int step = i / (V / 4), cv = i % (V / 4);
-      uu[p] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (i < NU && step < n_steps) uu[p] = *(const float4*)(a.dy + (((long)b * a.T + t0 + step) * a.N + nh) * V + cv * 4);
+      const uint4 x = ld128(ures, i < NU ? (uint32_t)(((t0 + step) * a.N * V + cv * 4) * 4) : kBufferDrop);
+      uu[p] = make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
     }
-    f = 1.0f;
-    if (tid < n_steps && tid < SUB) f = a.f[((long)b * a.T + t0 + tid) * a.N + nh];
+    const float fl = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(fres, tid < SUB ? (uint32_t)((t0 + tid) * a.N * 4) : kBufferDrop, 0, 0));
+    f = tid < n_steps ? fl : 1.0f;
   }
 
   __device__ __forceinline__ void store(float* stage, int tid) const {
@@ -221,21 +236,19 @@ struct BwdSubRegs {
       }
     };
 #pragma unroll
-    for (int p = 0; p < PQK; ++p) {
+    for (int p = 0; p < PQ; ++p) {
       const int i = tid + p * NTH;
-      if (i < NQK) {
-        const int which = i / (SUB * QV), r = i % (SUB * QV), step = r / QV, cv = r % QV;
-        float x[VEC];
-        widen(qk[p], x);
+      if (i < NQ) {
+        const int step = i / QV, cv = i % QV;
+        float xq[VEC], xk[VEC];
+        widen(q[p], xq);
+        widen(k[p], xk);
         float* d = stage + step * St::STEP;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          if (which == 0) {
-            d[St::OQ + cv * VEC + e] = x[e];
-          } else {
-            d[St::OCK + cv * VEC + e] = kTwoLog2e * x[e];
-            d[St::OK + cv * VEC + e] = x[e];
-          }
+          d[St::OQ + cv * VEC + e] = xq[e];
+          d[St::OCK + cv * VEC + e] = kTwoLog2e * xk[e];
+          d[St::OK + cv * VEC + e] = xk[e];
         }
       }
     }
@@ -543,9 +556,14 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
 
   // Sub-segment checkpoints: the stage records of the next sub-segment to walk, in registers.
   BwdSubRegs<V, BF16IN, SUB, NTH> sub_regs;
+  const long lane_off = (long)(row0 + n) * V + 16 * w + 4 * g;
+  // The state entering the next sub-segment to walk (sub-segment checkpoints: prefetched one
+  // sub-segment ahead; segment checkpoints: from this workgroup's scratch).
+  float4 nextH = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if constexpr (SUBCK) {
     const int tl = ((a.T - 1) / SUB) * SUB;  // the last sub-segment
     sub_regs.load(a, b, nh, row0, tl, min(SUB, a.T - tl), tid);
+    nextH = *(const float4*)(a.ckpt + ((long)u * nck + nck - 1) * KV + lane_off);
   }
 
   for (int seg = nseg - 1; seg >= 0; --seg) {
@@ -559,13 +577,11 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       bwd_stage_segment<V, BF16IN>(a, b, nh, row0, t0, nst, nsub * SUB, stage, tid, NTH);
     }
 
-    // The checkpoint entering sub-segment m of this segment (SUBCK), or the segment's own.
-    const long lane_off = (long)(row0 + n) * V + 16 * w + 4 * g;
-    auto ck_at = [&](int m) { return a.ckpt + ((long)u * nck + (SUBCK ? seg * NSUB + m : seg)) * KV + lane_off; };
-    const float* ck = ck_at(0);
-    float H[4];
-    {
-      const float4 h4 = *(const float4*)(SUBCK ? ck_at(nsub - 1) : ck);
+    // The checkpoint entering this segment (segment checkpoints).
+    const float* ck = a.ckpt + ((long)u * nck + seg) * KV + lane_off;
+    float H[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (!SUBCK) {
+      const float4 h4 = *(const float4*)ck;
       H[0] = h4.x; H[1] = h4.y; H[2] = h4.z; H[3] = h4.w;
     }
 
@@ -589,33 +605,38 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     }
 
     // ---------------- sub-segments, last to first ----------------
-    float4 nextH = make_float4(0.0f, 0.0f, 0.0f, 0.0f);  // prefetched state entering sub-segment m - 1
     for (int m = nsub - 1; m >= 0; --m) {
       const int jb = m * SUB;
-      if (m < nsub - 1) {
-        H[0] = nextH.x; H[1] = nextH.y; H[2] = nextH.z; H[3] = nextH.w;
-      }
-      if (m > 0) {
-        if constexpr (SUBCK) nextH = *(const float4*)ck_at(m - 1);
-        else nextH = *(const float4*)(m - 1 > 0 ? subck + (long)(m - 1) * 16 * V : ck);
+      if constexpr (!SUBCK) {
+        if (m < nsub - 1) {
+          H[0] = nextH.x; H[1] = nextH.y; H[2] = nextH.z; H[3] = nextH.w;
+        }
+        if (m > 0) nextH = *(const float4*)(m - 1 > 0 ? subck + (long)(m - 1) * 16 * V : ck);
       }
 
       // 1. Recompute the sub-segment: hst[j] = H_{t-1} (split), zst[j] = Z_t.
       lds_barrier();  // the previous walk is done with hst, zst, the partial sums (and the stage)
-      if (pending_tb >= 0) finalize(pending_tb);
-      pending_tb = t0 + jb;
       // Records of this sub-segment: in the segment's stage, or (sub-segment checkpoints) written
-      // now from the registers prefetched during the previous walk, which then take the records
-      // of the sub-segment before this one in time.
+      // now from the registers prefetched during the previous walk.
       const float* sstage = SUBCK ? stage : stage + jb * St::STEP;
-      if constexpr (SUBCK) {
-        sub_regs.store(stage, tid);
-        const int pm = m > 0 ? m : NSUB;                 // previous sub-segment: (seg, m-1) or (seg-1, last)
-        const int pt0 = (m > 0 ? t0 : t0 - kBwdSeg) + (pm - 1) * SUB;
-        if (pt0 >= 0) sub_regs.load(a, b, nh, row0, pt0, min(SUB, a.T - pt0), tid);
-      }
       uint2 hh, hl;
-      put_tile(hst, H, hh, hl);
+      if constexpr (SUBCK) {
+        // Everything prefetched for this sub-segment is used before the next prefetch is issued,
+        // so that waiting for it never waits for the new loads.
+        H[0] = nextH.x; H[1] = nextH.y; H[2] = nextH.z; H[3] = nextH.w;
+        sub_regs.store(stage, tid);
+        put_tile(hst, H, hh, hl);
+        if (pending_tb >= 0) finalize(pending_tb);
+        pending_tb = t0 + jb;
+        // Prefetch the sub-segment before this one in time (at the first one: itself again).
+        const int pp = max(seg * NSUB + m - 1, 0);
+        nextH = *(const float4*)(a.ckpt + ((long)u * nck + pp) * KV + lane_off);
+        sub_regs.load(a, b, nh, row0, pp * SUB, min(SUB, a.T - pp * SUB), tid);
+      } else {
+        if (pending_tb >= 0) finalize(pending_tb);
+        pending_tb = t0 + jb;
+        put_tile(hst, H, hh, hl);
+      }
       lds_barrier();  // hst, and the stage records written above by every wave, are complete
       f32x4 kv = rank1(sstage);
 #pragma unroll
