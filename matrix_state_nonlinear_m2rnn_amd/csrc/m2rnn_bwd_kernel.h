@@ -307,17 +307,22 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   // A single wave needs no parity buffers for D (its own LDS accesses complete in order) and
   // writes dq, dk, df straight from its lanes.
   constexpr bool ONE = NT == 1;
+  // Interleaved walk (V = 64): sub-segment p is walked while sub-segment p - 1 is recomputed into
+  // a second set of buffers, one barrier per pair of steps, so that each chain fills the other's
+  // waits.  (A one-wave workgroup gets that from the other workgroups on its SIMD instead.)
+  constexpr bool INTERLEAVE = SUBCK && V == 64;
+  constexpr int NBUF = INTERLEAVE ? 2 : 1;
   using St = BwdStage<V>;
   static_assert(kBwdSeg % SUB == 0 && SUB % 2 == 0, "sub-segments tile a segment");
 
   // Stage records: the whole segment (segment checkpoints: pass A runs over it), or only the
   // sub-segment being recomputed and walked (sub-segment checkpoints).
-  __shared__ __attribute__((aligned(16))) float stage[(SUBCK ? SUB : kBwdSeg) * St::STEP];
+  __shared__ __attribute__((aligned(16))) float stage[NBUF * (SUBCK ? SUB : kBwdSeg) * St::STEP];
   // H_{t-1} of the sub-segment's steps, split fp16: [SUB][NT tiles][hi|lo][64 slots][2 dwords].
   // Pass A uses entries 0 and 1 as its exchange buffer.
-  __shared__ __attribute__((aligned(16))) uint32_t hst[SUB * ENTRY];
+  __shared__ __attribute__((aligned(16))) uint32_t hst[NBUF * SUB * ENTRY];
   // Z_t of the sub-segment's steps: [SUB][NT][64 lanes][4 floats].
-  __shared__ __attribute__((aligned(16))) float zst[SUB * NT * 64 * 4];
+  __shared__ __attribute__((aligned(16))) float zst[NBUF * SUB * NT * 64 * 4];
   // D_t exchange, by step parity (one buffer for a single wave): [2][NT tiles][hi|lo][64 slots][2 dwords].
   __shared__ __attribute__((aligned(16))) uint32_t dx[(ONE ? 1 : 2) * ENTRY];
   // Per-wave partial sums of dq, dk (per row) and df over the sub-segment's steps (several waves;
@@ -528,11 +533,14 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   float dwr4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
   // dq, dk, df of the sub-segment's steps [tb, tb + SUB) from the per-wave partials.
-  auto finalize = [&](int tb) {
+  // (tbq: first step of the sub-segment whose dq is pending, tbk: whose dk, df; < 0: none.)
+  auto finalize2 = [&](int tbq, int tbk) {
     if constexpr (ONE) return;
     for (int i = tid; i < SUB * 16 * 2 + SUB; i += NTH) {
       if (i < SUB * 32) {
         const int which = i / (SUB * 16), j = (i / 16) % SUB, row = i % 16;
+        const int tb = which == 0 ? tbq : tbk;
+        if (tb < 0) continue;
         const int t = tb + j;
         float acc = 0.0f;
 #pragma unroll
@@ -540,7 +548,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
         if (t < a.T) (which == 0 ? a.dq : a.dk)[(((long)b * a.T + t) * a.N + nh) * a.K + row0 + row] = acc;
       } else {
         const int j = i - SUB * 32;
-        const int t = tb + j;
+        if (tbk < 0) continue;
+        const int t = tbk + j;
         float acc = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < NT; ++ww) acc += red_f[j][ww][0];
@@ -548,11 +557,212 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       }
     }
   };
+  auto finalize = [&](int tb) { finalize2(tb, tb); };
 
   // Lane partials of the current group of four steps: dv, dk, df (walk) and dq (recompute).
   float xq[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xk[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float xh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   int pending_tb = -1;                     // sub-segment whose dq, dk, df await finalize
+
+  // ---------------- walk helpers ----------------
+  struct RevIn {
+    float f, qn;
+    float4 u4, v4, z4;
+    uint2 h_hi, h_lo;
+  };
+  // Inputs of walk step j from a sub-segment's stage records (ss), H_{t-1} tiles (hs) and Z (zs).
+  auto load_rev = [&](const float* ss, const uint32_t* hs, const float* zs, int j) __attribute__((always_inline)) {
+    RevIn in;
+    const float* st = ss + j * St::STEP;
+    const uint32_t* hj = hs + j * ENTRY;
+    in.f = st[0];
+    in.qn = st[St::OQ + n];
+    in.u4 = *(const float4*)(st + St::OU + 16 * w + 4 * g);
+    in.v4 = *(const float4*)(st + St::OV + 16 * w + 4 * g);
+    in.h_hi = *(const uint2*)(hj + tile_off(w, 0) + 2 * own_slot);
+    in.h_lo = *(const uint2*)(hj + tile_off(w, 1) + 2 * own_slot);
+    in.z4 = *(const float4*)(zs + ((j * NT + w) * 64 + lane) * 4);
+    return in;
+  };
+  struct RevFront {
+    uint2 dh, dl;   // own split D tile (own halves of the chain's B operand)
+    f32x4 cinit;    // f R
+    float dk_l, df_l;
+  };
+  // R, D of step j (the chain's critical path), published at once; then f R and the per-lane
+  // partial sums of dk, df and dw_r in the shadow of that write.
+  auto front = [&](int j, const RevIn& in) __attribute__((always_inline)) {
+    RevFront fr;
+    const float Z[4] = {in.z4.x, in.z4.y, in.z4.z, in.z4.w};
+    const float uu[4] = {in.u4.x, in.u4.y, in.u4.z, in.u4.w};
+    const float vv[4] = {in.v4.x, in.v4.y, in.v4.z, in.v4.w};
+    const float g1 = 1.0f - in.f;
+    float R[4], D[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      R[r] = __builtin_fmaf(in.qn, uu[r], C[r]);
+      D[r] = (g1 * R[r]) * __builtin_fmaf(-Z[r], Z[r], 1.0f);
+    }
+    put_tile(dx + (ONE ? 0 : (j & 1) * ENTRY), D, fr.dh, fr.dl);
+    __builtin_amdgcn_sched_barrier(0);
+    float Hp[4];  // H_{t-1}
+    Hp[0] = f16_lo_to_f32(in.h_hi.x) + f16_lo_to_f32(in.h_lo.x);
+    Hp[1] = f16_hi_to_f32(in.h_hi.x) + f16_hi_to_f32(in.h_lo.x);
+    Hp[2] = f16_lo_to_f32(in.h_hi.y) + f16_lo_to_f32(in.h_lo.y);
+    Hp[3] = f16_hi_to_f32(in.h_hi.y) + f16_hi_to_f32(in.h_lo.y);
+    fr.dk_l = fr.df_l = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      fr.cinit[r] = in.f * R[r];
+      fr.df_l = __builtin_fmaf(R[r], Hp[r] - Z[r], fr.df_l);
+      fr.dk_l = __builtin_fmaf(D[r], vv[r], fr.dk_l);
+      dwr4[r] = __builtin_fmaf(uu[r], vv[r], dwr4[r]);
+    }
+    return fr;
+  };
+
+  // dq of a recomputed step j of the sub-segment starting at step tb (H = H_t): grouped four steps
+  // at a time (lane (g, n) ends with step j0 + g, j0 = j & ~3).
+  auto rec_dq = [&](const float (&Hn)[4], const float* st, int j, int tb) __attribute__((always_inline)) {
+    const float4 u4 = *(const float4*)(st + St::OU + 16 * w + 4 * g);
+    float dq_l = Hn[0] * u4.x;
+    dq_l = __builtin_fmaf(Hn[1], u4.y, dq_l);
+    dq_l = __builtin_fmaf(Hn[2], u4.z, dq_l);
+    dq_l = __builtin_fmaf(Hn[3], u4.w, dq_l);
+    if constexpr (GROUP4) {
+      xh[j & 3] = dq_l;
+      if ((j & 3) == 3) {
+        const float dq4 = reduce_rows4(xh[0], xh[1], xh[2], xh[3]);
+        if constexpr (ONE) {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq4), dqres,
+                                                qk_lane + (uint32_t)((tb + j - 3) * qkstep * 4), 0, 0);
+        } else {
+          red_q[j - 3 + g][w][n] = dq4;
+        }
+      }
+    } else {
+      dq_l = sum_rows4(dq_l);
+      if constexpr (ONE) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq_l), dqres,
+                                              g == 0 ? qk_lane + (uint32_t)((tb + j) * qkstep * 4) : kBufferDrop, 0, 0);
+      } else if (g == 0) {
+        red_q[j][w][n] = dq_l;
+      }
+    }
+  };
+
+  // Walk step j of the sub-segment starting at step tb (records ss, tiles hs, Z zs), software-
+  // pipelined: the inputs of step j-1 are read right after step j's barrier together with step
+  // j's exchange reads, and the step ends with step j-1's R, D and publish (which wait for step
+  // j's chain MFMAs).  The hooks add independent work: reads (issued with the step's reads),
+  // MFMAs (queued behind the chain's), and a tail (after the publish of D).
+  // (fr: step j's front, nxt: step j-1's inputs, both carried from step to step.)
+  RevIn nxt;
+  RevFront fr;
+  auto walk_step = [&](int j, int tb, const float* ss, const uint32_t* hs, const float* zs, auto&& hook_reads,
+                       auto&& hook_mfma, auto&& hook_tail) __attribute__((always_inline)) {
+    const int js = tb + j;  // global step
+    const float* st = ss + j * St::STEP;
+    const uint32_t* hj = hs + j * ENTRY;
+    const uint32_t* dxp = dx + (ONE ? 0 : (j & 1) * ENTRY);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+
+    // Step j's exchange reads (chain operands, transposed tiles for dW and dv), and step j-1's
+    // inputs.
+    const Ops o = read_ops(dxp);
+    const uint2 hT = lds_read_tr(hj + tile_off(w, 0) + 2 * tr_slot);
+    uint2 dT[NT], dThi = make_uint2(0, 0);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      dT[tt] = lds_read_tr(dxp + tile_off(tt, 0) + 2 * tr_slot);
+      if (tt == w) dThi = dT[tt];  // (a select: indexing dT by w would put dT in memory)
+    }
+    const uint2 dTlo = lds_read_tr(dxp + tile_off(w, 1) + 2 * tr_slot);
+    const float4 k4 = *(const float4*)(st + St::OK + 4 * g);
+    if (j > 0) nxt = load_rev(ss, hs, zs, j - 1);
+    hook_reads();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Chain: C_{t-1} = f R + D W^T on the split-precision MFMA.
+    const f32x4 acc =
+        contract(fr.cinit, bOwnHi, bOwnLo, bOthHi, bOthLo, fr.dh, fr.dl, o);
+    hook_mfma();
+
+    // dW[16w + m][16tt + j] += sum_rows H_{t-1}[row][16w + m] D[row][16tt + j]: one fp16 16x16x16
+    // MFMA per D tile, both operands read transposed from LDS (rows on the contraction index).
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) dWacc[tt] = mfma16_f16(hT, dT[tt], dWacc[tt]);
+
+    // Off the chain, while the MFMAs run.  dk, df: sums over this wave's 16 columns (the four
+    // lane rows); df also over the 16 rows.  Grouped: steps j .. j+3 (j % 4 == 0) reduced
+    // together, lane (g, n) ending with step j + g.
+    if (!GROUP4 || (j & 3) == 0) {
+      float dk_l, df_l;
+      if constexpr (GROUP4) {
+        xk[j & 3] = fr.dk_l;
+        xf[j & 3] = fr.df_l;
+        dk_l = reduce_rows4(xk[0], xk[1], xk[2], xk[3]);
+        df_l = reduce_rows4(xf[0], xf[1], xf[2], xf[3]);
+      } else {
+        dk_l = sum_rows4(fr.dk_l);
+        df_l = sum_rows4(fr.df_l);
+      }
+      df_l += dpp<kDppRowMirror>(df_l);
+      df_l += dpp<kDppRowHalfMirror>(df_l);
+      df_l += dpp<kDppQuadXor1>(df_l);
+      df_l += dpp<kDppQuadXor2>(df_l);
+      if constexpr (ONE) {
+        const uint32_t tstep = (uint32_t)js;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dk_l), dkres,
+                                              GROUP4 || g == 0 ? qk_lane + tstep * qkstep * 4 : kBufferDrop, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(df_l), dfres,
+                                              df_lane == kBufferDrop ? kBufferDrop : df_lane + tstep * a.N * 4, 0, 0);
+      } else if constexpr (GROUP4) {
+        red_k[j + g][w][n] = dk_l;
+        red_f[j + g][w][n] = df_l;
+      } else if (g == 0) {
+        red_k[j][w][n] = dk_l;
+        red_f[j][w][n] = df_l;
+      }
+    } else {
+      xk[j & 3] = fr.dk_l;
+      xf[j & 3] = fr.df_l;
+    }
+
+    // Step j-1's R, D and publish as soon as the chain has produced C.
+    // (the padding steps of a ragged tail must leave the chain unchanged: no clamp there)
+    const bool real = js < a.T;
+    const float lo = real ? clip_lo : -__builtin_inff(), hi = real ? clip_hi : __builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) C[r] = __builtin_amdgcn_fmed3f(acc[r], lo, hi);
+    if (j > 0) fr = front(j - 1, nxt);
+    hook_tail();
+
+    // dv[col 16w + i] = sum_rows D[row][col] k[row] (+ w_r u when this workgroup holds all rows).
+    float x = k4.x * (f16_lo_to_f32(dThi.x) + f16_lo_to_f32(dTlo.x));
+    x = __builtin_fmaf(k4.y, f16_hi_to_f32(dThi.x) + f16_hi_to_f32(dTlo.x), x);
+    x = __builtin_fmaf(k4.z, f16_lo_to_f32(dThi.y) + f16_lo_to_f32(dTlo.y), x);
+    x = __builtin_fmaf(k4.w, f16_hi_to_f32(dThi.y) + f16_hi_to_f32(dTlo.y), x);
+    if constexpr (GROUP4) {
+      // Steps j .. j+3 are collected in xq; one cross-row reduction of the four leaves lane (g, i)
+      // with dv[step j0 + g][16w + i].
+      xq[j & 3] = x;
+      if ((j & 3) == 0) {
+        float dvv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
+        const float ucol = ss[(j + g) * St::STEP + St::OU + 16 * w + n];
+        dvv = __builtin_fmaf(wr_col, ucol, dvv);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv), dvres, dv_lane + (uint32_t)(js * ystep * 4), 0, 0);
+      }
+    } else {
+      x = sum_rows4(x);
+      const float ucol = st[St::OU + 16 * w + n];
+      const float dvv = __builtin_fmaf(wr_col, ucol, x);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv), dvres,
+                                            g == 0 ? dv_lane + (uint32_t)(js * ystep * 4) : kBufferDrop, 0, 0);
+    }
+  };
+  auto none = [] {};
 
   // Sub-segment checkpoints: the stage records of the next sub-segment to walk, in registers.
   BwdSubRegs<V, BF16IN, SUB, NTH> sub_regs;
@@ -565,287 +775,199 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     sub_regs.load(a, b, nh, row0, tl, min(SUB, a.T - tl), tid);
     nextH = *(const float4*)(a.ckpt + ((long)u * nck + nck - 1) * KV + lane_off);
   }
+  // Prefetch of sub-segment p (clamped at 0) with sub-segment checkpoints.
+  auto prefetch = [&](int p) __attribute__((always_inline)) {
+    const int pp = max(p, 0);
+    nextH = *(const float4*)(a.ckpt + ((long)u * nck + pp) * KV + lane_off);
+    sub_regs.load(a, b, nh, row0, pp * SUB, min(SUB, a.T - pp * SUB), tid);
+  };
 
-  for (int seg = nseg - 1; seg >= 0; --seg) {
-    const int t0 = seg * kBwdSeg;
-    const int nst = min(kBwdSeg, a.T - t0);
-    const int nsub = (nst + SUB - 1) / SUB;
-    if constexpr (!SUBCK) {
-      lds_barrier();  // the previous segment's readers are done with the stage
-      if (pending_tb >= 0) finalize(pending_tb);
-      pending_tb = -1;
-      bwd_stage_segment<V, BF16IN>(a, b, nh, row0, t0, nst, nsub * SUB, stage, tid, NTH);
-    }
+  if constexpr (INTERLEAVE) {
+    // Buffers of sub-segment p (p >= -1).
+    auto stg = [&](int p) { return stage + ((p + 2) & 1) * (SUB * St::STEP); };
+    auto hsb = [&](int p) { return hst + ((p + 2) & 1) * (SUB * ENTRY); };
+    auto zsb = [&](int p) { return zst + ((p + 2) & 1) * (SUB * NT * 64 * 4); };
+    const int P = nck;  // sub-segments
+    float Hr[4];        // state of the sub-segment being recomputed
+    uint2 hh, hl;
+    // Writes the prefetched records and entry state of sub-segment p into its buffers.
+    auto take = [&](int p) __attribute__((always_inline)) {
+      Hr[0] = nextH.x; Hr[1] = nextH.y; Hr[2] = nextH.z; Hr[3] = nextH.w;
+      sub_regs.store(stg(p), tid);
+      put_tile(hsb(p), Hr, hh, hl);
+    };
 
-    // The checkpoint entering this segment (segment checkpoints).
-    const float* ck = a.ckpt + ((long)u * nck + seg) * KV + lane_off;
-    float H[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (!SUBCK) {
-      const float4 h4 = *(const float4*)ck;
-      H[0] = h4.x; H[1] = h4.y; H[2] = h4.z; H[3] = h4.w;
-    }
-
-    // ---------------- pass A: forward up to the last sub-segment (segment checkpoints only) ----------------
-    if (!SUBCK && nsub > 1) {
-      uint2 hh, hl;
-      put_tile(hst, H, hh, hl);
-      lds_barrier();  // (also makes the stage written above visible)
-      f32x4 kv = rank1(stage);
-      for (int m = 0; m < nsub - 1; ++m) {
-        if (m > 0) *(float4*)(subck + (long)m * 16 * V) = make_float4(H[0], H[1], H[2], H[3]);
-#pragma unroll
-        for (int j = 0; j < SUB; ++j) {
-          float Z[4];
-          const float* st = stage + (m * SUB + j) * St::STEP;
-          fwd_step(st, st + St::STEP, hst + (j & 1) * ENTRY, hst + ((j + 1) & 1) * ENTRY, kv, H, Z, hh, hl);
-          lds_barrier();
-        }
-      }
-      __threadfence_block();  // the scratch states are read back by the same lanes below
-    }
-
-    // ---------------- sub-segments, last to first ----------------
-    for (int m = nsub - 1; m >= 0; --m) {
-      const int jb = m * SUB;
-      if constexpr (!SUBCK) {
-        if (m < nsub - 1) {
-          H[0] = nextH.x; H[1] = nextH.y; H[2] = nextH.z; H[3] = nextH.w;
-        }
-        if (m > 0) nextH = *(const float4*)(m - 1 > 0 ? subck + (long)(m - 1) * 16 * V : ck);
-      }
-
-      // 1. Recompute the sub-segment: hst[j] = H_{t-1} (split), zst[j] = Z_t.
-      lds_barrier();  // the previous walk is done with hst, zst, the partial sums (and the stage)
-      // Records of this sub-segment: in the segment's stage, or (sub-segment checkpoints) written
-      // now from the registers prefetched during the previous walk.
-      const float* sstage = SUBCK ? stage : stage + jb * St::STEP;
-      uint2 hh, hl;
-      if constexpr (SUBCK) {
-        // Everything prefetched for this sub-segment is used before the next prefetch is issued,
-        // so that waiting for it never waits for the new loads.
-        H[0] = nextH.x; H[1] = nextH.y; H[2] = nextH.z; H[3] = nextH.w;
-        sub_regs.store(stage, tid);
-        put_tile(hst, H, hh, hl);
-        if (pending_tb >= 0) finalize(pending_tb);
-        pending_tb = t0 + jb;
-        // Prefetch the sub-segment before this one in time (at the first one: itself again).
-        const int pp = max(seg * NSUB + m - 1, 0);
-        nextH = *(const float4*)(a.ckpt + ((long)u * nck + pp) * KV + lane_off);
-        sub_regs.load(a, b, nh, row0, pp * SUB, min(SUB, a.T - pp * SUB), tid);
-      } else {
-        if (pending_tb >= 0) finalize(pending_tb);
-        pending_tb = t0 + jb;
-        put_tile(hst, H, hh, hl);
-      }
-      lds_barrier();  // hst, and the stage records written above by every wave, are complete
-      f32x4 kv = rank1(sstage);
+    // Prologue: the last sub-segment is recomputed alone.
+    take(P - 1);
+    prefetch(P - 2);
+    lds_barrier();
+    {
+      const float* ss = stg(P - 1);
+      f32x4 kv = rank1(ss);
 #pragma unroll
       for (int j = 0; j < SUB; ++j) {
         float Z[4];
-        const float* st = sstage + j * St::STEP;
-        fwd_step(st, j + 1 < SUB ? st + St::STEP : nullptr, hst + j * ENTRY,
-                 j + 1 < SUB ? hst + (j + 1) * ENTRY : nullptr, kv, H, Z, hh, hl);
-        *(float4*)(zst + ((j * NT + w) * 64 + lane) * 4) = make_float4(Z[0], Z[1], Z[2], Z[3]);
+        const float* st = ss + j * St::STEP;
+        fwd_step(st, j + 1 < SUB ? st + St::STEP : nullptr, hsb(P - 1) + j * ENTRY,
+                 j + 1 < SUB ? hsb(P - 1) + (j + 1) * ENTRY : nullptr, kv, Hr, Z, hh, hl);
+        *(float4*)(zsb(P - 1) + ((j * NT + w) * 64 + lane) * 4) = make_float4(Z[0], Z[1], Z[2], Z[3]);
         __builtin_amdgcn_sched_barrier(0);
-        // dq_t = H_t u_t (row sums over this wave's 16 columns) needs no backward quantity: it is
-        // formed here, in the shadow of the writes above.
-        const float4 u4 = *(const float4*)(st + St::OU + 16 * w + 4 * g);
-        float dq_l = H[0] * u4.x;
-        dq_l = __builtin_fmaf(H[1], u4.y, dq_l);
-        dq_l = __builtin_fmaf(H[2], u4.z, dq_l);
-        dq_l = __builtin_fmaf(H[3], u4.w, dq_l);
-        if constexpr (GROUP4) {
-          // Steps j0 .. j0+3 (j0 = j & ~3) are reduced together: lane (g, n) ends with step j0 + g.
-          xh[j & 3] = dq_l;
-          if ((j & 3) == 3) {
-            const float dq4 = reduce_rows4(xh[0], xh[1], xh[2], xh[3]);
-            if constexpr (ONE) {
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq4), dqres,
-                                                    qk_lane + (uint32_t)((t0 + jb + j - 3) * qkstep * 4), 0, 0);
-            } else {
-              red_q[j - 3 + g][w][n] = dq4;
-            }
-          }
-        } else {
-          dq_l = sum_rows4(dq_l);
-          if constexpr (ONE) {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq_l), dqres,
-                                                  g == 0 ? qk_lane + (uint32_t)((t0 + jb + j) * qkstep * 4) : kBufferDrop,
-                                                  0, 0);
-          } else if (g == 0) {
-            red_q[j][w][n] = dq_l;
-          }
-        }
+        rec_dq(Hr, st, j, (P - 1) * SUB);
         lds_barrier();
-      }
-
-      // 2. Walk the sub-segment backwards, software-pipelined: the inputs of step j-1 are read right
-      //    after step j's barrier together with step j's exchange reads, and iteration j ends with
-      //    step j-1's R, D and publish (which wait for step j's chain MFMAs).
-      struct RevIn {
-        float f, qn;
-        float4 u4, v4, z4;
-        uint2 h_hi, h_lo;
-      };
-      auto load_rev = [&](int j) {
-        RevIn in;
-        const float* st = sstage + j * St::STEP;
-        const uint32_t* hj = hst + j * ENTRY;
-        in.f = st[0];
-        in.qn = st[St::OQ + n];
-        in.u4 = *(const float4*)(st + St::OU + 16 * w + 4 * g);
-        in.v4 = *(const float4*)(st + St::OV + 16 * w + 4 * g);
-        in.h_hi = *(const uint2*)(hj + tile_off(w, 0) + 2 * own_slot);
-        in.h_lo = *(const uint2*)(hj + tile_off(w, 1) + 2 * own_slot);
-        in.z4 = *(const float4*)(zst + ((j * NT + w) * 64 + lane) * 4);
-        return in;
-      };
-      struct RevFront {
-        uint2 dh, dl;   // own split D tile (own halves of the chain's B operand)
-        float cinit[4]; // f R
-        float dk_l, df_l;
-      };
-      // R, D of step j (the chain's critical path), published at once; then f R and the per-lane
-      // partial sums of dk, df and dw_r in the shadow of that write.
-      auto front = [&](int j, const RevIn& in) {
-        RevFront fr;
-        const float Z[4] = {in.z4.x, in.z4.y, in.z4.z, in.z4.w};
-        const float uu[4] = {in.u4.x, in.u4.y, in.u4.z, in.u4.w};
-        const float vv[4] = {in.v4.x, in.v4.y, in.v4.z, in.v4.w};
-        const float g1 = 1.0f - in.f;
-        float R[4], D[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          R[r] = __builtin_fmaf(in.qn, uu[r], C[r]);
-          D[r] = (g1 * R[r]) * __builtin_fmaf(-Z[r], Z[r], 1.0f);
-        }
-        put_tile(dx + (ONE ? 0 : (j & 1) * ENTRY), D, fr.dh, fr.dl);
-        __builtin_amdgcn_sched_barrier(0);
-        float Hp[4];  // H_{t-1}
-        Hp[0] = f16_lo_to_f32(in.h_hi.x) + f16_lo_to_f32(in.h_lo.x);
-        Hp[1] = f16_hi_to_f32(in.h_hi.x) + f16_hi_to_f32(in.h_lo.x);
-        Hp[2] = f16_lo_to_f32(in.h_hi.y) + f16_lo_to_f32(in.h_lo.y);
-        Hp[3] = f16_hi_to_f32(in.h_hi.y) + f16_hi_to_f32(in.h_lo.y);
-        fr.dk_l = fr.df_l = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          fr.cinit[r] = in.f * R[r];
-          fr.df_l = __builtin_fmaf(R[r], Hp[r] - Z[r], fr.df_l);
-          fr.dk_l = __builtin_fmaf(D[r], vv[r], fr.dk_l);
-          dwr4[r] = __builtin_fmaf(uu[r], vv[r], dwr4[r]);
-        }
-        return fr;
-      };
-
-      RevIn nxt = load_rev(SUB - 1);
-      RevFront fr = front(SUB - 1, nxt);
-#pragma unroll
-      for (int j = SUB - 1; j >= 0; --j) {
-        const int js = jb + j;
-        const float* st = sstage + j * St::STEP;
-        const uint32_t* hj = hst + j * ENTRY;
-        const uint32_t* dxp = dx + (ONE ? 0 : (j & 1) * ENTRY);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_barrier();
-
-        // Step j's exchange reads (chain operands, transposed tiles for dW and dv), and step j-1's
-        // inputs.
-        const Ops o = read_ops(dxp);
-        const uint2 hT = lds_read_tr(hj + tile_off(w, 0) + 2 * tr_slot);
-        uint2 dT[NT], dThi = make_uint2(0, 0);
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          dT[tt] = lds_read_tr(dxp + tile_off(tt, 0) + 2 * tr_slot);
-          if (tt == w) dThi = dT[tt];  // (a select: indexing dT by w would put dT in memory)
-        }
-        const uint2 dTlo = lds_read_tr(dxp + tile_off(w, 1) + 2 * tr_slot);
-        const float4 k4 = *(const float4*)(st + St::OK + 4 * g);
-        if (j > 0) nxt = load_rev(j - 1);
-        __builtin_amdgcn_sched_barrier(0);
-
-        // Chain: C_{t-1} = f R + D W^T on the split-precision MFMA.
-        const f32x4 acc =
-            contract(f32x4{fr.cinit[0], fr.cinit[1], fr.cinit[2], fr.cinit[3]}, bOwnHi, bOwnLo, bOthHi, bOthLo,
-                     fr.dh, fr.dl, o);
-
-        // dW[16w + m][16tt + j] += sum_rows H_{t-1}[row][16w + m] D[row][16tt + j]: one fp16 16x16x16
-        // MFMA per D tile, both operands read transposed from LDS (rows on the contraction index).
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) dWacc[tt] = mfma16_f16(hT, dT[tt], dWacc[tt]);
-
-        // Off the chain, while the MFMAs run.  dk, df: sums over this wave's 16 columns (the four
-        // lane rows); df also over the 16 rows.
-        // Grouped: steps j .. j+3 (j % 4 == 0) reduced together, lane (g, n) ending with step j + g.
-        if (!GROUP4 || (j & 3) == 0) {
-          float dk_l, df_l;
-          if constexpr (GROUP4) {
-            xk[j & 3] = fr.dk_l;
-            xf[j & 3] = fr.df_l;
-            dk_l = reduce_rows4(xk[0], xk[1], xk[2], xk[3]);
-            df_l = reduce_rows4(xf[0], xf[1], xf[2], xf[3]);
-          } else {
-            dk_l = sum_rows4(fr.dk_l);
-            df_l = sum_rows4(fr.df_l);
-          }
-          df_l += dpp<kDppRowMirror>(df_l);
-          df_l += dpp<kDppRowHalfMirror>(df_l);
-          df_l += dpp<kDppQuadXor1>(df_l);
-          df_l += dpp<kDppQuadXor2>(df_l);
-          if constexpr (ONE) {
-            const uint32_t tstep = (uint32_t)(t0 + js);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dk_l), dkres,
-                                                  GROUP4 || g == 0 ? qk_lane + tstep * qkstep * 4 : kBufferDrop, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(df_l), dfres,
-                                                  df_lane == kBufferDrop ? kBufferDrop : df_lane + tstep * a.N * 4, 0, 0);
-          } else if constexpr (GROUP4) {
-            red_k[j + g][w][n] = dk_l;
-            red_f[j + g][w][n] = df_l;
-          } else if (g == 0) {
-            red_k[j][w][n] = dk_l;
-            red_f[j][w][n] = df_l;
-          }
-        } else {
-          xk[j & 3] = fr.dk_l;
-          xf[j & 3] = fr.df_l;
-        }
-
-        // Step j-1's R, D and publish as soon as the chain has produced C.
-        // (the padding steps of a ragged tail must leave the chain unchanged: no clamp there)
-        const bool real = t0 + js < a.T;
-        const float lo = real ? clip_lo : -__builtin_inff(), hi = real ? clip_hi : __builtin_inff();
-#pragma unroll
-        for (int r = 0; r < 4; ++r) C[r] = __builtin_amdgcn_fmed3f(acc[r], lo, hi);
-        if (j > 0) fr = front(j - 1, nxt);
-
-        // dv[col 16w + i] = sum_rows D[row][col] k[row] (+ w_r u when this workgroup holds all rows).
-        float x = k4.x * (f16_lo_to_f32(dThi.x) + f16_lo_to_f32(dTlo.x));
-        x = __builtin_fmaf(k4.y, f16_hi_to_f32(dThi.x) + f16_hi_to_f32(dTlo.x), x);
-        x = __builtin_fmaf(k4.z, f16_lo_to_f32(dThi.y) + f16_lo_to_f32(dTlo.y), x);
-        x = __builtin_fmaf(k4.w, f16_hi_to_f32(dThi.y) + f16_hi_to_f32(dTlo.y), x);
-        if constexpr (GROUP4) {
-          // Steps jb + (j & ~3) + q are collected in xq[q]; one cross-row reduction of the four
-          // leaves lane (g, i) with dv[step jb + (j & ~3) + g][16w + i].
-          xq[j & 3] = x;
-          if ((j & 3) == 0) {
-            float dvv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
-            const float ucol = sstage[(j + g) * St::STEP + St::OU + 16 * w + n];
-            dvv = __builtin_fmaf(wr_col, ucol, dvv);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv), dvres,
-                                                  dv_lane + (uint32_t)((t0 + js) * ystep * 4), 0, 0);
-          }
-        } else {
-          x = sum_rows4(x);
-          const float ucol = st[St::OU + 16 * w + n];
-          const float dvv = __builtin_fmaf(wr_col, ucol, x);
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv), dvres,
-                                                g == 0 ? dv_lane + (uint32_t)((t0 + js) * ystep * 4) : kBufferDrop, 0,
-                                                0);
-        }
       }
     }
+
+    for (int p = P - 1; p >= 0; --p) {
+      lds_barrier();  // the previous pair of sub-segments is done with the buffers of p - 1
+      take(p - 1);    // (at p = 0 a repeat of sub-segment 0, recomputed and never used)
+      finalize2(p * SUB, p + 1 < P ? (p + 1) * SUB : -1);
+      prefetch(p - 2);
+      lds_barrier();
+
+      const float* ws = stg(p);
+      const uint32_t* wh = hsb(p);
+      const float* wz = zsb(p);
+      const float* rs = stg(p - 1);
+      uint32_t* rh = hsb(p - 1);
+      float* rz = zsb(p - 1);
+      nxt = load_rev(ws, wh, wz, SUB - 1);
+      fr = front(SUB - 1, nxt);
+      f32x4 kv = rank1(rs);
+#pragma unroll
+      for (int i = 0; i < SUB; ++i) {
+        const int j = SUB - 1 - i;
+        // Recompute step i of sub-segment p - 1 (as fwd_step, split around the walk step's phases).
+        const float* st = rs + i * St::STEP;
+        Ops ro;
+        float avn = 0.0f, bkn = 0.0f, f = 0.0f;
+        f32x4 racc;
+        walk_step(
+            j, p * SUB, ws, wh, wz,
+            [&]() __attribute__((always_inline)) {
+              ro = read_ops(rh + i * ENTRY);
+              if (i + 1 < SUB) {
+                avn = st[St::STEP + (g == 0 ? St::OV + 16 * w + n : 3)];
+                bkn = st[St::STEP + (g == 0 ? St::OCK + n : 3)];
+              }
+              f = st[0];
+            },
+            [&]() __attribute__((always_inline)) { racc = contract(kv, fOwnHi, fOwnLo, fOthHi, fOthLo, hh, hl, ro); },
+            [&]() __attribute__((always_inline)) {
+              const float g1 = 1.0f - f, m2g = -2.0f * g1;
+              float Z[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float rr = tanh_recip(racc[r]);
+                Z[r] = __builtin_fmaf(-2.0f, rr, 1.0f);
+                Hr[r] = __builtin_fmaf(m2g, rr, __builtin_fmaf(f, Hr[r], g1));
+              }
+              if (i + 1 < SUB) {
+                put_tile(rh + (i + 1) * ENTRY, Hr, hh, hl);
+              }
+              *(float4*)(rz + ((i * NT + w) * 64 + lane) * 4) = make_float4(Z[0], Z[1], Z[2], Z[3]);
+              rec_dq(Hr, st, i, (p - 1) * SUB);
+              if (i + 1 < SUB) kv = mfma_f32(avn, bkn, zero4);
+            });
+      }
+    }
+    lds_barrier();
+    finalize2(-1, 0);
+  } else {
+    for (int seg = nseg - 1; seg >= 0; --seg) {
+      const int t0 = seg * kBwdSeg;
+      const int nst = min(kBwdSeg, a.T - t0);
+      const int nsub = (nst + SUB - 1) / SUB;
+      if constexpr (!SUBCK) {
+        lds_barrier();  // the previous segment's readers are done with the stage
+        if (pending_tb >= 0) finalize(pending_tb);
+        pending_tb = -1;
+        bwd_stage_segment<V, BF16IN>(a, b, nh, row0, t0, nst, nsub * SUB, stage, tid, NTH);
+      }
+
+      // The checkpoint entering this segment (segment checkpoints).
+      const float* ck = a.ckpt + ((long)u * nck + seg) * KV + lane_off;
+      float H[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (!SUBCK) {
+        const float4 h4 = *(const float4*)ck;
+        H[0] = h4.x; H[1] = h4.y; H[2] = h4.z; H[3] = h4.w;
+      }
+
+      // ---------------- pass A: forward up to the last sub-segment (segment checkpoints only) ----------------
+      if (!SUBCK && nsub > 1) {
+        uint2 hh, hl;
+        put_tile(hst, H, hh, hl);
+        lds_barrier();  // (also makes the stage written above visible)
+        f32x4 kv = rank1(stage);
+        for (int m = 0; m < nsub - 1; ++m) {
+          if (m > 0) *(float4*)(subck + (long)m * 16 * V) = make_float4(H[0], H[1], H[2], H[3]);
+#pragma unroll
+          for (int j = 0; j < SUB; ++j) {
+            float Z[4];
+            const float* st = stage + (m * SUB + j) * St::STEP;
+            fwd_step(st, st + St::STEP, hst + (j & 1) * ENTRY, hst + ((j + 1) & 1) * ENTRY, kv, H, Z, hh, hl);
+            lds_barrier();
+          }
+        }
+        __threadfence_block();  // the scratch states are read back by the same lanes below
+      }
+
+      // ---------------- sub-segments, last to first ----------------
+      for (int m = nsub - 1; m >= 0; --m) {
+        const int jb = m * SUB;
+        if constexpr (!SUBCK) {
+          if (m < nsub - 1) {
+            H[0] = nextH.x; H[1] = nextH.y; H[2] = nextH.z; H[3] = nextH.w;
+          }
+          if (m > 0) nextH = *(const float4*)(m - 1 > 0 ? subck + (long)(m - 1) * 16 * V : ck);
+        }
+
+        // 1. Recompute the sub-segment: hst[j] = H_{t-1} (split), zst[j] = Z_t.
+        lds_barrier();  // the previous walk is done with hst, zst, the partial sums (and the stage)
+        // Records of this sub-segment: in the segment's stage, or (sub-segment checkpoints) written
+        // now from the registers prefetched during the previous walk.
+        const float* sstage = SUBCK ? stage : stage + jb * St::STEP;
+        uint2 hh, hl;
+        if constexpr (SUBCK) {
+          // Everything prefetched for this sub-segment is used before the next prefetch is issued,
+          // so that waiting for it never waits for the new loads.
+          H[0] = nextH.x; H[1] = nextH.y; H[2] = nextH.z; H[3] = nextH.w;
+          sub_regs.store(stage, tid);
+          put_tile(hst, H, hh, hl);
+          if (pending_tb >= 0) finalize(pending_tb);
+          pending_tb = t0 + jb;
+          // Prefetch the sub-segment before this one in time (at the first one: itself again).
+          prefetch(seg * NSUB + m - 1);
+        } else {
+          if (pending_tb >= 0) finalize(pending_tb);
+          pending_tb = t0 + jb;
+          put_tile(hst, H, hh, hl);
+        }
+        lds_barrier();  // hst, and the stage records written above by every wave, are complete
+        f32x4 kv = rank1(sstage);
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) {
+          float Z[4];
+          const float* st = sstage + j * St::STEP;
+          fwd_step(st, j + 1 < SUB ? st + St::STEP : nullptr, hst + j * ENTRY,
+                   j + 1 < SUB ? hst + (j + 1) * ENTRY : nullptr, kv, H, Z, hh, hl);
+          *(float4*)(zst + ((j * NT + w) * 64 + lane) * 4) = make_float4(Z[0], Z[1], Z[2], Z[3]);
+          __builtin_amdgcn_sched_barrier(0);
+          // dq_t = H_t u_t (row sums over this wave's 16 columns) needs no backward quantity: it
+          // is formed here, in the shadow of the writes above.
+          rec_dq(H, st, j, t0 + jb);
+          lds_barrier();
+        }
+
+        // 2. Walk the sub-segment backwards.
+        nxt = load_rev(sstage, hst, zst, SUB - 1);
+        fr = front(SUB - 1, nxt);
+#pragma unroll
+        for (int j = SUB - 1; j >= 0; --j) walk_step(j, t0 + jb, sstage, hst, zst, none, none, none);
+      }
+    }
+    lds_barrier();
+    if (pending_tb >= 0) finalize(pending_tb);
   }
-  lds_barrier();
-  if (pending_tb >= 0) finalize(pending_tb);
 
   if (a.dH0) *(float4*)(a.dH0 + own_off) = make_float4(C[0], C[1], C[2], C[3]);
   if (s == 0 && n == 0)
