@@ -318,12 +318,12 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   // Stage records: the whole segment (segment checkpoints: pass A runs over it), or only the
   // sub-segment being recomputed and walked (sub-segment checkpoints).
   __shared__ __attribute__((aligned(16))) float stage[NBUF * (SUBCK ? SUB : kBwdSeg) * St::STEP];
-  // H_{t-1} of the sub-segment's steps, split fp16: [SUB][NT tiles][hi|lo][64 slots][2 dwords].
+  // H_{t-1} of the sub-segment's steps, split fp16: [SUB][hi|lo][NT tiles][64 slots][2 dwords].
   // Pass A uses entries 0 and 1 as its exchange buffer.
   __shared__ __attribute__((aligned(16))) uint32_t hst[NBUF * SUB * ENTRY];
   // Z_t of the sub-segment's steps: [SUB][NT][64 lanes][4 floats].
   __shared__ __attribute__((aligned(16))) float zst[NBUF * SUB * NT * 64 * 4];
-  // D_t exchange, by step parity (one buffer for a single wave): [2][NT tiles][hi|lo][64 slots][2 dwords].
+  // D_t exchange, by step parity (one buffer for a single wave): [2][hi|lo][NT tiles][64 slots][2 dwords].
   __shared__ __attribute__((aligned(16))) uint32_t dx[(ONE ? 1 : 2) * ENTRY];
   // Per-wave partial sums of dq, dk (per row) and df over the sub-segment's steps (several waves;
   // red_f holds 16 equal copies, one per lane of a row, so that every lane stores).
@@ -357,8 +357,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   // ---- operands of W ----
   // forward contraction: A = (c W)^T, A[m][k] = c W[k][16w + m]   (as in the forward scan)
   // backward chain:      A = W,       A[m][k] = W[16w + m][k]
-  // The chunk holding this wave's own tile takes that tile in k-slots 0..3 (from registers) and
-  // its partner tile w^1 in k-slots 4..7; the other chunks hold tiles 2cc, 2cc+1.
+  // Chunk cc covers tiles 2cc (k-slots 0..3) and 2cc+1 (k-slots 4..7).  The chunk co = w/2 holding
+  // this wave's own tile is listed first ("own"), the others after it.
   const float* Wn = a.W + (long)nh * V * V;
   const int col = 16 * w + n;
   const int co = w >> 1;
@@ -380,8 +380,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     lo = make_uint4(l[0], l[1], l[2], l[3]);
   };
   uint4 fOwnHi, fOwnLo, bOwnHi, bOwnLo, fOthHi[NOTH], fOthLo[NOTH], bOthHi[NOTH], bOthLo[NOTH];
-  wchunk(w, w ^ 1, true, fOwnHi, fOwnLo);
-  wchunk(w, w ^ 1, false, bOwnHi, bOwnLo);
+  wchunk(2 * co, 2 * co + 1, true, fOwnHi, fOwnLo);
+  wchunk(2 * co, 2 * co + 1, false, bOwnHi, bOwnLo);
 #pragma unroll
   for (int i = 0; i < NCH - 1; ++i) {
     const int cc = i < co ? i : i + 1;
@@ -393,8 +393,9 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   // Lane-constant slots: own record (row n, group g) and the transposing-read slot.
   const int own_slot = tile_slot(n, g);
   const int tr_slot = tile_slot(4 * g + (n >> 2), n & 3);
-  // Dword offset of (tile, hi|lo) within one entry of hst or dx.
-  auto tile_off = [](int tile, int hl) { return (tile * 2 + hl) * 128; };
+  // Dword offset of (tile, hi|lo) within one entry of hst or dx: [hi|lo][tile][64 slots][2 dwords],
+  // so that the two tiles of a chunk are one 512-byte stride apart (one paired read each).
+  auto tile_off = [](int tile, int hl) { return (hl * NT + tile) * 128; };
   constexpr bool has_partner = NT > 1;  // (with an even tile count every wave has one)
 
   // Writes this wave's tile (split fp16) into `entry`; returns the split (own B-operand halves).
@@ -407,18 +408,23 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     *(uint2*)(entry + tile_off(w, 0) + 2 * own_slot) = hi;
     *(uint2*)(entry + tile_off(w, 1) + 2 * own_slot) = lo;
   };
-  // B operands of one contraction from a step's entry: the partner halves of the own chunk and the
-  // other chunks (the own halves come from registers).
+  // B operands of one contraction from a step's entry, every chunk read whole (the own tile too,
+  // so that each read lands in its operand registers); a single tile (no partner) is taken from
+  // registers with zeros in k-slots 4..7.
   struct Ops {
-    uint2 ph, pl;
+    uint4 wh, wl;  // own chunk
     uint4 oh[NOTH], ol[NOTH];
   };
   auto read_ops = [&](const uint32_t* entry) {
     Ops o;
-    o.ph = o.pl = make_uint2(0, 0);
+    o.wh = o.wl = make_uint4(0, 0, 0, 0);
     if constexpr (has_partner) {
-      o.ph = *(const uint2*)(entry + tile_off(w ^ 1, 0) + 2 * own_slot);
-      o.pl = *(const uint2*)(entry + tile_off(w ^ 1, 1) + 2 * own_slot);
+      const uint2 h0 = *(const uint2*)(entry + tile_off(2 * co, 0) + 2 * own_slot);
+      const uint2 h1 = *(const uint2*)(entry + tile_off(2 * co + 1, 0) + 2 * own_slot);
+      const uint2 l0 = *(const uint2*)(entry + tile_off(2 * co, 1) + 2 * own_slot);
+      const uint2 l1 = *(const uint2*)(entry + tile_off(2 * co + 1, 1) + 2 * own_slot);
+      o.wh = make_uint4(h0.x, h0.y, h1.x, h1.y);
+      o.wl = make_uint4(l0.x, l0.y, l1.x, l1.y);
     }
 #pragma unroll
     for (int i = 0; i < NCH - 1; ++i) {
@@ -435,8 +441,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   // acc += A B over all chunks (three split passes per chunk).
   auto contract = [&](f32x4 acc, const uint4& AownHi, const uint4& AownLo, const uint4 (&AothHi)[NOTH],
                       const uint4 (&AothLo)[NOTH], const uint2& own_hi, const uint2& own_lo, const Ops& o) {
-    const uint4 bh = make_uint4(own_hi.x, own_hi.y, o.ph.x, o.ph.y);
-    const uint4 bl = make_uint4(own_lo.x, own_lo.y, o.pl.x, o.pl.y);
+    const uint4 bh = has_partner ? o.wh : make_uint4(own_hi.x, own_hi.y, 0, 0);
+    const uint4 bl = has_partner ? o.wl : make_uint4(own_lo.x, own_lo.y, 0, 0);
     acc = mfma_f16(AownHi, bh, acc);
     acc = mfma_f16(AownLo, bh, acc);
     acc = mfma_f16(AownHi, bl, acc);
@@ -672,12 +678,11 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     // inputs.
     const Ops o = read_ops(dxp);
     const uint2 hT = lds_read_tr(hj + tile_off(w, 0) + 2 * tr_slot);
-    uint2 dT[NT], dThi = make_uint2(0, 0);
+    uint2 dT[NT];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      dT[tt] = lds_read_tr(dxp + tile_off(tt, 0) + 2 * tr_slot);
-      if (tt == w) dThi = dT[tt];  // (a select: indexing dT by w would put dT in memory)
-    }
+    for (int tt = 0; tt < NT; ++tt) dT[tt] = lds_read_tr(dxp + tile_off(tt, 0) + 2 * tr_slot);
+    // (the own tile read again rather than selected from dT, which would wait for those reads)
+    const uint2 dThi = lds_read_tr(dxp + tile_off(w, 0) + 2 * tr_slot);
     const uint2 dTlo = lds_read_tr(dxp + tile_off(w, 1) + 2 * tr_slot);
     const float4 k4 = *(const float4*)(st + St::OK + 4 * g);
     if (j > 0) nxt = load_rev(ss, hs, zs, j - 1);
