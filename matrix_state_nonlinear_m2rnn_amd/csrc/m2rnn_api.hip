@@ -299,7 +299,6 @@ bool shared_qk_sum(const m2rnn_dims* d) { return qk_heads(d) == 1 && d->N > 1; }
 BwdLayout bwd_layout(const m2rnn_dims* d) {
   BwdLayout L;
   const long S = d->K / 16;
-  const long nseg = (d->T + kBwdSeg - 1) / kBwdSeg;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -453,7 +452,8 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
   char* ws = (char*)workspace;
   const int S = (int)(K / 16);
 
-  // 1. Checkpoints: the state entering every kBwdSeg-step segment (unless the forward kept them).
+  // 1. Checkpoints: the state entering every I-th step, I = ckpt_interval (unless the forward kept
+  //    them).
   const float* ckpt = ckpt_in ? ckpt_in : (const float*)(ws + L.ckpt);
   if (!ckpt_in) {
     FwdArgs a{};

@@ -7,17 +7,19 @@
 //     dW = sum_t H_{t-1}^T D_t,  dw_r = sum_t u_t (.) v_t,  dH_0 = C_0.
 //
 // Work decomposition (one 16-row block of one (b, n) pair per workgroup, wave w owns value
-// columns [16w, 16w+16), same register layout as the forward scan).  For every 64-step segment,
-// last to first:
-//   1. stage the segment's q, k, v, f, dy in LDS (a ragged last segment is padded with f = 1 and
-//      zero inputs, steps that leave the state and the chain exactly unchanged);
-//   2. pass A: run the forward from the segment's checkpoint, keeping the state that enters every
-//      SUB-step sub-segment;
-//   3. for every sub-segment, last to first: recompute it from its entry state, keeping each
-//      step's H_{t-1} (split fp16 hi/lo) and Z_t in LDS, then walk it backwards: R, D and the
-//      row/column partial sums in registers; D is published through LDS like H in the forward and
-//      the chain's D W^T runs on the split-precision MFMA; dW and dv read the H_{t-1} and D tiles
-//      transposed straight from LDS (ds_read_b64_tr_b16).
+// columns [16w, 16w+16), same register layout as the forward scan).  Time is walked last to first
+// in sub-segments of SUB steps (8 for V <= 64, 2 for V = 128).  For each sub-segment:
+//   1. its q, k, v, f, dy records are in LDS (a ragged tail is padded with f = 1 and zero inputs,
+//      steps that leave the state and the chain exactly unchanged);
+//   2. recompute: the forward from the sub-segment's entry state, keeping each step's H_{t-1}
+//      (split fp16 hi/lo tiles) and Z_t in LDS;
+//   3. walk it backwards: R, D and the row/column partial sums in registers; D is published
+//      through LDS like H in the forward and the chain's D W^T runs on the split-precision MFMA;
+//      dW and dv read the H_{t-1} and D tiles transposed straight from LDS (ds_read_b64_tr_b16).
+// Entry states: with checkpoints at every sub-segment (V <= 64) they are read from the checkpoint
+// array, prefetched with the records one sub-segment ahead; with checkpoints every 64 steps
+// (V = 128) a segment is staged whole and a forward pass over it (pass A) keeps them in scratch.
+// At V = 64 the walk of sub-segment p runs interleaved with the recompute of sub-segment p - 1.
 // Per-workgroup partials of dv, df and dW are summed by separate, deterministic passes.
 #pragma once
 
@@ -25,7 +27,7 @@
 
 namespace m2rnn {
 
-constexpr int kBwdSeg = 64;  // checkpoint interval (steps)
+constexpr int kBwdSeg = 64;  // segment (checkpoint interval at V = 128), a multiple of every SUB
 
 struct BwdArgs {
   const void* q;
