@@ -122,25 +122,32 @@ struct ChunkRegs {
   TileLoader<S::TC, V, S::NTH, BF16> v;
   float f;
 
+  // The pieces of q, k, v and f start at different waves (thread indices rotated by 64 per
+  // tensor), so that no single wave carries the whole staging while the others wait for it at
+  // the next barrier.
+  static __device__ __forceinline__ int rot(int tid, int r) { return (tid + S::NTH - r % S::NTH) % S::NTH; }
+
   __device__ __forceinline__ void load(const FwdArgs& a, int b, int nh, int row0, int t0, int tid) {
     const int valid = min(S::TC, a.T - t0);
     const long qk_off = (((long)b * a.T + t0) * a.Nqk + (a.Nqk == 1 ? 0 : nh)) * a.K + row0;
     const long v_off = (((long)b * a.T + t0) * a.N + nh) * V;
     const int esz = BF16 ? 2 : 4;
     q.load((const char*)a.q + qk_off * esz, (long)a.Nqk * a.K, valid, tid);
-    k.load((const char*)a.k + qk_off * esz, (long)a.Nqk * a.K, valid, tid);
-    v.load((const char*)a.v + v_off * esz, (long)a.N * V, valid, tid);
+    k.load((const char*)a.k + qk_off * esz, (long)a.Nqk * a.K, valid, rot(tid, 64));
+    v.load((const char*)a.v + v_off * esz, (long)a.N * V, valid, rot(tid, 128));
+    const int tf = rot(tid, 192);
     f = 1.0f;
-    if (tid < valid) f = a.f[((long)b * a.T + t0 + tid) * a.N + nh];
+    if (tf < valid) f = a.f[((long)b * a.T + t0 + tf) * a.N + nh];
   }
   __device__ __forceinline__ void store(float* stage, int tid) const {
     using St = Stage<V, RB * RW>;
     q.store(stage, St::STEP, St::OQ, 1.0f, tid);
-    k.store(stage, St::STEP, St::OK, kTwoLog2e, tid);
-    v.store(stage, St::STEP, St::OV, 1.0f, tid);
-    if (tid < S::TC) {
+    k.store(stage, St::STEP, St::OK, kTwoLog2e, rot(tid, 64));
+    v.store(stage, St::STEP, St::OV, 1.0f, rot(tid, 128));
+    const int tf = rot(tid, 192);
+    if (tf < S::TC) {
       const float gf = 1.0f - f;
-      *(float4*)(stage + tid * St::STEP) = make_float4(f, gf, -2.0f * gf, 0.0f);
+      *(float4*)(stage + tf * St::STEP) = make_float4(f, gf, -2.0f * gf, 0.0f);
     }
   }
 };
