@@ -82,7 +82,10 @@ enum {
   M2RNN_EHIP = -4          /* a HIP launch or runtime call failed */
 };
 
-/* Library version, as MAJOR*10000 + MINOR*100 + PATCH. */
+/* Library version, as MAJOR*10000 + MINOR*100 + PATCH.  The minor number changes with every
+ * change of an entry point's arguments; a caller built against this header should check that
+ * m2rnn_version() == M2RNN_VERSION before calling anything else. */
+#define M2RNN_VERSION 200
 int m2rnn_version(void);
 
 /* Human-readable text for a status code (static storage). */

@@ -51,6 +51,9 @@ class M2RNNError(RuntimeError):
 
 _lib = None
 
+# The C ABI version these bindings are written for (M2RNN_VERSION in include/m2rnn.h).
+ABI_VERSION = 200
+
 
 def lib() -> ctypes.CDLL:
     """Loads libm2rnn.so (raises if it has not been built)."""
@@ -64,6 +67,9 @@ def lib() -> ctypes.CDLL:
         dp = ctypes.POINTER(Dims)
         L.m2rnn_version.restype = ci
         L.m2rnn_version.argtypes = []
+        if L.m2rnn_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.m2rnn_version()}, these bindings expect {ABI_VERSION}: "
+                               "rebuild it with `python -c 'import __graft_entry__ as g; g.build()'`")
         L.m2rnn_status_string.restype = ctypes.c_char_p
         L.m2rnn_status_string.argtypes = [ci]
         L.m2rnn_last_hip_error.restype = ci

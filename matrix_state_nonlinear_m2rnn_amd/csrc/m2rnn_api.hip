@@ -342,7 +342,7 @@ int resolve_bwd_math(int math) {
 
 extern "C" {
 
-int m2rnn_version(void) { return 100; }
+int m2rnn_version(void) { return M2RNN_VERSION; }
 
 const char* m2rnn_status_string(int status) {
   switch (status) {

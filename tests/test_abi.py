@@ -26,8 +26,13 @@ def test_exports_every_declared_function():
     assert set(names) == set(m2.EXPORTED)
 
 
+def test_header_and_bindings_agree_on_the_abi_version():
+    text = open(os.path.join(ROOT, "include", "m2rnn.h")).read()
+    assert int(re.search(r"#define M2RNN_VERSION (\d+)", text).group(1)) == m2.ABI_VERSION
+
+
 def test_version_and_status_strings():
-    assert m2.lib().m2rnn_version() >= 100
+    assert m2.lib().m2rnn_version() == m2.ABI_VERSION
     assert m2.status_string(0) == "ok"
     assert "workspace" in m2.status_string(m2.M2RNN_EWORKSPACE)
 
