@@ -418,7 +418,7 @@ def main() -> int:
         torch.cuda.synchronize()
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == "long_b2_h32_t16384_kv64" else f"M²RNN fwd head-steps/sec ({w.name}, 1 GPU)",
         "value": value,
         "unit": "head-steps/s",
         "n_gpus": 1,
