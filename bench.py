@@ -8,7 +8,7 @@ readout finish) exactly as ``m2rnn_fwd`` does; HIP events on the launch stream b
 kernel of every timed step, which gives the dominant kernel's average duration for the roofline.
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: the recurrence of one (batch, head) pair is
-a serial chain that this build runs on a single GPU.
+a serial chain that the library runs on a single GPU.
 """
 from __future__ import annotations
 
@@ -341,7 +341,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): the recurrence of a "
-              "(batch, head) pair is a serial chain and this build has no multi-GPU path.", file=sys.stderr)
+              "(batch, head) pair is a serial chain and the library has no multi-GPU path.", file=sys.stderr)
         return 2
 
     import numpy as np
