@@ -203,6 +203,10 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_bwd_kernel(
   float4 acc[QMAX];
 #pragma unroll
   for (int q = 0; q < QMAX; ++q) acc[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  // Up to 2048 features a row's y, gate and dout stay in registers between the two passes (the
+  // second pass would otherwise read them from HBM again); wider rows are read twice.
+  constexpr bool KEEP = QMAX <= 8;
+  float4 ykeep[KEEP ? QMAX : 1], gkeep[KEEP ? QMAX : 1], dkeep[KEEP ? QMAX : 1];
   for (long r = r0; r < r1; ++r) {
     const long base = r * D;
     float ss = 0.0f, rp = 0.0f;
@@ -214,6 +218,11 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_bwd_kernel(
         const float4 g = load4<BF16>(gz, base + j);
         const float4 gm = *(const float4*)(gamma + j);
         const float4 d = *(const float4*)(dout + base + j);
+        if constexpr (KEEP) {
+          ykeep[q] = yv;
+          gkeep[q] = g;
+          dkeep[q] = d;
+        }
         const float x0 = yv.x * siluf_(g.x), x1 = yv.y * siluf_(g.y), x2 = yv.z * siluf_(g.z),
                     x3 = yv.w * siluf_(g.w);
         ss += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
@@ -231,10 +240,17 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_bwd_kernel(
     for (int q = 0; q < QMAX; ++q) {
       const int j = 4 * (lane + 64 * q);
       if (j < D) {
-        const float4 yv = *(const float4*)(y + base + j);
-        const float4 g = load4<BF16>(gz, base + j);
+        float4 yv, g, d;
+        if constexpr (KEEP) {
+          yv = ykeep[q];
+          g = gkeep[q];
+          d = dkeep[q];
+        } else {
+          yv = *(const float4*)(y + base + j);
+          g = load4<BF16>(gz, base + j);
+          d = *(const float4*)(dout + base + j);
+        }
         const float4 gm = *(const float4*)(gamma + j);
-        const float4 d = *(const float4*)(dout + base + j);
         const float gs[4] = {g.x, g.y, g.z, g.w}, ys[4] = {yv.x, yv.y, yv.z, yv.w};
         const float gms[4] = {gm.x, gm.y, gm.z, gm.w}, ds[4] = {d.x, d.y, d.z, d.w};
         float oy[4], og[4], ag[4];
