@@ -80,6 +80,8 @@ int check_conv(int64_t B, int64_t T, int64_t C, int dtype) {
   if (dtype != M2RNN_DTYPE_F32 && dtype != M2RNN_DTYPE_BF16) return M2RNN_EINVAL;
   if (C % 4 != 0) return M2RNN_EUNSUPPORTED;
   if (B > 2147483647 || T > 2147483647 || C > 2147483647) return M2RNN_EUNSUPPORTED;
+  // the kernels number their waves with an int
+  if ((double)B * ceil_div(T, kConvChunkFwd) * ceil_div(C / 4, 64) > 2147483647.0) return M2RNN_EUNSUPPORTED;
   return M2RNN_OK;
 }
 
@@ -98,12 +100,13 @@ size_t norm_ws_bytes(int64_t rows, int64_t D) {
 }
 
 size_t conv_ws_bytes(int64_t B, int64_t T, int64_t C) {
-  const long parts = (long)B * ceil_div(T, kConvChunk);
+  const long parts = (long)B * ceil_div(T, kConvChunkBwd);
   return round_up256((size_t)parts * 5 * C * sizeof(float)) + round_up256(reduce_scratch(parts, 5 * C) * sizeof(float));
 }
 
-long conv_threads(int64_t B, int64_t T, int64_t C) {
-  return (long)B * ((T + kConvChunk - 1) / kConvChunk) * (C / 4);
+// Workgroups of the conv kernels: one wave per (b, chunk of `chunk` steps, 64 groups of 4 channels).
+long conv_blocks(int64_t B, int64_t T, int64_t C, int chunk) {
+  return ceil_div(B * ceil_div(T, chunk) * ceil_div(C / 4, 64), kBlkThreads / 64);
 }
 
 }  // namespace
@@ -226,19 +229,18 @@ int m2rnn_conv4_silu_fwd(int64_t B, int64_t T, int64_t C, int dtype, const void*
                          void* u, void* stream) {
   int st = check_conv(B, T, C, dtype);
   if (st) return st;
-  const long nth = conv_threads(B, T, C);
-  if (nth == 0) return M2RNN_OK;
+  const long blocks = conv_blocks(B, T, C, kConvChunkFwd);
+  if (blocks == 0) return M2RNN_OK;
   if (!x || !w || !u) return M2RNN_EINVAL;
   const void* ps[] = {x, w, bias, u};
   for (const void* p : ps)
     if (p && !al16(p)) return M2RNN_EINVAL;
   hipStream_t s = (hipStream_t)stream;
-  const unsigned blocks = (unsigned)((nth + kBlkThreads - 1) / kBlkThreads);
   if (dtype == M2RNN_DTYPE_BF16)
-    hipLaunchKernelGGL(m2rnn_conv4_silu_fwd_kernel<true>, dim3(blocks), dim3(kBlkThreads), 0, s, x, w, bias, (int)B,
+    hipLaunchKernelGGL(m2rnn_conv4_silu_fwd_kernel<true>, dim3((unsigned)blocks), dim3(kBlkThreads), 0, s, x, w, bias, (int)B,
                        (int)T, (int)C, u);
   else
-    hipLaunchKernelGGL(m2rnn_conv4_silu_fwd_kernel<false>, dim3(blocks), dim3(kBlkThreads), 0, s, x, w, bias, (int)B,
+    hipLaunchKernelGGL(m2rnn_conv4_silu_fwd_kernel<false>, dim3((unsigned)blocks), dim3(kBlkThreads), 0, s, x, w, bias, (int)B,
                        (int)T, (int)C, u);
   return status(hipGetLastError());
 }
@@ -257,24 +259,23 @@ int m2rnn_conv4_silu_bwd(int64_t B, int64_t T, int64_t C, int dtype, const void*
   int st = check_conv(B, T, C, dtype);
   if (st) return st;
   if (!w || !dw) return M2RNN_EINVAL;
-  const long nth = conv_threads(B, T, C);
-  if (nth > 0 && (!x || !du || !dx)) return M2RNN_EINVAL;
+  const long blocks = conv_blocks(B, T, C, kConvChunkBwd);
+  if (blocks > 0 && (!x || !du || !dx)) return M2RNN_EINVAL;
   const void* ps[] = {x, w, bias, du, dx, dw, dbias};
   for (const void* p : ps)
     if (p && !al16(p)) return M2RNN_EINVAL;
   hipStream_t s = (hipStream_t)stream;
-  const long parts = (long)B * ceil_div(T, kConvChunk);
+  const long parts = (long)B * ceil_div(T, kConvChunkBwd);
   if (parts > 0 && (!workspace || workspace_bytes < conv_ws_bytes(B, T, C) || !al16(workspace)))
     return M2RNN_EWORKSPACE;
   float* part = (float*)workspace;
   float* scratch = parts > 0 ? (float*)((char*)workspace + round_up256((size_t)parts * 5 * C * sizeof(float))) : nullptr;
-  if (nth > 0) {
-    const unsigned blocks = (unsigned)((nth + kBlkThreads - 1) / kBlkThreads);
+  if (blocks > 0) {
     if (dtype == M2RNN_DTYPE_BF16)
-      hipLaunchKernelGGL(m2rnn_conv4_silu_bwd_kernel<true>, dim3(blocks), dim3(kBlkThreads), 0, s, x, w, bias, du,
+      hipLaunchKernelGGL(m2rnn_conv4_silu_bwd_kernel<true>, dim3((unsigned)blocks), dim3(kBlkThreads), 0, s, x, w, bias, du,
                          (int)B, (int)T, (int)C, dx, part);
     else
-      hipLaunchKernelGGL(m2rnn_conv4_silu_bwd_kernel<false>, dim3(blocks), dim3(kBlkThreads), 0, s, x, w, bias, du,
+      hipLaunchKernelGGL(m2rnn_conv4_silu_bwd_kernel<false>, dim3((unsigned)blocks), dim3(kBlkThreads), 0, s, x, w, bias, du,
                          (int)B, (int)T, (int)C, dx, part);
   }
   reduce_rows(part, parts, 5 * C, 5 * C, dw, 4 * C, dbias, scratch, s);

@@ -44,6 +44,21 @@ __device__ __forceinline__ void store4(void* base, long i, float4 v) {
   }
 }
 
+// store4 as a non-temporal store: the caches need not keep a stream written once and not read
+// back by the kernel.
+template <bool BF16>
+__device__ __forceinline__ void store4_nt(void* base, long i, const float (&o)[4]) {
+  if constexpr (BF16) {
+    typedef unsigned u2v __attribute__((ext_vector_type(2)));
+    const u2v v = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+    __builtin_nontemporal_store(v, (u2v*)((uint16_t*)base + i));
+  } else {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const f4v v = {o[0], o[1], o[2], o[3]};
+    __builtin_nontemporal_store(v, (f4v*)((float*)base + i));
+  }
+}
+
 // Sum over the workgroup (kBlkThreads threads) of a pair of values, in a fixed order; every
 // thread receives the totals.  `red` holds 2 * (kBlkThreads / 64) floats.
 __device__ __forceinline__ float2 block_sum2(float a, float b, float* red) {
@@ -299,23 +314,37 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_sum_slices_kernel(const flo
 
 // ------------------------------------------------------------------ causal conv4 + SiLU (§2.3)
 
-constexpr int kConvChunk = 64;  // steps per thread (a sliding window over time)
-constexpr int kConvBatch = 4;   // steps whose loads are issued together
+// Steps per thread (a sliding window over time).  The backward takes longer chunks: half the
+// partial sums of dw and dbias, and fewer re-read steps at the chunk edges.
+constexpr int kConvChunkFwd = 64;
+constexpr int kConvChunkBwd = 128;
+constexpr int kConvBatch = 4;  // steps whose loads are issued together
 
-// Thread (b, chunk of kConvChunk steps, 4 channels c4): pre_t = sum_i w[c][i] x_{t-3+i} + bias[c],
+// The threads of a wave share one (b, chunk) and take 64 consecutive groups of 4 channels; a row
+// of C/4 groups spans ceil(C/256) waves.  b, chunk and the step range are then uniform over the
+// wave (scalar registers and branches).  False for a lane with nothing to do.
+template <int CHUNK>
+__device__ __forceinline__ bool conv_pos(int B, int T, int C, int& b, int& chunk, int& c4) {
+  const int C4 = C / 4;
+  const int nchunk = (T + CHUNK - 1) / CHUNK;
+  const int wpr = (C4 + 63) / 64;
+  const int gw = (int)blockIdx.x * (kBlkThreads / 64) + __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
+  const int bc = gw / wpr;
+  c4 = (gw - bc * wpr) * 64 + (int)(threadIdx.x & 63);
+  chunk = bc % nchunk;
+  b = bc / nchunk;
+  return b < B && c4 < C4;
+}
+
+// Thread (b, chunk of kConvChunkFwd steps, 4 channels c4): pre_t = sum_i w[c][i] x_{t-3+i} + bias[c],
 // u_t = SiLU(pre_t), with x_t = 0 for t < 0.  Layout [B, T, C]; C is a multiple of 4.
 template <bool BF16>
 __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_fwd_kernel(const void* __restrict__ x,
                                                                             const float* __restrict__ w,
                                                                             const float* __restrict__ bias, int B,
                                                                             int T, int C, void* __restrict__ u) {
-  const int C4 = C / 4;
-  const int nchunk = (T + kConvChunk - 1) / kConvChunk;
-  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (long)B * nchunk * C4) return;
-  const int c4 = (int)(gid % C4);
-  const int chunk = (int)((gid / C4) % nchunk);
-  const int b = (int)(gid / ((long)C4 * nchunk));
+  int b, chunk, c4;
+  if (!conv_pos<kConvChunkFwd>(B, T, C, b, chunk, c4)) return;
   const int c = 4 * c4;
   float wk[4][4];  // [channel][tap]
 #pragma unroll
@@ -325,8 +354,8 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_fwd_kernel(const
   }
   const float4 bv = bias ? *(const float4*)(bias + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   const float bs[4] = {bv.x, bv.y, bv.z, bv.w};
-  const int t0 = chunk * kConvChunk;
-  const int t1 = min(T, t0 + kConvChunk);
+  const int t0 = chunk * kConvChunkFwd;
+  const int t1 = min(T, t0 + kConvChunkFwd);
   const long row = (long)b * T;
   // window: xs[0..2] = x_{t-3..t-1}
   float xs[3][4];
@@ -336,12 +365,18 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_fwd_kernel(const
     const float4 v = src >= 0 ? load4<BF16>(x, (row + src) * C + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     xs[i][0] = v.x; xs[i][1] = v.y; xs[i][2] = v.z; xs[i][3] = v.w;
   }
-  // Eight steps' loads are issued together, then consumed in order.
-  for (int tb = t0; tb < t1; tb += kConvBatch) {
-    float4 xv[kConvBatch];
+  // The loads run one batch of kConvBatch steps ahead of the arithmetic, so a wave always has a
+  // batch in flight.  A step past the thread's last one re-reads the last (no branch, no extra
+  // HBM traffic).
+  auto issue = [&](int tb, float4(&o)[kConvBatch]) {
 #pragma unroll
-    for (int k = 0; k < kConvBatch; ++k)
-      xv[k] = tb + k < t1 ? load4<BF16>(x, (row + tb + k) * C + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int k = 0; k < kConvBatch; ++k) o[k] = load4<BF16>(x, (row + min(tb + k, t1 - 1)) * C + c);
+  };
+  float4 xv[kConvBatch];
+  issue(t0, xv);
+  for (int tb = t0; tb < t1; tb += kConvBatch) {
+    float4 xn[kConvBatch];
+    issue(tb + kConvBatch, xn);
 #pragma unroll
     for (int k = 0; k < kConvBatch; ++k) {
       if (tb + k < t1) {
@@ -356,15 +391,17 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_fwd_kernel(const
           xs[1][e] = xs[2][e];
           xs[2][e] = xc[e];
         }
-        store4<BF16>(u, (row + tb + k) * C + c, make_float4(o[0], o[1], o[2], o[3]));
+        store4_nt<BF16>(u, (row + tb + k) * C + c, o);
       }
     }
+#pragma unroll
+    for (int k = 0; k < kConvBatch; ++k) xv[k] = xn[k];
   }
 }
 
-// Backward, same thread layout.  dpre_t = du_t SiLU'(pre_t); dx_s = sum_i w[c][i] dpre_{s+3-i};
-// the thread's partials of dw[c][i] = sum dpre_t x_{t-3+i} and dbias[c] = sum dpre_t go to
-// part[(b * nchunk + chunk)] as [C][4] taps followed by C biases.
+// Backward, same layout with chunks of kConvChunkBwd steps.  dpre_t = du_t SiLU'(pre_t),
+// dx_s = sum_i w[c][i] dpre_{s+3-i}; the thread's partials of dw[c][i] = sum dpre_t x_{t-3+i} and
+// dbias[c] = sum dpre_t go to part[(b * nchunk + chunk)] as [C][4] taps followed by C biases.
 template <bool BF16>
 __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_bwd_kernel(const void* __restrict__ x,
                                                                             const float* __restrict__ w,
@@ -372,13 +409,8 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_bwd_kernel(const
                                                                             const float* __restrict__ du, int B, int T,
                                                                             int C, float* __restrict__ dx,
                                                                             float* __restrict__ part) {
-  const int C4 = C / 4;
-  const int nchunk = (T + kConvChunk - 1) / kConvChunk;
-  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (long)B * nchunk * C4) return;
-  const int c4 = (int)(gid % C4);
-  const int chunk = (int)((gid / C4) % nchunk);
-  const int b = (int)(gid / ((long)C4 * nchunk));
+  int b, chunk, c4;
+  if (!conv_pos<kConvChunkBwd>(B, T, C, b, chunk, c4)) return;
   const int c = 4 * c4;
   float wk[4][4];
 #pragma unroll
@@ -388,8 +420,8 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_bwd_kernel(const
   }
   const float4 bv = bias ? *(const float4*)(bias + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   const float bs[4] = {bv.x, bv.y, bv.z, bv.w};
-  const int t0 = chunk * kConvChunk;
-  const int t1 = min(T, t0 + kConvChunk);
+  const int t0 = chunk * kConvChunkBwd;
+  const int t1 = min(T, t0 + kConvChunkBwd);
   const long row = (long)b * T;
   auto xat = [&](int t, float (&o)[4]) {
     const float4 v = (t >= 0 && t < T) ? load4<BF16>(x, (row + t) * C + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -425,16 +457,23 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_bwd_kernel(const
   }
   float aw[4][4] = {}, ab[4] = {};
   const int tend = t1 + 3;
-  for (int tb = t0; tb < tend; tb += kConvBatch) {
-    // Eight steps' x and du loads in flight together.
-    float4 xv[kConvBatch], dv[kConvBatch];
+  // x and du loads run one batch of kConvBatch steps ahead of the arithmetic.  A step at or past
+  // min(tend, T) re-reads the last one below it; such values only meet dpre = 0 (selected, so
+  // they cannot leak) and take no part in dw.
+  const int tlast = min(tend, T) - 1;
+  auto issue = [&](int tb, float4(&xo)[kConvBatch], float4(&dvo)[kConvBatch]) {
 #pragma unroll
     for (int k = 0; k < kConvBatch; ++k) {
-      const int t = tb + k;
-      const bool in = t < tend && t < T;
-      xv[k] = in ? load4<BF16>(x, (row + t) * C + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      dv[k] = in ? *(const float4*)(du + (row + t) * C + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      const long i = (row + min(tb + k, tlast)) * C + c;
+      xo[k] = load4<BF16>(x, i);
+      dvo[k] = *(const float4*)(du + i);
     }
+  };
+  float4 xv[kConvBatch], dv[kConvBatch];
+  issue(t0, xv, dv);
+  for (int tb = t0; tb < tend; tb += kConvBatch) {
+    float4 xn[kConvBatch], dn[kConvBatch];
+    issue(tb + kConvBatch, xn, dn);
 #pragma unroll
     for (int k = 0; k < kConvBatch; ++k) {
       const int t = tb + k;
@@ -461,7 +500,7 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_bwd_kernel(const
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             o[e] = wk[e][3] * dp[0][e] + wk[e][2] * dp[1][e] + wk[e][1] * dp[2][e] + wk[e][0] * dp[3][e];
-          *(float4*)(dx + (row + sidx) * C + c) = make_float4(o[0], o[1], o[2], o[3]);
+          store4_nt<false>(dx, (row + sidx) * C + c, o);
         }
 #pragma unroll
         for (int i = 0; i < 3; ++i)
@@ -472,8 +511,14 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_bwd_kernel(const
           }
       }
     }
+#pragma unroll
+    for (int k = 0; k < kConvBatch; ++k) {
+      xv[k] = xn[k];
+      dv[k] = dn[k];
+    }
   }
-  float* pp = part + (long)(b * nchunk + chunk) * C * 5;  // [4C: dw as [C][4] | C: dbias]
+  // [4C: dw as [C][4] | C: dbias]
+  float* pp = part + ((long)b * ((T + kConvChunkBwd - 1) / kConvChunkBwd) + chunk) * C * 5;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     *(float4*)(pp + (c + e) * 4) = make_float4(aw[e][0], aw[e][1], aw[e][2], aw[e][3]);

@@ -88,8 +88,11 @@ def test_out_norm_forward_and_backward(B, T, N, V, gz_dtype):
     assert e <= 1e-5, e
 
 
+# Ragged cases: C = 12 fills part of a wave; C = 328 spans two waves per row, the second partly;
+# T = 70, 129 and 300 end inside a chunk of the forward (64 steps) and of the backward (128 steps).
 @pytest.mark.parametrize("B,T,C,dtype,with_bias", [(2, 70, 12, "f32", True), (4, 2048, 1024, "bf16", True),
-                                                   (1, 3, 4, "f32", False), (3, 129, 64, "bf16", False)])
+                                                   (1, 3, 4, "f32", False), (3, 129, 64, "bf16", False),
+                                                   (2, 300, 328, "bf16", True)])
 def test_conv4_silu_forward_and_backward(B, T, C, dtype, with_bias):
     import matrix_state_nonlinear_m2rnn_amd as m2
     r = rng(T + C)
