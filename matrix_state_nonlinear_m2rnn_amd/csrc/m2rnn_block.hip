@@ -27,10 +27,11 @@ unsigned grid_for(long count) {
   return (unsigned)(blocks > 0 ? blocks : 1);
 }
 
-constexpr int kNormRowsPer = 16;      // rows per wave of the RMSNorm backward
+constexpr int kNormRowsPer = 16;      // rows per workgroup of the RMSNorm backward
 constexpr long kGateMaxParts = 1024;  // workgroups (partial sums) of the gate backward
-constexpr int kSlice = 64;             // rows per slice of the partial-sum reduction tree
-constexpr int kNormMaxD = 4 * 64 * 32;  // features per row of the RMSNorm (32 groups of 4 per lane)
+constexpr int kSlice = 64;            // rows per slice of the partial-sum reduction tree
+// features per row of the RMSNorm: 8 groups of 4 per thread
+constexpr int kNormMaxD = 4 * kBlkThreads * 8;
 
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
@@ -179,12 +180,13 @@ int m2rnn_out_norm_fwd(int64_t rows, int64_t D, const float* y, const void* gz, 
   for (const void* p : ps)
     if (!al16(p)) return M2RNN_EINVAL;
   hipStream_t s = (hipStream_t)stream;
-  if (gz_dtype == M2RNN_DTYPE_BF16)
-    hipLaunchKernelGGL(m2rnn_out_norm_fwd_kernel<true>, dim3((unsigned)rows), dim3(kBlkThreads), 0, s, y, gz, gamma,
-                       (int)D, eps, out);
-  else
-    hipLaunchKernelGGL(m2rnn_out_norm_fwd_kernel<false>, dim3((unsigned)rows), dim3(kBlkThreads), 0, s, y, gz, gamma,
-                       (int)D, eps, out);
+  // groups of 4 features per thread: 2 up to 2048 features, else 8 (kNormMaxD)
+  static_assert(kNormMaxD <= 4 * kBlkThreads * 8, "RMSNorm forward: row wider than its registers");
+  const bool bf = gz_dtype == M2RNN_DTYPE_BF16;
+  const auto kern = D <= 4 * kBlkThreads * 2
+                        ? (bf ? &m2rnn_out_norm_fwd_kernel<true, 2> : &m2rnn_out_norm_fwd_kernel<false, 2>)
+                        : (bf ? &m2rnn_out_norm_fwd_kernel<true, 8> : &m2rnn_out_norm_fwd_kernel<false, 8>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(kBlkThreads), 0, s, y, gz, gamma, (int)D, eps, out);
   return status(hipGetLastError());
 }
 
@@ -207,7 +209,7 @@ int m2rnn_out_norm_bwd(int64_t rows, int64_t D, const float* y, const void* gz, 
   for (const void* p : ps)
     if (p && !al16(p)) return M2RNN_EINVAL;
   hipStream_t s = (hipStream_t)stream;
-  const long parts = ceil_div(rows, kNormRowsPer);  // one wave per kNormRowsPer rows
+  const long parts = ceil_div(rows, kNormRowsPer);  // one workgroup per kNormRowsPer rows
   if (parts == 0) {
     reduce_rows(nullptr, 0, D, D, dgamma, D, nullptr, nullptr, s);
     return status(hipGetLastError());
@@ -215,10 +217,12 @@ int m2rnn_out_norm_bwd(int64_t rows, int64_t D, const float* y, const void* gz, 
   if (!workspace || workspace_bytes < norm_ws_bytes(rows, D) || !al16(workspace)) return M2RNN_EWORKSPACE;
   float* part = (float*)workspace;
   float* scratch = (float*)((char*)workspace + round_up256((size_t)parts * D * sizeof(float)));
-  const dim3 grid((unsigned)ceil_div(parts, kBlkThreads / 64));
+  const dim3 grid((unsigned)parts);
   const bool bf = gz_dtype == M2RNN_DTYPE_BF16;
-  const auto kern = D <= 4 * 64 * 8 ? (bf ? &m2rnn_out_norm_bwd_kernel<true, 8> : &m2rnn_out_norm_bwd_kernel<false, 8>)
-                                    : (bf ? &m2rnn_out_norm_bwd_kernel<true, 32> : &m2rnn_out_norm_bwd_kernel<false, 32>);
+  // groups of 4 features per thread, as in the forward
+  const auto kern = D <= 4 * kBlkThreads * 2
+                        ? (bf ? &m2rnn_out_norm_bwd_kernel<true, 2> : &m2rnn_out_norm_bwd_kernel<false, 2>)
+                        : (bf ? &m2rnn_out_norm_bwd_kernel<true, 8> : &m2rnn_out_norm_bwd_kernel<false, 8>);
   hipLaunchKernelGGL(kern, grid, dim3(kBlkThreads), 0, s, y, gz, gamma, (int)D, eps, dout, (long)rows, kNormRowsPer,
                      dy, dgz, part);
   reduce_rows(part, parts, D, D, dgamma, D, nullptr, scratch, s);

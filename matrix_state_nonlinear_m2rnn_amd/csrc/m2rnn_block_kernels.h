@@ -175,8 +175,9 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_col_sum2_kernel(const float
 // ------------------------------------------------------------------ output gate + RMSNorm (§2.3, App. C)
 
 // One workgroup per row (token) of D features: x = y (.) SiLU(gz), out = gamma (.) x / sqrt(mean x^2 + eps).
-// Thread t owns the 4-feature groups t, t + 256, ...; D is a multiple of 4.
-template <bool BF16>
+// Thread t owns the 4-feature groups t, t + 256, ... (QMAX of them at most; D is a multiple of 4)
+// and keeps their x in registers between the sum of squares and the scaling.
+template <bool BF16, int QMAX>
 __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_fwd_kernel(const float* __restrict__ y,
                                                                           const void* __restrict__ gz,
                                                                           const float* __restrict__ gamma, int D,
@@ -185,89 +186,93 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_fwd_kernel(const f
   const long row = blockIdx.x;
   const long base = row * D;
   float ss = 0.0f;
-  for (int j = 4 * threadIdx.x; j < D; j += 4 * kBlkThreads) {
-    const float4 yv = *(const float4*)(y + base + j);
-    const float4 g = load4<BF16>(gz, base + j);
-    const float x0 = yv.x * siluf_(g.x), x1 = yv.y * siluf_(g.y), x2 = yv.z * siluf_(g.z), x3 = yv.w * siluf_(g.w);
-    ss += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+  float4 xk[QMAX];
+#pragma unroll
+  for (int q = 0; q < QMAX; ++q) {
+    const int j = 4 * ((int)threadIdx.x + kBlkThreads * q);
+    if (j < D) {
+      const float4 yv = *(const float4*)(y + base + j);
+      const float4 g = load4<BF16>(gz, base + j);
+      xk[q] = make_float4(yv.x * siluf_(g.x), yv.y * siluf_(g.y), yv.z * siluf_(g.z), yv.w * siluf_(g.w));
+      ss += xk[q].x * xk[q].x + xk[q].y * xk[q].y + xk[q].z * xk[q].z + xk[q].w * xk[q].w;
+    }
   }
   const float s = 1.0f / sqrtf(block_sum2(ss, 0.0f, red).x / (float)D + eps);
-  for (int j = 4 * threadIdx.x; j < D; j += 4 * kBlkThreads) {
-    const float4 yv = *(const float4*)(y + base + j);
-    const float4 g = load4<BF16>(gz, base + j);
-    const float4 gm = *(const float4*)(gamma + j);
-    *(float4*)(out + base + j) = make_float4(gm.x * yv.x * siluf_(g.x) * s, gm.y * yv.y * siluf_(g.y) * s,
-                                             gm.z * yv.z * siluf_(g.z) * s, gm.w * yv.w * siluf_(g.w) * s);
+#pragma unroll
+  for (int q = 0; q < QMAX; ++q) {
+    const int j = 4 * ((int)threadIdx.x + kBlkThreads * q);
+    if (j < D) {
+      const float4 gm = *(const float4*)(gamma + j);
+      const float o[4] = {gm.x * xk[q].x * s, gm.y * xk[q].y * s, gm.z * xk[q].z * s, gm.w * xk[q].w * s};
+      store4_nt<false>(out, base + j, o);
+    }
   }
 }
 
-// Backward (Appendix C), one wave per `rows_per` consecutive rows, reductions within the wave:
+// Backward (Appendix C), one workgroup per `rows_per` consecutive rows, in the forward's layout:
 // p = gamma (.) dout, r = sum p x, dx = s p - r s^3 x / D; dy = dx (.) SiLU(gz);
-// dgz = dx (.) y (.) SiLU'(gz).  The wave's partial of dgamma = sum over its rows of dout (.) x s goes
-// to dgamma_part[wave][D].  Lane l owns the 4-feature groups l, l + 64, ... (QMAX of them at most).
+// dgz = dx (.) y (.) SiLU'(gz).  The workgroup's partial of dgamma = sum over its rows of
+// dout (.) x s goes to dgamma_part[workgroup][D].  With at most 2 groups per thread the next row's
+// loads are in flight while the current row is reduced and written.
 template <bool BF16, int QMAX>
 __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_bwd_kernel(
     const float* __restrict__ y, const void* __restrict__ gz, const float* __restrict__ gamma, int D, float eps,
     const float* __restrict__ dout, long rows, int rows_per, float* __restrict__ dy, float* __restrict__ dgz,
     float* __restrict__ dgamma_part) {
-  const int lane = threadIdx.x & 63;
-  const long wave = (long)blockIdx.x * (kBlkThreads / 64) + (threadIdx.x >> 6);
-  const long r0 = wave * rows_per;
-  if (r0 >= rows) return;  // no barrier in this kernel
-  const long r1 = r0 + rows_per < rows ? r0 + rows_per : rows;
-  float4 acc[QMAX];
+  __shared__ float red[2 * kBlkThreads / 64];
+  constexpr bool PIPE = QMAX <= 2;
+  const int tid = threadIdx.x;
+  const long r0 = (long)blockIdx.x * rows_per;
+  const long r1 = min(rows, r0 + rows_per);
+  struct Row {
+    float4 y[QMAX], g[QMAX], d[QMAX];
+  };
+  auto load = [&](long r, Row& o) {
 #pragma unroll
-  for (int q = 0; q < QMAX; ++q) acc[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  // Up to 2048 features a row's y, gate and dout stay in registers between the two passes (the
-  // second pass would otherwise read them from HBM again); wider rows are read twice.
-  constexpr bool KEEP = QMAX <= 8;
-  float4 ykeep[KEEP ? QMAX : 1], gkeep[KEEP ? QMAX : 1], dkeep[KEEP ? QMAX : 1];
+    for (int q = 0; q < QMAX; ++q) {
+      const int j = 4 * (tid + kBlkThreads * q);
+      if (j < D) {
+        o.y[q] = *(const float4*)(y + r * D + j);
+        o.g[q] = load4<BF16>(gz, r * D + j);
+        o.d[q] = *(const float4*)(dout + r * D + j);
+      }
+    }
+  };
+  float4 gm[QMAX], acc[QMAX];
+#pragma unroll
+  for (int q = 0; q < QMAX; ++q) {
+    const int j = 4 * (tid + kBlkThreads * q);
+    gm[q] = j < D ? *(const float4*)(gamma + j) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    acc[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+  Row cur;
+  load(r0, cur);
   for (long r = r0; r < r1; ++r) {
-    const long base = r * D;
+    Row nxt;
+    if constexpr (PIPE) load(min(r + 1, r1 - 1), nxt);
     float ss = 0.0f, rp = 0.0f;
 #pragma unroll
     for (int q = 0; q < QMAX; ++q) {
-      const int j = 4 * (lane + 64 * q);
+      const int j = 4 * (tid + kBlkThreads * q);
       if (j < D) {
-        const float4 yv = *(const float4*)(y + base + j);
-        const float4 g = load4<BF16>(gz, base + j);
-        const float4 gm = *(const float4*)(gamma + j);
-        const float4 d = *(const float4*)(dout + base + j);
-        if constexpr (KEEP) {
-          ykeep[q] = yv;
-          gkeep[q] = g;
-          dkeep[q] = d;
-        }
+        const float4 yv = cur.y[q], g = cur.g[q], d = cur.d[q];
         const float x0 = yv.x * siluf_(g.x), x1 = yv.y * siluf_(g.y), x2 = yv.z * siluf_(g.z),
                     x3 = yv.w * siluf_(g.w);
         ss += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
-        rp += gm.x * d.x * x0 + gm.y * d.y * x1 + gm.z * d.z * x2 + gm.w * d.w * x3;
+        rp += gm[q].x * d.x * x0 + gm[q].y * d.y * x1 + gm[q].z * d.z * x2 + gm[q].w * d.w * x3;
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      ss += __shfl_xor(ss, o);
-      rp += __shfl_xor(rp, o);
-    }
-    const float s = 1.0f / sqrtf(ss / (float)D + eps);
-    const float c = rp * s * s * s / (float)D;
+    const float2 t = block_sum2(ss, rp, red);
+    const float s = 1.0f / sqrtf(t.x / (float)D + eps);
+    const float c = t.y * s * s * s / (float)D;
 #pragma unroll
     for (int q = 0; q < QMAX; ++q) {
-      const int j = 4 * (lane + 64 * q);
+      const int j = 4 * (tid + kBlkThreads * q);
       if (j < D) {
-        float4 yv, g, d;
-        if constexpr (KEEP) {
-          yv = ykeep[q];
-          g = gkeep[q];
-          d = dkeep[q];
-        } else {
-          yv = *(const float4*)(y + base + j);
-          g = load4<BF16>(gz, base + j);
-          d = *(const float4*)(dout + base + j);
-        }
-        const float4 gm = *(const float4*)(gamma + j);
-        const float gs[4] = {g.x, g.y, g.z, g.w}, ys[4] = {yv.x, yv.y, yv.z, yv.w};
-        const float gms[4] = {gm.x, gm.y, gm.z, gm.w}, ds[4] = {d.x, d.y, d.z, d.w};
+        const float gs[4] = {cur.g[q].x, cur.g[q].y, cur.g[q].z, cur.g[q].w};
+        const float ys[4] = {cur.y[q].x, cur.y[q].y, cur.y[q].z, cur.y[q].w};
+        const float ds[4] = {cur.d[q].x, cur.d[q].y, cur.d[q].z, cur.d[q].w};
+        const float gms[4] = {gm[q].x, gm[q].y, gm[q].z, gm[q].w};
         float oy[4], og[4], ag[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -278,19 +283,23 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_bwd_kernel(
           og[e] = dx * ys[e] * silu_gradf_(gs[e]);
           ag[e] = ds[e] * x * s;
         }
-        *(float4*)(dy + base + j) = make_float4(oy[0], oy[1], oy[2], oy[3]);
-        *(float4*)(dgz + base + j) = make_float4(og[0], og[1], og[2], og[3]);
+        store4_nt<false>(dy, r * D + j, oy);
+        store4_nt<false>(dgz, r * D + j, og);
         acc[q].x += ag[0];
         acc[q].y += ag[1];
         acc[q].z += ag[2];
         acc[q].w += ag[3];
       }
     }
+    if constexpr (PIPE)
+      cur = nxt;
+    else if (r + 1 < r1)
+      load(r + 1, cur);
   }
 #pragma unroll
   for (int q = 0; q < QMAX; ++q) {
-    const int j = 4 * (lane + 64 * q);
-    if (j < D) *(float4*)(dgamma_part + wave * D + j) = acc[q];
+    const int j = 4 * (tid + kBlkThreads * q);
+    if (j < D) *(float4*)(dgamma_part + (long)blockIdx.x * D + j) = acc[q];
   }
 }
 

@@ -61,8 +61,10 @@ def test_gate_forward_and_backward(B, T, N):
         assert e <= 1e-5, (n, e)
 
 
+# D = N V features per row: 48, 1024, 512 and 2048 take the narrow register layouts; 2304 (a ragged
+# last group) and 8192 (the widest row the library takes) the wide ones.
 @pytest.mark.parametrize("B,T,N,V,gz_dtype", [(2, 9, 3, 16, "f32"), (4, 2048, 16, 64, "bf16"), (1, 130, 4, 128, "f32"),
-                                              (2, 5, 128, 16, "bf16")])
+                                              (2, 5, 128, 16, "bf16"), (2, 4, 36, 64, "f32"), (1, 3, 64, 128, "bf16")])
 def test_out_norm_forward_and_backward(B, T, N, V, gz_dtype):
     import matrix_state_nonlinear_m2rnn_amd as m2
     r = rng(N * V + T)
