@@ -316,6 +316,80 @@ def bench_block(args) -> int:
     return 0
 
 
+def bench_fused_block(args) -> int:
+    """Times the block forward from the gate pre-activation to the normalised output: the fused
+    entry point (m2rnn_fwd_block: gate pass, scan, one epilogue pass per token) next to the three
+    separate calls it replaces (m2rnn_gate_fwd, m2rnn_fwd, m2rnn_out_norm_fwd)."""
+    import numpy as np
+    import torch
+
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    from matrix_state_nonlinear_m2rnn_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    math_mode = "f16x3" if args.math == "auto" else args.math
+    d = inputs.workload_inputs(w.name)
+    dev = torch.device("cuda:0")
+    qkv_t = torch.bfloat16 if w.qkv_dtype == "bf16" else torch.float32
+    t = {n: torch.from_numpy(np.ascontiguousarray(a)).to(dev) for n, a in d.items() if a is not None}
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(qkv_t).contiguous()
+    B, T, N, K, V = w.B, w.T, w.N, w.K, w.V
+    g = torch.Generator(device="cpu").manual_seed(4321)
+    a = (torch.randn(B, T, N, generator=g) * 2.0).to(dev)
+    alpha, beta = (torch.rand(N, generator=g) * 2.0 + 0.5).to(dev), torch.randn(N, generator=g).to(dev)
+    gz = (torch.randn(B, T, N, V, generator=g) * 2.0).to(torch.bfloat16).to(dev)
+    gamma = (torch.randn(N, V, generator=g) * 0.1 + 1.0).to(dev)
+    out = torch.empty((B, T, N, V), dtype=torch.float32, device=dev)
+    H_T = torch.empty((B, N, K, V), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, _fwd_block_ws(m2, w, math_mode, args.row_blocks)), dtype=torch.uint8, device=dev)
+
+    def fused():
+        m2.m2rnn_fwd_block(t["q"], t["k"], t["v"], a, alpha, beta, t["W"], t["w_r"], gz, gamma, None,
+                           math=math_mode, row_blocks=args.row_blocks, out=out, H_T=H_T, workspace=ws)
+
+    def unfused():
+        f = m2.m2rnn_gate_fwd(a, alpha, beta)
+        y, _ = m2.m2rnn_fwd(t["q"], t["k"], t["v"], f, t["W"], t["w_r"], None, math=math_mode,
+                            row_blocks=args.row_blocks, H_T=H_T)
+        m2.m2rnn_out_norm_fwd(y, gz, gamma, out=out)
+
+    res = {}
+    for name, fn in (("fused", fused), ("unfused", unfused)):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / args.steps
+    ms = res["fused"]
+    line = {"metric": "M²RNN block forward (gate, recurrence, output gate + RMSNorm) head-steps/sec",
+            "value": B * T * N / (ms * 1e-3), "unit": "head-steps/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": w.name, "B": B, "T": T, "N": N, "K": K, "V": V, "qkv_dtype": w.qkv_dtype,
+                       "gz_dtype": "bf16", "math": math_mode, "entry": "m2rnn_fwd_block"},
+            "unfused_ms": res["unfused"], "saved_ms": res["unfused"] - ms}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def _fwd_block_ws(m2, w, math_mode, row_blocks) -> int:
+    import ctypes
+    n = ctypes.c_size_t(0)
+    dims = m2.Dims(w.B, w.T, w.N, w.K, w.V, 1 if w.shared_qk else w.N)
+    dt = m2.DTYPE_BF16 if w.qkv_dtype == "bf16" else m2.DTYPE_F32
+    st = m2.lib().m2rnn_fwd_block_workspace_size(ctypes.byref(dims), dt, m2.MATH[math_mode], int(row_blocks),
+                                                 ctypes.byref(n))
+    if st != m2.M2RNN_OK:
+        raise RuntimeError(f"m2rnn_fwd_block_workspace_size: {m2.status_string(st)}")
+    return int(n.value)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,6 +406,8 @@ def main() -> int:
                     help="time one training step of the layer (m2rnn_fwd_ckpt + m2rnn_bwd_ckpt) on the BPTT workload")
     ap.add_argument("--block", action="store_true",
                     help="time the gate, conv4 + SiLU and output gate + RMSNorm (fwd and bwd) at the workload's shapes")
+    ap.add_argument("--fused-block", action="store_true",
+                    help="time m2rnn_fwd_block (gate, scan, fused output gate + RMSNorm) against the separate calls")
     ap.add_argument("--decode", action="store_true",
                     help="time m2rnn_decode_step on the batch-128 decode workload (its own JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -359,6 +435,8 @@ def main() -> int:
         return bench_decode(args)
     if args.block:
         return bench_block(args)
+    if args.fused_block:
+        return bench_fused_block(args)
     w = inputs.WORKLOADS[args.workload]
     math_mode = "f16x3" if args.math == "auto" else args.math
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)

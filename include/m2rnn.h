@@ -85,7 +85,7 @@ enum {
 /* Library version, as MAJOR*10000 + MINOR*100 + PATCH.  The minor number changes with every
  * change of an entry point's arguments; a caller built against this header should check that
  * m2rnn_version() == M2RNN_VERSION before calling anything else. */
-#define M2RNN_VERSION 200
+#define M2RNN_VERSION 300
 int m2rnn_version(void);
 
 /* Human-readable text for a status code (static storage). */
@@ -242,6 +242,31 @@ int m2rnn_out_norm_bwd_workspace_size(int64_t rows, int64_t D, size_t* bytes);
 int m2rnn_out_norm_bwd(int64_t rows, int64_t D, const float* y, const void* gz, int gz_dtype,
                        const float* gamma, float eps, const float* dout, float* dy, float* dgz,
                        float* dgamma, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The block's forward from the gate pre-activation to the normalised output, for inference and
+ * prefill (§2.2, §2.3 steps 2-4, Appendix C):
+ *     f = exp(-alpha softplus(a + beta)),   y = M2RNN(q, k, v, f; W, w_r, H0)  (as m2rnn_fwd),
+ *     out = gamma (.) x / sqrt(mean_j x_j^2 + eps),   x = y (.) SiLU(gz)  over the N V features of a token.
+ * Three launches: the gate into the workspace ([B,T,N], 1/V of y's size), the scan, and one
+ * epilogue pass per token that sums the scan's partial readouts, adds w_r (.) v and applies the
+ * output gate and the norm, so y is never written to HBM (when one workgroup carries all K rows
+ * the scan writes y to the workspace and the epilogue reads it once).  out is bit-identical to
+ * m2rnn_gate_fwd, m2rnn_fwd and m2rnn_out_norm_fwd in turn.  The backward needs y: a training
+ * step takes those three calls instead.
+ *   a            gate pre-activation [B,T,N] fp32; alpha, beta [N] fp32 (4-byte aligned).
+ *   gz           output gate pre-activation [B,T,N,V] (gz_dtype fp32 or bf16); gamma [N V] fp32;
+ *                eps >= 0.  N V at most 8192.
+ *   out          [B,T,N,V] fp32.  The other arguments are m2rnn_fwd's.
+ *   workspace    at least m2rnn_fwd_block_workspace_size() bytes.
+ */
+int m2rnn_fwd_block_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks,
+                                   size_t* bytes);
+int m2rnn_fwd_block(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q,
+                    const void* k, const void* v, const float* a, const float* alpha,
+                    const float* beta, const float* W, const float* w_r, const float* H0,
+                    const void* gz, int gz_dtype, const float* gamma, float eps, float* out,
+                    float* H_T, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Causal depthwise Conv1D of kernel size 4 + SiLU (§2.3, step 1), applied to each of q, k, v:

@@ -34,6 +34,7 @@ EXPORTED = (
     "m2rnn_gate_fwd", "m2rnn_gate_bwd_workspace_size", "m2rnn_gate_bwd",
     "m2rnn_out_norm_fwd", "m2rnn_out_norm_bwd_workspace_size", "m2rnn_out_norm_bwd",
     "m2rnn_conv4_silu_fwd", "m2rnn_conv4_silu_bwd_workspace_size", "m2rnn_conv4_silu_bwd",
+    "m2rnn_fwd_block_workspace_size", "m2rnn_fwd_block",
 )
 
 
@@ -52,7 +53,7 @@ class M2RNNError(RuntimeError):
 _lib = None
 
 # The C ABI version these bindings are written for (M2RNN_VERSION in include/m2rnn.h).
-ABI_VERSION = 200
+ABI_VERSION = 300
 
 
 def lib() -> ctypes.CDLL:
@@ -111,6 +112,11 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = ci
             fn.argtypes = args
+        L.m2rnn_fwd_block_workspace_size.restype = ci
+        L.m2rnn_fwd_block_workspace_size.argtypes = [dp, ci, ci, ci, ctypes.POINTER(sz)]
+        L.m2rnn_fwd_block.restype = ci
+        L.m2rnn_fwd_block.argtypes = ([dp, ci, ci, ci] + [vp] * 3 + [vp] * 3 + [vp] * 3 + [vp, ci, vp, cf]
+                                      + [vp, vp] + [vp, sz, vp])
         L.m2rnn_decode_step.restype = ci
         L.m2rnn_decode_step.argtypes = [dp, ci, ci] + [vp] * 3 + [vp] * 3 + [vp, vp, vp, vp]
         _lib = L
@@ -266,6 +272,32 @@ def m2rnn_fwd(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int = 0, 
     y, H_T, _ = _call_fwd("m2rnn_fwd", q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, workspace, stream,
                           return_state)
     return y, H_T
+
+
+def m2rnn_fwd_block(q, k, v, a, alpha, beta, W, w_r, gz, gamma, H0=None, *, eps: float = 1e-6, math="auto",
+                    row_blocks: int = 0, out=None, H_T=None, workspace=None, stream=None,
+                    return_state: bool = True) -> Tuple[object, Optional[object]]:
+    """The block forward from the gate pre-activation to the normalised output (M²RNN notes §2.2,
+    §2.3, Appendix C): f = exp(-alpha softplus(a + beta)), the recurrence, then
+    out = gamma (.) x / sqrt(mean x^2 + eps) with x = y (.) SiLU(gz) over the N V features of a
+    token, formed by the pass that sums the readouts (y never goes to HBM).  a [B,T,N] fp32; alpha, beta [N] fp32;
+    gz [B,T,N,V] fp32 or bf16; gamma [N,V] fp32; the rest as m2rnn_fwd.  Returns (out, H_T)."""
+    import torch
+    dims, dt, m, rb, out, H_T = _fwd_prepare(q, k, v, a, W, w_r, H0, out, H_T, math, row_blocks, return_state)
+    dev = q.device
+    _require(alpha, "alpha", torch.float32, (dims.N,), dev)
+    _require(beta, "beta", torch.float32, (dims.N,), dev)
+    _require(gz, "gz", (torch.float32, torch.bfloat16), (dims.B, dims.T, dims.N, dims.V), dev)
+    _require(gamma, "gamma", torch.float32, (dims.N, dims.V), dev)
+    n = ctypes.c_size_t(0)
+    _check("m2rnn_fwd_block_workspace_size",
+           lib().m2rnn_fwd_block_workspace_size(ctypes.byref(dims), dt, m, rb, ctypes.byref(n)))
+    ws = _workspace(int(n.value), dev, workspace)
+    _check("m2rnn_fwd_block", lib().m2rnn_fwd_block(
+        ctypes.byref(dims), dt, m, rb, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(alpha), _ptr(beta), _ptr(W),
+        _ptr(w_r), _ptr(H0), _ptr(gz), _dtype_code(gz), _ptr(gamma), float(eps), _ptr(out), _ptr(H_T), _ptr(ws),
+        int(n.value), _stream(stream)))
+    return out, H_T
 
 
 def m2rnn_scan_fwd(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int = 0, y=None, H_T=None,

@@ -6,6 +6,7 @@
 #include <unordered_map>
 
 #include "../../include/m2rnn.h"
+#include "m2rnn_block_launch.h"
 #include "m2rnn_bwd_kernel.h"
 #include "m2rnn_decode_kernel.h"
 #include "m2rnn_select.h"
@@ -206,7 +207,8 @@ struct FwdCall {
   float* ckpt = nullptr;  // optional: the backward's checkpoints (every ckpt_interval(V) steps)
 };
 
-// Validates a forward call; on success fills the resolved math mode and row blocks.
+// Validates a forward call and fills the resolved math mode and row blocks (also when the only
+// fault is the workspace, M2RNN_EWORKSPACE, the last check).
 int check_fwd(const FwdCall& c, int* math_out, int* rb_out) {
   int st = check_dims(c.d, c.qkv_dtype);
   if (st) return st;
@@ -225,10 +227,10 @@ int check_fwd(const FwdCall& c, int* math_out, int* rb_out) {
   }
   const int rb = plan_row_blocks(d, math, bf16, MODE_FWD, c.row_blocks);
   if (rb < 0) return c.row_blocks > 0 && (d->K / 16) % c.row_blocks != 0 ? M2RNN_EINVAL : M2RNN_EUNSUPPORTED;
-  const size_t need = empty ? 0 : fwd_partial_bytes(d, rb, math);
-  if (need > 0 && (!c.ws || c.ws_bytes < need || !aligned16(c.ws))) return M2RNN_EWORKSPACE;
   *math_out = math;
   *rb_out = rb;
+  const size_t need = empty ? 0 : fwd_partial_bytes(d, rb, math);
+  if (need > 0 && (!c.ws || c.ws_bytes < need || !aligned16(c.ws))) return M2RNN_EWORKSPACE;
   return M2RNN_OK;
 }
 
@@ -398,6 +400,74 @@ int m2rnn_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, c
   st = launch_scan(c, m, rb);
   if (st) return st;
   return launch_finish(c, m, rb);
+}
+
+// The block forward's workspace: the gate f [B,T,N], then the scan's readout planes (S > 1) or y
+// (S = 1), which the epilogue reads once.
+size_t fwd_block_f_bytes(const m2rnn_dims* d) { return round_up((size_t)d->B * d->T * d->N * sizeof(float)); }
+
+size_t fwd_block_ws_bytes(const m2rnn_dims* d, int rb, int math) {
+  if (d->B == 0 || d->N == 0 || d->T == 0) return 0;
+  const size_t planes = fwd_partial_bytes(d, rb, math);
+  return fwd_block_f_bytes(d) + (planes > 0 ? planes : round_up((size_t)d->B * d->T * d->N * d->V * sizeof(float)));
+}
+
+int m2rnn_fwd_block_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks,
+                                   size_t* bytes) {
+  if (!bytes) return M2RNN_EINVAL;
+  int st = check_dims(dims, qkv_dtype);
+  if (st) return st;
+  const int m = resolve_math(math);
+  if (m < 0 || row_blocks < 0) return M2RNN_EINVAL;
+  const int rb = plan_row_blocks(dims, m, qkv_dtype == M2RNN_DTYPE_BF16, MODE_FWD, row_blocks);
+  if (rb < 0) return row_blocks > 0 && (dims->K / 16) % row_blocks != 0 ? M2RNN_EINVAL : M2RNN_EUNSUPPORTED;
+  *bytes = fwd_block_ws_bytes(dims, rb, m);
+  return M2RNN_OK;
+}
+
+int m2rnn_fwd_block(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q, const void* k,
+                    const void* v, const float* a, const float* alpha, const float* beta, const float* W,
+                    const float* w_r, const float* H0, const void* gz, int gz_dtype, const float* gamma, float eps,
+                    float* out, float* H_T, void* workspace, size_t workspace_bytes, void* stream) {
+  // Validated as m2rnn_fwd with f = a; the workspace is checked below (the gate comes first in it).
+  FwdCall c{dims, qkv_dtype, math, row_blocks, q, k, v, a, W, w_r, H0, out, H_T, nullptr, 0,
+            (hipStream_t)stream};
+  int m = 0, rb = 0;
+  int st = check_fwd(c, &m, &rb);
+  if (st == M2RNN_EWORKSPACE) st = M2RNN_OK;  // the partial planes live after the gate
+  if (st) return st;
+  if (gz_dtype != M2RNN_DTYPE_F32 && gz_dtype != M2RNN_DTYPE_BF16) return M2RNN_EINVAL;
+  if (!(eps >= 0.0f) || eps > 1e30f) return M2RNN_EINVAL;
+  if (dims->N * dims->V > kNormMaxFeatures) return M2RNN_EUNSUPPORTED;
+  const bool work = dims->B > 0 && dims->N > 0 && dims->T > 0;
+  if (work) {
+    if (!alpha || !beta || !gz || !gamma) return M2RNN_EINVAL;
+    if (((uintptr_t)alpha | (uintptr_t)beta) & 3u) return M2RNN_EINVAL;
+    if (!aligned16(gz) || !aligned16(gamma)) return M2RNN_EINVAL;
+    const size_t need = fwd_block_ws_bytes(dims, rb, m);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return M2RNN_EWORKSPACE;
+  }
+  if (!work) return launch_scan(c, m, rb);  // T = 0: H_T = H0; B N = 0: nothing
+  // 1. the gate into the workspace.  A pass of its own: forming it in the scan's staging would put
+  //    three dependent transcendentals before every chunk's barrier.
+  float* f = (float*)workspace;
+  st = m2rnn_gate_fwd(dims->B, dims->T, dims->N, a, alpha, beta, f, stream);
+  if (st) return st;
+  // 2. the scan: partial readouts (S > 1) or y (S = 1) into the workspace after f
+  const int S = (int)readout_planes(dims, rb, m);
+  float* planes = (float*)((char*)workspace + fwd_block_f_bytes(dims));
+  c.f = f;
+  c.ws = planes;
+  c.ws_bytes = workspace_bytes - fwd_block_f_bytes(dims);
+  if (S <= 1) c.y = planes;
+  st = launch_scan(c, m, rb);
+  if (st) return st;
+  // 3. the epilogue: y, the output gate and the norm, token by token
+  const long rows = dims->B * dims->T;
+  const int D = (int)(dims->N * dims->V);
+  return hip_status((hipError_t)launch_fwd_finish_norm(
+      planes, S, rows * D, v, qkv_dtype == M2RNN_DTYPE_BF16, S > 1 ? w_r : nullptr, gz, gz_dtype == M2RNN_DTYPE_BF16,
+      gamma, rows, D, eps, out, (hipStream_t)stream));
 }
 
 int m2rnn_bwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes) {

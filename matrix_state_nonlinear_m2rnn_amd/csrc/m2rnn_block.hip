@@ -4,6 +4,7 @@
 
 #include "../../include/m2rnn.h"
 #include "m2rnn_block_kernels.h"
+#include "m2rnn_block_launch.h"
 
 using namespace m2rnn;
 
@@ -32,6 +33,7 @@ constexpr long kGateMaxParts = 1024;  // workgroups (partial sums) of the gate b
 constexpr int kSlice = 64;            // rows per slice of the partial-sum reduction tree
 // features per row of the RMSNorm: 8 groups of 4 per thread
 constexpr int kNormMaxD = 4 * kBlkThreads * 8;
+static_assert(kNormMaxD == kNormMaxFeatures, "the recurrence's entry points check rows against kNormMaxFeatures");
 
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
@@ -287,3 +289,24 @@ int m2rnn_conv4_silu_bwd(int64_t B, int64_t T, int64_t C, int dtype, const void*
 }
 
 }  // extern "C"
+
+namespace m2rnn {
+
+int launch_fwd_finish_norm(const float* part, int S, long plane, const void* v, bool v_bf16, const float* w_r,
+                           const void* gz, bool gz_bf16, const float* gamma, long rows, int D, float eps, float* out,
+                           hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const bool wide = D > 4 * kBlkThreads * 2;
+  using Kern = void (*)(const float*, int, long, const void*, const float*, const void*, const float*, int, float,
+                        float*);
+  static const Kern kerns[2][2][2] = {
+      {{m2rnn_fwd_finish_norm_kernel<false, false, 2>, m2rnn_fwd_finish_norm_kernel<false, true, 2>},
+       {m2rnn_fwd_finish_norm_kernel<true, false, 2>, m2rnn_fwd_finish_norm_kernel<true, true, 2>}},
+      {{m2rnn_fwd_finish_norm_kernel<false, false, 8>, m2rnn_fwd_finish_norm_kernel<false, true, 8>},
+       {m2rnn_fwd_finish_norm_kernel<true, false, 8>, m2rnn_fwd_finish_norm_kernel<true, true, 8>}}};
+  hipLaunchKernelGGL(kerns[wide][v_bf16][gz_bf16], dim3((unsigned)rows), dim3(kBlkThreads), 0, stream, part, S, plane,
+                     v, w_r, gz, gamma, D, eps, out);
+  return hipGetLastError();
+}
+
+}  // namespace m2rnn

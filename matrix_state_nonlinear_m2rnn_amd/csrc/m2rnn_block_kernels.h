@@ -11,20 +11,6 @@ namespace m2rnn {
 
 constexpr int kBlkThreads = 256;
 
-// e^x and ln x from the hardware's 2^x and log2 x (v_exp_f32, v_log_f32), about 1 ulp each plus the
-// rounding of the base change; 1/x from v_rcp_f32.
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-__device__ __forceinline__ float exp_(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
-__device__ __forceinline__ float log_(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
-__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + exp_(-x)); }
-// log(1 + e^x) without overflow.
-__device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.0f) + log_(1.0f + exp_(-fabsf(x))); }
-__device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
-__device__ __forceinline__ float silu_gradf_(float x) {
-  const float s = sigmoidf_(x);
-  return s * (1.0f + x * (1.0f - s));
-}
 
 template <bool BF16>
 __device__ __forceinline__ float4 load4(const void* base, long i) {
@@ -92,7 +78,7 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_gate_fwd_kernel(const float
                                                                       float* __restrict__ f) {
   for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (long)gridDim.x * blockDim.x) {
     const int n = (int)(i % N);
-    f[i] = exp_(-alpha[n] * softplusf_(a[i] + beta[n]));
+    f[i] = gate_f(a[i], alpha[n], beta[n]);
   }
 }
 
@@ -193,6 +179,55 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_fwd_kernel(const f
     if (j < D) {
       const float4 yv = *(const float4*)(y + base + j);
       const float4 g = load4<BF16>(gz, base + j);
+      xk[q] = make_float4(yv.x * siluf_(g.x), yv.y * siluf_(g.y), yv.z * siluf_(g.z), yv.w * siluf_(g.w));
+      ss += xk[q].x * xk[q].x + xk[q].y * xk[q].y + xk[q].z * xk[q].z + xk[q].w * xk[q].w;
+    }
+  }
+  const float s = 1.0f / sqrtf(block_sum2(ss, 0.0f, red).x / (float)D + eps);
+#pragma unroll
+  for (int q = 0; q < QMAX; ++q) {
+    const int j = 4 * ((int)threadIdx.x + kBlkThreads * q);
+    if (j < D) {
+      const float4 gm = *(const float4*)(gamma + j);
+      const float o[4] = {gm.x * xk[q].x * s, gm.y * xk[q].y * s, gm.z * xk[q].z * s, gm.w * xk[q].w * s};
+      store4_nt<false>(out, base + j, o);
+    }
+  }
+}
+
+// The block forward's output epilogue, one workgroup per token: y = the sum of the scan's S
+// readout planes + w_r (.) v (w_r null: the single plane already holds y), then the output gate
+// and RMSNorm exactly as m2rnn_out_norm_fwd_kernel takes them (same operations in the same
+// order, so the result is bit-identical to the two passes).  y itself never goes to HBM.
+template <bool BF16V, bool BF16G, int QMAX>
+__global__ void __launch_bounds__(kBlkThreads) m2rnn_fwd_finish_norm_kernel(
+    const float* __restrict__ part, int S, long plane, const void* __restrict__ v, const float* __restrict__ w_r,
+    const void* __restrict__ gz, const float* __restrict__ gamma, int D, float eps, float* __restrict__ out) {
+  __shared__ float red[2 * kBlkThreads / 64];
+  const long base = (long)blockIdx.x * D;
+  float ss = 0.0f;
+  float4 xk[QMAX];
+#pragma unroll
+  for (int q = 0; q < QMAX; ++q) {
+    const int j = 4 * ((int)threadIdx.x + kBlkThreads * q);
+    if (j < D) {
+      float4 yv = *(const float4*)(part + base + j);
+      for (int s = 1; s < S; ++s) {
+        const float4 p = *(const float4*)(part + (long)s * plane + base + j);
+        yv.x += p.x;
+        yv.y += p.y;
+        yv.z += p.z;
+        yv.w += p.w;
+      }
+      if (w_r) {
+        const float4 wr = *(const float4*)(w_r + j);
+        const float4 vv = load4<BF16V>(v, base + j);
+        yv.x = __builtin_fmaf(wr.x, vv.x, yv.x);
+        yv.y = __builtin_fmaf(wr.y, vv.y, yv.y);
+        yv.z = __builtin_fmaf(wr.z, vv.z, yv.z);
+        yv.w = __builtin_fmaf(wr.w, vv.w, yv.w);
+      }
+      const float4 g = load4<BF16G>(gz, base + j);
       xk[q] = make_float4(yv.x * siluf_(g.x), yv.y * siluf_(g.y), yv.z * siluf_(g.z), yv.w * siluf_(g.w));
       ss += xk[q].x * xk[q].x + xk[q].y * xk[q].y + xk[q].z * xk[q].z + xk[q].w * xk[q].w;
     }

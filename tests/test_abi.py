@@ -150,6 +150,33 @@ def test_block_entry_points_check_their_arguments():
     assert L.m2rnn_conv4_silu_bwd(1, 8, 8, 0, p, p, None, p, p, p, None, None, 0, None) == m2.M2RNN_EWORKSPACE
 
 
+def test_fused_block_forward_checks_its_arguments():
+    L = m2.lib()
+    D = m2.Dims
+    p = ctypes.c_void_p(16)
+
+    def call(dims, alpha=True, gz_dtype=0, eps=1e-6, ws=None, nbytes=0, gz=True):
+        return L.m2rnn_fwd_block(ctypes.byref(dims), 0, -1, 0, p, p, p, p, p if alpha else None, p, p, p, None,
+                                 p if gz else None, gz_dtype, p, ctypes.c_float(eps), p, None, ws, nbytes, None)
+    assert call(D(1, 4, 2, 16, 16), alpha=False) == m2.M2RNN_EINVAL
+    assert call(D(1, 4, 2, 16, 16), gz=False) == m2.M2RNN_EINVAL
+    assert call(D(1, 4, 2, 16, 16), gz_dtype=5) == m2.M2RNN_EINVAL
+    assert call(D(1, 4, 2, 16, 16), eps=-1.0) == m2.M2RNN_EINVAL
+    assert call(D(1, 4, 128, 16, 128)) == m2.M2RNN_EUNSUPPORTED          # N V = 16384 features
+    assert call(D(1, 4, 2, 16, 16)) == m2.M2RNN_EWORKSPACE                # y goes through the workspace
+    assert call(D(1, 4, 2, 16, 16), ws=p, nbytes=256 + 4 * 2 * 16 * 4 - 4) == m2.M2RNN_EWORKSPACE
+    n = ctypes.c_size_t(0)
+    # the gate f [B,T,N], then y [B,T,N,V] (one workgroup per pair) or the partial planes (rows split:
+    # K = 64, V = 32)
+    f_bytes = (2 * 10 * 3 * 4 + 255) // 256 * 256
+    assert L.m2rnn_fwd_block_workspace_size(ctypes.byref(D(2, 10, 3, 16, 16)), 0, -1, 0, ctypes.byref(n)) == 0
+    assert n.value >= f_bytes + 2 * 10 * 3 * 16 * 4
+    assert L.m2rnn_fwd_block_workspace_size(ctypes.byref(D(2, 10, 3, 64, 32)), 1, 1, 1, ctypes.byref(n)) == 0
+    assert n.value == f_bytes + m2.m2rnn_fwd_workspace_size(D(2, 10, 3, 64, 32), 1, "f16x3", 1)
+    assert L.m2rnn_fwd_block_workspace_size(ctypes.byref(D(2, 0, 3, 16, 16)), 0, -1, 0, ctypes.byref(n)) == 0
+    assert n.value == 0
+
+
 def test_checkpoint_interval():
     # every sub-segment of the backward for V <= 64, every 64-step segment at V = 128
     assert [m2.m2rnn_checkpoint_interval(m2.Dims(1, 100, 1, 16, V)) for V in (16, 32, 64, 128)] == [8, 8, 8, 64]
