@@ -11,6 +11,25 @@ namespace m2rnn {
 
 constexpr int kBlkThreads = 256;
 
+// e^x and ln x from the hardware's 2^x and log2 x (v_exp_f32, v_log_f32), about 1 ulp each plus the
+// rounding of the base change; 1/x from v_rcp_f32.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ float exp_(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float log_(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + exp_(-x)); }
+// log(1 + e^x) without overflow.
+__device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.0f) + log_(1.0f + exp_(-fabsf(x))); }
+__device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
+__device__ __forceinline__ float silu_gradf_(float x) {
+  const float s = sigmoidf_(x);
+  return s * (1.0f + x * (1.0f - s));
+}
+// The forget gate of the M2RNN block (notes §2.2): f = exp(-alpha softplus(a + beta)) from the
+// pre-activation a and the head's alpha, beta.
+__device__ __forceinline__ float gate_f(float a, float alpha, float beta) {
+  return exp_(-alpha * softplusf_(a + beta));
+}
 
 template <bool BF16>
 __device__ __forceinline__ float4 load4(const void* base, long i) {
