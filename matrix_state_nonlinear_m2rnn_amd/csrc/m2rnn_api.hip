@@ -570,7 +570,7 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
                        (const float*)(ws + L.df), S, cnt, df);
   }
   if (shared_qk_sum(d)) {
-    const long cnt = B * T * K;
+    const long cnt = B * T * K / 4;  // one thread per 4 consecutive k
     hipLaunchKernelGGL(m2rnn_bwd_sum_heads_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream,
                        (const float*)(ws + L.dq), (int)N, B * T, (int)K, dq);
     hipLaunchKernelGGL(m2rnn_bwd_sum_heads_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream,

@@ -998,17 +998,27 @@ __global__ void __launch_bounds__(256) m2rnn_bwd_sum_df_kernel(const float* __re
 }
 
 // Gradient of a query/key shared by all heads (§2.7: summed over the heads): out[bt][k] =
-// sum over n (in order) of the per-head gradients part[bt][n][k].
+// sum over n (in order) of the per-head gradients part[bt][n][k].  A thread takes 4 consecutive k
+// (K is a multiple of 16); the loads do not depend on the running sum, so they go out eight heads
+// ahead of the additions, and as non-temporal loads (each partial is read once).
 __global__ void __launch_bounds__(256) m2rnn_bwd_sum_heads_kernel(const float* __restrict__ part, int N, long rows,
                                                                    int K, float* __restrict__ out) {
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;  // index into [rows][K]
-  if (i >= rows * K) return;
-  const long bt = i / K;
-  const int kk = (int)(i % K);
-  const float* p = part + bt * N * K + kk;
-  float acc = p[0];
-  for (int n = 1; n < N; ++n) acc += p[(long)n * K];
-  out[i] = acc;
+  const int K4 = K / 4;
+  const long i4 = (long)blockIdx.x * blockDim.x + threadIdx.x;  // index into [rows][K / 4]
+  if (i4 >= rows * K4) return;
+  const long bt = i4 / K4;
+  const f32x4* p = (const f32x4*)(part + bt * N * K) + (i4 - bt * K4);
+  f32x4 acc = __builtin_nontemporal_load(p);
+  int n = 1;
+  for (; n + 8 <= N; n += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + (long)(n + u) * K4);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; n < N; ++n) acc += __builtin_nontemporal_load(p + (long)n * K4);
+  *(f32x4*)(out + 4 * i4) = acc;
 }
 
 // dW[n] = sum over (b, s) of the workgroup partials, in a fixed order.
