@@ -40,6 +40,20 @@ __device__ __forceinline__ float4 load4(const void* base, long i) {
   return *(const float4*)((const float*)base + i);
 }
 
+// load4 as a non-temporal load, for streams read once.  (It helps the RMSNorm and the conv
+// backward by 2-4%; the conv forward, whose x rows are also read by the neighbouring chunk's
+// window, runs slower with it.)
+template <bool BF16>
+__device__ __forceinline__ float4 load4_nt(const void* base, long i) {
+  if constexpr (BF16) {
+    typedef unsigned u2v __attribute__((ext_vector_type(2)));
+    const u2v r = __builtin_nontemporal_load((const u2v*)((const uint16_t*)base + i));
+    return make_float4(bf16_lo_to_f32(r[0]), bf16_hi_to_f32(r[0]), bf16_lo_to_f32(r[1]), bf16_hi_to_f32(r[1]));
+  }
+  const f32x4 t = __builtin_nontemporal_load((const f32x4*)((const float*)base + i));
+  return make_float4(t[0], t[1], t[2], t[3]);
+}
+
 template <bool BF16>
 __device__ __forceinline__ void store4(void* base, long i, float4 v) {
   if constexpr (BF16) {
@@ -196,8 +210,8 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_fwd_kernel(const f
   for (int q = 0; q < QMAX; ++q) {
     const int j = 4 * ((int)threadIdx.x + kBlkThreads * q);
     if (j < D) {
-      const float4 yv = *(const float4*)(y + base + j);
-      const float4 g = load4<BF16>(gz, base + j);
+      const float4 yv = load4_nt<false>(y, base + j);
+      const float4 g = load4_nt<BF16>(gz, base + j);
       xk[q] = make_float4(yv.x * siluf_(g.x), yv.y * siluf_(g.y), yv.z * siluf_(g.z), yv.w * siluf_(g.w));
       ss += xk[q].x * xk[q].x + xk[q].y * xk[q].y + xk[q].z * xk[q].z + xk[q].w * xk[q].w;
     }
@@ -236,13 +250,13 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_fwd_finish_norm_kernel(
       float4 yv = make_float4(ys[0], ys[1], ys[2], ys[3]);
       if (w_r) {
         const float4 wr = *(const float4*)(w_r + j);
-        const float4 vv = load4<BF16V>(v, base + j);
+        const float4 vv = load4_nt<BF16V>(v, base + j);
         yv.x = __builtin_fmaf(wr.x, vv.x, yv.x);
         yv.y = __builtin_fmaf(wr.y, vv.y, yv.y);
         yv.z = __builtin_fmaf(wr.z, vv.z, yv.z);
         yv.w = __builtin_fmaf(wr.w, vv.w, yv.w);
       }
-      const float4 g = load4<BF16G>(gz, base + j);
+      const float4 g = load4_nt<BF16G>(gz, base + j);
       xk[q] = make_float4(yv.x * siluf_(g.x), yv.y * siluf_(g.y), yv.z * siluf_(g.z), yv.w * siluf_(g.w));
       ss += xk[q].x * xk[q].x + xk[q].y * xk[q].y + xk[q].z * xk[q].z + xk[q].w * xk[q].w;
     }
@@ -282,9 +296,9 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_bwd_kernel(
     for (int q = 0; q < QMAX; ++q) {
       const int j = 4 * (tid + kBlkThreads * q);
       if (j < D) {
-        o.y[q] = *(const float4*)(y + r * D + j);
-        o.g[q] = load4<BF16>(gz, r * D + j);
-        o.d[q] = *(const float4*)(dout + r * D + j);
+        o.y[q] = load4_nt<false>(y, r * D + j);
+        o.g[q] = load4_nt<BF16>(gz, r * D + j);
+        o.d[q] = load4_nt<false>(dout, r * D + j);
       }
     }
   };
@@ -524,8 +538,8 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_bwd_kernel(const
 #pragma unroll
     for (int k = 0; k < kConvBatch; ++k) {
       const long i = (row + min(tb + k, tlast)) * C + c;
-      xo[k] = load4<BF16>(x, i);
-      dvo[k] = *(const float4*)(du + i);
+      xo[k] = load4_nt<BF16>(x, i);
+      dvo[k] = load4_nt<false>(du, i);
     }
   };
   float4 xv[kConvBatch], dv[kConvBatch];
