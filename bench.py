@@ -378,6 +378,63 @@ def bench_fused_block(args) -> int:
     return 0
 
 
+def bench_layer(args) -> int:
+    """Times one training step of the whole M²RNN layer around the recurrence: causal conv4 + SiLU
+    on q, k, v, the gate, the recurrence keeping checkpoints, the output gate + RMSNorm, then the
+    backward of each (RMSNorm, recurrence from the checkpoints, gate, the three convs), on the BPTT
+    workload's shapes with fp32 activations and random-init parameters."""
+    import numpy as np
+    import torch
+
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    from matrix_state_nonlinear_m2rnn_amd import inputs
+
+    name = args.workload if args.workload != "long_b2_h32_t16384_kv64" else "bwd_b4_h16_t4096_kv64"
+    w = inputs.WORKLOADS[name]
+    B, T, N, K, V = w.B, w.T, w.N, w.K, w.V
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(2468)
+    rn = lambda *s, sd=1.0: (torch.randn(*s, generator=g) * sd).to(dev)  # noqa: E731
+    x = {c: rn(B, T, N * (V if c == "v" else K), sd=0.7) for c in "qkv"}
+    cw = {c: rn(x[c].shape[-1], 4, sd=0.5) for c in "qkv"}
+    cb = {c: rn(x[c].shape[-1], sd=0.1) for c in "qkv"}
+    a, alpha, beta = rn(B, T, N, sd=2.0), rn(N).abs() + 0.5, rn(N)
+    W = torch.stack([torch.linalg.qr(torch.randn(V, V, generator=g))[0] for _ in range(N)]).mul(0.9).to(dev)
+    w_r, gz, gamma = rn(N, V, sd=0.3), rn(B, T, N, V, sd=2.0), rn(N, V, sd=0.1) + 1.0
+    dout = rn(B, T, N, V)
+
+    def step():
+        u = {c: m2.m2rnn_conv4_silu_fwd(x[c], cw[c], cb[c]).view(B, T, N, -1) for c in "qkv"}
+        f = m2.m2rnn_gate_fwd(a, alpha, beta)
+        y, _, ck = m2.m2rnn_fwd_ckpt(u["q"], u["k"], u["v"], f, W, w_r)
+        m2.m2rnn_out_norm_fwd(y, gz, gamma)
+        gn = m2.m2rnn_out_norm_bwd(y, gz, gamma, dout)
+        gs = m2.m2rnn_bwd_ckpt(u["q"], u["k"], u["v"], f, W, w_r, ck, gn["dy"], want_dH0=False)
+        m2.m2rnn_gate_bwd(a, alpha, beta, gs["df"])
+        for c, du in (("q", gs["dq"]), ("k", gs["dk"]), ("v", gs["dv"])):
+            m2.m2rnn_conv4_silu_bwd(x[c], cw[c], cb[c], du.view(B, T, -1))
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    line = {"metric": "M²RNN layer training step (conv4+SiLU on q,k,v, gate, recurrence, output gate + RMSNorm; "
+                      "fwd + bwd) tokens/sec",
+            "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": w.name, "B": B, "T": T, "N": N, "K": K, "V": V, "activations": "fp32",
+                       "math": "f16x3", "params": "random init"}}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def _fwd_block_ws(m2, w, math_mode, row_blocks) -> int:
     import ctypes
     n = ctypes.c_size_t(0)
@@ -408,6 +465,8 @@ def main() -> int:
                     help="time the gate, conv4 + SiLU and output gate + RMSNorm (fwd and bwd) at the workload's shapes")
     ap.add_argument("--fused-block", action="store_true",
                     help="time m2rnn_fwd_block (gate, scan, fused output gate + RMSNorm) against the separate calls")
+    ap.add_argument("--layer", action="store_true",
+                    help="time one training step of the whole layer (convs, gate, recurrence, norm; fwd + bwd)")
     ap.add_argument("--decode", action="store_true",
                     help="time m2rnn_decode_step on the batch-128 decode workload (its own JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -437,6 +496,8 @@ def main() -> int:
         return bench_block(args)
     if args.fused_block:
         return bench_fused_block(args)
+    if args.layer:
+        return bench_layer(args)
     w = inputs.WORKLOADS[args.workload]
     math_mode = "f16x3" if args.math == "auto" else args.math
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
