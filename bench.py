@@ -3,9 +3,11 @@
 
 One step = one full forward pass (all T steps of the recurrence for every (batch, head)) of the
 16K-token workload B=2, N=32 heads, T=16384, K=V=64 with bf16 q/k/v and fp32 state, on synthetic
-seeded inputs already resident in HBM.  The step runs the library's two launches (the scan and the
-readout finish) exactly as ``m2rnn_fwd`` does; HIP events on the launch stream bracket the scan
-kernel of every timed step, which gives the dominant kernel's average duration for the roofline.
+seeded inputs already resident in HBM: one ``m2rnn_fwd`` call (which runs long sequences in time
+segments, each segment's readout finish overlapping the next segment's scan).  After the timed
+region the scan kernel runs alone over the whole sequence, each launch between two HIP events on
+its stream: that gives the dominant kernel's launch duration for the roofline (``--scan-only``
+runs just that loop, for counter passes and kernel traces).
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: the recurrence of one (batch, head) pair is
 a serial chain that the library runs on a single GPU.
@@ -469,6 +471,8 @@ def main() -> int:
                     help="time one training step of the whole layer (convs, gate, recurrence, norm; fwd + bwd)")
     ap.add_argument("--decode", action="store_true",
                     help="time m2rnn_decode_step on the batch-128 decode workload (its own JSON line)")
+    ap.add_argument("--scan-only", action="store_true",
+                    help="time the forward scan kernel alone over the whole sequence (for counters and traces)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -515,33 +519,49 @@ def main() -> int:
     nbytes = m2.m2rnn_fwd_workspace_size(dims, dt, math_mode, args.row_blocks)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     common = dict(math=math_mode, row_blocks=args.row_blocks, y=y, H_T=H_T, workspace=ws)
+    fwd_in = (t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], None)
 
-    def step(ev0=None, ev1=None):
-        if ev0 is not None:
-            ev0.record()
-        m2.m2rnn_scan_fwd(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], None, **common)
-        if ev1 is not None:
-            ev1.record()
-        m2.m2rnn_scan_fwd_finish(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], None, **common)
+    def scan_loop(n):
+        """n launches of the scan alone over the whole sequence, each between two events on the
+        stream it runs on: the dominant kernel's launch duration for the roofline."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in evs:
+            e0.record()
+            m2.m2rnn_scan_fwd(*fwd_in, **common)
+            e1.record()
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in evs]
+        return sum(ms) / len(ms)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e_start.record()
-    for i in range(args.steps):
-        step(*evs[i])
-    e_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    total_ms = e_start.elapsed_time(e_end)
-    scan_ms = [a.elapsed_time(b) for a, b in evs]
-    scan_avg = sum(scan_ms) / len(scan_ms)
+    if args.scan_only:
+        # The scan kernel alone (the counter passes and the roofline's kernel trace run this).
+        for _ in range(args.warmup):
+            m2.m2rnn_scan_fwd(*fwd_in, **common)
+        torch.cuda.synchronize()
+        total_ms = None
+        scan_avg = scan_loop(args.steps)
+        wall = None
+    else:
+        # One step is m2rnn_fwd, the forward a caller runs (for long sequences: time segments whose
+        # finish passes overlap the next segment's scan).
+        print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+        for _ in range(args.warmup):
+            m2.m2rnn_fwd(*fwd_in, **common)
+        torch.cuda.synchronize()
+        e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+        w0 = time.perf_counter()
+        e_start.record()
+        for _ in range(args.steps):
+            m2.m2rnn_fwd(*fwd_in, **common)
+        e_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        total_ms = e_start.elapsed_time(e_end)
+        # After the timed region: the scan kernel alone over the whole sequence, for the roofline.
+        scan_avg = scan_loop(args.steps)
+    if total_ms is None:
+        total_ms = scan_avg * args.steps
     head_steps = B * N * T
     value = head_steps * args.steps / (total_ms * 1e-3)
     flops = 2.0 * K * V * V * head_steps
@@ -574,6 +594,7 @@ def main() -> int:
         "tokens_per_s": B * T * args.steps / (total_ms * 1e-3),
         "ns_per_recurrence_step": scan_avg * 1e6 / T,
         "scan_ms": scan_avg,
+        "timed": "m2rnn_scan_fwd alone (whole sequence)" if args.scan_only else "m2rnn_fwd",
         "wall_s": wall,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,

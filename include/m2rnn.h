@@ -106,6 +106,14 @@ int m2rnn_last_hip_error(void);
  *   y            output [B,T,N,V] (may be NULL only when T == 0 or B*N == 0).
  *   H_T          final state [B,N,K,V], or NULL to skip it.
  *   workspace    device scratch of at least m2rnn_fwd_workspace_size() bytes (NULL if that is 0).
+ *
+ * With split rows and T >= 4096, m2rnn_fwd runs the sequence in (up to four) time segments, each
+ * starting from the state the previous one ended in, and the second pass of each segment runs on
+ * a library-owned side stream (default priority, one per device) while the next segment is
+ * scanned; the call's stream waits for all of it before any later work.  This needs the two state
+ * buffers that m2rnn_fwd_workspace_size() adds for such shapes; with a smaller workspace (the
+ * partial planes only), or on a stream under graph capture, the single pass runs instead.  The
+ * two ways of running agree to rounding (about one unit in the last place of fp32).
  */
 int m2rnn_fwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks,
                              size_t* bytes);
@@ -115,11 +123,12 @@ int m2rnn_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, c
               void* stream);
 
 /*
- * The two launches m2rnn_fwd makes, exposed so that a caller can time them apart.  Same
- * arguments as m2rnn_fwd.  m2rnn_scan_fwd runs the recurrence (it writes y directly when one
- * workgroup carries all K rows, else per-workgroup partial readouts into the workspace);
- * m2rnn_scan_fwd_finish then forms y = sum of partials + w_r (.) v, and is a no-op when the scan
- * already wrote y.  Calling both, in order, on one stream is exactly m2rnn_fwd.
+ * The two launches of m2rnn_fwd's single pass, exposed so that a caller can time them apart.
+ * Same arguments as m2rnn_fwd.  m2rnn_scan_fwd runs the recurrence over the whole sequence (it
+ * writes y directly when one workgroup carries all K rows, else per-workgroup partial readouts
+ * into the workspace); m2rnn_scan_fwd_finish then forms y = sum of partials + w_r (.) v, and is a
+ * no-op when the scan already wrote y.  Calling both, in order, on one stream is exactly
+ * m2rnn_fwd's single pass (see above for the time segments of long sequences).
  */
 int m2rnn_scan_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q,
                    const void* k, const void* v, const float* f, const float* W, const float* w_r,

@@ -2,6 +2,7 @@
 // declared in include/m2rnn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <unordered_map>
 
@@ -234,6 +235,36 @@ int check_fwd(const FwdCall& c, int* math_out, int* rb_out) {
   return M2RNN_OK;
 }
 
+// The scan over steps [t0, t0 + len) of the sequence, from state H0 (null: zeros) to H_T (null:
+// not kept).  The whole sequence is t0 = 0, len = T with the call's own H0 and H_T.
+int launch_scan_seg(const FwdCall& c, int math, int rb, long t0, long len, const float* H0, float* H_T) {
+  const m2rnn_dims* d = c.d;
+  const bool bf16 = c.qkv_dtype == M2RNN_DTYPE_BF16;
+  const int rw = row_groups(d, rb, math);
+  const int S = (int)readout_planes(d, rb, math);  // workgroups per (b, n), one readout plane each
+  const long qk_row = qk_heads(d) * d->K, v_row = d->N * d->V;
+  const size_t esz = bf16 ? 2 : 4;
+  FwdArgs a{};
+  a.q = (const char*)c.q + t0 * qk_row * esz;
+  a.k = (const char*)c.k + t0 * qk_row * esz;
+  a.v = (const char*)c.v + t0 * v_row * esz;
+  a.f = c.f + t0 * d->N;
+  a.W = c.W; a.w_r = c.w_r; a.H0 = H0;
+  a.y = (S > 1 ? (float*)c.ws : c.y) + t0 * v_row;
+  a.H_T = H_T;
+  a.ckpt = t0 == 0 && len == d->T ? c.ckpt : nullptr;
+  a.B = (int)d->B; a.T = (int)len; a.N = (int)d->N; a.K = (int)d->K;
+  a.Nqk = qk_heads(d);
+  a.S = S;
+  a.seg = a.ckpt ? ckpt_interval((int)d->V) : 0;
+  a.Ts = (int)d->T;
+  const void* kern = fwd_kernel(math, (int)d->V, rb, rw, bf16, MODE_FWD);
+  if (!kern) return M2RNN_EUNSUPPORTED;
+  void* args[] = {&a};
+  const dim3 grid((unsigned)(d->B * d->N * S)), block((unsigned)(4 * d->V * rw));
+  return hip_status(hipLaunchKernel(kern, grid, block, args, 0, c.stream));
+}
+
 int launch_scan(const FwdCall& c, int math, int rb) {
   const m2rnn_dims* d = c.d;
   if (d->B == 0 || d->N == 0) return M2RNN_OK;
@@ -245,36 +276,112 @@ int launch_scan(const FwdCall& c, int math, int rb) {
     // Nothing to scan: H_T = H0 (or zeros); there are no segments to checkpoint.
     return fill(c.H_T, c.H0, d->B * d->N * d->K * d->V, c.stream);
   }
-  FwdArgs a{};
-  a.q = c.q; a.k = c.k; a.v = c.v; a.f = c.f; a.W = c.W; a.w_r = c.w_r; a.H0 = c.H0;
-  a.y = planes > 1 ? (float*)c.ws : c.y;
-  a.H_T = c.H_T;
-  a.ckpt = c.ckpt;
-  a.B = (int)d->B; a.T = (int)d->T; a.N = (int)d->N; a.K = (int)d->K;
-  a.Nqk = qk_heads(d);
-  a.S = S;
-  a.seg = c.ckpt ? ckpt_interval((int)d->V) : 0;
-  const void* kern = fwd_kernel(math, (int)d->V, rb, rw, bf16, MODE_FWD);
-  if (!kern) return M2RNN_EUNSUPPORTED;
-  void* args[] = {&a};
-  const dim3 grid((unsigned)(d->B * d->N * S)), block((unsigned)(4 * d->V * rw));
-  return hip_status(hipLaunchKernel(kern, grid, block, args, 0, c.stream));
+  return launch_scan_seg(c, math, rb, 0, d->T, c.H0, c.H_T);
+}
+
+// The finish pass over steps [t0, t0 + len) of every batch entry (the whole tensor: t0 = 0, len = T).
+int launch_finish_seg(const FwdCall& c, int math, int rb, long t0, long len, hipStream_t stream) {
+  const m2rnn_dims* d = c.d;
+  const int S = (int)readout_planes(d, rb, math);
+  const long row = d->N * d->V, plane = d->B * d->T * row;
+  const bool whole = t0 == 0 && len == d->T;
+  const long count = whole ? plane : len * row;  // elements per row of blocks
+  const dim3 grid((unsigned)((count / 4 + 255) / 256), whole ? 1u : (unsigned)d->B);
+  const long bstride = whole ? 0 : d->T * row;
+  if (c.qkv_dtype == M2RNN_DTYPE_BF16)
+    hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<true>, grid, dim3(256), 0, stream, (const float*)c.ws, S, plane, c.v,
+                       c.w_r, (int)d->N, (int)d->V, c.y, count, bstride, t0 * row);
+  else
+    hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<false>, grid, dim3(256), 0, stream, (const float*)c.ws, S, plane, c.v,
+                       c.w_r, (int)d->N, (int)d->V, c.y, count, bstride, t0 * row);
+  return hip_status(hipGetLastError());
 }
 
 int launch_finish(const FwdCall& c, int math, int rb) {
   const m2rnn_dims* d = c.d;
   if (d->B == 0 || d->N == 0 || d->T == 0) return M2RNN_OK;
-  const int S = (int)readout_planes(d, rb, math);
-  if (S <= 1) return M2RNN_OK;
-  const long plane = d->B * d->T * d->N * d->V;
-  const unsigned blocks = (unsigned)((plane / 4 + 255) / 256);
-  if (c.qkv_dtype == M2RNN_DTYPE_BF16)
-    hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<true>, dim3(blocks), dim3(256), 0, c.stream, (const float*)c.ws, S,
-                       plane, c.v, c.w_r, (int)d->N, (int)d->V, c.y);
-  else
-    hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<false>, dim3(blocks), dim3(256), 0, c.stream, (const float*)c.ws, S,
-                       plane, c.v, c.w_r, (int)d->N, (int)d->V, c.y);
-  return hip_status(hipGetLastError());
+  if (readout_planes(d, rb, math) <= 1) return M2RNN_OK;
+  return launch_finish_seg(c, math, rb, 0, d->T, c.stream);
+}
+
+// Time segments of m2rnn_fwd for long sequences with split rows: each segment's finish pass runs
+// on a side stream while the next segment is scanned (the scan keeps one wave per SIMD, so the
+// finish pass's waves use the free slots), instead of the whole finish pass after the whole scan.
+// The state goes from one segment to the next through two buffers after the partial planes.
+constexpr int kFwdSegs = 4;
+constexpr long kFwdSegMinT = 4096;
+
+bool fwd_segmentable(const m2rnn_dims* d, int rb, int math) {
+  return d->T >= kFwdSegMinT && d->B * d->N > 0 && d->B <= 65535 && readout_planes(d, rb, math) > 1;
+}
+
+size_t fwd_seg_state_bytes(const m2rnn_dims* d) {
+  return round_up((size_t)d->B * d->N * d->K * d->V * sizeof(float));
+}
+
+// m2rnn_fwd's workspace: the partial planes, and the segment states when it segments.
+size_t fwd_ws_bytes(const m2rnn_dims* d, int rb, int math) {
+  if (d->B == 0 || d->N == 0) return 0;
+  return fwd_partial_bytes(d, rb, math) + (fwd_segmentable(d, rb, math) ? 2 * fwd_seg_state_bytes(d) : 0);
+}
+
+// The side stream (default priority, non-blocking) and events of the current device, made on
+// first use; null when they cannot be made.  Callers hold g_side_mu.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t ev[kFwdSegs + 1] = {};
+  int state = 0;  // 0: not made yet, 1: ready, -1: failed
+};
+std::mutex g_side_mu;
+
+SideStream* side_stream_locked() {
+  static std::unordered_map<int, SideStream> streams;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  SideStream& e = streams[dev];
+  if (e.state == 0) {
+    e.state = -1;
+    if (hipStreamCreateWithFlags(&e.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    for (hipEvent_t& ev : e.ev)
+      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return nullptr;
+    e.state = 1;
+  }
+  return e.state == 1 ? &e : nullptr;
+}
+
+// The segmented forward; returns 1 when it does not apply (a stream under graph capture, or no
+// side stream), and the caller then runs the single scan and finish pass.
+int fwd_segmented(const FwdCall& c, int math, int rb) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(c.stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return 1;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* side = side_stream_locked();
+  if (!side) return 1;
+  const m2rnn_dims* d = c.d;
+  const long L = ((d->T + kFwdSegs - 1) / kFwdSegs + 31) / 32 * 32;  // at most kFwdSegs segments
+  char* hb = (char*)c.ws + fwd_partial_bytes(d, rb, math);
+  float* hbuf[2] = {(float*)hb, (float*)(hb + fwd_seg_state_bytes(d))};
+  const float* H0 = c.H0;
+  int st = M2RNN_OK, i = 0;
+  bool forked = false;
+  for (long t0 = 0; t0 < d->T && st == M2RNN_OK; t0 += L, ++i) {
+    const long len = std::min(L, d->T - t0);
+    float* HT = t0 + len >= d->T ? c.H_T : hbuf[i & 1];
+    st = launch_scan_seg(c, math, rb, t0, len, H0, HT);
+    if (st) break;
+    st = record_hip_status(hipEventRecord(side->ev[i], c.stream));
+    if (!st) st = record_hip_status(hipStreamWaitEvent(side->s, side->ev[i], 0));
+    if (st) break;
+    forked = true;
+    st = launch_finish_seg(c, math, rb, t0, len, side->s);
+    H0 = HT;
+  }
+  if (forked) {  // the call's stream waits for every finish pass, also after an error
+    const int j = record_hip_status(hipEventRecord(side->ev[kFwdSegs], side->s));
+    const int k = j ? j : record_hip_status(hipStreamWaitEvent(c.stream, side->ev[kFwdSegs], 0));
+    if (!st) st = k;
+  }
+  return st;
 }
 
 // ---------------------------------------------------------------- backward
@@ -367,7 +474,7 @@ int m2rnn_fwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, in
   if (m < 0 || row_blocks < 0) return M2RNN_EINVAL;
   const int rb = plan_row_blocks(dims, m, qkv_dtype == M2RNN_DTYPE_BF16, MODE_FWD, row_blocks);
   if (rb < 0) return row_blocks > 0 && (dims->K / 16) % row_blocks != 0 ? M2RNN_EINVAL : M2RNN_EUNSUPPORTED;
-  *bytes = (dims->B == 0 || dims->N == 0) ? 0 : fwd_partial_bytes(dims, rb, m);
+  *bytes = fwd_ws_bytes(dims, rb, m);
   return M2RNN_OK;
 }
 
@@ -397,6 +504,10 @@ int m2rnn_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, c
               const void* v, const float* f, const float* W, const float* w_r, const float* H0, float* y, float* H_T,
               void* workspace, size_t workspace_bytes, void* stream) {
   FWD_CALL
+  if (fwd_segmentable(dims, rb, m) && workspace_bytes >= fwd_ws_bytes(dims, rb, m)) {
+    st = fwd_segmented(c, m, rb);
+    if (st != 1) return st;
+  }
   st = launch_scan(c, m, rb);
   if (st) return st;
   return launch_finish(c, m, rb);
@@ -530,6 +641,7 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
     a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.H0 = H0;
     a.y = nullptr; a.H_T = nullptr; a.ckpt = (float*)(ws + L.ckpt);
     a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S; a.seg = ckpt_interval((int)V);
+    a.Ts = (int)T;
     a.Nqk = qk_heads(d);
     const void* kern = fwd_kernel(M2RNN_MATH_F16X3, (int)V, 1, 1, bf16, MODE_CKPT);
     if (!kern) return M2RNN_EUNSUPPORTED;
@@ -564,7 +676,7 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
   if (S > 1) {
     const long plane = B * T * N * V;
     hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<false>, dim3((unsigned)((plane / 4 + 255) / 256)), dim3(256), 0, stream,
-                       (const float*)(ws + L.dv), S, plane, (const void*)dy, w_r, (int)N, (int)V, dv);
+                       (const float*)(ws + L.dv), S, plane, (const void*)dy, w_r, (int)N, (int)V, dv, plane, 0L, 0L);
     const long cnt = B * T * N;
     hipLaunchKernelGGL(m2rnn_bwd_sum_df_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream,
                        (const float*)(ws + L.df), S, cnt, df);

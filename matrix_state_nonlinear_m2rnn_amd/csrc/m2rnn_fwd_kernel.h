@@ -43,6 +43,9 @@ struct FwdArgs {
   int Nqk;        // heads of q and k: N, or 1 when one query/key is shared by all heads
   int S;          // workgroups per (b, n)
   int seg;        // checkpoint interval, a multiple of 8 (when ckpt is set)
+  int Ts;         // steps between batch entries in q, k, v, f, y and the planes: T, or more when
+                  // the launch covers a time segment of a longer sequence (the pointers then start
+                  // at the segment's first step; checkpoints are not kept then)
 };
 
 // RW: row waves, independent groups of NT waves in one workgroup, each carrying its own row
@@ -129,15 +132,15 @@ struct ChunkRegs {
 
   __device__ __forceinline__ void load(const FwdArgs& a, int b, int nh, int row0, int t0, int tid) {
     const int valid = min(S::TC, a.T - t0);
-    const long qk_off = (((long)b * a.T + t0) * a.Nqk + (a.Nqk == 1 ? 0 : nh)) * a.K + row0;
-    const long v_off = (((long)b * a.T + t0) * a.N + nh) * V;
+    const long qk_off = (((long)b * a.Ts + t0) * a.Nqk + (a.Nqk == 1 ? 0 : nh)) * a.K + row0;
+    const long v_off = (((long)b * a.Ts + t0) * a.N + nh) * V;
     const int esz = BF16 ? 2 : 4;
     q.load((const char*)a.q + qk_off * esz, (long)a.Nqk * a.K, valid, tid);
     k.load((const char*)a.k + qk_off * esz, (long)a.Nqk * a.K, valid, rot(tid, 64));
     v.load((const char*)a.v + v_off * esz, (long)a.N * V, valid, rot(tid, 128));
     const int tf = rot(tid, 192);
     f = 1.0f;
-    if (tf < valid) f = a.f[((long)b * a.T + t0 + tf) * a.N + nh];
+    if (tf < valid) f = a.f[((long)b * a.Ts + t0 + tf) * a.N + nh];
   }
   __device__ __forceinline__ void store(float* stage, int tid) const {
     using St = Stage<V, RB * RW>;
@@ -433,8 +436,8 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
   float* ybase = nullptr;  // y (S == 1) or this row group's partial plane, at [b, 0, nh, 0]
   int ybytes = 0;
   if constexpr (MODE == MODE_FWD) {
-    const long plane = (long)a.B * a.T * a.N * V;
-    ybase = a.y + (planes > 1 ? (long)s * plane : 0) + ((long)b * a.T * a.N + nh) * V;
+    const long plane = (long)a.B * a.Ts * a.N * V;
+    ybase = a.y + (planes > 1 ? (long)s * plane : 0) + ((long)b * a.Ts * a.N + nh) * V;
     // Element (t, nh, c) is valid iff t < T, i.e. iff it lies below (T N V - nh V) floats from ybase.
     ybytes = (a.T * a.N - nh) * V * 4;
   }
@@ -780,17 +783,20 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
   }
 }
 
-// y = sum_s partial_s + w_r (.) v, elementwise over [B,T,N,V] (4 elements per thread).  The planes
-// are read once and y written once: non-temporal accesses keep them from displacing each other in
+// y = sum_s partial_s + w_r (.) v, elementwise over [B,T,N,V] (4 elements per thread): for batch
+// entry blockIdx.y, the `count` elements from off0 + blockIdx.y * bstride (the whole tensor with
+// one row of blocks and bstride = 0, or a time segment of every batch entry).  The planes are
+// read once and y written once: non-temporal accesses keep them from displacing each other in
 // the caches (258 -> 224 us at B2 N32 T16384 K=V=64, S = 4).
 template <bool BF16IN>
 __global__ void __launch_bounds__(256) m2rnn_fwd_finish_kernel(const float* __restrict__ part, int S,
                                                                 long plane, const void* __restrict__ v,
                                                                 const float* __restrict__ w_r, int N, int V,
-                                                                float* __restrict__ y) {
+                                                                float* __restrict__ y, long count, long bstride,
+                                                                long off0) {
   const long i4 = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long i = i4 * 4;
-  if (i >= plane) return;
+  if (i4 * 4 >= count) return;
+  const long i = off0 + (long)blockIdx.y * bstride + i4 * 4;
   f32x4 acc = __builtin_nontemporal_load((const f32x4*)(part + i));
   for (int s = 1; s < S; ++s) acc += __builtin_nontemporal_load((const f32x4*)(part + (long)s * plane + i));
   const int colv = (int)(i % V);

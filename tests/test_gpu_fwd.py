@@ -158,3 +158,28 @@ def test_row_groups_in_a_workgroup(K, V, T, math):
     ey, eh = max_abs(y, yr), max_abs(H, Hr)
     say("errors", ey, eh)
     assert ey <= TOL[math] and eh <= TOL[math], (ey, eh)
+
+
+def test_long_sequence_time_segments():
+    # T >= 4096 with split rows: m2rnn_fwd scans time segments, each from the state the previous one
+    # ended in, with each segment's readout finish overlapping the next scan.  It must agree with the
+    # single pass (scan + finish over the whole sequence) to rounding, and with the oracle.
+    torch = torch_cuda()
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    d = inputs.make_inputs(1, 4100, 8, 64, 64, qkv_dtype="bf16", seed=31)  # the last segment is ragged
+    dd = to_device(d, "bf16")
+    say("time segments", 1, 4100, 8, 64, 64)
+    args = (dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], None)
+    y, H = m2.m2rnn_fwd(*args, math="f16x3")
+    y1, H1, ws = m2.m2rnn_scan_fwd(*args, math="f16x3")
+    m2.m2rnn_scan_fwd_finish(*args, math="f16x3", y=y1, H_T=H1, workspace=ws)
+    torch.cuda.synchronize()
+    ey, eh = float((y - y1).abs().max()), float((H - H1).abs().max())
+    say("segments vs single pass", ey, eh)
+    assert ey <= 1e-5 and eh <= 1e-5, (ey, eh)
+    y, H = y.cpu().numpy().astype(np.float64), H.cpu().numpy().astype(np.float64)
+    for (b, n), (yr, Hr) in oracle_units(d, [(0, 0), (0, 7)]).items():
+        ey, eh = max_abs(y[b, :, n], yr), max_abs(H[b, n], Hr)
+        say((b, n), ey, eh)
+        assert ey <= TOL["f16x3"] and eh <= TOL["f16x3"], ((b, n), ey, eh)
+
