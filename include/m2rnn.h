@@ -257,10 +257,11 @@ int m2rnn_out_norm_bwd(int64_t rows, int64_t D, const float* y, const void* gz, 
  * prefill (§2.2, §2.3 steps 2-4, Appendix C):
  *     f = exp(-alpha softplus(a + beta)),   y = M2RNN(q, k, v, f; W, w_r, H0)  (as m2rnn_fwd),
  *     out = gamma (.) x / sqrt(mean_j x_j^2 + eps),   x = y (.) SiLU(gz)  over the N V features of a token.
- * Three launches: the gate into the workspace ([B,T,N], 1/V of y's size), the scan, and one
- * epilogue pass per token that sums the scan's partial readouts, adds w_r (.) v and applies the
- * output gate and the norm, so y is never written to HBM (when one workgroup carries all K rows
- * the scan writes y to the workspace and the epilogue reads it once).  out is bit-identical to
+ * The gate goes into the workspace ([B,T,N], 1/V of y's size); then the scan, and one epilogue
+ * pass per token that sums the scan's partial readouts, adds w_r (.) v and applies the output
+ * gate and the norm, so y is never written to HBM (when one workgroup carries all K rows the scan
+ * writes y to the workspace and the epilogue reads it once).  Long sequences run in time segments
+ * as in m2rnn_fwd, each segment's epilogue on the side stream.  out is bit-identical to
  * m2rnn_gate_fwd, m2rnn_fwd and m2rnn_out_norm_fwd in turn.  The backward needs y: a training
  * step takes those three calls instead.
  *   a            gate pre-activation [B,T,N] fp32; alpha, beta [N] fp32 (4-byte aligned).

@@ -349,9 +349,11 @@ SideStream* side_stream_locked() {
   return e.state == 1 ? &e : nullptr;
 }
 
-// The segmented forward; returns 1 when it does not apply (a stream under graph capture, or no
-// side stream), and the caller then runs the single scan and finish pass.
-int fwd_segmented(const FwdCall& c, int math, int rb) {
+// The segmented forward: the scan of each time segment on the call's stream, then
+// second(t0, len, side stream) for that segment.  Returns 1 when it does not apply (a stream under
+// graph capture, or no side stream); the caller then runs the single pass.
+template <class Second>
+int fwd_segmented(const FwdCall& c, int math, int rb, Second second) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(c.stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return 1;
   std::lock_guard<std::mutex> lock(g_side_mu);
@@ -373,7 +375,7 @@ int fwd_segmented(const FwdCall& c, int math, int rb) {
     if (!st) st = record_hip_status(hipStreamWaitEvent(side->s, side->ev[i], 0));
     if (st) break;
     forked = true;
-    st = launch_finish_seg(c, math, rb, t0, len, side->s);
+    st = second(t0, len, side->s);
     H0 = HT;
   }
   if (forked) {  // the call's stream waits for every finish pass, also after an error
@@ -505,7 +507,9 @@ int m2rnn_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, c
               void* workspace, size_t workspace_bytes, void* stream) {
   FWD_CALL
   if (fwd_segmentable(dims, rb, m) && workspace_bytes >= fwd_ws_bytes(dims, rb, m)) {
-    st = fwd_segmented(c, m, rb);
+    st = fwd_segmented(c, m, rb, [&](long t0, long len, hipStream_t s2) {
+      return launch_finish_seg(c, m, rb, t0, len, s2);
+    });
     if (st != 1) return st;
   }
   st = launch_scan(c, m, rb);
@@ -520,7 +524,9 @@ size_t fwd_block_f_bytes(const m2rnn_dims* d) { return round_up((size_t)d->B * d
 size_t fwd_block_ws_bytes(const m2rnn_dims* d, int rb, int math) {
   if (d->B == 0 || d->N == 0 || d->T == 0) return 0;
   const size_t planes = fwd_partial_bytes(d, rb, math);
-  return fwd_block_f_bytes(d) + (planes > 0 ? planes : round_up((size_t)d->B * d->T * d->N * d->V * sizeof(float)));
+  // planes, or y; then the states of the time segments (as m2rnn_fwd's workspace after the planes)
+  return fwd_block_f_bytes(d) + (planes > 0 ? planes : round_up((size_t)d->B * d->T * d->N * d->V * sizeof(float))) +
+         (fwd_segmentable(d, rb, math) ? 2 * fwd_seg_state_bytes(d) : 0);
 }
 
 int m2rnn_fwd_block_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks,
@@ -549,7 +555,7 @@ int m2rnn_fwd_block(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blo
   if (st) return st;
   if (gz_dtype != M2RNN_DTYPE_F32 && gz_dtype != M2RNN_DTYPE_BF16) return M2RNN_EINVAL;
   if (!(eps >= 0.0f) || eps > 1e30f) return M2RNN_EINVAL;
-  if (dims->N * dims->V > kNormMaxFeatures) return M2RNN_EUNSUPPORTED;
+  if (dims->N * dims->V > kNormMaxFeatures || dims->B > 65535) return M2RNN_EUNSUPPORTED;
   const bool work = dims->B > 0 && dims->N > 0 && dims->T > 0;
   if (work) {
     if (!alpha || !beta || !gz || !gamma) return M2RNN_EINVAL;
@@ -571,14 +577,20 @@ int m2rnn_fwd_block(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blo
   c.ws = planes;
   c.ws_bytes = workspace_bytes - fwd_block_f_bytes(dims);
   if (S <= 1) c.y = planes;
+  // 3. the epilogue: y, the output gate and the norm, token by token (over a time segment, or all)
+  const int D = (int)(dims->N * dims->V);
+  auto epilogue = [&](long t0, long len, hipStream_t s2) {
+    return hip_status((hipError_t)launch_fwd_finish_norm(planes, S, v, qkv_dtype == M2RNN_DTYPE_BF16,
+                                                         S > 1 ? w_r : nullptr, gz, gz_dtype == M2RNN_DTYPE_BF16,
+                                                         gamma, dims->B, dims->T, t0, len, D, eps, out, s2));
+  };
+  if (fwd_segmentable(dims, rb, m)) {  // the workspace holds the segment states (checked above)
+    st = fwd_segmented(c, m, rb, epilogue);
+    if (st != 1) return st;
+  }
   st = launch_scan(c, m, rb);
   if (st) return st;
-  // 3. the epilogue: y, the output gate and the norm, token by token
-  const long rows = dims->B * dims->T;
-  const int D = (int)(dims->N * dims->V);
-  return hip_status((hipError_t)launch_fwd_finish_norm(
-      planes, S, rows * D, v, qkv_dtype == M2RNN_DTYPE_BF16, S > 1 ? w_r : nullptr, gz, gz_dtype == M2RNN_DTYPE_BF16,
-      gamma, rows, D, eps, out, (hipStream_t)stream));
+  return epilogue(0, dims->T, (hipStream_t)stream);
 }
 
 int m2rnn_bwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes) {

@@ -292,20 +292,21 @@ int m2rnn_conv4_silu_bwd(int64_t B, int64_t T, int64_t C, int dtype, const void*
 
 namespace m2rnn {
 
-int launch_fwd_finish_norm(const float* part, int S, long plane, const void* v, bool v_bf16, const float* w_r,
-                           const void* gz, bool gz_bf16, const float* gamma, long rows, int D, float eps, float* out,
-                           hipStream_t stream) {
-  if (rows == 0) return hipSuccess;
+int launch_fwd_finish_norm(const float* part, int S, const void* v, bool v_bf16, const float* w_r, const void* gz,
+                           bool gz_bf16, const float* gamma, long B, long T, long t0, long len, int D, float eps,
+                           float* out, hipStream_t stream) {
+  if (B == 0 || len == 0) return hipSuccess;
+  const long plane = B * T * D;
   const bool wide = D > 4 * kBlkThreads * 2;
   using Kern = void (*)(const float*, int, long, const void*, const float*, const void*, const float*, int, float,
-                        float*);
+                        float*, long, long);
   static const Kern kerns[2][2][2] = {
       {{m2rnn_fwd_finish_norm_kernel<false, false, 2>, m2rnn_fwd_finish_norm_kernel<false, true, 2>},
        {m2rnn_fwd_finish_norm_kernel<true, false, 2>, m2rnn_fwd_finish_norm_kernel<true, true, 2>}},
       {{m2rnn_fwd_finish_norm_kernel<false, false, 8>, m2rnn_fwd_finish_norm_kernel<false, true, 8>},
        {m2rnn_fwd_finish_norm_kernel<true, false, 8>, m2rnn_fwd_finish_norm_kernel<true, true, 8>}}};
-  hipLaunchKernelGGL(kerns[wide][v_bf16][gz_bf16], dim3((unsigned)rows), dim3(kBlkThreads), 0, stream, part, S, plane,
-                     v, w_r, gz, gamma, D, eps, out);
+  hipLaunchKernelGGL(kerns[wide][v_bf16][gz_bf16], dim3((unsigned)len, (unsigned)B), dim3(kBlkThreads), 0, stream,
+                     part, S, plane, v, w_r, gz, gamma, D, eps, out, T, t0);
   return hipGetLastError();
 }
 

@@ -231,13 +231,15 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_out_norm_fwd_kernel(const f
 // The block forward's output epilogue, one workgroup per token: y = the sum of the scan's S
 // readout planes + w_r (.) v (w_r null: the single plane already holds y), then the output gate
 // and RMSNorm exactly as m2rnn_out_norm_fwd_kernel takes them (same operations in the same
-// order, so the result is bit-identical to the two passes).  y itself never goes to HBM.
+// order, so the result is bit-identical to the two passes).  y itself never goes to HBM.  Token
+// (b = blockIdx.y, t = t0 + blockIdx.x) of a [B, T] sequence.
 template <bool BF16V, bool BF16G, int QMAX>
 __global__ void __launch_bounds__(kBlkThreads) m2rnn_fwd_finish_norm_kernel(
     const float* __restrict__ part, int S, long plane, const void* __restrict__ v, const float* __restrict__ w_r,
-    const void* __restrict__ gz, const float* __restrict__ gamma, int D, float eps, float* __restrict__ out) {
+    const void* __restrict__ gz, const float* __restrict__ gamma, int D, float eps, float* __restrict__ out, long T,
+    long t0) {
   __shared__ float red[2 * kBlkThreads / 64];
-  const long base = (long)blockIdx.x * D;
+  const long base = ((long)blockIdx.y * T + t0 + blockIdx.x) * D;
   float ss = 0.0f;
   float4 xk[QMAX];
 #pragma unroll

@@ -70,6 +70,7 @@ CASES = [
     (2, 40, 8, 64, 16, "bf16", "bf16", "f16x3", 0, True, False),     # shared q/k, V = 16 (the pages' shape)
     (1, 21, 64, 16, 64, "bf16", "bf16", "f16x3", 0, False, False),   # N V = 4096 features: the wide epilogue
     (2, 17, 5, 128, 128, "bf16", "bf16", "f16x3", 0, False, False),  # K = V = 128
+    (1, 4100, 8, 64, 64, "bf16", "bf16", "f16x3", 0, False, False),   # time segments (as m2rnn_fwd's)
 ]
 
 
