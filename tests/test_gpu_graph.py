@@ -71,3 +71,36 @@ def test_side_stream_equals_default_stream():
         y1, H1 = m2.m2rnn_fwd(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], dd["H0"])
     torch.cuda.synchronize()
     assert torch.equal(y0, y1) and torch.equal(H0, H1)
+
+
+def test_graph_capture_of_a_long_forward_takes_the_single_pass():
+    # At T >= 4096 with split rows m2rnn_fwd runs time segments on a side stream; under graph
+    # capture it takes the single pass instead, so replays equal the eager scan + finish bit for bit.
+    torch = torch_cuda()
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    B, T, N, K, V = 1, 4100, 8, 64, 64
+    d = inputs.make_inputs(B, T, N, K, V, qkv_dtype="bf16", seed=4242)
+    dd = to_device(d, "bf16")
+    say("graph capture of a long forward")
+    args = (dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], None)
+    y = torch.empty((B, T, N, V), device="cuda")
+    H_T = torch.empty((B, N, K, V), device="cuda")
+    ws = torch.empty(m2.m2rnn_fwd_workspace_size(m2.Dims(B, T, N, K, V), m2.DTYPE_BF16), dtype=torch.uint8,
+                     device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        m2.m2rnn_scan_fwd(*args, y=y, H_T=H_T, workspace=ws)
+        m2.m2rnn_scan_fwd_finish(*args, y=y, H_T=H_T, workspace=ws)
+    torch.cuda.synchronize()
+    ref_y, ref_H = y.clone(), H_T.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        m2.m2rnn_fwd(*args, y=y, H_T=H_T, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.fill_(float("nan"))
+        H_T.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref_y) and torch.equal(H_T, ref_H), rep
