@@ -84,7 +84,7 @@ int check_conv(int64_t B, int64_t T, int64_t C, int dtype) {
   if (C % 4 != 0) return M2RNN_EUNSUPPORTED;
   if (B > 2147483647 || T > 2147483647 || C > 2147483647) return M2RNN_EUNSUPPORTED;
   // the kernels number their waves with an int
-  if ((double)B * ceil_div(T, kConvChunkFwd) * ceil_div(C / 4, 64) > 2147483647.0) return M2RNN_EUNSUPPORTED;
+  if ((double)B * ceil_div(T, kConvChunkMin) * ceil_div(C / 4, 64) > 2147483647.0) return M2RNN_EUNSUPPORTED;
   return M2RNN_OK;
 }
 
@@ -102,8 +102,16 @@ size_t norm_ws_bytes(int64_t rows, int64_t D) {
   return round_up256((size_t)parts * D * sizeof(float)) + round_up256(reduce_scratch(parts, D) * sizeof(float));
 }
 
+// Steps per thread of the conv kernels: `base`, halved down to kConvChunkMin while the grid (one
+// wave per batch entry, chunk and 64 channel groups) would hold fewer than kConvMinWaves waves.
+int conv_chunk(int64_t B, int64_t T, int64_t C, int base) {
+  int chunk = base;
+  while (chunk > kConvChunkMin && B * ceil_div(T, chunk) * ceil_div(C / 4, 64) < kConvMinWaves) chunk /= 2;
+  return chunk;
+}
+
 size_t conv_ws_bytes(int64_t B, int64_t T, int64_t C) {
-  const long parts = (long)B * ceil_div(T, kConvChunkBwd);
+  const long parts = (long)B * ceil_div(T, conv_chunk(B, T, C, kConvChunkBwd));
   return round_up256((size_t)parts * 5 * C * sizeof(float)) + round_up256(reduce_scratch(parts, 5 * C) * sizeof(float));
 }
 
@@ -235,7 +243,8 @@ int m2rnn_conv4_silu_fwd(int64_t B, int64_t T, int64_t C, int dtype, const void*
                          void* u, void* stream) {
   int st = check_conv(B, T, C, dtype);
   if (st) return st;
-  const long blocks = conv_blocks(B, T, C, kConvChunkFwd);
+  const int chunk = conv_chunk(B, T, C, kConvChunkFwd);
+  const long blocks = conv_blocks(B, T, C, chunk);
   if (blocks == 0) return M2RNN_OK;
   if (!x || !w || !u) return M2RNN_EINVAL;
   const void* ps[] = {x, w, bias, u};
@@ -243,11 +252,11 @@ int m2rnn_conv4_silu_fwd(int64_t B, int64_t T, int64_t C, int dtype, const void*
     if (p && !al16(p)) return M2RNN_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   if (dtype == M2RNN_DTYPE_BF16)
-    hipLaunchKernelGGL(m2rnn_conv4_silu_fwd_kernel<true>, dim3((unsigned)blocks), dim3(kBlkThreads), 0, s, x, w, bias, (int)B,
-                       (int)T, (int)C, u);
+    hipLaunchKernelGGL(m2rnn_conv4_silu_fwd_kernel<true>, dim3((unsigned)blocks), dim3(kBlkThreads), 0, s, x, w, bias,
+                       (int)B, (int)T, (int)C, chunk, u);
   else
-    hipLaunchKernelGGL(m2rnn_conv4_silu_fwd_kernel<false>, dim3((unsigned)blocks), dim3(kBlkThreads), 0, s, x, w, bias, (int)B,
-                       (int)T, (int)C, u);
+    hipLaunchKernelGGL(m2rnn_conv4_silu_fwd_kernel<false>, dim3((unsigned)blocks), dim3(kBlkThreads), 0, s, x, w, bias,
+                       (int)B, (int)T, (int)C, chunk, u);
   return status(hipGetLastError());
 }
 
@@ -265,24 +274,25 @@ int m2rnn_conv4_silu_bwd(int64_t B, int64_t T, int64_t C, int dtype, const void*
   int st = check_conv(B, T, C, dtype);
   if (st) return st;
   if (!w || !dw) return M2RNN_EINVAL;
-  const long blocks = conv_blocks(B, T, C, kConvChunkBwd);
+  const int chunk = conv_chunk(B, T, C, kConvChunkBwd);
+  const long blocks = conv_blocks(B, T, C, chunk);
   if (blocks > 0 && (!x || !du || !dx)) return M2RNN_EINVAL;
   const void* ps[] = {x, w, bias, du, dx, dw, dbias};
   for (const void* p : ps)
     if (p && !al16(p)) return M2RNN_EINVAL;
   hipStream_t s = (hipStream_t)stream;
-  const long parts = (long)B * ceil_div(T, kConvChunkBwd);
+  const long parts = (long)B * ceil_div(T, chunk);
   if (parts > 0 && (!workspace || workspace_bytes < conv_ws_bytes(B, T, C) || !al16(workspace)))
     return M2RNN_EWORKSPACE;
   float* part = (float*)workspace;
   float* scratch = parts > 0 ? (float*)((char*)workspace + round_up256((size_t)parts * 5 * C * sizeof(float))) : nullptr;
   if (blocks > 0) {
     if (dtype == M2RNN_DTYPE_BF16)
-      hipLaunchKernelGGL(m2rnn_conv4_silu_bwd_kernel<true>, dim3((unsigned)blocks), dim3(kBlkThreads), 0, s, x, w, bias, du,
-                         (int)B, (int)T, (int)C, dx, part);
+      hipLaunchKernelGGL(m2rnn_conv4_silu_bwd_kernel<true>, dim3((unsigned)blocks), dim3(kBlkThreads), 0, s, x, w, bias,
+                         du, (int)B, (int)T, (int)C, chunk, dx, part);
     else
-      hipLaunchKernelGGL(m2rnn_conv4_silu_bwd_kernel<false>, dim3((unsigned)blocks), dim3(kBlkThreads), 0, s, x, w, bias, du,
-                         (int)B, (int)T, (int)C, dx, part);
+      hipLaunchKernelGGL(m2rnn_conv4_silu_bwd_kernel<false>, dim3((unsigned)blocks), dim3(kBlkThreads), 0, s, x, w, bias,
+                         du, (int)B, (int)T, (int)C, chunk, dx, part);
   }
   reduce_rows(part, parts, 5 * C, 5 * C, dw, 4 * C, dbias, scratch, s);
   return status(hipGetLastError());

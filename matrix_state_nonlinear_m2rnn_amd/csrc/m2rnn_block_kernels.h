@@ -391,15 +391,18 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_sum_slices_kernel(const flo
 
 // Steps per thread (a sliding window over time).  The backward takes longer chunks: half the
 // partial sums of dw and dbias, and fewer re-read steps at the chunk edges.
+// (The host halves them, down to kConvChunkMin, while the grid would hold fewer than
+// kConvMinWaves waves: short or narrow inputs then still fill the chip.)
 constexpr int kConvChunkFwd = 64;
 constexpr int kConvChunkBwd = 128;
+constexpr int kConvChunkMin = 16;
+constexpr long kConvMinWaves = 2048;
 constexpr int kConvBatch = 4;  // steps whose loads are issued together
 
 // The threads of a wave share one (b, chunk) and take 64 consecutive groups of 4 channels; a row
 // of C/4 groups spans ceil(C/256) waves.  b, chunk and the step range are then uniform over the
 // wave (scalar registers and branches).  False for a lane with nothing to do.
-template <int CHUNK>
-__device__ __forceinline__ bool conv_pos(int B, int T, int C, int& b, int& chunk, int& c4) {
+__device__ __forceinline__ bool conv_pos(int B, int T, int C, int CHUNK, int& b, int& chunk, int& c4) {
   const int C4 = C / 4;
   const int nchunk = (T + CHUNK - 1) / CHUNK;
   const int wpr = (C4 + 63) / 64;
@@ -411,15 +414,16 @@ __device__ __forceinline__ bool conv_pos(int B, int T, int C, int& b, int& chunk
   return b < B && c4 < C4;
 }
 
-// Thread (b, chunk of kConvChunkFwd steps, 4 channels c4): pre_t = sum_i w[c][i] x_{t-3+i} + bias[c],
+// Thread (b, chunk of CHUNK steps, 4 channels c4): pre_t = sum_i w[c][i] x_{t-3+i} + bias[c],
 // u_t = SiLU(pre_t), with x_t = 0 for t < 0.  Layout [B, T, C]; C is a multiple of 4.
 template <bool BF16>
 __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_fwd_kernel(const void* __restrict__ x,
                                                                             const float* __restrict__ w,
                                                                             const float* __restrict__ bias, int B,
-                                                                            int T, int C, void* __restrict__ u) {
+                                                                            int T, int C, int CHUNK,
+                                                                            void* __restrict__ u) {
   int b, chunk, c4;
-  if (!conv_pos<kConvChunkFwd>(B, T, C, b, chunk, c4)) return;
+  if (!conv_pos(B, T, C, CHUNK, b, chunk, c4)) return;
   const int c = 4 * c4;
   float wk[4][4];  // [channel][tap]
 #pragma unroll
@@ -429,8 +433,8 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_fwd_kernel(const
   }
   const float4 bv = bias ? *(const float4*)(bias + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   const float bs[4] = {bv.x, bv.y, bv.z, bv.w};
-  const int t0 = chunk * kConvChunkFwd;
-  const int t1 = min(T, t0 + kConvChunkFwd);
+  const int t0 = chunk * CHUNK;
+  const int t1 = min(T, t0 + CHUNK);
   const long row = (long)b * T;
   // window: xs[0..2] = x_{t-3..t-1}
   float xs[3][4];
@@ -474,7 +478,7 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_fwd_kernel(const
   }
 }
 
-// Backward, same layout with chunks of kConvChunkBwd steps.  dpre_t = du_t SiLU'(pre_t),
+// Backward, same layout (its chunks start at kConvChunkBwd steps).  dpre_t = du_t SiLU'(pre_t),
 // dx_s = sum_i w[c][i] dpre_{s+3-i}; the thread's partials of dw[c][i] = sum dpre_t x_{t-3+i} and
 // dbias[c] = sum dpre_t go to part[(b * nchunk + chunk)] as [C][4] taps followed by C biases.
 template <bool BF16>
@@ -482,10 +486,10 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_bwd_kernel(const
                                                                             const float* __restrict__ w,
                                                                             const float* __restrict__ bias,
                                                                             const float* __restrict__ du, int B, int T,
-                                                                            int C, float* __restrict__ dx,
+                                                                            int C, int CHUNK, float* __restrict__ dx,
                                                                             float* __restrict__ part) {
   int b, chunk, c4;
-  if (!conv_pos<kConvChunkBwd>(B, T, C, b, chunk, c4)) return;
+  if (!conv_pos(B, T, C, CHUNK, b, chunk, c4)) return;
   const int c = 4 * c4;
   float wk[4][4];
 #pragma unroll
@@ -495,8 +499,8 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_bwd_kernel(const
   }
   const float4 bv = bias ? *(const float4*)(bias + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   const float bs[4] = {bv.x, bv.y, bv.z, bv.w};
-  const int t0 = chunk * kConvChunkBwd;
-  const int t1 = min(T, t0 + kConvChunkBwd);
+  const int t0 = chunk * CHUNK;
+  const int t1 = min(T, t0 + CHUNK);
   const long row = (long)b * T;
   auto xat = [&](int t, float (&o)[4]) {
     const float4 v = (t >= 0 && t < T) ? load4<BF16>(x, (row + t) * C + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -593,7 +597,7 @@ __global__ void __launch_bounds__(kBlkThreads) m2rnn_conv4_silu_bwd_kernel(const
     }
   }
   // [4C: dw as [C][4] | C: dbias]
-  float* pp = part + ((long)b * ((T + kConvChunkBwd - 1) / kConvChunkBwd) + chunk) * C * 5;
+  float* pp = part + ((long)b * ((T + CHUNK - 1) / CHUNK) + chunk) * C * 5;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     *(float4*)(pp + (c + e) * 4) = make_float4(aw[e][0], aw[e][1], aw[e][2], aw[e][3]);
