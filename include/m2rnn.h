@@ -173,7 +173,8 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
  * keeping only the states that enter every I-th step (an eighth to a sixty-fourth of the states)
  * lets the backward skip that re-run.
  *
- * m2rnn_fwd_ckpt     m2rnn_fwd plus `ckpt` [B,N,ceil(T/I),K,V] fp32 with I = m2rnn_checkpoint_interval():
+ * m2rnn_fwd_ckpt     m2rnn_fwd's single pass (never time segments) plus `ckpt` [B,N,ceil(T/I),K,V] fp32
+ *                    with I = m2rnn_checkpoint_interval():
  *                    ckpt[b][n][s] is the state entering step I s (ckpt[b][n][0] = H0, or zeros).
  *                    Required when T > 0.
  * m2rnn_bwd_ckpt     m2rnn_bwd with `ckpt` from m2rnn_fwd_ckpt on the same inputs in place of H0
