@@ -360,15 +360,19 @@ int fwd_segmented(const FwdCall& c, int math, int rb, Second second) {
   SideStream* side = side_stream_locked();
   if (!side) return 1;
   const m2rnn_dims* d = c.d;
-  const long L = ((d->T + kFwdSegs - 1) / kFwdSegs + 31) / 32 * 32;  // at most kFwdSegs segments
+  // Segment ends at 5/16, 10/16 and 15/16 of T (multiples of 32 steps): the last finish pass,
+  // which nothing overlaps, covers a sixteenth of the sequence.
+  long ends[kFwdSegs];
+  for (int e = 0; e < kFwdSegs - 1; ++e) ends[e] = d->T * (5 * (e + 1)) / 16 / 32 * 32;
+  ends[kFwdSegs - 1] = d->T;
   char* hb = (char*)c.ws + fwd_partial_bytes(d, rb, math);
   float* hbuf[2] = {(float*)hb, (float*)(hb + fwd_seg_state_bytes(d))};
   const float* H0 = c.H0;
   int st = M2RNN_OK, i = 0;
   bool forked = false;
-  for (long t0 = 0; t0 < d->T && st == M2RNN_OK; t0 += L, ++i) {
-    const long len = std::min(L, d->T - t0);
-    float* HT = t0 + len >= d->T ? c.H_T : hbuf[i & 1];
+  for (long t0 = 0; i < kFwdSegs && st == M2RNN_OK; t0 = ends[i++]) {
+    const long len = ends[i] - t0;
+    float* HT = i == kFwdSegs - 1 ? c.H_T : hbuf[i & 1];
     st = launch_scan_seg(c, math, rb, t0, len, H0, HT);
     if (st) break;
     st = record_hip_status(hipEventRecord(side->ev[i], c.stream));
