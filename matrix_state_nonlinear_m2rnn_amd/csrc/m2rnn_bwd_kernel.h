@@ -401,8 +401,9 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   constexpr bool has_partner = NT > 1;  // (with an even tile count every wave has one)
 
   // Writes this wave's tile (split fp16) into `entry`; returns the split (own B-operand halves).
-  auto put_tile = [&](uint32_t* entry, const float (&x)[4], uint2& hi, uint2& lo) {
+  auto put_tile = [&](uint32_t* entry, float (&x)[4], uint2& hi, uint2& lo) {
     uint32_t h01, h23, l01, l23;
+    opaque4(x);  // the split is a function of the fp32 values alone
     split_pair<MATH_F16X3>(x[0], x[1], h01, l01);
     split_pair<MATH_F16X3>(x[2], x[3], h23, l23);
     hi = make_uint2(h01, h23);
@@ -486,6 +487,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       put_tile(dst, H, hh, hl);
     } else {
       uint32_t h01, h23, l01, l23;
+      opaque4(H);
       split_pair<MATH_F16X3>(H[0], H[1], h01, l01);
       split_pair<MATH_F16X3>(H[2], H[3], h23, l23);
       hh = make_uint2(h01, h23);

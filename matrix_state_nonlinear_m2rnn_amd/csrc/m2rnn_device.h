@@ -136,6 +136,16 @@ __device__ __forceinline__ f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
                                                  c, 0, 0, 0);
 }
 
+// Makes four values opaque to the compiler at this point (an empty asm that "modifies" them in
+// place), so that a later fp16 conversion rounds the fp32 values themselves.  Without it the
+// compiler may fold the FMA that produced a value into the conversion (v_fma_mix with an fp16
+// result), which rounds the unrounded FMA once instead of the fp32 value: the split of a state
+// would then depend on how the value was produced, and a scan restarted from a stored fp32 state
+// would differ from a continuous one.
+__device__ __forceinline__ void opaque4(float (&x)[4]) {
+  asm("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+}
+
 // tanh(x/c) from x = c*P, c = 2 log2 e:  tanh(P) = 1 - 2 / (1 + 2^x).  Returns r = 1/(1 + 2^x)
 // so that callers fold "1 - 2r" into the gate blend.  2^x overflowing to +inf gives r = 0
 // (tanh = 1); underflowing to 0 gives r = 1 (tanh = -1).

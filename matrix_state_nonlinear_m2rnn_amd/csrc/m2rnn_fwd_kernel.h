@@ -391,6 +391,7 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
           *(float4*)&xbuf[buf][wr][((rb * NT + w) * 64 + lane) * 4] = make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
       } else {
         uint32_t h0, h1, l0, l1;
+        opaque4(H[rb]);  // the split is a function of the fp32 state alone
         split_pair<MATH>(H[rb][0], H[rb][1], h0, l0);
         split_pair<MATH>(H[rb][2], H[rb][3], h1, l1);
         hq[rb].x = h0;

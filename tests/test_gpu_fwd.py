@@ -162,8 +162,9 @@ def test_row_groups_in_a_workgroup(K, V, T, math):
 
 def test_long_sequence_time_segments():
     # T >= 4096 with split rows: m2rnn_fwd scans time segments, each from the state the previous one
-    # ended in, with each segment's readout finish overlapping the next scan.  It must agree with the
-    # single pass (scan + finish over the whole sequence) to rounding, and with the oracle.
+    # ended in, with each segment's readout finish overlapping the next scan.  H_t depends on H_{t-1}
+    # and the inputs only (Eq. 10-12), so the result must equal the single pass (scan + finish over
+    # the whole sequence) bit for bit, and the oracle within tolerance.
     torch = torch_cuda()
     import matrix_state_nonlinear_m2rnn_amd as m2
     d = inputs.make_inputs(1, 4100, 8, 64, 64, qkv_dtype="bf16", seed=31)  # the last segment is ragged
@@ -176,10 +177,34 @@ def test_long_sequence_time_segments():
     torch.cuda.synchronize()
     ey, eh = float((y - y1).abs().max()), float((H - H1).abs().max())
     say("segments vs single pass", ey, eh)
-    assert ey <= 1e-5 and eh <= 1e-5, (ey, eh)
+    assert torch.equal(y, y1) and torch.equal(H, H1), (ey, eh)
     y, H = y.cpu().numpy().astype(np.float64), H.cpu().numpy().astype(np.float64)
     for (b, n), (yr, Hr) in oracle_units(d, [(0, 0), (0, 7)]).items():
         ey, eh = max_abs(y[b, :, n], yr), max_abs(H[b, n], Hr)
         say((b, n), ey, eh)
         assert ey <= TOL["f16x3"] and eh <= TOL["f16x3"], ((b, n), ey, eh)
 
+
+
+@pytest.mark.parametrize("B,N,T1,T2", [(1, 8, 96, 70), (2, 32, 256, 131), (1, 8, 1, 33)])
+@pytest.mark.parametrize("math", ["f16x3", "f32", "bf16x3"])
+def test_chained_calls_equal_one_pass(B, N, T1, T2, math):
+    # Eq. 10-12 carry the state from H_{t-1} only: a forward over T1 steps, then one over the next T2
+    # steps started from its H_T, must give the bits of one forward over T1 + T2 steps (y and H_T),
+    # for every row split.
+    torch = torch_cuda()
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    d = inputs.make_inputs(B, T1 + T2, N, 64, 64, qkv_dtype="bf16", seed=900 + B * N + T1, with_H0=True)
+    dd = to_device(d, "bf16")
+    for rb in (1, 2, 4):
+        say("chained", B, N, T1, T2, math, "row_blocks", rb)
+        seq = [dd[x] for x in ("q", "k", "v", "f")]
+        y, H = m2.m2rnn_fwd(*seq, dd["W"], dd["w_r"], dd["H0"], math=math, row_blocks=rb)
+        first = [x[:, :T1].contiguous() for x in seq]
+        second = [x[:, T1:].contiguous() for x in seq]
+        ya, Ha = m2.m2rnn_fwd(*first, dd["W"], dd["w_r"], dd["H0"], math=math, row_blocks=rb)
+        yb, Hb = m2.m2rnn_fwd(*second, dd["W"], dd["w_r"], Ha, math=math, row_blocks=rb)
+        torch.cuda.synchronize()
+        assert torch.equal(H, Hb), float((H - Hb).abs().max())
+        assert torch.equal(y[:, :T1], ya) and torch.equal(y[:, T1:], yb), (
+            float((y[:, :T1] - ya).abs().max()), float((y[:, T1:] - yb).abs().max()))
