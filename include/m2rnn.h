@@ -70,7 +70,13 @@ enum { M2RNN_DTYPE_F32 = 0, M2RNN_DTYPE_BF16 = 1 };
  *           fp32 accumulation (about 22 significant bits per product).
  *   BF16X3  split precision with bf16 halves: W_hi H_hi + W_lo H_hi + W_hi H_lo.
  *   BF16    one bf16 pass: bf16(W) bf16(H) (coarse; meant for a 2e-2 error budget).
- *   AUTO    the library's default (F16X3). */
+ *   AUTO    the library's default (F16X3).
+ * Range of the split modes: the contraction takes 2 log2(e) W (so that tanh is one exp2) and the
+ * state as 16-bit halves.  F16X3 needs |W| < 65504 / (2 log2 e) ~ 22700 elementwise and a state
+ * below 65504 (with f in [0, 1] the state stays within max(|H0|, 1), Eq. 11); the fp16 remainder is
+ * subnormal below about 6e-5, so its absolute rounding is about 3e-8 whatever the value's size,
+ * which the state's [-1, 1] range makes small.  Outside these bounds the results are undefined
+ * (inf or NaN); they are not checked. */
 enum { M2RNN_MATH_AUTO = -1, M2RNN_MATH_F32 = 0, M2RNN_MATH_F16X3 = 1, M2RNN_MATH_BF16X3 = 2, M2RNN_MATH_BF16 = 3 };
 
 /* Status codes. */
@@ -157,6 +163,16 @@ int m2rnn_scan_fwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, int r
  *   dq, dk [B,T,Nqk,K]; dv [B,T,N,V]; df [B,T,N]; dW [N,V,V] and dw_r [N,V] summed over batch and
  *   time; dH0 [B,N,K,V] or NULL to skip it.  All fp32.
  *   math   M2RNN_MATH_F16X3 or M2RNN_MATH_AUTO (the other modes return M2RNN_EUNSUPPORTED).
+ *
+ * Scale of dy.  Every gradient is linear in (dy, dH_T) jointly, and the walk holds the chain's
+ * D_t = ((1 - f_t) R_t) (.) (1 - Z_t^2) in split fp16, whose accurate range is narrow.  So each
+ * (b, n) pair runs at its own power-of-two scale: a first pass finds the largest |dy| and |dH_T|
+ * of the pair, the walk takes 2^e dy and 2^e dH_T with the largest in [1, 2) (and the clip bound
+ * 2^e grad_clip), and every gradient is multiplied by 2^-e before it is stored.  Both products
+ * are exact, so the result for 2^k dy is exactly 2^k times the result for dy (over the whole
+ * fp32 range of dy, bar fp32 underflow or overflow of the gradients themselves): training without
+ * loss scaling, whose activation gradients are far below unit size, keeps the same accuracy.
+ * W must satisfy |W| < 65504 elementwise (the chain multiplies by W^T in split fp16).
  */
 #define M2RNN_BWD_CHECKPOINT 64
 int m2rnn_bwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes);

@@ -393,7 +393,7 @@ int fwd_segmented(const FwdCall& c, int math, int rb, Second second) {
 // ---------------------------------------------------------------- backward
 
 struct BwdLayout {
-  size_t ckpt = 0, seg = 0, dv = 0, df = 0, dW = 0, dwr = 0, dq = 0, dk = 0, total = 0;
+  size_t ckpt = 0, seg = 0, dv = 0, df = 0, dW = 0, dwr = 0, dq = 0, dk = 0, umax = 0, total = 0;
   size_t total_no_ckpt = 0;  // the workspace when the caller supplies the checkpoints
 };
 
@@ -405,6 +405,16 @@ size_t ckpt_bytes(const m2rnn_dims* d) {
   const long I = ckpt_interval((int)d->V);
   const long nck = (d->T + I - 1) / I;
   return (size_t)d->B * d->N * nck * d->K * d->V * sizeof(float);
+}
+
+// Time parts of the |dy| maxima per (b, n) (m2rnn_bwd_absmax_kernel): about 1024 blocks over the
+// read of dy, at most 64 parts (one per lane of the wave that combines them), at least 16 steps each.
+int absmax_parts(const m2rnn_dims* d) {
+  const long win = (d->N * d->V + 1023) / 1024;
+  long P = (1024 + d->B * win - 1) / (d->B * win);
+  P = std::min(P, 64L);
+  P = std::min(P, std::max(1L, (long)(d->T / 16)));
+  return (int)std::max(P, 1L);
 }
 
 // A shared query/key (Nqk = 1) with several heads: per-head dq, dk go to the workspace and are
@@ -431,6 +441,7 @@ BwdLayout bwd_layout(const m2rnn_dims* d) {
   const size_t qk_part = shared_qk_sum(d) ? (size_t)d->B * d->T * d->N * d->K * sizeof(float) : 0;
   L.dq = take(qk_part);
   L.dk = take(qk_part);
+  L.umax = take((size_t)d->B * d->N * absmax_parts(d) * sizeof(float));
   L.total_no_ckpt = off;
   L.ckpt = take(ckpt_bytes(d));
   L.total = off;
@@ -665,7 +676,16 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
     st = hip_status(hipLaunchKernel(kern, dim3((unsigned)(B * N * S)), dim3((unsigned)(4 * V)), args, 0, stream));
     if (st) return st;
   }
-  // 2. Reverse scan.
+  // 2. The scale of every (b, n) pair: partial maxima of |dy| and |dH_T|.
+  const int P = absmax_parts(d);
+  {
+    const dim3 grid((unsigned)(B * P), (unsigned)((N * V + 1023) / 1024));
+    hipLaunchKernelGGL(m2rnn_bwd_absmax_kernel, grid, dim3(256), 0, stream, dy, dH_T, (int)T, (int)N, (int)K, (int)V, P,
+                       (float*)(ws + L.umax));
+    st = hip_status(hipGetLastError());
+    if (st) return st;
+  }
+  // 3. Reverse scan.
   {
     BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.dy = dy; a.dH_T = dH_T;
@@ -679,6 +699,8 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
     a.dW_part = (float*)(ws + L.dW);
     a.dwr_part = (float*)(ws + L.dwr);
     a.dH0 = dH0;
+    a.umax = (const float*)(ws + L.umax);
+    a.umax_parts = P;
     a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S;
     a.Nqk = qk_heads(d);
     a.clip = grad_clip;
@@ -688,7 +710,7 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
     st = hip_status(hipLaunchKernel(kern, dim3((unsigned)(B * N * S)), dim3((unsigned)(4 * V)), args, 0, stream));
     if (st) return st;
   }
-  // 3. Deterministic sums of the per-workgroup partials, and dw_r.
+  // 4. Deterministic sums of the per-workgroup partials, and dw_r.
   if (S > 1) {
     const long plane = B * T * N * V;
     hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<false>, dim3((unsigned)((plane / 4 + 255) / 256)), dim3(256), 0, stream,

@@ -21,6 +21,14 @@
 // (V = 128) a segment is staged whole and a forward pass over it (pass A) keeps them in scratch.
 // At V = 64 the walk of sub-segment p runs interleaved with the recompute of sub-segment p - 1.
 // Per-workgroup partials of dv, df and dW are summed by separate, deterministic passes.
+//
+// Range: every gradient is linear in (dy, dH_T) jointly (§2.7), and the walk holds D_t in split
+// fp16, whose accurate range is narrow (the remainder becomes subnormal below about 6e-5 and the
+// high part overflows above 65504).  So each (b, n) pair runs at a power-of-two scale 2^e chosen
+// from the largest |dy| and |dH_T| of the pair (m2rnn_bwd_absmax_kernel): u = 2^e dy and
+// C_T = 2^e dH_T (with the clip bound scaled alike), which puts the largest |u| in [1, 2), and every
+// gradient is multiplied by 2^-e before it is stored.  Both multiplications are exact, so the
+// gradients do not depend on the scale of dy except through rounding at unit scale.
 #pragma once
 
 #include "m2rnn_fwd_kernel.h"
@@ -47,6 +55,8 @@ struct BwdArgs {
   float* dW_part;      // [B*S][N][V][V]
   float* dwr_part;     // [B][N][V] (written by the workgroups with s == 0)
   float* dH0;          // may be null
+  const float* umax;   // [B*N][umax_parts]: partial maxima of |dy| and |dH_T| per (b, n)
+  int umax_parts;      // 1 .. 64
   int B, T, N, K;
   int Nqk;             // heads of q and k: N, or 1 when one query/key is shared by all heads
   int S;
@@ -85,7 +95,7 @@ struct BwdCkpt {
 // to `n_pad` get f = 1 and zero q, k, v, u.
 template <int V, bool BF16IN>
 __device__ __forceinline__ void bwd_stage_segment(const BwdArgs& a, int b, int nh, int row0, int t0, int n_steps,
-                                                  int n_pad, float* stage, int tid, int nth) {
+                                                  int n_pad, float* stage, int tid, int nth, float uscale) {
   using St = BwdStage<V>;
   const int esz = BF16IN ? 2 : 4;
   constexpr int VEC = BF16IN ? 8 : 4;
@@ -153,7 +163,8 @@ __device__ __forceinline__ void bwd_stage_segment(const BwdArgs& a, int b, int n
     const int step = i / UV, cv = i % UV;
     float4 u4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (step < n_steps) u4 = *(const float4*)(a.dy + (((long)b * a.T + t0 + step) * a.N + nh) * V + cv * 4);
-    *(float4*)(stage + step * St::STEP + St::OU + cv * 4) = u4;
+    *(float4*)(stage + step * St::STEP + St::OU + cv * 4) =
+        make_float4(u4.x * uscale, u4.y * uscale, u4.z * uscale, u4.w * uscale);
   }
   for (int i = tid; i < n_pad; i += nth) {
     const float fv = i < n_steps ? a.f[((long)b * a.T + t0 + i) * a.N + nh] : 1.0f;
@@ -222,7 +233,7 @@ struct BwdSubRegs {
     f = tid < n_steps ? fl : 1.0f;
   }
 
-  __device__ __forceinline__ void store(float* stage, int tid) const {
+  __device__ __forceinline__ void store(float* stage, int tid, float uscale) const {
     using St = BwdStage<V>;
     auto widen = [](const uint4& raw, float (&x)[VEC]) {
       if constexpr (BF16IN) {
@@ -271,7 +282,9 @@ struct BwdSubRegs {
       const int i = tid + p * NTH;
       if (i < NU) {
         const int step = i / (V / 4), cv = i % (V / 4);
-        *(float4*)(stage + step * St::STEP + St::OU + cv * 4) = uu[p];
+        const float4 x = uu[p];
+        *(float4*)(stage + step * St::STEP + St::OU + cv * 4) =
+            make_float4(x.x * uscale, x.y * uscale, x.z * uscale, x.w * uscale);
       }
     }
     if (tid < SUB) *(float4*)(stage + tid * St::STEP) = make_float4(f, 0.0f, 0.0f, 0.0f);
@@ -497,15 +510,31 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     if (st_next) kv = mfma_f32(avn, bkn, zero4);
   };
 
+  // Scale of this pair: us = 2^e puts the largest |dy|, |dH_T| of the pair in [1, 2); gradients
+  // are stored times ug = 2^-e.  (Zero, infinite or NaN maxima keep the unit scale.)
+  float us = 1.0f, ug = 1.0f;
+  {
+    float m = 0.0f;
+    for (int i = lane; i < a.umax_parts; i += 64) m = fmaxf(m, a.umax[(long)u * a.umax_parts + i]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (m > 0.0f && m <= 3.0e38f) {
+      // m = mant 2^ex with mant in [0.5, 1): us = 2^(1 - ex), kept well inside the normal range.
+      const int e = min(max(1 - __builtin_amdgcn_frexp_expf(m), -100), 100);
+      us = __builtin_amdgcn_ldexpf(1.0f, e);
+      ug = __builtin_amdgcn_ldexpf(1.0f, -e);
+    }
+  }
+
   // State of the chain.
   float C[4];
   // Bounds of the chain state (infinite without clipping: the clamp is then the identity).
-  const float clip_hi = a.clip > 0.0f ? a.clip : __builtin_inff();
+  const float clip_hi = a.clip > 0.0f ? a.clip * us : __builtin_inff();
   const float clip_lo = -clip_hi;
   const long own_off = ((long)b * a.N + nh) * KV + (long)(row0 + n) * V + 16 * w + 4 * g;
   if (a.dH_T) {
     const float4 c4 = *(const float4*)(a.dH_T + own_off);
-    C[0] = c4.x; C[1] = c4.y; C[2] = c4.z; C[3] = c4.w;
+    C[0] = c4.x * us; C[1] = c4.y * us; C[2] = c4.z * us; C[3] = c4.w * us;
   } else {
     C[0] = C[1] = C[2] = C[3] = 0.0f;
   }
@@ -555,7 +584,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
         float acc = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < NT; ++ww) acc += which == 0 ? red_q[j][ww][row] : red_k[j][ww][row];
-        if (t < a.T) (which == 0 ? a.dq : a.dk)[(((long)b * a.T + t) * a.N + nh) * a.K + row0 + row] = acc;
+        if (t < a.T) (which == 0 ? a.dq : a.dk)[(((long)b * a.T + t) * a.N + nh) * a.K + row0 + row] = acc * ug;
       } else {
         const int j = i - SUB * 32;
         if (tbk < 0) continue;
@@ -563,7 +592,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
         float acc = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < NT; ++ww) acc += red_f[j][ww][0];
-        if (t < a.T) df_dst[((long)b * a.T + t) * a.N + nh] = acc;
+        if (t < a.T) df_dst[((long)b * a.T + t) * a.N + nh] = acc * ug;
       }
     }
   };
@@ -644,7 +673,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       if ((j & 3) == 3) {
         const float dq4 = reduce_rows4(xh[0], xh[1], xh[2], xh[3]);
         if constexpr (ONE) {
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq4), dqres,
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq4 * ug), dqres,
                                                 qk_lane + (uint32_t)((tb + j - 3) * qkstep * 4), 0, 0);
         } else {
           red_q[j - 3 + g][w][n] = dq4;
@@ -653,7 +682,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     } else {
       dq_l = sum_rows4(dq_l);
       if constexpr (ONE) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq_l), dqres,
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq_l * ug), dqres,
                                               g == 0 ? qk_lane + (uint32_t)((tb + j) * qkstep * 4) : kBufferDrop, 0, 0);
       } else if (g == 0) {
         red_q[j][w][n] = dq_l;
@@ -723,9 +752,9 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       df_l += dpp<kDppQuadXor2>(df_l);
       if constexpr (ONE) {
         const uint32_t tstep = (uint32_t)js;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dk_l), dkres,
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dk_l * ug), dkres,
                                               GROUP4 || g == 0 ? qk_lane + tstep * qkstep * 4 : kBufferDrop, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(df_l), dfres,
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(df_l * ug), dfres,
                                               df_lane == kBufferDrop ? kBufferDrop : df_lane + tstep * a.N * 4, 0, 0);
       } else if constexpr (GROUP4) {
         red_k[j + g][w][n] = dk_l;
@@ -761,13 +790,13 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
         float dvv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
         const float ucol = ss[(j + g) * St::STEP + St::OU + 16 * w + n];
         dvv = __builtin_fmaf(wr_col, ucol, dvv);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv), dvres, dv_lane + (uint32_t)(js * ystep * 4), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv * ug), dvres, dv_lane + (uint32_t)(js * ystep * 4), 0, 0);
       }
     } else {
       x = sum_rows4(x);
       const float ucol = st[St::OU + 16 * w + n];
       const float dvv = __builtin_fmaf(wr_col, ucol, x);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv), dvres,
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv * ug), dvres,
                                             g == 0 ? dv_lane + (uint32_t)(js * ystep * 4) : kBufferDrop, 0, 0);
     }
   };
@@ -802,7 +831,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     // Writes the prefetched records and entry state of sub-segment p into its buffers.
     auto take = [&](int p) __attribute__((always_inline)) {
       Hr[0] = nextH.x; Hr[1] = nextH.y; Hr[2] = nextH.z; Hr[3] = nextH.w;
-      sub_regs.store(stg(p), tid);
+      sub_regs.store(stg(p), tid, us);
       put_tile(hsb(p), Hr, hh, hl);
     };
 
@@ -890,7 +919,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
         lds_barrier();  // the previous segment's readers are done with the stage
         if (pending_tb >= 0) finalize(pending_tb);
         pending_tb = -1;
-        bwd_stage_segment<V, BF16IN>(a, b, nh, row0, t0, nst, nsub * SUB, stage, tid, NTH);
+        bwd_stage_segment<V, BF16IN>(a, b, nh, row0, t0, nst, nsub * SUB, stage, tid, NTH, us);
       }
 
       // The checkpoint entering this segment (segment checkpoints).
@@ -940,7 +969,7 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
           // Everything prefetched for this sub-segment is used before the next prefetch is issued,
           // so that waiting for it never waits for the new loads.
           H[0] = nextH.x; H[1] = nextH.y; H[2] = nextH.z; H[3] = nextH.w;
-          sub_regs.store(stage, tid);
+          sub_regs.store(stage, tid, us);
           put_tile(hst, H, hh, hl);
           if (pending_tb >= 0) finalize(pending_tb);
           pending_tb = t0 + jb;
@@ -978,15 +1007,51 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     if (pending_tb >= 0) finalize(pending_tb);
   }
 
-  if (a.dH0) *(float4*)(a.dH0 + own_off) = make_float4(C[0], C[1], C[2], C[3]);
+  if (a.dH0) *(float4*)(a.dH0 + own_off) = make_float4(C[0] * ug, C[1] * ug, C[2] * ug, C[3] * ug);
   if (s == 0 && n == 0)
-    *(float4*)(a.dwr_part + ((long)b * a.N + nh) * V + 16 * w + 4 * g) = make_float4(dwr4[0], dwr4[1], dwr4[2], dwr4[3]);
+    *(float4*)(a.dwr_part + ((long)b * a.N + nh) * V + 16 * w + 4 * g) = make_float4(dwr4[0] * ug, dwr4[1] * ug, dwr4[2] * ug, dwr4[3] * ug);
   // dW partial of this workgroup: dWacc[tt] at lane (g, j) reg r = dW[16w + 4g + r][16tt + j].
   float* dWp = a.dW_part + ((long)(b * a.S + s) * a.N + nh) * V * V;
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dWp[(long)(16 * w + 4 * g + r) * V + 16 * tt + n] = dWacc[tt][r];
+    for (int r = 0; r < 4; ++r) dWp[(long)(16 * w + 4 * g + r) * V + 16 * tt + n] = dWacc[tt][r] * ug;
+}
+
+// Partial maxima of |dy| and |dH_T| per (b, n) pair, for the pair's power-of-two scale in the
+// reverse kernel.  Block (b P + p, w) covers time part p of batch entry b and the 1024-float window w of
+// the N V features of a step (1024 / V whole heads; a thread keeps one float4 column): each step's
+// window is one contiguous 4 KiB read.  The blocks with p == 0 add the pair's |dH_T|.  Every entry
+// part[(b N + n) P + p] is written by exactly one thread (zero for an empty part).
+__global__ void __launch_bounds__(256) m2rnn_bwd_absmax_kernel(const float* __restrict__ dy,
+                                                                const float* __restrict__ dH_T, int T, int N, int K,
+                                                                int V, int P, float* __restrict__ part) {
+  const int p = blockIdx.x % P, b = blockIdx.x / P;
+  const long NV = (long)N * V;
+  const long c = (long)blockIdx.y * 1024 + 4 * threadIdx.x;  // first feature of this thread
+  const bool live = c < NV;
+  const int len = (T + P - 1) / P;
+  const int t0 = p * len, t1 = min(T, t0 + len);
+  float m = 0.0f;
+  if (live) {
+    const float* src = dy + (long)b * T * NV + c;
+    for (int t = t0; t < t1; ++t) {
+      const float4 x = *(const float4*)(src + (long)t * NV);
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+    }
+  }
+  const int nh = (int)(c / V);
+  const int sub = (int)((c % V) / 4);  // this thread's float4 within the head (V / 4 per head)
+  if (live && p == 0 && dH_T) {
+    const float* h = dH_T + ((long)b * N + nh) * K * V;
+    for (long i = sub; i < (long)K * V / 4; i += V / 4) {
+      const float4 x = *(const float4*)(h + 4 * i);
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+    }
+  }
+  // Maximum over the V / 4 consecutive threads of a head (within one wave: V / 4 <= 32).
+  for (int o = 1; o < V / 4; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (live && sub == 0) part[((long)b * N + nh) * P + p] = m;
 }
 
 // df = sum_s df_s  (S > 1).
