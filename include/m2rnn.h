@@ -26,8 +26,9 @@
  *        y, dy     [B, T, N, V]     fp32
  *    Gradients have the shape of their input and are fp32.
  *  - Every array pointer is a DEVICE pointer on the current HIP device, 16-byte aligned.  The
- *    caller owns all memory, including the workspace; the library allocates no device memory
- *    and keeps no mutable global state, so calls on different streams may run concurrently.
+ *    caller owns all memory, including the workspace, and every stream: the library allocates no
+ *    device memory and keeps no mutable global state,
+ *    so calls on different streams may run concurrently.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call returns
  *    without synchronising.  Outputs are valid once the stream reaches that point.
  *  - Outputs are overwritten, never accumulated.  Outputs must not alias inputs or each other.
@@ -91,7 +92,7 @@ enum {
 /* Library version, as MAJOR*10000 + MINOR*100 + PATCH.  The minor number changes with every
  * change of an entry point's arguments; a caller built against this header should check that
  * m2rnn_version() == M2RNN_VERSION before calling anything else. */
-#define M2RNN_VERSION 300
+#define M2RNN_VERSION 400
 int m2rnn_version(void);
 
 /* Human-readable text for a status code (static storage). */
@@ -99,6 +100,18 @@ const char* m2rnn_status_string(int status);
 
 /* hipError_t of the last HIP failure seen by this thread (0 if none). */
 int m2rnn_last_hip_error(void);
+
+/*
+ * Overlap object: a side stream (default priority) and the events that fork work onto it from a
+ * call's stream and join it back, on the device current at creation.  The forward calls below take
+ * one to overlap the second pass of a long sequence with its scan (see m2rnn_fwd); NULL runs
+ * everything on the call's stream.  The caller owns it: one object serves one call at a time, so
+ * give each stream (or thread) that issues calls its own, and destroy it once its work is done.
+ * Returns M2RNN_EHIP if the stream or an event cannot be made.
+ */
+typedef struct m2rnn_overlap_s* m2rnn_overlap;
+int m2rnn_overlap_create(m2rnn_overlap* out);
+int m2rnn_overlap_destroy(m2rnn_overlap overlap);
 
 /*
  * Forward pass, Eq. (10)-(12).  One pass over all T steps for every (b, n).
@@ -113,20 +126,24 @@ int m2rnn_last_hip_error(void);
  *   H_T          final state [B,N,K,V], or NULL to skip it.
  *   workspace    device scratch of at least m2rnn_fwd_workspace_size() bytes (NULL if that is 0).
  *
- * With split rows and T >= 4096, m2rnn_fwd runs the sequence in (up to four) time segments, each
- * starting from the state the previous one ended in, and the second pass of each segment runs on
- * a library-owned side stream (default priority, one per device) while the next segment is
- * scanned; the call's stream waits for all of it before any later work.  This needs the two state
- * buffers that m2rnn_fwd_workspace_size() adds for such shapes; with a smaller workspace (the
- * partial planes only), or on a stream under graph capture, the single pass runs instead.  The
- * two ways of running agree to rounding (about one unit in the last place of fp32).
+ *   overlap      NULL, or an overlap object of the current device (see above).
+ *
+ * With split rows, T >= 4096 and an overlap object, m2rnn_fwd runs the sequence in four time
+ * segments, each starting from the state the previous one ended in, and the second pass of each
+ * segment runs on the object's side stream while the next segment is scanned; the call's stream
+ * waits for all of it before any later work.  This needs the two state buffers that
+ * m2rnn_fwd_workspace_size() adds for such shapes; with a smaller workspace (the partial planes
+ * only), without an overlap object, or on a stream under graph capture, the single pass runs
+ * instead.  The two ways of running give the same bits: H_t is a function of H_{t-1} and the
+ * step's inputs only, and a scan started from a stored state computes exactly what a continuous
+ * scan does.
  */
 int m2rnn_fwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks,
                              size_t* bytes);
 int m2rnn_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q,
               const void* k, const void* v, const float* f, const float* W, const float* w_r,
               const float* H0, float* y, float* H_T, void* workspace, size_t workspace_bytes,
-              void* stream);
+              void* stream, m2rnn_overlap overlap);
 
 /*
  * The two launches of m2rnn_fwd's single pass, exposed so that a caller can time them apart.
@@ -189,8 +206,8 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
  * keeping only the states that enter every I-th step (an eighth to a sixty-fourth of the states)
  * lets the backward skip that re-run.
  *
- * m2rnn_fwd_ckpt     m2rnn_fwd's single pass (never time segments) plus `ckpt` [B,N,ceil(T/I),K,V] fp32
- *                    with I = m2rnn_checkpoint_interval():
+ * m2rnn_fwd_ckpt     m2rnn_fwd (time segments included, with the same overlap argument and the
+ *                    same bits) plus `ckpt` [B,N,ceil(T/I),K,V] fp32 with I = m2rnn_checkpoint_interval():
  *                    ckpt[b][n][s] is the state entering step I s (ckpt[b][n][0] = H0, or zeros).
  *                    Required when T > 0.
  * m2rnn_bwd_ckpt     m2rnn_bwd with `ckpt` from m2rnn_fwd_ckpt on the same inputs in place of H0
@@ -206,7 +223,7 @@ int m2rnn_checkpoint_interval(const m2rnn_dims* dims, int64_t* steps);
 int m2rnn_fwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q,
                    const void* k, const void* v, const float* f, const float* W, const float* w_r,
                    const float* H0, float* y, float* H_T, float* ckpt, void* workspace,
-                   size_t workspace_bytes, void* stream);
+                   size_t workspace_bytes, void* stream, m2rnn_overlap overlap);
 int m2rnn_bwd_ckpt_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes);
 int m2rnn_bwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k,
                    const void* v, const float* f, const float* W, const float* w_r, const float* ckpt,
@@ -278,7 +295,8 @@ int m2rnn_out_norm_bwd(int64_t rows, int64_t D, const float* y, const void* gz, 
  * pass per token that sums the scan's partial readouts, adds w_r (.) v and applies the output
  * gate and the norm, so y is never written to HBM (when one workgroup carries all K rows the scan
  * writes y to the workspace and the epilogue reads it once).  Long sequences run in time segments
- * as in m2rnn_fwd, each segment's epilogue on the side stream.  out is bit-identical to
+ * as in m2rnn_fwd, each segment's epilogue on the overlap object's side stream (NULL: one pass).
+ * out is bit-identical to
  * m2rnn_gate_fwd, m2rnn_fwd and m2rnn_out_norm_fwd in turn.  The backward needs y: a training
  * step takes those three calls instead.
  *   a            gate pre-activation [B,T,N] fp32; alpha, beta [N] fp32 (4-byte aligned).
@@ -293,7 +311,8 @@ int m2rnn_fwd_block(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blo
                     const void* k, const void* v, const float* a, const float* alpha,
                     const float* beta, const float* W, const float* w_r, const float* H0,
                     const void* gz, int gz_dtype, const float* gamma, float eps, float* out,
-                    float* H_T, void* workspace, size_t workspace_bytes, void* stream);
+                    float* H_T, void* workspace, size_t workspace_bytes, void* stream,
+                    m2rnn_overlap overlap);
 
 /*
  * Causal depthwise Conv1D of kernel size 4 + SiLU (§2.3, step 1), applied to each of q, k, v:

@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 from typing import Dict, Optional, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +35,7 @@ EXPORTED = (
     "m2rnn_gate_fwd", "m2rnn_gate_bwd_workspace_size", "m2rnn_gate_bwd",
     "m2rnn_out_norm_fwd", "m2rnn_out_norm_bwd_workspace_size", "m2rnn_out_norm_bwd",
     "m2rnn_conv4_silu_fwd", "m2rnn_conv4_silu_bwd_workspace_size", "m2rnn_conv4_silu_bwd",
-    "m2rnn_fwd_block_workspace_size", "m2rnn_fwd_block",
+    "m2rnn_fwd_block_workspace_size", "m2rnn_fwd_block", "m2rnn_overlap_create", "m2rnn_overlap_destroy",
 )
 
 
@@ -53,7 +54,7 @@ class M2RNNError(RuntimeError):
 _lib = None
 
 # The C ABI version these bindings are written for (M2RNN_VERSION in include/m2rnn.h).
-ABI_VERSION = 300
+ABI_VERSION = 400
 
 
 def lib() -> ctypes.CDLL:
@@ -78,10 +79,16 @@ def lib() -> ctypes.CDLL:
         L.m2rnn_fwd_workspace_size.restype = ci
         L.m2rnn_fwd_workspace_size.argtypes = [dp, ci, ci, ci, ctypes.POINTER(sz)]
         fwd_args = [dp, ci, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp] + [vp, sz, vp]
-        for name in ("m2rnn_fwd", "m2rnn_scan_fwd", "m2rnn_scan_fwd_finish"):
+        for name in ("m2rnn_scan_fwd", "m2rnn_scan_fwd_finish"):
             fn = getattr(L, name)
             fn.restype = ci
             fn.argtypes = fwd_args
+        L.m2rnn_fwd.restype = ci
+        L.m2rnn_fwd.argtypes = fwd_args + [vp]
+        L.m2rnn_overlap_create.restype = ci
+        L.m2rnn_overlap_create.argtypes = [ctypes.POINTER(vp)]
+        L.m2rnn_overlap_destroy.restype = ci
+        L.m2rnn_overlap_destroy.argtypes = [vp]
         if hasattr(L, "m2rnn_bwd"):
             L.m2rnn_bwd_workspace_size.restype = ci
             L.m2rnn_bwd_workspace_size.argtypes = [dp, ci, ci, ctypes.POINTER(sz)]
@@ -91,7 +98,7 @@ def lib() -> ctypes.CDLL:
         L.m2rnn_checkpoint_interval.restype = ci
         L.m2rnn_checkpoint_interval.argtypes = [dp, ctypes.POINTER(ctypes.c_int64)]
         L.m2rnn_fwd_ckpt.restype = ci
-        L.m2rnn_fwd_ckpt.argtypes = [dp, ci, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp, vp] + [vp, sz, vp]
+        L.m2rnn_fwd_ckpt.argtypes = [dp, ci, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp, vp] + [vp, sz, vp, vp]
         L.m2rnn_bwd_ckpt_workspace_size.restype = ci
         L.m2rnn_bwd_ckpt_workspace_size.argtypes = [dp, ci, ci, ctypes.POINTER(sz)]
         L.m2rnn_bwd_ckpt.restype = ci
@@ -116,7 +123,7 @@ def lib() -> ctypes.CDLL:
         L.m2rnn_fwd_block_workspace_size.argtypes = [dp, ci, ci, ci, ctypes.POINTER(sz)]
         L.m2rnn_fwd_block.restype = ci
         L.m2rnn_fwd_block.argtypes = ([dp, ci, ci, ci] + [vp] * 3 + [vp] * 3 + [vp] * 3 + [vp, ci, vp, cf]
-                                      + [vp, vp] + [vp, sz, vp])
+                                      + [vp, vp] + [vp, sz, vp, vp])
         L.m2rnn_decode_step.restype = ci
         L.m2rnn_decode_step.argtypes = [dp, ci, ci] + [vp] * 3 + [vp] * 3 + [vp, vp, vp, vp]
         _lib = L
@@ -219,13 +226,68 @@ def _workspace(nbytes: int, device, workspace):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def _call_fwd(name, q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, workspace, stream, return_state):
+class Overlap:
+    """An m2rnn_overlap of the current device: a side stream (default priority) and its events, on
+    which the forward calls overlap the second pass of a long sequence with the scan.  One object
+    serves one call at a time: give each stream that issues calls its own."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check("m2rnn_overlap_create", lib().m2rnn_overlap_create(ctypes.byref(h)))
+        self._h = h.value
+
+    @property
+    def handle(self) -> Optional[int]:
+        return self._h
+
+    def close(self) -> None:
+        if self._h:
+            h, self._h = self._h, None
+            _check("m2rnn_overlap_destroy", lib().m2rnn_overlap_destroy(h))
+
+    def __del__(self, _finalizing=sys.is_finalizing):
+        if not _finalizing():  # the HIP runtime may already be gone at interpreter exit
+            try:
+                self.close()
+            except Exception:
+                pass
+
+
+# overlap="auto": one Overlap per (device, stream) that issues forward calls, made on first use and
+# kept for the life of the process.
+_overlaps: Dict[Tuple[int, int], Overlap] = {}
+
+
+def _overlap(overlap, device, stream) -> Optional[int]:
+    if overlap is None:
+        return None
+    if isinstance(overlap, Overlap):
+        return overlap.handle
+    if overlap != "auto":
+        raise ValueError("overlap must be 'auto', None or an Overlap")
+    import torch
+    if torch.cuda.is_current_stream_capturing():
+        return None  # a captured call runs the single pass anyway (and may not create streams)
+    key = (device.index if device.index is not None else torch.cuda.current_device(), _stream(stream) or 0)
+    ov = _overlaps.get(key)
+    if ov is None:
+        with torch.cuda.device(key[0]):
+            ov = Overlap()
+        _overlaps[key] = ov
+    return ov.handle
+
+
+def _call_fwd(name, q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, workspace, stream, return_state,
+              overlap=None):
     dims, dt, m, rb, y, H_T = _fwd_prepare(q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, return_state)
     nbytes = m2rnn_fwd_workspace_size(dims, dt, m, rb)
     ws = _workspace(nbytes, q.device, workspace)
     fn = getattr(lib(), name)
-    _check(name, fn(ctypes.byref(dims), dt, m, rb, _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0),
-                    _ptr(y), _ptr(H_T), _ptr(ws), nbytes, _stream(stream)))
+    args = [ctypes.byref(dims), dt, m, rb, _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0),
+            _ptr(y), _ptr(H_T), _ptr(ws), nbytes, _stream(stream)]
+    if name == "m2rnn_fwd":
+        args.append(_overlap(overlap, q.device, stream))
+    _check(name, fn(*args))
     return y, H_T, ws
 
 
@@ -243,7 +305,7 @@ def checkpoint_count(T: int, V: int) -> int:
 
 
 def m2rnn_fwd_ckpt(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int = 0, y=None, H_T=None, ckpt=None,
-                   workspace=None, stream=None):
+                   workspace=None, stream=None, overlap="auto"):
     """m2rnn_fwd that also keeps the backward's checkpoints: returns (y, H_T, ckpt) with ckpt
     [B,N,ceil(T/I),K,V] fp32, the state entering every I-th step, I = m2rnn_checkpoint_interval
     (for m2rnn_bwd_ckpt)."""
@@ -257,26 +319,27 @@ def m2rnn_fwd_ckpt(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int 
     ws = _workspace(nbytes, q.device, workspace)
     _check("m2rnn_fwd_ckpt", lib().m2rnn_fwd_ckpt(
         ctypes.byref(dims), dt, m, rb, _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(y),
-        _ptr(H_T), _ptr(ckpt), _ptr(ws), nbytes, _stream(stream)))
+        _ptr(H_T), _ptr(ckpt), _ptr(ws), nbytes, _stream(stream), _overlap(overlap, q.device, stream)))
     return y, H_T, ckpt
 
 
 def m2rnn_fwd(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int = 0, y=None, H_T=None, workspace=None,
-              stream=None, return_state: bool = True) -> Tuple[object, Optional[object]]:
+              stream=None, return_state: bool = True, overlap="auto") -> Tuple[object, Optional[object]]:
     """Forward recurrence (M²RNN notes §2.1, Eq. 10-12) on the current HIP stream.
 
     q, k: [B,T,Nqk,K] with Nqk = N, or 1 for one query/key shared by all heads (§2.4); v: [B,T,N,V]
     (all float32 or all bfloat16); f: [B,T,N] fp32; W: [N,V,V] fp32; w_r: [N,V] fp32; H0: [B,N,K,V]
-    fp32 or None.  Returns (y [B,T,N,V] fp32, H_T [B,N,K,V] fp32).
+    fp32 or None.  Returns (y [B,T,N,V] fp32, H_T [B,N,K,V] fp32).  overlap: "auto" (one side stream
+    per calling stream, made on first use), None (everything on the call's stream) or an Overlap.
     """
     y, H_T, _ = _call_fwd("m2rnn_fwd", q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, workspace, stream,
-                          return_state)
+                          return_state, overlap)
     return y, H_T
 
 
 def m2rnn_fwd_block(q, k, v, a, alpha, beta, W, w_r, gz, gamma, H0=None, *, eps: float = 1e-6, math="auto",
                     row_blocks: int = 0, out=None, H_T=None, workspace=None, stream=None,
-                    return_state: bool = True) -> Tuple[object, Optional[object]]:
+                    return_state: bool = True, overlap="auto") -> Tuple[object, Optional[object]]:
     """The block forward from the gate pre-activation to the normalised output (M²RNN notes §2.2,
     §2.3, Appendix C): f = exp(-alpha softplus(a + beta)), the recurrence, then
     out = gamma (.) x / sqrt(mean x^2 + eps) with x = y (.) SiLU(gz) over the N V features of a
@@ -296,7 +359,7 @@ def m2rnn_fwd_block(q, k, v, a, alpha, beta, W, w_r, gz, gamma, H0=None, *, eps:
     _check("m2rnn_fwd_block", lib().m2rnn_fwd_block(
         ctypes.byref(dims), dt, m, rb, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(alpha), _ptr(beta), _ptr(W),
         _ptr(w_r), _ptr(H0), _ptr(gz), _dtype_code(gz), _ptr(gamma), float(eps), _ptr(out), _ptr(H_T), _ptr(ws),
-        int(n.value), _stream(stream)))
+        int(n.value), _stream(stream), _overlap(overlap, dev, stream)))
     return out, H_T
 
 

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <new>
 #include <unordered_map>
 
 #include "../../include/m2rnn.h"
@@ -209,8 +210,9 @@ struct FwdCall {
 };
 
 // Validates a forward call and fills the resolved math mode and row blocks (also when the only
-// fault is the workspace, M2RNN_EWORKSPACE, the last check).
-int check_fwd(const FwdCall& c, int* math_out, int* rb_out) {
+// fault is the workspace, M2RNN_EWORKSPACE, the last check).  need_ws = false: the caller brings
+// the partial planes' memory itself.
+int check_fwd(const FwdCall& c, int* math_out, int* rb_out, bool need_ws = true) {
   int st = check_dims(c.d, c.qkv_dtype);
   if (st) return st;
   const int math = resolve_math(c.math);
@@ -230,14 +232,25 @@ int check_fwd(const FwdCall& c, int* math_out, int* rb_out) {
   if (rb < 0) return c.row_blocks > 0 && (d->K / 16) % c.row_blocks != 0 ? M2RNN_EINVAL : M2RNN_EUNSUPPORTED;
   *math_out = math;
   *rb_out = rb;
-  const size_t need = empty ? 0 : fwd_partial_bytes(d, rb, math);
+  const size_t need = empty || !need_ws ? 0 : fwd_partial_bytes(d, rb, math);
   if (need > 0 && (!c.ws || c.ws_bytes < need || !aligned16(c.ws))) return M2RNN_EWORKSPACE;
   return M2RNN_OK;
 }
 
+// Where a launch's partial readouts go (S > 1): planes [S][B][Tp][N][V] from `base`, the launch's
+// first step at step t0 of them.  The whole sequence: the workspace, Tp = T, t0 = the launch's own
+// first step; planes that hold one time segment only: Tp = its length, t0 = 0.
+struct Planes {
+  float* base;
+  long Tp, t0;
+};
+Planes whole_planes(const FwdCall& c, long t0) { return Planes{(float*)c.ws, c.d->T, t0}; }
+
 // The scan over steps [t0, t0 + len) of the sequence, from state H0 (null: zeros) to H_T (null:
-// not kept).  The whole sequence is t0 = 0, len = T with the call's own H0 and H_T.
-int launch_scan_seg(const FwdCall& c, int math, int rb, long t0, long len, const float* H0, float* H_T) {
+// not kept).  The whole sequence is t0 = 0, len = T with the call's own H0 and H_T.  The call's
+// checkpoints (if any) of the steps in the range are kept: t0 is then a multiple of the interval.
+int launch_scan_seg(const FwdCall& c, int math, int rb, long t0, long len, const float* H0, float* H_T,
+                    const Planes& pl) {
   const m2rnn_dims* d = c.d;
   const bool bf16 = c.qkv_dtype == M2RNN_DTYPE_BF16;
   const int rw = row_groups(d, rb, math);
@@ -250,13 +263,23 @@ int launch_scan_seg(const FwdCall& c, int math, int rb, long t0, long len, const
   a.v = (const char*)c.v + t0 * v_row * esz;
   a.f = c.f + t0 * d->N;
   a.W = c.W; a.w_r = c.w_r; a.H0 = H0;
-  a.y = (S > 1 ? (float*)c.ws : c.y) + t0 * v_row;
+  if (S > 1) {
+    a.y = pl.base + pl.t0 * v_row;
+    a.Tp = (int)pl.Tp;
+  } else {
+    a.y = c.y + t0 * v_row;
+    a.Tp = (int)d->T;
+  }
   a.H_T = H_T;
-  a.ckpt = t0 == 0 && len == d->T ? c.ckpt : nullptr;
+  a.ckpt = c.ckpt;
   a.B = (int)d->B; a.T = (int)len; a.N = (int)d->N; a.K = (int)d->K;
   a.Nqk = qk_heads(d);
   a.S = S;
-  a.seg = a.ckpt ? ckpt_interval((int)d->V) : 0;
+  if (a.ckpt) {
+    a.seg = ckpt_interval((int)d->V);
+    a.nck = (int)((d->T + a.seg - 1) / a.seg);
+    a.ck0 = (int)(t0 / a.seg);
+  }
   a.Ts = (int)d->T;
   const void* kern = fwd_kernel(math, (int)d->V, rb, rw, bf16, MODE_FWD);
   if (!kern) return M2RNN_EUNSUPPORTED;
@@ -268,32 +291,29 @@ int launch_scan_seg(const FwdCall& c, int math, int rb, long t0, long len, const
 int launch_scan(const FwdCall& c, int math, int rb) {
   const m2rnn_dims* d = c.d;
   if (d->B == 0 || d->N == 0) return M2RNN_OK;
-  const bool bf16 = c.qkv_dtype == M2RNN_DTYPE_BF16;
-  const int rw = row_groups(d, rb, math);
-  const int S = (int)readout_planes(d, rb, math);  // workgroups per (b, n), one readout plane each
-  const int planes = S;
   if (d->T == 0) {
     // Nothing to scan: H_T = H0 (or zeros); there are no segments to checkpoint.
     return fill(c.H_T, c.H0, d->B * d->N * d->K * d->V, c.stream);
   }
-  return launch_scan_seg(c, math, rb, 0, d->T, c.H0, c.H_T);
+  return launch_scan_seg(c, math, rb, 0, d->T, c.H0, c.H_T, whole_planes(c, 0));
 }
 
-// The finish pass over steps [t0, t0 + len) of every batch entry (the whole tensor: t0 = 0, len = T).
-int launch_finish_seg(const FwdCall& c, int math, int rb, long t0, long len, hipStream_t stream) {
+// The finish pass over steps [t0, t0 + len) of every batch entry (the whole tensor: t0 = 0, len = T),
+// from the planes `pl` of that range.
+int launch_finish_seg(const FwdCall& c, int math, int rb, long t0, long len, hipStream_t stream, const Planes& pl) {
   const m2rnn_dims* d = c.d;
   const int S = (int)readout_planes(d, rb, math);
-  const long row = d->N * d->V, plane = d->B * d->T * row;
-  const bool whole = t0 == 0 && len == d->T;
-  const long count = whole ? plane : len * row;  // elements per row of blocks
+  const long row = d->N * d->V, plane = d->B * pl.Tp * row;
+  const bool whole = t0 == 0 && len == d->T && pl.Tp == d->T;
+  const long count = whole ? d->B * d->T * row : len * row;  // elements per row of blocks
   const dim3 grid((unsigned)((count / 4 + 255) / 256), whole ? 1u : (unsigned)d->B);
-  const long bstride = whole ? 0 : d->T * row;
+  const long bstride = whole ? 0 : d->T * row, pbstride = whole ? 0 : pl.Tp * row;
   if (c.qkv_dtype == M2RNN_DTYPE_BF16)
-    hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<true>, grid, dim3(256), 0, stream, (const float*)c.ws, S, plane, c.v,
-                       c.w_r, (int)d->N, (int)d->V, c.y, count, bstride, t0 * row);
+    hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<true>, grid, dim3(256), 0, stream, (const float*)pl.base, S, plane,
+                       pl.t0 * row, pbstride, c.v, c.w_r, (int)d->N, (int)d->V, c.y, count, bstride, t0 * row);
   else
-    hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<false>, grid, dim3(256), 0, stream, (const float*)c.ws, S, plane, c.v,
-                       c.w_r, (int)d->N, (int)d->V, c.y, count, bstride, t0 * row);
+    hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<false>, grid, dim3(256), 0, stream, (const float*)pl.base, S, plane,
+                       pl.t0 * row, pbstride, c.v, c.w_r, (int)d->N, (int)d->V, c.y, count, bstride, t0 * row);
   return hip_status(hipGetLastError());
 }
 
@@ -301,13 +321,13 @@ int launch_finish(const FwdCall& c, int math, int rb) {
   const m2rnn_dims* d = c.d;
   if (d->B == 0 || d->N == 0 || d->T == 0) return M2RNN_OK;
   if (readout_planes(d, rb, math) <= 1) return M2RNN_OK;
-  return launch_finish_seg(c, math, rb, 0, d->T, c.stream);
+  return launch_finish_seg(c, math, rb, 0, d->T, c.stream, whole_planes(c, 0));
 }
 
 // Time segments of m2rnn_fwd for long sequences with split rows: each segment's finish pass runs
-// on a side stream while the next segment is scanned (the scan keeps one wave per SIMD, so the
-// finish pass's waves use the free slots), instead of the whole finish pass after the whole scan.
-// The state goes from one segment to the next through two buffers after the partial planes.
+// on the caller's side stream while the next segment is scanned (the scan keeps one wave per SIMD,
+// so the finish pass's waves use the free slots), instead of the whole finish pass after the whole
+// scan.  The state goes from one segment to the next through two buffers after the partial planes.
 constexpr int kFwdSegs = 4;
 constexpr long kFwdSegMinT = 4096;
 
@@ -325,45 +345,32 @@ size_t fwd_ws_bytes(const m2rnn_dims* d, int rb, int math) {
   return fwd_partial_bytes(d, rb, math) + (fwd_segmentable(d, rb, math) ? 2 * fwd_seg_state_bytes(d) : 0);
 }
 
-// The side stream (default priority, non-blocking) and events of the current device, made on
-// first use; null when they cannot be made.  Callers hold g_side_mu.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t ev[kFwdSegs + 1] = {};
-  int state = 0;  // 0: not made yet, 1: ready, -1: failed
-};
-std::mutex g_side_mu;
+}  // namespace
 
-SideStream* side_stream_locked() {
-  static std::unordered_map<int, SideStream> streams;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  SideStream& e = streams[dev];
-  if (e.state == 0) {
-    e.state = -1;
-    if (hipStreamCreateWithFlags(&e.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    for (hipEvent_t& ev : e.ev)
-      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return nullptr;
-    e.state = 1;
-  }
-  return e.state == 1 ? &e : nullptr;
-}
+// A caller's side stream and the events that fork the finish passes off the call's stream and join
+// them back (include/m2rnn.h: m2rnn_overlap).
+struct m2rnn_overlap_s {
+  int device = -1;
+  hipStream_t side = nullptr;
+  hipEvent_t ev[kFwdSegs + 1] = {};
+};
+
+namespace {
 
 // The segmented forward: the scan of each time segment on the call's stream, then
-// second(t0, len, side stream) for that segment.  Returns 1 when it does not apply (a stream under
-// graph capture, or no side stream); the caller then runs the single pass.
+// second(t0, len, side stream) for that segment.  Returns 1 when it does not apply (no overlap
+// object, or a stream under graph capture); the caller then runs the single pass.  Segment ends
+// are multiples of 64 steps, so that they fall on checkpoints.
 template <class Second>
-int fwd_segmented(const FwdCall& c, int math, int rb, Second second) {
+int fwd_segmented(const FwdCall& c, m2rnn_overlap_s* ov, int math, int rb, Second second) {
+  if (!ov) return 1;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(c.stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return 1;
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStream* side = side_stream_locked();
-  if (!side) return 1;
   const m2rnn_dims* d = c.d;
-  // Segment ends at 5/16, 10/16 and 15/16 of T (multiples of 32 steps): the last finish pass,
-  // which nothing overlaps, covers a sixteenth of the sequence.
+  // Segment ends at 5/16, 10/16 and 15/16 of T: the last finish pass, which nothing overlaps,
+  // covers a sixteenth of the sequence.
   long ends[kFwdSegs];
-  for (int e = 0; e < kFwdSegs - 1; ++e) ends[e] = d->T * (5 * (e + 1)) / 16 / 32 * 32;
+  for (int e = 0; e < kFwdSegs - 1; ++e) ends[e] = d->T * (5 * (e + 1)) / 16 / 64 * 64;
   ends[kFwdSegs - 1] = d->T;
   char* hb = (char*)c.ws + fwd_partial_bytes(d, rb, math);
   float* hbuf[2] = {(float*)hb, (float*)(hb + fwd_seg_state_bytes(d))};
@@ -373,21 +380,29 @@ int fwd_segmented(const FwdCall& c, int math, int rb, Second second) {
   for (long t0 = 0; i < kFwdSegs && st == M2RNN_OK; t0 = ends[i++]) {
     const long len = ends[i] - t0;
     float* HT = i == kFwdSegs - 1 ? c.H_T : hbuf[i & 1];
-    st = launch_scan_seg(c, math, rb, t0, len, H0, HT);
+    st = launch_scan_seg(c, math, rb, t0, len, H0, HT, whole_planes(c, t0));
     if (st) break;
-    st = record_hip_status(hipEventRecord(side->ev[i], c.stream));
-    if (!st) st = record_hip_status(hipStreamWaitEvent(side->s, side->ev[i], 0));
+    st = record_hip_status(hipEventRecord(ov->ev[i], c.stream));
+    if (!st) st = record_hip_status(hipStreamWaitEvent(ov->side, ov->ev[i], 0));
     if (st) break;
     forked = true;
-    st = second(t0, len, side->s);
+    st = second(t0, len, ov->side);
     H0 = HT;
   }
   if (forked) {  // the call's stream waits for every finish pass, also after an error
-    const int j = record_hip_status(hipEventRecord(side->ev[kFwdSegs], side->s));
-    const int k = j ? j : record_hip_status(hipStreamWaitEvent(c.stream, side->ev[kFwdSegs], 0));
+    const int j = record_hip_status(hipEventRecord(ov->ev[kFwdSegs], ov->side));
+    const int k = j ? j : record_hip_status(hipStreamWaitEvent(c.stream, ov->ev[kFwdSegs], 0));
     if (!st) st = k;
   }
   return st;
+}
+
+// An overlap object is usable on the current device only.
+int check_overlap(const m2rnn_overlap_s* ov) {
+  if (!ov) return M2RNN_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return M2RNN_EHIP;
+  return dev == ov->device ? M2RNN_OK : M2RNN_EINVAL;
 }
 
 // ---------------------------------------------------------------- backward
@@ -483,6 +498,33 @@ const char* m2rnn_status_string(int status) {
 
 int m2rnn_last_hip_error(void) { return g_last_hip_error; }
 
+int m2rnn_overlap_create(m2rnn_overlap* out) {
+  if (!out) return M2RNN_EINVAL;
+  *out = nullptr;
+  m2rnn_overlap_s* ov = new (std::nothrow) m2rnn_overlap_s;
+  if (!ov) return M2RNN_EINVAL;
+  int st = hip_status(hipGetDevice(&ov->device));
+  // default priority: streams of other priorities are not used by this library
+  if (!st) st = hip_status(hipStreamCreateWithFlags(&ov->side, hipStreamNonBlocking));
+  for (int i = 0; !st && i <= kFwdSegs; ++i) st = hip_status(hipEventCreateWithFlags(&ov->ev[i], hipEventDisableTiming));
+  if (st) {
+    m2rnn_overlap_destroy(ov);
+    return st;
+  }
+  *out = ov;
+  return M2RNN_OK;
+}
+
+int m2rnn_overlap_destroy(m2rnn_overlap ov) {
+  if (!ov) return M2RNN_OK;
+  int st = M2RNN_OK;
+  for (hipEvent_t& e : ov->ev)
+    if (e && hipEventDestroy(e) != hipSuccess && !st) st = M2RNN_EHIP;
+  if (ov->side && hipStreamDestroy(ov->side) != hipSuccess && !st) st = M2RNN_EHIP;
+  delete ov;
+  return st;
+}
+
 int m2rnn_fwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, size_t* bytes) {
   if (!bytes) return M2RNN_EINVAL;
   int st = check_dims(dims, qkv_dtype);
@@ -519,11 +561,12 @@ int m2rnn_scan_fwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, int r
 
 int m2rnn_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q, const void* k,
               const void* v, const float* f, const float* W, const float* w_r, const float* H0, float* y, float* H_T,
-              void* workspace, size_t workspace_bytes, void* stream) {
+              void* workspace, size_t workspace_bytes, void* stream, m2rnn_overlap overlap) {
   FWD_CALL
-  if (fwd_segmentable(dims, rb, m) && workspace_bytes >= fwd_ws_bytes(dims, rb, m)) {
-    st = fwd_segmented(c, m, rb, [&](long t0, long len, hipStream_t s2) {
-      return launch_finish_seg(c, m, rb, t0, len, s2);
+  if ((st = check_overlap(overlap))) return st;
+  if (overlap && fwd_segmentable(dims, rb, m) && workspace_bytes >= fwd_ws_bytes(dims, rb, m)) {
+    st = fwd_segmented(c, overlap, m, rb, [&](long t0, long len, hipStream_t s2) {
+      return launch_finish_seg(c, m, rb, t0, len, s2, whole_planes(c, t0));
     });
     if (st != 1) return st;
   }
@@ -560,7 +603,8 @@ int m2rnn_fwd_block_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int ma
 int m2rnn_fwd_block(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q, const void* k,
                     const void* v, const float* a, const float* alpha, const float* beta, const float* W,
                     const float* w_r, const float* H0, const void* gz, int gz_dtype, const float* gamma, float eps,
-                    float* out, float* H_T, void* workspace, size_t workspace_bytes, void* stream) {
+                    float* out, float* H_T, void* workspace, size_t workspace_bytes, void* stream,
+                    m2rnn_overlap overlap) {
   // Validated as m2rnn_fwd with f = a; the workspace is checked below (the gate comes first in it).
   FwdCall c{dims, qkv_dtype, math, row_blocks, q, k, v, a, W, w_r, H0, out, H_T, nullptr, 0,
             (hipStream_t)stream};
@@ -568,6 +612,7 @@ int m2rnn_fwd_block(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blo
   int st = check_fwd(c, &m, &rb);
   if (st == M2RNN_EWORKSPACE) st = M2RNN_OK;  // the partial planes live after the gate
   if (st) return st;
+  if ((st = check_overlap(overlap))) return st;
   if (gz_dtype != M2RNN_DTYPE_F32 && gz_dtype != M2RNN_DTYPE_BF16) return M2RNN_EINVAL;
   if (!(eps >= 0.0f) || eps > 1e30f) return M2RNN_EINVAL;
   if (dims->N * dims->V > kNormMaxFeatures || dims->B > 65535) return M2RNN_EUNSUPPORTED;
@@ -599,8 +644,8 @@ int m2rnn_fwd_block(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blo
                                                          S > 1 ? w_r : nullptr, gz, gz_dtype == M2RNN_DTYPE_BF16,
                                                          gamma, dims->B, dims->T, t0, len, D, eps, out, s2));
   };
-  if (fwd_segmentable(dims, rb, m)) {  // the workspace holds the segment states (checked above)
-    st = fwd_segmented(c, m, rb, epilogue);
+  if (overlap && fwd_segmentable(dims, rb, m)) {  // the workspace holds the segment states (checked above)
+    st = fwd_segmented(c, overlap, m, rb, epilogue);
     if (st != 1) return st;
   }
   st = launch_scan(c, m, rb);
@@ -668,7 +713,10 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
     a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.H0 = H0;
     a.y = nullptr; a.H_T = nullptr; a.ckpt = (float*)(ws + L.ckpt);
     a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S; a.seg = ckpt_interval((int)V);
+    a.nck = (int)((T + a.seg - 1) / a.seg);
+    a.ck0 = 0;
     a.Ts = (int)T;
+    a.Tp = (int)T;
     a.Nqk = qk_heads(d);
     const void* kern = fwd_kernel(M2RNN_MATH_F16X3, (int)V, 1, 1, bf16, MODE_CKPT);
     if (!kern) return M2RNN_EUNSUPPORTED;
@@ -714,7 +762,8 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
   if (S > 1) {
     const long plane = B * T * N * V;
     hipLaunchKernelGGL(m2rnn_fwd_finish_kernel<false>, dim3((unsigned)((plane / 4 + 255) / 256)), dim3(256), 0, stream,
-                       (const float*)(ws + L.dv), S, plane, (const void*)dy, w_r, (int)N, (int)V, dv, plane, 0L, 0L);
+                       (const float*)(ws + L.dv), S, plane, 0L, 0L, (const void*)dy, w_r, (int)N, (int)V, dv, plane, 0L,
+                       0L);
     const long cnt = B * T * N;
     hipLaunchKernelGGL(m2rnn_bwd_sum_df_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream,
                        (const float*)(ws + L.df), S, cnt, df);
@@ -775,13 +824,21 @@ int m2rnn_bwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, const void* 
 
 int m2rnn_fwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q, const void* k,
                    const void* v, const float* f, const float* W, const float* w_r, const float* H0, float* y,
-                   float* H_T, float* ckpt, void* workspace, size_t workspace_bytes, void* stream) {
+                   float* H_T, float* ckpt, void* workspace, size_t workspace_bytes, void* stream,
+                   m2rnn_overlap overlap) {
   FwdCall c{dims, qkv_dtype, math, row_blocks, q, k, v, f, W, w_r, H0, y, H_T, workspace, workspace_bytes,
             (hipStream_t)stream, ckpt};
   int m = 0, rb = 0;
   int st = check_fwd(c, &m, &rb);
   if (st) return st;
+  if ((st = check_overlap(overlap))) return st;
   if (dims->T > 0 && dims->B > 0 && dims->N > 0 && !ckpt) return M2RNN_EINVAL;
+  if (overlap && fwd_segmentable(dims, rb, m) && workspace_bytes >= fwd_ws_bytes(dims, rb, m)) {
+    st = fwd_segmented(c, overlap, m, rb, [&](long t0, long len, hipStream_t s2) {
+      return launch_finish_seg(c, m, rb, t0, len, s2, whole_planes(c, t0));
+    });
+    if (st != 1) return st;
+  }
   st = launch_scan(c, m, rb);
   if (st) return st;
   return launch_finish(c, m, rb);

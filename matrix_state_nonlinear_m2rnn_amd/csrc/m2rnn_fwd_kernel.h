@@ -37,15 +37,21 @@ struct FwdArgs {
   const float* H0;
   float* y;       // final readout (S == 1) or partial readouts [S][B*T*N*V] (S > 1)
   float* H_T;     // may be null
-  float* ckpt;    // states entering each seg-step segment [B][N][nseg][K][V] (checkpoint mode;
+  float* ckpt;    // states entering each seg-step segment [B][N][nck][K][V] (checkpoint mode;
                   // optional in the forward mode, null = none)
   int B, T, N, K;
   int Nqk;        // heads of q and k: N, or 1 when one query/key is shared by all heads
   int S;          // workgroups per (b, n)
   int seg;        // checkpoint interval, a multiple of 8 (when ckpt is set)
-  int Ts;         // steps between batch entries in q, k, v, f, y and the planes: T, or more when
-                  // the launch covers a time segment of a longer sequence (the pointers then start
-                  // at the segment's first step; checkpoints are not kept then)
+  int nck;        // checkpoints per (b, n) in ckpt
+  int ck0;        // index of the checkpoint entering this launch's first step (a time segment of a
+                  // longer sequence starts at a multiple of seg)
+  int Ts;         // steps between batch entries in q, k, v and f: T, or more when the launch covers
+                  // a time segment of a longer sequence (the pointers then start at the segment's
+                  // first step)
+  int Tp;         // steps between batch entries in y (S == 1) or the readout planes (S > 1): Ts
+                  // when they cover the whole sequence, or the segment's length for planes that
+                  // hold one segment only
 };
 
 // RW: row waves, independent groups of NT waves in one workgroup, each carrying its own row
@@ -437,8 +443,8 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
   float* ybase = nullptr;  // y (S == 1) or this row group's partial plane, at [b, 0, nh, 0]
   int ybytes = 0;
   if constexpr (MODE == MODE_FWD) {
-    const long plane = (long)a.B * a.Ts * a.N * V;
-    ybase = a.y + (planes > 1 ? (long)s * plane : 0) + ((long)b * a.Ts * a.N + nh) * V;
+    const long plane = (long)a.B * a.Tp * a.N * V;
+    ybase = a.y + (planes > 1 ? (long)s * plane : 0) + ((long)b * a.Tp * a.N + nh) * V;
     // Element (t, nh, c) is valid iff t < T, i.e. iff it lies below (T N V - nh V) floats from ybase.
     ybytes = (a.T * a.N - nh) * V * 4;
   }
@@ -484,8 +490,6 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
   pre.store(stage[0], tid);
   if (a.T > TC) pre.load(a, b, nh, row0_wg, TC, tid);
   publish(0);
-
-  const int nseg = a.seg > 0 ? (a.T + a.seg - 1) / a.seg : 0;
 
   lds_barrier();
 
@@ -542,7 +546,7 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
       // can start a segment.
       if ((j % 8) == 0 && (MODE == MODE_CKPT || a.ckpt != nullptr)) {
         if (t % a.seg == 0 && t < a.T) {
-          float* dst = a.ckpt + ((long)(b * a.N + nh) * nseg + t / a.seg) * KV;
+          float* dst = a.ckpt + ((long)(b * a.N + nh) * a.nck + a.ck0 + t / a.seg) * KV;
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             *(float4*)(dst + (long)(row0 + 16 * rb + n) * V + 16 * w + 4 * g) =
@@ -785,21 +789,24 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
 }
 
 // y = sum_s partial_s + w_r (.) v, elementwise over [B,T,N,V] (4 elements per thread): for batch
-// entry blockIdx.y, the `count` elements from off0 + blockIdx.y * bstride (the whole tensor with
-// one row of blocks and bstride = 0, or a time segment of every batch entry).  The planes are
-// read once and y written once: non-temporal accesses keep them from displacing each other in
-// the caches (258 -> 224 us at B2 N32 T16384 K=V=64, S = 4).
+// entry blockIdx.y, the `count` elements from off0 + blockIdx.y * bstride of y and v, and from
+// poff0 + blockIdx.y * pbstride of each plane (the whole tensor: one row of blocks, zero offsets
+// and strides; a time segment of every batch entry: planes laid out like y, or holding that
+// segment only).  The planes are read once and y written once: non-temporal accesses keep them
+// from displacing each other in the caches (258 -> 224 us at B2 N32 T16384 K=V=64, S = 4).
 template <bool BF16IN>
 __global__ void __launch_bounds__(256) m2rnn_fwd_finish_kernel(const float* __restrict__ part, int S,
-                                                                long plane, const void* __restrict__ v,
+                                                                long plane, long poff0, long pbstride,
+                                                                const void* __restrict__ v,
                                                                 const float* __restrict__ w_r, int N, int V,
                                                                 float* __restrict__ y, long count, long bstride,
                                                                 long off0) {
   const long i4 = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i4 * 4 >= count) return;
   const long i = off0 + (long)blockIdx.y * bstride + i4 * 4;
-  f32x4 acc = __builtin_nontemporal_load((const f32x4*)(part + i));
-  for (int s = 1; s < S; ++s) acc += __builtin_nontemporal_load((const f32x4*)(part + (long)s * plane + i));
+  const long pi = poff0 + (long)blockIdx.y * pbstride + i4 * 4;
+  f32x4 acc = __builtin_nontemporal_load((const f32x4*)(part + pi));
+  for (int s = 1; s < S; ++s) acc += __builtin_nontemporal_load((const f32x4*)(part + (long)s * plane + pi));
   const int colv = (int)(i % V);
   const int nh = (int)((i / V) % N);
   const float4 wr = *(const float4*)(w_r + (long)nh * V + colv);

@@ -41,7 +41,7 @@ def fwd(dims, dtype=0, math=-1, rb=0, ptr=16, ws=None, nbytes=0, y=True, q=True,
     L = m2.lib()
     p = ctypes.c_void_p(ptr)
     return L.m2rnn_fwd(ctypes.byref(dims) if dims is not None else None, dtype, math, rb, p if q else None, p, p,
-                       p if f else None, p, p, None, p if y else None, None, ws, nbytes, None)
+                       p if f else None, p, p, None, p if y else None, None, ws, nbytes, None, None)
 
 
 def test_invalid_arguments_are_rejected_on_the_host():
@@ -115,7 +115,7 @@ def test_checkpoint_entry_points_check_their_arguments():
     dims = D(1, 4, 2, 16, 16)
     # forward that keeps checkpoints: the checkpoint buffer is required when there are steps
     assert L.m2rnn_fwd_ckpt(ctypes.byref(dims), 0, -1, 0, p, p, p, p, p, p, None, p, None, None, None, 0,
-                            None) == m2.M2RNN_EINVAL
+                            None, None) == m2.M2RNN_EINVAL
     # backward from checkpoints: likewise
     assert L.m2rnn_bwd_ckpt(ctypes.byref(dims), 0, -1, p, p, p, p, p, p, None, p, None, 0.0, p, p, p, p, p, p, None,
                             p, 1 << 30, None) == m2.M2RNN_EINVAL
@@ -157,7 +157,8 @@ def test_fused_block_forward_checks_its_arguments():
 
     def call(dims, alpha=True, gz_dtype=0, eps=1e-6, ws=None, nbytes=0, gz=True):
         return L.m2rnn_fwd_block(ctypes.byref(dims), 0, -1, 0, p, p, p, p, p if alpha else None, p, p, p, None,
-                                 p if gz else None, gz_dtype, p, ctypes.c_float(eps), p, None, ws, nbytes, None)
+                                 p if gz else None, gz_dtype, p, ctypes.c_float(eps), p, None, ws, nbytes, None,
+                                 None)
     assert call(D(1, 4, 2, 16, 16), alpha=False) == m2.M2RNN_EINVAL
     assert call(D(1, 4, 2, 16, 16), gz=False) == m2.M2RNN_EINVAL
     assert call(D(1, 4, 2, 16, 16), gz_dtype=5) == m2.M2RNN_EINVAL
@@ -181,3 +182,9 @@ def test_checkpoint_interval():
     # every sub-segment of the backward for V <= 64, every 64-step segment at V = 128
     assert [m2.m2rnn_checkpoint_interval(m2.Dims(1, 100, 1, 16, V)) for V in (16, 32, 64, 128)] == [8, 8, 8, 64]
     assert m2.checkpoint_count(4096, 64) == 512 and m2.checkpoint_count(70, 16) == 9
+
+
+def test_overlap_object_arguments():
+    L = m2.lib()
+    assert L.m2rnn_overlap_create(None) == m2.M2RNN_EINVAL
+    assert L.m2rnn_overlap_destroy(None) == m2.M2RNN_OK

@@ -208,3 +208,30 @@ def test_chained_calls_equal_one_pass(B, N, T1, T2, math):
         assert torch.equal(H, Hb), float((H - Hb).abs().max())
         assert torch.equal(y[:, :T1], ya) and torch.equal(y[:, T1:], yb), (
             float((y[:, :T1] - ya).abs().max()), float((y[:, T1:] - yb).abs().max()))
+
+
+def test_two_streams_with_their_own_overlap_objects():
+    # Two segmented forwards issued at once on two streams, each with its own side stream (the
+    # caller's m2rnn_overlap): no shared queue and no cross-stream dependence, and each result is
+    # its solo run bit for bit.
+    torch = torch_cuda()
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    runs = []
+    for B, T, N, seed in ((1, 4160, 8, 41), (2, 4100, 4, 42)):
+        dd = to_device(inputs.make_inputs(B, T, N, 64, 64, qkv_dtype="bf16", seed=seed), "bf16")
+        args = (dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], None)
+        y, H = m2.m2rnn_fwd(*args, math="f16x3", overlap=None)
+        runs.append((args, y, H))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    overlaps = [m2.Overlap(), m2.Overlap()]
+    out = []
+    for (args, _, _), s, ov in zip(runs, streams, overlaps):
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            out.append(m2.m2rnn_fwd(*args, math="f16x3", overlap=ov))
+    torch.cuda.synchronize()
+    for (_, y, H), (y2, H2) in zip(runs, out):
+        assert torch.equal(y, y2) and torch.equal(H, H2)
+    for ov in overlaps:
+        ov.close()

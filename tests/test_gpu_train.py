@@ -109,15 +109,31 @@ def test_backward_from_fp32_contraction_checkpoints():
 
 
 def test_training_pair_on_the_bwd_workload():
-    # B4 N16 T4096 K=V=64 fp32: the pair gives exactly m2rnn_bwd's gradients.
+    # B4 N16 T4096 K=V=64 fp32.  The checkpoint-keeping forward runs in time segments there (their
+    # second passes on a side stream); its checkpoints are the single pass's bit for bit, so the pair
+    # gives exactly m2rnn_bwd's gradients, and sampled heads meet the oracle.
     torch = torch_cuda()
     import matrix_state_nonlinear_m2rnn_amd as m2
     d = inputs.workload_inputs("bwd_b4_h16_t4096_kv64")
     say("bwd_b4_h16_t4096_kv64 training pair")
     dd = to_device(d, "f32")
-    _, _, ck = fwd_ckpt(dd)
+    y, H_T, ck = fwd_ckpt(dd)
+    y1, H1, ck1 = m2.m2rnn_fwd_ckpt(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], None, overlap=None)
     g = m2.m2rnn_bwd_ckpt(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], ck, dd["dy"])
     g0 = m2.m2rnn_bwd(dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], None, dd["dy"])
     torch.cuda.synchronize()
+    assert torch.equal(y, y1) and torch.equal(H_T, H1) and torch.equal(ck, ck1)
     for n in GRADS:
         assert torch.equal(g[n], g0[n]), n
+    got = {n: g[n].cpu().numpy().astype(np.float64) for n in GRADS}
+    for n in (0, 15):
+        sub = dict(q=d["q"][:, :, n:n + 1], k=d["k"][:, :, n:n + 1], v=d["v"][:, :, n:n + 1], f=d["f"][:, :, n:n + 1],
+                   W=d["W"][n:n + 1], w_r=d["w_r"][n:n + 1], H0=None, dy=d["dy"][:, :, n:n + 1], dH_T=None)
+        ref = oracle_bwd(sub)
+        part = {"dq": got["dq"][:, :, n:n + 1], "dk": got["dk"][:, :, n:n + 1], "dv": got["dv"][:, :, n:n + 1],
+                "df": got["df"][:, :, n:n + 1], "dW": got["dW"][n:n + 1], "dw_r": got["dw_r"][n:n + 1],
+                "dH0": got["dH0"][:, n:n + 1]}
+        errs = {x: rel_l2(part[x], ref[x]) for x in GRADS}
+        say("head", n, errs)
+        for x, e in errs.items():
+            assert e <= 1e-3, (n, x, e)
