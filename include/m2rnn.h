@@ -27,7 +27,7 @@
  *    Gradients have the shape of their input and are fp32.
  *  - Every array pointer is a DEVICE pointer on the current HIP device, 16-byte aligned.  The
  *    caller owns all memory, including the workspace, and every stream: the library allocates no
- *    device memory and keeps no mutable global state,
+ *    device memory and keeps no mutable global state (bar m2rnn_fwd_noalloc's fixed array, below),
  *    so calls on different streams may run concurrently.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call returns
  *    without synchronising.  Outputs are valid once the stream reaches that point.
@@ -144,6 +144,24 @@ int m2rnn_fwd(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, c
               const void* k, const void* v, const float* f, const float* W, const float* w_r,
               const float* H0, float* y, float* H_T, void* workspace, size_t workspace_bytes,
               void* stream, m2rnn_overlap overlap);
+
+/*
+ * m2rnn_fwd for callers that cannot allocate: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments as m2rnn_fwd without the workspace and the
+ * overlap object; the same bits as m2rnn_fwd.  It allocates nothing: the partial readouts of split
+ * rows and the states between time segments live in a fixed device array of the library
+ * (m2rnn_fwd_noalloc_max_bytes() = 64 MiB; every device that runs the library holds one copy until
+ * the process ends).  Long sequences run in time segments whose partial planes fit in it (each
+ * segment's second pass on the call's stream).  Sizes whose two states and 16 steps of partial
+ * planes do not fit return M2RNN_EUNSUPPORTED: 2 B N K V + 16 S B N V floats (S = partial planes,
+ * K / 16 / row_blocks when the rows are split) at most.  When one workgroup carries all rows the
+ * array is not used.  All calls on one device share the array: calls that overlap in time on one
+ * device (on different streams, or from several threads) race, and must be ordered by the caller.
+ */
+int m2rnn_fwd_noalloc_max_bytes(size_t* bytes);
+int m2rnn_fwd_noalloc(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q,
+                      const void* k, const void* v, const float* f, const float* W, const float* w_r,
+                      const float* H0, float* y, float* H_T, void* stream);
 
 /*
  * The two launches of m2rnn_fwd's single pass, exposed so that a caller can time them apart.

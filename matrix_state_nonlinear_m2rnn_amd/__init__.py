@@ -36,6 +36,7 @@ EXPORTED = (
     "m2rnn_out_norm_fwd", "m2rnn_out_norm_bwd_workspace_size", "m2rnn_out_norm_bwd",
     "m2rnn_conv4_silu_fwd", "m2rnn_conv4_silu_bwd_workspace_size", "m2rnn_conv4_silu_bwd",
     "m2rnn_fwd_block_workspace_size", "m2rnn_fwd_block", "m2rnn_overlap_create", "m2rnn_overlap_destroy",
+    "m2rnn_fwd_noalloc", "m2rnn_fwd_noalloc_max_bytes",
 )
 
 
@@ -85,6 +86,10 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = fwd_args
         L.m2rnn_fwd.restype = ci
         L.m2rnn_fwd.argtypes = fwd_args + [vp]
+        L.m2rnn_fwd_noalloc.restype = ci
+        L.m2rnn_fwd_noalloc.argtypes = [dp, ci, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp] + [vp]
+        L.m2rnn_fwd_noalloc_max_bytes.restype = ci
+        L.m2rnn_fwd_noalloc_max_bytes.argtypes = [ctypes.POINTER(sz)]
         L.m2rnn_overlap_create.restype = ci
         L.m2rnn_overlap_create.argtypes = [ctypes.POINTER(vp)]
         L.m2rnn_overlap_destroy.restype = ci
@@ -334,6 +339,18 @@ def m2rnn_fwd(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int = 0, 
     """
     y, H_T, _ = _call_fwd("m2rnn_fwd", q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, workspace, stream,
                           return_state, overlap)
+    return y, H_T
+
+
+def m2rnn_fwd_noalloc(q, k, v, f, W, w_r, H0=None, *, math="auto", row_blocks: int = 0, y=None, H_T=None,
+                      stream=None, return_state: bool = True) -> Tuple[object, Optional[object]]:
+    """m2rnn_fwd without a workspace: the library's fixed device array holds the partial readouts
+    and the states between time segments (for callers that cannot allocate; pass y and H_T to
+    allocate nothing here either).  Calls that overlap in time on one device race."""
+    dims, dt, m, rb, y, H_T = _fwd_prepare(q, k, v, f, W, w_r, H0, y, H_T, math, row_blocks, return_state)
+    _check("m2rnn_fwd_noalloc", lib().m2rnn_fwd_noalloc(
+        ctypes.byref(dims), dt, m, rb, _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(y),
+        _ptr(H_T), _stream(stream)))
     return y, H_T
 
 

@@ -844,6 +844,85 @@ int m2rnn_fwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, int row_bloc
   return launch_finish(c, m, rb);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free forward
+
+namespace {
+
+// Device memory of m2rnn_fwd_noalloc: the partial readout planes of one time segment, then the two
+// states that carry the recurrence from one segment to the next.  Every device that runs the
+// library holds one copy until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its address on a device comes from hipGetSymbolAddress (scratch_on_device).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch_ptr;  // device -> address of `scratch` on it
+
+// The address of `scratch` on the current device, looked up once per device with that device current.
+int scratch_on_device(void** out) {
+  int dev = 0;
+  int st = hip_status(hipGetDevice(&dev));
+  if (st) return st;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* p = nullptr;
+    st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (st) return st;
+    it = g_scratch_ptr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return M2RNN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int m2rnn_fwd_noalloc_max_bytes(size_t* bytes) {
+  if (!bytes) return M2RNN_EINVAL;
+  *bytes = kNoAllocScratchBytes;
+  return M2RNN_OK;
+}
+
+int m2rnn_fwd_noalloc(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q, const void* k,
+                      const void* v, const float* f, const float* W, const float* w_r, const float* H0, float* y,
+                      float* H_T, void* stream) {
+  FwdCall c{dims, qkv_dtype, math, row_blocks, q, k, v, f, W, w_r, H0, y, H_T, nullptr, 0, (hipStream_t)stream};
+  int m = 0, rb = 0;
+  int st = check_fwd(c, &m, &rb, /*need_ws=*/false);
+  if (st) return st;
+  const m2rnn_dims* d = dims;
+  if (d->B == 0 || d->N == 0 || d->T == 0) return launch_scan(c, m, rb);
+  const long S = readout_planes(d, rb, m);
+  if (S <= 1) return launch_scan(c, m, rb);  // one workgroup per pair: the scan writes y itself
+  // Segments of L steps (a multiple of 16) whose planes fit beside the two states.
+  const size_t state = fwd_seg_state_bytes(d);
+  const size_t per_step = (size_t)S * d->B * d->N * d->V * sizeof(float);
+  if (d->B > 65535 || 2 * state + 256 + 16 * per_step > kNoAllocScratchBytes) return M2RNN_EUNSUPPORTED;
+  const long L = (long)((kNoAllocScratchBytes - 2 * state - 256) / per_step) / 16 * 16;
+  void* base = nullptr;
+  if ((st = scratch_on_device(&base))) return st;
+  float* planes = (float*)base;
+  char* hb = (char*)base + round_up((size_t)L * per_step);
+  float* hbuf[2] = {(float*)hb, (float*)(hb + state)};
+  // Every plane element of a segment is written by its scan before the finish pass reads it, and
+  // every state before the next segment reads it: nothing needs clearing between calls.
+  const float* Hin = c.H0;
+  long i = 0;
+  for (long t0 = 0; t0 < d->T; t0 += L, ++i) {
+    const long len = std::min(L, d->T - t0);
+    float* Hout = t0 + len == d->T ? c.H_T : hbuf[i & 1];
+    const Planes pl{planes, len, 0};
+    if ((st = launch_scan_seg(c, m, rb, t0, len, Hin, Hout, pl))) return st;
+    if ((st = launch_finish_seg(c, m, rb, t0, len, c.stream, pl))) return st;
+    Hin = Hout;
+  }
+  return M2RNN_OK;
+}
+
 int m2rnn_decode_step(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k,
                       const void* v, const float* f, const float* W, const float* w_r, const float* H_in,
                       float* H_out, float* y, void* stream) {
