@@ -36,7 +36,8 @@
  *    an error status and touches no memory.  M2RNN_EHIP reports a launch failure
  *    (m2rnn_last_hip_error() gives the hipError_t of the most recent one on this thread).
  *  - Supported sizes: V in {16, 32, 64, 128}; K a positive multiple of 16; B, T, N >= 0;
- *    Nqk in {0, 1, N}.
+ *    Nqk in {0, 1, N}; one batch entry's slice of a tensor below 2 GiB (T N max(K, V) fp32 values),
+ *    whatever the batch (whole tensors may exceed 4 GiB); B N K / 16 below 2^31.
  *    T = 0 is legal: y is empty and H_T = H0 (or zeros).
  */
 #ifndef M2RNN_H_

@@ -42,9 +42,11 @@ int check_dims(const m2rnn_dims* d, int qkv_dtype) {
   if (d->Nqk != 0 && d->Nqk != 1 && d->Nqk != d->N) return M2RNN_EINVAL;
   if (d->V != 16 && d->V != 32 && d->V != 64 && d->V != 128) return M2RNN_EUNSUPPORTED;
   if (d->K <= 0 || d->K % 16 != 0) return M2RNN_EUNSUPPORTED;
-  // 32-bit indices inside the kernels: every (b, t, n) index and plane must fit.
-  const double plane = (double)d->B * d->T * d->N * (d->K > d->V ? d->K : d->V);
-  if (plane * 4.0 > 2147483647.0 || (double)d->B * d->N * d->K / 16 > 2147483647.0) return M2RNN_EUNSUPPORTED;
+  // Offsets from a tensor's start are 64-bit; inside the kernels, offsets within the slice of one
+  // batch entry (the buffer resources that end at a pair's last step) are 32-bit, so that slice,
+  // T N max(K, V) fp32 values, must stay below 2 GiB.  Grids hold B N K / 16 workgroups at most.
+  const double slice = (double)d->T * d->N * (d->K > d->V ? d->K : d->V);
+  if (slice * 4.0 > 2147483647.0 || (double)d->B * d->N * d->K / 16 > 2147483647.0) return M2RNN_EUNSUPPORTED;
   return M2RNN_OK;
 }
 

@@ -188,3 +188,17 @@ def test_overlap_object_arguments():
     L = m2.lib()
     assert L.m2rnn_overlap_create(None) == m2.M2RNN_EINVAL
     assert L.m2rnn_overlap_destroy(None) == m2.M2RNN_OK
+
+
+def test_tensors_beyond_2_gib_are_accepted_per_batch_slice():
+    # The 16K-token context at batch 16 (B16 N32 T16384 K=V=64): y is 2 GiB and the split-row
+    # readout planes 8 GiB; only one batch entry's slice must stay below 2 GiB.
+    n = ctypes.c_size_t(0)
+    dims = m2.Dims(16, 16384, 32, 64, 64)
+    assert m2.lib().m2rnn_fwd_workspace_size(ctypes.byref(dims), m2.DTYPE_BF16, -1, 1, ctypes.byref(n)) == m2.M2RNN_OK
+    assert n.value >= 4 * 16 * 16384 * 32 * 64 * 4  # four planes of [B,T,N,V] fp32
+    assert m2.lib().m2rnn_bwd_workspace_size(ctypes.byref(dims), m2.DTYPE_BF16, -1, ctypes.byref(n)) == m2.M2RNN_OK
+    # one batch entry's slice of 2 GiB or more is refused
+    big = m2.Dims(1, 1 << 20, 32, 64, 64)
+    assert m2.lib().m2rnn_fwd_workspace_size(ctypes.byref(big), m2.DTYPE_BF16, -1, 0, ctypes.byref(n)) == \
+        m2.M2RNN_EUNSUPPORTED

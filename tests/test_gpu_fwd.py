@@ -235,3 +235,48 @@ def test_two_streams_with_their_own_overlap_objects():
         assert torch.equal(y, y2) and torch.equal(H, H2)
     for ov in overlaps:
         ov.close()
+
+
+def test_batch_16_at_16k_tokens_beyond_2_gib():
+    # The 16K-token context at batch 16 (B16 N32 T16384 K=V=64, bf16 q/k/v, f = sigmoid(N(3, 1))):
+    # y is 2 GiB and the split-row readout planes 8 GiB, past 32-bit offsets from the tensors'
+    # starts.  Inputs are eight seeded B2 draws side by side (W and w_r from the first); sampled
+    # units from the first and last batch entries are checked against the oracle, with split rows
+    # (four readout planes, time segments) and with all rows in one workgroup.
+    torch = torch_cuda()
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    B, T, N, K, V = 16, 16384, 32, 64, 64
+    q = torch.empty((B, T, N, K), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty((B, T, N, V), dtype=torch.bfloat16, device="cuda")
+    f = torch.empty((B, T, N), dtype=torch.float32, device="cuda")
+    units = {(0, 0): None, (1, 31): None, (9, 17): None, (15, 31): None, (14, 2): None}
+    W = w_r = None
+    for i in range(B // 2):
+        d = inputs.make_inputs(2, T, N, K, V, qkv_dtype="bf16", f_mean=3.0, seed=4400 + i)
+        if W is None:
+            W, w_r = d["W"], d["w_r"]
+        dd = to_device(d, "bf16")
+        for name, dst in (("q", q), ("k", k), ("v", v), ("f", f)):
+            dst[2 * i:2 * i + 2].copy_(dd[name])
+        for (b, n) in units:
+            if b // 2 == i:
+                bb = b - 2 * i
+                units[(b, n)] = dict(q=d["q"][bb:bb + 1, :, n:n + 1], k=d["k"][bb:bb + 1, :, n:n + 1],
+                                     v=d["v"][bb:bb + 1, :, n:n + 1], f=d["f"][bb:bb + 1, :, n:n + 1],
+                                     W=W[n:n + 1], w_r=w_r[n:n + 1], H0=None)
+        del dd, d
+    Wd = torch.from_numpy(W).cuda()
+    wrd = torch.from_numpy(w_r).cuda()
+    refs = {u: oracle_fwd(sub) for u, sub in units.items()}
+    for rb in (1, 4):
+        say("B16 N32 T16384 K=V=64, row_blocks", rb)
+        y, H = m2.m2rnn_fwd(q, k, v, f, Wd, wrd, None, math="f16x3", row_blocks=rb)
+        torch.cuda.synchronize()
+        for (b, n), (yr, Hr) in refs.items():
+            ey = max_abs(y[b, :, n].cpu().numpy(), yr[0, :, 0])
+            eh = max_abs(H[b, n].cpu().numpy(), Hr[0, 0])
+            say((b, n), ey, eh)
+            assert ey <= TOL["f16x3"] and eh <= TOL["f16x3"], ((b, n), ey, eh)
+        del y, H
+        torch.cuda.empty_cache()
