@@ -30,14 +30,21 @@ METRIC = "M²RNN fwd head-steps/sec + % MFMA peak at K=V=64, T=16384 (1 GPU)"
 PEAK_TFLOPS = {"f32": 157.3, "f16x3": 2500.0, "bf16x3": 2500.0, "bf16": 2500.0}
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["m2rnn_device.h", "m2rnn_fwd_kernel.h"]
+BWD_KERNEL_SOURCES = ["m2rnn_device.h", "m2rnn_fwd_kernel.h", "m2rnn_bwd_kernel.h"]
 
 
-def kernel_hash() -> str:
-    """Hash of the forward kernel's sources with comments and blank lines removed: a counter
-    summary stays valid across edits of comments, and goes stale with any change of code."""
+def arithmetic(math_mode: str) -> str:
+    """What the path computes in: the state and every accumulation in fp32, the per-step contraction
+    in the given mode (f16x3: three fp16 MFMA passes over split operands)."""
+    return f"f32 state, {math_mode} contraction"
+
+
+def kernel_hash(sources=KERNEL_SOURCES) -> str:
+    """Hash of a kernel's sources with comments and blank lines removed: a counter summary stays
+    valid across edits of comments, and goes stale with any change of code."""
     import re
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "matrix_state_nonlinear_m2rnn_amd", "csrc", name)) as fh:
             text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
         for line in text.splitlines():
@@ -47,10 +54,10 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, math_mode: str):
-    """HBM bytes per scan launch from the committed rocprofv3 counter summary, or None when the
-    summary is missing or was taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"m2rnn_scan_fwd_{workload}_{math_mode}_pmc.txt")
+def measured_traffic(workload: str, math_mode: str, kernel: str = "m2rnn_scan_fwd", sources=KERNEL_SOURCES):
+    """HBM bytes per launch of the kernel from the committed rocprofv3 counter summary, or None
+    when the summary is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_{math_mode}_pmc.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -59,7 +66,7 @@ def measured_traffic(workload: str, math_mode: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("kernel_sources_sha256_16") != kernel_hash():
+    if fields.get("kernel_sources_sha256_16") != kernel_hash(sources):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -67,10 +74,24 @@ def measured_traffic(workload: str, math_mode: str):
         return None
 
 
-def cpu_baseline(d, w, seconds: float):
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo, as lscpu reports it)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(d, w, seconds: float, backward: bool = False):
     """Times the fp64 oracle (as it stands) on a bounded sample of the same workload: the first
-    `threads` (batch, head) units, each over the first T_s steps, one unit per thread.  T_s is
-    sized from a one-thread probe so that the sample takes about `seconds` of wall time."""
+    `threads` (batch, head) units, each over the first T_s steps, one unit per thread (forward, or
+    forward + manual BPTT).  T_s is sized from a one-thread probe so that the sample takes about
+    `seconds` of wall time; one unit on one thread over a few seconds gives the single-thread rate."""
     import numpy as np
     import oracle
 
@@ -86,20 +107,30 @@ def cpu_baseline(d, w, seconds: float):
         W = np.stack([d["W"][n] for _, n in sel])
         w_r = np.stack([d["w_r"][n] for _, n in sel])
         t0 = time.perf_counter()
-        oracle.ref_fwd(g(d["q"]), g(d["k"]), g(d["v"]), g(d["f"]), W, w_r, None, nthreads=threads)
+        if backward:
+            oracle.ref_bwd(g(d["q"]), g(d["k"]), g(d["v"]), g(d["f"]), W, w_r, None, g(d["dy"]), None,
+                           nthreads=threads)
+        else:
+            oracle.ref_fwd(g(d["q"]), g(d["k"]), g(d["v"]), g(d["f"]), W, w_r, None, nthreads=threads)
         return time.perf_counter() - t0
 
     probe_T = min(w.T, 128)
     per_step = run(probe_T, 1, 1) / probe_T
+    T_1 = int(max(probe_T, min(w.T, 2.0 / max(per_step, 1e-9))))
+    single = T_1 / run(T_1, 1, 1)
     T_s = int(max(64, min(w.T, seconds / max(per_step, 1e-9))))
     if T_s == w.T:
         # A full-length unit per thread is shorter than the target: give each thread more units.
         reps = max(1, int(seconds / max(per_step * w.T, 1e-9)))
         units = min(w.B * w.N, nthreads * reps)
     wall = run(T_s, units, nthreads)
+    what = "forward + manual BPTT" if backward else "forward"
     return {"value": units * T_s / wall, "unit": "head-steps/s", "cores": min(nthreads, units), "kind": "oracle",
-            "sample": f"{units} (batch, head) units x {T_s} steps of {w.name} (fp64, units spread over threads)",
-            "wall_s": round(wall, 3)}
+            "sample": f"{units} (batch, head) units x {T_s} steps of {w.name} ({what}, fp64, units spread over "
+                      "threads)",
+            "wall_s": round(wall, 3), "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
+            "single_thread_value": single,
+            "single_thread_sample": f"1 unit x {T_1} steps on one thread"}
 
 
 def bench_backward(args) -> int:
@@ -143,26 +174,82 @@ def bench_backward(args) -> int:
             return m2.m2rnn_bwd(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], None, t["dy"], None,
                                 workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    # The reverse kernel alone (with the pass that finds each pair's scale before it): checkpoints
+    # from one forward, then launches of m2rnn_scan_bwd, each between two events on its stream.
+    ck_r = torch.empty((B, N, m2.checkpoint_count(T, V), K, V), dtype=torch.float32, device=dev)
+    y_r = torch.empty((B, T, N, V), dtype=torch.float32, device=dev)
+    m2.m2rnn_fwd_ckpt(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], None, y=y_r, ckpt=ck_r)
+    rws = torch.empty(max(m2.m2rnn_bwd_ckpt_workspace_size(dims, dt, "auto"), 1), dtype=torch.uint8, device=dev)
+    e = lambda *sh: torch.empty(sh, dtype=torch.float32, device=dev)  # noqa: E731
+    Nqk = dims.Nqk
+    gout = {"dq": e(B, T, Nqk, K), "dk": e(B, T, Nqk, K), "dv": e(B, T, N, V), "df": e(B, T, N), "dW": e(N, V, V),
+            "dw_r": e(N, V), "dH0": None}
+
+    def scan_bwd_loop(n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a0, a1 in evs:
+            a0.record()
+            m2.m2rnn_scan_bwd(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], ck_r, t["dy"], None,
+                              workspace=rws, out=gout)
+            a1.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / n
+
+    if args.copy_calibration:
+        # A fill and a plain copy of 256 MiB each: their FETCH_SIZE / WRITE_SIZE readings scale the
+        # reverse kernel's.
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+    if args.scan_only:
+        for _ in range(args.warmup):
+            m2.m2rnn_scan_bwd(t["q"], t["k"], t["v"], t["f"], t["W"], t["w_r"], ck_r, t["dy"], None,
+                              workspace=rws, out=gout)
+        torch.cuda.synchronize()
+        scan_ms = scan_bwd_loop(args.steps)
+        ms = scan_ms
+    else:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        scan_ms = scan_bwd_loop(args.steps)
     hs = B * N * T
+    # Algorithmic MFMA work of the reverse kernel per head-step: the recompute of H_{t-1} W (2 K V^2),
+    # the chain's D W^T (2 K V^2) and dW's H_{t-1}^T D (2 K V^2).
+    flops = 6.0 * K * V * V * hs
+    achieved = flops / (scan_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["f16x3"]
     metric = ("M²RNN training step (fwd keeping checkpoints + BPTT) head-steps/sec" if train
               else "M²RNN bwd (BPTT) head-steps/sec")
     out = {"metric": metric, "value": hs / (ms * 1e-3), "unit": "head-steps/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "scaling": "weak", "vs_baseline": None, "dtype": arithmetic("f16x3"), "data": "synthetic",
            "config": {"workload": w.name, "B": B, "T": T, "N": N, "K": K, "V": V, "qkv_dtype": w.qkv_dtype,
                       "math": "f16x3", "segment": m2.BWD_CHECKPOINT,
                       "checkpoint_interval": m2.m2rnn_checkpoint_interval(dims)},
-           "tokens_per_s": B * T / (ms * 1e-3)}
+           "timed": ("m2rnn_scan_bwd alone" if args.scan_only else
+                     "m2rnn_fwd_ckpt + m2rnn_bwd_ckpt" if train else "m2rnn_bwd"),
+           "tokens_per_s": B * T / (ms * 1e-3),
+           "scan_bwd_ms": scan_ms,
+           "ns_per_recurrence_step": scan_ms * 1e6 / T,
+           "roofline": {"bound": "mfma", "kernel": "m2rnn_scan_bwd_kernel (with the scale pass before it)",
+                        "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                        "traffic": measured_traffic(w.name, "f16x3", "m2rnn_scan_bwd", BWD_KERNEL_SOURCES),
+                        "algorithmic_flops_per_launch": flops,
+                        "frac_of_fp32_mfma_peak": achieved / PEAK_TFLOPS["f32"]}}
+    tr = out["roofline"]["traffic"]
+    if tr:
+        out["roofline"]["hbm_GBs"] = tr / (scan_ms * 1e-3) / 1e9
+    if args.cpu_baseline == "on" and not args.scan_only:
+        print("[bench] cpu baseline (fp64 oracle, forward + BPTT)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(d, w, args.cpu_seconds, backward=True)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -229,7 +316,8 @@ def bench_decode(args) -> int:
     out = {"metric": f"M²RNN decode step head-steps/sec (B={B}, N={N}, K={K}, V={V}, state in HBM)",
            "value": head_steps * args.steps / (total_ms * 1e-3), "unit": "head-steps/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": total_ms / args.steps,
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": arithmetic("f16x3"),
+           "data": "synthetic",
            "config": {"workload": w.name, "B": B, "T": 1, "N": N, "K": K, "V": V, "qkv_dtype": w.qkv_dtype,
                       "math": "f16x3", "in_place": True, "launch": "K steps captured in one hip graph"},
            "kernel_us": kern_ms * 1e3, "wall_s": wall,
@@ -372,7 +460,7 @@ def bench_fused_block(args) -> int:
     line = {"metric": "M²RNN block forward (gate, recurrence, output gate + RMSNorm) head-steps/sec",
             "value": B * T * N / (ms * 1e-3), "unit": "head-steps/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "vs_baseline": None, "dtype": arithmetic(math_mode), "data": "synthetic",
             "config": {"workload": w.name, "B": B, "T": T, "N": N, "K": K, "V": V, "qkv_dtype": w.qkv_dtype,
                        "gz_dtype": "bf16", "math": math_mode, "entry": "m2rnn_fwd_block"},
             "unfused_ms": res["unfused"], "saved_ms": res["unfused"] - ms}
@@ -430,7 +518,7 @@ def bench_layer(args) -> int:
                       "fwd + bwd) tokens/sec",
             "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "vs_baseline": None, "dtype": arithmetic("f16x3"), "data": "synthetic",
             "config": {"workload": w.name, "B": B, "T": T, "N": N, "K": K, "V": V, "activations": "fp32",
                        "math": "f16x3", "params": "random init"}}
     print(json.dumps(line), flush=True)
@@ -472,7 +560,8 @@ def main() -> int:
     ap.add_argument("--decode", action="store_true",
                     help="time m2rnn_decode_step on the batch-128 decode workload (its own JSON line)")
     ap.add_argument("--scan-only", action="store_true",
-                    help="time the forward scan kernel alone over the whole sequence (for counters and traces)")
+                    help="time the forward scan kernel alone over the whole sequence (with --backward: the reverse "
+                         "scan alone), for counters and traces")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -568,6 +657,9 @@ def main() -> int:
     achieved = flops / (scan_avg * 1e-3) / 1e12
     peak = PEAK_TFLOPS[math_mode]
     traffic = measured_traffic(w.name, math_mode)
+    esz = 2 if w.qkv_dtype == "bf16" else 4
+    # Algorithmic HBM bytes per head-step: q, k, v, f read and y written once.
+    alg_bytes = head_steps * ((2 * K + V) * esz + 4 + 4 * V)
 
     if args.copy_calibration:
         # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings scale the scan's.
@@ -587,7 +679,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": arithmetic(math_mode),
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "T": T, "N": N, "K": K, "V": V, "qkv_dtype": w.qkv_dtype,
                    "math": math_mode, "row_blocks": args.row_blocks or "auto"},
@@ -599,7 +691,10 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "algorithmic_flops_per_launch": flops,
-                     "frac_of_fp32_mfma_peak": achieved / PEAK_TFLOPS["f32"]},
+                     "frac_of_fp32_mfma_peak": achieved / PEAK_TFLOPS["f32"],
+                     "algorithmic_hbm_bytes_per_launch": alg_bytes,
+                     "algorithmic_hbm_GBs": alg_bytes / (scan_avg * 1e-3) / 1e9,
+                     "hbm_GBs": traffic / (scan_avg * 1e-3) / 1e9 if traffic else None},
     }
     if args.cpu_baseline == "on":
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)

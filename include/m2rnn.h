@@ -251,6 +251,25 @@ int m2rnn_bwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, const void* 
                    void* stream);
 
 /*
+ * The launches of m2rnn_bwd_ckpt apart, so that a caller can time the reverse scan alone.  Same
+ * arguments as m2rnn_bwd_ckpt.  m2rnn_scan_bwd runs the pass that finds each pair's scale (the
+ * largest |dy|, |dH_T|) and the reverse scan, which writes dq, dk and dH0 (or per-head partials of
+ * a shared q/k), and dv, df (or per-workgroup partials when a pair's rows are split) and per-
+ * workgroup partials of dW, dw_r into the workspace; m2rnn_scan_bwd_finish sums those partials in a
+ * fixed order.  Calling both, in order, on one stream with the same workspace is m2rnn_bwd_ckpt.
+ */
+int m2rnn_scan_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k,
+                   const void* v, const float* f, const float* W, const float* w_r, const float* ckpt,
+                   const float* dy, const float* dH_T, float grad_clip, float* dq, float* dk, float* dv,
+                   float* df, float* dW, float* dw_r, float* dH0, void* workspace, size_t workspace_bytes,
+                   void* stream);
+int m2rnn_scan_bwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k,
+                          const void* v, const float* f, const float* W, const float* w_r,
+                          const float* ckpt, const float* dy, const float* dH_T, float grad_clip, float* dq,
+                          float* dk, float* dv, float* df, float* dW, float* dw_r, float* dH0,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One step of Eq. (10)-(12) for every (b, n), with the state kept in device memory: the decode
  * (token-by-token inference) form of the layer.  The notes point out that inference carries a
  * fixed-size recurrent state (§2.6); this call reads it, advances it by one token and writes it

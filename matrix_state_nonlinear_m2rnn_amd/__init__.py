@@ -36,7 +36,7 @@ EXPORTED = (
     "m2rnn_out_norm_fwd", "m2rnn_out_norm_bwd_workspace_size", "m2rnn_out_norm_bwd",
     "m2rnn_conv4_silu_fwd", "m2rnn_conv4_silu_bwd_workspace_size", "m2rnn_conv4_silu_bwd",
     "m2rnn_fwd_block_workspace_size", "m2rnn_fwd_block", "m2rnn_overlap_create", "m2rnn_overlap_destroy",
-    "m2rnn_fwd_noalloc", "m2rnn_fwd_noalloc_max_bytes",
+    "m2rnn_fwd_noalloc", "m2rnn_fwd_noalloc_max_bytes", "m2rnn_scan_bwd", "m2rnn_scan_bwd_finish",
 )
 
 
@@ -106,9 +106,11 @@ def lib() -> ctypes.CDLL:
         L.m2rnn_fwd_ckpt.argtypes = [dp, ci, ci, ci] + [vp] * 3 + [vp] * 4 + [vp, vp, vp] + [vp, sz, vp, vp]
         L.m2rnn_bwd_ckpt_workspace_size.restype = ci
         L.m2rnn_bwd_ckpt_workspace_size.argtypes = [dp, ci, ci, ctypes.POINTER(sz)]
-        L.m2rnn_bwd_ckpt.restype = ci
-        L.m2rnn_bwd_ckpt.argtypes = ([dp, ci, ci] + [vp] * 3 + [vp] * 3 + [vp] + [vp, vp] + [ctypes.c_float]
-                                     + [vp] * 7 + [vp, sz, vp])
+        for name in ("m2rnn_bwd_ckpt", "m2rnn_scan_bwd", "m2rnn_scan_bwd_finish"):
+            fn = getattr(L, name)
+            fn.restype = ci
+            fn.argtypes = ([dp, ci, ci] + [vp] * 3 + [vp] * 3 + [vp] + [vp, vp] + [ctypes.c_float] + [vp] * 7
+                           + [vp, sz, vp])
         i64, cf = ctypes.c_int64, ctypes.c_float
         for name, args in (
             ("m2rnn_gate_fwd", [i64] * 3 + [vp] * 4 + [vp]),
@@ -409,9 +411,7 @@ def m2rnn_bwd_ckpt_workspace_size(dims: Dims, qkv_dtype: int, math="auto") -> in
     return int(n.value)
 
 
-def m2rnn_bwd_ckpt(q, k, v, f, W, w_r, ckpt, dy, dH_T=None, *, math="auto", grad_clip: float = 0.0,
-                   want_dH0: bool = True, workspace=None, stream=None) -> Dict[str, object]:
-    """m2rnn_bwd from the checkpoints that m2rnn_fwd_ckpt kept (no forward re-run)."""
+def _call_bwd_ckpt(name, q, k, v, f, W, w_r, ckpt, dy, dH_T, math, grad_clip, want_dH0, workspace, stream, out):
     import torch
     dims, dt, m, _, _, _ = _fwd_prepare(q, k, v, f, W, w_r, None, None, None, math, 0, False)
     B, T, N, K, V, Nqk = dims.B, dims.T, dims.N, dims.K, dims.V, dims.Nqk
@@ -421,15 +421,44 @@ def m2rnn_bwd_ckpt(q, k, v, f, W, w_r, ckpt, dy, dH_T=None, *, math="auto", grad
     if dH_T is not None:
         _require(dH_T, "dH_T", torch.float32, (B, N, K, V), dev)
     e = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
-    out = {"dq": e(B, T, Nqk, K), "dk": e(B, T, Nqk, K), "dv": e(B, T, N, V), "df": e(B, T, N), "dW": e(N, V, V),
-           "dw_r": e(N, V), "dH0": e(B, N, K, V) if want_dH0 else None}
+    if out is None:
+        out = {"dq": e(B, T, Nqk, K), "dk": e(B, T, Nqk, K), "dv": e(B, T, N, V), "df": e(B, T, N),
+               "dW": e(N, V, V), "dw_r": e(N, V), "dH0": e(B, N, K, V) if want_dH0 else None}
+    shapes = {"dq": (B, T, Nqk, K), "dk": (B, T, Nqk, K), "dv": (B, T, N, V), "df": (B, T, N), "dW": (N, V, V),
+              "dw_r": (N, V), "dH0": (B, N, K, V)}
+    for g, shape in shapes.items():
+        if out.get(g) is not None or g != "dH0":
+            _require(out.get(g), g, torch.float32, shape, dev)
     nbytes = m2rnn_bwd_ckpt_workspace_size(dims, dt, m)
     ws = _workspace(nbytes, dev, workspace)
-    _check("m2rnn_bwd_ckpt", lib().m2rnn_bwd_ckpt(
+    _check(name, getattr(lib(), name)(
         ctypes.byref(dims), dt, m, _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r), _ptr(ckpt), _ptr(dy),
         _ptr(dH_T), float(grad_clip), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dW"]),
-        _ptr(out["dw_r"]), _ptr(out["dH0"]), _ptr(ws), nbytes, _stream(stream)))
+        _ptr(out["dw_r"]), _ptr(out.get("dH0")), _ptr(ws), nbytes, _stream(stream)))
     return out
+
+
+def m2rnn_bwd_ckpt(q, k, v, f, W, w_r, ckpt, dy, dH_T=None, *, math="auto", grad_clip: float = 0.0,
+                   want_dH0: bool = True, workspace=None, stream=None, out=None) -> Dict[str, object]:
+    """m2rnn_bwd from the checkpoints that m2rnn_fwd_ckpt kept (no forward re-run).  `out` may hold
+    the gradient tensors to write (a dict as returned)."""
+    return _call_bwd_ckpt("m2rnn_bwd_ckpt", q, k, v, f, W, w_r, ckpt, dy, dH_T, math, grad_clip, want_dH0, workspace,
+                          stream, out)
+
+
+def m2rnn_scan_bwd(q, k, v, f, W, w_r, ckpt, dy, dH_T=None, *, math="auto", grad_clip: float = 0.0,
+                   want_dH0: bool = True, workspace=None, stream=None, out=None) -> Dict[str, object]:
+    """The scale pass and the reverse scan of m2rnn_bwd_ckpt alone; m2rnn_scan_bwd_finish with the
+    same workspace and outputs completes it."""
+    return _call_bwd_ckpt("m2rnn_scan_bwd", q, k, v, f, W, w_r, ckpt, dy, dH_T, math, grad_clip, want_dH0, workspace,
+                          stream, out)
+
+
+def m2rnn_scan_bwd_finish(q, k, v, f, W, w_r, ckpt, dy, dH_T=None, *, math="auto", grad_clip: float = 0.0,
+                          workspace=None, stream=None, out=None) -> Dict[str, object]:
+    """The fixed-order sums of m2rnn_bwd_ckpt's per-workgroup partials (after m2rnn_scan_bwd)."""
+    return _call_bwd_ckpt("m2rnn_scan_bwd_finish", q, k, v, f, W, w_r, ckpt, dy, dH_T, math, grad_clip,
+                          out.get("dH0") is not None, workspace, stream, out)
 
 
 def m2rnn_bwd(q, k, v, f, W, w_r, H0, dy, dH_T=None, *, math="auto", grad_clip: float = 0.0, want_dH0: bool = True,

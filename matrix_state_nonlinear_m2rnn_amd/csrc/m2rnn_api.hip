@@ -670,12 +670,17 @@ int m2rnn_bwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, si
 
 namespace {
 
+// Parts of the backward: the checkpoint pass, the scale pass and the reverse scan, and the sums of
+// the per-workgroup partials.
+enum { BWD_SCAN = 1, BWD_SUMS = 2, BWD_ALL = 3 };
+
 // The backward; ckpt_in = the checkpoints of a forward that kept them (then no forward re-run), or
-// null (then the checkpoints are computed here, into the workspace).
+// null (then the checkpoints are computed here, into the workspace).  `parts` selects what runs.
 int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k, const void* v,
              const float* f, const float* W, const float* w_r, const float* H0, const float* ckpt_in,
              const float* dy, const float* dH_T, float grad_clip, float* dq, float* dk, float* dv, float* df,
-             float* dW, float* dw_r, float* dH0, void* workspace, size_t workspace_bytes, void* stream_) {
+             float* dW, float* dw_r, float* dH0, void* workspace, size_t workspace_bytes, void* stream_,
+             int parts = BWD_ALL) {
   int st = check_dims(dims, qkv_dtype);
   if (st) return st;
   if (!(grad_clip >= 0.0f)) return M2RNN_EINVAL;  // negative or NaN
@@ -697,6 +702,7 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
   const long N = d->N, V = d->V, K = d->K, B = d->B, T = d->T;
   if (T == 0) {
     // No steps: every gradient is zero except dH0 = dH_T.
+    if (!(parts & BWD_SUMS)) return M2RNN_OK;
     if ((st = fill(dW, nullptr, N * V * V, stream))) return st;
     if ((st = fill(dw_r, nullptr, N * V, stream))) return st;
     return fill(dH0, dH_T, B * N * K * V, stream);
@@ -710,56 +716,59 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
   // 1. Checkpoints: the state entering every I-th step, I = ckpt_interval (unless the forward kept
   //    them).
   const float* ckpt = ckpt_in ? ckpt_in : (const float*)(ws + L.ckpt);
-  if (!ckpt_in) {
-    FwdArgs a{};
-    a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.H0 = H0;
-    a.y = nullptr; a.H_T = nullptr; a.ckpt = (float*)(ws + L.ckpt);
-    a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S; a.seg = ckpt_interval((int)V);
-    a.nck = (int)((T + a.seg - 1) / a.seg);
-    a.ck0 = 0;
-    a.Ts = (int)T;
-    a.Tp = (int)T;
-    a.Nqk = qk_heads(d);
-    const void* kern = fwd_kernel(M2RNN_MATH_F16X3, (int)V, 1, 1, bf16, MODE_CKPT);
-    if (!kern) return M2RNN_EUNSUPPORTED;
-    void* args[] = {&a};
-    st = hip_status(hipLaunchKernel(kern, dim3((unsigned)(B * N * S)), dim3((unsigned)(4 * V)), args, 0, stream));
-    if (st) return st;
+  if (parts & BWD_SCAN) {
+    if (!ckpt_in) {
+      FwdArgs a{};
+      a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.H0 = H0;
+      a.y = nullptr; a.H_T = nullptr; a.ckpt = (float*)(ws + L.ckpt);
+      a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S; a.seg = ckpt_interval((int)V);
+      a.nck = (int)((T + a.seg - 1) / a.seg);
+      a.ck0 = 0;
+      a.Ts = (int)T;
+      a.Tp = (int)T;
+      a.Nqk = qk_heads(d);
+      const void* kern = fwd_kernel(M2RNN_MATH_F16X3, (int)V, 1, 1, bf16, MODE_CKPT);
+      if (!kern) return M2RNN_EUNSUPPORTED;
+      void* args[] = {&a};
+      st = hip_status(hipLaunchKernel(kern, dim3((unsigned)(B * N * S)), dim3((unsigned)(4 * V)), args, 0, stream));
+      if (st) return st;
+    }
+    // 2. The scale of every (b, n) pair: partial maxima of |dy| and |dH_T|.
+    const int P = absmax_parts(d);
+    {
+      const dim3 grid((unsigned)(B * P), (unsigned)((N * V + 1023) / 1024));
+      hipLaunchKernelGGL(m2rnn_bwd_absmax_kernel, grid, dim3(256), 0, stream, dy, dH_T, (int)T, (int)N, (int)K,
+                         (int)V, P, (float*)(ws + L.umax));
+      st = hip_status(hipGetLastError());
+      if (st) return st;
+    }
+    // 3. Reverse scan.
+    {
+      BwdArgs a{};
+      a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.dy = dy; a.dH_T = dH_T;
+      a.ckpt = ckpt;
+      a.subck = (float*)(ws + L.seg);
+      const bool sum_qk = shared_qk_sum(d);
+      a.dq = sum_qk ? (float*)(ws + L.dq) : dq;
+      a.dk = sum_qk ? (float*)(ws + L.dk) : dk;
+      a.dv = S > 1 ? (float*)(ws + L.dv) : dv;
+      a.df = S > 1 ? (float*)(ws + L.df) : df;
+      a.dW_part = (float*)(ws + L.dW);
+      a.dwr_part = (float*)(ws + L.dwr);
+      a.dH0 = dH0;
+      a.umax = (const float*)(ws + L.umax);
+      a.umax_parts = P;
+      a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S;
+      a.Nqk = qk_heads(d);
+      a.clip = grad_clip;
+      const void* kern = bwd_kernel((int)V, bf16);
+      if (!kern) return M2RNN_EUNSUPPORTED;
+      void* args[] = {&a};
+      st = hip_status(hipLaunchKernel(kern, dim3((unsigned)(B * N * S)), dim3((unsigned)(4 * V)), args, 0, stream));
+      if (st) return st;
+    }
   }
-  // 2. The scale of every (b, n) pair: partial maxima of |dy| and |dH_T|.
-  const int P = absmax_parts(d);
-  {
-    const dim3 grid((unsigned)(B * P), (unsigned)((N * V + 1023) / 1024));
-    hipLaunchKernelGGL(m2rnn_bwd_absmax_kernel, grid, dim3(256), 0, stream, dy, dH_T, (int)T, (int)N, (int)K, (int)V, P,
-                       (float*)(ws + L.umax));
-    st = hip_status(hipGetLastError());
-    if (st) return st;
-  }
-  // 3. Reverse scan.
-  {
-    BwdArgs a{};
-    a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.w_r = w_r; a.dy = dy; a.dH_T = dH_T;
-    a.ckpt = ckpt;
-    a.subck = (float*)(ws + L.seg);
-    const bool sum_qk = shared_qk_sum(d);
-    a.dq = sum_qk ? (float*)(ws + L.dq) : dq;
-    a.dk = sum_qk ? (float*)(ws + L.dk) : dk;
-    a.dv = S > 1 ? (float*)(ws + L.dv) : dv;
-    a.df = S > 1 ? (float*)(ws + L.df) : df;
-    a.dW_part = (float*)(ws + L.dW);
-    a.dwr_part = (float*)(ws + L.dwr);
-    a.dH0 = dH0;
-    a.umax = (const float*)(ws + L.umax);
-    a.umax_parts = P;
-    a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S;
-    a.Nqk = qk_heads(d);
-    a.clip = grad_clip;
-    const void* kern = bwd_kernel((int)V, bf16);
-    if (!kern) return M2RNN_EUNSUPPORTED;
-    void* args[] = {&a};
-    st = hip_status(hipLaunchKernel(kern, dim3((unsigned)(B * N * S)), dim3((unsigned)(4 * V)), args, 0, stream));
-    if (st) return st;
-  }
+  if (!(parts & BWD_SUMS)) return M2RNN_OK;
   // 4. Deterministic sums of the per-workgroup partials, and dw_r.
   if (S > 1) {
     const long plane = B * T * N * V;
@@ -822,6 +831,25 @@ int m2rnn_bwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, const void* 
   if (dims && dims->T > 0 && dims->B > 0 && dims->N > 0 && !ckpt) return M2RNN_EINVAL;
   return bwd_impl(dims, qkv_dtype, math, q, k, v, f, W, w_r, nullptr, ckpt, dy, dH_T, grad_clip, dq, dk, dv, df, dW,
                   dw_r, dH0, workspace, workspace_bytes, stream);
+}
+
+int m2rnn_scan_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k, const void* v,
+                   const float* f, const float* W, const float* w_r, const float* ckpt, const float* dy,
+                   const float* dH_T, float grad_clip, float* dq, float* dk, float* dv, float* df, float* dW,
+                   float* dw_r, float* dH0, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dims && dims->T > 0 && dims->B > 0 && dims->N > 0 && !ckpt) return M2RNN_EINVAL;
+  return bwd_impl(dims, qkv_dtype, math, q, k, v, f, W, w_r, nullptr, ckpt, dy, dH_T, grad_clip, dq, dk, dv, df, dW,
+                  dw_r, dH0, workspace, workspace_bytes, stream, BWD_SCAN);
+}
+
+int m2rnn_scan_bwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, const void* k,
+                          const void* v, const float* f, const float* W, const float* w_r, const float* ckpt,
+                          const float* dy, const float* dH_T, float grad_clip, float* dq, float* dk, float* dv,
+                          float* df, float* dW, float* dw_r, float* dH0, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (dims && dims->T > 0 && dims->B > 0 && dims->N > 0 && !ckpt) return M2RNN_EINVAL;
+  return bwd_impl(dims, qkv_dtype, math, q, k, v, f, W, w_r, nullptr, ckpt, dy, dH_T, grad_clip, dq, dk, dv, df, dW,
+                  dw_r, dH0, workspace, workspace_bytes, stream, BWD_SUMS);
 }
 
 int m2rnn_fwd_ckpt(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks, const void* q, const void* k,

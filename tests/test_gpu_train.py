@@ -137,3 +137,25 @@ def test_training_pair_on_the_bwd_workload():
         say("head", n, errs)
         for x, e in errs.items():
             assert e <= 1e-3, (n, x, e)
+
+
+def test_scan_and_finish_equal_the_checkpoint_backward():
+    # m2rnn_scan_bwd then m2rnn_scan_bwd_finish on one stream and workspace is m2rnn_bwd_ckpt, bit for
+    # bit (split rows and a shared q/k, whose partials go through the workspace).
+    torch = torch_cuda()
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    for B, T, N, K, V, shared in ((2, 130, 3, 32, 64, False), (1, 70, 4, 64, 16, True)):
+        d = inputs.make_inputs(B, T, N, K, V, qkv_dtype="bf16", seed=880 + T, with_H0=True, with_dy=True,
+                               with_dHT=True, shared_qk=shared)
+        dd = to_device(d, "bf16")
+        say("scan + finish", B, T, N, K, V, shared)
+        _, _, ck = fwd_ckpt(dd, "f16x3")
+        args = (dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], ck, dd["dy"], dd["dH_T"])
+        g0 = m2.m2rnn_bwd_ckpt(*args)
+        dims = m2.Dims(B, T, N, K, V, 1 if shared else N)
+        ws = torch.empty(m2.m2rnn_bwd_ckpt_workspace_size(dims, m2.DTYPE_BF16), dtype=torch.uint8, device="cuda")
+        g = m2.m2rnn_scan_bwd(*args, workspace=ws)
+        m2.m2rnn_scan_bwd_finish(*args, workspace=ws, out=g)
+        torch.cuda.synchronize()
+        for n in GRADS:
+            assert torch.equal(g[n], g0[n]), n
