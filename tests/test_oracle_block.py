@@ -81,6 +81,26 @@ def test_rmsnorm_output_has_unit_rms_and_is_scale_invariant():
     np.testing.assert_allclose(block.out_norm_fwd(y, big, np.ones((4, 8)), 0.0), ref.reshape(y.shape), rtol=1e-12)
 
 
+def test_rmsnorm_forward_matches_torch_rms_norm_with_gamma_and_eps():
+    # The per-feature scale and the epsilon against torch's own RMSNorm (a library routine), on the
+    # gated row x = y (.) SiLU(gz) over all N V features of a token.
+    torch = pytest.importorskip("torch")
+    r = rng(6)
+    B, T, N, V = 3, 5, 4, 8
+    y = r.normal(0, 1, (B, T, N, V))
+    gz = r.normal(0, 1.5, y.shape)
+    gamma = r.normal(1, 0.4, (N, V))
+    for eps in (1e-6, 1e-2, 0.7):
+        out = block.out_norm_fwd(y, gz, gamma, eps)
+        x = torch.from_numpy(y) * torch.nn.functional.silu(torch.from_numpy(gz))
+        ref = torch.nn.functional.rms_norm(x.reshape(B, T, N * V), (N * V,), weight=torch.from_numpy(gamma).reshape(-1),
+                                           eps=eps)
+        np.testing.assert_allclose(out, ref.reshape(B, T, N, V).numpy(), rtol=1e-12, atol=1e-14)
+    # and eps matters: a large eps shrinks the output where the mean square is small
+    small = 1e-3 * y
+    assert np.all(np.abs(block.out_norm_fwd(small, gz, gamma, 0.7)) < np.abs(block.out_norm_fwd(small, gz, gamma, 0.0)))
+
+
 def test_rmsnorm_backward_matches_torch_autograd_and_differences():
     torch = pytest.importorskip("torch")
     r = rng(5)
