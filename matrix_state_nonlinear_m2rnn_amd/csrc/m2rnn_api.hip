@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <mutex>
 #include <new>
 #include <unordered_map>
@@ -128,6 +129,27 @@ bool spills(const void* kernel) {
   return s;
 }
 
+// Whether the forward runs its readout in waves of their own where that kernel is built (the
+// default).  M2RNN_FWD_READOUT_WAVES=0 in the environment selects the single-role kernel, which
+// gives the same bits (for comparison).
+bool readout_waves() {
+  const char* e = getenv("M2RNN_FWD_READOUT_WAVES");
+  return !(e && e[0] == '0');
+}
+
+// The forward kernel of a launch (MODE_FWD: with readout waves where built) and its threads.
+const void* fwd_launch_kernel(const m2rnn_dims* d, int math, int rb, bool bf16, int mode, int* threads) {
+  const int rw = row_groups(d, rb, math);
+  if (mode == MODE_FWD && readout_waves()) {
+    if (const void* k = fwd_kernel(math, (int)d->V, rb, rw, bf16, MODE_FWD_RO)) {
+      *threads = (int)(8 * d->V * rw);
+      return k;
+    }
+  }
+  *threads = (int)(4 * d->V * rw);
+  return fwd_kernel(math, (int)d->V, rb, rw, bf16, mode);
+}
+
 // Row blocks per workgroup: among the kernels that keep everything in registers, the smallest
 // that lets every workgroup be resident at once (one wave of workgroups), else the one with the
 // fewest waves of workgroups.  A kernel that spills (several row blocks of a wide state) runs
@@ -145,14 +167,15 @@ int plan_row_blocks(const m2rnn_dims* d, int math, bool bf16, int mode, int requ
   for (int rb : {1, 2, 4}) {
     if (kb % rb != 0) continue;
     const int rw = row_groups(d, rb, math);
-    const void* kern = fwd_kernel(math, (int)d->V, rb, rw, bf16, mode);
+    int threads = 0;
+    const void* kern = fwd_launch_kernel(d, math, rb, bf16, mode, &threads);
     if (!kern) continue;
     if (info.cus > 0 && spills(kern)) {
       if (spilling < 0) spilling = rb;
       continue;
     }
     const long blocks = units * (kb / (rb * rw));
-    const int occ = info.cus > 0 ? occupancy(kern, (int)(4 * d->V * rw)) : 0;
+    const int occ = info.cus > 0 ? occupancy(kern, threads) : 0;
     const double cap = (double)occ * info.cus;
     const double rounds = cap > 0 ? (double)((blocks + (long)cap - 1) / (long)cap) : 1.0;
     if (rounds < best_rounds) {
@@ -283,10 +306,11 @@ int launch_scan_seg(const FwdCall& c, int math, int rb, long t0, long len, const
     a.ck0 = (int)(t0 / a.seg);
   }
   a.Ts = (int)d->T;
-  const void* kern = fwd_kernel(math, (int)d->V, rb, rw, bf16, MODE_FWD);
+  int threads = 0;
+  const void* kern = fwd_launch_kernel(d, math, rb, bf16, MODE_FWD, &threads);
   if (!kern) return M2RNN_EUNSUPPORTED;
   void* args[] = {&a};
-  const dim3 grid((unsigned)(d->B * d->N * S)), block((unsigned)(4 * d->V * rw));
+  const dim3 grid((unsigned)(d->B * d->N * S)), block((unsigned)threads);
   return hip_status(hipLaunchKernel(kern, grid, block, args, 0, c.stream));
 }
 

@@ -257,6 +257,8 @@ __device__ __forceinline__ float reduce_rows4(float x0, float x1, float x2, floa
 // MODE_FWD: full forward with readout.  MODE_CKPT: state only, storing the state that enters
 // every `seg`-step segment (used by the backward pass).
 enum { MODE_FWD = 0, MODE_CKPT = 1 };
+// MODE_FWD_RO: the forward with readout waves of its own (m2rnn_scan_fwd_ro_kernel), where built.
+constexpr int MODE_FWD_RO = 2;
 
 template <int V, int RB, int MATH, bool BF16IN, int MODE, int RW = 1>
 __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(const FwdArgs a) {
@@ -785,6 +787,360 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
     for (int rb = 0; rb < RB; ++rb)
       *(float4*)(a.H_T + state_base + (long)(row0 + 16 * rb + n) * V + 16 * w + 4 * g) =
           make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
+  }
+}
+
+// Forward scan with its readout and input staging in waves of their own (MODE_FWD of the split
+// contractions, one row group).  The workgroup has NT chain waves, which carry the recurrence exactly
+// as m2rnn_scan_fwd_kernel does (exchange reads, contraction, tanh and gate blend, publish of the
+// split state, the next step's rank-1 term), and NT readout waves, one per value tile, which
+//   - read the published split tile of H_{t-1} at step t (from the same exchange buffer the chain
+//     reads at that step), transpose it with two MFMAs against the identity, form its q-weighted
+//     row sums, and every four steps reduce across rows and store y (or the partial plane), and
+//   - stage the next chunk of q, k, v, f from HBM into the LDS ring.
+// Both roles meet at the one LDS barrier per step.  With two waves on every SIMD, the scheduler
+// fills one wave's waits (barrier, LDS round trip, MFMA latency) with the other's instructions, and
+// the chain waves no longer issue the readout and staging work at all.  The arithmetic is the same
+// as m2rnn_scan_fwd_kernel's, operation for operation, so the two give the same bits.
+template <int V, int RB, int MATH, bool BF16IN>
+__global__ void __launch_bounds__(2 * 64 * (V / 16)) m2rnn_scan_fwd_ro_kernel(const FwdArgs a) {
+  using Sh = FwdShape<V, 1>;
+  using St = Stage<V, RB>;
+  constexpr int NT = Sh::NT;
+  constexpr int TC = Sh::TC;
+  constexpr int ROWS = 16 * RB;
+  constexpr int NCH = NT / 2;  // 32-wide contraction chunks
+  constexpr int NOTH = NCH > 1 ? NCH - 1 : 1;
+  static_assert(MATH != MATH_F32 && NT >= 2 && NT % 2 == 0, "split contractions with an even tile count");
+  static_assert(TC % 4 == 0, "readout groups of four steps do not straddle chunks");
+
+  __shared__ __attribute__((aligned(16))) float stage[2][TC * St::STEP];
+  // Exchange buffer by step parity: [2][RB][NCH][hi|lo][half][64 lanes][2 dwords], as in
+  // m2rnn_scan_fwd_kernel.
+  constexpr int XWORDS = RB * NCH * 2 * 64 * 4;
+  __shared__ __attribute__((aligned(16))) uint32_t xbuf[2][XWORDS];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const bool chain = wave < NT;  // uniform in a wave
+  const int w = chain ? wave : wave - NT;  // value tile of this wave
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+
+  const int U = a.B * a.N;
+  int u, s;
+  if ((U & 7) == 0 && a.S > 1) {
+    const int slot = blockIdx.x >> 3;
+    s = slot % a.S;
+    u = (slot / a.S) * 8 + (blockIdx.x & 7);
+  } else {
+    u = blockIdx.x / a.S;
+    s = blockIdx.x % a.S;
+  }
+  const int b = u / a.N;
+  const int nh = u % a.N;
+  const int row0 = s * ROWS;
+  const long KV = (long)a.K * V;
+  const long state_base = ((long)b * a.N + nh) * KV;
+
+  if (chain) {
+    // ---------------- chain waves: the recurrence ----------------
+    const float* Wn = a.W + (long)nh * V * V;
+    const int col = 16 * w + n;
+    const int co = w >> 1;  // own chunk
+    uint4 wOwnHi, wOwnLo, wOthHi[NOTH], wOthLo[NOTH];
+    auto wchunk = [&](int t_lo, int t_hi, uint4& hi, uint4& lo) {
+      float wv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int tile = (i >> 2) ? t_hi : t_lo;
+        wv[i] = kTwoLog2e * Wn[(16 * tile + 4 * g + (i & 3)) * V + col];
+      }
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = wv[2 * i], x1 = wv[2 * i + 1];
+        if constexpr (MATH == MATH_F16X3) {
+          h[i] = pack_f16(x0, x1);
+          l[i] = pack_f16(x0 - f16_lo_to_f32(h[i]), x1 - f16_hi_to_f32(h[i]));
+        } else {
+          h[i] = pack_bf16(x0, x1);
+          l[i] = pack_bf16(x0 - bf16_lo_to_f32(h[i]), x1 - bf16_hi_to_f32(h[i]));
+        }
+      }
+      hi = make_uint4(h[0], h[1], h[2], h[3]);
+      lo = make_uint4(l[0], l[1], l[2], l[3]);
+    };
+    wchunk(w, w ^ 1, wOwnHi, wOwnLo);
+#pragma unroll
+    for (int i = 0; i < NCH - 1; ++i) {
+      const int cc = i < co ? i : i + 1;
+      wchunk(2 * cc, 2 * cc + 1, wOthHi[i], wOthLo[i]);
+    }
+
+    float H[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const long off = state_base + (long)(row0 + 16 * rb + n) * V + 16 * w + 4 * g;
+      if (a.H0) {
+        const float4 h = *(const float4*)(a.H0 + off);
+        H[rb][0] = h.x; H[rb][1] = h.y; H[rb][2] = h.z; H[rb][3] = h.w;
+      } else {
+        H[rb][0] = H[rb][1] = H[rb][2] = H[rb][3] = 0.0f;
+      }
+    }
+    uint4 hq[RB], lq[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) hq[rb] = lq[rb] = make_uint4(0, 0, 0, 0);
+    auto publish = [&](int buf) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        uint32_t h0, h1, l0, l1;
+        opaque4(H[rb]);  // the split is a function of the fp32 state alone
+        split_pair<MATH>(H[rb][0], H[rb][1], h0, l0);
+        split_pair<MATH>(H[rb][2], H[rb][3], h1, l1);
+        hq[rb].x = h0;
+        hq[rb].y = h1;
+        lq[rb].x = l0;
+        lq[rb].y = l1;
+        const int base = ((rb * NCH + (w >> 1)) * 4 + (w & 1)) * 128 + lane * 2;
+        *(uint2*)&xbuf[buf][base] = make_uint2(h0, h1);
+        if constexpr (MATH != MATH_BF16) *(uint2*)&xbuf[buf][base + 256] = make_uint2(l0, l1);
+      }
+    };
+    // Per-step inputs of the chain: the gate scalars and the rank-1 operands.
+    const int o_av = g == 0 ? St::OV + 16 * w + n : 3;
+    int o_bk[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) o_bk[rb] = g == 0 ? St::OK + 16 * rb + n : 3;
+    struct In {
+      float f, gf, m2g, av;
+      float bk[RB];
+    };
+    auto read_in = [&](const float* st) {
+      In r;
+      const float4 gate = *(const float4*)st;
+      r.f = gate.x;
+      r.gf = gate.y;
+      r.m2g = gate.z;
+      r.av = st[o_av];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) r.bk[rb] = st[o_bk[rb]];
+      return r;
+    };
+    int phi_off[RB], plo_off[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      phi_off[rb] = ((rb * NCH + co) * 4 + ((w & 1) ^ 1)) * 64 + lane;
+      plo_off[rb] = phi_off[rb] + 128;
+      asm volatile("" : "+v"(plo_off[rb]));
+    }
+
+    publish(0);
+    lds_barrier();  // the readout waves have staged chunk 0; every wave's H0 tile is published
+
+    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    In cur = read_in(stage[0]);
+    f32x4 kv[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) kv[rb] = mfma_f32(cur.av, cur.bk[rb], zero4);
+
+    auto run_chunk = [&](auto CB, int c0) __attribute__((always_inline)) {
+      constexpr int cb = decltype(CB)::value;
+#pragma unroll
+      for (int j = 0; j < TC; ++j) {
+        const int t = c0 + j;
+        if ((j % 8) == 0 && a.ckpt != nullptr) {
+          if (t % a.seg == 0 && t < a.T) {
+            float* dst = a.ckpt + ((long)(b * a.N + nh) * a.nck + a.ck0 + t / a.seg) * KV;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              *(float4*)(dst + (long)(row0 + 16 * rb + n) * V + 16 * w + 4 * g) =
+                  make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
+          }
+        }
+        const uint32_t* xr = xbuf[j & 1];
+        // (1) B operands: the partner half of the own chunk and the other chunks.
+        uint4 bh[RB * NOTH], bl[RB * NOTH];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const uint2 ph = ((const uint2*)xr)[phi_off[rb]];
+          hq[rb].z = ph.x;
+          hq[rb].w = ph.y;
+          if constexpr (MATH != MATH_BF16) {
+            const uint2 pl = ((const uint2*)xbuf[j & 1])[plo_off[rb]];
+            lq[rb].z = pl.x;
+            lq[rb].w = pl.y;
+          }
+#pragma unroll
+          for (int i = 0; i < NCH - 1; ++i) {
+            const int cc = i < co ? i : i + 1;
+            const int base = (rb * NCH + cc) * 4 * 128 + lane * 2;
+            const uint2 h0 = *(const uint2*)&xr[base], h1 = *(const uint2*)&xr[base + 128];
+            bh[rb * NOTH + i] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+            if constexpr (MATH != MATH_BF16) {
+              const uint2 l0 = *(const uint2*)&xr[base + 256], l1 = *(const uint2*)&xr[base + 384];
+              bl[rb * NOTH + i] = make_uint4(l0.x, l0.y, l1.x, l1.y);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // (2) contraction acc = (c k_t) v_t^T + W'^T H^T
+        f32x4 acc[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[rb] = kv[rb];
+        auto contract = [&](int rb, const uint4& Ahi, const uint4& Alo, const uint4& h, const uint4& l) {
+          if constexpr (MATH == MATH_F16X3) {
+            acc[rb] = mfma_f16(Ahi, h, acc[rb]);
+            acc[rb] = mfma_f16(Alo, h, acc[rb]);
+            acc[rb] = mfma_f16(Ahi, l, acc[rb]);
+          } else if constexpr (MATH == MATH_BF16X3) {
+            acc[rb] = mfma_bf16(Ahi, h, acc[rb]);
+            acc[rb] = mfma_bf16(Alo, h, acc[rb]);
+            acc[rb] = mfma_bf16(Ahi, l, acc[rb]);
+          } else {
+            acc[rb] = mfma_bf16(Ahi, h, acc[rb]);
+          }
+        };
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) contract(rb, wOwnHi, wOwnLo, hq[rb], lq[rb]);
+#pragma unroll
+        for (int i = 0; i < NCH - 1; ++i)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) contract(rb, wOthHi[i], wOthLo[i], bh[rb * NOTH + i], bl[rb * NOTH + i]);
+        // the next step's inputs (complete one barrier before this step; past the last step a stale
+        // record that is never used)
+        const In nxt = read_in(j + 1 == TC ? stage[cb ^ 1] : stage[cb] + (j + 1) * St::STEP);
+        // (3) tanh + gate blend, publish
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float keep = __builtin_fmaf(cur.f, H[rb][r], cur.gf);
+            H[rb][r] = __builtin_fmaf(cur.m2g, tanh_recip(acc[rb][r]), keep);
+          }
+        }
+        publish((j + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // (4) the rank-1 term of step t+1 in the shadow of the write
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) kv[rb] = mfma_f32(nxt.av, nxt.bk[rb], zero4);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        cur = nxt;
+      }
+    };
+    for (int c0 = 0; c0 < a.T; c0 += 2 * TC) {
+      run_chunk(std::integral_constant<int, 0>{}, c0);
+      if (c0 + TC < a.T) run_chunk(std::integral_constant<int, 1>{}, c0 + TC);
+    }
+    if (a.H_T) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        *(float4*)(a.H_T + state_base + (long)(row0 + 16 * rb + n) * V + 16 * w + 4 * g) =
+            make_float4(H[rb][0], H[rb][1], H[rb][2], H[rb][3]);
+    }
+  } else {
+    // ---------------- readout waves: y and the staging of the inputs ----------------
+    const int rtid = tid - Sh::NTH;  // thread index among the readout waves
+    const int ycol = 16 * w + n;
+    const float wrv = a.S == 1 ? a.w_r[(long)nh * V + ycol] : 0.0f;
+    const int ystep = a.N * V;
+    const long plane = (long)a.B * a.Tp * a.N * V;
+    float* ybase = a.y + (a.S > 1 ? (long)s * plane : 0) + ((long)b * a.Tp * a.N + nh) * V;
+    const __amdgpu_buffer_rsrc_t yres =
+        __builtin_amdgcn_make_buffer_rsrc(ybase, (short)0, (a.T * a.N - nh) * V * 4, kBufferRsrcWord3);
+    const uint32_t ylane = (uint32_t)((g * ystep + ycol) * 4);
+    const int vlane = g * St::STEP + St::OV + ycol;  // v[ycol] of step g of a group, in the stage
+    const int qlane = St::OQ + 4 * g;                // q of rows 4g .. 4g+3 (+ 16 rb)
+    uint2 bsel;
+    {
+      const uint32_t one = MATH == MATH_F16X3 ? 0x3C00u : 0x3F80u;
+      uint32_t e16[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) e16[e] = (n == 4 * g + e) ? one : 0u;
+      bsel = make_uint2(e16[0] | (e16[1] << 16), e16[2] | (e16[3] << 16));
+    }
+    int tile_off[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) tile_off[rb] = ((rb * NCH + (w >> 1)) * 4 + (w & 1)) * 128 + lane * 2;
+    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    float xq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Readout of step tr (state H_tr in exchange buffer xb, q_tr in record `st`): the q-weighted sum of
+    // the transposed tile over this lane's rows, kept for the group of four steps.
+    auto readout = [&](const uint32_t* xb, const float* st, int slot) __attribute__((always_inline)) {
+      f32x4 yT[RB];
+      float4 q4[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const uint2 oh = *(const uint2*)&xb[tile_off[rb]];
+        uint2 ol = make_uint2(0, 0);
+        if constexpr (MATH != MATH_BF16) ol = *(const uint2*)&xb[tile_off[rb] + 256];
+        q4[rb] = *(const float4*)(st + qlane + 16 * rb);
+        if constexpr (MATH == MATH_F16X3) {
+          yT[rb] = mfma16_f16(ol, bsel, mfma16_f16(oh, bsel, zero4));
+        } else if constexpr (MATH == MATH_BF16X3) {
+          yT[rb] = mfma16_bf16(ol, bsel, mfma16_bf16(oh, bsel, zero4));
+        } else {
+          yT[rb] = mfma16_bf16(oh, bsel, zero4);
+        }
+      }
+      float x = 0.0f;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        x = rb == 0 ? q4[rb].x * yT[rb][0] : __builtin_fmaf(q4[rb].x, yT[rb][0], x);
+        x = __builtin_fmaf(q4[rb].y, yT[rb][1], x);
+        x = __builtin_fmaf(q4[rb].z, yT[rb][2], x);
+        x = __builtin_fmaf(q4[rb].w, yT[rb][3], x);
+      }
+      xq[slot] = x;
+    };
+    // The group of four steps starting at step tg, its v records starting at `vst`: one cross-row
+    // reduction leaves lane (g, j) with y[tg + g][16w + j].
+    auto store_group = [&](int tg, const float* vst) __attribute__((always_inline)) {
+      float yv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
+      yv = __builtin_fmaf(wrv, vst[vlane], yv);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, ylane + (uint32_t)(tg * ystep * 4), 0, 0);
+    };
+
+    ChunkRegs<V, RB, BF16IN, 1> pre;
+    pre.load(a, b, nh, row0, 0, rtid);
+    pre.store(stage[0], rtid);
+    if (a.T > TC) pre.load(a, b, nh, row0, TC, rtid);
+    lds_barrier();
+
+    auto run_chunk = [&](auto CB, int c0) __attribute__((always_inline)) {
+      constexpr int cb = decltype(CB)::value;
+#pragma unroll
+      for (int j = 0; j < TC; ++j) {
+        const int t = c0 + j;
+        // readout of step t-1 (published at step t-1 into the buffer the chain reads now)
+        if (j > 0 || c0 > 0) {
+          const float* st = j == 0 ? stage[cb ^ 1] + (TC - 1) * St::STEP : stage[cb] + (j - 1) * St::STEP;
+          readout(xbuf[j & 1], st, (j + 3) & 3);
+          if (j % 4 == 0) store_group(t - 4, j == 0 ? stage[cb ^ 1] + (TC - 4) * St::STEP : stage[cb] + (j - 4) * St::STEP);
+        }
+        if (j == TC - 2) pre.store(stage[cb ^ 1], rtid);
+        lds_barrier();
+        if (j == TC - 2) {
+          const int t_next = c0 + 2 * TC;  // first step of the chunk after the one just staged
+          if (t_next < a.T) pre.load(a, b, nh, row0, t_next, rtid);
+        }
+      }
+    };
+    for (int c0 = 0; c0 < a.T; c0 += 2 * TC) {
+      run_chunk(std::integral_constant<int, 0>{}, c0);
+      if (c0 + TC < a.T) run_chunk(std::integral_constant<int, 1>{}, c0 + TC);
+    }
+    // the last step of the last chunk, and its group
+    const int tp = (a.T + TC - 1) / TC * TC;
+    if (tp > 0) {
+      const int cbl = (tp / TC - 1) & 1;
+      readout(xbuf[tp & 1], stage[cbl] + (TC - 1) * St::STEP, 3);
+      store_group(tp - 4, stage[cbl] + (TC - 4) * St::STEP);
+    }
   }
 }
 
