@@ -373,7 +373,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   // forward contraction: A = (c W)^T, A[m][k] = c W[k][16w + m]   (as in the forward scan)
   // backward chain:      A = W,       A[m][k] = W[16w + m][k]
   // Chunk cc covers tiles 2cc (k-slots 0..3) and 2cc+1 (k-slots 4..7).  The chunk co = w/2 holding
-  // this wave's own tile is listed first ("own"), the others after it.
+  // this wave's own tile is listed first ("own"), with the own tile in k-slots 0..3 and its partner
+  // w ^ 1 in 4..7 (so that the own halves come from registers); the others after it.
   const float* Wn = a.W + (long)nh * V * V;
   const int col = 16 * w + n;
   const int co = w >> 1;
@@ -395,8 +396,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     lo = make_uint4(l[0], l[1], l[2], l[3]);
   };
   uint4 fOwnHi, fOwnLo, bOwnHi, bOwnLo, fOthHi[NOTH], fOthLo[NOTH], bOthHi[NOTH], bOthLo[NOTH];
-  wchunk(2 * co, 2 * co + 1, true, fOwnHi, fOwnLo);
-  wchunk(2 * co, 2 * co + 1, false, bOwnHi, bOwnLo);
+  wchunk(w, w ^ 1, true, fOwnHi, fOwnLo);
+  wchunk(w, w ^ 1, false, bOwnHi, bOwnLo);
 #pragma unroll
   for (int i = 0; i < NCH - 1; ++i) {
     const int cc = i < co ? i : i + 1;
@@ -424,23 +425,23 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     *(uint2*)(entry + tile_off(w, 0) + 2 * own_slot) = hi;
     *(uint2*)(entry + tile_off(w, 1) + 2 * own_slot) = lo;
   };
-  // B operands of one contraction from a step's entry, every chunk read whole (the own tile too,
-  // so that each read lands in its operand registers); a single tile (no partner) is taken from
-  // registers with zeros in k-slots 4..7.
+  // B operands of one contraction from a step's entry: the partner half of the own chunk and every
+  // other chunk read whole (the own tile's halves are in registers); a single tile (no partner)
+  // gets zeros in k-slots 4..7.
   struct Ops {
-    uint4 wh, wl;  // own chunk
+    uint2 ph, pl;  // partner tile of the own chunk
     uint4 oh[NOTH], ol[NOTH];
   };
+  // (the lo read's offset goes through an empty asm so that the two 8-byte partner reads are not
+  // paired into one instruction, whose four destination registers would then need copies)
+  int plo = tile_off(w ^ 1, 1) + 2 * own_slot;
+  asm volatile("" : "+v"(plo));
   auto read_ops = [&](const uint32_t* entry) {
     Ops o;
-    o.wh = o.wl = make_uint4(0, 0, 0, 0);
+    o.ph = o.pl = make_uint2(0, 0);
     if constexpr (has_partner) {
-      const uint2 h0 = *(const uint2*)(entry + tile_off(2 * co, 0) + 2 * own_slot);
-      const uint2 h1 = *(const uint2*)(entry + tile_off(2 * co + 1, 0) + 2 * own_slot);
-      const uint2 l0 = *(const uint2*)(entry + tile_off(2 * co, 1) + 2 * own_slot);
-      const uint2 l1 = *(const uint2*)(entry + tile_off(2 * co + 1, 1) + 2 * own_slot);
-      o.wh = make_uint4(h0.x, h0.y, h1.x, h1.y);
-      o.wl = make_uint4(l0.x, l0.y, l1.x, l1.y);
+      o.ph = *(const uint2*)(entry + tile_off(w ^ 1, 0) + 2 * own_slot);
+      o.pl = *(const uint2*)(entry + plo);
     }
 #pragma unroll
     for (int i = 0; i < NCH - 1; ++i) {
@@ -457,8 +458,8 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   // acc += A B over all chunks (three split passes per chunk).
   auto contract = [&](f32x4 acc, const uint4& AownHi, const uint4& AownLo, const uint4 (&AothHi)[NOTH],
                       const uint4 (&AothLo)[NOTH], const uint2& own_hi, const uint2& own_lo, const Ops& o) {
-    const uint4 bh = has_partner ? o.wh : make_uint4(own_hi.x, own_hi.y, 0, 0);
-    const uint4 bl = has_partner ? o.wl : make_uint4(own_lo.x, own_lo.y, 0, 0);
+    const uint4 bh = make_uint4(own_hi.x, own_hi.y, o.ph.x, o.ph.y);
+    const uint4 bl = make_uint4(own_lo.x, own_lo.y, o.pl.x, o.pl.y);
     acc = mfma_f16(AownHi, bh, acc);
     acc = mfma_f16(AownLo, bh, acc);
     acc = mfma_f16(AownHi, bl, acc);
@@ -644,16 +645,17 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     }
     put_tile(dx + (ONE ? 0 : (j & 1) * ENTRY), D, fr.dh, fr.dl);
     __builtin_amdgcn_sched_barrier(0);
-    float Hp[4];  // H_{t-1}
-    Hp[0] = f16_lo_to_f32(in.h_hi.x) + f16_lo_to_f32(in.h_lo.x);
-    Hp[1] = f16_hi_to_f32(in.h_hi.x) + f16_hi_to_f32(in.h_lo.x);
-    Hp[2] = f16_lo_to_f32(in.h_hi.y) + f16_lo_to_f32(in.h_lo.y);
-    Hp[3] = f16_hi_to_f32(in.h_hi.y) + f16_hi_to_f32(in.h_lo.y);
+    // H_{t-1} - Z_t from the fp16 halves of H_{t-1}: (hi - Z) + lo, each a v_fma_mix_f32
+    float HmZ[4];
+    HmZ[0] = add_mix_f16<false>(in.h_lo.x, add_mix_f16<false>(in.h_hi.x, -Z[0]));
+    HmZ[1] = add_mix_f16<true>(in.h_lo.x, add_mix_f16<true>(in.h_hi.x, -Z[1]));
+    HmZ[2] = add_mix_f16<false>(in.h_lo.y, add_mix_f16<false>(in.h_hi.y, -Z[2]));
+    HmZ[3] = add_mix_f16<true>(in.h_lo.y, add_mix_f16<true>(in.h_hi.y, -Z[3]));
     fr.dk_l = fr.df_l = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       fr.cinit[r] = in.f * R[r];
-      fr.df_l = __builtin_fmaf(R[r], Hp[r] - Z[r], fr.df_l);
+      fr.df_l = __builtin_fmaf(R[r], HmZ[r], fr.df_l);
       fr.dk_l = __builtin_fmaf(D[r], vv[r], fr.dk_l);
       dwr4[r] = __builtin_fmaf(uu[r], vv[r], dwr4[r]);
     }
@@ -778,10 +780,15 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     hook_tail();
 
     // dv[col 16w + i] = sum_rows D[row][col] k[row] (+ w_r u when this workgroup holds all rows).
-    float x = k4.x * (f16_lo_to_f32(dThi.x) + f16_lo_to_f32(dTlo.x));
-    x = __builtin_fmaf(k4.y, f16_hi_to_f32(dThi.x) + f16_hi_to_f32(dTlo.x), x);
-    x = __builtin_fmaf(k4.z, f16_lo_to_f32(dThi.y) + f16_lo_to_f32(dTlo.y), x);
-    x = __builtin_fmaf(k4.w, f16_hi_to_f32(dThi.y) + f16_hi_to_f32(dTlo.y), x);
+    // (hi and lo halves of D each times k, one v_fma_mix_f32 apiece)
+    float x = fma_mix_f16<false>(dThi.x, k4.x, 0.0f);
+    x = fma_mix_f16<false>(dTlo.x, k4.x, x);
+    x = fma_mix_f16<true>(dThi.x, k4.y, x);
+    x = fma_mix_f16<true>(dTlo.x, k4.y, x);
+    x = fma_mix_f16<false>(dThi.y, k4.z, x);
+    x = fma_mix_f16<false>(dTlo.y, k4.z, x);
+    x = fma_mix_f16<true>(dThi.y, k4.w, x);
+    x = fma_mix_f16<true>(dTlo.y, k4.w, x);
     if constexpr (GROUP4) {
       // Steps j .. j+3 are collected in xq; one cross-row reduction of the four leaves lane (g, i)
       // with dv[step j0 + g][16w + i].
