@@ -309,7 +309,8 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint32_t* p) {
 }
 
 template <int V, bool BF16IN>
-__global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(64 * (V / 16)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+m2rnn_scan_bwd_kernel(const BwdArgs a) {
   constexpr bool SUBCK = BwdCkpt<V>::sub;  // checkpoints at every sub-segment
   constexpr int NT = V / 16;
   constexpr int NTH = 64 * NT;
@@ -343,7 +344,10 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
   // Per-wave partial sums of dq, dk (per row) and df over the sub-segment's steps (several waves;
   // red_f holds 16 equal copies, one per lane of a row, so that every lane stores).
   constexpr int RED = ONE ? 1 : SUB;
-  __shared__ float red_q[RED][NT][16], red_k[RED][NT][16], red_f[RED][NT][16];
+  __shared__ float red[3][RED][NT][16];
+  auto& red_q = red[0];
+  auto& red_k = red[1];
+  auto& red_f = red[2];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -598,6 +602,32 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     }
   };
   auto finalize = [&](int tb) { finalize2(tb, tb); };
+  // The interleaved walk sums the four waves' partials of one group of four steps in the step
+  // after they are written, one gradient per wave: wave 0 dq, wave 1 dk, wave 2 df (lane (g, n):
+  // step t0 + g, row n), in the order of finalize2.  group_read issues the reads of groups jq (dq)
+  // and jk (dk, df) of the partial arrays, group_store adds and stores them (first steps tq, tk;
+  // a negative first step stores nothing).
+  const int wv = __builtin_amdgcn_readfirstlane(w);
+  auto group_read = [&](int jq, int jk, float (&x)[4]) __attribute__((always_inline)) {
+    const float* src = &red[min(wv, 2)][(wv == 0 ? jq : jk) + g][0][n];
+#pragma unroll
+    for (int ww = 0; ww < NT; ++ww) x[ww] = src[ww * 16];
+  };
+  auto group_store = [&](const float (&x)[4], int tq, int tk) __attribute__((always_inline)) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < NT; ++ww) acc += x[ww];
+    const uint32_t val = __float_as_uint(acc * ug);
+    if (wv == 0) {
+      if (tq >= 0) __builtin_amdgcn_raw_buffer_store_b32(val, dqres, qk_lane + (uint32_t)(tq * qkstep * 4), 0, 0);
+    } else if (wv == 1) {
+      if (tk >= 0) __builtin_amdgcn_raw_buffer_store_b32(val, dkres, qk_lane + (uint32_t)(tk * qkstep * 4), 0, 0);
+    } else if (wv == 2) {
+      if (tk >= 0)
+        __builtin_amdgcn_raw_buffer_store_b32(
+            val, dfres, df_lane == kBufferDrop ? kBufferDrop : df_lane + (uint32_t)(tk * a.N * 4), 0, 0);
+    }
+  };
 
   // Lane partials of the current group of four steps: dv, dk, df (walk) and dq (recompute).
   float xq[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xk[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -712,6 +742,14 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     // Step j's exchange reads (chain operands, transposed tiles for dW and dv), and step j-1's
     // inputs.
     const Ops o = read_ops(dxp);
+    hook_reads();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Chain: C_{t-1} = f R + D W^T on the split-precision MFMA.
+    const f32x4 acc =
+        contract(fr.cinit, bOwnHi, bOwnLo, bOthHi, bOthLo, fr.dh, fr.dl, o);
+    // The reads that the chains do not wait for, issued behind the chain's MFMAs: the transposed
+    // tiles for dW and dv, and step j-1's inputs.
     const uint2 hT = lds_read_tr(hj + tile_off(w, 0) + 2 * tr_slot);
     uint2 dT[NT];
 #pragma unroll
@@ -721,19 +759,16 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     const uint2 dTlo = lds_read_tr(dxp + tile_off(w, 1) + 2 * tr_slot);
     const float4 k4 = *(const float4*)(st + St::OK + 4 * g);
     if (j > 0) nxt = load_rev(ss, hs, zs, j - 1);
-    hook_reads();
-    __builtin_amdgcn_sched_barrier(0);
-
-    // Chain: C_{t-1} = f R + D W^T on the split-precision MFMA.
-    const f32x4 acc =
-        contract(fr.cinit, bOwnHi, bOwnLo, bOthHi, bOthLo, fr.dh, fr.dl, o);
-    hook_mfma();
-
-    // dW[16w + m][16tt + j] += sum_rows H_{t-1}[row][16w + m] D[row][16tt + j]: one fp16 16x16x16
-    // MFMA per D tile, both operands read transposed from LDS (rows on the contraction index).
+#ifdef BWD_ILV
+    // one chain MFMA, then three reads, six times
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) dWacc[tt] = mfma16_f16(hT, dT[tt], dWacc[tt]);
-
+    for (int q = 0; q < 6; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+#endif
+    __builtin_amdgcn_sched_barrier(0);
+    hook_mfma();
     // Off the chain, while the MFMAs run.  dk, df: sums over this wave's 16 columns (the four
     // lane rows); df also over the 16 rows.  Grouped: steps j .. j+3 (j % 4 == 0) reduced
     // together, lane (g, n) ending with step j + g.
@@ -777,8 +812,15 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
 #pragma unroll
     for (int r = 0; r < 4; ++r) C[r] = __builtin_amdgcn_fmed3f(acc[r], lo, hi);
     if (j > 0) fr = front(j - 1, nxt);
-    hook_tail();
-
+    __builtin_amdgcn_sched_barrier(0);
+    // The cross-wave sums of one group of four steps (interleaved walk): at j = 3, dk and df of
+    // steps tb + 4 .. 7 and the recompute's dq of steps tb - SUB .. tb - SUB + 3; at j = 7, dk and
+    // df of steps tb + SUB .. tb + SUB + 3 (written at the last step of the previous pair) and the
+    // recompute's dq of steps tb + 4 .. 7.
+    float gx[4];
+    if constexpr (INTERLEAVE) {
+      if ((j & 3) == 3) group_read(j == 3 ? 0 : 4, j == 3 ? 4 : 0, gx);
+    }
     // dv[col 16w + i] = sum_rows D[row][col] k[row] (+ w_r u when this workgroup holds all rows).
     // (hi and lo halves of D each times k, one v_fma_mix_f32 apiece)
     float x = fma_mix_f16<false>(dThi.x, k4.x, 0.0f);
@@ -806,7 +848,19 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv * ug), dvres,
                                             g == 0 ? dv_lane + (uint32_t)(js * ystep * 4) : kBufferDrop, 0, 0);
     }
+  
+    // dW[16w + m][16tt + j] += sum_rows H_{t-1}[row][16w + m] D[row][16tt + j]: one fp16 16x16x16
+    // MFMA per D tile, both operands read transposed from LDS (rows on the contraction index).
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) dWacc[tt] = mfma16_f16(hT, dT[tt], dWacc[tt]);
+
+    hook_tail();
+    if constexpr (INTERLEAVE) {
+      if ((j & 3) == 3) group_store(gx, j == 3 ? tb - SUB : tb + 4, j == 3 ? tb + 4 : tb + SUB);
+    }
+
   };
+
   auto none = [] {};
 
   // Sub-segment checkpoints: the stage records of the next sub-segment to walk, in registers.
@@ -853,11 +907,14 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       for (int j = 0; j < SUB; ++j) {
         float Z[4];
         const float* st = ss + j * St::STEP;
+        float gx[4];
+        if (j == 4) group_read(0, 0, gx);  // dq of steps 0 .. 3 of this sub-segment
         fwd_step(st, j + 1 < SUB ? st + St::STEP : nullptr, hsb(P - 1) + j * ENTRY,
                  j + 1 < SUB ? hsb(P - 1) + (j + 1) * ENTRY : nullptr, kv, Hr, Z, hh, hl);
         *(float4*)(zsb(P - 1) + ((j * NT + w) * 64 + lane) * 4) = make_float4(Z[0], Z[1], Z[2], Z[3]);
         __builtin_amdgcn_sched_barrier(0);
         rec_dq(Hr, st, j, (P - 1) * SUB);
+        if (j == 4) group_store(gx, (P - 1) * SUB, -1);
         lds_barrier();
       }
     }
@@ -865,7 +922,6 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
     for (int p = P - 1; p >= 0; --p) {
       lds_barrier();  // the previous pair of sub-segments is done with the buffers of p - 1
       take(p - 1);    // (at p = 0 a repeat of sub-segment 0, recomputed and never used)
-      finalize2(p * SUB, p + 1 < P ? (p + 1) * SUB : -1);
       prefetch(p - 2);
       lds_barrier();
 
@@ -916,7 +972,11 @@ __global__ void __launch_bounds__(64 * (V / 16)) m2rnn_scan_bwd_kernel(const Bwd
       }
     }
     lds_barrier();
-    finalize2(-1, 0);
+    {
+      float x[4];
+      group_read(0, 0, x);
+      group_store(x, -1, 0);  // dk, df of steps 0 .. 3
+    }
   } else {
     for (int seg = nseg - 1; seg >= 0; --seg) {
       const int t0 = seg * kBwdSeg;
