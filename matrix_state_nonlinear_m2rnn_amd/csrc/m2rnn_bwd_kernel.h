@@ -575,6 +575,9 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
   // dw_r[16w + 4g + r] partial over this batch entry (every lane of a row group holds the same sums;
   // the workgroups with s == 0 write them).
   float dwr4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // (grouped steps: lane (g, n) sums the products of column 16w + n at the steps congruent to g mod 4
+  // instead, and the four lane rows are added at the end)
+  float dwr1 = 0.0f;
 
   // dq, dk, df of the sub-segment's steps [tb, tb + SUB) from the per-wave partials.
   // (tbq: first step of the sub-segment whose dq is pending, tbk: whose dk, df; < 0: none.)
@@ -677,25 +680,26 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     // H_{t-1} - Z_t from the fp16 halves of H_{t-1}: (hi - Z) + lo, each a v_fma_mix_f32
     float HmZ[4];
-    HmZ[0] = add_mix_f16<false>(in.h_lo.x, add_mix_f16<false>(in.h_hi.x, -Z[0]));
-    HmZ[1] = add_mix_f16<true>(in.h_lo.x, add_mix_f16<true>(in.h_hi.x, -Z[1]));
-    HmZ[2] = add_mix_f16<false>(in.h_lo.y, add_mix_f16<false>(in.h_hi.y, -Z[2]));
-    HmZ[3] = add_mix_f16<true>(in.h_lo.y, add_mix_f16<true>(in.h_hi.y, -Z[3]));
+    HmZ[0] = add_mix_f16<false>(in.h_lo.x, sub_mix_f16<false>(in.h_hi.x, Z[0]));
+    HmZ[1] = add_mix_f16<true>(in.h_lo.x, sub_mix_f16<true>(in.h_hi.x, Z[1]));
+    HmZ[2] = add_mix_f16<false>(in.h_lo.y, sub_mix_f16<false>(in.h_hi.y, Z[2]));
+    HmZ[3] = add_mix_f16<true>(in.h_lo.y, sub_mix_f16<true>(in.h_hi.y, Z[3]));
     fr.dk_l = fr.df_l = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       fr.cinit[r] = in.f * R[r];
       fr.df_l = __builtin_fmaf(R[r], HmZ[r], fr.df_l);
       fr.dk_l = __builtin_fmaf(D[r], vv[r], fr.dk_l);
-      dwr4[r] = __builtin_fmaf(uu[r], vv[r], dwr4[r]);
+      if constexpr (!GROUP4) dwr4[r] = __builtin_fmaf(uu[r], vv[r], dwr4[r]);
     }
     return fr;
   };
 
   // dq of a recomputed step j of the sub-segment starting at step tb (H = H_t): grouped four steps
   // at a time (lane (g, n) ends with step j0 + g, j0 = j & ~3).
-  auto rec_dq = [&](const float (&Hn)[4], const float* st, int j, int tb) __attribute__((always_inline)) {
-    const float4 u4 = *(const float4*)(st + St::OU + 16 * w + 4 * g);
+  // (u4: the step's u at this lane's four columns, read by the caller ahead of use)
+  auto rec_u4 = [&](const float* st) { return *(const float4*)(st + St::OU + 16 * w + 4 * g); };
+  auto rec_dq = [&](const float (&Hn)[4], const float4 u4, int j, int tb) __attribute__((always_inline)) {
     float dq_l = Hn[0] * u4.x;
     dq_l = __builtin_fmaf(Hn[1], u4.y, dq_l);
     dq_l = __builtin_fmaf(Hn[2], u4.z, dq_l);
@@ -751,14 +755,22 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
     // The reads that the chains do not wait for, issued behind the chain's MFMAs: the transposed
     // tiles for dW and dv, and step j-1's inputs.
     const uint2 hT = lds_read_tr(hj + tile_off(w, 0) + 2 * tr_slot);
+    // (dT[tt] is tile w + tt mod NT, so that the own tile, which dv also reads, is dT[0])
     uint2 dT[NT];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) dT[tt] = lds_read_tr(dxp + tile_off(tt, 0) + 2 * tr_slot);
-    // (the own tile read again rather than selected from dT, which would wait for those reads)
-    const uint2 dThi = lds_read_tr(dxp + tile_off(w, 0) + 2 * tr_slot);
+    for (int tt = 0; tt < NT; ++tt) dT[tt] = lds_read_tr(dxp + tile_off((w + tt) & (NT - 1), 0) + 2 * tr_slot);
+    const uint2 dThi = dT[0];
     const uint2 dTlo = lds_read_tr(dxp + tile_off(w, 1) + 2 * tr_slot);
     const float4 k4 = *(const float4*)(st + St::OK + 4 * g);
     if (j > 0) nxt = load_rev(ss, hs, zs, j - 1);
+    // (grouped steps: u and v of step j + g at column 16w + n, for dv's w_r term and dw_r)
+    float ucol = 0.0f, vcol = 0.0f;
+    if constexpr (GROUP4) {
+      if ((j & 3) == 0) {
+        ucol = ss[(j + g) * St::STEP + St::OU + 16 * w + n];
+        vcol = ss[(j + g) * St::STEP + St::OV + 16 * w + n];
+      }
+    }
 #ifdef BWD_ILV
     // one chain MFMA, then three reads, six times
 #pragma unroll
@@ -837,7 +849,7 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
       xq[j & 3] = x;
       if ((j & 3) == 0) {
         float dvv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
-        const float ucol = ss[(j + g) * St::STEP + St::OU + 16 * w + n];
+        dwr1 = __builtin_fmaf(ucol, vcol, dwr1);  // dw_r's product of step j + g, column 16w + n
         dvv = __builtin_fmaf(wr_col, ucol, dvv);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv * ug), dvres, dv_lane + (uint32_t)(js * ystep * 4), 0, 0);
       }
@@ -849,7 +861,7 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
                                             g == 0 ? dv_lane + (uint32_t)(js * ystep * 4) : kBufferDrop, 0, 0);
     }
   
-    // dW[16w + m][16tt + j] += sum_rows H_{t-1}[row][16w + m] D[row][16tt + j]: one fp16 16x16x16
+    // dW[16w + m][16u + j] += sum_rows H_{t-1}[row][16w + m] D[row][16u + j], u = w + tt mod NT: one fp16 16x16x16
     // MFMA per D tile, both operands read transposed from LDS (rows on the contraction index).
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) dWacc[tt] = mfma16_f16(hT, dT[tt], dWacc[tt]);
@@ -913,7 +925,7 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
                  j + 1 < SUB ? hsb(P - 1) + (j + 1) * ENTRY : nullptr, kv, Hr, Z, hh, hl);
         *(float4*)(zsb(P - 1) + ((j * NT + w) * 64 + lane) * 4) = make_float4(Z[0], Z[1], Z[2], Z[3]);
         __builtin_amdgcn_sched_barrier(0);
-        rec_dq(Hr, st, j, (P - 1) * SUB);
+        rec_dq(Hr, rec_u4(st), j, (P - 1) * SUB);
         if (j == 4) group_store(gx, (P - 1) * SUB, -1);
         lds_barrier();
       }
@@ -940,6 +952,7 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
         // Recompute step i of sub-segment p - 1 (as fwd_step, split around the walk step's phases).
         const float* st = rs + i * St::STEP;
         Ops ro;
+        float4 uq4;
         float avn = 0.0f, bkn = 0.0f, f = 0.0f;
         f32x4 racc;
         walk_step(
@@ -951,6 +964,7 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
                 bkn = st[St::STEP + (g == 0 ? St::OCK + n : 3)];
               }
               f = st[0];
+              uq4 = rec_u4(st);
             },
             [&]() __attribute__((always_inline)) { racc = contract(kv, fOwnHi, fOwnLo, fOthHi, fOthLo, hh, hl, ro); },
             [&]() __attribute__((always_inline)) {
@@ -966,7 +980,7 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
                 put_tile(rh + (i + 1) * ENTRY, Hr, hh, hl);
               }
               *(float4*)(rz + ((i * NT + w) * 64 + lane) * 4) = make_float4(Z[0], Z[1], Z[2], Z[3]);
-              rec_dq(Hr, st, i, (p - 1) * SUB);
+              rec_dq(Hr, uq4, i, (p - 1) * SUB);
               if (i + 1 < SUB) kv = mfma_f32(avn, bkn, zero4);
             });
       }
@@ -1059,7 +1073,7 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
           __builtin_amdgcn_sched_barrier(0);
           // dq_t = H_t u_t (row sums over this wave's 16 columns) needs no backward quantity: it
           // is formed here, in the shadow of the writes above.
-          rec_dq(H, st, j, t0 + jb);
+          rec_dq(H, rec_u4(st), j, t0 + jb);
           lds_barrier();
         }
 
@@ -1075,14 +1089,18 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
   }
 
   if (a.dH0) *(float4*)(a.dH0 + own_off) = make_float4(C[0] * ug, C[1] * ug, C[2] * ug, C[3] * ug);
-  if (s == 0 && n == 0)
+  if constexpr (GROUP4) {
+    const float dwr = sum_rows4(dwr1);
+    if (s == 0 && g == 0) a.dwr_part[((long)b * a.N + nh) * V + 16 * w + n] = dwr * ug;
+  } else if (s == 0 && n == 0) {
     *(float4*)(a.dwr_part + ((long)b * a.N + nh) * V + 16 * w + 4 * g) = make_float4(dwr4[0] * ug, dwr4[1] * ug, dwr4[2] * ug, dwr4[3] * ug);
-  // dW partial of this workgroup: dWacc[tt] at lane (g, j) reg r = dW[16w + 4g + r][16tt + j].
+  }
+  // dW partial of this workgroup: dWacc[tt] at lane (g, j) reg r = dW[16w + 4g + r][16((w + tt) mod NT) + j].
   float* dWp = a.dW_part + ((long)(b * a.S + s) * a.N + nh) * V * V;
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dWp[(long)(16 * w + 4 * g + r) * V + 16 * tt + n] = dWacc[tt][r] * ug;
+    for (int r = 0; r < 4; ++r) dWp[(long)(16 * w + 4 * g + r) * V + 16 * ((w + tt) & (NT - 1)) + n] = dWacc[tt][r] * ug;
 }
 
 // Partial maxima of |dy| and |dH_T| per (b, n) pair, for the pair's power-of-two scale in the

@@ -168,6 +168,18 @@ __device__ __forceinline__ float add_mix_f16(uint32_t h, float c) {
   return d;
 }
 
+// h - c in fp32 with h one fp16 half of a packed pair (HI: the high half): one v_fma_mix_f32 with
+// the negation as a source modifier.
+template <bool HI>
+__device__ __forceinline__ float sub_mix_f16(uint32_t h, float c) {
+  float d;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(c));
+  else
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(c));
+  return d;
+}
+
 // tanh(x/c) from x = c*P, c = 2 log2 e:  tanh(P) = 1 - 2 / (1 + 2^x).  Returns r = 1/(1 + 2^x)
 // so that callers fold "1 - 2r" into the gate blend.  2^x overflowing to +inf gives r = 0
 // (tanh = 1); underflowing to 0 gives r = 1 (tanh = -1).
