@@ -1119,8 +1119,18 @@ __global__ void __launch_bounds__(256) m2rnn_bwd_absmax_kernel(const float* __re
   const int t0 = p * len, t1 = min(T, t0 + len);
   float m = 0.0f;
   if (live) {
+    // (eight steps' loads in flight per thread: the read is latency-bound otherwise)
     const float* src = dy + (long)b * T * NV + c;
-    for (int t = t0; t < t1; ++t) {
+    int t = t0;
+    for (; t + 8 <= t1; t += 8) {
+      f32x4 x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = __builtin_nontemporal_load((const f32x4*)(src + (long)(t + i) * NV));
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(x[i][0]), fabsf(x[i][1])), fmaxf(fabsf(x[i][2]), fabsf(x[i][3]))));
+    }
+    for (; t < t1; ++t) {
       const float4 x = *(const float4*)(src + (long)t * NV);
       m = fmaxf(m, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
     }
