@@ -489,7 +489,16 @@ BwdLayout bwd_layout(const m2rnn_dims* d) {
   return L;
 }
 
-const void* bwd_kernel(int V, bool bf16) {
+// The reverse kernel at V = 64 with the walk and the recompute in waves of their own (8 waves per
+// workgroup); M2RNN_BWD_ROLES=0 selects the one-role kernel (4 waves), which gives the same bits.
+bool bwd_roles() {
+  const char* e = getenv("M2RNN_BWD_ROLES");
+  return !(e && e[0] == '0');
+}
+
+const void* bwd_kernel(int V, bool bf16, bool roles) {
+  if (V == 64 && roles)
+    return bf16 ? (const void*)&m2rnn_scan_bwd_kernel<64, true, true> : (const void*)&m2rnn_scan_bwd_kernel<64, false, true>;
   switch (V) {
     case 16: return bf16 ? (const void*)&m2rnn_scan_bwd_kernel<16, true> : (const void*)&m2rnn_scan_bwd_kernel<16, false>;
     case 32: return bf16 ? (const void*)&m2rnn_scan_bwd_kernel<32, true> : (const void*)&m2rnn_scan_bwd_kernel<32, false>;
@@ -785,10 +794,12 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
       a.B = (int)B; a.T = (int)T; a.N = (int)N; a.K = (int)K; a.S = S;
       a.Nqk = qk_heads(d);
       a.clip = grad_clip;
-      const void* kern = bwd_kernel((int)V, bf16);
+      const bool roles = V == 64 && bwd_roles();
+      const void* kern = bwd_kernel((int)V, bf16, roles);
       if (!kern) return M2RNN_EUNSUPPORTED;
       void* args[] = {&a};
-      st = hip_status(hipLaunchKernel(kern, dim3((unsigned)(B * N * S)), dim3((unsigned)(4 * V)), args, 0, stream));
+      st = hip_status(
+          hipLaunchKernel(kern, dim3((unsigned)(B * N * S)), dim3((unsigned)(roles ? 8 * V : 4 * V)), args, 0, stream));
       if (st) return st;
     }
   }

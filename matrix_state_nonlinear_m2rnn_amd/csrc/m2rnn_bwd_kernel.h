@@ -308,9 +308,15 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint32_t* p) {
   return o;
 }
 
-template <int V, bool BF16IN>
-__global__ void __launch_bounds__(64 * (V / 16)) __attribute__((amdgpu_waves_per_eu(1, 1)))
-m2rnn_scan_bwd_kernel(const BwdArgs a) {
+// WS (V = 64 only): the interleaved walk with waves of their own.  Waves 0 .. NT-1 walk (exchange
+// of D, the chain, R and D, dk, df), waves NT .. 2NT-1 recompute (exchange of H, the forward step,
+// dq) and form dW, dv and dw_r from the transposed tiles, so that each SIMD holds one wave of each
+// and the two roles split the LDS reads, which one wave can only drain at a limited rate.  Both
+// roles meet at the same barriers; the arithmetic is the one-role kernel's, operation for
+// operation.
+template <int V, bool BF16IN, bool WS = false>
+__global__ void __launch_bounds__(64 * (V / 16) * (WS ? 2 : 1))
+__attribute__((amdgpu_waves_per_eu(WS ? 2 : 1, WS ? 2 : 1))) m2rnn_scan_bwd_kernel(const BwdArgs a) {
   constexpr bool SUBCK = BwdCkpt<V>::sub;  // checkpoints at every sub-segment
   constexpr int NT = V / 16;
   constexpr int NTH = 64 * NT;
@@ -328,6 +334,7 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
   // waits.  (A one-wave workgroup gets that from the other workgroups on its SIMD instead.)
   constexpr bool INTERLEAVE = SUBCK && V == 64;
   constexpr int NBUF = INTERLEAVE ? 2 : 1;
+  static_assert(!WS || INTERLEAVE, "the roles split the interleaved walk");
   using St = BwdStage<V>;
   static_assert(kBwdSeg % SUB == 0 && SUB % 2 == 0, "sub-segments tile a segment");
 
@@ -350,7 +357,8 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
   auto& red_f = red[2];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = WS ? (tid >> 6) & (NT - 1) : tid >> 6;  // value tile of this wave
+  const bool walker = !WS || (tid >> 6) < NT;           // (uniform in a wave)
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int n = lane & 15;
@@ -388,7 +396,7 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
     for (int i = 0; i < 8; ++i) {
       const int tile = (i >> 2) ? t_hi : t_lo;
       const int vin = 16 * tile + 4 * g + (i & 3);
-      wv[i] = tile < NT ? (fwd ? kTwoLog2e * Wn[vin * V + col] : Wn[col * V + vin]) : 0.0f;
+      wv[i] = tile < NT ? (fwd ? opaque1(kTwoLog2e * Wn[vin * V + col]) : Wn[col * V + vin]) : 0.0f;
     }
     uint32_t h[4], l[4];
 #pragma unroll
@@ -400,14 +408,18 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
     lo = make_uint4(l[0], l[1], l[2], l[3]);
   };
   uint4 fOwnHi, fOwnLo, bOwnHi, bOwnLo, fOthHi[NOTH], fOthLo[NOTH], bOthHi[NOTH], bOthLo[NOTH];
-  wchunk(w, w ^ 1, true, fOwnHi, fOwnLo);
-  wchunk(w, w ^ 1, false, bOwnHi, bOwnLo);
+  auto load_w = [&](bool fwd, bool bwd) __attribute__((always_inline)) {
+    if (fwd) wchunk(w, w ^ 1, true, fOwnHi, fOwnLo);
+    if (bwd) wchunk(w, w ^ 1, false, bOwnHi, bOwnLo);
 #pragma unroll
-  for (int i = 0; i < NCH - 1; ++i) {
-    const int cc = i < co ? i : i + 1;
-    wchunk(2 * cc, 2 * cc + 1, true, fOthHi[i], fOthLo[i]);
-    wchunk(2 * cc, 2 * cc + 1, false, bOthHi[i], bOthLo[i]);
-  }
+    for (int i = 0; i < NCH - 1; ++i) {
+      const int cc = i < co ? i : i + 1;
+      if (fwd) wchunk(2 * cc, 2 * cc + 1, true, fOthHi[i], fOthLo[i]);
+      if (bwd) wchunk(2 * cc, 2 * cc + 1, false, bOthHi[i], bOthLo[i]);
+    }
+  };
+  // (with roles each role loads its own operands, inside its own branch)
+  if constexpr (!WS) load_w(true, true);
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
   // Lane-constant slots: own record (row n, group g) and the transposing-read slot.
@@ -537,12 +549,15 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
   const float clip_hi = a.clip > 0.0f ? a.clip * us : __builtin_inff();
   const float clip_lo = -clip_hi;
   const long own_off = ((long)b * a.N + nh) * KV + (long)(row0 + n) * V + 16 * w + 4 * g;
-  if (a.dH_T) {
-    const float4 c4 = *(const float4*)(a.dH_T + own_off);
-    C[0] = c4.x * us; C[1] = c4.y * us; C[2] = c4.z * us; C[3] = c4.w * us;
-  } else {
-    C[0] = C[1] = C[2] = C[3] = 0.0f;
-  }
+  auto init_C = [&]() __attribute__((always_inline)) {
+    if (a.dH_T) {
+      const float4 c4 = *(const float4*)(a.dH_T + own_off);
+      C[0] = c4.x * us; C[1] = c4.y * us; C[2] = c4.z * us; C[3] = c4.w * us;
+    } else {
+      C[0] = C[1] = C[2] = C[3] = 0.0f;
+    }
+  };
+  if constexpr (!WS) init_C();
   f32x4 dWacc[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) dWacc[tt] = zero4;
@@ -726,14 +741,83 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
     }
   };
 
+  RevIn nxt;
+  RevFront fr;
+  // dk, df of walk step j + 1 (the partials of the front carried in fr): sums over this wave's 16
+  // columns (the four lane rows); df also over the 16 rows.  Grouped: steps j .. j+3 (j % 4 == 0)
+  // reduced together, lane (g, n) ending with step j + g.
+  auto walk_sums = [&](int j, int js) __attribute__((always_inline)) {
+    if (!GROUP4 || (j & 3) == 0) {
+      float dk_l, df_l;
+      if constexpr (GROUP4) {
+        xk[j & 3] = fr.dk_l;
+        xf[j & 3] = fr.df_l;
+        dk_l = reduce_rows4(xk[0], xk[1], xk[2], xk[3]);
+        df_l = reduce_rows4(xf[0], xf[1], xf[2], xf[3]);
+      } else {
+        dk_l = sum_rows4(fr.dk_l);
+        df_l = sum_rows4(fr.df_l);
+      }
+      df_l += dpp<kDppRowMirror>(df_l);
+      df_l += dpp<kDppRowHalfMirror>(df_l);
+      df_l += dpp<kDppQuadXor1>(df_l);
+      df_l += dpp<kDppQuadXor2>(df_l);
+      if constexpr (ONE) {
+        const uint32_t tstep = (uint32_t)js;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dk_l * ug), dkres,
+                                              GROUP4 || g == 0 ? qk_lane + tstep * qkstep * 4 : kBufferDrop, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(df_l * ug), dfres,
+                                              df_lane == kBufferDrop ? kBufferDrop : df_lane + tstep * a.N * 4, 0, 0);
+      } else if constexpr (GROUP4) {
+        red_k[j + g][w][n] = dk_l;
+        red_f[j + g][w][n] = df_l;
+      } else if (g == 0) {
+        red_k[j][w][n] = dk_l;
+        red_f[j][w][n] = df_l;
+      }
+    } else {
+      xk[j & 3] = fr.dk_l;
+      xf[j & 3] = fr.df_l;
+    }
+  };
+  // dv[col 16w + i] of walk step j = sum_rows D[row][col] k[row] (+ w_r u when this workgroup holds
+  // all rows), from the transposed D tile's hi and lo halves, each times k (one v_fma_mix_f32
+  // apiece); st is the step's record; ucol, vcol the grouped u, v reads (step j + g, column 16w + n).
+  auto dv_step = [&](int j, int js, const float* st, uint2 dThi, uint2 dTlo, float4 k4, float ucol, float vcol)
+                     __attribute__((always_inline)) {
+    float x = fma_mix_f16<false>(dThi.x, k4.x, 0.0f);
+    x = fma_mix_f16<false>(dTlo.x, k4.x, x);
+    x = fma_mix_f16<true>(dThi.x, k4.y, x);
+    x = fma_mix_f16<true>(dTlo.x, k4.y, x);
+    x = fma_mix_f16<false>(dThi.y, k4.z, x);
+    x = fma_mix_f16<false>(dTlo.y, k4.z, x);
+    x = fma_mix_f16<true>(dThi.y, k4.w, x);
+    x = fma_mix_f16<true>(dTlo.y, k4.w, x);
+    if constexpr (GROUP4) {
+      // Steps j .. j+3 are collected in xq; one cross-row reduction of the four leaves lane (g, i)
+      // with dv[step j0 + g][16w + i].
+      xq[j & 3] = x;
+      if ((j & 3) == 0) {
+        float dvv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
+        dwr1 = __builtin_fmaf(ucol, vcol, dwr1);  // dw_r's product of step j + g, column 16w + n
+        dvv = __builtin_fmaf(wr_col, ucol, dvv);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv * ug), dvres, dv_lane + (uint32_t)(js * ystep * 4), 0, 0);
+      }
+    } else {
+      x = sum_rows4(x);
+      const float u1 = st[St::OU + 16 * w + n];
+      const float dvv = __builtin_fmaf(wr_col, u1, x);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv * ug), dvres,
+                                            g == 0 ? dv_lane + (uint32_t)(js * ystep * 4) : kBufferDrop, 0, 0);
+    }
+  };
+
   // Walk step j of the sub-segment starting at step tb (records ss, tiles hs, Z zs), software-
   // pipelined: the inputs of step j-1 are read right after step j's barrier together with step
   // j's exchange reads, and the step ends with step j-1's R, D and publish (which wait for step
   // j's chain MFMAs).  The hooks add independent work: reads (issued with the step's reads),
   // MFMAs (queued behind the chain's), and a tail (after the publish of D).
   // (fr: step j's front, nxt: step j-1's inputs, both carried from step to step.)
-  RevIn nxt;
-  RevFront fr;
   auto walk_step = [&](int j, int tb, const float* ss, const uint32_t* hs, const float* zs, auto&& hook_reads,
                        auto&& hook_mfma, auto&& hook_tail) __attribute__((always_inline)) {
     const int js = tb + j;  // global step
@@ -781,41 +865,8 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
 #endif
     __builtin_amdgcn_sched_barrier(0);
     hook_mfma();
-    // Off the chain, while the MFMAs run.  dk, df: sums over this wave's 16 columns (the four
-    // lane rows); df also over the 16 rows.  Grouped: steps j .. j+3 (j % 4 == 0) reduced
-    // together, lane (g, n) ending with step j + g.
-    if (!GROUP4 || (j & 3) == 0) {
-      float dk_l, df_l;
-      if constexpr (GROUP4) {
-        xk[j & 3] = fr.dk_l;
-        xf[j & 3] = fr.df_l;
-        dk_l = reduce_rows4(xk[0], xk[1], xk[2], xk[3]);
-        df_l = reduce_rows4(xf[0], xf[1], xf[2], xf[3]);
-      } else {
-        dk_l = sum_rows4(fr.dk_l);
-        df_l = sum_rows4(fr.df_l);
-      }
-      df_l += dpp<kDppRowMirror>(df_l);
-      df_l += dpp<kDppRowHalfMirror>(df_l);
-      df_l += dpp<kDppQuadXor1>(df_l);
-      df_l += dpp<kDppQuadXor2>(df_l);
-      if constexpr (ONE) {
-        const uint32_t tstep = (uint32_t)js;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dk_l * ug), dkres,
-                                              GROUP4 || g == 0 ? qk_lane + tstep * qkstep * 4 : kBufferDrop, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(df_l * ug), dfres,
-                                              df_lane == kBufferDrop ? kBufferDrop : df_lane + tstep * a.N * 4, 0, 0);
-      } else if constexpr (GROUP4) {
-        red_k[j + g][w][n] = dk_l;
-        red_f[j + g][w][n] = df_l;
-      } else if (g == 0) {
-        red_k[j][w][n] = dk_l;
-        red_f[j][w][n] = df_l;
-      }
-    } else {
-      xk[j & 3] = fr.dk_l;
-      xf[j & 3] = fr.df_l;
-    }
+    // Off the chain, while the MFMAs run.
+    walk_sums(j, js);
 
     // Step j-1's R, D and publish as soon as the chain has produced C.
     // (the padding steps of a ragged tail must leave the chain unchanged: no clamp there)
@@ -833,34 +884,8 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
     if constexpr (INTERLEAVE) {
       if ((j & 3) == 3) group_read(j == 3 ? 0 : 4, j == 3 ? 4 : 0, gx);
     }
-    // dv[col 16w + i] = sum_rows D[row][col] k[row] (+ w_r u when this workgroup holds all rows).
-    // (hi and lo halves of D each times k, one v_fma_mix_f32 apiece)
-    float x = fma_mix_f16<false>(dThi.x, k4.x, 0.0f);
-    x = fma_mix_f16<false>(dTlo.x, k4.x, x);
-    x = fma_mix_f16<true>(dThi.x, k4.y, x);
-    x = fma_mix_f16<true>(dTlo.x, k4.y, x);
-    x = fma_mix_f16<false>(dThi.y, k4.z, x);
-    x = fma_mix_f16<false>(dTlo.y, k4.z, x);
-    x = fma_mix_f16<true>(dThi.y, k4.w, x);
-    x = fma_mix_f16<true>(dTlo.y, k4.w, x);
-    if constexpr (GROUP4) {
-      // Steps j .. j+3 are collected in xq; one cross-row reduction of the four leaves lane (g, i)
-      // with dv[step j0 + g][16w + i].
-      xq[j & 3] = x;
-      if ((j & 3) == 0) {
-        float dvv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
-        dwr1 = __builtin_fmaf(ucol, vcol, dwr1);  // dw_r's product of step j + g, column 16w + n
-        dvv = __builtin_fmaf(wr_col, ucol, dvv);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv * ug), dvres, dv_lane + (uint32_t)(js * ystep * 4), 0, 0);
-      }
-    } else {
-      x = sum_rows4(x);
-      const float ucol = st[St::OU + 16 * w + n];
-      const float dvv = __builtin_fmaf(wr_col, ucol, x);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv * ug), dvres,
-                                            g == 0 ? dv_lane + (uint32_t)(js * ystep * 4) : kBufferDrop, 0, 0);
-    }
-  
+    dv_step(j, js, st, dThi, dTlo, k4, ucol, vcol);
+
     // dW[16w + m][16u + j] += sum_rows H_{t-1}[row][16w + m] D[row][16u + j], u = w + tt mod NT: one fp16 16x16x16
     // MFMA per D tile, both operands read transposed from LDS (rows on the contraction index).
 #pragma unroll
@@ -881,7 +906,7 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
   // The state entering the next sub-segment to walk (sub-segment checkpoints: prefetched one
   // sub-segment ahead; segment checkpoints: from this workgroup's scratch).
   float4 nextH = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  if constexpr (SUBCK) {
+  if constexpr (SUBCK && !WS) {
     const int tl = ((a.T - 1) / SUB) * SUB;  // the last sub-segment
     sub_regs.load(a, b, nh, row0, tl, min(SUB, a.T - tl), tid);
     nextH = *(const float4*)(a.ckpt + ((long)u * nck + nck - 1) * KV + lane_off);
@@ -893,7 +918,239 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
     sub_regs.load(a, b, nh, row0, pp * SUB, min(SUB, a.T - pp * SUB), tid);
   };
 
-  if constexpr (INTERLEAVE) {
+  // Results held in registers, stored at the end (by the role that holds them).
+  auto store_dH0 = [&]() __attribute__((always_inline)) {
+    if (a.dH0) *(float4*)(a.dH0 + own_off) = make_float4(C[0] * ug, C[1] * ug, C[2] * ug, C[3] * ug);
+  };
+  auto store_dwr = [&]() __attribute__((always_inline)) {
+    if constexpr (GROUP4) {
+      const float dwr = sum_rows4(dwr1);
+      if (s == 0 && g == 0) a.dwr_part[((long)b * a.N + nh) * V + 16 * w + n] = dwr * ug;
+    } else if (s == 0 && n == 0) {
+      *(float4*)(a.dwr_part + ((long)b * a.N + nh) * V + 16 * w + 4 * g) =
+          make_float4(dwr4[0] * ug, dwr4[1] * ug, dwr4[2] * ug, dwr4[3] * ug);
+    }
+  };
+  // dW partial of this workgroup: dWacc[tt] at lane (g, j) reg r = dW[16w + 4g + r][16((w + tt) mod NT) + j].
+  auto store_dW = [&]() __attribute__((always_inline)) {
+    float* dWp = a.dW_part + ((long)(b * a.S + s) * a.N + nh) * V * V;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dWp[(long)(16 * w + 4 * g + r) * V + 16 * ((w + tt) & (NT - 1)) + n] = dWacc[tt][r] * ug;
+  };
+
+  if constexpr (WS) {
+    // Buffers of sub-segment p (p >= -1), as in the one-role interleaved walk below.
+    auto stg = [&](int p) { return stage + ((p + 2) & 1) * (SUB * St::STEP); };
+    auto hsb = [&](int p) { return hst + ((p + 2) & 1) * (SUB * ENTRY); };
+    auto zsb = [&](int p) { return zst + ((p + 2) & 1) * (SUB * NT * 64 * 4); };
+    const int P = nck;  // sub-segments
+    // Both roles pass the same barriers: one before the recompute of the last sub-segment, one per
+    // step of it, then per pair two at its start and one per step, and one at the end.
+    if (walker) {
+      // ---------------- walk waves: the records, the chain, R and D, dk and df ----------------
+      load_w(false, true);
+      init_C();
+      // (the walk waves stage every sub-segment's records: tid < NTH)
+      auto load_records = [&](int p) __attribute__((always_inline)) {
+        const int pp = max(p, 0);
+        sub_regs.load(a, b, nh, row0, pp * SUB, min(SUB, a.T - pp * SUB), tid);
+      };
+      load_records(P - 1);
+      sub_regs.store(stg(P - 1), tid, us);
+      load_records(P - 2);
+      lds_barrier();
+      for (int j = 0; j < SUB; ++j) lds_barrier();  // the recompute waves' pass over sub-segment P - 1
+      for (int p = P - 1; p >= 0; --p) {
+        lds_barrier();                        // the previous pair is done with the buffers of p - 1
+        sub_regs.store(stg(p - 1), tid, us);  // (at p = 0 a repeat of sub-segment 0, never used)
+        load_records(p - 2);
+        lds_barrier();
+        const float* ws = stg(p);
+        const uint32_t* wh = hsb(p);
+        const float* wz = zsb(p);
+        nxt = load_rev(ws, wh, wz, SUB - 1);
+        fr = front(SUB - 1, nxt);
+#pragma unroll
+        for (int i = 0; i < SUB; ++i) {
+          const int j = SUB - 1 - i;
+          const int tb = p * SUB;
+          const int js = tb + j;
+          const uint32_t* dxp = dx + (j & 1) * ENTRY;
+          __builtin_amdgcn_sched_barrier(0);
+          lds_barrier();
+          const Ops o = read_ops(dxp);
+          if (j > 0) nxt = load_rev(ws, wh, wz, j - 1);
+          // The cross-wave sums of dk (wave 0) and df (wave 1) of one group: at j = 3 steps
+          // tb + 4 .. 7, at j = 7 steps tb + SUB .. tb + SUB + 3 (of the previous pair).
+          const bool gsum = (j & 3) == 3 && w < 2;
+          float gx[4];
+          if (gsum) {
+            const float* src = &red[1 + w][(j == 3 ? 4 : 0) + g][0][n];
+#pragma unroll
+            for (int ww = 0; ww < NT; ++ww) gx[ww] = src[ww * 16];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const f32x4 acc = contract(fr.cinit, bOwnHi, bOwnLo, bOthHi, bOthLo, fr.dh, fr.dl, o);
+          walk_sums(j, js);
+          // Step j-1's R, D and publish as soon as the chain has produced C (no clamp on the
+          // padding steps of a ragged tail, which must leave the chain unchanged).
+          const bool real = js < a.T;
+          const float lo = real ? clip_lo : -__builtin_inff(), hi = real ? clip_hi : __builtin_inff();
+#pragma unroll
+          for (int r = 0; r < 4; ++r) C[r] = __builtin_amdgcn_fmed3f(acc[r], lo, hi);
+          if (j > 0) fr = front(j - 1, nxt);
+          if (gsum) {
+            float acc_s = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < NT; ++ww) acc_s += gx[ww];
+            const int tk = j == 3 ? tb + 4 : tb + SUB;
+            const uint32_t val = __float_as_uint(acc_s * ug);
+            if (w == 0) {
+              __builtin_amdgcn_raw_buffer_store_b32(val, dkres, qk_lane + (uint32_t)(tk * qkstep * 4), 0, 0);
+            } else {
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  val, dfres, df_lane == kBufferDrop ? kBufferDrop : df_lane + (uint32_t)(tk * a.N * 4), 0, 0);
+            }
+          }
+        }
+      }
+      lds_barrier();
+      if (w < 2) {  // dk, df of steps 0 .. 3
+        float acc_s = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NT; ++ww) acc_s += red[1 + w][g][ww][n];
+        const uint32_t val = __float_as_uint(acc_s * ug);
+        if (w == 0) {
+          __builtin_amdgcn_raw_buffer_store_b32(val, dkres, qk_lane, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(val, dfres, df_lane, 0, 0);
+        }
+      }
+      store_dH0();
+    } else {
+      // ---------------- recompute waves: the forward step, dq, and dW, dv, dw_r of the walk ----------------
+      load_w(true, false);
+      float Hr[4];
+      uint2 hh, hl;
+      auto load_entry = [&](int p) __attribute__((always_inline)) {
+        return *(const float4*)(a.ckpt + ((long)u * nck + max(p, 0)) * KV + lane_off);
+      };
+      auto take_entry = [&](int p, float4 h) __attribute__((always_inline)) {
+        Hr[0] = h.x; Hr[1] = h.y; Hr[2] = h.z; Hr[3] = h.w;
+        put_tile(hsb(p), Hr, hh, hl);
+      };
+      // the cross-wave dq sum of one group (wave 0): reads of red_q rows jq .. jq + 3, then the store
+      auto dq_read = [&](int jq, float (&x)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ww = 0; ww < NT; ++ww) x[ww] = red_q[jq + g][ww][n];
+      };
+      auto dq_store = [&](const float (&x)[4], int tq) __attribute__((always_inline)) {
+        float acc_s = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NT; ++ww) acc_s += x[ww];
+        if (tq >= 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc_s * ug), dqres, qk_lane + (uint32_t)(tq * qkstep * 4),
+                                                0, 0);
+      };
+      take_entry(P - 1, load_entry(P - 1));
+      float4 nextE = load_entry(P - 2);
+      lds_barrier();
+      {
+        const float* ss = stg(P - 1);
+        f32x4 kv = rank1(ss);
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) {
+          float Z[4];
+          const float* st = ss + j * St::STEP;
+          float gq[4];
+          if (j == 4 && w == 0) dq_read(0, gq);  // dq of steps 0 .. 3 of this sub-segment
+          fwd_step(st, j + 1 < SUB ? st + St::STEP : nullptr, hsb(P - 1) + j * ENTRY,
+                   j + 1 < SUB ? hsb(P - 1) + (j + 1) * ENTRY : nullptr, kv, Hr, Z, hh, hl);
+          *(float4*)(zsb(P - 1) + ((j * NT + w) * 64 + lane) * 4) = make_float4(Z[0], Z[1], Z[2], Z[3]);
+          __builtin_amdgcn_sched_barrier(0);
+          rec_dq(Hr, rec_u4(st), j, (P - 1) * SUB);
+          if (j == 4 && w == 0) dq_store(gq, (P - 1) * SUB);
+          lds_barrier();
+        }
+      }
+      for (int p = P - 1; p >= 0; --p) {
+        lds_barrier();  // the previous pair is done with the buffers of p - 1
+        take_entry(p - 1, nextE);
+        nextE = load_entry(p - 2);
+        lds_barrier();
+        const float* ws = stg(p);
+        const uint32_t* wh = hsb(p);
+        const float* rs = stg(p - 1);
+        uint32_t* rh = hsb(p - 1);
+        float* rz = zsb(p - 1);
+        f32x4 kv = rank1(rs);
+#pragma unroll
+        for (int i = 0; i < SUB; ++i) {
+          const int j = SUB - 1 - i;  // the walk step of this barrier
+          const int js = p * SUB + j;
+          const float* st = rs + i * St::STEP;
+          const float* sw = ws + j * St::STEP;
+          const uint32_t* hj = wh + j * ENTRY;
+          const uint32_t* dxp = dx + (j & 1) * ENTRY;
+          __builtin_amdgcn_sched_barrier(0);
+          lds_barrier();
+          // Recompute step i's operands and inputs first; the dq sum of one group (wave 0): at
+          // j = 3 steps (p - 1) SUB .. + 3 of the recompute, at j = 7 steps p SUB + 4 .. 7.
+          const Ops ro = read_ops(rh + i * ENTRY);
+          float avn = 0.0f, bkn = 0.0f;
+          if (i + 1 < SUB) {
+            avn = st[St::STEP + (g == 0 ? St::OV + 16 * w + n : 3)];
+            bkn = st[St::STEP + (g == 0 ? St::OCK + n : 3)];
+          }
+          const float f = st[0];
+          const float4 uq4 = rec_u4(st);
+          const bool gsum = (j & 3) == 3 && w == 0;
+          float gq[4];
+          if (gsum) dq_read(j == 3 ? 0 : 4, gq);
+          __builtin_amdgcn_sched_barrier(0);
+          const f32x4 racc = contract(kv, fOwnHi, fOwnLo, fOthHi, fOthLo, hh, hl, ro);
+          // Walk step j's transposed tiles (H_{t-1} and D) and k for dW and dv, behind the MFMAs.
+          const uint2 hT = lds_read_tr(hj + tile_off(w, 0) + 2 * tr_slot);
+          uint2 dT[NT];
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) dT[tt] = lds_read_tr(dxp + tile_off((w + tt) & (NT - 1), 0) + 2 * tr_slot);
+          const uint2 dTlo = lds_read_tr(dxp + tile_off(w, 1) + 2 * tr_slot);
+          const float4 k4 = *(const float4*)(sw + St::OK + 4 * g);
+          float ucol = 0.0f, vcol = 0.0f;
+          if ((j & 3) == 0) {
+            ucol = ws[(j + g) * St::STEP + St::OU + 16 * w + n];
+            vcol = ws[(j + g) * St::STEP + St::OV + 16 * w + n];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) dWacc[tt] = mfma16_f16(hT, dT[tt], dWacc[tt]);
+          {
+            const float g1 = 1.0f - f, m2g = -2.0f * g1;
+            float Z[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float rr = tanh_recip(racc[r]);
+              Z[r] = __builtin_fmaf(-2.0f, rr, 1.0f);
+              Hr[r] = __builtin_fmaf(m2g, rr, __builtin_fmaf(f, Hr[r], g1));
+            }
+            if (i + 1 < SUB) put_tile(rh + (i + 1) * ENTRY, Hr, hh, hl);
+            *(float4*)(rz + ((i * NT + w) * 64 + lane) * 4) = make_float4(Z[0], Z[1], Z[2], Z[3]);
+            rec_dq(Hr, uq4, i, (p - 1) * SUB);
+            if (i + 1 < SUB) kv = mfma_f32(avn, bkn, zero4);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          dv_step(j, js, sw, dT[0], dTlo, k4, ucol, vcol);
+          if (gsum) dq_store(gq, j == 3 ? (p - 1) * SUB : p * SUB + 4);
+        }
+      }
+      lds_barrier();
+      store_dwr();
+      store_dW();
+    }
+  } else if constexpr (INTERLEAVE) {
     // Buffers of sub-segment p (p >= -1).
     auto stg = [&](int p) { return stage + ((p + 2) & 1) * (SUB * St::STEP); };
     auto hsb = [&](int p) { return hst + ((p + 2) & 1) * (SUB * ENTRY); };
@@ -1088,19 +1345,11 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
     if (pending_tb >= 0) finalize(pending_tb);
   }
 
-  if (a.dH0) *(float4*)(a.dH0 + own_off) = make_float4(C[0] * ug, C[1] * ug, C[2] * ug, C[3] * ug);
-  if constexpr (GROUP4) {
-    const float dwr = sum_rows4(dwr1);
-    if (s == 0 && g == 0) a.dwr_part[((long)b * a.N + nh) * V + 16 * w + n] = dwr * ug;
-  } else if (s == 0 && n == 0) {
-    *(float4*)(a.dwr_part + ((long)b * a.N + nh) * V + 16 * w + 4 * g) = make_float4(dwr4[0] * ug, dwr4[1] * ug, dwr4[2] * ug, dwr4[3] * ug);
+  if constexpr (!WS) {
+    store_dH0();
+    store_dwr();
+    store_dW();
   }
-  // dW partial of this workgroup: dWacc[tt] at lane (g, j) reg r = dW[16w + 4g + r][16((w + tt) mod NT) + j].
-  float* dWp = a.dW_part + ((long)(b * a.S + s) * a.N + nh) * V * V;
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dWp[(long)(16 * w + 4 * g + r) * V + 16 * ((w + tt) & (NT - 1)) + n] = dWacc[tt][r] * ug;
 }
 
 // Partial maxima of |dy| and |dH_T| per (b, n) pair, for the pair's power-of-two scale in the

@@ -121,7 +121,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) m2rnn_decode_kernel(const DecA
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int vin = 16 * (2 * c + (i >> 2)) + 4 * gg + (i & 3);
-      x[i] = vin < V ? kTwoLog2e * Wn[vin * V + 16 * tile + m] : 0.0f;
+      x[i] = vin < V ? opaque1(kTwoLog2e * Wn[vin * V + 16 * tile + m]) : 0.0f;
     }
     uint32_t h[4], lo[4];
     split4_f16(x, h[0], h[1], lo[0], lo[1]);

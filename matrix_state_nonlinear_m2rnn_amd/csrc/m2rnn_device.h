@@ -146,6 +146,16 @@ __device__ __forceinline__ void opaque4(float (&x)[4]) {
   asm("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
 }
 
+// x rounded to fp32 at this point: an empty asm that "modifies" it, so that the compiler cannot fuse
+// the multiply that produced it into a later operation.  The split of c W into fp16 hi/lo parts
+// needs it: with the product fused into the remainder's v_fma_mix, lo = fp16(c W - hi) would be
+// taken from the exact product in some kernels and from the fp32 one in others, and kernels that
+// should agree bit for bit would not.
+__device__ __forceinline__ float opaque1(float x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
 // fma(h, b, c) in fp32 with h one fp16 half of a packed pair (HI: the high half), widened exactly
 // inside the instruction: one v_fma_mix_f32 in place of a conversion and an FMA.
 template <bool HI>

@@ -328,7 +328,7 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
     for (int i = 0; i < 8; ++i) {
       const int tile = (i >> 2) ? t_hi : t_lo;
       const int vin = 16 * tile + 4 * g + (i & 3);
-      wv[i] = tile < NT ? kTwoLog2e * Wn[vin * V + col] : 0.0f;
+      wv[i] = tile < NT ? opaque1(kTwoLog2e * Wn[vin * V + col]) : 0.0f;
     }
     uint32_t h[4], l[4];
 #pragma unroll
@@ -855,7 +855,7 @@ __global__ void __launch_bounds__(2 * 64 * (V / 16)) m2rnn_scan_fwd_ro_kernel(co
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int tile = (i >> 2) ? t_hi : t_lo;
-        wv[i] = kTwoLog2e * Wn[(16 * tile + 4 * g + (i & 3)) * V + col];
+        wv[i] = opaque1(kTwoLog2e * Wn[(16 * tile + 4 * g + (i & 3)) * V + col]);
       }
       uint32_t h[4], l[4];
 #pragma unroll

@@ -176,3 +176,31 @@ def test_gradient_scale_clipped():
     unit = gpu_bwd(to_device(d, "bf16"), grad_clip=0.6)
     for n in GRADS:
         assert np.array_equal(got[n], unit[n] * float(s)), n
+
+
+@pytest.mark.parametrize("B,T,N,dtype,clip,scale", [
+    (2, 300, 3, "bf16", 0.0, 0),     # five pairs of sub-segments and a ragged tail
+    (1, 70, 2, "f32", 0.6, 0),       # clipped recurrent gradient
+    (2, 9, 2, "bf16", 0.0, -20),     # two sub-segments, dy at 2^-20
+    (1, 1, 1, "f32", 0.0, 0),        # a single step
+])
+def test_roles_give_the_one_role_kernels_bits(B, T, N, dtype, clip, scale, monkeypatch):
+    # The reverse kernel at V = 64 with the walk and the recompute in waves of their own computes
+    # every operation of the one-role kernel in the same order: all seven gradients are the same
+    # bits.  (Both are also checked against the oracle.)
+    torch_cuda()
+    d = inputs.make_inputs(B, T, N, 64, 64, qkv_dtype=dtype, seed=900 + T + N, with_H0=True, with_dy=True,
+                           with_dHT=True)
+    s = np.float32(2.0 ** scale)
+    d["dy"] = (d["dy"] * s).astype(np.float32)
+    d["dH_T"] = (d["dH_T"] * s).astype(np.float32)
+    dd = to_device(d, dtype)
+    say("bwd roles", B, T, N, dtype, clip, scale)
+    monkeypatch.delenv("M2RNN_BWD_ROLES", raising=False)
+    g1 = gpu_bwd(dd, grad_clip=clip * float(s))
+    monkeypatch.setenv("M2RNN_BWD_ROLES", "0")
+    g0 = gpu_bwd(dd, grad_clip=clip * float(s))
+    monkeypatch.delenv("M2RNN_BWD_ROLES", raising=False)
+    for n in GRADS:
+        assert np.array_equal(g1[n], g0[n]), n
+    check(g1, oracle_bwd(d, clip=clip * float(s)))
