@@ -309,11 +309,11 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint32_t* p) {
 }
 
 // WS (V = 64 only): the interleaved walk with waves of their own.  Waves 0 .. NT-1 walk (exchange
-// of D, the chain, R and D, dk, df), waves NT .. 2NT-1 recompute (exchange of H, the forward step,
-// dq) and form dW, dv and dw_r from the transposed tiles, so that each SIMD holds one wave of each
-// and the two roles split the LDS reads, which one wave can only drain at a limited rate.  Both
-// roles meet at the same barriers; the arithmetic is the one-role kernel's, operation for
-// operation.
+// of D, the chain, R and D, dk, df, and dv, dw_r from the transposed D tiles), waves NT .. 2NT-1
+// recompute (exchange of H, the forward step, dq) and form dW, so that each SIMD holds one wave of
+// each and the two roles split the LDS reads, which one wave can only drain at a limited rate, and
+// the issue of VALU and MFMA work.  Both roles meet at the same barriers; the arithmetic is the
+// one-role kernel's, operation for operation.
 template <int V, bool BF16IN, bool WS = false>
 __global__ void __launch_bounds__(64 * (V / 16) * (WS ? 2 : 1))
 __attribute__((amdgpu_waves_per_eu(WS ? 2 : 1, WS ? 2 : 1))) m2rnn_scan_bwd_kernel(const BwdArgs a) {
@@ -942,6 +942,9 @@ __attribute__((amdgpu_waves_per_eu(WS ? 2 : 1, WS ? 2 : 1))) m2rnn_scan_bwd_kern
   };
 
   if constexpr (WS) {
+    // Which role forms dW and which dv and dw_r: measured, dv and dw_r with the walk (2.19 -> 2.04 ms),
+    // dW with the recompute (the same time with either role).
+    constexpr bool DW_WALK = false, DV_WALK = true;
     // Buffers of sub-segment p (p >= -1), as in the one-role interleaved walk below.
     auto stg = [&](int p) { return stage + ((p + 2) & 1) * (SUB * St::STEP); };
     auto hsb = [&](int p) { return hst + ((p + 2) & 1) * (SUB * ENTRY); };
@@ -994,6 +997,24 @@ __attribute__((amdgpu_waves_per_eu(WS ? 2 : 1, WS ? 2 : 1))) m2rnn_scan_bwd_kern
           }
           __builtin_amdgcn_sched_barrier(0);
           const f32x4 acc = contract(fr.cinit, bOwnHi, bOwnLo, bOthHi, bOthLo, fr.dh, fr.dl, o);
+          uint2 hT = make_uint2(0, 0), dT[NT], dTlo = make_uint2(0, 0);
+          float4 k4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          float ucol = 0.0f, vcol = 0.0f;
+          if constexpr (DW_WALK) {
+            hT = lds_read_tr(wh + j * ENTRY + tile_off(w, 0) + 2 * tr_slot);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) dT[tt] = lds_read_tr(dxp + tile_off((w + tt) & (NT - 1), 0) + 2 * tr_slot);
+          } else if constexpr (DV_WALK) {
+            dT[0] = lds_read_tr(dxp + tile_off(w, 0) + 2 * tr_slot);
+          }
+          if constexpr (DV_WALK) {
+            dTlo = lds_read_tr(dxp + tile_off(w, 1) + 2 * tr_slot);
+            k4 = *(const float4*)(ws + j * St::STEP + St::OK + 4 * g);
+            if ((j & 3) == 0) {
+              ucol = ws[(j + g) * St::STEP + St::OU + 16 * w + n];
+              vcol = ws[(j + g) * St::STEP + St::OV + 16 * w + n];
+            }
+          }
           walk_sums(j, js);
           // Step j-1's R, D and publish as soon as the chain has produced C (no clamp on the
           // padding steps of a ragged tail, which must leave the chain unchanged).
@@ -1002,6 +1023,11 @@ __attribute__((amdgpu_waves_per_eu(WS ? 2 : 1, WS ? 2 : 1))) m2rnn_scan_bwd_kern
 #pragma unroll
           for (int r = 0; r < 4; ++r) C[r] = __builtin_amdgcn_fmed3f(acc[r], lo, hi);
           if (j > 0) fr = front(j - 1, nxt);
+          if constexpr (DW_WALK) {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) dWacc[tt] = mfma16_f16(hT, dT[tt], dWacc[tt]);
+          }
+          if constexpr (DV_WALK) dv_step(j, js, ws + j * St::STEP, dT[0], dTlo, k4, ucol, vcol);
           if (gsum) {
             float acc_s = 0.0f;
 #pragma unroll
@@ -1030,6 +1056,8 @@ __attribute__((amdgpu_waves_per_eu(WS ? 2 : 1, WS ? 2 : 1))) m2rnn_scan_bwd_kern
         }
       }
       store_dH0();
+      if constexpr (DW_WALK) store_dW();
+      if constexpr (DV_WALK) store_dwr();
     } else {
       // ---------------- recompute waves: the forward step, dq, and dW, dv, dw_r of the walk ----------------
       load_w(true, false);
@@ -1113,20 +1141,29 @@ __attribute__((amdgpu_waves_per_eu(WS ? 2 : 1, WS ? 2 : 1))) m2rnn_scan_bwd_kern
           __builtin_amdgcn_sched_barrier(0);
           const f32x4 racc = contract(kv, fOwnHi, fOwnLo, fOthHi, fOthLo, hh, hl, ro);
           // Walk step j's transposed tiles (H_{t-1} and D) and k for dW and dv, behind the MFMAs.
-          const uint2 hT = lds_read_tr(hj + tile_off(w, 0) + 2 * tr_slot);
-          uint2 dT[NT];
-#pragma unroll
-          for (int tt = 0; tt < NT; ++tt) dT[tt] = lds_read_tr(dxp + tile_off((w + tt) & (NT - 1), 0) + 2 * tr_slot);
-          const uint2 dTlo = lds_read_tr(dxp + tile_off(w, 1) + 2 * tr_slot);
-          const float4 k4 = *(const float4*)(sw + St::OK + 4 * g);
+          uint2 hT = make_uint2(0, 0), dT[NT], dTlo = make_uint2(0, 0);
+          float4 k4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
           float ucol = 0.0f, vcol = 0.0f;
-          if ((j & 3) == 0) {
-            ucol = ws[(j + g) * St::STEP + St::OU + 16 * w + n];
-            vcol = ws[(j + g) * St::STEP + St::OV + 16 * w + n];
+          if constexpr (!DW_WALK) {
+            hT = lds_read_tr(hj + tile_off(w, 0) + 2 * tr_slot);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) dT[tt] = lds_read_tr(dxp + tile_off((w + tt) & (NT - 1), 0) + 2 * tr_slot);
+          } else if constexpr (!DV_WALK) {
+            dT[0] = lds_read_tr(dxp + tile_off(w, 0) + 2 * tr_slot);
+          }
+          if constexpr (!DV_WALK) {
+            dTlo = lds_read_tr(dxp + tile_off(w, 1) + 2 * tr_slot);
+            k4 = *(const float4*)(sw + St::OK + 4 * g);
+            if ((j & 3) == 0) {
+              ucol = ws[(j + g) * St::STEP + St::OU + 16 * w + n];
+              vcol = ws[(j + g) * St::STEP + St::OV + 16 * w + n];
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
+          if constexpr (!DW_WALK) {
 #pragma unroll
-          for (int tt = 0; tt < NT; ++tt) dWacc[tt] = mfma16_f16(hT, dT[tt], dWacc[tt]);
+            for (int tt = 0; tt < NT; ++tt) dWacc[tt] = mfma16_f16(hT, dT[tt], dWacc[tt]);
+          }
           {
             const float g1 = 1.0f - f, m2g = -2.0f * g1;
             float Z[4];
@@ -1142,13 +1179,13 @@ __attribute__((amdgpu_waves_per_eu(WS ? 2 : 1, WS ? 2 : 1))) m2rnn_scan_bwd_kern
             if (i + 1 < SUB) kv = mfma_f32(avn, bkn, zero4);
           }
           __builtin_amdgcn_sched_barrier(0);
-          dv_step(j, js, sw, dT[0], dTlo, k4, ucol, vcol);
+          if constexpr (!DV_WALK) dv_step(j, js, sw, dT[0], dTlo, k4, ucol, vcol);
           if (gsum) dq_store(gq, j == 3 ? (p - 1) * SUB : p * SUB + 4);
         }
       }
       lds_barrier();
-      store_dwr();
-      store_dW();
+      if constexpr (!DV_WALK) store_dwr();
+      if constexpr (!DW_WALK) store_dW();
     }
   } else if constexpr (INTERLEAVE) {
     // Buffers of sub-segment p (p >= -1).
