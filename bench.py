@@ -230,9 +230,10 @@ def bench_backward(args) -> int:
               else "M²RNN bwd (BPTT) head-steps/sec")
     out = {"metric": metric, "value": hs / (ms * 1e-3), "unit": "head-steps/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": arithmetic("f16x3"), "data": "synthetic",
+           "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32 state, bf16x3 checkpoint forward, f16x3 reverse scan", "data": "synthetic",
            "config": {"workload": w.name, "B": B, "T": T, "N": N, "K": K, "V": V, "qkv_dtype": w.qkv_dtype,
-                      "math": "f16x3", "segment": m2.BWD_CHECKPOINT,
+                      "math": {"forward": "bf16x3", "reverse": "f16x3"}, "segment": m2.BWD_CHECKPOINT,
                       "checkpoint_interval": m2.m2rnn_checkpoint_interval(dims)},
            "timed": ("m2rnn_scan_bwd alone" if args.scan_only else
                      "m2rnn_fwd_ckpt + m2rnn_bwd_ckpt" if train else "m2rnn_bwd"),
@@ -417,7 +418,7 @@ def bench_fused_block(args) -> int:
     from matrix_state_nonlinear_m2rnn_amd import inputs
 
     w = inputs.WORKLOADS[args.workload]
-    math_mode = "f16x3" if args.math == "auto" else args.math
+    math_mode = "bf16x3" if args.math == "auto" else args.math
     d = inputs.workload_inputs(w.name)
     dev = torch.device("cuda:0")
     qkv_t = torch.bfloat16 if w.qkv_dtype == "bf16" else torch.float32
@@ -518,9 +519,9 @@ def bench_layer(args) -> int:
                       "fwd + bwd) tokens/sec",
             "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": arithmetic("f16x3"), "data": "synthetic",
+            "vs_baseline": None, "dtype": "f32 state, bf16x3 forward, f16x3 reverse scan", "data": "synthetic",
             "config": {"workload": w.name, "B": B, "T": T, "N": N, "K": K, "V": V, "activations": "fp32",
-                       "math": "f16x3", "params": "random init"}}
+                       "math": {"forward": "bf16x3", "reverse": "f16x3"}, "params": "random init"}}
     print(json.dumps(line), flush=True)
     return 0
 
@@ -592,7 +593,7 @@ def main() -> int:
     if args.layer:
         return bench_layer(args)
     w = inputs.WORKLOADS[args.workload]
-    math_mode = "f16x3" if args.math == "auto" else args.math
+    math_mode = "bf16x3" if args.math == "auto" else args.math
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     d = inputs.workload_inputs(w.name)
     dev = torch.device("cuda:0")

@@ -72,7 +72,10 @@ enum { M2RNN_DTYPE_F32 = 0, M2RNN_DTYPE_BF16 = 1 };
  *           fp32 accumulation (about 22 significant bits per product).
  *   BF16X3  split precision with bf16 halves: W_hi H_hi + W_lo H_hi + W_hi H_lo.
  *   BF16    one bf16 pass: bf16(W) bf16(H) (coarse; meant for a 2e-2 error budget).
- *   AUTO    the library's default (F16X3).
+ *   AUTO    the forwards' default: BF16X3 (measured 2% faster than F16X3 at the 16K-token
+ *           workload, with the full fp32 exponent range; about 3e-6 max-abs error on the state
+ *           where F16X3 gives 3e-7, both far inside a 5e-4 budget).  The backward's own
+ *           contraction is F16X3 (below).
  * Range of the split modes: the contraction takes 2 log2(e) W (so that tanh is one exp2) and the
  * state as 16-bit halves.  F16X3 needs |W| < 65504 / (2 log2 e) ~ 22700 elementwise and a state
  * below 65504 (with f in [0, 1] the state stays within max(|H0|, 1), Eq. 11); the fp16 remainder is
@@ -198,7 +201,9 @@ int m2rnn_scan_fwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, int r
  *          dH_T enter unclamped.  Negative or NaN: M2RNN_EINVAL.
  *   dq, dk [B,T,Nqk,K]; dv [B,T,N,V]; df [B,T,N]; dW [N,V,V] and dw_r [N,V] summed over batch and
  *   time; dH0 [B,N,K,V] or NULL to skip it.  All fp32.
- *   math   M2RNN_MATH_F16X3 or M2RNN_MATH_AUTO (the other modes return M2RNN_EUNSUPPORTED).
+ *   math   M2RNN_MATH_F16X3 or M2RNN_MATH_AUTO (the other modes return M2RNN_EUNSUPPORTED).  The
+ *          reverse scan recomputes the forward with F16X3 either way; the checkpoint pass that
+ *          m2rnn_bwd runs first uses the forwards' default for AUTO and F16X3 for F16X3.
  *
  * Scale of dy.  Every gradient is linear in (dy, dH_T) jointly, and the walk holds the chain's
  * D_t = ((1 - f_t) R_t) (.) (1 - Z_t^2) in split fp16, whose accurate range is narrow.  So each
@@ -232,8 +237,9 @@ int m2rnn_bwd(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, co
  * m2rnn_bwd_ckpt     m2rnn_bwd with `ckpt` from m2rnn_fwd_ckpt on the same inputs in place of H0
  *                    (H0 is ckpt[., ., 0]); its workspace (m2rnn_bwd_ckpt_workspace_size) excludes
  *                    the checkpoints.  Gradients equal m2rnn_bwd's when the forward used the
- *                    F16X3 contraction (the backward's own); another contraction mode gives
- *                    checkpoints, and so gradients, that differ within that mode's error.
+ *                    contraction of m2rnn_bwd's own checkpoint pass: the forwards' default for
+ *                    math = AUTO, F16X3 for math = F16X3.  Checkpoints from another mode give
+ *                    gradients that differ within that mode's error.
  */
 /* Steps between checkpoints (I above): 8 for V <= 64, 64 for V = 128.  Smaller
  * intervals let the backward skip a forward pass over every segment; at V = 128 the state is large

@@ -55,7 +55,7 @@ int check_dims(const m2rnn_dims* d, int qkv_dtype) {
 int qk_heads(const m2rnn_dims* d) { return d->Nqk == 1 ? 1 : (int)d->N; }
 
 int resolve_math(int math) {
-  if (math == M2RNN_MATH_AUTO) return M2RNN_MATH_F16X3;
+  if (math == M2RNN_MATH_AUTO) return M2RNN_MATH_BF16X3;
   if (math < M2RNN_MATH_F32 || math > M2RNN_MATH_BF16) return -1;
   return math;
 }
@@ -760,7 +760,9 @@ int bwd_impl(const m2rnn_dims* dims, int qkv_dtype, int math, const void* q, con
       a.Ts = (int)T;
       a.Tp = (int)T;
       a.Nqk = qk_heads(d);
-      const void* kern = fwd_kernel(M2RNN_MATH_F16X3, (int)V, 1, 1, bf16, MODE_CKPT);
+      // (the forwards' contraction: the default's unless F16X3 was asked for)
+      const void* kern = fwd_kernel(math == M2RNN_MATH_F16X3 ? M2RNN_MATH_F16X3 : resolve_math(M2RNN_MATH_AUTO),
+                                    (int)V, 1, 1, bf16, MODE_CKPT);
       if (!kern) return M2RNN_EUNSUPPORTED;
       void* args[] = {&a};
       st = hip_status(hipLaunchKernel(kern, dim3((unsigned)(B * N * S)), dim3((unsigned)(4 * V)), args, 0, stream));

@@ -18,7 +18,7 @@ const void* pick_fwd_vrb(bool bf16, int mode) {
   if (mode == MODE_FWD)
     return bf16 ? (const void*)&m2rnn_scan_fwd_kernel<V, RB, MATH, true, MODE_FWD, RW>
                 : (const void*)&m2rnn_scan_fwd_kernel<V, RB, MATH, false, MODE_FWD, RW>;
-  if constexpr ((MATH == MATH_F32 || MATH == MATH_F16X3) && RW == 1) {
+  if constexpr (MATH != MATH_BF16 && RW == 1) {
     if (mode == MODE_CKPT)
       return bf16 ? (const void*)&m2rnn_scan_fwd_kernel<V, RB, MATH, true, MODE_CKPT>
                   : (const void*)&m2rnn_scan_fwd_kernel<V, RB, MATH, false, MODE_CKPT>;

@@ -40,8 +40,10 @@ def test_b4_h16_t2048_kv64_full(math):
 
 @pytest.mark.parametrize("name,units,math", [
     ("long_b2_h32_t16384_kv64", [(0, 0), (1, 31), (0, 17), (1, 5)], "f16x3"),
+    ("long_b2_h32_t16384_kv64", [(0, 0), (1, 31), (0, 17), (1, 5)], "bf16x3"),
     ("long_b2_h32_t16384_kv64", [(0, 3), (1, 20)], "f32"),
     ("b8_h16_t4096_kv128", [(0, 0), (7, 15)], "f16x3"),
+    ("b8_h16_t4096_kv128", [(0, 0), (7, 15)], "bf16x3"),
     ("b1_h16_t4096_kv128", [(0, 0), (0, 9)], "f16x3"),
 ])
 def test_full_size_sampled_units(name, units, math):
