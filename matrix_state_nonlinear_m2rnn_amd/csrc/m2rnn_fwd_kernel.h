@@ -225,11 +225,11 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
     lo = l;
   } else if constexpr (MATH == MATH_BF16X3) {
     hi = pack_bf16(a, b);
-    // Both fp32 values of hi are taken from the packed word (a shift and a mask); left visible, the
-    // compiler converts a once more on its own to form the first (two more VALU instructions).
-    uint32_t h = hi;
-    asm("" : "+v"(h));
-    lo = pack_bf16(a - bf16_lo_to_f32(h), b - bf16_hi_to_f32(h));
+    // The fp32 values of hi's halves, each one byte permute of the packed word (a shift or a mask
+    // written plainly, the compiler converts a once more to form the first, or copies hi).
+    const float ha = __uint_as_float(__builtin_amdgcn_perm(0u, hi, 0x01000c0cu));
+    const float hb = __uint_as_float(__builtin_amdgcn_perm(0u, hi, 0x03020c0cu));
+    lo = pack_bf16(a - ha, b - hb);
   } else {
     hi = pack_bf16(a, b);
     lo = 0;
