@@ -314,9 +314,14 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint32_t* p) {
 // each and the two roles split the LDS reads, which one wave can only drain at a limited rate, and
 // the issue of VALU and MFMA work.  Both roles meet at the same barriers; the arithmetic is the
 // one-role kernel's, operation for operation.
+// Waves per SIMD the compiler schedules for: one for the one-role kernel at V = 64 (its LDS holds
+// one workgroup of four waves per CU), two otherwise.  (The one-wave hint on the one-wave
+// workgroups of V = 16, of which two share each SIMD, took the paper shape's reverse scan from 2.9
+// to 4.0 ms.)
 template <int V, bool BF16IN, bool WS = false>
 __global__ void __launch_bounds__(64 * (V / 16) * (WS ? 2 : 1))
-__attribute__((amdgpu_waves_per_eu(WS ? 2 : 1, WS ? 2 : 1))) m2rnn_scan_bwd_kernel(const BwdArgs a) {
+__attribute__((amdgpu_waves_per_eu(!WS && V == 64 ? 1 : 2, !WS && V == 64 ? 1 : 2)))
+m2rnn_scan_bwd_kernel(const BwdArgs a) {
   constexpr bool SUBCK = BwdCkpt<V>::sub;  // checkpoints at every sub-segment
   constexpr int NT = V / 16;
   constexpr int NTH = 64 * NT;
