@@ -860,14 +860,6 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
         vcol = ss[(j + g) * St::STEP + St::OV + 16 * w + n];
       }
     }
-#ifdef BWD_ILV
-    // one chain MFMA, then three reads, six times
-#pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-    }
-#endif
     __builtin_amdgcn_sched_barrier(0);
     hook_mfma();
     // Off the chain, while the MFMAs run.
