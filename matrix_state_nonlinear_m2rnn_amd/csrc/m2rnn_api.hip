@@ -383,6 +383,26 @@ struct m2rnn_overlap_s {
 
 namespace {
 
+// Estimated time of the second pass per step over the scan's time per step, for the segment plan.
+// The second pass streams the S partial planes and v in and the output out, B N V (4 S + 8) bytes
+// per step, taken at 5.5 TB/s; the scan takes at least 220 ns per step and round of resident
+// workgroups on MI355X (228 ns at K = V = 64 with one round; more at larger V and in the fp32
+// contraction), so the ratio is an upper estimate except for the one-pass bf16 contraction.
+double second_pass_ratio(const FwdCall& c, int math, int rb) {
+  const m2rnn_dims* d = c.d;
+  const DeviceInfo info = device_info();
+  int threads = 0;
+  const void* kern = fwd_launch_kernel(d, math, rb, c.qkv_dtype == M2RNN_DTYPE_BF16, MODE_FWD, &threads);
+  const int occ = kern && info.cus > 0 ? occupancy(kern, threads) : 0;
+  if (occ <= 0) return 1e30;
+  const long S = readout_planes(d, rb, math);
+  const long blocks = d->B * d->N * S;
+  const long cap = (long)occ * info.cus;
+  const double rounds = (double)((blocks + cap - 1) / cap);
+  const double second = (double)d->B * d->N * d->V * (4.0 * S + 8.0) / 5.5e12;
+  return second / (220e-9 * rounds);
+}
+
 // The segmented forward: the scan of each time segment on the call's stream, then
 // second(t0, len, side stream) for that segment.  Returns 1 when it does not apply (no overlap
 // object, or a stream under graph capture); the caller then runs the single pass.  Segment ends
@@ -393,19 +413,32 @@ int fwd_segmented(const FwdCall& c, m2rnn_overlap_s* ov, int math, int rb, Secon
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(c.stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return 1;
   const m2rnn_dims* d = c.d;
-  // Segment ends at 5/16, 10/16 and 15/16 of T: the last finish pass, which nothing overlaps,
-  // covers a sixteenth of the sequence.
+  // Each segment's second pass runs under the next segment's scan; the last one, which nothing
+  // overlaps, should be short, and every launch boundary costs about 15 us.  With r the estimated
+  // ratio above times a margin of 1.5: when r <= 1/4, two segments, the second just long enough
+  // (a fraction r / (1 + r) of T) to cover the first's second pass (at 16K steps and K = V = 64:
+  // 1792 steps); otherwise four, ending at 5/16, 10/16 and 15/16 of T, each second pass under a
+  // scan as long as its own segment and the last over a sixteenth.
   long ends[kFwdSegs];
-  for (int e = 0; e < kFwdSegs - 1; ++e) ends[e] = d->T * (5 * (e + 1)) / 16 / 64 * 64;
-  ends[kFwdSegs - 1] = d->T;
+  int nseg = kFwdSegs;
+  const double r = 1.5 * second_pass_ratio(c, math, rb);
+  if (r <= 0.25) {
+    const long tail = ((long)(d->T * r / (1.0 + r)) + 63) / 64 * 64;
+    ends[0] = (d->T - std::max(tail, 64L)) / 64 * 64;
+    ends[1] = d->T;
+    nseg = 2;
+  } else {
+    for (int e = 0; e < kFwdSegs - 1; ++e) ends[e] = d->T * (5 * (e + 1)) / 16 / 64 * 64;
+    ends[kFwdSegs - 1] = d->T;
+  }
   char* hb = (char*)c.ws + fwd_partial_bytes(d, rb, math);
   float* hbuf[2] = {(float*)hb, (float*)(hb + fwd_seg_state_bytes(d))};
   const float* H0 = c.H0;
   int st = M2RNN_OK, i = 0;
   bool forked = false;
-  for (long t0 = 0; i < kFwdSegs && st == M2RNN_OK; t0 = ends[i++]) {
+  for (long t0 = 0; i < nseg && st == M2RNN_OK; t0 = ends[i++]) {
     const long len = ends[i] - t0;
-    float* HT = i == kFwdSegs - 1 ? c.H_T : hbuf[i & 1];
+    float* HT = i == nseg - 1 ? c.H_T : hbuf[i & 1];
     st = launch_scan_seg(c, math, rb, t0, len, H0, HT, whole_planes(c, t0));
     if (st) break;
     st = record_hip_status(hipEventRecord(ov->ev[i], c.stream));
