@@ -132,13 +132,13 @@ int m2rnn_overlap_destroy(m2rnn_overlap overlap);
  *
  *   overlap      NULL, or an overlap object of the current device (see above).
  *
- * With split rows, T >= 4096 and an overlap object, m2rnn_fwd runs the sequence in four time
- * segments, each starting from the state the previous one ended in, and the second pass of each
- * segment runs on the object's side stream while the next segment is scanned; the call's stream
- * waits for all of it before any later work.  This needs the two state buffers that
- * m2rnn_fwd_workspace_size() adds for such shapes; with a smaller workspace (the partial planes
- * only), without an overlap object, or on a stream under graph capture, the single pass runs
- * instead.  The two ways of running give the same bits: H_t is a function of H_{t-1} and the
+ * With split rows, T >= 4096 and an overlap object, m2rnn_fwd runs the sequence in two time
+ * segments, the second starting from the state the first ended in, and the first segment's second
+ * pass runs on the object's side stream while the second segment is scanned (the second segment is
+ * sized to cover it); the call's stream waits for all of it before any later work.  This needs the
+ * state buffer that m2rnn_fwd_workspace_size() adds for such shapes; with a smaller workspace (the
+ * partial planes only), without an overlap object, or on a stream under graph capture, the single
+ * pass runs instead.  The two ways of running give the same bits: H_t is a function of H_{t-1} and the
  * step's inputs only, and a scan started from a stored state computes exactly what a continuous
  * scan does.
  */

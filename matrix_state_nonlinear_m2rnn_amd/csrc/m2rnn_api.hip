@@ -354,7 +354,7 @@ int launch_finish(const FwdCall& c, int math, int rb) {
 // on the caller's side stream while the next segment is scanned (the scan keeps one wave per SIMD,
 // so the finish pass's waves use the free slots), instead of the whole finish pass after the whole
 // scan.  The state goes from one segment to the next through two buffers after the partial planes.
-constexpr int kFwdSegs = 4;
+constexpr int kFwdSegs = 2;
 constexpr long kFwdSegMinT = 4096;
 
 bool fwd_segmentable(const m2rnn_dims* d, int rb, int math) {
@@ -365,10 +365,11 @@ size_t fwd_seg_state_bytes(const m2rnn_dims* d) {
   return round_up((size_t)d->B * d->N * d->K * d->V * sizeof(float));
 }
 
-// m2rnn_fwd's workspace: the partial planes, and the segment states when it segments.
+// m2rnn_fwd's workspace: the partial planes, and the state between the time segments when it
+// segments.
 size_t fwd_ws_bytes(const m2rnn_dims* d, int rb, int math) {
   if (d->B == 0 || d->N == 0) return 0;
-  return fwd_partial_bytes(d, rb, math) + (fwd_segmentable(d, rb, math) ? 2 * fwd_seg_state_bytes(d) : 0);
+  return fwd_partial_bytes(d, rb, math) + (fwd_segmentable(d, rb, math) ? fwd_seg_state_bytes(d) : 0);
 }
 
 }  // namespace
@@ -413,32 +414,22 @@ int fwd_segmented(const FwdCall& c, m2rnn_overlap_s* ov, int math, int rb, Secon
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(c.stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return 1;
   const m2rnn_dims* d = c.d;
-  // Each segment's second pass runs under the next segment's scan; the last one, which nothing
-  // overlaps, should be short, and every launch boundary costs about 15 us.  With r the estimated
-  // ratio above times a margin of 1.5: when r <= 1/4, two segments, the second just long enough
-  // (a fraction r / (1 + r) of T) to cover the first's second pass (at 16K steps and K = V = 64:
-  // 1792 steps); otherwise four, ending at 5/16, 10/16 and 15/16 of T, each second pass under a
-  // scan as long as its own segment and the last over a sixteenth.
-  long ends[kFwdSegs];
-  int nseg = kFwdSegs;
+  // Two segments: the first segment's second pass runs under the second segment's scan, and only
+  // the second segment's own second pass is left over, so the second segment is made just long
+  // enough to cover the first's: a fraction r / (1 + r) of T, with r the estimated ratio above
+  // times a margin of 1.5 (at 16K steps and K = V = 64, r = 0.12 and 1792 steps), at most half.
+  // Every launch boundary costs about 15 us, so more segments do not pay where r is small (as at
+  // every split-row shape the kernels are built for, r <= 0.25).
   const double r = 1.5 * second_pass_ratio(c, math, rb);
-  if (r <= 0.25) {
-    const long tail = ((long)(d->T * r / (1.0 + r)) + 63) / 64 * 64;
-    ends[0] = (d->T - std::max(tail, 64L)) / 64 * 64;
-    ends[1] = d->T;
-    nseg = 2;
-  } else {
-    for (int e = 0; e < kFwdSegs - 1; ++e) ends[e] = d->T * (5 * (e + 1)) / 16 / 64 * 64;
-    ends[kFwdSegs - 1] = d->T;
-  }
-  char* hb = (char*)c.ws + fwd_partial_bytes(d, rb, math);
-  float* hbuf[2] = {(float*)hb, (float*)(hb + fwd_seg_state_bytes(d))};
+  const long tail = std::min(((long)(d->T * std::min(r / (1.0 + r), 0.5)) + 63) / 64 * 64, d->T / 2);
+  const long ends[kFwdSegs] = {(d->T - std::max(tail, 64L)) / 64 * 64, d->T};
+  float* hmid = (float*)((char*)c.ws + fwd_partial_bytes(d, rb, math));  // the state between them
   const float* H0 = c.H0;
   int st = M2RNN_OK, i = 0;
   bool forked = false;
-  for (long t0 = 0; i < nseg && st == M2RNN_OK; t0 = ends[i++]) {
+  for (long t0 = 0; i < kFwdSegs && st == M2RNN_OK; t0 = ends[i++]) {
     const long len = ends[i] - t0;
-    float* HT = i == nseg - 1 ? c.H_T : hbuf[i & 1];
+    float* HT = i == kFwdSegs - 1 ? c.H_T : hmid;
     st = launch_scan_seg(c, math, rb, t0, len, H0, HT, whole_planes(c, t0));
     if (st) break;
     st = record_hip_status(hipEventRecord(ov->ev[i], c.stream));
@@ -650,9 +641,9 @@ size_t fwd_block_f_bytes(const m2rnn_dims* d) { return round_up((size_t)d->B * d
 size_t fwd_block_ws_bytes(const m2rnn_dims* d, int rb, int math) {
   if (d->B == 0 || d->N == 0 || d->T == 0) return 0;
   const size_t planes = fwd_partial_bytes(d, rb, math);
-  // planes, or y; then the states of the time segments (as m2rnn_fwd's workspace after the planes)
+  // planes, or y; then the state between the time segments (as m2rnn_fwd's workspace after the planes)
   return fwd_block_f_bytes(d) + (planes > 0 ? planes : round_up((size_t)d->B * d->T * d->N * d->V * sizeof(float))) +
-         (fwd_segmentable(d, rb, math) ? 2 * fwd_seg_state_bytes(d) : 0);
+         (fwd_segmentable(d, rb, math) ? fwd_seg_state_bytes(d) : 0);
 }
 
 int m2rnn_fwd_block_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blocks,
@@ -712,7 +703,7 @@ int m2rnn_fwd_block(const m2rnn_dims* dims, int qkv_dtype, int math, int row_blo
                                                          S > 1 ? w_r : nullptr, gz, gz_dtype == M2RNN_DTYPE_BF16,
                                                          gamma, dims->B, dims->T, t0, len, D, eps, out, s2));
   };
-  if (overlap && fwd_segmentable(dims, rb, m)) {  // the workspace holds the segment states (checked above)
+  if (overlap && fwd_segmentable(dims, rb, m)) {  // the workspace holds the segment state (checked above)
     st = fwd_segmented(c, overlap, m, rb, epilogue);
     if (st != 1) return st;
   }
