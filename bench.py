@@ -541,8 +541,8 @@ def _fwd_block_ws(m2, w, math_mode, row_blocks) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_b2_h32_t16384_kv64")
     ap.add_argument("--math", default="auto", choices=["auto", "f32", "f16x3", "bf16x3", "bf16"])
     ap.add_argument("--row-blocks", type=int, default=0)
