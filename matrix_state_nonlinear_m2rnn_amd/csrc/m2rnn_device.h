@@ -96,24 +96,6 @@ __device__ __forceinline__ float f16_hi_to_f32(uint32_t w) {
   return (float)__builtin_bit_cast(fp16x2, w)[1];
 }
 
-// Splits two fp32 values into (hi, lo) 16-bit pairs for the split-precision contraction.
-//   F16X3:  hi = fp16(x), lo = bf16(x - hi)  (x - hi is exact in fp32)
-//   BF16X3: hi = bf16(x), lo = bf16(x - hi)
-//   BF16:   hi = bf16(x), lo unused
-template <int MATH>
-__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
-  if constexpr (MATH == MATH_F16X3) {
-    hi = pack_f16(a, b);
-    lo = pack_bf16(a - f16_lo_to_f32(hi), b - f16_hi_to_f32(hi));
-  } else if constexpr (MATH == MATH_BF16X3) {
-    hi = pack_bf16(a, b);
-    lo = pack_bf16(a - bf16_lo_to_f32(hi), b - bf16_hi_to_f32(hi));
-  } else {
-    hi = pack_bf16(a, b);
-    lo = 0;
-  }
-}
-
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
