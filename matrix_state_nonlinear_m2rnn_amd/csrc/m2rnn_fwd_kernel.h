@@ -61,6 +61,9 @@ struct FwdShape {
   static constexpr int NT = V / 16;          // value tiles = waves per row group
   static constexpr int NTH = 64 * NT * RW;   // threads per workgroup
   static constexpr int TC = 16;              // steps per staged chunk (the step loop is unrolled per chunk)
+  // Steps per chunk of the readout-waves kernel: its readout waves stage a chunk while the chain
+  // runs, and fewer, longer chunks mean fewer staging steps (64 against 16: 2% faster at 16K steps).
+  static constexpr int TC_RO = 64;
 };
 
 // Per-step stage record (fp32): [f, 1-f, -2(1-f), 0 | q rows | c*k rows | v (V)] (slot 3 is the
@@ -123,12 +126,12 @@ struct TileLoader {
 };
 
 // Prefetch registers for one chunk of q, k, v, f.
-template <int V, int RB, bool BF16, int RW = 1>
+template <int V, int RB, bool BF16, int RW = 1, int TC = FwdShape<V, RW>::TC>
 struct ChunkRegs {
   using S = FwdShape<V, RW>;
   static constexpr int ROWS = 16 * RB * RW;  // rows staged for the whole workgroup
-  TileLoader<S::TC, ROWS, S::NTH, BF16> q, k;
-  TileLoader<S::TC, V, S::NTH, BF16> v;
+  TileLoader<TC, ROWS, S::NTH, BF16> q, k;
+  TileLoader<TC, V, S::NTH, BF16> v;
   float f;
 
   // The pieces of q, k, v and f start at different waves (thread indices rotated by 64 per
@@ -137,7 +140,7 @@ struct ChunkRegs {
   static __device__ __forceinline__ int rot(int tid, int r) { return (tid + S::NTH - r % S::NTH) % S::NTH; }
 
   __device__ __forceinline__ void load(const FwdArgs& a, int b, int nh, int row0, int t0, int tid) {
-    const int valid = min(S::TC, a.T - t0);
+    const int valid = min(TC, a.T - t0);
     const long qk_off = (((long)b * a.Ts + t0) * a.Nqk + (a.Nqk == 1 ? 0 : nh)) * a.K + row0;
     const long v_off = (((long)b * a.Ts + t0) * a.N + nh) * V;
     const int esz = BF16 ? 2 : 4;
@@ -154,7 +157,7 @@ struct ChunkRegs {
     k.store(stage, St::STEP, St::OK, kTwoLog2e, rot(tid, 64));
     v.store(stage, St::STEP, St::OV, 1.0f, rot(tid, 128));
     const int tf = rot(tid, 192);
-    if (tf < S::TC) {
+    if (tf < TC) {
       const float gf = 1.0f - f;
       *(float4*)(stage + tf * St::STEP) = make_float4(f, gf, -2.0f * gf, 0.0f);
     }
@@ -811,7 +814,7 @@ __global__ void __launch_bounds__(2 * 64 * (V / 16)) m2rnn_scan_fwd_ro_kernel(co
   using Sh = FwdShape<V, 1>;
   using St = Stage<V, RB>;
   constexpr int NT = Sh::NT;
-  constexpr int TC = Sh::TC;
+  constexpr int TC = Sh::TC_RO;
   constexpr int ROWS = 16 * RB;
   constexpr int NCH = NT / 2;  // 32-wide contraction chunks
   constexpr int NOTH = NCH > 1 ? NCH - 1 : 1;
@@ -1109,7 +1112,7 @@ __global__ void __launch_bounds__(2 * 64 * (V / 16)) m2rnn_scan_fwd_ro_kernel(co
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, ylane + (uint32_t)(tg * ystep * 4), 0, 0);
     };
 
-    ChunkRegs<V, RB, BF16IN, 1> pre;
+    ChunkRegs<V, RB, BF16IN, 1, TC> pre;
     pre.load(a, b, nh, row0, 0, rtid);
     pre.store(stage[0], rtid);
     if (a.T > TC) pre.load(a, b, nh, row0, TC, rtid);
