@@ -60,7 +60,9 @@ template <int V, int RW = 1>
 struct FwdShape {
   static constexpr int NT = V / 16;          // value tiles = waves per row group
   static constexpr int NTH = 64 * NT * RW;   // threads per workgroup
-  static constexpr int TC = 16;              // steps per staged chunk (the step loop is unrolled per chunk)
+  // Steps per staged chunk (the step loop is unrolled per chunk): 32 where the state is narrow
+  // (V <= 32: the step is short, so the staging step and its barriers weigh more), else 16.
+  static constexpr int TC = V <= 32 ? 32 : 16;
   // Steps per chunk of the readout-waves kernel: its readout waves stage a chunk while the chain
   // runs, and fewer, longer chunks mean fewer staging steps (64 against 16: 2% faster at 16K steps).
   static constexpr int TC_RO = 64;
@@ -286,12 +288,13 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
   //          of a chunk, 512 bytes apart, are read by one 2 x 8-byte instruction.
   constexpr int XWORDS = SPLIT ? (RB * NCH * 2 * 64 * 4) : (RB * NT * 64 * 4);
   __shared__ __attribute__((aligned(16))) uint32_t xbuf[2][RW][XWORDS];
-  // Several row groups (split modes): their readout partials meet here, [3 chunks][4 groups of four
-  // steps][RW][NT][64 lanes], and are summed in the workgroup (a ring of three chunks: a chunk's
-  // groups are summed one chunk later, and its slot is reused two chunks after that, so barriers
-  // at every chunk keep writers and readers apart).
+  // Several row groups (split modes): their readout partials meet here, [3 chunks][TC / 4 groups of
+  // four steps][RW][NT][64 lanes], and are summed in the workgroup (a ring of three chunks: a
+  // chunk's groups are summed one chunk later, and its slot is reused two chunks after that, so
+  // barriers at every chunk keep writers and readers apart).
   constexpr bool YRED = MODE == MODE_FWD && SPLIT && RW > 1;
-  __shared__ float ybuf[YRED ? 3 * 4 * RW * NT * 64 : 1];
+  constexpr int GPC = TC / 4;  // groups of four steps per chunk
+  __shared__ float ybuf[YRED ? 3 * GPC * RW * NT * 64 : 1];
 
   const int tid = threadIdx.x;
   const int w = (tid >> 6) % NT;   // value tile of this wave
@@ -474,7 +477,7 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
   auto ykeep = [&](int tg, float yv) {
     if constexpr (YRED) {
       const int slot = (tg / TC) % 3, k = (tg % TC) / 4;
-      ybuf[(((slot * 4 + k) * RW + wr) * NT + w) * 64 + lane] = yv;
+      ybuf[(((slot * GPC + k) * RW + wr) * NT + w) * 64 + lane] = yv;
     }
   };
   // ... and summed, for the chunk starting at tc: wave (w, wr) stores the groups k = wr, wr + RW, ...
@@ -483,10 +486,10 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
     if constexpr (YRED) {
       const int slot = (tc / TC) % 3;
 #pragma unroll
-      for (int k = wr; k < 4; k += RW) {
+      for (int k = wr; k < GPC; k += RW) {
         float yv = 0.0f;
 #pragma unroll
-        for (int r = 0; r < RW; ++r) yv += ybuf[(((slot * 4 + k) * RW + r) * NT + w) * 64 + lane];
+        for (int r = 0; r < RW; ++r) yv += ybuf[(((slot * GPC + k) * RW + r) * NT + w) * 64 + lane];
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yres, ylane + (uint32_t)((tc + 4 * k) * ystep * 4), 0,
                                               0);
       }
