@@ -120,8 +120,9 @@ int m2rnn_overlap_destroy(m2rnn_overlap overlap);
 /*
  * Forward pass, Eq. (10)-(12).  One pass over all T steps for every (b, n).
  *
- *   row_blocks   0 = automatic; otherwise the number of 16-row blocks of the state that one
- *                workgroup carries (must divide K/16).  The K rows of a state evolve
+ *   row_blocks   0 = automatic (one, wherever that kernel keeps its state in registers);
+ *                otherwise the number of 16-row blocks of the state that one workgroup carries
+ *                (must divide K/16).  The K rows of a state evolve
  *                independently (W mixes only the value dimension, §1.2), so a (b, n) pair may be
  *                split over S = K/(16*row_blocks) workgroups; when S > 1 their partial readouts are
  *                summed by a second, deterministic pass.

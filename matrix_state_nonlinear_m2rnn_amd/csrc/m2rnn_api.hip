@@ -137,11 +137,13 @@ bool readout_waves() {
   return !(e && e[0] == '0');
 }
 
-// The forward kernel of a launch (MODE_FWD: with readout waves where built) and its threads.
+// The forward kernel of a launch (MODE_FWD: with readout waves where built and kept in registers)
+// and its threads.
 const void* fwd_launch_kernel(const m2rnn_dims* d, int math, int rb, bool bf16, int mode, int* threads) {
   const int rw = row_groups(d, rb, math);
   if (mode == MODE_FWD && readout_waves()) {
-    if (const void* k = fwd_kernel(math, (int)d->V, rb, rw, bf16, MODE_FWD_RO)) {
+    const void* k = fwd_kernel(math, (int)d->V, rb, rw, bf16, MODE_FWD_RO);
+    if (k && !(device_info().cus > 0 && spills(k))) {
       *threads = (int)(8 * d->V * rw);
       return k;
     }
@@ -150,41 +152,34 @@ const void* fwd_launch_kernel(const m2rnn_dims* d, int math, int rb, bool bf16, 
   return fwd_kernel(math, (int)d->V, rb, rw, bf16, mode);
 }
 
-// Row blocks per workgroup: among the kernels that keep everything in registers, the smallest
-// that lets every workgroup be resident at once (one wave of workgroups), else the one with the
-// fewest waves of workgroups.  A kernel that spills (several row blocks of a wide state) runs
-// far slower than more waves of workgroups, so it is taken only when nothing else is built.
+// Row blocks per wave: the fewest whose kernel keeps everything in registers.  A wave's work per
+// step grows with its row blocks, so once a CU holds enough waves, packing more row blocks into a
+// wave saves nothing, and smaller workgroups fill the last round of resident workgroups better.
+// Measured with bf16x3 at T = 2048 over 512 to 8192 row blocks and V = 16..128, one row block was
+// the fastest or tied in every case, also where it needs more rounds of workgroups (K = V = 64,
+// B12 N32: 2.25 ms against 3.20 ms with four row blocks and half the rounds; K = V = 128, B6 N16:
+// 2.99 against 4.19 ms with two).  A kernel that spills runs far slower still, so it is taken only
+// when nothing else is built.
 int plan_row_blocks(const m2rnn_dims* d, int math, bool bf16, int mode, int requested) {
   const int kb = (int)(d->K / 16);
   if (requested > 0)
     return (kb % requested == 0 && fwd_kernel(math, (int)d->V, requested, row_groups(d, requested, math), bf16, mode))
                ? requested
                : -1;
-  const DeviceInfo info = device_info();
-  const long units = d->B * d->N;
-  int best = -1, spilling = -1;
-  double best_rounds = 1e30;
+  const bool on_device = device_info().cus > 0;
+  int spilling = -1;
   for (int rb : {1, 2, 4}) {
     if (kb % rb != 0) continue;
-    const int rw = row_groups(d, rb, math);
     int threads = 0;
     const void* kern = fwd_launch_kernel(d, math, rb, bf16, mode, &threads);
     if (!kern) continue;
-    if (info.cus > 0 && spills(kern)) {
+    if (on_device && spills(kern)) {
       if (spilling < 0) spilling = rb;
       continue;
     }
-    const long blocks = units * (kb / (rb * rw));
-    const int occ = info.cus > 0 ? occupancy(kern, threads) : 0;
-    const double cap = (double)occ * info.cus;
-    const double rounds = cap > 0 ? (double)((blocks + (long)cap - 1) / (long)cap) : 1.0;
-    if (rounds < best_rounds) {
-      best_rounds = rounds;
-      best = rb;
-    }
-    if (rounds <= 1.0) break;
+    return rb;
   }
-  return best > 0 ? best : spilling;
+  return spilling;
 }
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }

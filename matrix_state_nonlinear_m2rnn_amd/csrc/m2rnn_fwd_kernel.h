@@ -65,7 +65,8 @@ struct FwdShape {
   static constexpr int TC = V <= 32 ? 32 : 16;
   // Steps per chunk of the readout-waves kernel: its readout waves stage a chunk while the chain
   // runs, and fewer, longer chunks mean fewer staging steps (64 against 16: 2% faster at 16K steps).
-  static constexpr int TC_RO = 64;
+  // At V = 128 a chunk of 32 keeps the staging registers within the 128 VGPRs of a 16-wave group.
+  static constexpr int TC_RO = V <= 64 ? 64 : 32;
 };
 
 // Per-step stage record (fp32): [f, 1-f, -2(1-f), 0 | q rows | c*k rows | v (V)] (slot 3 is the

@@ -288,15 +288,16 @@ def test_batch_16_at_16k_tokens_beyond_2_gib():
 def test_readout_waves_give_the_single_role_kernels_bits(math, monkeypatch):
     # The forward with its readout and staging in waves of their own computes every operation of
     # the single-role kernel in the same order: y, H_T and the checkpoints are the same bits, for
-    # every row split and a ragged tail.
+    # every row split and a ragged tail (K = V = 128: 32-step chunks, one row block per wave).
     torch = torch_cuda()
     import matrix_state_nonlinear_m2rnn_amd as m2
-    for B, T, N, seed in ((2, 300, 8, 61), (1, 70, 3, 62), (1, 33, 2, 63)):
-        d = inputs.make_inputs(B, T, N, 64, 64, qkv_dtype="bf16", seed=seed, with_H0=True)
+    for B, T, N, KV, seed in ((2, 300, 8, 64, 61), (1, 70, 3, 64, 62), (1, 33, 2, 64, 63), (2, 130, 4, 128, 64),
+                              (1, 31, 1, 128, 65)):
+        d = inputs.make_inputs(B, T, N, KV, KV, qkv_dtype="bf16", seed=seed, with_H0=True)
         dd = to_device(d, "bf16")
         args = (dd["q"], dd["k"], dd["v"], dd["f"], dd["W"], dd["w_r"], dd["H0"])
-        for rb in (1, 2, 4):
-            say("readout waves", B, T, N, math, "row_blocks", rb)
+        for rb in ((1, 2, 4) if KV == 64 else (1,)):
+            say("readout waves", B, T, N, KV, math, "row_blocks", rb)
             monkeypatch.delenv("M2RNN_FWD_READOUT_WAVES", raising=False)
             y1, H1, c1 = m2.m2rnn_fwd_ckpt(*args, math=math, row_blocks=rb)
             monkeypatch.setenv("M2RNN_FWD_READOUT_WAVES", "0")
