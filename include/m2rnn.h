@@ -27,7 +27,8 @@
  *    Gradients have the shape of their input and are fp32.
  *  - Every array pointer is a DEVICE pointer on the current HIP device, 16-byte aligned.  The
  *    caller owns all memory, including the workspace, and every stream: the library allocates no
- *    device memory and keeps no mutable global state (bar m2rnn_fwd_noalloc's fixed array, below),
+ *    device memory and keeps no state that one call leaves for another (bar m2rnn_fwd_noalloc's
+ *    fixed array, below; the host side caches only device and kernel attributes, under a lock),
  *    so calls on different streams may run concurrently.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call returns
  *    without synchronising.  Outputs are valid once the stream reaches that point.
