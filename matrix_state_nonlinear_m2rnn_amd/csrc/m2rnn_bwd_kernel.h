@@ -476,9 +476,16 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
     }
     return o;
   };
-  // acc += A B over all chunks (three split passes per chunk).
+  // acc += A B over all chunks (three split passes per chunk).  A single tile (V = 16) has no
+  // partner: its low halves take the empty k-slots 4..7, and two MFMAs, against [A_hi | A_hi] and
+  // [A_lo | 0] (A_lo's slots 4..7 are zero), form the three products.
   auto contract = [&](f32x4 acc, const uint4& AownHi, const uint4& AownLo, const uint4 (&AothHi)[NOTH],
                       const uint4 (&AothLo)[NOTH], const uint2& own_hi, const uint2& own_lo, const Ops& o) {
+    if constexpr (!has_partner) {
+      const uint4 b = make_uint4(own_hi.x, own_hi.y, own_lo.x, own_lo.y);
+      acc = mfma_f16(make_uint4(AownHi.x, AownHi.y, AownHi.x, AownHi.y), b, acc);
+      return mfma_f16(AownLo, b, acc);
+    }
     const uint4 bh = make_uint4(own_hi.x, own_hi.y, o.ph.x, o.ph.y);
     const uint4 bl = make_uint4(own_lo.x, own_lo.y, o.pl.x, o.pl.y);
     acc = mfma_f16(AownHi, bh, acc);

@@ -332,6 +332,11 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
   // from LDS (k-slots 4..7); the other chunks are read whole.  The A operands follow that order.
   constexpr int NOTH = NCH > 1 ? NCH - 1 : 1;
   const int co = w >> 1;  // own chunk
+  // A single tile (V = 16) leaves k-slots 4..7 of its chunk empty; the split modes put the state's
+  // low halves there (hq = [hi | lo]), so that one MFMA against [W_hi | W_hi] forms
+  // W_hi H_hi + W_hi H_lo and a second against [W_lo | 0] adds W_lo H_hi: two MFMAs a step instead
+  // of three (paper head shape 1.10 -> 1.02 ms), and the readout transposes [hi | lo] with one.
+  constexpr bool PACK1 = SPLIT && NT == 1 && MATH != MATH_BF16;
   uint4 wOwnHi, wOwnLo, wOthHi[NOTH], wOthLo[NOTH];
   auto wchunk = [&](int t_lo, int t_hi, uint4& hi, uint4& lo) {
     float wv[8];
@@ -417,6 +422,10 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
         hq[rb].y = h1;
         lq[rb].x = l0;
         lq[rb].y = l1;
+        if constexpr (PACK1) {
+          hq[rb].z = l0;
+          hq[rb].w = l1;
+        }
         if constexpr (NT > 1) {
           const int base = ((rb * NCH + (w >> 1)) * 4 + (w & 1)) * 128 + lane * 2;
           *(uint2*)&xbuf[buf][wr][base] = make_uint2(h0, h1);
@@ -665,12 +674,26 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
             acc[rb] = mfma_bf16(Ahi, h, acc[rb]);
           }
         };
+        if constexpr (PACK1) {
+          const uint4 a1 = make_uint4(wOwnHi.x, wOwnHi.y, wOwnHi.x, wOwnHi.y);  // [W_hi | W_hi]
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) contract(rb, wOwnHi, wOwnLo, hq[rb], lq[rb]);
+          for (int rb = 0; rb < RB; ++rb) {
+            if constexpr (MATH == MATH_F16X3) {
+              acc[rb] = mfma_f16(a1, hq[rb], acc[rb]);
+              acc[rb] = mfma_f16(wOwnLo, hq[rb], acc[rb]);  // [W_lo | 0]
+            } else {
+              acc[rb] = mfma_bf16(a1, hq[rb], acc[rb]);
+              acc[rb] = mfma_bf16(wOwnLo, hq[rb], acc[rb]);
+            }
+          }
+        } else {
 #pragma unroll
-        for (int i = 0; i < NCH - 1; ++i)
+          for (int rb = 0; rb < RB; ++rb) contract(rb, wOwnHi, wOwnLo, hq[rb], lq[rb]);
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) contract(rb, wOthHi[i], wOthLo[i], bh[rb * NOTH + i], bl[rb * NOTH + i]);
+          for (int i = 0; i < NCH - 1; ++i)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) contract(rb, wOthHi[i], wOthLo[i], bh[rb * NOTH + i], bl[rb * NOTH + i]);
+        }
       }
 
       // Next step's inputs (the stage record of step t+1 is complete, see above; past the last
@@ -709,7 +732,12 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
             const uint2 oh = make_uint2(hq[rb].x, hq[rb].y), ol = make_uint2(lq[rb].x, lq[rb].y);
-            if constexpr (MATH == MATH_F16X3) {
+            if constexpr (PACK1) {
+              // [hi | lo] against the identity twice (hi + lo is exact in fp32)
+              const uint4 bs2 = make_uint4(bsel.x, bsel.y, bsel.x, bsel.y);
+              if constexpr (MATH == MATH_F16X3) yT[rb] = mfma_f16(hq[rb], bs2, zero4);
+              else yT[rb] = mfma_bf16(hq[rb], bs2, zero4);
+            } else if constexpr (MATH == MATH_F16X3) {
               yT[rb] = mfma16_f16(ol, bsel, mfma16_f16(oh, bsel, zero4));
             } else if constexpr (MATH == MATH_BF16X3) {
               yT[rb] = mfma16_bf16(ol, bsel, mfma16_bf16(oh, bsel, zero4));
@@ -806,13 +834,14 @@ __global__ void __launch_bounds__(64 * (V / 16) * RW) m2rnn_scan_fwd_kernel(cons
 // as m2rnn_scan_fwd_kernel does (exchange reads, contraction, tanh and gate blend, publish of the
 // split state, the next step's rank-1 term), and NT readout waves, one per value tile, which
 //   - read the published split tile of H_{t-1} at step t (from the same exchange buffer the chain
-//     reads at that step), transpose it with two MFMAs against the identity, form its q-weighted
+//     reads at that step), transpose it with one MFMA against the identity, form its q-weighted
 //     row sums, and every four steps reduce across rows and store y (or the partial plane), and
 //   - stage the next chunk of q, k, v, f from HBM into the LDS ring.
 // Both roles meet at the one LDS barrier per step.  With two waves on every SIMD, the scheduler
 // fills one wave's waits (barrier, LDS round trip, MFMA latency) with the other's instructions, and
-// the chain waves no longer issue the readout and staging work at all.  The arithmetic is the same
-// as m2rnn_scan_fwd_kernel's, operation for operation, so the two give the same bits.
+// the chain waves no longer issue the readout and staging work at all.  The arithmetic is
+// m2rnn_scan_fwd_kernel's, operation for operation, except that the readout's transpose is one MFMA
+// where that kernel issues two (hi, then lo); hi + lo is exact in fp32, so the two give the same bits.
 template <int V, int RB, int MATH, bool BF16IN>
 __global__ void __launch_bounds__(2 * 64 * (V / 16)) m2rnn_scan_fwd_ro_kernel(const FwdArgs a) {
   using Sh = FwdShape<V, 1>;
@@ -1073,6 +1102,7 @@ __global__ void __launch_bounds__(2 * 64 * (V / 16)) m2rnn_scan_fwd_ro_kernel(co
       for (int e = 0; e < 4; ++e) e16[e] = (n == 4 * g + e) ? one : 0u;
       bsel = make_uint2(e16[0] | (e16[1] << 16), e16[2] | (e16[3] << 16));
     }
+    const uint4 bsel2 = make_uint4(bsel.x, bsel.y, bsel.x, bsel.y);
     int tile_off[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) tile_off[rb] = ((rb * NCH + (w >> 1)) * 4 + (w & 1)) * 128 + lane * 2;
@@ -1090,10 +1120,14 @@ __global__ void __launch_bounds__(2 * 64 * (V / 16)) m2rnn_scan_fwd_ro_kernel(co
         uint2 ol = make_uint2(0, 0);
         if constexpr (MATH != MATH_BF16) ol = *(const uint2*)&xb[tile_off[rb] + 256];
         q4[rb] = *(const float4*)(st + qlane + 16 * rb);
+        // One 16x16x32 MFMA with hi and lo side by side on the contraction index and the identity
+        // twice: hi + lo is exact in fp32, so this gives the bits of the two 16x16x16 transposes
+        // (hi, then + lo) for one MFMA issue instead of two.
+        const uint4 hl4 = make_uint4(oh.x, oh.y, ol.x, ol.y);
         if constexpr (MATH == MATH_F16X3) {
-          yT[rb] = mfma16_f16(ol, bsel, mfma16_f16(oh, bsel, zero4));
+          yT[rb] = mfma_f16(hl4, bsel2, zero4);
         } else if constexpr (MATH == MATH_BF16X3) {
-          yT[rb] = mfma16_bf16(ol, bsel, mfma16_bf16(oh, bsel, zero4));
+          yT[rb] = mfma_bf16(hl4, bsel2, zero4);
         } else {
           yT[rb] = mfma16_bf16(oh, bsel, zero4);
         }
