@@ -9,9 +9,9 @@ namespace m2rnn {
 template <int MATH, int V, int RB, int RW>
 const void* pick_fwd_vrb(bool bf16, int mode) {
   if (mode == MODE_FWD_RO) {
-    // readout waves: the split contractions at V = 64 and 128 (up to two row blocks there, whose
-    // 64-step stage ring fits the LDS), one row group
-    if constexpr (MATH != MATH_F32 && RW == 1 && (V == 64 || (V == 128 && RB <= 2)))
+    // readout waves: the split contractions at V = 64, and at V = 128 with one row block per wave
+    // (two would spill in a 16-wave workgroup), one row group
+    if constexpr (MATH != MATH_F32 && RW == 1 && (V == 64 || (V == 128 && RB == 1)))
       return bf16 ? (const void*)&m2rnn_scan_fwd_ro_kernel<V, RB, MATH, true>
                   : (const void*)&m2rnn_scan_fwd_ro_kernel<V, RB, MATH, false>;
     return nullptr;
