@@ -306,3 +306,18 @@ def test_readout_waves_give_the_single_role_kernels_bits(math, monkeypatch):
             torch.cuda.synchronize()
             assert torch.equal(y1, y0) and torch.equal(H1, H0) and torch.equal(c1, c0), (
                 float((y1 - y0).abs().max()), float((H1 - H0).abs().max()))
+
+
+@pytest.mark.parametrize("B,N,K,V", [(12, 32, 64, 64), (8, 16, 128, 128), (16, 128, 64, 16), (2, 32, 64, 64)])
+def test_automatic_plan_takes_one_row_block(B, N, K, V):
+    # The automatic plan takes one 16-row block per wave wherever that kernel keeps its state in
+    # registers, also where that needs several rounds of resident workgroups: the readout planes it
+    # sizes the workspace for (one per workgroup of a pair) are then those of row_blocks = 1.
+    torch_cuda()
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    dims = m2.Dims(B, 4096, N, K, V)
+    for math in ("bf16x3", "f16x3"):
+        auto = m2.m2rnn_fwd_workspace_size(dims, m2.DTYPE_BF16, math, 0)
+        one = m2.m2rnn_fwd_workspace_size(dims, m2.DTYPE_BF16, math, 1)
+        say("plan", B, N, K, V, math, auto, one)
+        assert auto == one, (auto, one)
