@@ -793,32 +793,27 @@ m2rnn_scan_bwd_kernel(const BwdArgs a) {
     }
   };
   // dv[col 16w + i] of walk step j = sum_rows D[row][col] k[row] (+ w_r u when this workgroup holds
-  // all rows), from the transposed D tile's hi and lo halves, each times k (one v_fma_mix_f32
-  // apiece); st is the step's record; ucol, vcol the grouped u, v reads (step j + g, column 16w + n).
+  // all rows), from the transposed D tile's hi and lo halves on the MFMA (k in one fp16 pass: a
+  // relative rounding of 2^-12 per term, as dW's); st is the step's record; ucol, vcol the grouped u,
+  // v reads (step j + g, column 16w + n).
   auto dv_step = [&](int j, int js, const float* st, uint2 dThi, uint2 dTlo, float4 k4, float ucol, float vcol)
                      __attribute__((always_inline)) {
-    float x = fma_mix_f16<false>(dThi.x, k4.x, 0.0f);
-    x = fma_mix_f16<false>(dTlo.x, k4.x, x);
-    x = fma_mix_f16<true>(dThi.x, k4.y, x);
-    x = fma_mix_f16<true>(dTlo.x, k4.y, x);
-    x = fma_mix_f16<false>(dThi.y, k4.z, x);
-    x = fma_mix_f16<false>(dTlo.y, k4.z, x);
-    x = fma_mix_f16<true>(dThi.y, k4.w, x);
-    x = fma_mix_f16<true>(dTlo.y, k4.w, x);
+    // One 16x16x32 fp16 MFMA: B = D's transposed hi and lo halves stacked on the contraction index
+    // (rows 4g .. 4g+3 of each), A = the rows' k (one fp16 pass) twice, the same in every output
+    // row: every lane (g, i) ends with dv[16w + i] in all four registers.
+    const uint32_t k01 = pack_f16(k4.x, k4.y), k23 = pack_f16(k4.z, k4.w);
+    const f32x4 c = mfma_f16(make_uint4(k01, k23, k01, k23), make_uint4(dThi.x, dThi.y, dTlo.x, dTlo.y), zero4);
     if constexpr (GROUP4) {
-      // Steps j .. j+3 are collected in xq; one cross-row reduction of the four leaves lane (g, i)
-      // with dv[step j0 + g][16w + i].
-      xq[j & 3] = x;
+      // lane (g, i) keeps step j0 + g of the group of four, stored once the group is complete
+      if ((j & 3) == g) xq[0] = c[0];
       if ((j & 3) == 0) {
-        float dvv = reduce_rows4(xq[0], xq[1], xq[2], xq[3]);
         dwr1 = __builtin_fmaf(ucol, vcol, dwr1);  // dw_r's product of step j + g, column 16w + n
-        dvv = __builtin_fmaf(wr_col, ucol, dvv);
+        const float dvv = __builtin_fmaf(wr_col, ucol, xq[0]);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv * ug), dvres, dv_lane + (uint32_t)(js * ystep * 4), 0, 0);
       }
     } else {
-      x = sum_rows4(x);
       const float u1 = st[St::OU + 16 * w + n];
-      const float dvv = __builtin_fmaf(wr_col, u1, x);
+      const float dvv = __builtin_fmaf(wr_col, u1, c[0]);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dvv * ug), dvres,
                                             g == 0 ? dv_lane + (uint32_t)(js * ystep * 4) : kBufferDrop, 0, 0);
     }
