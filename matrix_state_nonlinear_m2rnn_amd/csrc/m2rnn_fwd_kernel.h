@@ -222,12 +222,13 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
   if constexpr (MATH == MATH_F16X3) {
     hi = pack_f16(a, b);
     uint32_t l;
-    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\ts_nop 1" : "=v"(l) : "v"(hi), "v"(a));
-    // The trailing s_nop gives the two wait states that a VALU write needs before an MFMA may read
-    // the register; the compiler inserts them for its own instructions but not after inline asm.
-    asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\ts_nop 1"
-        : "+v"(l)
-        : "v"(hi), "v"(b));
+    // Both halves in one asm block (the output is written before b is read: early clobber).  The
+    // trailing s_nop gives the two wait states that a VALU write needs before an MFMA may read the
+    // register; the compiler inserts them for its own instructions but not after inline asm.
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\ts_nop 1"
+        : "=&v"(l)
+        : "v"(hi), "v"(a), "v"(b));
     lo = l;
   } else if constexpr (MATH == MATH_BF16X3) {
     hi = pack_bf16(a, b);
