@@ -73,7 +73,7 @@ enum { M2RNN_DTYPE_F32 = 0, M2RNN_DTYPE_BF16 = 1 };
  *           fp32 accumulation (about 22 significant bits per product).
  *   BF16X3  split precision with bf16 halves: W_hi H_hi + W_lo H_hi + W_hi H_lo.
  *   BF16    one bf16 pass: bf16(W) bf16(H) (coarse; meant for a 2e-2 error budget).
- *   AUTO    the forwards' default: BF16X3 (measured 3% faster than F16X3 at the 16K-token
+ *   AUTO    the forwards' default: BF16X3 (measured as fast as F16X3 at the 16K-token
  *           workload, with the full fp32 exponent range; about 3e-6 max-abs error on the state
  *           where F16X3 gives 3e-7, both far inside a 5e-4 budget).  The backward's own
  *           contraction is F16X3 (below).
