@@ -104,3 +104,59 @@ def test_graph_capture_of_a_long_forward_takes_the_single_pass():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, ref_y) and torch.equal(H_T, ref_H), rep
+
+
+def test_graph_replays_of_a_layer_training_step():
+    # The whole layer's training step (conv4+SiLU, gate, the checkpoint-keeping forward, output gate
+    # + RMSNorm, and the backward of each) captured once and replayed: every output and gradient of
+    # every replay equals the eager step bit for bit.
+    torch = torch_cuda()
+    import numpy as np
+    import matrix_state_nonlinear_m2rnn_amd as m2
+    B, T, N, K, V = 2, 100, 4, 32, 64
+    r = np.random.default_rng(4242)
+    f32 = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float32)).cuda()  # noqa: E731
+    t = {"xq": f32(r.normal(0, 0.7, (B, T, N * K))), "xk": f32(r.normal(0, 0.7, (B, T, N * K))),
+         "xv": f32(r.normal(0, 1.0, (B, T, N * V))), "wq": f32(r.normal(0, 0.5, (N * K, 4))),
+         "wk": f32(r.normal(0, 0.5, (N * K, 4))), "wv": f32(r.normal(0, 0.5, (N * V, 4))),
+         "bq": f32(r.normal(0, 0.1, N * K)), "bk": f32(r.normal(0, 0.1, N * K)), "bv": f32(r.normal(0, 0.1, N * V)),
+         "a": f32(r.normal(0, 2.0, (B, T, N))), "alpha": f32(r.uniform(0.1, 3.0, N)), "beta": f32(r.normal(0, 1, N)),
+         "W": f32(np.stack([np.linalg.qr(r.normal(0, 1, (V, V)))[0] for _ in range(N)]) * 0.9),
+         "w_r": f32(r.normal(0, 0.3, (N, V))), "gz": f32(r.normal(0, 2.0, (B, T, N, V))),
+         "gamma": f32(1.0 + 0.1 * r.normal(0, 1, (N, V))), "dout": f32(r.normal(0, 1.0, (B, T, N, V)))}
+    say("graph capture: layer training step", B, T, N, K, V)
+
+    def step():
+        uq = m2.m2rnn_conv4_silu_fwd(t["xq"], t["wq"], t["bq"]).view(B, T, N, K)
+        uk = m2.m2rnn_conv4_silu_fwd(t["xk"], t["wk"], t["bk"]).view(B, T, N, K)
+        uv = m2.m2rnn_conv4_silu_fwd(t["xv"], t["wv"], t["bv"]).view(B, T, N, V)
+        f = m2.m2rnn_gate_fwd(t["a"], t["alpha"], t["beta"])
+        y, H_T, ckpt = m2.m2rnn_fwd_ckpt(uq, uk, uv, f, t["W"], t["w_r"])
+        out = m2.m2rnn_out_norm_fwd(y, t["gz"], t["gamma"], 1e-6)
+        gn = m2.m2rnn_out_norm_bwd(y, t["gz"], t["gamma"], t["dout"], 1e-6)
+        gs = m2.m2rnn_bwd_ckpt(uq, uk, uv, f, t["W"], t["w_r"], ckpt, gn["dy"])
+        gg = m2.m2rnn_gate_bwd(t["a"], t["alpha"], t["beta"], gs["df"])
+        res = {"out": out, "H_T": H_T, "dgz": gn["dgz"], "dgamma": gn["dgamma"], "dW": gs["dW"], "dw_r": gs["dw_r"],
+               "da": gg["da"], "dalpha": gg["dalpha"], "dbeta": gg["dbeta"]}
+        for x in ("q", "k", "v"):
+            c = m2.m2rnn_conv4_silu_bwd(t["x" + x], t["w" + x], t["b" + x],
+                                        gs["d" + x].reshape(B, T, -1).contiguous())
+            res["dx" + x], res["dw" + x], res["db" + x] = c["dx"], c["dw"], c["dbias"]
+        return res
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        eager = {k: v.clone() for k, v in step().items()}
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        cap = step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in cap.values():
+            v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, ref in eager.items():
+            assert torch.equal(cap[name], ref), (rep, name)
