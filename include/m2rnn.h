@@ -215,7 +215,9 @@ int m2rnn_scan_fwd_finish(const m2rnn_dims* dims, int qkv_dtype, int math, int r
  * are exact, so the result for 2^k dy is exactly 2^k times the result for dy (over the whole
  * fp32 range of dy, bar fp32 underflow or overflow of the gradients themselves): training without
  * loss scaling, whose activation gradients are far below unit size, keeps the same accuracy.
- * W must satisfy |W| < 65504 elementwise (the chain multiplies by W^T in split fp16).
+ * W must satisfy |W| < 65504 elementwise (the chain multiplies by W^T in split fp16), and k
+ * |k| < 65504 (dv = D^T k is formed on fp16 MFMA with k in one fp16 pass, a relative rounding of
+ * 2^-12 per term, as dW's operands).
  */
 #define M2RNN_BWD_CHECKPOINT 64
 int m2rnn_bwd_workspace_size(const m2rnn_dims* dims, int qkv_dtype, int math, size_t* bytes);
