@@ -69,7 +69,7 @@ def test_shapes_and_ragged_steps(K, V, T):
     d = inputs.make_inputs(2, T, 3, K, V, qkv_dtype="bf16", seed=1000 + K + V + T, with_H0=True)
     dd = to_device(d, "bf16")
     yr, Hr = oracle_fwd(d)
-    for math in ("f32", "f16x3"):
+    for math in ("f32", "f16x3", "bf16x3"):
         say("shape", K, V, T, math)
         y, H = gpu_fwd(dd, math)
         assert max_abs(y, yr) <= TOL[math] and max_abs(H, Hr) <= TOL[math], (math, max_abs(y, yr), max_abs(H, Hr))
